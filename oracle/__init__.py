@@ -1,0 +1,31 @@
+"""CPU oracle for exact Lookahead decoding -- TEST INFRASTRUCTURE ONLY.
+
+A plain, slow, obviously-correct numpy implementation of what the packed
+lookahead + verification step computes.  It follows the pages in their order
+and notation:
+
+* "M7.3 - Lookahead Decoding: Jacobi Iterations, N-Gram Pools, and Parallel
+  Verification" (the primary specification: window, pool, packed rows and
+  branch visibility, greedy and one-hot sampling verification, publication);
+* "Break the Sequential Dependency of LLM Inference Using Lookahead Decoding"
+  (paper summary: lossless claim, G = W practice, expected-accepted model);
+* "Speculative Decoding" lesson, Chapters 1-2 (general p/q rejection
+  sampling, the three-token vocabulary, the acceptance-rate arithmetic).
+
+Floating point is fp64 except where the method fixes a storage precision
+(the model's storage dtype at every stored activation, float32 logits).
+
+Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may
+import this package.  It shares no code with the HIP path and imports
+nothing from it; the only common dependency is the seeded input generator
+module `synthetic`, which holds none of the method's arithmetic.
+
+Parity status per module:
+  numerics, rows, window, pool, commit, verify, philox, jacobi, acceptance,
+  attention -- pinned by page values, closed forms or brute force in
+  tests/test_oracle_*.py.
+  model -- parity unpinned by the pages (they print no activations); pinned
+  internally by textbook identities (softmax attention against an explicit
+  loop, RoPE rotation invariants, RMSNorm scale invariance) and by the
+  separate-forwards == dense-mask == autoregressive equalities.
+"""
