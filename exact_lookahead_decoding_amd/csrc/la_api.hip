@@ -1,0 +1,758 @@
+// Host orchestrator and C ABI (include/la.h).
+//
+// One context = one request.  A round follows "M7.3 - Lookahead Decoding"
+// (0x03A lifecycle, 0x06 loop, 0x06A publication plan, 0x07 fail-closed
+// publication):
+//   la_predict : pool lookup for x_t (after warmup) -> row manifest ->
+//                target forward over the packed rows -> fp32 logits of the
+//                out / inp / guess rows only;
+//   la_verify  : argmax (greedy) or one-hot sampling -> accept record + z;
+//   la_commit  : validate the plan, then K/V compaction, pool upsert from
+//                the pre-shift window and z, window advance, output append.
+// The only host<->device synchronisations of a round are the candidate
+// count after the lookup and the accept record after verification.
+#include "../../include/la.h"
+#include "la_kernels.h"
+
+#include <algorithm>
+#include <cstdarg>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#define PREFILL_CHUNK 128
+
+static thread_local std::string g_err;
+
+struct la_ctx {
+  la_config cfg;
+  la_model_dims dims;
+  la_model w;
+  hipStream_t st;
+  int dtype, esz;
+  int L, d, H, Hkv, dh, F, V, qkvdim;
+  int R, S;
+  int t_cap, q_max, m_max, ws_cap, n_logit_max, nb_max, maxp_max, words_max, spans_max, wstride, rows_words;
+  int rope_rows;      // positions reach kv_len + maxp, beyond the K/V capacity
+  // device
+  char* kc;
+  char* vc;
+  void *x, *nrm, *qkv, *q, *o, *act, *fin, *kw, *vw;
+  float *gemm_p, *attn_po, *attn_pml, *logits;
+  float2* rope;
+  int32_t* rowbuf;
+  int32_t *pf_tok, *pf_pos, *pf_branch, *pf_path, *pf_logit;
+  int32_t *pool_cnt, *pool_ent;
+  int32_t* win[2];
+  int cur;
+  int32_t *cand, *ncand, *vcand, *amax, *z, *z2, *tok1;
+  LaAcceptDev* acc;
+  double* escr;
+  // host state
+  std::vector<int32_t> out;
+  int kv_len = 0;
+  int round_id = 0;
+  int sizes[LA_MAX_N];
+  bool warm = false;
+  bool pending = false, verified = false;
+  LaLayout lay;
+  LaRowsDev rows;
+  std::vector<int32_t> cand_host;
+  la_accept vacc;
+  la_stats_t stats;
+  std::string err;
+};
+
+static int fail(la_ctx* c, int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  if (c) c->err = buf;
+  g_err = buf;
+  return code;
+}
+
+#define HIPCHK(c, call)                                                                         \
+  do {                                                                                          \
+    hipError_t _e = (call);                                                                     \
+    if (_e != hipSuccess) return fail((c), LA_EDEVICE, "%s: %s", #call, hipGetErrorString(_e)); \
+  } while (0)
+
+// ------------------------------------------------------------------ sizing
+
+static int validate_cfg(const la_config* cfg, const la_model_dims* d, la_ctx* c) {
+  if (!cfg || !d) return fail(c, LA_EINVAL, "null config or dims");
+  if (cfg->N < 3 || cfg->N > LA_MAX_N) return fail(c, LA_EINVAL, "N=%d not admitted (pinned schedule needs 3 <= N <= %d)", cfg->N, LA_MAX_N);
+  if (cfg->W < 1 || cfg->W > 64) return fail(c, LA_EINVAL, "W=%d out of range [1, 64]", cfg->W);
+  if (cfg->G < 0 || cfg->G > 64) return fail(c, LA_EINVAL, "G=%d out of range [0, 64]", cfg->G);
+  if (cfg->max_new < 1 || cfg->max_prompt < 1) return fail(c, LA_EINVAL, "max_new and max_prompt must be >= 1");
+  if (cfg->verify_mode != LA_VERIFY_GREEDY && cfg->verify_mode != LA_VERIFY_SAMPLE)
+    return fail(c, LA_EINVAL, "verify_mode %d", cfg->verify_mode);
+  if (cfg->verify_mode == LA_VERIFY_SAMPLE && !(cfg->temperature > 0.0)) return fail(c, LA_EINVAL, "temperature must be > 0");
+  if (d->dtype != LA_DTYPE_F32 && d->dtype != LA_DTYPE_BF16) return fail(c, LA_EINVAL, "dtype %d", d->dtype);
+  if (d->n_layers < 1 || d->d_model < 16 || d->n_heads < 1 || d->n_kv_heads < 1 || d->n_heads % d->n_kv_heads)
+    return fail(c, LA_EINVAL, "bad model dims");
+  const int dh = d->head_dim;
+  if (!(d->dtype == LA_DTYPE_BF16 ? (dh == 128 || dh == 64) : (dh == 16 || dh == 64)))
+    return fail(c, LA_EINVAL, "head_dim %d unsupported", dh);
+  if (d->vocab < 2 || d->vocab > 65536) return fail(c, LA_EINVAL, "vocab %d out of range", d->vocab);
+  return LA_OK;
+}
+
+static void setup_dims(la_ctx* c) {
+  const la_config& g = c->cfg;
+  const la_model_dims& d = c->dims;
+  c->dtype = d.dtype == LA_DTYPE_BF16 ? LA_DT_BF16 : LA_DT_F32;
+  c->esz = d.dtype == LA_DTYPE_BF16 ? 2 : 4;
+  c->L = d.n_layers; c->d = d.d_model; c->H = d.n_heads; c->Hkv = d.n_kv_heads; c->dh = d.head_dim;
+  c->F = d.d_ff; c->V = d.vocab;
+  c->qkvdim = (c->H + 2 * c->Hkv) * c->dh;
+  c->R = g.N - 1; c->S = g.N - 1;
+  // most rows over the warmup schedule and the steady state with G candidates
+  int sz[LA_MAX_N] = {0};
+  sz[0] = g.W + g.N - 3;
+  int qmax = 0, lmax = 0, ncmax = 0, pmax = c->S;
+  for (int stage = 0; stage < c->R; ++stage) {
+    LaLayout L{};
+    L.p = 0; L.R = c->R; L.C = g.G; L.S = c->S;
+    for (int r = 0; r < c->R; ++r) { L.sizes[r] = sz[r]; L.starts[r] = r == 0 ? 1 : 0; }
+    if (la_layout_finish(&L) == 0) {
+      qmax = std::max(qmax, L.Q); lmax = std::max(lmax, L.n_logit);
+      ncmax = std::max(ncmax, L.NB); pmax = std::max(pmax, L.maxp);
+    }
+    int dpt = 0;
+    for (int r = 0; r < c->R; ++r) if (sz[r] > 0) dpt = r;
+    if (dpt + 1 < c->R) {
+      const int ninp = sz[dpt];
+      for (int r = 0; r <= dpt; ++r) sz[r] -= 1;
+      sz[dpt + 1] = ninp - (dpt >= 1 ? 1 : 0);
+    }
+  }
+  c->q_max = std::max(qmax, 1);
+  c->n_logit_max = std::max(lmax, 1);
+  c->nb_max = std::max(ncmax, 1);
+  c->maxp_max = std::max(pmax, 1);
+  c->words_max = (c->q_max + 31) / 32;
+  c->m_max = std::max(c->q_max, PREFILL_CHUNK);
+  c->ws_cap = c->q_max;
+  c->t_cap = g.max_prompt + g.max_new + 16;
+  c->spans_max = la_attention_spans(c->t_cap + c->q_max);
+  c->rope_rows = c->t_cap + c->q_max + 1;
+  c->wstride = g.W + g.N;
+  c->rows_words = 8 * c->q_max + c->nb_max * c->maxp_max + c->nb_max + c->n_logit_max + c->q_max * c->words_max;
+}
+
+static size_t gemm_partial_floats(la_ctx* c) {
+  struct { int N, K, sw, M; } mats[] = {
+      {c->qkvdim, c->d, 0, c->m_max}, {c->d, c->H * c->dh, 0, c->m_max}, {c->F, c->d, 1, c->m_max},
+      {c->d, c->F, 0, c->m_max},      {c->V, c->d, 0, c->n_logit_max}};
+  size_t mx = 0;
+  for (auto& m : mats) {
+    const int s = la_gemm_splits(m.N, m.K, c->dtype, m.sw);
+    if (s > 1) mx = std::max(mx, (size_t)s * m.M * (m.sw ? 2 * m.N : m.N));
+  }
+  return mx;
+}
+
+static size_t carve(la_ctx* c, char* base) {
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> void* {
+    void* p = base ? (void*)(base + off) : nullptr;
+    off += (bytes + 255) & ~(size_t)255;
+    return p;
+  };
+  const size_t e = c->esz;
+  c->x = take((size_t)c->m_max * c->d * e);
+  c->nrm = take((size_t)c->m_max * c->d * e);
+  c->qkv = take((size_t)c->m_max * c->qkvdim * e);
+  c->q = take((size_t)c->m_max * c->H * c->dh * e);
+  c->o = take((size_t)c->m_max * c->H * c->dh * e);
+  c->act = take((size_t)c->m_max * c->F * e);
+  c->fin = take((size_t)c->n_logit_max * c->d * e);
+  c->kw = take((size_t)c->L * c->Hkv * c->ws_cap * c->dh * e);
+  c->vw = take((size_t)c->L * c->Hkv * c->ws_cap * c->dh * e);
+  c->gemm_p = (float*)take(std::max<size_t>(gemm_partial_floats(c), 1) * 4);
+  c->attn_po = (float*)take((size_t)c->spans_max * c->H * c->m_max * c->dh * 4);
+  c->attn_pml = (float*)take((size_t)c->spans_max * c->H * c->m_max * 2 * 4);
+  c->logits = (float*)take((size_t)c->n_logit_max * c->V * 4);
+  c->rope = (float2*)take((size_t)c->rope_rows * (c->dh / 2) * sizeof(float2));
+  c->rowbuf = (int32_t*)take((size_t)c->rows_words * 4);
+  c->pf_tok = (int32_t*)take((size_t)c->m_max * 4);
+  c->pf_pos = (int32_t*)take((size_t)c->m_max * 4);
+  c->pf_branch = (int32_t*)take((size_t)c->m_max * 4);
+  c->pf_path = (int32_t*)take(64);
+  c->pf_logit = (int32_t*)take(64);
+  c->pool_cnt = (int32_t*)take((size_t)c->V * 4);
+  c->pool_ent = (int32_t*)take((size_t)c->V * std::max(c->cfg.G, 1) * c->S * 4);
+  c->win[0] = (int32_t*)take((size_t)c->R * c->wstride * 4);
+  c->win[1] = (int32_t*)take((size_t)c->R * c->wstride * 4);
+  c->cand = (int32_t*)take((size_t)64 * LA_MAX_N * 4);
+  c->vcand = (int32_t*)take((size_t)64 * LA_MAX_N * 4);
+  c->ncand = (int32_t*)take(64);
+  c->amax = (int32_t*)take((size_t)std::max(c->n_logit_max, 64) * 4);
+  c->acc = (LaAcceptDev*)take(sizeof(LaAcceptDev));
+  c->z = (int32_t*)take((size_t)c->wstride * 4);
+  c->z2 = (int32_t*)take((size_t)std::max(c->wstride, 64) * 4);
+  c->tok1 = (int32_t*)take(64);
+  c->escr = (double*)take((size_t)c->V * 8);
+  return off;
+}
+
+extern "C" int la_query_sizes(const la_config* cfg, const la_model_dims* dims, la_sizes* out) {
+  int rc = validate_cfg(cfg, dims, nullptr);
+  if (rc) return rc;
+  if (!out) return fail(nullptr, LA_EINVAL, "null output");
+  la_ctx c{};
+  c.cfg = *cfg;
+  c.dims = *dims;
+  setup_dims(&c);
+  out->kv_bytes = 2ull * c.L * c.Hkv * (size_t)c.t_cap * c.dh * c.esz;
+  out->arena_bytes = carve(&c, nullptr);
+  out->t_cap = c.t_cap;
+  out->q_max = c.q_max;
+  out->n_logit_max = c.n_logit_max;
+  out->reserved = 0;
+  return LA_OK;
+}
+
+// ------------------------------------------------------------------ forward
+
+static const char* wptr(const void* base, size_t elems_per_layer, int l, int esz) {
+  return (const char*)base + (size_t)l * elems_per_layer * esz;
+}
+
+static int gemm(la_ctx* c, int epi, const void* X, const void* W, void* Y, const void* Rr, int M, int N, int K,
+                int up_off) {
+  LaGemmArgs a{};
+  a.X = X; a.W = W; a.Y = Y; a.R = Rr; a.P = c->gemm_p;
+  a.M = M; a.N = N; a.K = K; a.ldx = K; a.ldy = N;
+  a.splits = la_gemm_splits(N, K, c->dtype, epi == LA_EPI_SWIGLU);
+  a.up_off = up_off;
+  a.pcols = epi == LA_EPI_SWIGLU ? 2 * N : N;
+  const int rc = la_gemm_launch(c->dtype, epi, a, c->st);
+  if (rc) return fail(c, rc == -2 ? LA_EINVAL : LA_EDEVICE, "gemm launch failed (M=%d N=%d K=%d rc=%d)", M, N, K, rc);
+  return LA_OK;
+}
+
+// Forward M rows.  K/V of rows < n_direct go to cache rows cache_row0 + m,
+// the others to workspace rows m - n_direct.  Keys below shared_end come
+// from the cache.  Logits (fp32) of logit_rows[0..n_logit) land in c->logits.
+static int forward(la_ctx* c, int M, const int32_t* tok, const int32_t* pos, const int32_t* branch,
+                   const int32_t* path, const int32_t* path_len, int maxp, int n_direct, int cache_row0,
+                   int shared_end, int max_pos, const int32_t* logit_rows, int n_logit) {
+  const int esz = c->esz;
+  const size_t kvl = (size_t)c->Hkv * c->t_cap * c->dh;   // elements per layer
+  const size_t wsl = (size_t)c->Hkv * c->ws_cap * c->dh;
+  la_embed_launch(c->dtype, c->w.embed, tok, c->x, M, c->d, c->st);
+  LaAttnArgs at{};
+  at.q = c->q; at.o = c->o; at.part_o = c->attn_po; at.part_ml = c->attn_pml;
+  at.pos = pos; at.branch = branch; at.path = path; at.path_len = path_len;
+  at.Q = M; at.H = c->H; at.Hkv = c->Hkv; at.dh = c->dh; at.T_cap = c->t_cap; at.ws_cap = c->ws_cap; at.maxp = maxp;
+  at.shared_end = shared_end;
+  at.n_spans = la_attention_spans(max_pos);
+  at.scale = 1.0f / sqrtf((float)c->dh);
+  if (at.n_spans > c->spans_max) return fail(c, LA_EOVERFLOW, "attention spans %d > %d", at.n_spans, c->spans_max);
+  for (int l = 0; l < c->L; ++l) {
+    const char* attn_norm = wptr(c->w.attn_norm, c->d, l, esz);
+    const char* mlp_norm = wptr(c->w.mlp_norm, c->d, l, esz);
+    const char* wqkv = wptr(c->w.wqkv, (size_t)c->qkvdim * c->d, l, esz);
+    const char* wo = wptr(c->w.wo, (size_t)c->d * c->H * c->dh, l, esz);
+    const char* wgu = wptr(c->w.w_gate_up, (size_t)2 * c->F * c->d, l, esz);
+    const char* wdn = wptr(c->w.w_down, (size_t)c->d * c->F, l, esz);
+    char* kc = c->kc + l * kvl * esz;
+    char* vc = c->vc + l * kvl * esz;
+    char* kw = (char*)c->kw + l * wsl * esz;
+    char* vw = (char*)c->vw + l * wsl * esz;
+    int rc;
+    la_rmsnorm_launch(c->dtype, c->x, attn_norm, c->nrm, nullptr, M, c->d, c->dims.eps, c->st);
+    if ((rc = gemm(c, LA_EPI_STORE, c->nrm, wqkv, c->qkv, nullptr, M, c->qkvdim, c->d, 0))) return rc;
+    la_qkv_post_launch(c->dtype, c->qkv, c->rope, pos, M, c->H, c->Hkv, c->dh, c->q, kc, vc, c->t_cap, cache_row0,
+                       n_direct, kw, vw, c->ws_cap, c->st);
+    at.kc = kc; at.vc = vc; at.kw = kw; at.vw = vw;
+    if ((rc = la_attention_launch(c->dtype, at, c->st))) return fail(c, LA_EDEVICE, "attention launch failed (%d)", rc);
+    if ((rc = gemm(c, LA_EPI_RESID, c->o, wo, c->x, c->x, M, c->d, c->H * c->dh, 0))) return rc;
+    la_rmsnorm_launch(c->dtype, c->x, mlp_norm, c->nrm, nullptr, M, c->d, c->dims.eps, c->st);
+    if ((rc = gemm(c, LA_EPI_SWIGLU, c->nrm, wgu, c->act, nullptr, M, c->F, c->d, c->F))) return rc;
+    if ((rc = gemm(c, LA_EPI_RESID, c->act, wdn, c->x, c->x, M, c->d, c->F, 0))) return rc;
+  }
+  if (n_logit > 0) {
+    la_rmsnorm_launch(c->dtype, c->x, c->w.final_norm, c->fin, logit_rows, n_logit, c->d, c->dims.eps, c->st);
+    int rc = gemm(c, LA_EPI_F32, c->fin, c->w.lm_head, c->logits, nullptr, n_logit, c->V, c->d, 0);
+    if (rc) return rc;
+  }
+  HIPCHK(c, hipGetLastError());
+  return LA_OK;
+}
+
+static void rows_layout(const LaLayout& L, int32_t* base, LaRowsDev* r, la_rows_info* info) {
+  const int Q = L.Q;
+  int off = 0;
+  auto take = [&](int n) { int o = off; off += n; return o; };
+  const int o_tok = take(Q), o_pos = take(Q), o_role = take(Q), o_level = take(Q), o_col = take(Q),
+            o_cand = take(Q), o_off = take(Q), o_branch = take(Q), o_path = take(L.NB * L.maxp),
+            o_plen = take(L.NB), o_logit = take(L.n_logit), o_mask = take(Q * L.mask_words);
+  if (r) {
+    r->tok = base + o_tok; r->pos = base + o_pos; r->role = base + o_role; r->level = base + o_level;
+    r->col = base + o_col; r->cand = base + o_cand; r->off = base + o_off; r->branch = base + o_branch;
+    r->path = base + o_path; r->path_len = base + o_plen; r->logit_rows = base + o_logit;
+    r->mask = (uint32_t*)(base + o_mask);
+  }
+  if (info) {
+    info->Q = Q; info->NB = L.NB; info->maxp = L.maxp; info->n_logit = L.n_logit; info->n_inp = L.n_inp;
+    info->n_cols = L.n_cols; info->mask_words = L.mask_words; info->total_words = off;
+    info->off_tok = o_tok; info->off_pos = o_pos; info->off_role = o_role; info->off_level = o_level;
+    info->off_col = o_col; info->off_cand = o_cand; info->off_off = o_off; info->off_branch = o_branch;
+    info->off_path = o_path; info->off_path_len = o_plen; info->off_logit_rows = o_logit; info->off_mask = o_mask;
+  }
+}
+
+// ------------------------------------------------------------------ lifecycle
+
+extern "C" int la_init(const la_config* cfg, const la_model_dims* dims, const la_model* weights, void* kv,
+                       void* arena, const int32_t* prompt, int32_t prompt_len, void* stream, la_ctx** out) {
+  if (!out) return fail(nullptr, LA_EINVAL, "null ctx output");
+  *out = nullptr;
+  int rc = validate_cfg(cfg, dims, nullptr);
+  if (rc) return rc;
+  if (!weights || !kv || !arena || !prompt) return fail(nullptr, LA_EINVAL, "null weights, buffers or prompt");
+  if (prompt_len < 1 || prompt_len > cfg->max_prompt)
+    return fail(nullptr, LA_EINVAL, "prompt_len %d outside [1, max_prompt=%d]", prompt_len, cfg->max_prompt);
+  for (int i = 0; i < prompt_len; ++i)
+    if (prompt[i] < 0 || prompt[i] >= dims->vocab) return fail(nullptr, LA_EINVAL, "prompt token %d out of range", i);
+  la_ctx* c = new la_ctx();
+  c->cfg = *cfg;
+  c->dims = *dims;
+  c->w = *weights;
+  c->st = (hipStream_t)stream;
+  setup_dims(c);
+  const size_t kvb = (size_t)c->L * c->Hkv * c->t_cap * c->dh * c->esz;
+  c->kc = (char*)kv;
+  c->vc = (char*)kv + kvb;
+  carve(c, (char*)arena);
+  memset(&c->stats, 0, sizeof c->stats);
+  for (int r = 0; r < LA_MAX_N; ++r) c->sizes[r] = 0;
+  c->cur = 0;
+  auto bail = [&](int code) { delete c; return code; };
+#define CK(call)                                                                   \
+  do {                                                                             \
+    hipError_t _e = (call);                                                        \
+    if (_e != hipSuccess) {                                                        \
+      fail(nullptr, LA_EDEVICE, "%s: %s", #call, hipGetErrorString(_e));           \
+      return bail(LA_EDEVICE);                                                     \
+    }                                                                              \
+  } while (0)
+  la_rope_table_launch(c->rope, c->rope_rows, c->dh, c->dims.rope_theta, c->st);
+  la_pool_clear_launch(c->pool_cnt, c->V, c->st);
+  // window: level 0 seeded with the last W + N - 3 prompt tokens (cyclic)
+  if (!c->cfg.ar_only) {
+    const int n0 = c->cfg.W + c->cfg.N - 3;
+    std::vector<int32_t> w0((size_t)c->R * c->wstride, 0);
+    for (int i = 0; i < n0; ++i) w0[i] = prompt[(((prompt_len - n0 + i) % prompt_len) + prompt_len) % prompt_len];
+    CK(hipMemcpyAsync(c->win[0], w0.data(), w0.size() * 4, hipMemcpyHostToDevice, c->st));
+    c->sizes[0] = n0;
+  }
+  // prefill in chunks; every row's K/V goes straight to the cache
+  std::vector<int32_t> tok, pos, br;
+  for (int c0 = 0; c0 < prompt_len; c0 += PREFILL_CHUNK) {
+    const int M = std::min(PREFILL_CHUNK, prompt_len - c0);
+    tok.assign(prompt + c0, prompt + c0 + M);
+    pos.resize(M);
+    br.assign(M, 0);
+    for (int i = 0; i < M; ++i) pos[i] = c0 + i;
+    const int32_t zero[2] = {0, M - 1};
+    CK(hipMemcpyAsync(c->pf_tok, tok.data(), M * 4, hipMemcpyHostToDevice, c->st));
+    CK(hipMemcpyAsync(c->pf_pos, pos.data(), M * 4, hipMemcpyHostToDevice, c->st));
+    CK(hipMemcpyAsync(c->pf_branch, br.data(), M * 4, hipMemcpyHostToDevice, c->st));
+    CK(hipMemcpyAsync(c->pf_path, zero, 4, hipMemcpyHostToDevice, c->st));
+    CK(hipMemcpyAsync(c->pf_logit, zero + 1, 4, hipMemcpyHostToDevice, c->st));
+    const bool last = c0 + M >= prompt_len;
+    rc = forward(c, M, c->pf_tok, c->pf_pos, c->pf_branch, c->pf_path, c->pf_path, 1, M, c0, c0 + M, c0 + M - 1,
+                 c->pf_logit, last ? 1 : 0);
+    if (rc) { g_err = c->err; return bail(rc); }
+    CK(hipStreamSynchronize(c->st));        // the host-side chunk arrays are reused
+  }
+  // first output token from the last prompt row
+  la_argmax_launch(c->logits, 1, c->V, c->amax, c->st);
+  if (c->cfg.verify_mode == LA_VERIFY_SAMPLE)
+    la_sample_row_launch(c->logits, c->V, c->cfg.temperature, c->cfg.seed, 0, c->amax, c->escr, c->tok1, c->st);
+  int32_t first = 0;
+  CK(hipMemcpyAsync(&first, c->cfg.verify_mode == LA_VERIFY_SAMPLE ? c->tok1 : c->amax, 4, hipMemcpyDeviceToHost,
+                    c->st));
+  CK(hipStreamSynchronize(c->st));
+#undef CK
+  c->out.push_back(first);
+  c->kv_len = prompt_len;
+  c->stats.tokens = 1;
+  *out = c;
+  return LA_OK;
+}
+
+extern "C" void la_destroy(la_ctx* c) { delete c; }
+
+// ------------------------------------------------------------------ round
+
+static bool is_warm(const la_ctx* c) {
+  for (int r = 0; r < c->R; ++r)
+    if (c->sizes[r] <= 0) return false;
+  return true;
+}
+
+extern "C" int la_predict(la_ctx* c, la_round_info* info) {
+  if (!c) return fail(nullptr, LA_EINVAL, "null ctx");
+  if (c->pending) return fail(c, LA_ESTATE, "round %d is pending commit", c->round_id + 1);
+  if ((int)c->out.size() >= c->cfg.max_new) return fail(c, LA_ESTATE, "max_new tokens already generated");
+  const int x_t = c->out.back();
+  const int p = c->kv_len;
+  if (p + 1 + c->S > c->t_cap) return fail(c, LA_EOVERFLOW, "K/V capacity %d exhausted", c->t_cap);
+  const bool warm = !c->cfg.ar_only && is_warm(c);
+  int C = 0;
+  c->cand_host.clear();
+  if (warm && c->cfg.G > 0) {
+    la_pool_lookup_launch(c->pool_cnt, c->pool_ent, x_t, c->cfg.G, c->S, c->cand, c->ncand, c->st);
+    int32_t nc = 0;
+    HIPCHK(c, hipMemcpyAsync(&nc, c->ncand, 4, hipMemcpyDeviceToHost, c->st));
+    HIPCHK(c, hipStreamSynchronize(c->st));
+    C = nc;
+    if (C > 0) {
+      c->cand_host.resize((size_t)C * c->S);
+      HIPCHK(c, hipMemcpyAsync(c->cand_host.data(), c->cand, (size_t)C * c->S * 4, hipMemcpyDeviceToHost, c->st));
+    }
+  }
+  LaLayout L{};
+  L.p = p; L.R = c->R; L.C = C; L.S = c->S;
+  for (int r = 0; r < c->R; ++r) { L.sizes[r] = c->cfg.ar_only ? 0 : c->sizes[r]; L.starts[r] = r == 0 ? 1 : 0; }
+  if (la_layout_finish(&L)) return fail(c, LA_EINVAL, "inconsistent window layout");
+  if (L.Q > c->q_max) return fail(c, LA_EOVERFLOW, "round needs %d rows > q_max %d", L.Q, c->q_max);
+  if (p + L.maxp >= c->rope_rows) return fail(c, LA_EOVERFLOW, "position %d beyond the RoPE table", p + L.maxp);
+  rows_layout(L, c->rowbuf, &c->rows, nullptr);
+  la_build_rows_launch(L, x_t, c->win[c->cur], c->wstride, c->cand, c->rows, c->st);
+  const int maxpos = p + L.maxp;             // a row's branch path covers its own position
+  int rc = forward(c, L.Q, c->rows.tok, c->rows.pos, c->rows.branch, c->rows.path, c->rows.path_len, L.maxp, 1, p,
+                   p + 1, maxpos, c->rows.logit_rows, L.n_logit);
+  if (rc) return rc;
+  c->lay = L;
+  c->pending = true;
+  c->verified = false;
+  c->warm = warm;
+  if (info) {
+    info->round_id = c->round_id + 1;
+    info->p = p; info->Q = L.Q; info->C = C; info->n_inp = L.n_inp; info->n_logit = L.n_logit;
+    info->warm = warm ? 1 : 0;
+    info->reserved = 0;
+    info->logits = c->logits;
+  }
+  return LA_OK;
+}
+
+extern "C" int la_verify(la_ctx* c, const float* logits, int32_t n_inp, const int32_t* cand, int32_t C, la_accept* out,
+                         int32_t* z_host) {
+  if (!c || !out) return fail(c, LA_EINVAL, "null ctx or output");
+  const bool own = logits == nullptr;
+  const int32_t* cand_dev;
+  int32_t* zdev;
+  if (own) {
+    if (!c->pending) return fail(c, LA_ESTATE, "no predicted round to verify");
+    logits = c->logits;
+    n_inp = c->lay.n_inp;
+    C = c->lay.C;
+    cand_dev = c->cand;
+    zdev = c->z;
+  } else {
+    if (C < 0 || C > 64 || n_inp < 0 || n_inp > c->wstride) return fail(c, LA_EINVAL, "bad C=%d or n_inp=%d", C, n_inp);
+    if (C > 0 && !cand) return fail(c, LA_EINVAL, "null candidates");
+    if (1 + n_inp + C * c->S > c->n_logit_max) return fail(c, LA_EOVERFLOW, "too many logit rows");
+    if (C > 0)
+      HIPCHK(c, hipMemcpyAsync(c->vcand, cand, (size_t)C * c->S * 4, hipMemcpyHostToDevice, c->st));
+    cand_dev = c->vcand;
+    zdev = c->z2;
+  }
+  const int n_logit = 1 + n_inp + C * c->S;
+  const int rid = c->round_id + 1;          // the draws of the round being decided
+  la_argmax_launch(logits, n_logit, c->V, c->amax, c->st);
+  if (c->cfg.verify_mode == LA_VERIFY_SAMPLE)
+    la_sample_accept_launch(logits, c->V, n_inp, c->amax, cand_dev, C, c->S, c->cfg.temperature, c->cfg.seed, rid,
+                            c->escr, c->acc, zdev, c->st);
+  else
+    la_greedy_accept_launch(c->amax, n_inp, cand_dev, C, c->S, c->acc, zdev, c->st);
+  LaAcceptDev a;
+  HIPCHK(c, hipGetLastError());
+  HIPCHK(c, hipMemcpyAsync(&a, c->acc, sizeof a, hipMemcpyDeviceToHost, c->st));
+  if (z_host && n_inp > 0) HIPCHK(c, hipMemcpyAsync(z_host, zdev, (size_t)n_inp * 4, hipMemcpyDeviceToHost, c->st));
+  HIPCHK(c, hipStreamSynchronize(c->st));
+  memset(out, 0, sizeof *out);
+  out->round_id = rid;
+  out->h = a.h;
+  out->winner = a.winner;
+  out->n_emit = a.n_emit;
+  for (int i = 0; i < a.n_emit && i < LA_MAX_EMIT; ++i) out->emitted[i] = a.emitted[i];
+  if (own) {
+    c->vacc = *out;
+    c->verified = true;
+  }
+  return LA_OK;
+}
+
+extern "C" int la_commit(la_ctx* c, const la_accept* a) {
+  if (!c || !a) return fail(c, LA_EINVAL, "null ctx or plan");
+  if (!c->pending || !c->verified) return fail(c, LA_ESTATE, "no verified round pending");
+  const int rid = c->round_id + 1;
+  if (a->round_id != rid) return fail(c, LA_ESTATE, "plan for round %d, pending round is %d", a->round_id, rid);
+  const LaLayout& L = c->lay;
+  const int S = c->S;
+  // --- validation: nothing below this block may fail before publication ---
+  if (a->h < 0 || a->h > S) return fail(c, LA_EPLAN, "h=%d outside [0, S=%d]", a->h, S);
+  if (a->n_emit != a->h + 1) return fail(c, LA_EPLAN, "n_emit=%d != h+1", a->n_emit);
+  if (a->h > 0 && (a->winner < 0 || a->winner >= L.C)) return fail(c, LA_EPLAN, "winner %d not a candidate", a->winner);
+  if (a->h == 0 && a->winner != -1) return fail(c, LA_EPLAN, "winner %d with h=0", a->winner);
+  for (int k = 0; k < a->n_emit; ++k)
+    if (a->emitted[k] < 0 || a->emitted[k] >= c->V) return fail(c, LA_EPLAN, "emitted token %d out of range", k);
+  for (int k = 0; k < a->h; ++k)
+    if (a->emitted[k] != c->cand_host[(size_t)a->winner * S + k])
+      return fail(c, LA_EPLAN, "emitted[%d] is not the winner's suffix token", k);
+  if (memcmp(a, &c->vacc, sizeof *a) != 0) return fail(c, LA_EPLAN, "plan differs from the verified result");
+  if (c->kv_len + 1 + a->h > c->t_cap) return fail(c, LA_EOVERFLOW, "K/V capacity");
+  // --- publication ---
+  const int cand_start = L.Q - L.C * S;
+  if (a->h > 0)
+    la_kv_commit_launch(c->dtype, c->kc, c->vc, c->kw, c->vw, c->L, c->Hkv, c->dh, c->t_cap, c->ws_cap,
+                        c->kv_len + 1, cand_start - 1 + a->winner * S, a->h, c->st);
+  if (!c->cfg.ar_only) {
+    if (c->warm && c->cfg.G > 0)
+      la_pool_collect_launch(c->pool_cnt, c->pool_ent, c->out.back(), c->win[c->cur], c->wstride, c->R, c->cfg.W,
+                             c->z, c->cfg.G, c->st);
+    int nsz[LA_MAX_N];
+    int deepest = 0;
+    for (int r = 0; r < c->R; ++r) if (c->sizes[r] > 0) deepest = r;
+    const bool warm = is_warm(c);
+    for (int r = 0; r < c->R; ++r) nsz[r] = c->sizes[r];
+    if (!warm) {
+      for (int r = 0; r <= deepest; ++r) nsz[r] = c->sizes[r] - 1;
+      nsz[deepest + 1] = c->sizes[deepest] - (deepest >= 1 ? 1 : 0);
+    }
+    la_window_next_launch(c->win[c->cur], c->win[c->cur ^ 1], c->wstride, c->R, c->sizes, nsz, deepest, warm ? 1 : 0,
+                          c->z, L.n_inp, c->st);
+    HIPCHK(c, hipGetLastError());
+    c->cur ^= 1;
+    for (int r = 0; r < c->R; ++r) c->sizes[r] = nsz[r];
+  }
+  HIPCHK(c, hipGetLastError());
+  c->kv_len += 1 + a->h;
+  int added = 0;
+  for (int k = 0; k < a->n_emit && (int)c->out.size() < c->cfg.max_new; ++k, ++added) c->out.push_back(a->emitted[k]);
+  c->round_id = rid;
+  c->pending = false;
+  c->verified = false;
+  c->stats.rounds += 1;
+  c->stats.tokens += added;
+  c->stats.candidates += L.C;
+  c->stats.accepted += a->h;
+  if (a->n_emit < LA_MAX_EMIT) c->stats.hist[a->n_emit] += 1;
+  return LA_OK;
+}
+
+extern "C" int la_step(la_ctx* c, int32_t* out_tokens, int32_t cap, int32_t* n_out) {
+  if (!c || !n_out) return fail(c, LA_EINVAL, "null argument");
+  *n_out = 0;
+  if ((int)c->out.size() >= c->cfg.max_new) return LA_OK;
+  if (cap < c->cfg.N) return fail(c, LA_EOVERFLOW, "cap %d < N=%d", cap, c->cfg.N);
+  const size_t before = c->out.size();
+  int rc = la_predict(c, nullptr);
+  if (rc) return rc;
+  la_accept a;
+  rc = la_verify(c, nullptr, 0, nullptr, 0, &a, nullptr);
+  if (rc) { c->pending = false; return rc; }
+  rc = la_commit(c, &a);
+  if (rc) { c->pending = false; c->verified = false; return rc; }
+  const size_t n = c->out.size() - before;
+  if (out_tokens)
+    for (size_t i = 0; i < n; ++i) out_tokens[i] = c->out[before + i];
+  *n_out = (int32_t)n;
+  return LA_OK;
+}
+
+extern "C" int la_generate(la_ctx* c, int32_t* out_tokens, int32_t cap, int32_t* n_out) {
+  if (!c || !n_out) return fail(c, LA_EINVAL, "null argument");
+  if (cap < c->cfg.max_new) return fail(c, LA_EOVERFLOW, "cap %d < max_new %d", cap, c->cfg.max_new);
+  int32_t buf[LA_MAX_EMIT];
+  while ((int)c->out.size() < c->cfg.max_new) {
+    int32_t n = 0;
+    int rc = la_step(c, buf, LA_MAX_EMIT, &n);
+    if (rc) return rc;
+  }
+  for (size_t i = 0; i < c->out.size(); ++i) out_tokens[i] = c->out[i];
+  *n_out = (int32_t)c->out.size();
+  return LA_OK;
+}
+
+// ------------------------------------------------------------------ pool, state
+
+extern "C" int la_pool_lookup(la_ctx* c, int32_t key, int32_t* out, int32_t* n) {
+  if (!c || !out || !n) return fail(c, LA_EINVAL, "null argument");
+  if (key < 0 || key >= c->V) return fail(c, LA_EINVAL, "key %d out of range", key);
+  if (c->cfg.G == 0) { *n = 0; return LA_OK; }
+  la_pool_lookup_launch(c->pool_cnt, c->pool_ent, key, c->cfg.G, c->S, c->vcand, c->ncand, c->st);
+  int32_t nc = 0;
+  HIPCHK(c, hipMemcpyAsync(&nc, c->ncand, 4, hipMemcpyDeviceToHost, c->st));
+  HIPCHK(c, hipStreamSynchronize(c->st));
+  if (nc > 0) {
+    HIPCHK(c, hipMemcpyAsync(out, c->vcand, (size_t)nc * c->S * 4, hipMemcpyDeviceToHost, c->st));
+    HIPCHK(c, hipStreamSynchronize(c->st));
+  }
+  *n = nc;
+  return LA_OK;
+}
+
+extern "C" int la_pool_insert(la_ctx* c, const int32_t* keys, const int32_t* suffixes, int32_t n) {
+  if (!c || (n > 0 && (!keys || !suffixes))) return fail(c, LA_EINVAL, "null argument");
+  if (n < 0 || n > 64) return fail(c, LA_EINVAL, "n=%d outside [0, 64] per call", n);
+  if (c->pending) return fail(c, LA_ESTATE, "a predicted round is pending");
+  if (c->cfg.G == 0 || n == 0) return LA_OK;
+  for (int i = 0; i < n; ++i) {
+    if (keys[i] < 0 || keys[i] >= c->V) return fail(c, LA_EINVAL, "key %d out of range", i);
+    for (int s = 0; s < c->S; ++s)
+      if (suffixes[i * c->S + s] < 0 || suffixes[i * c->S + s] >= c->V) return fail(c, LA_EINVAL, "suffix token out of range");
+  }
+  // keys then suffixes through the verification candidate scratch
+  std::vector<int32_t> buf((size_t)n * (1 + c->S));
+  for (int i = 0; i < n; ++i) buf[i] = keys[i];
+  memcpy(buf.data() + n, suffixes, (size_t)n * c->S * 4);
+  HIPCHK(c, hipMemcpyAsync(c->vcand, buf.data(), buf.size() * 4, hipMemcpyHostToDevice, c->st));
+  la_pool_upsert_launch(c->pool_cnt, c->pool_ent, c->vcand, c->vcand + n, n, c->cfg.G, c->S, c->st);
+  HIPCHK(c, hipGetLastError());
+  HIPCHK(c, hipStreamSynchronize(c->st));
+  return LA_OK;
+}
+
+extern "C" int la_get_state(la_ctx* c, la_state_t* s, int32_t* window, int32_t* output, int32_t out_cap) {
+  if (!c || !s) return fail(c, LA_EINVAL, "null argument");
+  memset(s, 0, sizeof *s);
+  s->round_id = c->round_id;
+  s->kv_len = c->kv_len;
+  s->n_out = (int32_t)c->out.size();
+  s->R = c->R;
+  for (int r = 0; r < c->R; ++r) s->level_sizes[r] = c->sizes[r];
+  s->warm = is_warm(c) ? 1 : 0;
+  s->win_stride = c->wstride;
+  if (window) {
+    HIPCHK(c, hipMemcpyAsync(window, c->win[c->cur], (size_t)c->R * c->wstride * 4, hipMemcpyDeviceToHost, c->st));
+    HIPCHK(c, hipStreamSynchronize(c->st));
+  }
+  if (output)
+    for (int i = 0; i < (int)c->out.size() && i < out_cap; ++i) output[i] = c->out[i];
+  return LA_OK;
+}
+
+extern "C" int la_stats(const la_ctx* c, la_stats_t* out) {
+  if (!c || !out) return LA_EINVAL;
+  *out = c->stats;
+  return LA_OK;
+}
+
+extern "C" const char* la_last_error(const la_ctx* c) { return c ? c->err.c_str() : g_err.c_str(); }
+
+// ------------------------------------------------------------------ context-free operators
+
+static int desc_layout(const la_rows_desc* d, LaLayout* L) {
+  if (!d || d->R < 1 || d->R > LA_MAX_N || d->S < 1 || d->S > LA_MAX_N || d->C < 0 || d->C > 64)
+    return fail(nullptr, LA_EINVAL, "bad rows descriptor");
+  memset(L, 0, sizeof *L);
+  L->p = d->p; L->R = d->R; L->C = d->C; L->S = d->S;
+  for (int r = 0; r < d->R; ++r) {
+    if (d->sizes[r] < 0 || (r > 0 && d->sizes[r] > 0 && d->sizes[r] > d->win_stride) || d->sizes[0] > d->win_stride)
+      return fail(nullptr, LA_EINVAL, "level %d size %d", r, d->sizes[r]);
+    L->sizes[r] = d->sizes[r];
+    L->starts[r] = r == 0 ? 1 : d->starts[r];
+  }
+  if (la_layout_finish(L)) return fail(nullptr, LA_EINVAL, "inconsistent level layout");
+  if (L->Q > 1024) return fail(nullptr, LA_EINVAL, "too many rows");
+  return LA_OK;
+}
+
+extern "C" int la_rows_query(const la_rows_desc* desc, la_rows_info* info) {
+  LaLayout L;
+  int rc = desc_layout(desc, &L);
+  if (rc) return rc;
+  if (!info) return fail(nullptr, LA_EINVAL, "null info");
+  rows_layout(L, nullptr, nullptr, info);
+  return LA_OK;
+}
+
+extern "C" int la_build_rows(const la_rows_desc* desc, const int32_t* window, const int32_t* cand, int32_t* out,
+                             void* stream, la_rows_info* info) {
+  LaLayout L;
+  int rc = desc_layout(desc, &L);
+  if (rc) return rc;
+  if (!out || !window || (L.C > 0 && !cand) || !info) return fail(nullptr, LA_EINVAL, "null argument");
+  LaRowsDev r;
+  rows_layout(L, out, &r, info);
+  la_build_rows_launch(L, desc->x_t, window, desc->win_stride, cand, r, (hipStream_t)stream);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(nullptr, LA_EDEVICE, "build rows: %s", hipGetErrorString(e));
+  return LA_OK;
+}
+
+extern "C" size_t la_attention_workspace(int32_t Q, int32_t H, int32_t dh, int32_t max_pos) {
+  const size_t spans = (size_t)la_attention_spans(max_pos);
+  return spans * H * Q * ((size_t)dh + 2) * 4 + 512;
+}
+
+extern "C" int la_attention(int32_t dtype, const void* q, const void* k_cache, const void* v_cache, int32_t t_cap,
+                            const void* k_ws, const void* v_ws, int32_t ws_cap, int32_t H, int32_t Hkv, int32_t dh,
+                            const int32_t* rows, const la_rows_info* info, int32_t shared_end, void* out,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k_cache || !v_cache || !rows || !info || !out || !workspace) return fail(nullptr, LA_EINVAL, "null argument");
+  if (dtype != LA_DTYPE_F32 && dtype != LA_DTYPE_BF16) return fail(nullptr, LA_EINVAL, "dtype");
+  if (H < 1 || Hkv < 1 || H % Hkv || shared_end < 1 || shared_end > t_cap) return fail(nullptr, LA_EINVAL, "bad shape");
+  if (info->Q > 1 && (!k_ws || !v_ws || ws_cap < info->Q - 1)) return fail(nullptr, LA_EINVAL, "workspace K/V too small");
+  // positions never exceed shared_end + maxp (a row's path covers its own position)
+  const int max_pos = shared_end + info->maxp;
+  const size_t need = la_attention_workspace(info->Q, H, dh, max_pos);
+  if (workspace_bytes < need) return fail(nullptr, LA_EOVERFLOW, "workspace %zu < %zu bytes", workspace_bytes, need);
+  LaAttnArgs a{};
+  a.q = q; a.kc = k_cache; a.vc = v_cache; a.kw = k_ws ? k_ws : k_cache; a.vw = v_ws ? v_ws : v_cache; a.o = out;
+  const size_t spans = (size_t)la_attention_spans(max_pos);
+  a.part_o = (float*)workspace;
+  a.part_ml = (float*)((char*)workspace + spans * H * info->Q * (size_t)dh * 4);
+  a.pos = rows + info->off_pos; a.branch = rows + info->off_branch; a.path = rows + info->off_path;
+  a.path_len = rows + info->off_path_len;
+  a.Q = info->Q; a.H = H; a.Hkv = Hkv; a.dh = dh; a.T_cap = t_cap; a.ws_cap = ws_cap > 0 ? ws_cap : 1;
+  a.maxp = info->maxp; a.shared_end = shared_end; a.n_spans = (int)spans;
+  a.scale = 1.0f / sqrtf((float)dh);
+  const int rc = la_attention_launch(dtype == LA_DTYPE_BF16 ? LA_DT_BF16 : LA_DT_F32, a, (hipStream_t)stream);
+  if (rc) return fail(nullptr, rc == -2 ? LA_EINVAL : LA_EDEVICE, "attention launch failed");
+  return LA_OK;
+}
+
+extern "C" size_t la_linear_workspace(int32_t dtype, int32_t epilogue, int32_t M, int32_t N, int32_t K) {
+  const int dt = dtype == LA_DTYPE_BF16 ? LA_DT_BF16 : LA_DT_F32;
+  const int sw = epilogue == LA_LINEAR_SWIGLU;
+  const int splits = la_gemm_splits(N, K, dt, sw);
+  return splits > 1 ? (size_t)splits * M * (sw ? 2 * N : N) * 4 : 0;
+}
+
+extern "C" int la_linear(int32_t dtype, int32_t epilogue, const void* X, const void* W, void* Y, const void* R,
+                         int32_t M, int32_t N, int32_t K, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!X || !W || !Y || (epilogue == LA_LINEAR_RESIDUAL && !R)) return fail(nullptr, LA_EINVAL, "null argument");
+  if (dtype != LA_DTYPE_F32 && dtype != LA_DTYPE_BF16) return fail(nullptr, LA_EINVAL, "dtype");
+  if (epilogue < LA_LINEAR_STORE || epilogue > LA_LINEAR_F32) return fail(nullptr, LA_EINVAL, "epilogue");
+  const size_t need = la_linear_workspace(dtype, epilogue, M, N, K);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(nullptr, LA_EOVERFLOW, "workspace %zu < %zu bytes", workspace_bytes, need);
+  const int dt = dtype == LA_DTYPE_BF16 ? LA_DT_BF16 : LA_DT_F32;
+  const int epi = epilogue == LA_LINEAR_STORE ? LA_EPI_STORE : epilogue == LA_LINEAR_RESIDUAL ? LA_EPI_RESID
+                  : epilogue == LA_LINEAR_SWIGLU ? LA_EPI_SWIGLU : LA_EPI_F32;
+  LaGemmArgs a{};
+  a.X = X; a.W = W; a.Y = Y; a.R = R; a.P = (float*)workspace;
+  a.M = M; a.N = N; a.K = K; a.ldx = K; a.ldy = N;
+  a.splits = la_gemm_splits(N, K, dt, epi == LA_EPI_SWIGLU);
+  a.up_off = N;
+  a.pcols = epi == LA_EPI_SWIGLU ? 2 * N : N;
+  const int rc = la_gemm_launch(dt, epi, a, (hipStream_t)stream);
+  if (rc == -2) return fail(nullptr, LA_EINVAL, "unsupported shape M=%d N=%d K=%d", M, N, K);
+  if (rc) return fail(nullptr, LA_EDEVICE, "linear launch failed");
+  return LA_OK;
+}

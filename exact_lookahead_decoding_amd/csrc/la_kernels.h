@@ -1,0 +1,112 @@
+// Internal launch interface between the host orchestrator and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+enum { LA_DT_F32 = 0, LA_DT_BF16 = 1 };
+enum { LA_EPI_STORE = 0, LA_EPI_RESID = 1, LA_EPI_SWIGLU = 2, LA_EPI_F32 = 3, LA_EPI_PARTIAL = 4 };
+
+struct LaGemmArgs {
+  const void* X;      // [M][ldx] storage dtype
+  const void* W;      // [rows][K] storage dtype (nn.Linear layout)
+  void* Y;            // output [M][ldy]
+  const void* R;      // residual [M][ldy] (RESID), may alias Y
+  float* P;           // split partials [splits][M][pcols]
+  int M, N, K;        // N = output columns (SWIGLU: F)
+  int ldx, ldy;
+  int splits, nchunks;
+  int up_off;         // SWIGLU: first row of the "up" half of W (= F)
+  int pcols;          // partial row length (SWIGLU: 2F, else N)
+  int swiglu_partial; // set by the launcher
+};
+int la_gemm_splits(int N, int K, int dtype, int swiglu);
+int la_gemm_launch(int dtype, int epi, LaGemmArgs a, hipStream_t st);
+
+// row metadata produced by the packed-row builder (device int32 arrays)
+struct LaRowsDev {
+  int32_t* tok;        // [Q] input token of each packed row
+  int32_t* pos;        // [Q] logical position
+  int32_t* role;       // [Q] 0 ordinary, 1 lookahead, 2 verify
+  int32_t* level;      // [Q] trajectory level (-1 verify)
+  int32_t* col;        // [Q] window column (-1 verify)
+  int32_t* cand;       // [Q] candidate (-1 otherwise)
+  int32_t* off;        // [Q] suffix offset (-1 otherwise)
+  int32_t* branch;     // [Q] branch id
+  int32_t* path;       // [NB][maxp] workspace row of logical position shared_end + k
+  int32_t* path_len;   // [NB]
+  int32_t* logit_rows; // [n_logit]: out, inp (column order), guess ((c, s) order)
+  uint32_t* mask;      // [Q][mask_words] visibility bits among current rows
+};
+
+struct LaLayout {        // host-side description of one round's rows
+  int p;                 // logical position of the ordinary row
+  int R;                 // number of trajectory levels
+  int sizes[16];         // cells per level (0 = not materialised)
+  int starts[16];        // first column of each level (level 0 starts at 1)
+  int C, S;              // candidates, suffix length
+  int Q, NB, maxp, n_logit, n_inp, n_cols, mask_words;
+};
+int la_layout_finish(LaLayout* L);   // fills Q, NB, ... ; returns 0 or -1 if inconsistent
+void la_build_rows_launch(const LaLayout& L, int x_t, const int32_t* win, int win_stride,
+                          const int32_t* cands, LaRowsDev rows, hipStream_t st);
+
+// attention
+struct LaAttnArgs {
+  const void* q;        // [Q][H][dh]
+  const void* kc;       // cache K [Hkv][T_cap][dh] (one layer)
+  const void* vc;
+  const void* kw;       // workspace K [Hkv][ws_cap][dh] (one layer), packed row k -> ws row k-1
+  const void* vw;
+  void* o;              // [Q][H][dh]
+  float* part_o;        // [n_spans][H][Q][dh]
+  float* part_ml;       // [n_spans][H][Q][2]
+  const int32_t* pos;
+  const int32_t* branch;
+  const int32_t* path;
+  const int32_t* path_len;
+  int Q, H, Hkv, dh, T_cap, ws_cap, maxp;
+  int shared_end;       // keys [0, shared_end) come from the cache, later ones from the row's path
+  int n_spans;
+  float scale;
+};
+int la_attention_launch(int dtype, const LaAttnArgs& a, hipStream_t st);
+int la_attention_spans(int max_pos);
+
+// model pieces
+void la_embed_launch(int dtype, const void* E, const int32_t* tok, void* x, int M, int d, hipStream_t st);
+void la_rmsnorm_launch(int dtype, const void* x, const void* w, void* y, const int32_t* rows, int M, int d,
+                       float eps, hipStream_t st);
+void la_rope_table_launch(float2* tab, int T, int dh, float theta, hipStream_t st);
+void la_qkv_post_launch(int dtype, const void* qkv, const float2* rope, const int32_t* pos, int M, int H, int Hkv,
+                        int dh, void* q, void* kc, void* vc, int T_cap, int cache_row0, int n_direct, void* kw,
+                        void* vw, int ws_cap, hipStream_t st);
+
+// verification
+void la_argmax_launch(const float* logits, int rows, int V, int32_t* out, hipStream_t st);
+struct LaAcceptDev {     // device image of one verification result
+  int32_t h, winner, n_emit, pad;
+  int32_t emitted[32];
+};
+void la_greedy_accept_launch(const int32_t* amax, int n_inp, const int32_t* cand, int C, int S,
+                             LaAcceptDev* acc, int32_t* z, hipStream_t st);
+void la_sample_accept_launch(const float* logits, int V, int n_inp, const int32_t* amax, const int32_t* cand,
+                             int C, int S, double T, uint64_t seed, int round_id, double* scratch,
+                             LaAcceptDev* acc, int32_t* z, hipStream_t st);
+void la_sample_row_launch(const float* logits, int V, double T, uint64_t seed, int round_id, const int32_t* amax,
+                          double* scratch, int32_t* out, hipStream_t st);
+
+// pool
+void la_pool_clear_launch(int32_t* cnt, int V, hipStream_t st);
+void la_pool_lookup_launch(const int32_t* cnt, const int32_t* ent, int key, int G, int S, int32_t* out,
+                           int32_t* n, hipStream_t st);
+void la_pool_upsert_launch(int32_t* cnt, int32_t* ent, const int32_t* keys, const int32_t* sufs, int n, int G,
+                           int S, hipStream_t st);
+void la_pool_collect_launch(int32_t* cnt, int32_t* ent, int x_t, const int32_t* win, int win_stride, int R,
+                            int W, const int32_t* z, int G, hipStream_t st);
+
+// window and commit
+void la_window_next_launch(const int32_t* win, int32_t* out, int stride, int R, const int* sizes_old,
+                           const int* sizes_new, int deepest, int warm, const int32_t* z, int nz, hipStream_t st);
+void la_kv_commit_launch(int dtype, void* kc, void* vc, const void* kw, const void* vw, int L, int Hkv, int dh,
+                         int T_cap, int ws_cap, int dst_row0, int src_row0, int h, hipStream_t st);
+void la_fill_i32_launch(int32_t* p, int n, int v, hipStream_t st);

@@ -1,0 +1,136 @@
+// Token-wise pieces of the target forward: embedding gather, RMSNorm, RoPE
+// at each row's logical position, and placement of each row's K/V.
+//
+// "M7.3 - Lookahead Decoding", 0x04: every packed row carries a logical
+// position (positions are not packed indices); 0x07: the ordinary row's K/V
+// is the start of the new frontier while every other packed row's K/V is
+// temporary workspace until publication.
+//
+// Every kernel here computes each row independently with a fixed reduction
+// order, so a row's values do not depend on which other rows share the call.
+#include "la_common.h"
+#include "la_kernels.h"
+
+template <typename T>
+__global__ void __launch_bounds__(256) embed_kernel(const T* E, const int32_t* tok, T* x, int d) {
+  const int m = blockIdx.x;
+  const T* src = E + (size_t)tok[m] * d;
+  T* dst = x + (size_t)m * d;
+  for (int i = threadIdx.x; i < d; i += 256) dst[i] = src[i];
+}
+
+void la_embed_launch(int dtype, const void* E, const int32_t* tok, void* x, int M, int d, hipStream_t st) {
+  if (M <= 0) return;
+  if (dtype == LA_DT_BF16)
+    hipLaunchKernelGGL(embed_kernel<bf16_t>, dim3(M), dim3(256), 0, st, (const bf16_t*)E, tok, (bf16_t*)x, d);
+  else
+    hipLaunchKernelGGL(embed_kernel<float>, dim3(M), dim3(256), 0, st, (const float*)E, tok, (float*)x, d);
+}
+
+// y[m] = T(x[src] * rs * w),  rs = 1/sqrt(mean(x^2) + eps), src = rows ? rows[m] : m
+template <typename T>
+__global__ void __launch_bounds__(256) rmsnorm_kernel(const T* x, const T* w, T* y, const int32_t* rows, int d,
+                                                      float eps) {
+  __shared__ float red[4];
+  const int m = blockIdx.x;
+  const int src = rows ? rows[m] : m;
+  const T* xr = x + (size_t)src * d;
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < d; i += 256) {
+    const float v = ld<T>(xr + i);
+    ss += v * v;
+  }
+  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+  const float rs = 1.0f / sqrtf(tot / (float)d + eps);
+  T* yr = y + (size_t)m * d;
+  for (int i = threadIdx.x; i < d; i += 256) st<T>(yr + i, ld<T>(xr + i) * rs * ld<T>(w + i));
+}
+
+void la_rmsnorm_launch(int dtype, const void* x, const void* w, void* y, const int32_t* rows, int M, int d,
+                       float eps, hipStream_t st) {
+  if (M <= 0) return;
+  if (dtype == LA_DT_BF16)
+    hipLaunchKernelGGL(rmsnorm_kernel<bf16_t>, dim3(M), dim3(256), 0, st, (const bf16_t*)x, (const bf16_t*)w,
+                       (bf16_t*)y, rows, d, eps);
+  else
+    hipLaunchKernelGGL(rmsnorm_kernel<float>, dim3(M), dim3(256), 0, st, (const float*)x, (const float*)w,
+                       (float*)y, rows, d, eps);
+}
+
+// cos/sin of t * theta^(-2i/dh), evaluated in fp64 and stored as fp32
+__global__ void rope_table_kernel(float2* tab, int T, int half, int dh, double theta) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= T * half) return;
+  const int t = idx / half, i = idx % half;
+  const double inv = pow(theta, -2.0 * (double)i / (double)dh);
+  const double ang = (double)t * inv;
+  tab[idx] = make_float2((float)cos(ang), (float)sin(ang));
+}
+
+void la_rope_table_launch(float2* tab, int T, int dh, float theta, hipStream_t st) {
+  const int half = dh / 2;
+  const int n = T * half;
+  hipLaunchKernelGGL(rope_table_kernel, dim3((n + 255) / 256), dim3(256), 0, st, tab, T, half, dh, (double)theta);
+}
+
+// qkv [M][(H + 2 Hkv) dh] -> q [M][H][dh] with RoPE; k (RoPE) and v to the
+// cache for the first n_direct rows (cache row cache_row0 + m), to the
+// workspace (row m - n_direct) for the others.  One block per (row, head).
+template <typename T>
+__global__ void __launch_bounds__(64) qkv_post_kernel(const T* qkv, const float2* rope, const int32_t* pos, int H,
+                                                      int Hkv, int dh, T* q, T* kc, T* vc, int T_cap, int cache_row0,
+                                                      int n_direct, T* kw, T* vw, int ws_cap) {
+  const int m = blockIdx.x;
+  const int hh = blockIdx.y;                     // 0..H-1 q, H..H+Hkv-1 k, then v
+  const int half = dh / 2;
+  const T* src = qkv + (size_t)m * (H + 2 * Hkv) * dh + (size_t)hh * dh;
+  const int p = pos[m];
+  T* dst;
+  if (hh < H) {
+    dst = q + ((size_t)m * H + hh) * dh;
+  } else {
+    const int g = hh < H + Hkv ? hh - H : hh - H - Hkv;
+    const bool isk = hh < H + Hkv;
+    if (m < n_direct) dst = (isk ? kc : vc) + ((size_t)g * T_cap + cache_row0 + m) * dh;
+    else dst = (isk ? kw : vw) + ((size_t)g * ws_cap + (m - n_direct)) * dh;
+  }
+  const bool rot = hh < H + Hkv;
+  for (int i = threadIdx.x; i < half; i += 64) {
+    const float x1 = ld<T>(src + i), x2 = ld<T>(src + i + half);
+    if (rot) {
+      const float2 cs = rope[(size_t)p * half + i];
+      st<T>(dst + i, x1 * cs.x - x2 * cs.y);
+      st<T>(dst + i + half, x2 * cs.x + x1 * cs.y);
+    } else {
+      st<T>(dst + i, x1);
+      st<T>(dst + i + half, x2);
+    }
+  }
+}
+
+void la_qkv_post_launch(int dtype, const void* qkv, const float2* rope, const int32_t* pos, int M, int H, int Hkv,
+                        int dh, void* q, void* kc, void* vc, int T_cap, int cache_row0, int n_direct, void* kw,
+                        void* vw, int ws_cap, hipStream_t st) {
+  if (M <= 0) return;
+  dim3 grid(M, H + 2 * Hkv);
+  if (dtype == LA_DT_BF16)
+    hipLaunchKernelGGL(qkv_post_kernel<bf16_t>, grid, dim3(64), 0, st, (const bf16_t*)qkv, rope, pos, H, Hkv, dh,
+                       (bf16_t*)q, (bf16_t*)kc, (bf16_t*)vc, T_cap, cache_row0, n_direct, (bf16_t*)kw, (bf16_t*)vw,
+                       ws_cap);
+  else
+    hipLaunchKernelGGL(qkv_post_kernel<float>, grid, dim3(64), 0, st, (const float*)qkv, rope, pos, H, Hkv, dh,
+                       (float*)q, (float*)kc, (float*)vc, T_cap, cache_row0, n_direct, (float*)kw, (float*)vw,
+                       ws_cap);
+}
+
+__global__ void fill_i32_kernel(int32_t* p, int n, int v) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+void la_fill_i32_launch(int32_t* p, int n, int v, hipStream_t st) {
+  if (n <= 0) return;
+  hipLaunchKernelGGL(fill_i32_kernel, dim3((n + 255) / 256), dim3(256), 0, st, p, n, v);
+}

@@ -1,0 +1,169 @@
+// Packed-row builder: one immutable row manifest per round.
+//
+// "M7.3 - Lookahead Decoding", 0x04 and 0x04A: one ordinary row, the
+// lookahead trajectory rows and C candidate suffixes of S rows are packed
+// into one call; a shared row record (role, level, column, candidate,
+// offset, logical position, requested logit) feeds tokens, positions, the
+// branch mask and the output slices; the visibility sets are
+//   Vis(b_j) = {b_k : k <= j},  Vis(u_(r,j)) = {b_k : k <= j} U {u_(q,j) : q <= r},
+//   Vis(v_(c,s)) = {b_0} U {v_(c,q) : q <= s},
+// plus the committed prefix for everyone.  Logical positions:
+// pos(b_j) = p + j, pos(u_(r,j)) = p + j + r, pos(v_(c,s)) = p + 1 + s.
+//
+// Physical order here is branch-major (the pages' dense path is level-major;
+// their specialised attention path uses its own permutation as well):
+// column j contributes [b_j, u_(1,j), ..., u_(d_j,j)] (b_0 is the ordinary
+// row, packed row 0), then candidate c contributes [v_(c,0..S-1)].
+//
+// Under these sets a row at position t sees exactly one row at each
+// logical position p .. t, so the mask is stored as a *path* per branch:
+// path[b][k] is the workspace row holding logical position p + 1 + k on
+// branch b (column j: b_1..b_j then u_(1..d_j, j); candidate c:
+// v_(c,0..S-1)).  Row i sees row k iff k is the ordinary row, or
+// pos_k <= pos_i and path[branch_i][pos_k - p - 1] is k's workspace row.
+// The attention kernel gathers keys through the path; the bit mask is the
+// same relation written out (for auditing against the dense definition).
+#include "la_common.h"
+#include "la_kernels.h"
+
+static int level_at(const LaLayout* L, int r, int j) {
+  return L->sizes[r] > 0 && j >= L->starts[r] && j < L->starts[r] + L->sizes[r];
+}
+
+int la_layout_finish(LaLayout* L) {
+  if (L->R < 1 || L->R > 16 || L->sizes[0] < 0 || L->S < 1 || L->C < 0) return -1;
+  L->starts[0] = 1;
+  const int ncols = L->sizes[0] + 1;
+  L->n_cols = ncols;
+  int Q = 0, maxp = L->S;
+  for (int j = 0; j < ncols; ++j) {
+    int depth = 0;
+    for (int r = 1; r < L->R; ++r) {
+      if (level_at(L, r, j)) {
+        if (depth != r - 1) return -1;            // levels at a column must be nested 1..d
+        depth = r;
+      }
+    }
+    Q += 1 + depth;
+    if (j + depth > maxp) maxp = j + depth;
+  }
+  for (int r = 1; r < L->R; ++r)
+    if (L->sizes[r] > 0 && (L->starts[r] < 0 || L->starts[r] + L->sizes[r] > ncols)) return -1;
+  Q += L->C * L->S;
+  L->Q = Q;
+  L->NB = ncols + L->C;
+  L->maxp = maxp;
+  int deepest = 0;
+  for (int r = 0; r < L->R; ++r)
+    if (L->sizes[r] > 0) deepest = r;
+  L->n_inp = L->sizes[deepest];
+  L->n_logit = 1 + L->n_inp + L->C * L->S;
+  L->mask_words = (Q + 31) / 32;
+  return 0;
+}
+
+__device__ static int d_level_at(const LaLayout& L, int r, int j) {
+  return L.sizes[r] > 0 && j >= L.starts[r] && j < L.starts[r] + L.sizes[r];
+}
+__device__ static int d_depth(const LaLayout& L, int j) {
+  int d = 0;
+  for (int r = 1; r < L.R; ++r)
+    if (d_level_at(L, r, j)) d = r;
+  return d;
+}
+__device__ static int d_col_start(const LaLayout& L, int j) {
+  int s = 0;
+  for (int k = 0; k < j; ++k) s += 1 + d_depth(L, k);
+  return s;
+}
+
+__global__ void __launch_bounds__(256) build_rows_kernel(LaLayout L, int x_t, const int32_t* win, int win_stride,
+                                                         const int32_t* cands, LaRowsDev o) {
+  const int t = threadIdx.x;
+  const int p = L.p;
+  const int cand_start = L.Q - L.C * L.S;
+  // columns
+  for (int j = t; j < L.n_cols; j += blockDim.x) {
+    const int cs = d_col_start(L, j);
+    const int depth = d_depth(L, j);
+    // b_j
+    o.tok[cs] = j == 0 ? x_t : win[j - 1];
+    o.pos[cs] = p + j;
+    o.role[cs] = j == 0 ? 0 : 1;
+    o.level[cs] = 0;
+    o.col[cs] = j;
+    o.cand[cs] = -1;
+    o.off[cs] = -1;
+    o.branch[cs] = j;
+    for (int r = 1; r <= depth; ++r) {
+      const int row = cs + r;
+      o.tok[row] = win[r * win_stride + (j - L.starts[r])];
+      o.pos[row] = p + j + r;
+      o.role[row] = 1;
+      o.level[row] = r;
+      o.col[row] = j;
+      o.cand[row] = -1;
+      o.off[row] = -1;
+      o.branch[row] = j;
+    }
+    int32_t* pth = o.path + (size_t)j * L.maxp;
+    for (int k = 0; k < j; ++k) pth[k] = d_col_start(L, k + 1) - 1;
+    for (int r = 1; r <= depth; ++r) pth[j + r - 1] = cs + r - 1;
+    o.path_len[j] = j + depth;
+  }
+  // candidates
+  for (int c = t; c < L.C; c += blockDim.x) {
+    const int b = L.n_cols + c;
+    for (int s = 0; s < L.S; ++s) {
+      const int row = cand_start + c * L.S + s;
+      o.tok[row] = cands[c * L.S + s];
+      o.pos[row] = p + 1 + s;
+      o.role[row] = 2;
+      o.level[row] = -1;
+      o.col[row] = -1;
+      o.cand[row] = c;
+      o.off[row] = s;
+      o.branch[row] = b;
+      o.path[(size_t)b * L.maxp + s] = row - 1;
+    }
+    o.path_len[b] = L.S;
+  }
+  // logit rows: out, inp (deepest level, column order), guess ((c, s) order)
+  int deepest = 0;
+  for (int r = 0; r < L.R; ++r)
+    if (L.sizes[r] > 0) deepest = r;
+  if (t == 0) o.logit_rows[0] = 0;
+  for (int i = t; i < L.n_inp; i += blockDim.x) {
+    const int j = deepest == 0 ? 1 + i : L.starts[deepest] + i;
+    o.logit_rows[1 + i] = d_col_start(L, j) + deepest;
+  }
+  for (int i = t; i < L.C * L.S; i += blockDim.x) o.logit_rows[1 + L.n_inp + i] = cand_start + i;
+  __syncthreads();
+  // compact visibility mask, derived from the paths
+  const int nw = L.mask_words;
+  for (int idx = t; idx < L.Q * nw; idx += blockDim.x) {
+    const int i = idx / nw, w = idx % nw;
+    const int pi = o.pos[i];
+    const int32_t* pth = o.path + (size_t)o.branch[i] * L.maxp;
+    const int plen = o.path_len[o.branch[i]];
+    uint32_t bits = 0;
+    for (int b = 0; b < 32; ++b) {
+      const int k = w * 32 + b;
+      if (k >= L.Q) break;
+      bool vis;
+      if (k == 0) vis = true;
+      else {
+        const int pk = o.pos[k];
+        const int e = pk - p - 1;
+        vis = pk <= pi && e >= 0 && e < plen && pth[e] == k - 1;
+      }
+      if (vis) bits |= 1u << b;
+    }
+    o.mask[(size_t)i * nw + w] = bits;
+  }
+}
+
+void la_build_rows_launch(const LaLayout& L, int x_t, const int32_t* win, int win_stride, const int32_t* cands,
+                          LaRowsDev rows, hipStream_t st) {
+  hipLaunchKernelGGL(build_rows_kernel, dim3(1), dim3(256), 0, st, L, x_t, win, win_stride, cands, rows);
+}

@@ -1,0 +1,281 @@
+// Verify-and-accept: greedy survivor matching and exact one-hot sampling.
+//
+// "M7.3 - Lookahead Decoding", 0x05A: the first emitted token is the
+// ordinary row's argmax; candidate c's hit length is the longest a with
+// g_(1..a) = z^(c)_(1..a), z^(c) = (argmax out, argmax guess^(c)_1, ...);
+// the accepted length h is the maximum hit, and every candidate reaching it
+// exposes the same conditionals, so the lowest-index one is committed.  A
+// full match emits S + 1 tokens.  Ties in argmax go to the lowest token id.
+//
+// 0x05B: at each offset the distinct tokens offered by the surviving
+// candidates are tested in candidate order as point masses -- token c is
+// accepted with probability p(c) / (1 - sum p(rejected)); a rejection
+// removes c's mass; acceptance filters the survivors; when every offered
+// token is rejected the output is drawn from the residual.  The arithmetic
+// is fixed IEEE fp64 so that the decisions are reproducible:
+//   e_v = expneg((double(l_v) - double(l_max)) / T)  (Cody-Waite reduction
+//   with a two-part ln2, degree-13 Taylor polynomial evaluated inner-first,
+//   ldexp), sums blocked by 256 ids in id order, acceptance test
+//   u * remaining < e_c, residual inverse-CDF over blocked cumulative sums.
+// Randomness: Philox4x32-10 (Salmon et al., SC'11) keyed by the seed,
+// counter (round, offset, draw, 0), u = ((x0>>5)*2^26 + (x1>>6)) * 2^-53.
+#include "la_common.h"
+#include "la_kernels.h"
+
+// ---------------------------------------------------------------- argmax
+__global__ void __launch_bounds__(256) argmax_kernel(const float* logits, int V, int32_t* out) {
+  __shared__ float bv[256];
+  __shared__ int bi[256];
+  const float* x = logits + (size_t)blockIdx.x * V;
+  float best = -__builtin_inff();
+  int idx = 0x7fffffff;
+  for (int i = threadIdx.x; i < V; i += 256) {
+    const float v = x[i];
+    if (v > best) { best = v; idx = i; }          // strided scan keeps the lowest index on ties
+  }
+  bv[threadIdx.x] = best;
+  bi[threadIdx.x] = idx;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (threadIdx.x < s) {
+      const float v2 = bv[threadIdx.x + s];
+      const int i2 = bi[threadIdx.x + s];
+      if (v2 > bv[threadIdx.x] || (v2 == bv[threadIdx.x] && i2 < bi[threadIdx.x])) {
+        bv[threadIdx.x] = v2;
+        bi[threadIdx.x] = i2;
+      }
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) out[blockIdx.x] = bi[0] == 0x7fffffff ? 0 : bi[0];
+}
+
+void la_argmax_launch(const float* logits, int rows, int V, int32_t* out, hipStream_t st) {
+  if (rows <= 0) return;
+  hipLaunchKernelGGL(argmax_kernel, dim3(rows), dim3(256), 0, st, logits, V, out);
+}
+
+// ---------------------------------------------------------------- greedy
+__global__ void greedy_accept_kernel(const int32_t* amax, int n_inp, const int32_t* cand, int C, int S,
+                                     LaAcceptDev* acc, int32_t* z) {
+  __shared__ int hits[64];
+  const int t = threadIdx.x;
+  const int gbase = 1 + n_inp;
+  for (int c = t; c < 64; c += blockDim.x) {
+    int a = 0;
+    if (c < C) {
+      while (a < S) {
+        const int za = a == 0 ? amax[0] : amax[gbase + c * S + a - 1];
+        if (cand[c * S + a] != za) break;
+        ++a;
+      }
+    }
+    hits[c] = c < C ? a : -1;
+  }
+  for (int j = t; j < n_inp; j += blockDim.x) z[j] = amax[1 + j];
+  __syncthreads();
+  if (t == 0) {
+    int h = 0, w = -1;
+    for (int c = 0; c < C; ++c)
+      if (hits[c] > h) { h = hits[c]; w = c; }
+    acc->h = h;
+    acc->winner = h > 0 ? w : -1;
+    acc->n_emit = h + 1;
+    acc->emitted[0] = amax[0];
+    for (int k = 1; k <= h; ++k) acc->emitted[k] = amax[gbase + w * S + k - 1];
+  }
+}
+
+void la_greedy_accept_launch(const int32_t* amax, int n_inp, const int32_t* cand, int C, int S, LaAcceptDev* acc,
+                             int32_t* z, hipStream_t st) {
+  hipLaunchKernelGGL(greedy_accept_kernel, dim3(1), dim3(64), 0, st, amax, n_inp, cand, C, S, acc, z);
+}
+
+// ---------------------------------------------------------------- sampling
+__device__ __forceinline__ void philox4x32_10(uint32_t c[4], uint32_t k0, uint32_t k1) {
+  for (int r = 0; r < 10; ++r) {
+    if (r) { k0 += 0x9E3779B9u; k1 += 0xBB67AE85u; }
+    const uint32_t lo0 = 0xD2511F53u * c[0], hi0 = __umulhi(0xD2511F53u, c[0]);
+    const uint32_t lo1 = 0xCD9E8D57u * c[2], hi1 = __umulhi(0xCD9E8D57u, c[2]);
+    const uint32_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+    c[0] = n0; c[1] = lo1; c[2] = n2; c[3] = lo0;
+  }
+}
+
+__device__ double la_uniform(uint64_t seed, uint32_t round, uint32_t offset, uint32_t draw) {
+  uint32_t c[4] = {round, offset, draw, 0u};
+  philox4x32_10(c, (uint32_t)seed, (uint32_t)(seed >> 32));
+  return ((double)(c[0] >> 5) * 67108864.0 + (double)(c[1] >> 6)) * (1.0 / 9007199254740992.0);
+}
+
+#pragma clang fp contract(off)
+__device__ double la_expneg(double a) {
+  const double LN2_HI = 0x1.62e42fee00000p-1;
+  const double LN2_LO = 0x1.a39ef35793c76p-33;
+  const double INV_LN2 = 0x1.71547652b82fep+0;
+  if (a < -745.0) return 0.0;
+  const double k = __builtin_rint(a * INV_LN2);
+  const double r = (a - k * LN2_HI) - k * LN2_LO;
+  double p = 1.0;
+  for (int n = 13; n >= 1; --n) p = 1.0 + (r / (double)n) * p;
+  return ldexp(p, (int)k);
+}
+
+#define SBLK 256
+#define MAXBLK 256
+
+// masses of one row into e[], block sums into bs[]; returns through shared memory
+__device__ void row_masses(const float* x, int V, double T, double* e, double* bs, float* red) {
+  float mx = -__builtin_inff();
+  for (int i = threadIdx.x; i < V; i += blockDim.x) mx = fmaxf(mx, x[i]);
+  red[threadIdx.x] = mx;
+  __syncthreads();
+  for (int s = blockDim.x / 2; s > 0; s >>= 1) {
+    if (threadIdx.x < s) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + s]);
+    __syncthreads();
+  }
+  const double lmax = (double)red[0];
+  const int nb = (V + SBLK - 1) / SBLK;
+  for (int b = threadIdx.x; b < nb; b += blockDim.x) {
+    double s = 0.0;
+    const int end = min(V, (b + 1) * SBLK);
+    for (int i = b * SBLK; i < end; ++i) {
+      const double ev = la_expneg(((double)x[i] - lmax) / T);
+      e[i] = ev;
+      s = s + ev;
+    }
+    bs[b] = s;
+  }
+  __syncthreads();
+}
+
+// single-thread residual draw (tokens in rej[] already excluded from e/bs)
+__device__ int residual_draw(const double* e, const double* bs, int V, double u, int amax_tok) {
+  const int nb = (V + SBLK - 1) / SBLK;
+  double R = 0.0;
+  for (int b = 0; b < nb; ++b) R = R + bs[b];
+  if (!(R > 0.0)) return amax_tok;
+  const double target = u * R;
+  double acc = 0.0;
+  for (int b = 0; b < nb; ++b) {
+    if (acc + bs[b] > target) {
+      double local = 0.0;
+      const int end = min(V, (b + 1) * SBLK);
+      for (int i = b * SBLK; i < end; ++i) {
+        local = local + e[i];
+        if (acc + local > target) return i;
+      }
+    }
+    acc = acc + bs[b];
+  }
+  for (int i = V - 1; i >= 0; --i)
+    if (e[i] > 0.0) return i;
+  return amax_tok;
+}
+
+// zero the masses of rejected tokens and recompute their block sums in id order
+__device__ void exclude(double* e, double* bs, int V, const int* rej, int nrej) {
+  for (int k = 0; k < nrej; ++k) e[rej[k]] = 0.0;
+  for (int k = 0; k < nrej; ++k) {
+    const int b = rej[k] / SBLK;
+    double s = 0.0;
+    const int end = min(V, (b + 1) * SBLK);
+    for (int i = b * SBLK; i < end; ++i) s = s + e[i];
+    bs[b] = s;
+  }
+}
+
+__global__ void __launch_bounds__(256) sample_accept_kernel(const float* logits, int V, int n_inp,
+                                                            const int32_t* amax, const int32_t* cand, int C, int S,
+                                                            double T, uint64_t seed, int round_id, double* e,
+                                                            LaAcceptDev* acc, int32_t* z) {
+  __shared__ double bs[MAXBLK];
+  __shared__ float red[256];
+  __shared__ int surv[64];
+  __shared__ int nsurv;
+  __shared__ int done, out_tok, accepted;
+  __shared__ int rej[64];
+  const int gbase = 1 + n_inp;
+  for (int j = threadIdx.x; j < n_inp; j += blockDim.x) z[j] = amax[1 + j];
+  if (threadIdx.x == 0) {
+    nsurv = C;
+    for (int c = 0; c < C; ++c) surv[c] = c;
+    done = 0;
+  }
+  __syncthreads();
+  int n_emit = 0;
+  for (int a = 0; a <= S; ++a) {
+    const int row = a == 0 ? 0 : gbase + surv[0] * S + a - 1;
+    row_masses(logits + (size_t)row * V, V, T, e, bs, red);
+    if (threadIdx.x == 0) {
+      const int nb = (V + SBLK - 1) / SBLK;
+      double Z = 0.0;
+      for (int b = 0; b < nb; ++b) Z = Z + bs[b];
+      double remaining = Z;
+      int nrej = 0;
+      accepted = -1;
+      if (a < S) {
+        int k = 0;
+        for (int si = 0; si < nsurv && accepted < 0; ++si) {
+          const int tok = cand[surv[si] * S + a];
+          bool seen = false;
+          for (int q = 0; q < nrej; ++q) seen |= rej[q] == tok;
+          if (seen) continue;
+          const double u = la_uniform(seed, (uint32_t)round_id, (uint32_t)a, (uint32_t)k);
+          ++k;
+          if (u * remaining < e[tok]) {
+            accepted = tok;
+          } else {
+            remaining = remaining - e[tok];
+            rej[nrej++] = tok;
+          }
+        }
+      }
+      if (accepted >= 0) {
+        acc->emitted[a] = accepted;
+        int ns = 0;
+        for (int si = 0; si < nsurv; ++si)
+          if (cand[surv[si] * S + a] == accepted) surv[ns++] = surv[si];
+        nsurv = ns;
+      } else {
+        exclude(e, bs, V, rej, nrej);
+        const double u = la_uniform(seed, (uint32_t)round_id, (uint32_t)a, 1024u);
+        acc->emitted[a] = residual_draw(e, bs, V, u, amax[row]);
+        done = 1;
+      }
+    }
+    __syncthreads();
+    n_emit = a + 1;
+    if (done) break;
+  }
+  if (threadIdx.x == 0) {
+    const int h = n_emit - 1;
+    acc->h = h;
+    acc->n_emit = n_emit;
+    acc->winner = h > 0 ? surv[0] : -1;
+  }
+}
+
+void la_sample_accept_launch(const float* logits, int V, int n_inp, const int32_t* amax, const int32_t* cand,
+                               int C, int S, double T, uint64_t seed, int round_id, double* scratch,
+                               LaAcceptDev* acc, int32_t* z, hipStream_t st) {
+  hipLaunchKernelGGL(sample_accept_kernel, dim3(1), dim3(256), 0, st, logits, V, n_inp, amax, cand, C, S, T, seed,
+                     round_id, scratch, acc, z);
+}
+
+// plain target sample of row 0 (first token after prefill; autoregressive sampling)
+__global__ void __launch_bounds__(256) sample_row_kernel(const float* logits, int V, double T, uint64_t seed,
+                                                         int round_id, const int32_t* amax, double* e, int32_t* out) {
+  __shared__ double bs[MAXBLK];
+  __shared__ float red[256];
+  row_masses(logits, V, T, e, bs, red);
+  if (threadIdx.x == 0) {
+    const double u = la_uniform(seed, (uint32_t)round_id, 0u, 1024u);
+    out[0] = residual_draw(e, bs, V, u, amax[0]);
+  }
+}
+
+void la_sample_row_launch(const float* logits, int V, double T, uint64_t seed, int round_id, const int32_t* amax,
+                          double* scratch, int32_t* out, hipStream_t st) {
+  hipLaunchKernelGGL(sample_row_kernel, dim3(1), dim3(256), 0, st, logits, V, T, seed, round_id, amax, scratch, out);
+}

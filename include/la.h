@@ -1,0 +1,293 @@
+/*
+ * la.h -- C ABI of the MI355X lookahead decoding library (liblookahead.so).
+ *
+ * Exact Lookahead decoding as described on "M7.3 - Lookahead Decoding:
+ * Jacobi Iterations, N-Gram Pools, and Parallel Verification" and in "Break
+ * the Sequential Dependency of LLM Inference Using Lookahead Decoding":
+ * one causal target forward per round updates a W-wide, (N-1)-level Jacobi
+ * trajectory window and verifies up to G candidate n-grams, taken from a
+ * keyed n-gram pool, against one committed prefix, then publishes exactly
+ * the greedy (or exactly sampled) tokens.  The round follows the pages'
+ * predict -> collect -> verify -> publish state machine (M7.3, 0x00 and
+ * 0x03A lifecycle steps 1-8).
+ *
+ * Conventions for every function:
+ *   - Return value: LA_OK (0) or a negative LA_E* code.  On error nothing is
+ *     published: output tokens, committed K/V length, window and pool keep
+ *     their previous contents (M7.3, 0x07 fail-closed publication).  A
+ *     message is available from la_last_error(ctx) (ctx may be NULL for the
+ *     context-free calls; the message is then per thread).
+ *   - "device" pointers are HIP device addresses on the current device;
+ *     "host" pointers are ordinary host memory and are only read/written
+ *     during the call.  The library never frees caller memory; it borrows
+ *     the device buffers passed to la_init until la_destroy.
+ *   - stream: a hipStream_t (passed as void*); all device work of a call is
+ *     ordered on it.  Calls that return host data synchronise that stream.
+ *   - A context serves one request and is not thread-safe.
+ *   - Token ids are int32 in [0, vocab).  Tensor layouts are row-major.
+ */
+#ifndef LA_H
+#define LA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ----------------------------------------------------------------- errors */
+#define LA_OK 0
+#define LA_EINVAL (-1)    /* bad argument: N < 3 or not admitted, W < 1, G < 0, sizes out of range */
+#define LA_ESTATE (-2)    /* call out of order, or an accept record from another round */
+#define LA_EPLAN (-3)     /* publication plan fails validation (winner/h/emitted inconsistent) */
+#define LA_EOVERFLOW (-4) /* K/V capacity, output capacity or a buffer too small */
+#define LA_EDEVICE (-5)   /* a HIP call failed */
+
+#define LA_MAX_N 16       /* N <= 16, so S = N - 1 <= 15 and a round emits <= N tokens */
+#define LA_MAX_EMIT 32
+
+enum { LA_DTYPE_F32 = 0, LA_DTYPE_BF16 = 1 };
+enum { LA_VERIFY_GREEDY = 0, LA_VERIFY_SAMPLE = 1 };
+
+/* ------------------------------------------------------------------ model */
+/* Llama-style decoder: RMSNorm, RoPE (rotate-half, theta), grouped-query
+ * attention, SwiGLU MLP, untied LM head, no biases. */
+typedef struct la_model_dims {
+  int32_t n_layers, d_model, n_heads, n_kv_heads, head_dim, d_ff, vocab;
+  int32_t dtype;            /* LA_DTYPE_*: storage of weights, activations and K/V */
+  float eps;                /* RMSNorm epsilon */
+  float rope_theta;
+} la_model_dims;
+
+/* Device weight pointers (read-only, dtype of dims.dtype, nn.Linear layout
+ * [out_features][in_features], layers stacked on the leading axis):
+ *   embed      [V][d]                 lm_head [V][d]          final_norm [d]
+ *   attn_norm  [L][d]                 mlp_norm [L][d]
+ *   wqkv       [L][(H + 2 Hkv) dh][d] rows: q heads, then k heads, then v heads
+ *   wo         [L][d][H dh]
+ *   w_gate_up  [L][2 F][d]            rows: gate (F rows), then up (F rows)
+ *   w_down     [L][d][F]                                                      */
+typedef struct la_model {
+  const void* embed;
+  const void* lm_head;
+  const void* final_norm;
+  const void* attn_norm;
+  const void* wqkv;
+  const void* wo;
+  const void* mlp_norm;
+  const void* w_gate_up;
+  const void* w_down;
+} la_model;
+
+/* ----------------------------------------------------------------- config */
+typedef struct la_config {
+  int32_t W;                /* window width (lookahead columns), >= 1 */
+  int32_t N;                /* n-gram size; the pinned schedule admits integer N >= 3 */
+  int32_t G;                /* max candidates verified per round, >= 0 */
+  int32_t max_new;          /* tokens to generate (the first comes from prefill) */
+  int32_t verify_mode;      /* LA_VERIFY_GREEDY | LA_VERIFY_SAMPLE */
+  int32_t ar_only;          /* 1: plain autoregressive decoding (1 row per round) with the same kernels */
+  double temperature;       /* sampling: p = softmax(logits / temperature) */
+  uint64_t seed;            /* sampling: Philox4x32-10 key */
+  int32_t max_prompt;       /* capacity planning: longest prompt passed to la_init */
+  int32_t reserved[3];
+} la_config;
+
+/* Buffer sizes for a (config, dims) pair.  The caller allocates
+ *   kv    : kv_bytes    device bytes (K then V, each [L][Hkv][t_cap][dh])
+ *   arena : arena_bytes device bytes (activations, workspace K/V, logits,
+ *           row manifest, n-gram pool, window, verification scratch)
+ * 256-byte aligned (torch allocations are). */
+typedef struct la_sizes {
+  uint64_t kv_bytes;
+  uint64_t arena_bytes;
+  int32_t t_cap;            /* K/V rows per layer and head */
+  int32_t q_max;            /* most packed rows in one round */
+  int32_t n_logit_max;      /* most logit rows in one round */
+  int32_t reserved;
+} la_sizes;
+
+/* One verification result (M7.3, 0x06A publication plan, output part). */
+typedef struct la_accept {
+  int32_t round_id;         /* round the result belongs to */
+  int32_t h;                /* accepted candidate tokens, 0..S */
+  int32_t winner;           /* candidate whose first h rows are committed, -1 if h == 0 */
+  int32_t n_emit;           /* h + 1 */
+  int32_t emitted[LA_MAX_EMIT];
+} la_accept;
+
+/* Description of the round that la_predict compiled and ran. */
+typedef struct la_round_info {
+  int32_t round_id;
+  int32_t p;                /* logical position of the ordinary row (= committed K/V rows) */
+  int32_t Q;                /* packed rows */
+  int32_t C;                /* candidates retrieved for the current token */
+  int32_t n_inp;            /* rows of the deepest trajectory level */
+  int32_t n_logit;          /* 1 + n_inp + C * S logit rows */
+  int32_t warm;             /* window fully materialised (pool updates active) */
+  int32_t reserved;
+  const float* logits;      /* device [n_logit][vocab] fp32: out, inp (column order), guess ((c, s) order) */
+} la_round_info;
+
+typedef struct la_stats_t {
+  int64_t rounds;
+  int64_t tokens;           /* emitted, including the prefill token */
+  int64_t candidates;       /* sum of C over rounds */
+  int64_t accepted;         /* sum of h over rounds */
+  int32_t hist[LA_MAX_EMIT];/* rounds by emitted count (index = n_emit) */
+} la_stats_t;
+
+typedef struct la_state_t {
+  int32_t round_id;
+  int32_t kv_len;           /* committed K/V rows (= prompt + committed inputs) */
+  int32_t n_out;            /* output tokens so far */
+  int32_t R;                /* trajectory levels (N - 1) */
+  int32_t level_sizes[LA_MAX_N];
+  int32_t warm;
+  int32_t win_stride;
+} la_state_t;
+
+typedef struct la_ctx la_ctx;
+
+/* ------------------------------------------------------------- lifecycle */
+
+/* Sizes of the caller-provided buffers.  LA_EINVAL for an inadmissible
+ * config (N < 3, W < 1, G < 0, N > LA_MAX_N, bad dims). */
+int la_query_sizes(const la_config* cfg, const la_model_dims* dims, la_sizes* out);
+
+/* Validate, clear the pool, seed the window from the prompt (level 0 holds
+ * the last W + N - 3 prompt tokens, cyclically), prefill the prompt (plain
+ * causal forward; its K/V land in kv rows 0..P-1) and select the first
+ * output token.  kv/arena: device buffers of at least la_query_sizes bytes.
+ * prompt: host [prompt_len], 1 <= prompt_len <= cfg->max_prompt. */
+int la_init(const la_config* cfg, const la_model_dims* dims, const la_model* weights, void* kv, void* arena,
+            const int32_t* prompt, int32_t prompt_len, void* stream, la_ctx** out);
+void la_destroy(la_ctx* ctx);
+
+/* One full round: la_predict, la_verify on the round's logits, la_commit.
+ * Writes the round's emitted tokens (after truncation at max_new) to
+ * out_tokens (host, cap entries); n_out receives their number (0 once
+ * max_new tokens exist).  LA_EOVERFLOW if cap is too small. */
+int la_step(la_ctx* ctx, int32_t* out_tokens, int32_t cap, int32_t* n_out);
+
+/* Run rounds until max_new tokens exist; out_tokens (host) receives the
+ * whole output (first token included); n_out its length. */
+int la_generate(la_ctx* ctx, int32_t* out_tokens, int32_t cap, int32_t* n_out);
+
+/* ------------------------------------------------------- round, in steps */
+
+/* Predict: look up <= G suffixes for the current token (after warmup),
+ * compile the packed rows, run the target forward.  Mutates nothing that
+ * la_commit publishes.  LA_ESTATE if a predicted round is pending commit. */
+int la_predict(la_ctx* ctx, la_round_info* info);
+
+/* Verify (pure: no request state changes).  logits: device
+ * [1 + n_inp + C*S][vocab] fp32 laid out like la_round_info.logits, or NULL
+ * for the pending round's own logits.  cand: host [C][S] suffixes in pool
+ * order (NULL with logits == NULL: the pending round's candidates).
+ * z (host, may be NULL) receives the argmax of the n_inp deepest-level rows.
+ * Greedy or one-hot sampling per cfg->verify_mode; sampling draws use the
+ * counter (round_id, offset, draw). */
+int la_verify(la_ctx* ctx, const float* logits, int32_t n_inp, const int32_t* cand, int32_t C, la_accept* out,
+              int32_t* z);
+
+/* Publish one accepted path of the pending round, fail-closed: the plan is
+ * validated first (round_id of the pending round, 0 <= h <= S, winner in
+ * [0, C) iff h > 0, n_emit = h + 1, emitted[0..h-1] equal the winner's
+ * suffix, tokens in range, K/V capacity); only then are the winner's h K/V
+ * rows copied behind the ordinary row, the W new n-grams upserted into the
+ * pool (pre-shift window + this round's z, column order), the window
+ * advanced and the tokens appended.  LA_ESTATE / LA_EPLAN / LA_EOVERFLOW
+ * leave every piece of state unchanged. */
+int la_commit(la_ctx* ctx, const la_accept* acc);
+
+/* -------------------------------------------------------- pool and state */
+
+/* Suffixes stored for key, least recently used first (at most G).
+ * out: host [G][S]; n receives the count. */
+int la_pool_lookup(la_ctx* ctx, int32_t key, int32_t* out, int32_t* n);
+
+/* Upsert n (key, suffix) pairs in order with the per-key LRU rule.
+ * keys: host [n]; suffixes: host [n][S]. */
+int la_pool_insert(la_ctx* ctx, const int32_t* keys, const int32_t* suffixes, int32_t n);
+
+/* Host snapshot of the request state; window (host, may be NULL) receives
+ * [R][win_stride] tokens, output (host, may be NULL) up to out_cap tokens. */
+int la_get_state(la_ctx* ctx, la_state_t* st, int32_t* window, int32_t* output, int32_t out_cap);
+
+int la_stats(const la_ctx* ctx, la_stats_t* out);
+const char* la_last_error(const la_ctx* ctx);
+
+/* ------------------------------------------------ context-free operators */
+
+/* Packed-row builder (M7.3, 0x04A row records and visibility).  desc
+ * describes the round: levels[r] cells at columns starts[r].. (level 0 at
+ * column 1, the ordinary row is column 0), C candidates of S tokens.
+ * Rows are emitted in branch-major order: column j gives
+ * [b_j, u_(1,j), ..., u_(d_j,j)], then candidate c gives [v_(c,0..S-1)].
+ * out (device int32) receives, at the offsets reported in info:
+ *   tok[Q] pos[Q] role[Q] (0 ordinary, 1 lookahead, 2 verify) level[Q]
+ *   col[Q] cand[Q] off[Q] branch[Q] path[NB][maxp] path_len[NB]
+ *   logit_rows[n_logit] mask[Q][mask_words] (bit k of row i: i sees k).
+ * path[b][k] is the packed row (minus one) holding logical position
+ * p + 1 + k on branch b.  window: device [R][win_stride] tokens; cand:
+ * device [C][S].  la_rows_query fills info without launching anything. */
+typedef struct la_rows_desc {
+  int32_t p;                /* logical position of the ordinary row */
+  int32_t R;                /* levels */
+  int32_t sizes[LA_MAX_N];  /* cells per level, 0 = absent */
+  int32_t starts[LA_MAX_N]; /* first column of levels r >= 1 (level 0 starts at 1) */
+  int32_t C, S;
+  int32_t x_t;              /* current token (ordinary row input) */
+  int32_t win_stride;
+} la_rows_desc;
+
+typedef struct la_rows_info {
+  int32_t Q, NB, maxp, n_logit, n_inp, n_cols, mask_words, total_words;
+  int32_t off_tok, off_pos, off_role, off_level, off_col, off_cand, off_off, off_branch;
+  int32_t off_path, off_path_len, off_logit_rows, off_mask;
+} la_rows_info;
+
+int la_rows_query(const la_rows_desc* desc, la_rows_info* info);
+int la_build_rows(const la_rows_desc* desc, const int32_t* window, const int32_t* cand, int32_t* out, void* stream,
+                  la_rows_info* info);
+
+/* Lookahead-mask attention for one layer (M7.3, 0x04A visibility; 0x07
+ * three-region K/V).  q: device [Q][H][dh]; k_cache/v_cache: device
+ * [Hkv][t_cap][dh] holding logical positions 0..shared_end-1; k_ws/v_ws:
+ * device [Hkv][ws_cap][dh], packed row k at row k-1; rows: the device
+ * buffer filled by la_build_rows with its info; out: device [Q][H][dh].
+ * Row i attends positions 0..pos_i: those below shared_end from the cache,
+ * the others through its branch path.  workspace: device scratch of
+ * la_attention_workspace(...) bytes.  Batch invariant: a row's result
+ * does not depend on the other rows of the call. */
+size_t la_attention_workspace(int32_t Q, int32_t H, int32_t dh, int32_t max_pos);
+int la_attention(int32_t dtype, const void* q, const void* k_cache, const void* v_cache, int32_t t_cap,
+                 const void* k_ws, const void* v_ws, int32_t ws_cap, int32_t H, int32_t Hkv, int32_t dh,
+                 const int32_t* rows, const la_rows_info* info, int32_t shared_end, void* out, void* workspace,
+                 size_t workspace_bytes, void* stream);
+
+/* Token-wise linear layer of the target forward ("M7.3", 0x05C: the
+ * projections and MLP run over every packed row), Y = epilogue(X W^T):
+ *   LA_LINEAR_STORE    Y[M][N] = round(X W^T)
+ *   LA_LINEAR_RESIDUAL Y[M][N] = round(R + X W^T)            (R may alias Y)
+ *   LA_LINEAR_SWIGLU   W is [2N][K] (gate rows, then up rows);
+ *                      Y[M][N] = round(silu(X Wg^T) * (X Wu^T))
+ *   LA_LINEAR_F32      Y[M][N] = X W^T in fp32 (Y is float)
+ * X: device [M][K], W: device [N or 2N][K] (nn.Linear layout), dtype of
+ * X/W/R/Y (except F32's Y) is dtype; fp32 accumulation.  1 <= M <= 256,
+ * K a multiple of 128 (bf16) or 64 (fp32), N a multiple of 32 (16 for
+ * SWIGLU).  The K split (and so every output bit) depends on (N, K) only,
+ * never on M: a row's result is the same whatever other rows share the call.
+ * workspace: device scratch of la_linear_workspace(...) bytes (0 allowed
+ * when that returns 0). */
+enum { LA_LINEAR_STORE = 0, LA_LINEAR_RESIDUAL = 1, LA_LINEAR_SWIGLU = 2, LA_LINEAR_F32 = 3 };
+size_t la_linear_workspace(int32_t dtype, int32_t epilogue, int32_t M, int32_t N, int32_t K);
+int la_linear(int32_t dtype, int32_t epilogue, const void* X, const void* W, void* Y, const void* R, int32_t M,
+              int32_t N, int32_t K, void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LA_H */

@@ -34,6 +34,30 @@ from synthetic import ModelDims, f32_from_bf16_bits
 from .numerics import round_to
 
 
+def silu(g):
+    return g / (1.0 + np.exp(-g))
+
+
+def linear(x, w, dtype):
+    """Stored projection: s(x W^T)."""
+    return round_to(x @ w.T, dtype)
+
+
+def linear_residual(x, w, r, dtype):
+    """Residual update: s(r + x W^T)."""
+    return round_to(r + x @ w.T, dtype)
+
+
+def linear_swiglu(x, wg, wu, dtype):
+    """SwiGLU activation: s(silu(x Wg^T) * (x Wu^T))."""
+    return round_to(silu(x @ wg.T) * (x @ wu.T), dtype)
+
+
+def logits_f32(x, w):
+    """LM head, promoted to float32."""
+    return (x @ w.T).astype(np.float32).astype(np.float64)
+
+
 class KVCache:
     """Committed K/V per layer: k[l] and v[l] are [H_kv, T, dh] fp64 arrays (storage-rounded)."""
 
@@ -103,9 +127,6 @@ class OracleModel:
         x1, x2 = x[..., :half], x[..., half:]
         return np.concatenate([x1 * cos - x2 * sin, x2 * cos + x1 * sin], axis=-1)
 
-    @staticmethod
-    def silu(g):
-        return g / (1.0 + np.exp(-g))
 
     # one forward over new rows --------------------------------------------
     def forward(self, tokens, positions, cache: KVCache | None, visible: np.ndarray,
@@ -129,9 +150,9 @@ class OracleModel:
         new_k, new_v = [], []
         for l in range(d.n_layers):
             nrm = self.rms_norm(x, self.weight("attn_norm", l))
-            q = self.s(nrm @ self.weight("wq", l).T).reshape(n, d.n_heads, d.head_dim)
-            k = self.s(nrm @ self.weight("wk", l).T).reshape(n, d.n_kv_heads, d.head_dim)
-            v = self.s(nrm @ self.weight("wv", l).T).reshape(n, d.n_kv_heads, d.head_dim)
+            q = linear(nrm, self.weight("wq", l), d.dtype).reshape(n, d.n_heads, d.head_dim)
+            k = linear(nrm, self.weight("wk", l), d.dtype).reshape(n, d.n_kv_heads, d.head_dim)
+            v = linear(nrm, self.weight("wv", l), d.dtype).reshape(n, d.n_kv_heads, d.head_dim)
             q = self.s(self.rope(q, positions))
             k = self.s(self.rope(k, positions))
             new_k.append(k)
@@ -155,15 +176,13 @@ class OracleModel:
                 p = p / p.sum(axis=1, keepdims=True)
                 o[:, h, :] = p @ vals
             o = self.s(o).reshape(n, d.q_dim)
-            h_res = self.s(x + o @ self.weight("wo", l).T)
+            h_res = linear_residual(o, self.weight("wo", l), x, d.dtype)
             n2 = self.rms_norm(h_res, self.weight("mlp_norm", l))
-            gte = n2 @ self.weight("w_gate", l).T
-            up = n2 @ self.weight("w_up", l).T
-            a = self.s(self.silu(gte) * up)
-            x = self.s(h_res + a @ self.weight("w_down", l).T)
+            a = linear_swiglu(n2, self.weight("w_gate", l), self.weight("w_up", l), d.dtype)
+            x = linear_residual(a, self.weight("w_down", l), h_res, d.dtype)
         rows = np.arange(n) if logit_rows is None else np.asarray(logit_rows, dtype=np.int64)
         xf = self.rms_norm(x[rows], self.weight("final_norm"))
-        logits = (xf @ self.weight("lm_head").T).astype(np.float32).astype(np.float64)
+        logits = logits_f32(xf, self.weight("lm_head"))
         return logits, new_k, new_v
 
     # conveniences ---------------------------------------------------------

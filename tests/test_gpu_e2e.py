@@ -1,0 +1,207 @@
+"""End-to-end GPU parity of the packed lookahead round through the C ABI.
+
+* tiny fp32 decoder (2 layers, d 64, 4x16 heads, MLP 256, vocab 256; W=5,
+  N=3, G=5, 32-token Markov prompt, 64 tokens): every round's candidates,
+  accepted length, winner and emitted tokens equal the oracle's; logits
+  within 1e-5; final tokens equal oracle autoregressive greedy; the device
+  pool and window equal the oracle's at the end;
+* GPU lookahead tokens equal GPU autoregressive tokens bit for bit (the
+  kernels are batch invariant), for bf16 models too;
+* sampling: tokens equal the oracle's sampled run with the same seed;
+* fail-closed publication: a corrupted plan is refused and changes nothing.
+"""
+import numpy as np
+import pytest
+
+import synthetic
+from oracle.decode import ar_generate, lookahead_generate
+from oracle.model import OracleModel
+from oracle import pool as opool
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+la = pytest.importorskip("exact_lookahead_decoding_amd.la")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    la.load()
+
+
+def _model(name, seed=0):
+    dims = synthetic.PRESETS[name]
+    w = synthetic.model_weights(dims, seed)
+    return dims, w, la.DeviceModel(dims, weights=w), OracleModel(dims, w)
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    return _model("tiny")
+
+
+@pytest.fixture(scope="module")
+def small_bf16():
+    return _model("small_bf16")
+
+
+def _logits_view(sess, info, V):
+    off = info.logits - sess.arena.data_ptr()
+    n = info.n_logit * V * 4
+    return sess.arena[off: off + n].view(torch.float32).view(info.n_logit, V)
+
+
+def _top2_gap(row):
+    s = np.sort(np.asarray(row, np.float64))
+    return s[-1] - s[-2]
+
+
+def test_tiny_rounds_match_oracle(tiny):
+    dims, w, dm, om = tiny
+    W, N, G, max_new = 5, 3, 5, 64
+    prompt = synthetic.markov_prompt(dims.vocab, 32, 0)
+    ref = lookahead_generate(om, prompt, W, N, G, max_new, record_logits=True)
+    ar = ar_generate(om, prompt, max_new)
+    assert ref["tokens"] == ar
+    sess = la.Session(dm, prompt, W=W, N=N, G=G, max_new=max_new)
+    worst = 0.0
+    for k, rr in enumerate(ref["rounds"]):
+        info = sess.la_predict()
+        print(f"round {k + 1}: Q={info.Q} C={info.C}", flush=True)
+        assert info.C == len(rr.candidates), k
+        assert info.Q == rr.Q
+        lg = _logits_view(sess, info, dims.vocab).cpu().numpy().astype(np.float64)
+        err = np.max(np.abs(lg - rr.logits))
+        worst = max(worst, err)
+        assert err <= 1e-5, (k, err)
+        acc, _ = sess.la_verify()
+        assert (acc.h, acc.winner) == (rr.h, rr.winner), k
+        assert list(acc.emitted[: acc.n_emit]) == rr.emitted, k
+        sess.la_commit(acc)
+    st = sess.la_get_state()
+    print(f"worst logit error {worst:.3g}; rounds {len(ref['rounds'])}", flush=True)
+    assert st["output"] == ar
+    assert st["levels"] == ref["window"]
+    for key in range(dims.vocab):
+        assert sess.la_pool_lookup(key) == opool.lookup(ref["token_map"], key, G), key
+
+
+@pytest.mark.parametrize("W,N,G", [(5, 3, 5), (4, 4, 3), (7, 5, 7)])
+def test_tiny_generate_equals_ar(tiny, W, N, G):
+    dims, w, dm, om = tiny
+    prompt = synthetic.markov_prompt(dims.vocab, 32, 1)
+    ar = ar_generate(om, prompt, 48)
+    la_tokens = la.Session(dm, prompt, W=W, N=N, G=G, max_new=48).la_generate()
+    gpu_ar = la.Session(dm, prompt, W=W, N=N, G=G, max_new=48, ar_only=True).la_generate()
+    assert la_tokens == gpu_ar
+    assert la_tokens == ar
+
+
+def test_bf16_lookahead_bitwise_equals_ar(small_bf16):
+    dims, w, dm, om = small_bf16
+    prompt = synthetic.markov_prompt(dims.vocab, 40, 2)
+    s_la = la.Session(dm, prompt, W=4, N=4, G=4, max_new=40)
+    toks = s_la.la_generate()
+    gpu_ar = la.Session(dm, prompt, W=4, N=4, G=4, max_new=40, ar_only=True).la_generate()
+    assert toks == gpu_ar
+    st = s_la.la_stats()
+    print(f"rounds {st['rounds']} for {st['tokens']} tokens", flush=True)
+    # against the oracle: equal up to the first position where the oracle's top-2 gap is below 2e-2
+    ref = ar_generate(om, prompt, 40)
+    cache, lg = om.prefill(prompt)
+    for i, (a, b) in enumerate(zip(toks, ref)):
+        if a != b:
+            seq = list(prompt) + ref[:i]
+            gap = _top2_gap(om.sequence_logits(seq))
+            print(f"first divergence at {i}, oracle top-2 gap {gap:.3g}", flush=True)
+            assert gap < 2e-2
+            break
+
+
+def test_sampling_matches_oracle(tiny):
+    dims, w, dm, om = tiny
+    prompt = synthetic.markov_prompt(dims.vocab, 32, 3)
+    for seed in (0, 1, 2):
+        ref = lookahead_generate(om, prompt, 5, 3, 5, 40, mode="sample", T=0.7, seed=seed)
+        toks = la.Session(dm, prompt, W=5, N=3, G=5, max_new=40, verify_mode=la.LA_VERIFY_SAMPLE, temperature=0.7,
+                          seed=seed).la_generate()
+        assert toks == ref["tokens"], seed
+
+
+def test_fail_closed_commit(tiny):
+    dims, w, dm, om = tiny
+    prompt = synthetic.markov_prompt(dims.vocab, 32, 0)
+    sess = la.Session(dm, prompt, W=5, N=3, G=5, max_new=64)
+    # run until a round with candidates and a hit is pending
+    acc = None
+    for _ in range(60):
+        info = sess.la_predict()
+        acc, _ = sess.la_verify()
+        if info.C > 0 and acc.h > 0:
+            break
+        sess.la_commit(acc)
+    assert acc is not None and acc.h > 0
+    before = sess.la_get_state()
+    keys = list(range(dims.vocab))
+    pool_before = [sess.la_pool_lookup(k) for k in keys]
+
+    def corrupt(**kw):
+        bad = la.la_accept()
+        bad.round_id, bad.h, bad.winner, bad.n_emit = acc.round_id, acc.h, acc.winner, acc.n_emit
+        for i in range(la.LA_MAX_EMIT):
+            bad.emitted[i] = acc.emitted[i]
+        for k, v in kw.items():
+            if k == "emitted0":
+                bad.emitted[0] = v
+            else:
+                setattr(bad, k, v)
+        return bad
+
+    cases = [(dict(h=acc.h + 5), la.LA_EPLAN), (dict(winner=99), la.LA_EPLAN), (dict(n_emit=acc.n_emit + 1), la.LA_EPLAN),
+             (dict(round_id=acc.round_id + 1), la.LA_ESTATE), (dict(emitted0=(acc.emitted[0] + 1) % dims.vocab),
+                                                               la.LA_EPLAN),
+             (dict(h=0, winner=-1, n_emit=1), la.LA_EPLAN)]
+    for kw, code in cases:
+        with pytest.raises(la.LaError) as e:
+            sess.la_commit(corrupt(**kw))
+        assert e.value.code == code, kw
+        assert sess.la_get_state() == before
+    assert [sess.la_pool_lookup(k) for k in keys] == pool_before
+    sess.la_commit(acc)
+    while sess.la_step():
+        pass
+    assert sess.la_get_state()["output"] == ar_generate(om, prompt, 64)
+
+
+# Two correct bf16 computations of this model whose pre-rounding values differ
+# only at fp32-vs-fp64 level (relative 1e-7) already disagree by up to ~0.03 on
+# these logits (tests/test_oracle_noise_floor.py measures it): each flipped bf16
+# rounding propagates through every later layer.  The model-level bound is
+# therefore twice that floor; single operators keep the 2e-2 bound.
+BF16_2LAYER_LOGIT_TOL = 0.06
+
+
+@pytest.mark.timeout(900)
+def test_llama7b_2layer_parity_and_invariance():
+    """7B widths (d 4096, 32 heads, MLP 11008, vocab 32000), 2 layers, bf16."""
+    dims, w, dm, om = _model("llama7b_2l")
+    prompt = synthetic.markov_prompt(dims.vocab, 64, 0)
+    s_la = la.Session(dm, prompt, W=7, N=5, G=7, max_new=32)
+    info_tokens = s_la.la_generate()
+    gpu_ar = la.Session(dm, prompt, W=7, N=5, G=7, max_new=32, ar_only=True).la_generate()
+    assert info_tokens == gpu_ar
+    # prefill logits of the last prompt row against the oracle
+    s = la.Session(dm, prompt, W=7, N=5, G=7, max_new=2)
+    info = s.la_predict()
+    lg = _logits_view(s, info, dims.vocab)[0].cpu().numpy().astype(np.float64)
+    first = s.la_get_state()["output"][0]
+    seq = list(prompt) + [first]
+    want = om.sequence_logits(seq)
+    d = np.abs(lg - want)
+    err = d.max()
+    print(f"7B-wide 2-layer: round-1 ordinary-row logits max abs err {err:.3g}, mean {d.mean():.3g}, "
+          f"logit std {want.std():.3g}, argmax gpu {int(np.argmax(lg))} oracle {int(np.argmax(want))}", flush=True)
+    assert err <= BF16_2LAYER_LOGIT_TOL
+    assert int(np.argmax(lg)) == int(np.argmax(want)) or _top2_gap(want) < 2e-2

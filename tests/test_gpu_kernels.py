@@ -1,0 +1,374 @@
+"""GPU parity of the individual hot-path kernels against the oracle, through the C ABI.
+
+Integer work (row manifest, mask, pool, accepted lengths, emitted tokens) is
+compared bit-exactly; attention within 1e-5 (fp32) / 2e-2 (bf16) max abs error.
+Inputs are seeded synthetic arrays; expected values come only from oracle/.
+"""
+import numpy as np
+import pytest
+
+import synthetic
+from oracle import attention as oattn
+from oracle import pool as opool
+from oracle import rows as orows
+from oracle import verify as overify
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+la = pytest.importorskip("exact_lookahead_decoding_amd.la")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    la.load()
+
+
+DEV = "cuda"
+
+
+def _levels(sizes, base=100):
+    return [None if n == 0 else [base + 10 * r + j for j in range(n)] for r, n in enumerate(sizes)]
+
+
+def _window_dev(levels, stride):
+    w = np.zeros((len(levels), stride), np.int32)
+    for r, lv in enumerate(levels):
+        if lv:
+            w[r, : len(lv)] = lv
+    return torch.from_numpy(w).to(DEV)
+
+
+def _identity(role, level, col, cand, off):
+    if role == 0:
+        return (orows.ORDINARY, 0, 0, -1, -1)
+    if role == 1:
+        return (orows.LOOKAHEAD, level, col, -1, -1)
+    return (orows.VERIFY, -1, -1, cand, off)
+
+
+def _build(sizes, starts, cands, S, p=50, x_t=7, stride=40):
+    levels = _levels(sizes)
+    comp = orows.compile_round(x_t, p, levels, cands, S, starts=starts)
+    win = _window_dev(levels, stride)
+    cd = torch.tensor(np.asarray(cands, np.int32).reshape(-1) if cands else np.zeros(1, np.int32), device=DEV)
+    desc = la.rows_desc(p, levels, S, len(cands), x_t, stride, starts)
+    buf, info = la.la_build_rows(desc, win, cd)
+    torch.cuda.synchronize()
+    return comp, buf.cpu().numpy(), info
+
+
+def _gpu_rows(b, info):
+    Q = info.Q
+    f = lambda off: b[off: off + Q]
+    ids = [_identity(*t) for t in zip(f(info.off_role), f(info.off_level), f(info.off_col), f(info.off_cand),
+                                       f(info.off_off))]
+    return ids, f(info.off_tok), f(info.off_pos)
+
+
+LAYOUTS = [
+    ([4, 5, 5], [1, 0, 0], [(1, 2, 3), (4, 5, 6)], 3),                  # page's W=5, N=4, G=2 coordinate
+    ([6, 0, 0], [1, 0, 0], [], 3),                                      # first warmup call
+    ([5, 6, 0], [1, 0, 0], [], 3),                                      # second warmup call
+    ([6, 7, 7, 7], [1, 0, 0, 0], [tuple(range(i, i + 4)) for i in range(7)], 4),   # N=5, W=7, G=7: 56 rows
+    ([15, 15, 15, 15], [1, 1, 1, 1], [tuple(range(i, i + 4)) for i in range(15)], 4),  # rectangular, 121 rows
+    ([14] + [15] * 5, [1, 0, 0, 0, 0, 0], [tuple(range(i, i + 6)) for i in range(15)], 6),  # N=7, W=15, G=15
+    ([0, 0], [1, 0], [], 2),                                            # autoregressive: one ordinary row
+    ([4, 5], [1, 0], [(9, 9), (9, 8), (9, 9)], 2),                      # duplicates among candidates
+]
+
+
+@pytest.mark.parametrize("case", range(len(LAYOUTS)))
+def test_build_rows_matches_oracle(case):
+    sizes, starts, cands, S = LAYOUTS[case]
+    comp, b, info = _build(sizes, starts, cands, S)
+    print(f"layout {sizes} C={len(cands)} Q={comp.Q}", flush=True)
+    assert info.Q == comp.Q
+    ids, tok, pos = _gpu_rows(b, info)
+    oid = [r.identity for r in comp.rows]
+    assert sorted(ids) == sorted(oid)
+    perm = [oid.index(i) for i in ids]                 # gpu row -> oracle row
+    assert [comp.rows[k].token for k in perm] == list(tok)
+    assert [comp.rows[k].logical_position for k in perm] == list(pos)
+    # logit rows: out, inp (column order), guess ((c, s) order) name the same rows
+    lr = b[info.off_logit_rows: info.off_logit_rows + info.n_logit]
+    want = [comp.out] + comp.inp + comp.guess
+    assert [perm[x] for x in lr] == want
+    # compact visibility mask == the Vis sets, bit for bit
+    words = info.mask_words
+    m = b[info.off_mask: info.off_mask + comp.Q * words].astype(np.uint32).reshape(comp.Q, words)
+    for i in range(comp.Q):
+        for k in range(comp.Q):
+            bit = (int(m[i, k // 32]) >> (k % 32)) & 1
+            assert bit == int(comp.visible[perm[i], perm[k]]), (i, k)
+
+
+def _attn_case(sizes, starts, cands, S, p, H, Hkv, dh, dtype, seed=0):
+    """Inputs in oracle row order -> GPU placement; returns (gpu out in oracle order, oracle out)."""
+    comp, b, info = _build(sizes, starts, cands, S, p=p)
+    Q = comp.Q
+    q, kp, vp, kn, vn = synthetic.attention_op_inputs(Q, H, Hkv, dh, p, seed=seed, dtype=dtype)
+    ids, _, _ = _gpu_rows(b, info)
+    oid = [r.identity for r in comp.rows]
+    perm = np.array([oid.index(i) for i in ids])
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+
+    def dev(a):
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        return (t.view(torch.int16).view(torch.bfloat16) if dtype == "bf16" else t).to(DEV)
+
+    f64 = (lambda a: synthetic.f32_from_bf16_bits(a).astype(np.float64)) if dtype == "bf16" else \
+        (lambda a: a.astype(np.float64))
+    t_cap = p + 8
+    kc = np.zeros((Hkv, t_cap, dh), kp.dtype)
+    vc = np.zeros((Hkv, t_cap, dh), vp.dtype)
+    kc[:, :p] = kp
+    vc[:, :p] = vp
+    kc[:, p] = kn[0]                      # ordinary row (oracle row 0) sits at cache row p
+    vc[:, p] = vn[0]
+    ws_cap = Q
+    kw = np.zeros((Hkv, ws_cap, dh), kn.dtype)
+    vw = np.zeros((Hkv, ws_cap, dh), vn.dtype)
+    for g_row in range(1, Q):
+        kw[:, g_row - 1] = kn[perm[g_row]]
+        vw[:, g_row - 1] = vn[perm[g_row]]
+    qg = q[perm]
+    rows_t = torch.from_numpy(b).to(DEV)
+    out = la.la_attention(dev(qg), dev(kc), dev(vc), dev(kw), dev(vw), rows_t, info, p + 1)
+    torch.cuda.synchronize()
+    if dtype == "bf16":
+        got_g = synthetic.f32_from_bf16_bits(out.view(torch.int16).cpu().numpy().view(np.uint16)).astype(np.float64)
+    else:
+        got_g = out.cpu().numpy().astype(np.float64)
+    got = np.zeros_like(got_g)
+    got[perm] = got_g
+    want = oattn.lookahead_attention(f64(q), f64(kp), f64(vp), f64(kn), f64(vn), comp.visible)
+    return got, want, (comp, b, info, perm, dev, q, kc, vc, kw, vw, out)
+
+
+ATTN = [
+    # (sizes, starts, cands, S, p, H, Hkv, dh, dtype, tol)
+    ([15, 15, 15, 15], [1, 1, 1, 1], [tuple(range(i, i + 4)) for i in range(15)], 4, 1024, 32, 32, 128, "bf16", 2e-2),
+    ([6, 7, 7, 7], [1, 0, 0, 0], [tuple(range(i, i + 4)) for i in range(7)], 4, 1000, 8, 2, 128, "bf16", 2e-2),
+    ([4, 5], [1, 0], [(1, 2), (3, 4), (5, 6)], 2, 37, 4, 4, 16, "f32", 1e-5),
+    ([4, 5, 5], [1, 0, 0], [(1, 2, 3), (4, 5, 6)], 3, 130, 4, 2, 64, "f32", 1e-5),
+    ([14] + [15] * 5, [1, 0, 0, 0, 0, 0], [tuple(range(i, i + 6)) for i in range(15)], 6, 300, 16, 2, 128, "bf16",
+     2e-2),
+    ([3, 0], [1, 0], [], 2, 0, 4, 4, 16, "f32", 1e-5),                 # empty prefix
+    ([0, 0], [1, 0], [], 2, 255, 4, 2, 64, "bf16", 2e-2),               # one ordinary row
+]
+
+
+@pytest.mark.parametrize("case", range(len(ATTN)))
+def test_attention_matches_oracle(case):
+    sizes, starts, cands, S, p, H, Hkv, dh, dtype, tol = ATTN[case]
+    print(f"attention case {case}: p={p} H={H}/{Hkv} dh={dh} {dtype}", flush=True)
+    got, want, _ = _attn_case(sizes, starts, cands, S, p, H, Hkv, dh, dtype)
+    err = np.max(np.abs(got - want))
+    print(f"  max abs err {err:.3g}", flush=True)
+    assert err <= tol
+
+
+def test_attention_batch_invariance():
+    """A packed row's output equals, bit for bit, the same row computed alone
+    with its branch ancestors committed to the cache (an autoregressive call)."""
+    sizes, starts = [6, 7, 7, 7], [1, 0, 0, 0]
+    cands = [tuple(range(i, i + 4)) for i in range(7)]
+    p, H, Hkv, dh = 1000, 8, 2, 128
+    got, want, ctx = _attn_case(sizes, starts, cands, 4, p, H, Hkv, dh, "bf16", seed=3)
+    comp, b, info, perm, dev, q, kc, vc, kw, vw, out = ctx
+    out_np = out.view(torch.int16).cpu().numpy()
+    kn = np.zeros((comp.Q, Hkv, dh), np.uint16)
+    vn = np.zeros_like(kn)
+    kn[perm[0]] = kc[:, p]
+    vn[perm[0]] = vc[:, p]
+    for g_row in range(1, comp.Q):
+        kn[perm[g_row]] = kw[:, g_row - 1]
+        vn[perm[g_row]] = vw[:, g_row - 1]
+    checked = 0
+    for g_row in range(comp.Q):
+        i = perm[g_row]
+        vis = sorted((j for j in range(comp.Q) if comp.visible[i, j]), key=lambda j: comp.rows[j].logical_position)
+        pos = comp.rows[i].logical_position
+        t_cap = pos + 8
+        kc1 = np.zeros((Hkv, t_cap, dh), np.uint16)
+        vc1 = np.zeros_like(kc1)
+        kc1[:, :p] = kc[:, :p]
+        vc1[:, :p] = vc[:, :p]
+        for j in vis:
+            t = comp.rows[j].logical_position
+            kc1[:, t] = kn[j]
+            vc1[:, t] = vn[j]
+        desc = la.rows_desc(pos, [None, None], 2, 0, 0, 8)     # a single ordinary row at pos
+        w = torch.zeros((2, 8), dtype=torch.int32, device=DEV)
+        rb, rinfo = la.la_build_rows(desc, w, torch.zeros(1, dtype=torch.int32, device=DEV))
+        o1 = la.la_attention(dev(q[i: i + 1]), dev(kc1), dev(vc1), None, None, rb, rinfo, pos + 1)
+        torch.cuda.synchronize()
+        assert np.array_equal(o1.view(torch.int16).cpu().numpy()[0], out_np[g_row]), f"row {comp.rows[i].identity}"
+        checked += 1
+    assert checked == comp.Q
+
+
+# ---------------------------------------------------------------- verify
+
+@pytest.fixture(scope="module")
+def verify_session():
+    """A context whose only job is to host la_verify (vocab 32000)."""
+    dims = synthetic.ModelDims(1, 64, 4, 4, 16, 128, 32000, "f32")
+    m = la.DeviceModel(dims, seed=1)
+    return la.Session(m, [1, 2, 3], W=7, N=5, G=7, max_new=4, verify_mode=la.LA_VERIFY_GREEDY)
+
+
+@pytest.fixture(scope="module")
+def sample_session():
+    dims = synthetic.ModelDims(1, 64, 4, 4, 16, 128, 32000, "f32")
+    m = la.DeviceModel(dims, seed=1)
+    return la.Session(m, [1, 2, 3], W=7, N=5, G=7, max_new=4, verify_mode=la.LA_VERIFY_SAMPLE, temperature=0.7,
+                      seed=1234)
+
+
+def _consistent_logits(rng, V, n_inp, cands, S, path, ties=False):
+    """Logits in which every row after the same accepted prefix is the same row
+    (the survivor invariant of the pages), with a greedy path planted."""
+    table = {}
+
+    def row(prefix):
+        if prefix not in table:
+            r = rng.standard_normal(V).astype(np.float32)
+            k = len(prefix)
+            if list(prefix) == list(path[:k]) and k < len(path):
+                r[path[k]] = 9.0
+            if ties:
+                j = int(np.argmax(r))
+                r[max(0, j - 3)] = r[j]              # an equal maximum at a lower id
+            table[prefix] = r
+        return table[prefix]
+    rows = [row(())] + [rng.standard_normal(V).astype(np.float32) for _ in range(n_inp)]
+    for c in cands:
+        rows += [row(tuple(c[: s + 1])) for s in range(S)]
+    return np.stack(rows)
+
+
+def test_verify_greedy_matches_oracle(verify_session):
+    sess = verify_session
+    S, V, n_inp = 4, 32000, 7
+    rng = np.random.default_rng(5)
+    for trial in range(40):
+        C = int(rng.integers(0, 8))
+        base = [int(t) for t in rng.integers(0, V, S)]
+        cands = []
+        for c in range(C):
+            k = int(rng.integers(0, S + 1))
+            cands.append(tuple(base[:k] + [int(t) for t in rng.integers(0, V, S - k)]))
+        if C and trial % 5 == 0:
+            cands[-1] = cands[0]                     # duplicate candidate
+        depth = int(rng.integers(0, S + 1))
+        path = base[:depth] + [int(t) for t in rng.integers(0, V, S + 1 - depth)]
+        lg = _consistent_logits(rng, V, n_inp, cands, S, path, ties=trial % 3 == 0)
+        dl = torch.from_numpy(lg).to(DEV)
+        acc, z = sess.la_verify(dl, n_inp, np.asarray(cands, np.int32).reshape(C, S) if C else None)
+        out = lg[0]
+        inp = lg[1: 1 + n_inp]
+        guess = [[lg[1 + n_inp + c * S + s] for s in range(S)] for c in range(C)]
+        em, win, h = overify.greedy_verify(out, guess, cands)
+        hits = overify.greedy_hits(out, guess, cands)
+        assert acc.h == (max(hits) if hits else 0) == h, trial
+        assert list(acc.emitted[: acc.n_emit]) == em
+        assert acc.winner == win
+        assert z == [int(np.flatnonzero(r == r.max())[0]) for r in inp]
+
+
+def test_verify_sampling_matches_oracle(sample_session):
+    sess = sample_session
+    S, V, n_inp = 4, 32000, 7
+    rng = np.random.default_rng(9)
+    n_cases = 60
+    for trial in range(n_cases):
+        C = int(rng.integers(0, 8))
+        lg = (rng.standard_normal((1 + n_inp + C * S, V)) * 2.0).astype(np.float32)
+        top = np.argsort(-lg, axis=1)[:, :3]
+        cands = []
+        for c in range(C):
+            # draw candidate tokens from each row's top-3 so acceptances happen
+            toks = [int(top[0, rng.integers(3)])]
+            for s in range(1, S):
+                toks.append(int(top[1 + n_inp + c * S + s - 1, rng.integers(3)]))
+            cands.append(tuple(toks))
+        dl = torch.from_numpy(lg).to(DEV)
+        st = sess.la_get_state(with_window=False)
+        acc, z = sess.la_verify(dl, n_inp, np.asarray(cands, np.int32).reshape(C, S) if C else None)
+        out = lg[0]
+        guess = [[lg[1 + n_inp + c * S + s] for s in range(S)] for c in range(C)]
+        em, win, h = overify.sample_verify(out, guess, cands, 0.7, 1234, st["round_id"] + 1)
+        assert (acc.h, acc.winner) == (h, win), trial
+        assert list(acc.emitted[: acc.n_emit]) == em, trial
+
+
+# ---------------------------------------------------------------- pool
+
+def test_pool_upserts_match_oracle(verify_session):
+    sess = verify_session
+    G, S = 7, 4
+    rng = np.random.default_rng(2)
+    tm = {}
+    keys_used = set()
+    for batch in range(12):
+        n = int(rng.integers(1, 40))
+        keys = rng.integers(0, 6, n)                 # few keys: collisions, reinsertions, evictions
+        sufs = rng.integers(0, 3, (n, S))
+        sess.la_pool_insert(keys, sufs)
+        for k, s in zip(keys, sufs):
+            opool.upsert_suffix_lru(tm, int(k), tuple(int(t) for t in s), G)
+            keys_used.add(int(k))
+    for k in sorted(keys_used) + [100, 31999]:
+        assert sess.la_pool_lookup(k) == opool.lookup(tm, k, G), k
+
+
+# ---------------------------------------------------------------- linear layers (target forward)
+
+LINEAR = [
+    # (epilogue, M, N, K): 7B-shaped projections of a 56-row round and its LM head
+    ("store", 56, 12288, 4096),
+    ("residual", 56, 4096, 4096),
+    ("swiglu", 56, 11008, 4096),
+    ("residual", 56, 4096, 11008),
+    ("f32", 36, 32000, 4096),
+    ("store", 181, 1536, 256),      # ragged M (12 row tiles), small K
+    ("swiglu", 17, 512, 256),
+]
+
+
+@pytest.mark.parametrize("case", range(len(LINEAR)))
+def test_linear_matches_oracle_and_is_batch_invariant(case):
+    from oracle.model import linear, linear_residual, linear_swiglu, logits_f32
+    epi, M, N, K = LINEAR[case]
+    rng = synthetic.misc_rng(0, 77, case)
+    rows_w = 2 * N if epi == "swiglu" else N
+    X = synthetic.bf16_bits_from_f32(rng.standard_normal((M, K)).astype(np.float32))
+    W = synthetic.bf16_bits_from_f32((rng.standard_normal((rows_w, K)) * 0.02).astype(np.float32))
+    R = synthetic.bf16_bits_from_f32(rng.standard_normal((M, N)).astype(np.float32))
+    f64 = lambda a: synthetic.f32_from_bf16_bits(a).astype(np.float64)
+    dev = lambda a: torch.from_numpy(a.view(np.int16)).to(DEV).view(torch.bfloat16)
+    code = {"store": la.LA_LINEAR_STORE, "residual": la.LA_LINEAR_RESIDUAL, "swiglu": la.LA_LINEAR_SWIGLU,
+            "f32": la.LA_LINEAR_F32}[epi]
+    Xd, Wd, Rd = dev(X), dev(W), dev(R)
+    y = la.la_linear(code, Xd, Wd, Rd if epi == "residual" else None)
+    y1 = la.la_linear(code, Xd[:1].contiguous(), Wd, Rd[:1].contiguous() if epi == "residual" else None)
+    torch.cuda.synchronize()
+    tohost = (lambda t: t.cpu().numpy().astype(np.float64)) if epi == "f32" else \
+        (lambda t: synthetic.f32_from_bf16_bits(t.view(torch.int16).cpu().numpy().view(np.uint16)).astype(np.float64))
+    got, got1 = tohost(y), tohost(y1)
+    if epi == "store":
+        want = linear(f64(X), f64(W), "bf16")
+    elif epi == "residual":
+        want = linear_residual(f64(X), f64(W), f64(R), "bf16")
+    elif epi == "swiglu":
+        want = linear_swiglu(f64(X), f64(W)[:N], f64(W)[N:], "bf16")
+    else:
+        want = logits_f32(f64(X), f64(W))
+    err = np.max(np.abs(got - want))
+    print(f"linear {epi} M={M} N={N} K={K}: max abs err {err:.3g}", flush=True)
+    assert err <= 2e-2
+    assert np.array_equal(got1[0], got[0])          # a row alone == the same row among M

@@ -1,0 +1,67 @@
+"""Host-side checks of the C-ABI library (no GPU): it loads, exports every
+symbol include/la.h declares, sizes rounds like the oracle, rejects bad input."""
+import os
+import re
+
+import pytest
+
+import synthetic
+from conftest import ROOT
+from oracle import rows as orows
+
+la = pytest.importorskip("exact_lookahead_decoding_amd.la")
+
+
+def _lib():
+    try:
+        return la.load()
+    except RuntimeError as e:
+        pytest.fail(f"library not built: {e}")
+
+
+def test_exports_match_header():
+    lib = _lib()
+    hdr = open(os.path.join(ROOT, "include", "la.h")).read()
+    names = set(re.findall(r"^\s*(?:int|void|size_t|const char\*)\s+(la_\w+)\s*\(", hdr, flags=re.M))
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(la.EXPORTS) == names
+
+
+@pytest.mark.parametrize("W,N,G,q", [(7, 5, 7, 56), (15, 5, 15, 120), (5, 3, 5, 20), (15, 7, 15, 180), (5, 4, 2, 21)])
+def test_query_sizes_row_ledger(W, N, G, q):
+    d = la.dims_struct(synthetic.PRESETS["llama7b"])
+    s = la.la_query_sizes(la.make_config(W, N, G, 64, 100), d)
+    assert s.q_max == q == (W + G) * (N - 1)
+    assert s.kv_bytes == 2 * 32 * 32 * s.t_cap * 128 * 2
+
+
+def test_invalid_configs_rejected():
+    d = la.dims_struct(synthetic.PRESETS["tiny"])
+    for args in [(5, 2, 5), (5, 1, 5), (0, 3, 5), (5, 3, -1), (5, 17, 5)]:
+        with pytest.raises(la.LaError) as e:
+            la.la_query_sizes(la.make_config(*args, 10, 10), d)
+        assert e.value.code == la.LA_EINVAL
+
+
+def _oracle_layout(levels, starts, C, S):
+    cands = [tuple(range(S)) for _ in range(C)]
+    return orows.compile_round(1, 10, levels, cands, S, starts=starts)
+
+
+@pytest.mark.parametrize("sizes,starts,C,S", [
+    ([4, 5, 5], [1, 0, 0], 2, 3),
+    ([6, 0, 0], [1, 0, 0], 0, 3),
+    ([5, 6, 0], [1, 0, 0], 0, 3),
+    ([15, 15, 15, 15], [1, 1, 1, 1], 15, 4),
+    ([14, 15, 15, 15, 15, 15], [1, 0, 0, 0, 0, 0], 15, 6),
+    ([0, 0], [1, 0], 0, 2),
+])
+def test_rows_query_matches_oracle(sizes, starts, C, S):
+    levels = [None if n == 0 else list(range(n)) for n in sizes]
+    comp = _oracle_layout(levels, starts, C, S)
+    info = la.la_rows_query(la.rows_desc(10, levels, S, C, 1, 32, starts))
+    assert info.Q == comp.Q
+    assert info.n_inp == len(comp.inp)
+    assert info.n_logit == 1 + len(comp.inp) + len(comp.guess)
