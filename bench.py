@@ -1,0 +1,242 @@
+#!/usr/bin/env python3
+"""Benchmark of the packed lookahead + verification round on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one full round (pool lookup, row manifest, target forward over the
+packed rows, LM head on the required rows, verification, K/V commit, pool
+upsert, window advance) through the C ABI's la_step.  Default workload: a
+Llama-2-7B-shaped random-init bf16 decoder (32 layers, d 4096, 32 heads,
+MLP 11008, vocab 32000), 512-token prompt from the seeded order-2 Markov
+chain, greedy lookahead with W=7, N=5, G=7, 256 new tokens.  Weights and
+prompt are resident in HBM before timing; prefill is outside the timed
+region.  value = emitted tokens / wall time of the K timed rounds.
+
+Also reported on the same line:
+  * roofline: the dominant kernel of the step (the batch-invariant GEMM that
+    streams the weights), algorithmic bytes per launch over its average
+    launch time from HIP events on the library's stream;
+  * lookahead_attn: the isolated lookahead-mask attention op (bf16, 32 heads
+    x 128, committed prefix 1024, 121 query rows: W=15, N=5, G=15 with the
+    rectangular window), timed with HIP events over rotating input sets that
+    exceed the 256 MB Infinity Cache;
+  * ar_tokens_per_s: plain autoregressive decoding with the same kernels;
+  * cpu_baseline: the CPU oracle on a bounded sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "accepted tokens/sec per sequence + lookahead-attn HBM GB/s (% of peak), 1 GPU"
+HBM_PEAK_GBS = 8000.0
+
+WORKLOADS = {
+    "llama7b_w7n5g7": dict(model="llama7b", W=7, N=5, G=7, prompt=512, max_new=256, desc=(
+        "Llama-2-7B-shaped bf16 decoder, 512-token Markov prompt, greedy lookahead W=7 N=5 G=7, 256 new tokens")),
+    "llama7b_long_w15n5g15": dict(model="llama7b", W=15, N=5, G=15, prompt=8192, max_new=256, desc=(
+        "Llama-2-7B-shaped bf16 decoder, 8192-token Markov prompt, greedy lookahead W=15 N=5 G=15")),
+    "tiny_w5n3g5": dict(model="tiny", W=5, N=3, G=5, prompt=32, max_new=64, desc=(
+        "tiny fp32 decoder (2 layers, d 64), 32-token Markov prompt, greedy lookahead W=5 N=3 G=5, 64 new tokens")),
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def run_steps(make_session, sess, steps):
+    """Time exactly `steps` rounds (steps > 0; a finished generation is restarted
+    outside the clock) or, for steps == 0, every round of one fresh generation."""
+    import torch
+    tokens = 0
+    elapsed = 0.0
+    done = 0
+    if steps == 0:
+        sess = make_session()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        while True:
+            out = sess.la_step()
+            if not out:
+                break
+            tokens += len(out)
+            done += 1
+        torch.cuda.synchronize()
+        return tokens, time.perf_counter() - t0, sess, done
+    while done < steps:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        n_here = 0
+        while done < steps:
+            out = sess.la_step()
+            if not out:
+                break
+            tokens += len(out)
+            done += 1
+            n_here += 1
+        torch.cuda.synchronize()
+        elapsed += time.perf_counter() - t0
+        if done < steps:
+            sess = make_session()
+    return tokens, elapsed, sess, done
+
+
+def attention_op(reps=200, sets=16):
+    """Isolated lookahead-mask attention at its published shape, rotating inputs."""
+    import numpy as np
+    import torch
+    import exact_lookahead_decoding_amd.la as la
+    H = Hkv = 32
+    dh, p, S = 128, 1024, 4
+    levels = [list(range(100, 115))] * 4
+    desc = la.rows_desc(p, levels, S, 15, 7, 16, starts=[1, 1, 1, 1])
+    win = torch.zeros((4, 16), dtype=torch.int32, device="cuda")
+    win[:, :15] = torch.arange(100, 115, dtype=torch.int32, device="cuda")
+    cand = torch.arange(60, dtype=torch.int32, device="cuda")
+    rows, info = la.la_build_rows(desc, win, cand)
+    Q = info.Q
+    g = torch.Generator(device="cuda").manual_seed(0)
+    mk = lambda *s: torch.randn(*s, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    bufs = [(mk(Q, H, dh), mk(Hkv, p + 8, dh), mk(Hkv, p + 8, dh), mk(Hkv, Q, dh), mk(Hkv, Q, dh))
+            for _ in range(sets)]
+    ws = torch.empty(la.load().la_attention_workspace(Q, H, dh, p + 1 + info.maxp), dtype=torch.uint8,
+                     device="cuda")
+    outs = [torch.empty(Q, H, dh, dtype=torch.bfloat16, device="cuda") for _ in range(sets)]
+    for i in range(sets):
+        la.la_attention(*bufs[i], rows, info, p + 1, out=outs[i], workspace=ws)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for r in range(reps):
+        b = bufs[r % sets]
+        ev[r][0].record()
+        la.la_attention(*b, rows, info, p + 1, out=outs[r % sets], workspace=ws)
+        ev[r][1].record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    alg = 2 * Hkv * p * dh * 2 + Q * Hkv * dh * 2 * 2 + 2 * Q * H * dh * 2
+    gbs = alg / (ms * 1e-3) / 1e9
+    kv_gbs = (2 * Hkv * p * dh * 2) / (ms * 1e-3) / 1e9
+    return {"workload": "lookahead-mask attention, bf16, 32 heads x 128, prefix 1024, 121 rows (W=15 N=5 G=15)",
+            "avg_us": ms * 1e3, "algorithmic_bytes": alg, "achieved_GBps": gbs, "kv_stream_GBps": kv_gbs,
+            "peak_GBps": HBM_PEAK_GBS, "frac": gbs / HBM_PEAK_GBS, "reps": reps, "input_sets": sets}
+
+
+def cpu_baseline(wl, budget_rounds=2, prefix=32):
+    """The oracle as it stands, on host cores: a 64-token prefix, then `budget_rounds` rounds."""
+    import synthetic
+    from oracle.decode import lookahead_generate
+    from oracle.model import OracleModel
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    dims = synthetic.PRESETS[wl["model"]]
+    w = synthetic.model_weights(dims, 0)
+    prompt = synthetic.markov_prompt(dims.vocab, wl["prompt"], 0)[:prefix]
+    om = OracleModel(dims, w)
+    times = []
+    res = lookahead_generate(om, prompt, wl["W"], wl["N"], wl["G"], 1 + budget_rounds, round_times=times)
+    toks = len(res["tokens"]) - 1
+    secs = sum(times)
+    return {"value": toks / secs, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"numpy fp64 oracle, same model and W/N/G, prompt truncated to its first {prefix} tokens, "
+                      f"prefill untimed, then {budget_rounds} rounds ({toks} tokens) in {secs:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=0,
+                    help="rounds to time; 0 (default) times one complete generation of the workload")
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama7b_w7n5g7", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-attn", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the lookahead round runs on a single MI355X (got --gpus {args.gpus}); "
+              f"lookahead parallelism across GPUs is not part of this build", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import synthetic
+    import exact_lookahead_decoding_amd.la as la
+    la.load()
+    torch.cuda.set_device(0)
+    wl = WORKLOADS[args.workload]
+    dims = synthetic.PRESETS[wl["model"]]
+    t = time.time()
+    model = la.DeviceModel(dims, seed=0)
+    log(f"weights on device: {model.weight_bytes / 1e9:.2f} GB in {time.time() - t:.1f} s")
+    prompt = synthetic.markov_prompt(dims.vocab, wl["prompt"], 0)
+
+    def make(ar=False, profile=False):
+        s = la.Session(model, prompt, W=wl["W"], N=wl["N"], G=wl["G"], max_new=wl["max_new"], ar_only=ar)
+        if profile:
+            s.la_profile(True)
+        return s
+
+    sess = make()
+    for _ in range(args.warmup):
+        sess.la_step()
+    tokens, secs, sess, steps = run_steps(make, sess, args.steps)
+    value = tokens / secs
+    log(f"lookahead: {tokens} tokens in {steps} rounds, {secs * 1e3 / steps:.3f} ms/round, {value:.1f} tokens/s")
+    # autoregressive decoding with the same kernels
+    ar = make(ar=True)
+    for _ in range(args.warmup):
+        ar.la_step()
+    ar_tokens, ar_secs, _, ar_steps = run_steps(lambda: make(ar=True), ar, args.steps)
+    ar_tps = ar_tokens / ar_secs
+    log(f"autoregressive: {ar_tokens} tokens in {ar_steps} rounds, {ar_tps:.1f} tokens/s")
+    # dominant kernel: GEMM weight stream, events around each launch
+    # a second pass with HIP events around every GEMM / attention launch (one
+    # context's totals; with --steps K the first context's rounds are the ones read)
+    prof = make(profile=True)
+    for _ in range(args.warmup):
+        prof.la_step()
+    prof.la_profile(True)
+    _, prof_secs, prof_end, _ = run_steps(lambda: make(profile=True), prof, args.steps)
+    pr = (prof_end if args.steps == 0 else prof).la_profile_read()
+    gemm_avg_ms = pr["gemm_ms"] / max(1, pr["gemm_launches"])
+    gemm_bytes = pr["gemm_bytes"] / max(1, pr["gemm_launches"])
+    achieved = pr["gemm_bytes"] / (pr["gemm_ms"] * 1e-3) / 1e9 if pr["gemm_ms"] > 0 else 0.0
+    attn_in_step = pr["attn_bytes"] / (pr["attn_ms"] * 1e-3) / 1e9 if pr["attn_ms"] > 0 else 0.0
+    log(f"gemm: {pr['gemm_launches']} launches, avg {gemm_avg_ms * 1e3:.1f} us, {achieved:.0f} GB/s; "
+        f"attention in step: {pr['attn_launches']} launches, avg {pr['attn_ms'] / max(1, pr['attn_launches']) * 1e3:.1f} us, "
+        f"{attn_in_step:.0f} GB/s; share of step: gemm {pr['gemm_ms'] / (secs * 1e3) * 100:.0f}%")
+    line = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+        "warmup": args.warmup, "ms_per_step": secs * 1e3 / steps, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if dims.dtype == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": wl["desc"], "W": wl["W"], "N": wl["N"], "G": wl["G"], "prompt_tokens": wl["prompt"],
+                   "max_new": wl["max_new"], "verify": "greedy", "batch": 1},
+        "tokens_per_round": tokens / steps,
+        "ar_tokens_per_s": ar_tps,
+        "speedup_vs_ar": value / ar_tps,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "la_gemm_kernel (+ split reduction), all projections, MLP and LM head of a round",
+                     "avg_launch_us": gemm_avg_ms * 1e3, "algorithmic_bytes_per_launch": gemm_bytes,
+                     "launches": pr["gemm_launches"]},
+        "attention_in_step": {"achieved_GBps": attn_in_step, "avg_launch_us":
+                              pr["attn_ms"] / max(1, pr["attn_launches"]) * 1e3, "launches": pr["attn_launches"]},
+    }
+    if not args.no_attn:
+        a = attention_op()
+        log(f"lookahead attention op: {a['avg_us']:.2f} us, {a['achieved_GBps']:.0f} GB/s ({a['frac'] * 100:.1f}%)")
+        line["lookahead_attn"] = a
+    if not args.no_cpu_baseline:
+        t = time.time()
+        line["cpu_baseline"] = cpu_baseline(wl)
+        log(f"cpu baseline: {line['cpu_baseline']['value']:.4f} tokens/s ({time.time() - t:.0f} s)")
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

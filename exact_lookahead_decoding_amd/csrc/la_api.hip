@@ -63,7 +63,46 @@ struct la_ctx {
   la_accept vacc;
   la_stats_t stats;
   std::string err;
+  // opt-in kernel timing
+  bool prof = false;
+  la_profile_t pr;
+  struct Mark { hipEvent_t a, b; int kind; double bytes, flops; };
+  std::vector<Mark> marks;      // recorded this round
+  std::vector<hipEvent_t> evpool;
+  size_t evnext = 0;
 };
+
+static hipEvent_t prof_event(la_ctx* c) {
+  if (c->evnext == c->evpool.size()) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    c->evpool.push_back(e);
+  }
+  return c->evpool[c->evnext++];
+}
+
+// bracket a launch: call with begin=true before it, begin=false after it
+static void prof_mark(la_ctx* c, bool begin, int kind, double bytes, double flops) {
+  if (!c->prof) return;
+  hipEvent_t e = prof_event(c);
+  if (!e) return;
+  hipEventRecord(e, c->st);
+  if (begin) c->marks.push_back({e, nullptr, kind, bytes, flops});
+  else c->marks.back().b = e;
+}
+
+// called after a stream synchronisation: fold the recorded pairs into the totals
+static void prof_collect(la_ctx* c) {
+  for (auto& m : c->marks) {
+    float ms = 0.f;
+    if (m.b && hipEventElapsedTime(&ms, m.a, m.b) == hipSuccess) {
+      if (m.kind == 0) { c->pr.gemm_ms += ms; c->pr.gemm_bytes += m.bytes; c->pr.gemm_flops += m.flops; c->pr.gemm_launches++; }
+      else { c->pr.attn_ms += ms; c->pr.attn_bytes += m.bytes; c->pr.attn_flops += m.flops; c->pr.attn_launches++; }
+    }
+  }
+  c->marks.clear();
+  c->evnext = 0;
+}
 
 static int fail(la_ctx* c, int code, const char* fmt, ...) {
   char buf[512];
@@ -233,7 +272,12 @@ static int gemm(la_ctx* c, int epi, const void* X, const void* W, void* Y, const
   a.splits = la_gemm_splits(N, K, c->dtype, epi == LA_EPI_SWIGLU);
   a.up_off = up_off;
   a.pcols = epi == LA_EPI_SWIGLU ? 2 * N : N;
+  const double wrows = epi == LA_EPI_SWIGLU ? 2.0 * N : (double)N;
+  const double ybytes = epi == LA_EPI_F32 ? 4.0 : (double)c->esz;
+  const double bytes = (wrows * K + (double)M * K) * c->esz + (double)M * N * ybytes * (epi == LA_EPI_RESID ? 2 : 1);
+  prof_mark(c, true, 0, bytes, 2.0 * M * wrows * K);
   const int rc = la_gemm_launch(c->dtype, epi, a, c->st);
+  prof_mark(c, false, 0, 0, 0);
   if (rc) return fail(c, rc == -2 ? LA_EINVAL : LA_EDEVICE, "gemm launch failed (M=%d N=%d K=%d rc=%d)", M, N, K, rc);
   return LA_OK;
 }
@@ -273,7 +317,16 @@ static int forward(la_ctx* c, int M, const int32_t* tok, const int32_t* pos, con
     la_qkv_post_launch(c->dtype, c->qkv, c->rope, pos, M, c->H, c->Hkv, c->dh, c->q, kc, vc, c->t_cap, cache_row0,
                        n_direct, kw, vw, c->ws_cap, c->st);
     at.kc = kc; at.vc = vc; at.kw = kw; at.vw = vw;
-    if ((rc = la_attention_launch(c->dtype, at, c->st))) return fail(c, LA_EDEVICE, "attention launch failed (%d)", rc);
+    {
+      // committed K/V read once (positions below shared_end), each packed row's K/V, Q in, O out
+      const double kvrow = 2.0 * c->Hkv * c->dh * c->esz;
+      const double bytes = shared_end * kvrow + (double)(M - n_direct) * kvrow + 2.0 * M * c->H * c->dh * c->esz;
+      const double flops = 4.0 * M * c->H * c->dh * (double)(max_pos + 1);
+      prof_mark(c, true, 1, bytes, flops);
+    }
+    rc = la_attention_launch(c->dtype, at, c->st);
+    prof_mark(c, false, 1, 0, 0);
+    if (rc) return fail(c, LA_EDEVICE, "attention launch failed (%d)", rc);
     if ((rc = gemm(c, LA_EPI_RESID, c->o, wo, c->x, c->x, M, c->d, c->H * c->dh, 0))) return rc;
     la_rmsnorm_launch(c->dtype, c->x, mlp_norm, c->nrm, nullptr, M, c->d, c->dims.eps, c->st);
     if ((rc = gemm(c, LA_EPI_SWIGLU, c->nrm, wgu, c->act, nullptr, M, c->F, c->d, c->F))) return rc;
@@ -391,7 +444,27 @@ extern "C" int la_init(const la_config* cfg, const la_model_dims* dims, const la
   return LA_OK;
 }
 
-extern "C" void la_destroy(la_ctx* c) { delete c; }
+extern "C" void la_destroy(la_ctx* c) {
+  if (!c) return;
+  for (auto e : c->evpool) hipEventDestroy(e);
+  delete c;
+}
+
+extern "C" int la_profile(la_ctx* c, int32_t enable) {
+  if (!c) return fail(nullptr, LA_EINVAL, "null ctx");
+  if (c->pending) return fail(c, LA_ESTATE, "a predicted round is pending");
+  c->prof = enable != 0;
+  memset(&c->pr, 0, sizeof c->pr);
+  c->marks.clear();
+  c->evnext = 0;
+  return LA_OK;
+}
+
+extern "C" int la_profile_read(const la_ctx* c, la_profile_t* out) {
+  if (!c || !out) return fail(nullptr, LA_EINVAL, "null argument");
+  *out = c->pr;
+  return LA_OK;
+}
 
 // ------------------------------------------------------------------ round
 
@@ -483,6 +556,7 @@ extern "C" int la_verify(la_ctx* c, const float* logits, int32_t n_inp, const in
   HIPCHK(c, hipMemcpyAsync(&a, c->acc, sizeof a, hipMemcpyDeviceToHost, c->st));
   if (z_host && n_inp > 0) HIPCHK(c, hipMemcpyAsync(z_host, zdev, (size_t)n_inp * 4, hipMemcpyDeviceToHost, c->st));
   HIPCHK(c, hipStreamSynchronize(c->st));
+  prof_collect(c);
   memset(out, 0, sizeof *out);
   out->round_id = rid;
   out->h = a.h;

@@ -75,6 +75,12 @@ class la_state_t(C.Structure):
                 ("level_sizes", C.c_int32 * LA_MAX_N), ("warm", C.c_int32), ("win_stride", C.c_int32)]
 
 
+class la_profile_t(C.Structure):
+    _fields_ = [("gemm_ms", C.c_double), ("gemm_bytes", C.c_double), ("gemm_flops", C.c_double),
+                ("attn_ms", C.c_double), ("attn_bytes", C.c_double), ("attn_flops", C.c_double),
+                ("gemm_launches", C.c_int64), ("attn_launches", C.c_int64)]
+
+
 class la_rows_desc(C.Structure):
     _fields_ = [("p", C.c_int32), ("R", C.c_int32), ("sizes", C.c_int32 * LA_MAX_N),
                 ("starts", C.c_int32 * LA_MAX_N), ("C", C.c_int32), ("S", C.c_int32), ("x_t", C.c_int32),
@@ -91,7 +97,7 @@ class la_rows_info(C.Structure):
 EXPORTS = ["la_query_sizes", "la_init", "la_destroy", "la_step", "la_generate", "la_predict", "la_verify",
            "la_commit", "la_pool_lookup", "la_pool_insert", "la_get_state", "la_stats", "la_last_error",
            "la_rows_query", "la_build_rows", "la_attention_workspace", "la_attention", "la_linear_workspace",
-           "la_linear"]
+           "la_linear", "la_profile", "la_profile_read"]
 LA_LINEAR_STORE, LA_LINEAR_RESIDUAL, LA_LINEAR_SWIGLU, LA_LINEAR_F32 = 0, 1, 2, 3
 
 _lib = None
@@ -132,6 +138,8 @@ def load() -> C.CDLL:
                           C.c_size_t, VP], I32),
         "la_linear_workspace": ([I32, I32, I32, I32, I32], C.c_size_t),
         "la_linear": ([I32, I32, VP, VP, VP, VP, I32, I32, I32, VP, C.c_size_t, VP], I32),
+        "la_profile": ([VP, I32], I32),
+        "la_profile_read": ([VP, P(la_profile_t)], I32),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -334,6 +342,14 @@ class Session:
         levels = [None if st.level_sizes[r] == 0 else [int(t) for t in win[r, : st.level_sizes[r]]] for r in range(R)]
         return {"round_id": st.round_id, "kv_len": st.kv_len, "n_out": st.n_out, "levels": levels,
                 "warm": bool(st.warm), "output": [int(t) for t in outb[: st.n_out]]}
+
+    def la_profile(self, enable=True):
+        _check(load().la_profile(self.ctx, int(bool(enable))), self.ctx)
+
+    def la_profile_read(self):
+        p = la_profile_t()
+        _check(load().la_profile_read(self.ctx, C.byref(p)), self.ctx)
+        return {f: getattr(p, f) for f, _ in la_profile_t._fields_}
 
     def la_stats(self):
         s = la_stats_t()

@@ -217,6 +217,21 @@ int la_pool_insert(la_ctx* ctx, const int32_t* keys, const int32_t* suffixes, in
 int la_get_state(la_ctx* ctx, la_state_t* st, int32_t* window, int32_t* output, int32_t out_cap);
 
 int la_stats(const la_ctx* ctx, la_stats_t* out);
+
+/* Opt-in kernel timing: while enabled, every GEMM launch (projections, MLP,
+ * LM head, with their split reductions) and every attention launch (with
+ * its span merge) of the context's rounds is bracketed by HIP events on the
+ * context's stream; elapsed times are accumulated at each verification sync,
+ * together with the algorithmic bytes and flops of each launch (weights +
+ * rows in + rows out for a GEMM; committed K/V read + branch K/V + Q + O
+ * for attention).  la_profile(ctx, 1) clears the totals. */
+typedef struct la_profile_t {
+  double gemm_ms, gemm_bytes, gemm_flops;
+  double attn_ms, attn_bytes, attn_flops;
+  int64_t gemm_launches, attn_launches;
+} la_profile_t;
+int la_profile(la_ctx* ctx, int32_t enable);
+int la_profile_read(const la_ctx* ctx, la_profile_t* out);
 const char* la_last_error(const la_ctx* ctx);
 
 /* ------------------------------------------------ context-free operators */

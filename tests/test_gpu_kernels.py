@@ -368,7 +368,14 @@ def test_linear_matches_oracle_and_is_batch_invariant(case):
         want = linear_swiglu(f64(X), f64(W)[:N], f64(W)[N:], "bf16")
     else:
         want = logits_f32(f64(X), f64(W))
-    err = np.max(np.abs(got - want))
-    print(f"linear {epi} M={M} N={N} K={K}: max abs err {err:.3g}", flush=True)
-    assert err <= 2e-2
+    diff = np.abs(got - want)
+    err = diff.max()
+    if epi == "f32":
+        assert err <= 2e-2
+    else:
+        # one bf16 rounding of an fp32 vs fp64 accumulation: 2e-2, or one bf16 ulp where values exceed 2.56
+        ulp = np.ldexp(1.0, np.frexp(np.abs(want))[1] - 8)
+        assert np.all(diff <= np.maximum(2e-2, ulp))
+        assert np.mean(diff > 0) < 1e-3             # flips only where the exact value sits at a rounding tie
+    print(f"linear {epi} M={M} N={N} K={K}: max abs err {err:.3g}, differing {np.mean(diff > 0):.2e}", flush=True)
     assert np.array_equal(got1[0], got[0])          # a row alone == the same row among M
