@@ -286,7 +286,7 @@ static int gemm(la_ctx* c, int epi, const void* X, const void* W, void* Y, const
 // the others to workspace rows m - n_direct.  Keys below shared_end come
 // from the cache.  Logits (fp32) of logit_rows[0..n_logit) land in c->logits.
 static int forward(la_ctx* c, int M, const int32_t* tok, const int32_t* pos, const int32_t* branch,
-                   const int32_t* path, const int32_t* path_len, int maxp, int n_direct, int cache_row0,
+                   const int32_t* path, const int32_t* path_len, int nb, int maxp, int n_direct, int cache_row0,
                    int shared_end, int max_pos, const int32_t* logit_rows, int n_logit) {
   const int esz = c->esz;
   const size_t kvl = (size_t)c->Hkv * c->t_cap * c->dh;   // elements per layer
@@ -298,6 +298,9 @@ static int forward(la_ctx* c, int M, const int32_t* tok, const int32_t* pos, con
   at.Q = M; at.H = c->H; at.Hkv = c->Hkv; at.dh = c->dh; at.T_cap = c->t_cap; at.ws_cap = c->ws_cap; at.maxp = maxp;
   at.shared_end = shared_end;
   at.n_spans = la_attention_spans(max_pos);
+  at.max_pos = max_pos;
+  at.nb = nb;
+  at.n_ws = M - n_direct;
   at.scale = 1.0f / sqrtf((float)c->dh);
   if (at.n_spans > c->spans_max) return fail(c, LA_EOVERFLOW, "attention spans %d > %d", at.n_spans, c->spans_max);
   for (int l = 0; l < c->L; ++l) {
@@ -423,8 +426,8 @@ extern "C" int la_init(const la_config* cfg, const la_model_dims* dims, const la
     CK(hipMemcpyAsync(c->pf_path, zero, 4, hipMemcpyHostToDevice, c->st));
     CK(hipMemcpyAsync(c->pf_logit, zero + 1, 4, hipMemcpyHostToDevice, c->st));
     const bool last = c0 + M >= prompt_len;
-    rc = forward(c, M, c->pf_tok, c->pf_pos, c->pf_branch, c->pf_path, c->pf_path, 1, M, c0, c0 + M, c0 + M - 1,
-                 c->pf_logit, last ? 1 : 0);
+    rc = forward(c, M, c->pf_tok, c->pf_pos, c->pf_branch, c->pf_path, c->pf_path, 1, 1, M, c0, c0 + M,
+                 c0 + M - 1, c->pf_logit, last ? 1 : 0);
     if (rc) { g_err = c->err; return bail(rc); }
     CK(hipStreamSynchronize(c->st));        // the host-side chunk arrays are reused
   }
@@ -504,8 +507,8 @@ extern "C" int la_predict(la_ctx* c, la_round_info* info) {
   rows_layout(L, c->rowbuf, &c->rows, nullptr);
   la_build_rows_launch(L, x_t, c->win[c->cur], c->wstride, c->cand, c->rows, c->st);
   const int maxpos = p + L.maxp;             // a row's branch path covers its own position
-  int rc = forward(c, L.Q, c->rows.tok, c->rows.pos, c->rows.branch, c->rows.path, c->rows.path_len, L.maxp, 1, p,
-                   p + 1, maxpos, c->rows.logit_rows, L.n_logit);
+  int rc = forward(c, L.Q, c->rows.tok, c->rows.pos, c->rows.branch, c->rows.path, c->rows.path_len, L.NB, L.maxp,
+                   1, p, p + 1, maxpos, c->rows.logit_rows, L.n_logit);
   if (rc) return rc;
   c->lay = L;
   c->pending = true;
@@ -795,6 +798,7 @@ extern "C" int la_attention(int32_t dtype, const void* q, const void* k_cache, c
   a.path_len = rows + info->off_path_len;
   a.Q = info->Q; a.H = H; a.Hkv = Hkv; a.dh = dh; a.T_cap = t_cap; a.ws_cap = ws_cap > 0 ? ws_cap : 1;
   a.maxp = info->maxp; a.shared_end = shared_end; a.n_spans = (int)spans;
+  a.max_pos = max_pos; a.nb = info->NB; a.n_ws = info->Q - 1;
   a.scale = 1.0f / sqrtf((float)dh);
   const int rc = la_attention_launch(dtype == LA_DTYPE_BF16 ? LA_DT_BF16 : LA_DT_F32, a, (hipStream_t)stream);
   if (rc) return fail(nullptr, rc == -2 ? LA_EINVAL : LA_EDEVICE, "attention launch failed");

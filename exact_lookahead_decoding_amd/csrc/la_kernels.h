@@ -67,6 +67,10 @@ struct LaAttnArgs {
   int Q, H, Hkv, dh, T_cap, ws_cap, maxp;
   int shared_end;       // keys [0, shared_end) come from the cache, later ones from the row's path
   int n_spans;
+  int max_pos;          // largest row position (bounds the spans that reach the packed rows)
+  int nb;               // branches in the path table
+  int n_ws;             // workspace rows written by this call (packed rows other than the ordinary row)
+  int rsplit;           // set by the launcher
   float scale;
 };
 int la_attention_launch(int dtype, const LaAttnArgs& a, hipStream_t st);

@@ -11,53 +11,131 @@
 #include "la_common.h"
 #include "la_kernels.h"
 
-template <typename T>
+// Rows are moved as 16-byte vectors; a thread issues all of its loads before
+// using any of them.
+template <typename T, int VPT>
 __global__ void __launch_bounds__(256) embed_kernel(const T* E, const int32_t* tok, T* x, int d) {
   const int m = blockIdx.x;
-  const T* src = E + (size_t)tok[m] * d;
-  T* dst = x + (size_t)m * d;
-  for (int i = threadIdx.x; i < d; i += 256) dst[i] = src[i];
+  const int nv = d * (int)sizeof(T) / 16;
+  const u32x4* src = (const u32x4*)(E + (size_t)tok[m] * d);
+  u32x4* dst = (u32x4*)(x + (size_t)m * d);
+  u32x4 r[VPT];
+#pragma unroll
+  for (int j = 0; j < VPT; ++j) {
+    const int v = threadIdx.x + 256 * j;
+    if (v < nv) r[j] = src[v];
+  }
+#pragma unroll
+  for (int j = 0; j < VPT; ++j) {
+    const int v = threadIdx.x + 256 * j;
+    if (v < nv) dst[v] = r[j];
+  }
+}
+
+static int vpt_for(int d, int esz) {
+  const int nv = d * esz / 16;
+  const int v = (nv + 255) / 256;
+  return v <= 1 ? 1 : v <= 2 ? 2 : v <= 4 ? 4 : 8;
+}
+
+template <typename T, int VPT>
+static void embed_t(const void* E, const int32_t* tok, void* x, int M, int d, hipStream_t st) {
+  hipLaunchKernelGGL((embed_kernel<T, VPT>), dim3(M), dim3(256), 0, st, (const T*)E, tok, (T*)x, d);
 }
 
 void la_embed_launch(int dtype, const void* E, const int32_t* tok, void* x, int M, int d, hipStream_t st) {
   if (M <= 0) return;
-  if (dtype == LA_DT_BF16)
-    hipLaunchKernelGGL(embed_kernel<bf16_t>, dim3(M), dim3(256), 0, st, (const bf16_t*)E, tok, (bf16_t*)x, d);
-  else
-    hipLaunchKernelGGL(embed_kernel<float>, dim3(M), dim3(256), 0, st, (const float*)E, tok, (float*)x, d);
+  const int esz = dtype == LA_DT_BF16 ? 2 : 4;
+  switch (vpt_for(d, esz) * 2 + (dtype == LA_DT_BF16)) {
+    case 2: embed_t<float, 1>(E, tok, x, M, d, st); break;
+    case 3: embed_t<bf16_t, 1>(E, tok, x, M, d, st); break;
+    case 4: embed_t<float, 2>(E, tok, x, M, d, st); break;
+    case 5: embed_t<bf16_t, 2>(E, tok, x, M, d, st); break;
+    case 8: embed_t<float, 4>(E, tok, x, M, d, st); break;
+    case 9: embed_t<bf16_t, 4>(E, tok, x, M, d, st); break;
+    case 16: embed_t<float, 8>(E, tok, x, M, d, st); break;
+    default: embed_t<bf16_t, 8>(E, tok, x, M, d, st); break;
+  }
 }
 
-// y[m] = T(x[src] * rs * w),  rs = 1/sqrt(mean(x^2) + eps), src = rows ? rows[m] : m
-template <typename T>
+// y[m] = T(x[src] * rs * w),  rs = 1/sqrt(mean(x^2) + eps), src = rows ? rows[m] : m.
+// The sum of squares has one fixed order for every row: each thread's
+// elements in index order, then a butterfly within the wave, then the four
+// wave sums in a fixed grouping.
+template <typename T, int VPT>
 __global__ void __launch_bounds__(256) rmsnorm_kernel(const T* x, const T* w, T* y, const int32_t* rows, int d,
                                                       float eps) {
+  constexpr int E = 16 / sizeof(T);
   __shared__ float red[4];
   const int m = blockIdx.x;
   const int src = rows ? rows[m] : m;
-  const T* xr = x + (size_t)src * d;
+  const int nv = d / E;
+  const u32x4* xr = (const u32x4*)(x + (size_t)src * d);
+  const u32x4* wr = (const u32x4*)w;
+  u32x4 xv[VPT], wv[VPT];
+#pragma unroll
+  for (int j = 0; j < VPT; ++j) {
+    const int v = threadIdx.x + 256 * j;
+    if (v < nv) {
+      xv[j] = xr[v];
+      wv[j] = wr[v];
+    }
+  }
   float ss = 0.f;
-  for (int i = threadIdx.x; i < d; i += 256) {
-    const float v = ld<T>(xr + i);
-    ss += v * v;
+#pragma unroll
+  for (int j = 0; j < VPT; ++j) {
+    const int v = threadIdx.x + 256 * j;
+    if (v < nv) {
+      const T* e = (const T*)&xv[j];
+#pragma unroll
+      for (int q = 0; q < E; ++q) {
+        const float f = ld<T>(e + q);
+        ss += f * f;
+      }
+    }
   }
   for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
   __syncthreads();
   const float tot = (red[0] + red[1]) + (red[2] + red[3]);
   const float rs = 1.0f / sqrtf(tot / (float)d + eps);
-  T* yr = y + (size_t)m * d;
-  for (int i = threadIdx.x; i < d; i += 256) st<T>(yr + i, ld<T>(xr + i) * rs * ld<T>(w + i));
+  u32x4* yr = (u32x4*)(y + (size_t)m * d);
+#pragma unroll
+  for (int j = 0; j < VPT; ++j) {
+    const int v = threadIdx.x + 256 * j;
+    if (v < nv) {
+      const T* e = (const T*)&xv[j];
+      const T* we = (const T*)&wv[j];
+      u32x4 ov;
+      T* oe = (T*)&ov;
+#pragma unroll
+      for (int q = 0; q < E; ++q) st<T>(oe + q, ld<T>(e + q) * rs * ld<T>(we + q));
+      yr[v] = ov;
+    }
+  }
+}
+
+template <typename T, int VPT>
+static void rms_t(const void* x, const void* w, void* y, const int32_t* rows, int M, int d, float eps,
+                  hipStream_t st) {
+  hipLaunchKernelGGL((rmsnorm_kernel<T, VPT>), dim3(M), dim3(256), 0, st, (const T*)x, (const T*)w, (T*)y, rows, d,
+                     eps);
 }
 
 void la_rmsnorm_launch(int dtype, const void* x, const void* w, void* y, const int32_t* rows, int M, int d,
                        float eps, hipStream_t st) {
   if (M <= 0) return;
-  if (dtype == LA_DT_BF16)
-    hipLaunchKernelGGL(rmsnorm_kernel<bf16_t>, dim3(M), dim3(256), 0, st, (const bf16_t*)x, (const bf16_t*)w,
-                       (bf16_t*)y, rows, d, eps);
-  else
-    hipLaunchKernelGGL(rmsnorm_kernel<float>, dim3(M), dim3(256), 0, st, (const float*)x, (const float*)w,
-                       (float*)y, rows, d, eps);
+  const int esz = dtype == LA_DT_BF16 ? 2 : 4;
+  switch (vpt_for(d, esz) * 2 + (dtype == LA_DT_BF16)) {
+    case 2: rms_t<float, 1>(x, w, y, rows, M, d, eps, st); break;
+    case 3: rms_t<bf16_t, 1>(x, w, y, rows, M, d, eps, st); break;
+    case 4: rms_t<float, 2>(x, w, y, rows, M, d, eps, st); break;
+    case 5: rms_t<bf16_t, 2>(x, w, y, rows, M, d, eps, st); break;
+    case 8: rms_t<float, 4>(x, w, y, rows, M, d, eps, st); break;
+    case 9: rms_t<bf16_t, 4>(x, w, y, rows, M, d, eps, st); break;
+    case 16: rms_t<float, 8>(x, w, y, rows, M, d, eps, st); break;
+    default: rms_t<bf16_t, 8>(x, w, y, rows, M, d, eps, st); break;
+  }
 }
 
 // cos/sin of t * theta^(-2i/dh), evaluated in fp64 and stored as fp32

@@ -23,20 +23,42 @@
 #include "la_kernels.h"
 
 // ---------------------------------------------------------------- argmax
-__global__ void __launch_bounds__(256) argmax_kernel(const float* logits, int V, int32_t* out) {
-  __shared__ float bv[256];
-  __shared__ int bi[256];
+// One 1024-thread block per row; each thread keeps 8 float4 loads in flight
+// and scans its elements in index order (first maximum kept), then the block
+// reduces with ties going to the lower index.
+__global__ void __launch_bounds__(1024) argmax_kernel(const float* logits, int V, int32_t* out) {
+  __shared__ float bv[1024];
+  __shared__ int bi[1024];
   const float* x = logits + (size_t)blockIdx.x * V;
   float best = -__builtin_inff();
   int idx = 0x7fffffff;
-  for (int i = threadIdx.x; i < V; i += 256) {
-    const float v = x[i];
-    if (v > best) { best = v; idx = i; }          // strided scan keeps the lowest index on ties
+  const int nv = V / 4;
+  for (int base = 0; base < nv; base += 1024 * 8) {
+    float4 r[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int v = base + threadIdx.x + 1024 * j;
+      if (v < nv) r[j] = ((const float4*)x)[v];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int v = base + threadIdx.x + 1024 * j;
+      if (v < nv) {
+        if (r[j].x > best) { best = r[j].x; idx = 4 * v; }
+        if (r[j].y > best) { best = r[j].y; idx = 4 * v + 1; }
+        if (r[j].z > best) { best = r[j].z; idx = 4 * v + 2; }
+        if (r[j].w > best) { best = r[j].w; idx = 4 * v + 3; }
+      }
+    }
+  }
+  for (int i = 4 * nv + threadIdx.x; i < V; i += 1024) {       // tail when V is not a multiple of 4
+    const float f = x[i];
+    if (f > best || (f == best && i < idx)) { best = f; idx = i; }
   }
   bv[threadIdx.x] = best;
   bi[threadIdx.x] = idx;
   __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
+  for (int s = 512; s > 0; s >>= 1) {
     if (threadIdx.x < s) {
       const float v2 = bv[threadIdx.x + s];
       const int i2 = bi[threadIdx.x + s];
@@ -52,7 +74,7 @@ __global__ void __launch_bounds__(256) argmax_kernel(const float* logits, int V,
 
 void la_argmax_launch(const float* logits, int rows, int V, int32_t* out, hipStream_t st) {
   if (rows <= 0) return;
-  hipLaunchKernelGGL(argmax_kernel, dim3(rows), dim3(256), 0, st, logits, V, out);
+  hipLaunchKernelGGL(argmax_kernel, dim3(rows), dim3(1024), 0, st, logits, V, out);
 }
 
 // ---------------------------------------------------------------- greedy
