@@ -34,7 +34,7 @@ struct la_ctx {
   int dtype, esz;
   int L, d, H, Hkv, dh, F, V, qkvdim;
   int R, S;
-  int t_cap, q_max, m_max, ws_cap, n_logit_max, nb_max, maxp_max, words_max, spans_max, wstride, rows_words;
+  int t_cap, q_max, m_max, ws_cap, n_logit_max, nb_max, maxp_max, words_max, parts, wstride, rows_words;
   int rope_rows;      // positions reach kv_len + maxp, beyond the K/V capacity
   // device
   char* kc;
@@ -179,7 +179,7 @@ static void setup_dims(la_ctx* c) {
   c->m_max = std::max(c->q_max, PREFILL_CHUNK);
   c->ws_cap = c->q_max;
   c->t_cap = g.max_prompt + g.max_new + 16;
-  c->spans_max = la_attention_spans(c->t_cap + c->q_max);
+  c->parts = la_attention_parts();
   c->rope_rows = c->t_cap + c->q_max + 1;
   c->wstride = g.W + g.N;
   c->rows_words = 8 * c->q_max + c->nb_max * c->maxp_max + c->nb_max + c->n_logit_max + c->q_max * c->words_max;
@@ -215,8 +215,8 @@ static size_t carve(la_ctx* c, char* base) {
   c->kw = take((size_t)c->L * c->Hkv * c->ws_cap * c->dh * e);
   c->vw = take((size_t)c->L * c->Hkv * c->ws_cap * c->dh * e);
   c->gemm_p = (float*)take(std::max<size_t>(gemm_partial_floats(c), 1) * 4);
-  c->attn_po = (float*)take((size_t)c->spans_max * c->H * c->m_max * c->dh * 4);
-  c->attn_pml = (float*)take((size_t)c->spans_max * c->H * c->m_max * 2 * 4);
+  c->attn_po = (float*)take((size_t)c->parts * c->H * c->m_max * c->dh * 4);
+  c->attn_pml = (float*)take((size_t)c->parts * c->H * c->m_max * 2 * 4);
   c->logits = (float*)take((size_t)c->n_logit_max * c->V * 4);
   c->rope = (float2*)take((size_t)c->rope_rows * (c->dh / 2) * sizeof(float2));
   c->rowbuf = (int32_t*)take((size_t)c->rows_words * 4);
@@ -297,12 +297,10 @@ static int forward(la_ctx* c, int M, const int32_t* tok, const int32_t* pos, con
   at.pos = pos; at.branch = branch; at.path = path; at.path_len = path_len;
   at.Q = M; at.H = c->H; at.Hkv = c->Hkv; at.dh = c->dh; at.T_cap = c->t_cap; at.ws_cap = c->ws_cap; at.maxp = maxp;
   at.shared_end = shared_end;
-  at.n_spans = la_attention_spans(max_pos);
   at.max_pos = max_pos;
   at.nb = nb;
   at.n_ws = M - n_direct;
   at.scale = 1.0f / sqrtf((float)c->dh);
-  if (at.n_spans > c->spans_max) return fail(c, LA_EOVERFLOW, "attention spans %d > %d", at.n_spans, c->spans_max);
   for (int l = 0; l < c->L; ++l) {
     const char* attn_norm = wptr(c->w.attn_norm, c->d, l, esz);
     const char* mlp_norm = wptr(c->w.mlp_norm, c->d, l, esz);
@@ -773,8 +771,9 @@ extern "C" int la_build_rows(const la_rows_desc* desc, const int32_t* window, co
 }
 
 extern "C" size_t la_attention_workspace(int32_t Q, int32_t H, int32_t dh, int32_t max_pos) {
-  const size_t spans = (size_t)la_attention_spans(max_pos);
-  return spans * H * Q * ((size_t)dh + 2) * 4 + 512;
+  (void)max_pos;
+  const size_t parts = (size_t)la_attention_parts();
+  return parts * H * Q * ((size_t)dh + 2) * 4 + 512;
 }
 
 extern "C" int la_attention(int32_t dtype, const void* q, const void* k_cache, const void* v_cache, int32_t t_cap,
@@ -786,18 +785,18 @@ extern "C" int la_attention(int32_t dtype, const void* q, const void* k_cache, c
   if (H < 1 || Hkv < 1 || H % Hkv || shared_end < 1 || shared_end > t_cap) return fail(nullptr, LA_EINVAL, "bad shape");
   if (info->Q > 1 && (!k_ws || !v_ws || ws_cap < info->Q - 1)) return fail(nullptr, LA_EINVAL, "workspace K/V too small");
   // positions never exceed shared_end + maxp (a row's path covers its own position)
-  const int max_pos = shared_end + info->maxp;
+  const int max_pos = shared_end - 1 + info->maxp;
   const size_t need = la_attention_workspace(info->Q, H, dh, max_pos);
   if (workspace_bytes < need) return fail(nullptr, LA_EOVERFLOW, "workspace %zu < %zu bytes", workspace_bytes, need);
   LaAttnArgs a{};
   a.q = q; a.kc = k_cache; a.vc = v_cache; a.kw = k_ws ? k_ws : k_cache; a.vw = v_ws ? v_ws : v_cache; a.o = out;
-  const size_t spans = (size_t)la_attention_spans(max_pos);
+  const size_t parts = (size_t)la_attention_parts();
   a.part_o = (float*)workspace;
-  a.part_ml = (float*)((char*)workspace + spans * H * info->Q * (size_t)dh * 4);
+  a.part_ml = (float*)((char*)workspace + parts * H * info->Q * (size_t)dh * 4);
   a.pos = rows + info->off_pos; a.branch = rows + info->off_branch; a.path = rows + info->off_path;
   a.path_len = rows + info->off_path_len;
   a.Q = info->Q; a.H = H; a.Hkv = Hkv; a.dh = dh; a.T_cap = t_cap; a.ws_cap = ws_cap > 0 ? ws_cap : 1;
-  a.maxp = info->maxp; a.shared_end = shared_end; a.n_spans = (int)spans;
+  a.maxp = info->maxp; a.shared_end = shared_end;
   a.max_pos = max_pos; a.nb = info->NB; a.n_ws = info->Q - 1;
   a.scale = 1.0f / sqrtf((float)dh);
   const int rc = la_attention_launch(dtype == LA_DTYPE_BF16 ? LA_DT_BF16 : LA_DT_F32, a, (hipStream_t)stream);

@@ -58,23 +58,26 @@ struct LaAttnArgs {
   const void* kw;       // workspace K [Hkv][ws_cap][dh] (one layer), packed row k -> ws row k-1
   const void* vw;
   void* o;              // [Q][H][dh]
-  float* part_o;        // [n_spans][H][Q][dh]
-  float* part_ml;       // [n_spans][H][Q][2]
+  float* part_o;        // [la_attention_parts()][H][Q][dh] softmax states (class chunks, then tail chunks)
+  float* part_ml;       // [la_attention_parts()][H][Q][2]  (m, l) of those states
   const int32_t* pos;
   const int32_t* branch;
   const int32_t* path;
   const int32_t* path_len;
   int Q, H, Hkv, dh, T_cap, ws_cap, maxp;
   int shared_end;       // keys [0, shared_end) come from the cache, later ones from the row's path
-  int n_spans;
-  int max_pos;          // largest row position (bounds the spans that reach the packed rows)
+  int max_pos;          // largest row position (an upper bound is fine)
   int nb;               // branches in the path table
   int n_ws;             // workspace rows written by this call (packed rows other than the ordinary row)
-  int rsplit;           // set by the launcher
-  float scale;
+  float scale;          // softmax scale (1/sqrt(dh))
+  // set by the launcher
+  int class_last;       // last chunk taken by the class workgroups (-1: none)
+  int tail0, n_tail;    // first chunk and number of chunks reaching past shared_end
+  int rgroups;          // row groups per KV head
+  float scale_log2;     // scale * log2(e)
 };
 int la_attention_launch(int dtype, const LaAttnArgs& a, hipStream_t st);
-int la_attention_spans(int max_pos);
+int la_attention_parts();   // softmax-state slots per (head, row) in part_o / part_ml
 
 // model pieces
 void la_embed_launch(int dtype, const void* E, const int32_t* tok, void* x, int M, int d, hipStream_t st);
