@@ -176,11 +176,11 @@ def test_fail_closed_commit(tiny):
 
 
 # Two correct bf16 computations of this model whose pre-rounding values differ
-# only at fp32-vs-fp64 level (relative 1e-7) already disagree by up to ~0.03 on
+# only at fp32-vs-fp64 level (relative 1e-7) already disagree by up to 0.035 on
 # these logits (tests/test_oracle_noise_floor.py measures it): each flipped bf16
 # rounding propagates through every later layer.  The model-level bound is
 # therefore twice that floor; single operators keep the 2e-2 bound.
-BF16_2LAYER_LOGIT_TOL = 0.06
+BF16_2LAYER_LOGIT_TOL = 0.07
 
 
 @pytest.mark.timeout(900)
