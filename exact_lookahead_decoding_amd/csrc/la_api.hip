@@ -26,10 +26,15 @@
 
 static thread_local std::string g_err;
 
+// Packed projection buffer: per layer wqkv, wo, w_gate_up, w_down, then
+// lm_head, each in the GEMM's packed layout (element offsets).
+struct PackedOffsets { size_t qkv, o, gu, dn, layer, lm, total; };
+
 struct la_ctx {
   la_config cfg;
   la_model_dims dims;
   la_model w;
+  PackedOffsets pk;
   hipStream_t st;
   int dtype, esz;
   int L, d, H, Hkv, dh, F, V, qkvdim;
@@ -139,7 +144,24 @@ static int validate_cfg(const la_config* cfg, const la_model_dims* d, la_ctx* c)
   if (!(d->dtype == LA_DTYPE_BF16 ? (dh == 128 || dh == 64) : (dh == 16 || dh == 64)))
     return fail(c, LA_EINVAL, "head_dim %d unsupported", dh);
   if (d->vocab < 2 || d->vocab > 65536) return fail(c, LA_EINVAL, "vocab %d out of range", d->vocab);
+  // the GEMM takes K in whole 128 (bf16) / 64 (fp32) element chunks and N in 16-column tiles
+  const int kc = d->dtype == LA_DTYPE_BF16 ? 128 : 64;
+  if (d->d_model % kc || (d->n_heads * dh) % kc || d->d_ff % kc || d->vocab % 16 || d->d_ff % 16)
+    return fail(c, LA_EINVAL, "d_model, n_heads*head_dim and d_ff must be multiples of %d, vocab of 16", kc);
   return LA_OK;
+}
+
+static PackedOffsets packed_offsets(const la_model_dims& d) {
+  const int qkvdim = (d.n_heads + 2 * d.n_kv_heads) * d.head_dim;
+  PackedOffsets p{};
+  p.qkv = 0;
+  p.o = la_gemm_packed_elems(qkvdim, d.d_model, 0);
+  p.gu = p.o + la_gemm_packed_elems(d.d_model, d.n_heads * d.head_dim, 0);
+  p.dn = p.gu + la_gemm_packed_elems(d.d_ff, d.d_model, 1);
+  p.layer = p.dn + la_gemm_packed_elems(d.d_model, d.d_ff, 0);
+  p.lm = p.layer * d.n_layers;
+  p.total = p.lm + la_gemm_packed_elems(d.vocab, d.d_model, 0);
+  return p;
 }
 
 static void setup_dims(la_ctx* c) {
@@ -265,13 +287,14 @@ static const char* wptr(const void* base, size_t elems_per_layer, int l, int esz
 }
 
 static int gemm(la_ctx* c, int epi, const void* X, const void* W, void* Y, const void* Rr, int M, int N, int K,
-                int up_off) {
+                int up_off, bool defer = false) {
   LaGemmArgs a{};
   a.X = X; a.W = W; a.Y = Y; a.R = Rr; a.P = c->gemm_p;
   a.M = M; a.N = N; a.K = K; a.ldx = K; a.ldy = N;
   a.splits = la_gemm_splits(N, K, c->dtype, epi == LA_EPI_SWIGLU);
   a.up_off = up_off;
   a.pcols = epi == LA_EPI_SWIGLU ? 2 * N : N;
+  a.defer_reduce = defer ? 1 : 0;
   const double wrows = epi == LA_EPI_SWIGLU ? 2.0 * N : (double)N;
   const double ybytes = epi == LA_EPI_F32 ? 4.0 : (double)c->esz;
   const double bytes = (wrows * K + (double)M * K) * c->esz + (double)M * N * ybytes * (epi == LA_EPI_RESID ? 2 : 1);
@@ -280,6 +303,15 @@ static int gemm(la_ctx* c, int epi, const void* X, const void* W, void* Y, const
   prof_mark(c, false, 0, 0, 0);
   if (rc) return fail(c, rc == -2 ? LA_EINVAL : LA_EDEVICE, "gemm launch failed (M=%d N=%d K=%d rc=%d)", M, N, K, rc);
   return LA_OK;
+}
+
+// A residual projection x += Y W^T.  With a split K its partials stay in
+// gemm_p and the next RMSNorm folds them into x (same sum, same rounding);
+// returns the number of pending partials (0 when x was updated in place).
+static int resid_gemm(la_ctx* c, const void* X, const void* W, int M, int K, int* pending) {
+  const int s = la_gemm_splits(c->d, K, c->dtype, 0);
+  *pending = s > 1 ? s : 0;
+  return gemm(c, LA_EPI_RESID, X, W, c->x, c->x, M, c->d, K, 0, s > 1);
 }
 
 // Forward M rows.  K/V of rows < n_direct go to cache rows cache_row0 + m,
@@ -301,19 +333,23 @@ static int forward(la_ctx* c, int M, const int32_t* tok, const int32_t* pos, con
   at.nb = nb;
   at.n_ws = M - n_direct;
   at.scale = 1.0f / sqrtf((float)c->dh);
+  int pend = 0;   // split partials of the last residual projection not yet folded into x
   for (int l = 0; l < c->L; ++l) {
     const char* attn_norm = wptr(c->w.attn_norm, c->d, l, esz);
     const char* mlp_norm = wptr(c->w.mlp_norm, c->d, l, esz);
-    const char* wqkv = wptr(c->w.wqkv, (size_t)c->qkvdim * c->d, l, esz);
-    const char* wo = wptr(c->w.wo, (size_t)c->d * c->H * c->dh, l, esz);
-    const char* wgu = wptr(c->w.w_gate_up, (size_t)2 * c->F * c->d, l, esz);
-    const char* wdn = wptr(c->w.w_down, (size_t)c->d * c->F, l, esz);
+    const char* wl = (const char*)c->w.packed + c->pk.layer * l * esz;
+    const char* wqkv = wl + c->pk.qkv * esz;
+    const char* wo = wl + c->pk.o * esz;
+    const char* wgu = wl + c->pk.gu * esz;
+    const char* wdn = wl + c->pk.dn * esz;
     char* kc = c->kc + l * kvl * esz;
     char* vc = c->vc + l * kvl * esz;
     char* kw = (char*)c->kw + l * wsl * esz;
     char* vw = (char*)c->vw + l * wsl * esz;
     int rc;
-    la_rmsnorm_launch(c->dtype, c->x, attn_norm, c->nrm, nullptr, M, c->d, c->dims.eps, c->st);
+    const size_t pstride = (size_t)M * c->d;
+    la_addnorm_launch(c->dtype, c->x, c->gemm_p, pend, pstride, 1, attn_norm, c->nrm, nullptr, M, c->d, c->dims.eps,
+                      c->st);
     if ((rc = gemm(c, LA_EPI_STORE, c->nrm, wqkv, c->qkv, nullptr, M, c->qkvdim, c->d, 0))) return rc;
     la_qkv_post_launch(c->dtype, c->qkv, c->rope, pos, M, c->H, c->Hkv, c->dh, c->q, kc, vc, c->t_cap, cache_row0,
                        n_direct, kw, vw, c->ws_cap, c->st);
@@ -328,14 +364,17 @@ static int forward(la_ctx* c, int M, const int32_t* tok, const int32_t* pos, con
     rc = la_attention_launch(c->dtype, at, c->st);
     prof_mark(c, false, 1, 0, 0);
     if (rc) return fail(c, LA_EDEVICE, "attention launch failed (%d)", rc);
-    if ((rc = gemm(c, LA_EPI_RESID, c->o, wo, c->x, c->x, M, c->d, c->H * c->dh, 0))) return rc;
-    la_rmsnorm_launch(c->dtype, c->x, mlp_norm, c->nrm, nullptr, M, c->d, c->dims.eps, c->st);
+    if ((rc = resid_gemm(c, c->o, wo, M, c->H * c->dh, &pend))) return rc;
+    la_addnorm_launch(c->dtype, c->x, c->gemm_p, pend, pstride, 1, mlp_norm, c->nrm, nullptr, M, c->d, c->dims.eps,
+                      c->st);
     if ((rc = gemm(c, LA_EPI_SWIGLU, c->nrm, wgu, c->act, nullptr, M, c->F, c->d, c->F))) return rc;
-    if ((rc = gemm(c, LA_EPI_RESID, c->act, wdn, c->x, c->x, M, c->d, c->F, 0))) return rc;
+    if ((rc = resid_gemm(c, c->act, wdn, M, c->F, &pend))) return rc;
   }
   if (n_logit > 0) {
-    la_rmsnorm_launch(c->dtype, c->x, c->w.final_norm, c->fin, logit_rows, n_logit, c->d, c->dims.eps, c->st);
-    int rc = gemm(c, LA_EPI_F32, c->fin, c->w.lm_head, c->logits, nullptr, n_logit, c->V, c->d, 0);
+    la_addnorm_launch(c->dtype, c->x, c->gemm_p, pend, (size_t)M * c->d, 0, c->w.final_norm, c->fin, logit_rows,
+                      n_logit, c->d, c->dims.eps, c->st);
+    int rc = gemm(c, LA_EPI_F32, c->fin, (const char*)c->w.packed + c->pk.lm * esz, c->logits, nullptr, n_logit, c->V,
+                  c->d, 0);
     if (rc) return rc;
   }
   HIPCHK(c, hipGetLastError());
@@ -373,6 +412,8 @@ extern "C" int la_init(const la_config* cfg, const la_model_dims* dims, const la
   int rc = validate_cfg(cfg, dims, nullptr);
   if (rc) return rc;
   if (!weights || !kv || !arena || !prompt) return fail(nullptr, LA_EINVAL, "null weights, buffers or prompt");
+  if (!weights->packed || !weights->embed || !weights->final_norm || !weights->attn_norm || !weights->mlp_norm)
+    return fail(nullptr, LA_EINVAL, "weights: packed projections (la_pack_weights), embed and norms are required");
   if (prompt_len < 1 || prompt_len > cfg->max_prompt)
     return fail(nullptr, LA_EINVAL, "prompt_len %d outside [1, max_prompt=%d]", prompt_len, cfg->max_prompt);
   for (int i = 0; i < prompt_len; ++i)
@@ -381,6 +422,7 @@ extern "C" int la_init(const la_config* cfg, const la_model_dims* dims, const la
   c->cfg = *cfg;
   c->dims = *dims;
   c->w = *weights;
+  c->pk = packed_offsets(*dims);
   c->st = (hipStream_t)stream;
   setup_dims(c);
   const size_t kvb = (size_t)c->L * c->Hkv * c->t_cap * c->dh * c->esz;
@@ -804,32 +846,111 @@ extern "C" int la_attention(int32_t dtype, const void* q, const void* k_cache, c
   return LA_OK;
 }
 
+static int linear_epi(int32_t epilogue) {
+  return epilogue == LA_LINEAR_STORE ? LA_EPI_STORE : epilogue == LA_LINEAR_RESIDUAL ? LA_EPI_RESID
+         : epilogue == LA_LINEAR_SWIGLU ? LA_EPI_SWIGLU : LA_EPI_F32;
+}
+static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+extern "C" size_t la_packed_linear_bytes(int32_t dtype, int32_t epilogue, int32_t N, int32_t K) {
+  if (N <= 0 || K <= 0) return 0;
+  return la_gemm_packed_elems(N, K, epilogue == LA_LINEAR_SWIGLU) * (dtype == LA_DTYPE_BF16 ? 2 : 4);
+}
+
 extern "C" size_t la_linear_workspace(int32_t dtype, int32_t epilogue, int32_t M, int32_t N, int32_t K) {
   const int dt = dtype == LA_DTYPE_BF16 ? LA_DT_BF16 : LA_DT_F32;
   const int sw = epilogue == LA_LINEAR_SWIGLU;
   const int splits = la_gemm_splits(N, K, dt, sw);
-  return splits > 1 ? (size_t)splits * M * (sw ? 2 * N : N) * 4 : 0;
+  const size_t part = splits > 1 ? (size_t)splits * M * (sw ? 2 * N : N) * 4 : 0;
+  return align256(la_packed_linear_bytes(dtype, epilogue, N, K)) + part;
 }
 
-extern "C" int la_linear(int32_t dtype, int32_t epilogue, const void* X, const void* W, void* Y, const void* R,
-                         int32_t M, int32_t N, int32_t K, void* workspace, size_t workspace_bytes, void* stream) {
+static int linear_check(int32_t dtype, int32_t epilogue, const void* X, const void* W, const void* Y, const void* R) {
   if (!X || !W || !Y || (epilogue == LA_LINEAR_RESIDUAL && !R)) return fail(nullptr, LA_EINVAL, "null argument");
   if (dtype != LA_DTYPE_F32 && dtype != LA_DTYPE_BF16) return fail(nullptr, LA_EINVAL, "dtype");
   if (epilogue < LA_LINEAR_STORE || epilogue > LA_LINEAR_F32) return fail(nullptr, LA_EINVAL, "epilogue");
+  return LA_OK;
+}
+
+extern "C" int la_pack_linear(int32_t dtype, int32_t epilogue, const void* W, int32_t N, int32_t K, void* Wp,
+                              void* stream) {
+  if (!W || !Wp) return fail(nullptr, LA_EINVAL, "null argument");
+  if (dtype != LA_DTYPE_F32 && dtype != LA_DTYPE_BF16) return fail(nullptr, LA_EINVAL, "dtype");
+  if (epilogue < LA_LINEAR_STORE || epilogue > LA_LINEAR_F32) return fail(nullptr, LA_EINVAL, "epilogue");
+  const int rc = la_gemm_pack_launch(dtype == LA_DTYPE_BF16 ? LA_DT_BF16 : LA_DT_F32, W, Wp, N, K,
+                                     epilogue == LA_LINEAR_SWIGLU, (hipStream_t)stream);
+  if (rc == -2) return fail(nullptr, LA_EINVAL, "unsupported shape N=%d K=%d", N, K);
+  if (rc) return fail(nullptr, LA_EDEVICE, "pack launch failed");
+  return LA_OK;
+}
+
+extern "C" int la_linear_packed(int32_t dtype, int32_t epilogue, const void* X, const void* Wp, void* Y,
+                                const void* R, int32_t M, int32_t N, int32_t K, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  int rc = linear_check(dtype, epilogue, X, Wp, Y, R);
+  if (rc) return rc;
   const size_t need = la_linear_workspace(dtype, epilogue, M, N, K);
-  if (need > 0 && (!workspace || workspace_bytes < need))
+  const size_t skip = align256(la_packed_linear_bytes(dtype, epilogue, N, K));
+  if (need > skip && (!workspace || workspace_bytes < need))
     return fail(nullptr, LA_EOVERFLOW, "workspace %zu < %zu bytes", workspace_bytes, need);
   const int dt = dtype == LA_DTYPE_BF16 ? LA_DT_BF16 : LA_DT_F32;
-  const int epi = epilogue == LA_LINEAR_STORE ? LA_EPI_STORE : epilogue == LA_LINEAR_RESIDUAL ? LA_EPI_RESID
-                  : epilogue == LA_LINEAR_SWIGLU ? LA_EPI_SWIGLU : LA_EPI_F32;
+  const int epi = linear_epi(epilogue);
   LaGemmArgs a{};
-  a.X = X; a.W = W; a.Y = Y; a.R = R; a.P = (float*)workspace;
+  a.X = X; a.W = Wp; a.Y = Y; a.R = R; a.P = need > skip ? (float*)((char*)workspace + skip) : nullptr;
   a.M = M; a.N = N; a.K = K; a.ldx = K; a.ldy = N;
   a.splits = la_gemm_splits(N, K, dt, epi == LA_EPI_SWIGLU);
   a.up_off = N;
   a.pcols = epi == LA_EPI_SWIGLU ? 2 * N : N;
-  const int rc = la_gemm_launch(dt, epi, a, (hipStream_t)stream);
+  rc = la_gemm_launch(dt, epi, a, (hipStream_t)stream);
   if (rc == -2) return fail(nullptr, LA_EINVAL, "unsupported shape M=%d N=%d K=%d", M, N, K);
   if (rc) return fail(nullptr, LA_EDEVICE, "linear launch failed");
+  return LA_OK;
+}
+
+extern "C" int la_linear(int32_t dtype, int32_t epilogue, const void* X, const void* W, void* Y, const void* R,
+                         int32_t M, int32_t N, int32_t K, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = linear_check(dtype, epilogue, X, W, Y, R);
+  if (rc) return rc;
+  const size_t need = la_linear_workspace(dtype, epilogue, M, N, K);
+  if (!workspace || workspace_bytes < need)
+    return fail(nullptr, LA_EOVERFLOW, "workspace %zu < %zu bytes", workspace_bytes, need);
+  if ((rc = la_pack_linear(dtype, epilogue, W, N, K, workspace, stream))) return rc;
+  return la_linear_packed(dtype, epilogue, X, workspace, Y, R, M, N, K, workspace, workspace_bytes, stream);
+}
+
+extern "C" uint64_t la_packed_weight_bytes(const la_model_dims* dims) {
+  if (!dims || dims->n_layers < 1) return 0;
+  return (uint64_t)packed_offsets(*dims).total * (dims->dtype == LA_DTYPE_BF16 ? 2 : 4);
+}
+
+extern "C" int la_pack_weights(const la_model_dims* dims, const la_model* plain, void* packed, void* stream) {
+  if (!dims || !plain || !packed) return fail(nullptr, LA_EINVAL, "null argument");
+  la_config probe{};
+  probe.W = 1; probe.N = 3; probe.max_new = 1; probe.max_prompt = 1;
+  int rc = validate_cfg(&probe, dims, nullptr);
+  if (rc) return rc;
+  if (!plain->wqkv || !plain->wo || !plain->w_gate_up || !plain->w_down || !plain->lm_head)
+    return fail(nullptr, LA_EINVAL, "null projection weights");
+  const PackedOffsets pk = packed_offsets(*dims);
+  const int dt = dims->dtype == LA_DTYPE_BF16 ? LA_DT_BF16 : LA_DT_F32;
+  const size_t esz = dims->dtype == LA_DTYPE_BF16 ? 2 : 4;
+  const int d = dims->d_model, F = dims->d_ff, hd = dims->n_heads * dims->head_dim;
+  const int qkvdim = (dims->n_heads + 2 * dims->n_kv_heads) * dims->head_dim;
+  hipStream_t st = (hipStream_t)stream;
+  char* out = (char*)packed;
+  for (int l = 0; l < dims->n_layers; ++l) {
+    char* pl = out + pk.layer * l * esz;
+    rc = la_gemm_pack_launch(dt, (const char*)plain->wqkv + (size_t)l * qkvdim * d * esz, pl + pk.qkv * esz, qkvdim,
+                             d, 0, st);
+    rc = rc ? rc : la_gemm_pack_launch(dt, (const char*)plain->wo + (size_t)l * d * hd * esz, pl + pk.o * esz, d, hd,
+                                       0, st);
+    rc = rc ? rc : la_gemm_pack_launch(dt, (const char*)plain->w_gate_up + (size_t)l * 2 * F * d * esz,
+                                       pl + pk.gu * esz, F, d, 1, st);
+    rc = rc ? rc : la_gemm_pack_launch(dt, (const char*)plain->w_down + (size_t)l * d * F * esz, pl + pk.dn * esz, d,
+                                       F, 0, st);
+    if (rc) return fail(nullptr, rc == -2 ? LA_EINVAL : LA_EDEVICE, "pack launch failed (layer %d)", l);
+  }
+  rc = la_gemm_pack_launch(dt, plain->lm_head, out + pk.lm * esz, dims->vocab, d, 0, st);
+  if (rc) return fail(nullptr, rc == -2 ? LA_EINVAL : LA_EDEVICE, "pack launch failed (lm_head)");
   return LA_OK;
 }

@@ -1,41 +1,76 @@
 // Skinny GEMM Y = X W^T for the packed rows (M <= 256), HBM-bound on W.
 //
-// The target forward of one packed round multiplies a few hundred rows by
+// The target forward of one packed round multiplies a few dozen rows by
 // every weight matrix ("M7.3 - Lookahead Decoding", 0x05C row and FLOP
-// ledger: token-wise target work over Q rows), so W is streamed once per
-// round and the rows stay on chip:
-//   * a workgroup (4 waves) owns a block of output columns and one split of
-//     the K dimension; each wave owns two 16-column MFMA tiles and all M rows;
-//   * W fragments go global -> registers, one K chunk ahead;
-//   * the X chunk is staged through LDS (double buffered) and shared by the
-//     four waves.
-// Batch invariance: the K partition (chunk size, split count) depends only
-// on (N, K), never on M, and every output element is produced by the same
-// MFMA sequence and the same fixed-order split reduction whatever row slot
-// it occupies.  A row therefore gets bit-identical results in a 1-row
-// autoregressive step and in a packed lookahead round.
+// ledger: token-wise target work over Q rows), so the round's cost is one
+// pass over the weights and the kernel's only job is to keep HBM busy:
+//   * a workgroup (4 waves) owns 4*NTW output tiles of 16 columns (SwiGLU:
+//     4 gate/up tile pairs) and one split of K;
+//   * W is stored packed (la_gemm_pack_launch): the MFMA B fragments of one
+//     workgroup step lie in one contiguous run of 4*NTW*NKB KB, in the order
+//     the DMA instructions read them, so every instruction reads 1 KB
+//     contiguous and a workgroup streams one contiguous region; the weight
+//     loads are non-temporal, so the single-use stream does not evict the
+//     activation rows every workgroup re-reads from L2;
+//   * W and X reach LDS through global_load_lds, one 1 KB MFMA fragment per
+//     DMA instruction (lane l's 16 bytes at 16 l, read back with
+//     conflict-free ds_read_b128), in a ring of DW+1 stages: each wave brings
+//     its own W fragments and a quarter of the X fragments shared by all
+//     four, DW steps ahead of the MFMAs;
+//   * per step: wait for this wave's step (a static vmcnt: every step is the
+//     same G loads per wave, steps past the end load 16 bytes of a valid
+//     address), a barrier that leaves the later steps in flight, issue step
+//     i + DW into the stage step i - 1 used, then the MFMAs.
+// The K partition (chunk size, split count) depends on (N, K) only; every
+// output element is the same chunk-ordered MFMA sequence (and, with splits,
+// the same fixed-order sum of split partials) whatever M is and whichever
+// tile slot its row occupies, so a row gets identical bits in a one-row
+// autoregressive step and inside a packed lookahead round.
+#include <algorithm>
+
 #include "la_common.h"
+#include "la_dev.h"
 #include "la_kernels.h"
 
-template <typename T> struct MM;
-template <> struct MM<bf16_t> {
-  static constexpr int KC = 128;     // K elements per chunk
-  static constexpr int KSTEP = 32;   // K per MFMA
-  static constexpr int VEC = 8;      // elements per lane per fragment
-  static constexpr int PAD = 8;
-  typedef bf16x8 frag;
-  static __device__ __forceinline__ frag ld(const bf16_t* p) { return *(const bf16x8*)p; }
-  static __device__ __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) { return mfma_bf16_32(a, b, c); }
+typedef LdsT<16>::T v4u;
+
+#define CPOL_NT 2   // cache policy of a load: non-temporal (streamed once)
+
+template <typename T> struct GT;
+template <> struct GT<bf16_t> {
+  static constexpr int KC = 128;   // K per chunk: 4 k-blocks of 32
+  static constexpr int EPL = 8;    // K elements in a lane's 16-byte piece
 };
-template <> struct MM<float> {
-  static constexpr int KC = 64;
-  static constexpr int KSTEP = 4;
-  static constexpr int VEC = 1;
-  static constexpr int PAD = 4;
-  typedef float frag;
-  static __device__ __forceinline__ frag ld(const float* p) { return *p; }
-  static __device__ __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) { return mfma_f32_4(a, b, c); }
+template <> struct GT<float> {
+  static constexpr int KC = 64;    // 4 k-blocks of 16
+  static constexpr int EPL = 4;
 };
+
+// One k-block: every lane holds 16 bytes of its A row / B column.
+//   bf16: one 16x16x32 MFMA; lane group g = l/16 holds k = 8g .. 8g+7.
+//   fp32: four 16x16x4 MFMAs; MFMA j takes k = 4g + j of lane group g.
+template <typename T> __device__ __forceinline__ f32x4 kblock(v4u a, v4u b, f32x4 c) {
+  if constexpr (sizeof(T) == 2) {
+    return mfma_bf16_32(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) c = mfma_f32_4(__uint_as_float(a[j]), __uint_as_float(b[j]), c);
+    return c;
+  }
+}
+
+// A ring step is NKB k-blocks (4 for narrow stages, 2 once the X and W
+// fragments of a k-block reach 12 KB); the ring holds DW+1 stages and the
+// per-step wait may not exceed vmcnt's 63.
+constexpr int gemm_nkb(int mt, int ntw) { return mt + 4 * ntw >= 12 ? 2 : 4; }
+constexpr int gemm_stage(int mt, int ntw) { return (mt + 4 * ntw) * gemm_nkb(mt, ntw) * 1024; }
+constexpr int gemm_loads(int mt, int ntw) { return (ntw + mt / 4) * gemm_nkb(mt, ntw) + (mt % 4) * gemm_nkb(mt, ntw) / 4; }
+constexpr int gemm_depth(int mt, int ntw) {
+  int d = 5;
+  while (d > 1 && (d + 1) * gemm_stage(mt, ntw) > LDS_BYTES) --d;
+  while (d > 1 && (d - 1) * gemm_loads(mt, ntw) > 63) --d;
+  return d;
+}
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g)); }
 
@@ -53,123 +88,149 @@ __device__ __forceinline__ void gemm_store(const LaGemmArgs& a, int m, int n, fl
   }
 }
 
-template <typename T, int MT, int EPI>
+template <typename T, int MT, int NTW, int EPI>
 __global__ void __launch_bounds__(256) la_gemm_kernel(LaGemmArgs a) {
-  typedef MM<T> mm;
-  constexpr int KC = mm::KC;
-  constexpr int NKS = KC / mm::KSTEP;        // k-steps per chunk
-  constexpr int LROW = KC + mm::PAD;         // LDS row length (elements)
-  constexpr int ROWS = MT * 16;
-  constexpr int EPP = 16 / sizeof(T);        // elements per 16-byte piece
-  constexpr int PPR = KC / EPP;              // pieces per row (16)
-  __shared__ __attribute__((aligned(16))) T xs[2][ROWS * LROW];
+  constexpr int KC = GT<T>::KC, EPL = GT<T>::EPL, KB = KC / 4;
+  constexpr int NKB = gemm_nkb(MT, NTW);         // k-blocks per ring step
+  constexpr int DW = gemm_depth(MT, NTW);
+  constexpr int R = DW + 1;                      // ring stages
+  constexpr int STAGE = gemm_stage(MT, NTW);
+  constexpr int WOFF = MT * NKB * 1024;          // W fragments after the X fragments
+  constexpr int XF = MT * NKB / 4;               // X fragments per step and wave
+  constexpr int G = NTW * NKB + XF;              // DMA instructions per step and wave
+  static_assert((MT * NKB) % 4 == 0, "X fragments split evenly over the waves");
+  static_assert(G == gemm_loads(MT, NTW), "load count");
+  extern __shared__ __attribute__((aligned(1024))) char lds[];
 
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int g = lane >> 4;
-  const int c16 = lane & 15;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
   const bool swiglu = (EPI == LA_EPI_SWIGLU) || (a.swiglu_partial != 0);
-  const int r0 = swiglu ? blockIdx.x * 64 + wave * 16 : blockIdx.x * 128 + wave * 32;
-  const int r1 = swiglu ? r0 + a.up_off : r0 + 16;
-  const bool active = r0 < a.N;
   const int split = blockIdx.y;
   const int c_begin = (int)(((long)split * a.nchunks) / a.splits);
-  const int c_end = (int)(((long)(split + 1) * a.nchunks) / a.splits);
+  const int nc = (int)(((long)(split + 1) * a.nchunks) / a.splits) - c_begin;   // >= 1 (splits <= nchunks)
+  const int n = nc * (4 / NKB);                                                  // ring steps
 
-  const T* X = (const T*)a.X;
+  // tile t of this wave: output columns colw + 16 t (SwiGLU: gate columns
+  // colw and their up rows); its fragment for k-block kb sits at packed
+  // fragment ((blockIdx.x * nkb + kb) * 4 + wave) * NTW + t
+  const int colw = (blockIdx.x * 4 + wave) * 16 * (swiglu ? 1 : NTW);
+  const size_t nkb = (size_t)(a.K / KB);
   const T* W = (const T*)a.W;
-  const T* w0p = W + (size_t)(active ? r0 + c16 : 0) * a.K + mm::VEC * g;
-  const T* w1p = W + (size_t)(active ? r1 + c16 : 0) * a.K + mm::VEC * g;
-
-  f32x4 acc[MT][2];
+  const T* X = (const T*)a.X;
+  const T* wp[NTW];
 #pragma unroll
-  for (int i = 0; i < MT; ++i) { acc[i][0] = f32x4{0, 0, 0, 0}; acc[i][1] = f32x4{0, 0, 0, 0}; }
-
-  typename mm::frag bcur[NKS][2], bnxt[NKS][2];
-  u32x4 xreg[MT];
-
-  auto load_b = [&](int c, typename mm::frag (&b)[NKS][2]) {
-    const size_t k0 = (size_t)c * KC;
+  for (int t = 0; t < NTW; ++t)
+    wp[t] = W + ((((size_t)blockIdx.x * nkb + (size_t)c_begin * 4) * 4 + wave) * NTW + t) * 64 * EPL + lane * EPL;
+  // X fragments this wave brings in: f = wave + 4 j is (row tile f / NKB,
+  // k-block f % NKB); rows past M load row M - 1 and are never stored
+  const T* xp = X + (size_t)c_begin * KC + EPL * g;
+  int xoff[XF];
 #pragma unroll
-    for (int s = 0; s < NKS; ++s) {
-      b[s][0] = mm::ld(w0p + k0 + s * mm::KSTEP);
-      b[s][1] = mm::ld(w1p + k0 + s * mm::KSTEP);
-    }
-  };
-  auto load_x = [&](int c) {
-#pragma unroll
-    for (int i = 0; i < MT; ++i) {
-      const int piece = threadIdx.x + 256 * i;
-      const int row = piece / PPR, col = (piece % PPR) * EPP;
-      if (row < a.M) xreg[i] = *(const u32x4*)(X + (size_t)row * a.ldx + (size_t)c * KC + col);
-      else xreg[i] = u32x4{0, 0, 0, 0};
-    }
-  };
-  auto store_x = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < MT; ++i) {
-      const int piece = threadIdx.x + 256 * i;
-      const int row = piece / PPR, col = (piece % PPR) * EPP;
-      *(u32x4*)(&xs[buf][row * LROW + col]) = xreg[i];
-    }
-  };
-
-  if (c_begin < c_end) {
-    if (active) load_b(c_begin, bcur);
-    load_x(c_begin);
-    store_x(0);
-    __syncthreads();
-    int buf = 0;
-    for (int c = c_begin; c < c_end; ++c) {
-      const bool more = c + 1 < c_end;
-      if (more) {
-        if (active) load_b(c + 1, bnxt);
-        load_x(c + 1);
-      }
-      if (active) {
-#pragma unroll
-        for (int s = 0; s < NKS; ++s) {
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) {
-            typename mm::frag af = mm::ld(&xs[buf][(mt * 16 + c16) * LROW + s * mm::KSTEP + mm::VEC * g]);
-            acc[mt][0] = mm::mma(af, bcur[s][0], acc[mt][0]);
-            acc[mt][1] = mm::mma(af, bcur[s][1], acc[mt][1]);
-          }
-        }
-      }
-      if (more) {
-        store_x(buf ^ 1);
-#pragma unroll
-        for (int s = 0; s < NKS; ++s) { bcur[s][0] = bnxt[s][0]; bcur[s][1] = bnxt[s][1]; }
-      }
-      __syncthreads();
-      buf ^= 1;
-    }
+  for (int j = 0; j < XF; ++j) {
+    const int f = wave + 4 * j;
+    xoff[j] = min((f / NKB) * 16 + c16, a.M - 1) * a.ldx + (f % NKB) * KB;
   }
-  if (!active) return;
 
-  // epilogue: D lane l holds rows 4*g + r, column c16 of each 16x16 tile
+  f32x4 acc[MT][NTW];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int t = 0; t < NTW; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // step i (relative to the split) into stage SL; past the split's last step
+  // every lane loads the same valid 16 bytes into a stage nobody reads
+  auto issue = [&](auto SL, int i) {
+    constexpr int sl = decltype(SL)::value;
+    const bool live = i < n;
+    const size_t k0 = (size_t)i * (NKB * KB);
+    char* stage = lds + sl * STAGE;
+#pragma unroll
+    for (int t = 0; t < NTW; ++t) {
+#pragma unroll
+      for (int s = 0; s < NKB; ++s) {
+        const T* src = live ? wp[t] + ((size_t)i * NKB + s) * (4 * NTW * 64 * EPL) : W;
+        __builtin_amdgcn_global_load_lds((const void*)src,
+                                         (lds_void_t*)(stage + WOFF + ((wave * NTW + t) * NKB + s) * 1024), 16, 0,
+                                         CPOL_NT);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < XF; ++j) {
+      const T* src = live ? xp + xoff[j] + k0 : X;
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(stage + (wave + 4 * j) * 1024), 16, 0, 0);
+    }
+  };
+
+  // X fragment (mt, s) sits at (mt * NKB + s) KB of the stage, W fragment
+  // (wave, t, s) at WOFF + ((wave * NTW + t) * NKB + s) KB; lane l's 16 bytes
+  // are at 16 l in both
+  auto compute = [&](auto SL) {
+    constexpr int sl = decltype(SL)::value;
+    const uint32_t xb = lds_addr(lds + sl * STAGE) + 16 * lane;
+    const uint32_t wb = xb + WOFF + wave * NTW * NKB * 1024;
+    v4u A[2][MT], B[2][NTW];
+    auto fetch = [&](auto S, auto BUF) {
+      constexpr int s = decltype(S)::value, b = decltype(BUF)::value;
+      static_for<0, MT>([&](auto J) { A[b][J] = lds_read<16, (decltype(J)::value * NKB + s) * 1024>(xb); });
+      static_for<0, NTW>([&](auto J) { B[b][J] = lds_read<16, (decltype(J)::value * NKB + s) * 1024>(wb); });
+    };
+    fetch(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+    lds_wait(A[0]);
+    lds_wait(B[0]);
+    static_for<0, NKB>([&](auto S) {
+      constexpr int s = decltype(S)::value, cur = s & 1, nxt = (s + 1) & 1;
+      if constexpr (s + 1 < NKB) fetch(std::integral_constant<int, s + 1>{}, std::integral_constant<int, nxt>{});
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int t = 0; t < NTW; ++t) acc[mt][t] = kblock<T>(A[cur][mt], B[cur][t], acc[mt][t]);
+      if constexpr (s + 1 < NKB) {
+        lds_wait(A[nxt]);
+        lds_wait(B[nxt]);
+      }
+    });
+  };
+
+  static_for<0, DW>([&](auto J) { issue(J, decltype(J)::value); });
+  for (int i0 = 0; i0 < n; i0 += R) {
+    static_for<0, R>([&](auto J) {
+      constexpr int j = decltype(J)::value;
+      const int i = i0 + j;
+      if (i < n) {
+        wait_vm<(DW - 1) * G>();   // step i landed (steps i+1 .. i+DW-1 may be in flight)
+        ring_barrier();            // ... for every wave; stage (i-1) % R is no longer read
+        issue(std::integral_constant<int, (j + DW) % R>{}, i + DW);
+        compute(J);
+      }
+    });
+  }
+  wait_vm<0>();   // no DMA may land after the workgroup has left
+
+  // D lane l holds rows 4*g + r, column c16 of each 16x16 tile
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int m = mt * 16 + 4 * g + r;
       if (m >= a.M) continue;
-      const float v0 = acc[mt][0][r], v1 = acc[mt][1][r];
-      if (EPI == LA_EPI_PARTIAL) {
-        float* P = a.P + ((size_t)split * a.M + m) * a.pcols;
-        if (swiglu) {
-          P[r0 + c16] = v0;
-          P[a.up_off + r0 + c16] = v1;
+      if (swiglu) {
+        if (colw >= a.N) continue;
+        const float v0 = acc[mt][0][r], v1 = acc[mt][NTW - 1][r];
+        if (EPI == LA_EPI_PARTIAL) {
+          float* P = a.P + ((size_t)split * a.M + m) * a.pcols;
+          P[colw + c16] = v0;
+          P[a.up_off + colw + c16] = v1;
         } else {
-          P[r0 + c16] = v0;
-          P[r0 + 16 + c16] = v1;
+          gemm_store<T, EPI>(a, m, colw + c16, v0, v1);
         }
-      } else if (EPI == LA_EPI_SWIGLU) {
-        gemm_store<T, EPI>(a, m, r0 + c16, v0, v1);
       } else {
-        gemm_store<T, EPI>(a, m, r0 + c16, v0, 0.f);
-        gemm_store<T, EPI>(a, m, r0 + 16 + c16, v1, 0.f);
+#pragma unroll
+        for (int t = 0; t < NTW; ++t) {
+          const int col = colw + 16 * t;
+          if (col >= a.N) continue;
+          if (EPI == LA_EPI_PARTIAL) a.P[((size_t)split * a.M + m) * a.pcols + col + c16] = acc[mt][t][r];
+          else gemm_store<T, EPI>(a, m, col + c16, acc[mt][t][r], 0.f);
+        }
       }
     }
   }
@@ -193,23 +254,98 @@ __global__ void __launch_bounds__(256) la_gemm_reduce_kernel(LaGemmArgs a) {
 
 // ---------------------------------------------------------------------------
 
+// Tiles per wave: a function of the weight shape only (it fixes the packed
+// layout); two when that still leaves ~200 workgroups, and always for SwiGLU
+// (its gate and up tiles).
+int la_gemm_ntw(int N, int swiglu) { return swiglu ? 2 : (N >= 25600 ? 2 : 1); }
+
+static size_t pack_blocks(int N, int swiglu) {
+  const int per = swiglu ? 4 : 4 * la_gemm_ntw(N, swiglu);   // output tiles per workgroup
+  return (size_t)((N / 16 + per - 1) / per);
+}
+
+size_t la_gemm_packed_elems(int N, int K, int swiglu) {
+  return pack_blocks(N, swiglu) * 4 * la_gemm_ntw(N, swiglu) * 16 * (size_t)K;
+}
+
+// Packed W: fragment f = ((b * nkb + kb) * 4 + w) * NTW + t holds, lane l
+// after lane, the 16 bytes of W row (tile row0 + l % 16), k = kb * KB +
+// EPL * (l / 16) .. +EPL-1; rows of tiles past N are zero.
+template <typename T>
+__global__ void __launch_bounds__(256) la_gemm_pack_kernel(const T* W, T* P, int N, int K, int up_off, int ntw,
+                                                           int swiglu, size_t pieces) {
+  constexpr int KB = GT<T>::KC / 4, EPL = GT<T>::EPL;
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= pieces) return;
+  const int lane = (int)(idx & 63);
+  const size_t f = idx >> 6;
+  const size_t nkb = (size_t)(K / KB);
+  const int t = (int)(f % ntw);
+  const int w = (int)((f / ntw) % 4);
+  const int kb = (int)((f / (4 * ntw)) % nkb);
+  const size_t b = f / (4 * ntw * nkb);
+  const int col = swiglu ? (int)(b * 4 + w) * 16 : (int)(b * 4 + w) * 16 * ntw + 16 * t;
+  u32x4 v = {0, 0, 0, 0};
+  if (col < N) {
+    const int row = (swiglu ? col + t * up_off : col) + (lane & 15);
+    v = *(const u32x4*)(W + (size_t)row * K + (size_t)kb * KB + EPL * (lane >> 4));
+  }
+  *(u32x4*)(P + idx * EPL) = v;
+}
+
+int la_gemm_pack_launch(int dtype, const void* W, void* P, int N, int K, int swiglu, hipStream_t st) {
+  const int kc = dtype == LA_DT_BF16 ? GT<bf16_t>::KC : GT<float>::KC;
+  if (N % 16 != 0 || K % kc != 0 || N <= 0) return -2;
+  const int ntw = la_gemm_ntw(N, swiglu);
+  const size_t pieces = la_gemm_packed_elems(N, K, swiglu) / (dtype == LA_DT_BF16 ? 8 : 4);
+  const unsigned grid = (unsigned)((pieces + 255) / 256);
+  if (dtype == LA_DT_BF16)
+    hipLaunchKernelGGL(la_gemm_pack_kernel<bf16_t>, dim3(grid), dim3(256), 0, st, (const bf16_t*)W, (bf16_t*)P, N, K,
+                       N, ntw, swiglu, pieces);
+  else
+    hipLaunchKernelGGL(la_gemm_pack_kernel<float>, dim3(grid), dim3(256), 0, st, (const float*)W, (float*)P, N, K, N,
+                       ntw, swiglu, pieces);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 int la_gemm_splits(int N, int K, int dtype, int swiglu) {
-  // depends on the weight shape only (never on M): aim at ~384 workgroups
-  const int kc = dtype == LA_DT_BF16 ? MM<bf16_t>::KC : MM<float>::KC;
-  const int nblk = swiglu ? (N + 63) / 64 : (N + 127) / 128;
+  // a function of the weight shape only (never of M): split K only when there
+  // are too few column tiles to give every CU a workgroup, up to 4 ways
+  const int kc = dtype == LA_DT_BF16 ? GT<bf16_t>::KC : GT<float>::KC;
   const int nchunks = K / kc;
-  int s = (384 + nblk - 1) / nblk;
-  if (s > nchunks / 2) s = nchunks / 2;
-  if (s < 1) s = 1;
-  return s;
+  const int blocks = (N / 16 + 3) / 4;
+  if (swiglu || blocks >= 128 || nchunks < 2) return 1;
+  int s = (256 + blocks - 1) / blocks;
+  s = std::min(s, 4);
+  s = std::min(s, nchunks);
+  return std::max(s, 1);
+}
+
+template <typename T, int MT, int NTW, int EPI>
+static void launch_k(const LaGemmArgs& a, dim3 grid, hipStream_t st) {
+  constexpr int lds = (gemm_depth(MT, NTW) + 1) * gemm_stage(MT, NTW);
+  static_assert(lds <= LDS_BYTES, "LDS");
+  auto kern = la_gemm_kernel<T, MT, NTW, EPI>;
+  static bool attr = false;   // idempotent, so a race between threads only repeats it
+  if (!attr) {
+    hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    attr = true;
+  }
+  hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, a);
 }
 
 template <typename T, int EPI, int MT>
-static void launch_mt(const LaGemmArgs& a, dim3 grid, hipStream_t st) {
-  if (a.splits > 1) {
-    hipLaunchKernelGGL((la_gemm_kernel<T, MT, LA_EPI_PARTIAL>), grid, dim3(256), 0, st, a);
+static void launch_mt(const LaGemmArgs& a, int ntw, hipStream_t st) {
+  const int tiles = a.N / 16;
+  const int per = a.swiglu_partial ? 4 : 4 * ntw;
+  dim3 grid((tiles + per - 1) / per, a.splits);
+  const bool part = a.splits > 1;
+  if (ntw == 2) {
+    if (part) launch_k<T, MT, 2, LA_EPI_PARTIAL>(a, grid, st);
+    else launch_k<T, MT, 2, EPI>(a, grid, st);
   } else {
-    hipLaunchKernelGGL((la_gemm_kernel<T, MT, EPI>), grid, dim3(256), 0, st, a);
+    if (part) launch_k<T, MT, 1, LA_EPI_PARTIAL>(a, grid, st);
+    else launch_k<T, MT, 1, EPI>(a, grid, st);
   }
 }
 
@@ -218,15 +354,23 @@ static int launch_t(LaGemmArgs a, hipStream_t st) {
   const int mt = (a.M + 15) / 16;
   const bool swiglu = EPI == LA_EPI_SWIGLU;
   a.swiglu_partial = swiglu ? 1 : 0;
-  const int nblk = swiglu ? (a.N + 63) / 64 : (a.N + 127) / 128;
-  dim3 grid(nblk, a.splits);
-  if (mt <= 1) launch_mt<T, EPI, 1>(a, grid, st);
-  else if (mt <= 2) launch_mt<T, EPI, 2>(a, grid, st);
-  else if (mt <= 4) launch_mt<T, EPI, 4>(a, grid, st);
-  else if (mt <= 8) launch_mt<T, EPI, 8>(a, grid, st);
-  else if (mt <= 12) launch_mt<T, EPI, 12>(a, grid, st);
-  else launch_mt<T, EPI, 16>(a, grid, st);
-  if (a.splits > 1) {
+  const int ntw = la_gemm_ntw(a.N, swiglu);
+  if constexpr (EPI == LA_EPI_SWIGLU) {
+    if (mt <= 1) launch_mt<T, EPI, 1>(a, 2, st);
+    else if (mt <= 2) launch_mt<T, EPI, 2>(a, 2, st);
+    else if (mt <= 4) launch_mt<T, EPI, 4>(a, 2, st);
+    else if (mt <= 8) launch_mt<T, EPI, 8>(a, 2, st);
+    else if (mt <= 12) launch_mt<T, EPI, 12>(a, 2, st);
+    else launch_mt<T, EPI, 16>(a, 2, st);
+  } else {
+    if (mt <= 1) launch_mt<T, EPI, 1>(a, ntw, st);
+    else if (mt <= 2) launch_mt<T, EPI, 2>(a, ntw, st);
+    else if (mt <= 4) launch_mt<T, EPI, 4>(a, ntw, st);
+    else if (mt <= 8) launch_mt<T, EPI, 8>(a, ntw, st);
+    else if (mt <= 12) launch_mt<T, EPI, 12>(a, ntw, st);
+    else launch_mt<T, EPI, 16>(a, ntw, st);
+  }
+  if (a.splits > 1 && !a.defer_reduce) {
     const size_t total = (size_t)a.M * a.N;
     hipLaunchKernelGGL((la_gemm_reduce_kernel<T, EPI>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, a);
   }
@@ -234,13 +378,14 @@ static int launch_t(LaGemmArgs a, hipStream_t st) {
 }
 
 int la_gemm_launch(int dtype, int epi, LaGemmArgs a, hipStream_t st) {
-  const int kc = dtype == LA_DT_BF16 ? MM<bf16_t>::KC : MM<float>::KC;
-  if (a.M < 1 || a.M > 256 || a.K % kc != 0 || a.N % 16 != 0) return -2;
-  if (epi != LA_EPI_SWIGLU && a.N % 32 != 0) return -2;
+  const int kc = dtype == LA_DT_BF16 ? GT<bf16_t>::KC : GT<float>::KC;
+  if (a.M < 1 || a.M > 256 || a.K % kc != 0 || a.N % 16 != 0 || a.ldx % (16 / (dtype == LA_DT_BF16 ? 2 : 4)))
+    return -2;
   a.nchunks = a.K / kc;
   if (a.splits < 1) a.splits = 1;
   if (a.splits > a.nchunks) return -2;
   if (a.splits > 1 && a.P == nullptr) return -2;
+  if (a.defer_reduce && (a.splits < 2 || epi != LA_EPI_RESID)) return -2;
   if (dtype == LA_DT_BF16) {
     switch (epi) {
       case LA_EPI_STORE: return launch_t<bf16_t, LA_EPI_STORE>(a, st);

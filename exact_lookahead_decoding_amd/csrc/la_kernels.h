@@ -8,7 +8,7 @@ enum { LA_EPI_STORE = 0, LA_EPI_RESID = 1, LA_EPI_SWIGLU = 2, LA_EPI_F32 = 3, LA
 
 struct LaGemmArgs {
   const void* X;      // [M][ldx] storage dtype
-  const void* W;      // [rows][K] storage dtype (nn.Linear layout)
+  const void* W;      // packed weights (la_gemm_pack_launch) of the [rows][K] nn.Linear matrix
   void* Y;            // output [M][ldy]
   const void* R;      // residual [M][ldy] (RESID), may alias Y
   float* P;           // split partials [splits][M][pcols]
@@ -18,8 +18,13 @@ struct LaGemmArgs {
   int up_off;         // SWIGLU: first row of the "up" half of W (= F)
   int pcols;          // partial row length (SWIGLU: 2F, else N)
   int swiglu_partial; // set by the launcher
+  int defer_reduce;   // RESID with splits > 1: leave the partials for la_addnorm_launch
 };
 int la_gemm_splits(int N, int K, int dtype, int swiglu);
+int la_gemm_ntw(int N, int swiglu);
+size_t la_gemm_packed_elems(int N, int K, int swiglu);   // elements of the packed copy of W
+// W [rows][K] (SwiGLU: gate rows 0..N-1, up rows N..2N-1) -> packed P
+int la_gemm_pack_launch(int dtype, const void* W, void* P, int N, int K, int swiglu, hipStream_t st);
 int la_gemm_launch(int dtype, int epi, LaGemmArgs a, hipStream_t st);
 
 // row metadata produced by the packed-row builder (device int32 arrays)
@@ -83,6 +88,11 @@ int la_attention_parts();   // softmax-state slots per (head, row) in part_o / p
 void la_embed_launch(int dtype, const void* E, const int32_t* tok, void* x, int M, int d, hipStream_t st);
 void la_rmsnorm_launch(int dtype, const void* x, const void* w, void* y, const int32_t* rows, int M, int d,
                        float eps, hipStream_t st);
+// Residual fold + RMSNorm: x' = T(((P_0 + P_1) + ...) + x) for the split
+// partials P_s = P + s * pstride ([M][d] fp32 each; none when S == 0), written
+// back to x when write_x; y[m] = RMSNorm(x'[src]) with src = rows ? rows[m] : m.
+void la_addnorm_launch(int dtype, void* x, const float* P, int S, size_t pstride, int write_x, const void* w, void* y,
+                       const int32_t* rows, int M, int d, float eps, hipStream_t st);
 void la_rope_table_launch(float2* tab, int T, int dh, float theta, hipStream_t st);
 void la_qkv_post_launch(int dtype, const void* qkv, const float2* rope, const int32_t* pos, int M, int H, int Hkv,
                         int dh, void* q, void* kc, void* vc, int T_cap, int cache_row0, int n_direct, void* kw,

@@ -58,29 +58,40 @@ void la_embed_launch(int dtype, const void* E, const int32_t* tok, void* x, int 
   }
 }
 
-// y[m] = T(x[src] * rs * w),  rs = 1/sqrt(mean(x^2) + eps), src = rows ? rows[m] : m.
+// Residual fold + RMSNorm.  x' = x[src], or, with NS split partials of the
+// residual GEMM pending, x' = T(((P_0 + P_1) + ...) + x[src]) (the same sum
+// and rounding as that GEMM's own epilogue), written back to x when write_x;
+// y[m] = T(x' * rs * w), rs = 1/sqrt(mean(x'^2) + eps), src = rows ? rows[m] : m.
 // The sum of squares has one fixed order for every row: each thread's
 // elements in index order, then a butterfly within the wave, then the four
-// wave sums in a fixed grouping.
-template <typename T, int VPT>
-__global__ void __launch_bounds__(256) rmsnorm_kernel(const T* x, const T* w, T* y, const int32_t* rows, int d,
-                                                      float eps) {
+// wave sums in a fixed grouping.  All loads of a thread are issued first.
+template <typename T, int VPT, int NS>
+__global__ void __launch_bounds__(256) addnorm_kernel(T* x, const float* P, size_t pstride, int write_x, const T* w,
+                                                      T* y, const int32_t* rows, int d, float eps) {
   constexpr int E = 16 / sizeof(T);
   __shared__ float red[4];
   const int m = blockIdx.x;
   const int src = rows ? rows[m] : m;
   const int nv = d / E;
-  const u32x4* xr = (const u32x4*)(x + (size_t)src * d);
+  u32x4* xr = (u32x4*)(x + (size_t)src * d);
   const u32x4* wr = (const u32x4*)w;
   u32x4 xv[VPT], wv[VPT];
+  float4 pv[NS > 0 ? NS : 1][VPT][E / 4];
 #pragma unroll
   for (int j = 0; j < VPT; ++j) {
     const int v = threadIdx.x + 256 * j;
     if (v < nv) {
       xv[j] = xr[v];
       wv[j] = wr[v];
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const float4* pp = (const float4*)(P + s * pstride + (size_t)src * d + (size_t)v * E);
+#pragma unroll
+        for (int q = 0; q < E / 4; ++q) pv[s][j][q] = pp[q];
+      }
     }
   }
+  float xf[VPT][E];
   float ss = 0.f;
 #pragma unroll
   for (int j = 0; j < VPT; ++j) {
@@ -89,8 +100,24 @@ __global__ void __launch_bounds__(256) rmsnorm_kernel(const T* x, const T* w, T*
       const T* e = (const T*)&xv[j];
 #pragma unroll
       for (int q = 0; q < E; ++q) {
-        const float f = ld<T>(e + q);
+        float f = ld<T>(e + q);
+        if constexpr (NS > 0) {
+          float acc = 0.f;
+#pragma unroll
+          for (int s = 0; s < NS; ++s) acc += ((const float*)&pv[s][j][0])[q];
+          f = StoreT<T>::round(acc + f);
+        }
+        xf[j][q] = f;
         ss += f * f;
+      }
+      if constexpr (NS > 0) {
+        if (write_x) {
+          u32x4 ov;
+          T* oe = (T*)&ov;
+#pragma unroll
+          for (int q = 0; q < E; ++q) st<T>(oe + q, xf[j][q]);
+          xr[v] = ov;
+        }
       }
     }
   }
@@ -104,38 +131,55 @@ __global__ void __launch_bounds__(256) rmsnorm_kernel(const T* x, const T* w, T*
   for (int j = 0; j < VPT; ++j) {
     const int v = threadIdx.x + 256 * j;
     if (v < nv) {
-      const T* e = (const T*)&xv[j];
       const T* we = (const T*)&wv[j];
       u32x4 ov;
       T* oe = (T*)&ov;
 #pragma unroll
-      for (int q = 0; q < E; ++q) st<T>(oe + q, ld<T>(e + q) * rs * ld<T>(we + q));
+      for (int q = 0; q < E; ++q) st<T>(oe + q, xf[j][q] * rs * ld<T>(we + q));
       yr[v] = ov;
     }
   }
 }
 
+template <typename T, int VPT, int NS>
+static void an_t(void* x, const float* P, size_t pstride, int write_x, const void* w, void* y, const int32_t* rows,
+                 int M, int d, float eps, hipStream_t st) {
+  hipLaunchKernelGGL((addnorm_kernel<T, VPT, NS>), dim3(M), dim3(256), 0, st, (T*)x, P, pstride, write_x,
+                     (const T*)w, (T*)y, rows, d, eps);
+}
+
 template <typename T, int VPT>
-static void rms_t(const void* x, const void* w, void* y, const int32_t* rows, int M, int d, float eps,
-                  hipStream_t st) {
-  hipLaunchKernelGGL((rmsnorm_kernel<T, VPT>), dim3(M), dim3(256), 0, st, (const T*)x, (const T*)w, (T*)y, rows, d,
-                     eps);
+static void an_s(int S, void* x, const float* P, size_t pstride, int write_x, const void* w, void* y,
+                 const int32_t* rows, int M, int d, float eps, hipStream_t st) {
+  switch (S) {
+    case 0: an_t<T, VPT, 0>(x, P, pstride, write_x, w, y, rows, M, d, eps, st); break;
+    case 1: an_t<T, VPT, 1>(x, P, pstride, write_x, w, y, rows, M, d, eps, st); break;
+    case 2: an_t<T, VPT, 2>(x, P, pstride, write_x, w, y, rows, M, d, eps, st); break;
+    case 3: an_t<T, VPT, 3>(x, P, pstride, write_x, w, y, rows, M, d, eps, st); break;
+    default: an_t<T, VPT, 4>(x, P, pstride, write_x, w, y, rows, M, d, eps, st); break;
+  }
+}
+
+void la_addnorm_launch(int dtype, void* x, const float* P, int S, size_t pstride, int write_x, const void* w, void* y,
+                       const int32_t* rows, int M, int d, float eps, hipStream_t st) {
+  if (M <= 0) return;
+  if (!P) S = 0;
+  const int esz = dtype == LA_DT_BF16 ? 2 : 4;
+  switch (vpt_for(d, esz) * 2 + (dtype == LA_DT_BF16)) {
+    case 2: an_s<float, 1>(S, x, P, pstride, write_x, w, y, rows, M, d, eps, st); break;
+    case 3: an_s<bf16_t, 1>(S, x, P, pstride, write_x, w, y, rows, M, d, eps, st); break;
+    case 4: an_s<float, 2>(S, x, P, pstride, write_x, w, y, rows, M, d, eps, st); break;
+    case 5: an_s<bf16_t, 2>(S, x, P, pstride, write_x, w, y, rows, M, d, eps, st); break;
+    case 8: an_s<float, 4>(S, x, P, pstride, write_x, w, y, rows, M, d, eps, st); break;
+    case 9: an_s<bf16_t, 4>(S, x, P, pstride, write_x, w, y, rows, M, d, eps, st); break;
+    case 16: an_s<float, 8>(S, x, P, pstride, write_x, w, y, rows, M, d, eps, st); break;
+    default: an_s<bf16_t, 8>(S, x, P, pstride, write_x, w, y, rows, M, d, eps, st); break;
+  }
 }
 
 void la_rmsnorm_launch(int dtype, const void* x, const void* w, void* y, const int32_t* rows, int M, int d,
                        float eps, hipStream_t st) {
-  if (M <= 0) return;
-  const int esz = dtype == LA_DT_BF16 ? 2 : 4;
-  switch (vpt_for(d, esz) * 2 + (dtype == LA_DT_BF16)) {
-    case 2: rms_t<float, 1>(x, w, y, rows, M, d, eps, st); break;
-    case 3: rms_t<bf16_t, 1>(x, w, y, rows, M, d, eps, st); break;
-    case 4: rms_t<float, 2>(x, w, y, rows, M, d, eps, st); break;
-    case 5: rms_t<bf16_t, 2>(x, w, y, rows, M, d, eps, st); break;
-    case 8: rms_t<float, 4>(x, w, y, rows, M, d, eps, st); break;
-    case 9: rms_t<bf16_t, 4>(x, w, y, rows, M, d, eps, st); break;
-    case 16: rms_t<float, 8>(x, w, y, rows, M, d, eps, st); break;
-    default: rms_t<bf16_t, 8>(x, w, y, rows, M, d, eps, st); break;
-  }
+  la_addnorm_launch(dtype, (void*)x, nullptr, 0, 0, 0, w, y, rows, M, d, eps, st);
 }
 
 // cos/sin of t * theta^(-2i/dh), evaluated in fp64 and stored as fp32

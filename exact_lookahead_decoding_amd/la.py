@@ -40,7 +40,7 @@ class la_model_dims(C.Structure):
 
 class la_model(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in ("embed", "lm_head", "final_norm", "attn_norm", "wqkv", "wo", "mlp_norm",
-                                          "w_gate_up", "w_down")]
+                                          "w_gate_up", "w_down", "packed")]
 
 
 class la_config(C.Structure):
@@ -97,7 +97,8 @@ class la_rows_info(C.Structure):
 EXPORTS = ["la_query_sizes", "la_init", "la_destroy", "la_step", "la_generate", "la_predict", "la_verify",
            "la_commit", "la_pool_lookup", "la_pool_insert", "la_get_state", "la_stats", "la_last_error",
            "la_rows_query", "la_build_rows", "la_attention_workspace", "la_attention", "la_linear_workspace",
-           "la_linear", "la_profile", "la_profile_read"]
+           "la_linear", "la_packed_linear_bytes", "la_pack_linear", "la_linear_packed", "la_packed_weight_bytes",
+           "la_pack_weights", "la_profile", "la_profile_read"]
 LA_LINEAR_STORE, LA_LINEAR_RESIDUAL, LA_LINEAR_SWIGLU, LA_LINEAR_F32 = 0, 1, 2, 3
 
 _lib = None
@@ -138,6 +139,11 @@ def load() -> C.CDLL:
                           C.c_size_t, VP], I32),
         "la_linear_workspace": ([I32, I32, I32, I32, I32], C.c_size_t),
         "la_linear": ([I32, I32, VP, VP, VP, VP, I32, I32, I32, VP, C.c_size_t, VP], I32),
+        "la_packed_linear_bytes": ([I32, I32, I32, I32], C.c_size_t),
+        "la_pack_linear": ([I32, I32, VP, I32, I32, VP, VP], I32),
+        "la_linear_packed": ([I32, I32, VP, VP, VP, VP, I32, I32, I32, VP, C.c_size_t, VP], I32),
+        "la_packed_weight_bytes": ([P(la_model_dims)], C.c_uint64),
+        "la_pack_weights": ([P(la_model_dims), P(la_model), VP, VP], I32),
         "la_profile": ([VP, I32], I32),
         "la_profile_read": ([VP, P(la_profile_t)], I32),
     }
@@ -228,17 +234,25 @@ class DeviceModel:
                 self.w_gate_up[l, :F] = up(arr["w_gate"])
                 self.w_gate_up[l, F:] = up(arr["w_up"])
                 self.w_down[l] = up(arr["w_down"])
+        # the projections in the GEMM's packed layout; the plain copies are dropped
+        lib = load()
+        dstruct = dims_struct(dims)
+        self.packed = torch.empty(lib.la_packed_weight_bytes(C.byref(dstruct)), dtype=torch.uint8, device=dev)
+        plain = la_model(*[self.__dict__[n].data_ptr() for n in ("embed", "lm_head", "final_norm", "attn_norm",
+                                                                 "wqkv", "wo", "mlp_norm", "w_gate_up", "w_down")],
+                         self.packed.data_ptr())
+        _check(lib.la_pack_weights(C.byref(dstruct), C.byref(plain), _ptr(self.packed), _stream(None)))
         torch.cuda.synchronize(dev)
+        del self.lm_head, self.wqkv, self.wo, self.w_gate_up, self.w_down
 
     def struct(self) -> la_model:
-        return la_model(*[self.__dict__[n].data_ptr() for n in ("embed", "lm_head", "final_norm", "attn_norm",
-                                                                "wqkv", "wo", "mlp_norm", "w_gate_up", "w_down")])
+        return la_model(self.embed.data_ptr(), None, self.final_norm.data_ptr(), self.attn_norm.data_ptr(), None,
+                        None, self.mlp_norm.data_ptr(), None, None, self.packed.data_ptr())
 
     @property
     def weight_bytes(self) -> int:
-        return sum(t.numel() * t.element_size() for t in (self.embed, self.lm_head, self.final_norm, self.attn_norm,
-                                                          self.wqkv, self.wo, self.mlp_norm, self.w_gate_up,
-                                                          self.w_down))
+        return sum(t.numel() * t.element_size() for t in (self.embed, self.final_norm, self.attn_norm, self.mlp_norm,
+                                                          self.packed))
 
 
 # ----------------------------------------------------------------- session
@@ -415,4 +429,29 @@ def la_linear(epilogue, X, W, R=None, out=None, stream=None):
         out = torch.empty((M, N), dtype=torch.float32 if epilogue == LA_LINEAR_F32 else X.dtype, device=X.device)
     _check(lib.la_linear(dtype, epilogue, _ptr(X), _ptr(W), _ptr(out), _ptr(R), M, N, K, _ptr(ws), ws.numel(),
                          _stream(stream)))
+    return out
+
+
+def la_pack_linear(epilogue, W, stream=None):
+    """Packed copy of an nn.Linear weight (see include/la.h) as a flat uint8 device tensor."""
+    dtype = LA_DTYPE_BF16 if W.dtype == torch.bfloat16 else LA_DTYPE_F32
+    K = W.shape[1]
+    N = W.shape[0] // 2 if epilogue == LA_LINEAR_SWIGLU else W.shape[0]
+    lib = load()
+    Wp = torch.empty(max(lib.la_packed_linear_bytes(dtype, epilogue, N, K), 1), dtype=torch.uint8, device=W.device)
+    _check(lib.la_pack_linear(dtype, epilogue, _ptr(W), N, K, _ptr(Wp), _stream(stream)))
+    return Wp
+
+
+def la_linear_packed(epilogue, X, Wp, N, R=None, out=None, stream=None):
+    """la_linear with a weight packed by la_pack_linear (N = output columns)."""
+    dtype = LA_DTYPE_BF16 if X.dtype == torch.bfloat16 else LA_DTYPE_F32
+    M, K = X.shape
+    lib = load()
+    need = lib.la_linear_workspace(dtype, epilogue, M, N, K)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=X.device)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32 if epilogue == LA_LINEAR_F32 else X.dtype, device=X.device)
+    _check(lib.la_linear_packed(dtype, epilogue, _ptr(X), _ptr(Wp), _ptr(out), _ptr(R), M, N, K, _ptr(ws),
+                                ws.numel(), _stream(stream)))
     return out

@@ -67,7 +67,11 @@ typedef struct la_model_dims {
  *   wqkv       [L][(H + 2 Hkv) dh][d] rows: q heads, then k heads, then v heads
  *   wo         [L][d][H dh]
  *   w_gate_up  [L][2 F][d]            rows: gate (F rows), then up (F rows)
- *   w_down     [L][d][F]                                                      */
+ *   w_down     [L][d][F]
+ *   packed     la_packed_weight_bytes(dims) bytes written by la_pack_weights
+ *              from the five projections above.
+ * la_init reads embed, the norms and packed; the plain projection pointers
+ * are read only by la_pack_weights (they may be null for la_init). */
 typedef struct la_model {
   const void* embed;
   const void* lm_head;
@@ -78,7 +82,18 @@ typedef struct la_model {
   const void* mlp_norm;
   const void* w_gate_up;
   const void* w_down;
+  const void* packed;
 } la_model;
+
+/* Packed projections.  A round streams every projection matrix once over the
+ * packed rows ("M7.3", 0x05C), so the library keeps them in the order its
+ * GEMM reads them: the 16-row MFMA operand slices one workgroup consumes per
+ * step lie in one contiguous run.  la_packed_weight_bytes: size of that
+ * buffer for dims (0 for bad dims).  la_pack_weights: fill it (device,
+ * 256-byte aligned, caller-owned) from plain's wqkv, wo, w_gate_up, w_down
+ * and lm_head, on stream; LA_EINVAL for bad dims or null pointers. */
+uint64_t la_packed_weight_bytes(const la_model_dims* dims);
+int la_pack_weights(const la_model_dims* dims, const la_model* plain, void* packed, void* stream);
 
 /* ----------------------------------------------------------------- config */
 typedef struct la_config {
@@ -292,15 +307,24 @@ int la_attention(int32_t dtype, const void* q, const void* k_cache, const void* 
  *   LA_LINEAR_F32      Y[M][N] = X W^T in fp32 (Y is float)
  * X: device [M][K], W: device [N or 2N][K] (nn.Linear layout), dtype of
  * X/W/R/Y (except F32's Y) is dtype; fp32 accumulation.  1 <= M <= 256,
- * K a multiple of 128 (bf16) or 64 (fp32), N a multiple of 32 (16 for
- * SWIGLU).  The K split (and so every output bit) depends on (N, K) only,
- * never on M: a row's result is the same whatever other rows share the call.
- * workspace: device scratch of la_linear_workspace(...) bytes (0 allowed
- * when that returns 0). */
+ * K a multiple of 128 (bf16) or 64 (fp32), N a multiple of 16.  The K split
+ * (and so every output bit) depends on (N, K) only, never on M: a row's
+ * result is the same whatever other rows share the call.
+ * workspace: device scratch of la_linear_workspace(...) bytes; la_linear
+ * first writes the packed copy of W there (la_pack_linear), then runs
+ * la_linear_packed.
+ * la_pack_linear: W -> Wp (la_packed_linear_bytes bytes, device, 256-byte
+ * aligned), the layout la_pack_weights uses; la_linear_packed: the same
+ * product from a packed Wp, workspace as for la_linear (its first
+ * la_packed_linear_bytes, rounded up to 256, are not used). */
 enum { LA_LINEAR_STORE = 0, LA_LINEAR_RESIDUAL = 1, LA_LINEAR_SWIGLU = 2, LA_LINEAR_F32 = 3 };
 size_t la_linear_workspace(int32_t dtype, int32_t epilogue, int32_t M, int32_t N, int32_t K);
 int la_linear(int32_t dtype, int32_t epilogue, const void* X, const void* W, void* Y, const void* R, int32_t M,
               int32_t N, int32_t K, void* workspace, size_t workspace_bytes, void* stream);
+size_t la_packed_linear_bytes(int32_t dtype, int32_t epilogue, int32_t N, int32_t K);
+int la_pack_linear(int32_t dtype, int32_t epilogue, const void* W, int32_t N, int32_t K, void* Wp, void* stream);
+int la_linear_packed(int32_t dtype, int32_t epilogue, const void* X, const void* Wp, void* Y, const void* R,
+                     int32_t M, int32_t N, int32_t K, void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -337,6 +337,7 @@ LINEAR = [
     ("f32", 36, 32000, 4096),
     ("store", 181, 1536, 256),      # ragged M (12 row tiles), small K
     ("swiglu", 17, 512, 256),
+    ("store", 40, 1040, 384),       # ragged N: the last workgroup holds one live tile of four
 ]
 
 
@@ -379,3 +380,21 @@ def test_linear_matches_oracle_and_is_batch_invariant(case):
         assert np.mean(diff > 0) < 1e-3             # flips only where the exact value sits at a rounding tie
     print(f"linear {epi} M={M} N={N} K={K}: max abs err {err:.3g}, differing {np.mean(diff > 0):.2e}", flush=True)
     assert np.array_equal(got1[0], got[0])          # a row alone == the same row among M
+
+
+@pytest.mark.parametrize("epi,M,N,K", [("store", 24, 1040, 384), ("f32", 9, 32000, 4096), ("swiglu", 33, 1040, 256)])
+def test_linear_packed_matches_linear(epi, M, N, K):
+    """A weight packed once (la_pack_linear) gives la_linear's bits through la_linear_packed."""
+    rng = synthetic.misc_rng(0, 79, M)
+    rows_w = 2 * N if epi == "swiglu" else N
+    X = synthetic.bf16_bits_from_f32(rng.standard_normal((M, K)).astype(np.float32))
+    W = synthetic.bf16_bits_from_f32((rng.standard_normal((rows_w, K)) * 0.02).astype(np.float32))
+    dev = lambda a: torch.from_numpy(a.view(np.int16)).to(DEV).view(torch.bfloat16)
+    code = {"store": la.LA_LINEAR_STORE, "swiglu": la.LA_LINEAR_SWIGLU, "f32": la.LA_LINEAR_F32}[epi]
+    Xd, Wd = dev(X), dev(W)
+    y = la.la_linear(code, Xd, Wd)
+    Wp = la.la_pack_linear(code, Wd)
+    yp = la.la_linear_packed(code, Xd, Wp, N)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.uint8) if y.dtype != torch.float32 else y.view(torch.int32),
+                       yp.view(torch.uint8) if yp.dtype != torch.float32 else yp.view(torch.int32))

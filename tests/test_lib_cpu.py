@@ -22,7 +22,7 @@ def _lib():
 def test_exports_match_header():
     lib = _lib()
     hdr = open(os.path.join(ROOT, "include", "la.h")).read()
-    names = set(re.findall(r"^\s*(?:int|void|size_t|const char\*)\s+(la_\w+)\s*\(", hdr, flags=re.M))
+    names = set(re.findall(r"^\s*(?:int|void|size_t|uint64_t|const char\*)\s+(la_\w+)\s*\(", hdr, flags=re.M))
     assert len(names) >= 15
     for n in names:
         assert hasattr(lib, n), n
