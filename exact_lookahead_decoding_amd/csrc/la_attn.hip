@@ -241,66 +241,51 @@ __device__ __forceinline__ void fold_state(float& ma, float& la, f32x4* oa, floa
 }
 
 
-// Store one row's state.  The lane holds output tiles dt0 .. dt0 + NT - 1 of
-// head dimension NDT*(4g + r) + dt; (m, l) is written by the owner of dt0 = 0.
-template <int NDT, int NT>
-__device__ __forceinline__ void store_state(float* po, float* pml, int g, int dt0, float m, float l, const f32x4* o) {
-  if (g == 0 && dt0 == 0) *(float2*)pml = make_float2(m, l);
-  if (m == NEG_INF) return;
-  float* dst = po + 4 * NDT * g + dt0;
-  if constexpr (NT % 4 == 0) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int q = 0; q < NT; q += 4)
-        *(float4*)(dst + NDT * r + q) = make_float4(o[q][r], o[q + 1][r], o[q + 2][r], o[q + 3][r]);
-  } else if constexpr (NT == 2) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) *(float2*)(dst + NDT * r) = make_float2(o[0][r], o[1][r]);
-  } else {
-    static_assert(NT == 1 && NDT == 1, "output tiles");
-    *(float4*)dst = make_float4(o[0][0], o[0][1], o[0][2], o[0][3]);
-  }
-}
-
-// Class workgroup: KV head g_kv, class cls, row group rg of TL tiles.  Its
-// TL * DHS waves share one LDS ring: wave w owns tile w % TL and output tiles
-// (head dimensions) slice w / TL of DHS; the DHS waves of a tile compute the
-// same scores and softmax (the same bits) and each accumulates its slice of O.
-template <typename T, int DH, int TL, int DHS>
-__global__ void __launch_bounds__(64 * TL * DHS) la_attn_kernel(LaAttnArgs a) {
+// One workgroup per (KV head, row group of TL tiles of 16 query rows);
+// wave w is class c = w / TL of tile slot w % TL.  Three phases:
+//   1. prefix: ring stage s holds keys [128 s, 128 s + 128) of the head (the
+//      class-c chunk 4 s + c, K and V, 16-byte pieces XOR-swizzled by row) for
+//      every chunk below shared_end (or up to the largest row position when
+//      nothing reaches past it); each class wave takes its chunk of the stage
+//      with the online step, so a stage is read from HBM once for all the
+//      workgroup's tiles and classes;
+//   2. tail: the chunks reaching past shared_end (at most one per class) are
+//      applied last in their class: the ring's space is reused to stage, per
+//      tile, the committed rows [32 tail0, shared_end) and, for each branch in
+//      the tile, its workspace rows of positions shared_end .. max_pos (read
+//      through the branch path); the scores come per branch and P V runs once
+//      per branch (rows of other branches add exact zeros);
+//   3. fold: classes 1..3 hand their states to class 0 through LDS, which
+//      folds 0, 1, 2, 3 in order and stores O / l.
+// Every global load is a DMA into LDS read back with inline asm; the waits
+// are static vmcnt counts (every wave issues the same DMA count per stage).
+template <typename T, int DH, int TL>
+__global__ void __launch_bounds__(256 * TL) __attribute__((amdgpu_waves_per_eu(1, TL))) la_attn_kernel(LaAttnArgs a) {
   typedef AttnT<T, DH> AT;
   typedef typename AT::QF QF;
-  constexpr int NW = TL * DHS;
+  typedef typename AT::VV VV;
+  constexpr int NW = NCLS * TL;
   constexpr int ROWB = AT::ROWB, PIECES = AT::PIECES, LP = AT::LP, NDT = AT::NDT, VB = AT::VB;
-  constexpr int NT = NDT / DHS;                 // output tiles of a wave
-  constexpr int VBW = VB / DHS;                 // bytes of one key row a wave's lane reads for PV
-  static_assert(NDT % DHS == 0 && VBW % 4 == 0, "head-dimension split");
-  typedef Words<VBW / 4> VV;
-  constexpr int CHB = CH * ROWB;               // bytes of K (or V) of one chunk
-  constexpr int NBLK = 2 * CHB / 1024;         // 1 KB DMA blocks per chunk, K then V
-  constexpr int CW = NBLK >= NW ? NBLK / NW : 1;
-  static_assert(NBLK % NW == 0 || NW > NBLK, "DMA blocks per wave");
-  constexpr int DEPTH = ring_depth(CHB, TL, ROWB, CW);
-  static_assert(DEPTH >= 2, "ring stages");
-  // dynamic LDS: DEPTH ring stages of K and V, then each tile's Q, then each
-  // tile's 16 row positions.  Every global load of this kernel is a DMA into
-  // LDS read back with inline asm.
+  constexpr int CHB = CH * ROWB;                // K (or V) of one chunk
+  constexpr int BLKB = NCLS * 2 * CHB;          // one ring stage: 4 chunks, K then V each
+  constexpr int NDMA = BLKB / 1024;
+  constexpr int CW = NDMA / NW;                 // DMA instructions per stage and wave
+  static_assert(NDMA % NW == 0 && CW >= 1, "DMA blocks per wave");
+  constexpr int DEPTH = 2;
+  constexpr int RPB = 1024 / ROWB;              // key rows per 1 KB DMA block
+  // Q tiles, row positions (one DMA of 64 lanes), branch paths; the ring starts 1 KB aligned
+  constexpr int FIX = (TL * (16 * ROWB + 256 + 16 * 64 * 4) + 1023) & ~1023;
   extern __shared__ __attribute__((aligned(1024))) char lds[];
+  char* const ring = lds + FIX;                 // ring stages, later the tail rows, then the fold states
 
-  // block -> (XCD, KV head, class, row group)
+  // block -> (XCD, KV head, row group): the row groups of one head share an XCD (and its L2)
   const int xcd = blockIdx.x & 7, bi = blockIdx.x >> 3;
-  const int hpx = (a.Hkv + 7) >> 3;
   const int rg = bi % a.rgroups;
-  const int hl = (bi / a.rgroups) % hpx;
-  const int cls = bi / (a.rgroups * hpx);
-  const int g_kv = xcd + 8 * hl;
-  if (g_kv >= a.Hkv || cls >= NCLS) return;
-  const int n = a.class_last >= cls ? (a.class_last - cls) / NCLS + 1 : 0;
-  if (n == 0) return;
+  const int g_kv = xcd + 8 * (bi / a.rgroups);
+  if (g_kv >= a.Hkv) return;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int tslot = wave % TL, half = wave / TL;
+  const int cls = wave / TL, tslot = wave % TL;
   const int g = lane >> 4, c16 = lane & 15;
   const int se = a.shared_end;
   const float sl2 = a.scale_log2;
@@ -314,11 +299,12 @@ __global__ void __launch_bounds__(64 * TL * DHS) la_attn_kernel(LaAttnArgs a) {
   const bool tv = tile < group * rtiles;
   const int hh = g_kv * group + (tv ? tile / rtiles : 0);
   const int row0 = (tv ? tile % rtiles : 0) * 16;
-  const bool rvalid = tv && row0 + c16 < a.Q;
-  char* const qa = lds + DEPTH * 2 * CHB + tslot * 16 * ROWB;
-  char* const pa = lds + DEPTH * 2 * CHB + TL * 16 * ROWB + tslot * 256;
-  constexpr int RPB = 1024 / ROWB;              // rows per 1 KB DMA block
-  if (half == 0) {
+  const int row = row0 + c16;
+  const bool rvalid = tv && row < a.Q;
+  char* const qa = lds + tslot * 16 * ROWB;
+  char* const pa = lds + TL * 16 * ROWB + tslot * 256;
+  int* const spath = (int*)(lds + TL * (16 * ROWB + 256)) + tslot * 1024;  // [16 branches][64 positions]
+  if (cls == 0) {
     __builtin_amdgcn_global_load_lds((const void*)(a.pos + min(row0 + (lane & 15), a.Q - 1)), (lds_void_t*)pa, 4, 0,
                                      0);
 #pragma unroll
@@ -329,32 +315,61 @@ __global__ void __launch_bounds__(64 * TL * DHS) la_attn_kernel(LaAttnArgs a) {
     }
   }
 
-  // chunk k of the class into a ring stage.  Every step issues exactly one
-  // stage, so the number of DMA operations in flight is the same on every path
-  // and the waits are static; past the last chunk all lanes load one 16-byte
-  // piece (a dummy that nobody reads).
-  auto issue = [&](char* stage, int k) {
-    const int c = cls + NCLS * k;
+  // ring stage s: chunks 4 s .. 4 s + 3; past the last stage every lane loads
+  // one 16-byte piece (a dummy that nobody reads), so every wave issues CW
+  // DMA instructions per stage on every path
+  const int nblk = (a.class_last + NCLS) / NCLS;   // stages (class_last = -1: none)
+  // wave w brings the DMA blocks w*CW .. w*CW + CW - 1 of a stage (a
+  // contiguous run inside its chunk cw of the stage: CW divides the 1 KB
+  // blocks of a chunk half or is a multiple of them).  The lane's source
+  // offset inside a chunk is the same for every stage; only stages that
+  // reach past shared_end clamp rows.
+  constexpr int HB = CHB / 1024;                // 1 KB blocks in a chunk's K (or V)
+  static_assert(HB % CW == 0 || CW % HB == 0, "DMA runs");
+  const int b0 = wave * CW;
+  const int cw = b0 / (2 * HB);
+  // K or V of block j: one half for the whole run when CW <= HB, else the
+  // run is a whole chunk (K blocks, then V blocks)
+  constexpr bool WHOLE = CW > HB;
+  const char* const half0 = ((b0 / HB) & 1) ? vc : kc;
+  auto kv_of = [&](int j) __attribute__((always_inline)) -> const char* { return WHOLE ? ((j / HB) ? vc : kc) : half0; };
+  int oj[CW];
 #pragma unroll
-    for (int j = 0; j < CW; ++j) {
-      const int b = wave + NW * j;
-      if (b < NBLK) {
-        const bool isv = b >= NBLK / 2;
-        const int bb = isv ? b - NBLK / 2 : b;
-        const int L = bb * 1024 + 16 * lane;
-        const int r = L / ROWB, slot = (L % ROWB) / 16;
-        const int piece = slot ^ (r % PIECES);
-        const char* src = k < n ? (isv ? vc : kc) + (size_t)min(CH * c + r, se - 1) * ROWB + 16 * piece
-                                : kc + (size_t)(se - 1) * ROWB;
-        __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(stage + (isv ? CHB : 0) + bb * 1024), 16,
-                                         0, 0);
+  for (int j = 0; j < CW; ++j) {
+    const int r = ((b0 + j) % HB) * RPB + lane / PIECES;
+    oj[j] = r * ROWB + 16 * ((lane % PIECES) ^ (r % PIECES));
+  }
+  auto issue = [&](char* stage, int s) __attribute__((always_inline)) {
+    const int x0 = CH * (NCLS * s + cw);
+    if (s < nblk && x0 + CH <= se) {            // the whole chunk lies below shared_end
+#pragma unroll
+      for (int j = 0; j < CW; ++j) {
+        const char* base = kv_of(j);
+        __builtin_amdgcn_global_load_lds((const void*)(base + (size_t)x0 * ROWB + oj[j]),
+                                         (lds_void_t*)(stage + (b0 + j) * 1024), 16, 0, 0);
       }
+    } else if (s < nblk) {                      // rows past shared_end - 1 repeat it (never visible)
+#pragma unroll
+      for (int j = 0; j < CW; ++j) {
+        const char* base = kv_of(j);
+        const int r = ((b0 + j) % HB) * RPB + lane / PIECES;
+        const int off = oj[j] - r * ROWB;
+        __builtin_amdgcn_global_load_lds((const void*)(base + (size_t)min(x0 + r, se - 1) * ROWB + off),
+                                         (lds_void_t*)(stage + (b0 + j) * 1024), 16, 0, 0);
+      }
+    } else {                                    // past the last stage: one valid 16-byte piece
+#pragma unroll
+      for (int j = 0; j < CW; ++j)
+        __builtin_amdgcn_global_load_lds((const void*)(kc + (size_t)(se - 1) * ROWB),
+                                         (lds_void_t*)(stage + (b0 + j) * 1024), 16, 0, 0);
     }
   };
+  // the row's branch (read now, used by the tail phase after the ring)
+  const int br = (a.n_tail > 0 && rvalid) ? a.branch[row] : -1;
 #pragma unroll
-  for (int k = 0; k < DEPTH; ++k) issue(lds + k * 2 * CHB, k);
-  wait_vm<(CW * DEPTH < 63 ? CW * DEPTH : 63)>();  // this wave's Q and positions (issued first) have landed
-  ring_barrier();                                   // ... and those of the other waves
+  for (int k = 0; k < DEPTH; ++k) issue(ring + k * BLKB, k);
+  wait_vm<(CW * DEPTH < 63 ? CW * DEPTH : 63)>();   // this wave's Q and positions (issued first) have landed
+  ring_barrier();                                    // ... and those of the other waves
   QF qf;
   int pos;
   {
@@ -377,49 +392,59 @@ __global__ void __launch_bounds__(64 * TL * DHS) la_attn_kernel(LaAttnArgs a) {
   for (int o = 32; o > 0; o >>= 1) pmin = min(pmin, __shfl_xor(pmin, o, 64));
   pmin = __builtin_amdgcn_readfirstlane(pmin);
 
-  // lane parts of the fragment addresses (stage, group and slot-half offsets are immediates)
+  // lane parts of the fragment addresses of the class's chunk (stage offsets are immediates)
   uint32_t koff[LP], voff[4];
 #pragma unroll
-  for (int s = 0; s < LP; ++s) koff[s] = lds_addr(lds + c16 * ROWB + 16 * ((LP * g + s) ^ (c16 % PIECES)));
+  for (int s = 0; s < LP; ++s)
+    koff[s] = lds_addr(ring + cls * 2 * CHB + c16 * ROWB + 16 * ((LP * g + s) ^ (c16 % PIECES)));
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int kk = 4 * g + e;                   // slot_key(g, e); slot e + 4 is 16 rows further
-    const int off = VB * c16 + VBW * half;
-    voff[e] = lds_addr(lds + CHB + kk * ROWB + 16 * ((off / 16) ^ (kk % PIECES)) + off % 16);
+    const int off = VB * c16;
+    voff[e] = lds_addr(ring + cls * 2 * CHB + CHB + kk * ROWB + 16 * ((off / 16) ^ (kk % PIECES)) + off % 16);
   }
 
   float M = NEG_INF, L = 0.f;
-  f32x4 O[NT];
+  f32x4 O[NDT];
 #pragma unroll
-  for (int dt = 0; dt < NT; ++dt) O[dt] = f32x4{0, 0, 0, 0};
+  for (int dt = 0; dt < NDT; ++dt) O[dt] = f32x4{0, 0, 0, 0};
 
-  auto step = [&](auto SI, int k) {
+  auto step = [&](auto SI, int s) __attribute__((always_inline)) {
     constexpr int S = decltype(SI)::value;
-    constexpr int SB = S * 2 * CHB;             // stage base
+    constexpr int SB = S * BLKB;                // stage base
     constexpr int SBH = SB & ~65535, SBL = SB & 65535;   // ds offsets reach 64 KB
-    wait_vm<CW * (DEPTH - 1)>();                // chunk k landed (DEPTH - 1 later stages may be in flight)
+    wait_vm<CW * (DEPTH - 1)>();                // stage s landed (the next one may be in flight)
     ring_barrier();
-    if (k < n) {
-      const int x0 = CH * (cls + NCLS * k);
-      typename LdsT<16>::T kraw[2 * LP];
+    const int k = NCLS * s + cls;               // the class's chunk
+    const bool live = k <= a.class_last;
+    // the chunk's K and V go to registers first, so the stage is released
+    // (and the stage two steps ahead issued) before any arithmetic
+    typename LdsT<16>::T kraw[2 * LP];
+    typename LdsT<VB>::T vraw[8];
+    if (live) {
 #pragma unroll
-      for (int s = 0; s < LP; ++s) {
-        kraw[s] = lds_read<16, SBL>(koff[s] + SBH);
-        kraw[LP + s] = lds_read<16, SBL + 16 * ROWB>(koff[s] + SBH);
+      for (int q = 0; q < LP; ++q) {
+        kraw[q] = lds_read<16, SBL>(koff[q] + SBH);
+        kraw[LP + q] = lds_read<16, SBL + 16 * ROWB>(koff[q] + SBH);
       }
-      typename LdsT<VBW>::T vraw[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        vraw[e] = lds_read<VBW, SBL>(voff[e] + SBH);
-        vraw[e + 4] = lds_read<VBW, SBL + 16 * ROWB>(voff[e] + SBH);
+        vraw[e] = lds_read<VB, SBL>(voff[e] + SBH);
+        vraw[e + 4] = lds_read<VB, SBL + 16 * ROWB>(voff[e] + SBH);
       }
       lds_wait(kraw);
+      lds_wait(vraw);
+    }
+    ring_barrier();                             // every wave has read the stage
+    issue(ring + SB, s + DEPTH);
+    if (live) {
+      const int x0 = CH * k;
       float sc[8];
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj) {
         QF kf;
 #pragma unroll
-        for (int s = 0; s < LP; ++s) kf.p[s] = __builtin_bit_cast(u32x4, kraw[LP * jj + s]);
+        for (int q = 0; q < LP; ++q) kf.p[q] = __builtin_bit_cast(u32x4, kraw[LP * jj + q]);
         const f32x4 s4 = AT::qk(kf, qf);
 #pragma unroll
         for (int r = 0; r < 4; ++r) sc[4 * jj + r] = s4[r];
@@ -429,92 +454,23 @@ __global__ void __launch_bounds__(64 * TL * DHS) la_attn_kernel(LaAttnArgs a) {
         for (int e = 0; e < 8; ++e) sc[e] = x0 + slot_key(g, e) <= pos ? sc[e] : NEG_INF;
       }
       const float wa = chunk_softmax(sc, sl2, M, L);
-      lds_wait(vraw);
       VV vv[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) vv[e] = __builtin_bit_cast(VV, vraw[e]);
-      ring_barrier();                           // every wave has read the stage
-      scale_o<NT>(O, wa);
       const typename AT::PP pp = AT::prep(sc);
+      scale_o<NDT>(O, wa);
 #pragma unroll
-      for (int dt = 0; dt < NT; ++dt) O[dt] = AT::pv(dt, vv, pp, O[dt]);
-      issue(lds + SB, k + DEPTH);
-    } else {                                    // past the last chunk: keep the DMA rhythm only
-      ring_barrier();
-      issue(lds + SB, k + DEPTH);
+      for (int dt = 0; dt < NDT; ++dt) O[dt] = AT::pv(dt, vv, pp, O[dt]);
     }
   };
-  for (int k0 = 0; k0 < n; k0 += DEPTH)
-    static_for<0, DEPTH>([&](auto SI) { step(SI, k0 + decltype(SI)::value); });
-  wait_vm<0>();                                   // no DMA may land after the workgroup has left
-  if (rvalid) {
-    const size_t base = ((size_t)cls * a.H + hh) * a.Q + row0 + c16;
-    store_state<NDT, NT>(a.part_o + base * DH, a.part_ml + base * 2, g, half * NT, M, L, O);
-  }
-}
-
-// Chunks that reach past shared_end and the final fold.  One wave per tile of
-// 16 rows: for each class it takes the class state, applies the class's tail
-// chunk with the online step (computed here from the tile's tail keys, staged
-// in LDS: each lane reads its key's K/V row through the branch path, once per
-// branch present in the tile), folds the classes in order and stores O / l.
-template <typename T, int DH>
-__global__ void __launch_bounds__(64) la_attn_tail_merge_kernel(LaAttnArgs a) {
-  typedef AttnT<T, DH> AT;
-  typedef typename AT::QF QF;
-  typedef typename AT::VV VV;
-  constexpr int ROWB = AT::ROWB, LP = AT::LP, NDT = AT::NDT, VB = AT::VB;
-  __shared__ int spath[16][64];                 // the tile's branches: workspace row of position shared_end + e
-  extern __shared__ __attribute__((aligned(1024))) char tls[];   // staged tail K rows, then V rows
-  const int lane = threadIdx.x, g = lane >> 4, c16 = lane & 15;
-  const int group = a.H / a.Hkv;
-  const int rtiles = (a.Q + 15) >> 4;
-  const int tiles_kv = group * rtiles;
-  const int g_kv = blockIdx.x / tiles_kv;
-  if (g_kv >= a.Hkv) return;
-  const int tile = blockIdx.x % tiles_kv;
-  const int hh = g_kv * group + tile / rtiles;
-  const int row = (tile % rtiles) * 16 + c16;
-  const bool rvalid = row < a.Q;
-  const int se = a.shared_end;
-  const float sl2 = a.scale_log2;
-
-  // class states of the lane's row, all loads issued up front
-  float cm[NCLS], cl[NCLS];
-  f32x4 co[NCLS][NDT];
-#pragma unroll
-  for (int cls = 0; cls < NCLS; ++cls) {
-    cm[cls] = NEG_INF;
-    cl[cls] = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) co[cls][dt] = f32x4{0, 0, 0, 0};
-    if (cls <= a.class_last && rvalid) {
-      const size_t base = ((size_t)cls * a.H + hh) * a.Q + row;
-      const float2 ml = *(const float2*)(a.part_ml + base * 2);
-      cm[cls] = ml.x;
-      cl[cls] = ml.y;
-      const float* src = a.part_o + base * DH + 4 * NDT * g;
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) co[cls][dt][r] = src[NDT * r + dt];
-    }
-  }
+  for (int s0 = 0; s0 < nblk; s0 += DEPTH)
+    static_for<0, DEPTH>([&](auto SI) { step(SI, s0 + decltype(SI)::value); });
+  wait_vm<0>();                                   // the dummy stages have landed: the ring is free
+  ring_barrier();
 
   if (a.n_tail > 0) {
-    const int pos = rvalid ? a.pos[row] : -1;
-    const int br = rvalid ? a.branch[row] : -1;
-    const char* kc = (const char*)a.kc + (size_t)g_kv * a.T_cap * ROWB;
-    const char* vc = (const char*)a.vc + (size_t)g_kv * a.T_cap * ROWB;
-    const char* kw = (const char*)a.kw + (size_t)g_kv * a.ws_cap * ROWB;
-    const char* vw = (const char*)a.vw + (size_t)g_kv * a.ws_cap * ROWB;
-    QF qf;
-    {
-      const char* qrow = (const char*)a.q + ((size_t)(rvalid ? row : 0) * a.H + hh) * ROWB + 16 * LP * g;
-#pragma unroll
-      for (int s = 0; s < LP; ++s) qf.p[s] = rvalid ? *(const u32x4*)(qrow + 16 * s) : u32x4{0, 0, 0, 0};
-    }
-    // the tile's branches that reach a tail chunk (at most 16 rows, so at most 16)
+    // the tile's branches that reach a tail chunk (at most 16); every class
+    // wave of the tile finds the same list
     const bool need0 = rvalid && pos >= CH * a.tail0;
     int nbr = 0;
     int bl = -1;                                  // lane i < nbr: branch i
@@ -525,67 +481,72 @@ __global__ void __launch_bounds__(64) la_attn_tail_merge_kernel(LaAttnArgs a) {
       if (lane == nbr) bl = b;
       ++nbr;
     }
-    // their paths into LDS: spath[i][e] = workspace row of position se + e on
-    // branch i, -1 when that position is not on the path.  Lane i reads branch
-    // i's path length, then every lane reads entry e = lane of every branch
-    // (all loads of a round issued together)
-    const int plen = lane < nbr ? min(a.path_len[bl], a.maxp) : 0;
-    int wv[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int b = __shfl(bl, i, 64), pl = __shfl(plen, i, 64);
-      wv[i] = (i < nbr && lane < pl) ? a.path[(size_t)b * a.maxp + lane] : -1;
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      if (i < nbr) spath[i][lane] = (unsigned)wv[i] < (unsigned)a.n_ws ? wv[i] : -1;
-    __syncthreads();
-    // The tail keys of the tile's branches are gathered into LDS with one round
-    // of DMA (16-byte pieces XOR-swizzled by staged row): first the committed
-    // rows [X0, se) shared by every branch, then EP rows per branch for the
-    // positions se .. max_pos (a clamped committed row where a position is not
-    // on the branch's path; it is never visible to the branch's rows).
     const int X0 = CH * a.tail0;
     const int ncom = se - X0;                       // 0 .. 31
-    const int EP = a.max_pos - se + 1;              // 1 .. 63
-    const int bb = min(nbr, (TAIL_ROWS - ncom) / EP);   // branches staged at once (>= 1)
-    constexpr int RPB = 1024 / ROWB, PIECES = AT::PIECES;
-    char* const ks = tls;
-    char* const vs = tls + TAIL_ROWS * ROWB;
-    auto stage = [&](int i0, int nb) {
-      const int nr = ncom + nb * EP;
-      for (int blk = 0; blk * RPB < nr; ++blk) {
+    const int EP = a.max_pos - se + 1;              // 1 .. 64
+    // the tile's branch paths: spath[i][e] = workspace row of position se + e
+    // on branch i (-1 when the position is not on it); class 0 writes them,
+    // every load issued before any is used
+    if (cls == 0) {
+      const int plen = lane < nbr ? min(a.path_len[bl], a.maxp) : 0;
+      int wv[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int b = __shfl(bl, i, 64), pl = __shfl(plen, i, 64);
+        wv[i] = (i < nbr && lane < pl) ? a.path[(size_t)b * a.maxp + lane] : -1;
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (i < nbr) spath[i * 64 + lane] = (unsigned)wv[i] < (unsigned)a.n_ws ? wv[i] : -1;
+    }
+    // branches staged at once per tile (the committed rows, then EP rows per
+    // branch), and the batches every tile of the workgroup goes through
+    const int bb = (a.trows - ncom) / EP;           // >= 1 (the launcher sizes trows)
+    int* const nbat = (int*)(lds + TL * 16 * ROWB);   // the row positions' space, free since the prologue
+    if (cls == 0 && lane == 0) nbat[tslot] = (nbr + bb - 1) / bb;
+    __syncthreads();
+    int nbatch = 0;
+#pragma unroll
+    for (int t = 0; t < TL; ++t) nbatch = max(nbatch, nbat[t]);
+    char* const ks = ring + tslot * 2 * a.trows * ROWB;
+    char* const vs = ks + a.trows * ROWB;
+    const char* kw = (const char*)a.kw + (size_t)g_kv * a.ws_cap * ROWB;
+    const char* vw = (const char*)a.vw + (size_t)g_kv * a.ws_cap * ROWB;
+    const int tau = (cls - a.tail0 % NCLS + NCLS) % NCLS;   // the class's tail chunk (at most one)
+    const int x0 = CH * (a.tail0 + tau);
+    const bool need = tau < a.n_tail && rvalid && pos >= x0;
+    for (int bt = 0; bt < nbatch; ++bt) {
+      const int i0 = bt * bb;
+      const int nb = max(0, min(bb, nbr - i0));
+      // staged row of key x on batch branch bi (x >= X0); a clamped committed
+      // row where a position is not on the branch's path (never visible to it)
+      const int nr = nb > 0 ? ncom + nb * EP : 0;
+      for (int blk = cls; blk * RPB < nr; blk += NCLS) {
         const int j = blk * RPB + lane / PIECES;
         const int piece = (lane % PIECES) ^ (j % PIECES);
         int crow = se - 1, wrow = -1;
         if (j < ncom) crow = X0 + j;
-        else if (j < nr) wrow = spath[i0 + (j - ncom) / EP][(j - ncom) % EP];
+        else if (j < nr) wrow = spath[(i0 + (j - ncom) / EP) * 64 + (j - ncom) % EP];
         const size_t off = (size_t)(wrow >= 0 ? wrow : crow) * ROWB + 16 * piece;
-        __builtin_amdgcn_global_load_lds((const void*)((wrow >= 0 ? kw : kc) + off), (lds_void_t*)(ks + blk * 1024), 16,
-                                         0, 0);
-        __builtin_amdgcn_global_load_lds((const void*)((wrow >= 0 ? vw : vc) + off), (lds_void_t*)(vs + blk * 1024), 16,
-                                         0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)((wrow >= 0 ? kw : kc) + off), (lds_void_t*)(ks + blk * 1024),
+                                         16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)((wrow >= 0 ? vw : vc) + off), (lds_void_t*)(vs + blk * 1024),
+                                         16, 0, 0);
       }
       wait_vm<0>();
-    };
-    // staged row of key x on batch branch bi (x >= X0)
-    auto srow = [&](int x, int bi) -> int {
-      if (x < se) return x - X0;
-      const int e = x - se;
-      return e < EP ? ncom + bi * EP + e : 0;
-    };
-    const bool one = nbr <= bb;
-    if (one) stage(0, nbr);
-    // the online step of tail chunk x0 on top of a class state (m, l, o)
-    auto tail_step = [&](int x0, float& m, float& l, f32x4* o) {
-      const bool need = rvalid && pos >= x0;
-      if (__ballot(need) == 0ull) return;
-      float sc[8];
+      __syncthreads();
+      auto srow = [&](int x, int bi) -> int {
+        if (x < se) return x - X0;
+        const int e = x - se;
+        return e < EP ? ncom + bi * EP + e : 0;
+      };
+      // rows of this batch's branches: the chunk's online step (for the
+      // wave's other rows every score stays -inf, which leaves their state
+      // exactly as it is, and P V adds exact zeros)
+      if (nb > 0 && __ballot(need) != 0ull) {
+        float sc[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sc[e] = NEG_INF;
-      for (int i0 = 0; i0 < nbr; i0 += bb) {
-        const int nb = min(bb, nbr - i0);
-        if (!one) stage(i0, nb);
+        for (int e = 0; e < 8; ++e) sc[e] = NEG_INF;
         for (int bi = 0; bi < nb; ++bi) {
           const int b = __shfl(bl, i0 + bi, 64);
           const bool mine = need && br == b;
@@ -595,7 +556,8 @@ __global__ void __launch_bounds__(64) la_attn_tail_merge_kernel(LaAttnArgs a) {
             const int r = srow(x0 + 16 * jj + c16, bi);
             QF kf;
 #pragma unroll
-            for (int s = 0; s < LP; ++s) kf.p[s] = *(const u32x4*)(ks + r * ROWB + 16 * ((LP * g + s) ^ (r % PIECES)));
+            for (int q = 0; q < LP; ++q)
+              kf.p[q] = *(const u32x4*)(ks + r * ROWB + 16 * ((LP * g + q) ^ (r % PIECES)));
             const f32x4 s4 = AT::qk(kf, qf);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -604,13 +566,8 @@ __global__ void __launch_bounds__(64) la_attn_tail_merge_kernel(LaAttnArgs a) {
             }
           }
         }
-      }
-      // softmax part and rescale, then P V once per branch (the other rows add exact zeros)
-      const float wa = chunk_softmax(sc, sl2, m, l);
-      scale_o<NDT>(o, wa);
-      for (int i0 = 0; i0 < nbr; i0 += bb) {
-        const int nb = min(bb, nbr - i0);
-        if (!one) stage(i0, nb);
+        const float wa = chunk_softmax(sc, sl2, M, L);
+        scale_o<NDT>(O, wa);
         for (int bi = 0; bi < nb; ++bi) {
           const int b = __shfl(bl, i0 + bi, 64);
           const bool mine = need && br == b;
@@ -626,85 +583,112 @@ __global__ void __launch_bounds__(64) la_attn_tail_merge_kernel(LaAttnArgs a) {
           }
           const typename AT::PP pp = AT::prep(ps);
 #pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) o[dt] = AT::pv(dt, vv, pp, o[dt]);
+          for (int dt = 0; dt < NDT; ++dt) O[dt] = AT::pv(dt, vv, pp, O[dt]);
         }
       }
-    };
-    // each tail chunk belongs to its own class (at most NCLS of them)
-#pragma unroll
-    for (int cls = 0; cls < NCLS; ++cls) {
-      const int tau = (cls - a.tail0 % NCLS + NCLS) % NCLS;
-      if (tau < a.n_tail) tail_step(CH * (a.tail0 + tau), cm[cls], cl[cls], co[cls]);
+      __syncthreads();                            // the staged rows are no longer read
     }
   }
 
-  float M = NEG_INF, L = 0.f;
-  f32x4 O[NDT];
+  // fold: classes 1..3 hand (m, l, O) over (lane for lane: same row, same
+  // head dimensions), class 0 folds 0, 1, 2, 3 in order
+  float* const xf = (float*)ring + (size_t)(tslot * (NCLS - 1)) * 64 * (4 * NDT + 2);
+  if (cls > 0) {
+    float* d = xf + (size_t)(cls - 1) * 64 * (4 * NDT + 2) + lane * (4 * NDT + 2);
+    d[0] = M;
+    d[1] = L;
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) O[dt] = f32x4{0, 0, 0, 0};
+    for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-  for (int cls = 0; cls < NCLS; ++cls) fold_state<NDT>(M, L, O, cm[cls], cl[cls], co[cls]);
-  if (rvalid) {
-    // lane holds head dimensions NDT*(4g + r) + dt: 4*NDT contiguous values
-    T* dst = (T*)a.o + ((size_t)row * a.H + hh) * DH + 4 * NDT * g;
+      for (int r = 0; r < 4; ++r) d[2 + 4 * dt + r] = O[dt][r];
+  }
+  __syncthreads();
+  if (cls == 0 && rvalid) {
+    float Mf = NEG_INF, Lf = 0.f;
+    f32x4 Of[NDT];
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+    for (int dt = 0; dt < NDT; ++dt) Of[dt] = f32x4{0, 0, 0, 0};
+    fold_state<NDT>(Mf, Lf, Of, M, L, O);
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) st<T>(dst + NDT * r + dt, O[dt][r] / L);
+    for (int c = 1; c < NCLS; ++c) {
+      const float* d = xf + (size_t)(c - 1) * 64 * (4 * NDT + 2) + lane * (4 * NDT + 2);
+      f32x4 Oc[NDT];
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Oc[dt][r] = d[2 + 4 * dt + r];
+      fold_state<NDT>(Mf, Lf, Of, d[0], d[1], Oc);
+    }
+    // lane holds head dimensions NDT*(4g + r) + dt: 4*NDT contiguous values,
+    // stored as 16-byte pieces
+    constexpr int EPW = 4 / sizeof(T);            // elements per 32-bit word
+    uint32_t ow[4 * NDT / EPW];
+#pragma unroll
+    for (int w = 0; w < 4 * NDT / EPW; ++w) {
+      uint32_t v = 0;
+#pragma unroll
+      for (int q = 0; q < EPW; ++q) {
+        const int i = w * EPW + q, r = i / NDT, dt = i % NDT;
+        const float x = Of[dt][r] / Lf;
+        v |= (sizeof(T) == 2 ? (uint32_t)f2bf(x) : __float_as_uint(x)) << (16 * q);
+      }
+      ow[w] = v;
+    }
+    u32x4* dst = (u32x4*)((T*)a.o + ((size_t)row * a.H + hh) * DH + 4 * NDT * g);
+#pragma unroll
+    for (int q = 0; q < 4 * NDT / EPW / 4; ++q) dst[q] = u32x4{ow[4 * q], ow[4 * q + 1], ow[4 * q + 2], ow[4 * q + 3]};
   }
 }
 
 int la_attention_parts() { return NCLS; }
 
-template <typename T, int DH, int TL, int DHS>
-static void launch_cls(const LaAttnArgs& a, int grid, hipStream_t st) {
-  constexpr int ROWB = AttnT<T, DH>::ROWB;
-  constexpr int NBLK = 2 * CH * ROWB / 1024, NW = TL * DHS;
-  constexpr int DEPTH = ring_depth(CH * ROWB, TL, ROWB, NBLK >= NW ? NBLK / NW : 1);
-  constexpr size_t lds = (size_t)DEPTH * 2 * CH * ROWB + (size_t)TL * 16 * ROWB + (size_t)TL * 256;
-  static_assert(lds <= LDS_BYTES, "LDS");
-  static const bool attr = hipFuncSetAttribute((const void*)&la_attn_kernel<T, DH, TL, DHS>,
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) == hipSuccess;
+// dynamic LDS of the kernel: the fixed part, then the largest of the ring,
+// the tail rows of TL tiles (trows each, K and V) and the fold states
+template <typename T, int DH, int TL>
+static size_t attn_lds(int trows) {
+  constexpr int ROWB = AttnT<T, DH>::ROWB, NDT = AttnT<T, DH>::NDT;
+  const size_t fix = ((size_t)TL * (16 * ROWB + 256 + 16 * 64 * 4) + 1023) & ~(size_t)1023;
+  const size_t ring = (size_t)2 * NCLS * 2 * CH * ROWB;
+  const size_t tail = (size_t)TL * 2 * trows * ROWB;
+  const size_t fold = (size_t)TL * (NCLS - 1) * 64 * (4 * NDT + 2) * 4;
+  return fix + std::max(ring, std::max(tail, fold));
+}
+
+template <typename T, int DH, int TL>
+static void launch_tl(const LaAttnArgs& a, int grid, size_t lds, hipStream_t st) {
+  static const bool attr = hipFuncSetAttribute((const void*)&la_attn_kernel<T, DH, TL>,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES) == hipSuccess;
   (void)attr;
-  hipLaunchKernelGGL((la_attn_kernel<T, DH, TL, DHS>), dim3(grid), dim3(64 * TL * DHS), lds, st, a);
+  hipLaunchKernelGGL((la_attn_kernel<T, DH, TL>), dim3(grid), dim3(256 * TL), lds, st, a);
 }
 
 template <typename T, int DH>
-static void launch_dh(LaAttnArgs a, hipStream_t st) {
-  constexpr int NDT = AttnT<T, DH>::NDT;
+static int launch_dh(LaAttnArgs a, hipStream_t st) {
   const int group = a.H / a.Hkv;
   const int tiles = group * ((a.Q + 15) / 16);
-  // tiles per class workgroup: at most 8, fewer while that keeps the grid under
-  // 256 workgroups; with 4 tiles or fewer each tile gets two waves (two halves
-  // of the head dimensions) so that every SIMD has two waves to interleave
-  int tl = 8;
-  while (tl > 1 && (tl / 2 >= tiles || a.Hkv * NCLS * ((tiles + tl - 1) / tl) < 256)) tl /= 2;
+  // staged tail rows per tile (K and V): what the LDS left after the fixed
+  // part holds, at least the committed rows of a tail chunk (< 32) and the
+  // EP positions of one branch; at most those of 16 branches
+  constexpr int ROWB = AttnT<T, DH>::ROWB, RPB = 1024 / ROWB;
+  const int EP = a.n_tail > 0 ? a.max_pos - a.shared_end + 1 : 0;
+  auto rows_for = [&](int tl) {
+    const size_t fix = (((size_t)tl * (16 * ROWB + 256 + 16 * 64 * 4)) + 1023) & ~(size_t)1023;
+    const int fit = (int)((LDS_BYTES - fix) / ((size_t)tl * 2 * ROWB)) / RPB * RPB;
+    const int want = ((CH - 1 + 16 * EP) + RPB - 1) / RPB * RPB;
+    return std::min(fit, want);
+  };
+  const int need_rows = ((CH - 1 + EP) + RPB - 1) / RPB * RPB;
+  int tl = tiles >= 4 ? 2 : 1;
+  if (a.n_tail > 0 && rows_for(tl) < need_rows) tl = 1;
+  if (a.n_tail > 0 && rows_for(tl) < need_rows) return -2;
+  a.trows = a.n_tail > 0 ? rows_for(tl) : 0;
+  const size_t l2 = attn_lds<T, DH, 2>(a.trows), l1 = attn_lds<T, DH, 1>(a.trows);
+  if ((tl == 1 ? l1 : l2) > LDS_BYTES) return -2;
   a.rgroups = (tiles + tl - 1) / tl;
-  if (a.class_last >= 0) {
-    const int hpx = (a.Hkv + 7) / 8;
-    const int grid = 8 * hpx * NCLS * a.rgroups;
-    if constexpr (NDT % 2 == 0) {
-      switch (tl) {
-        case 8: launch_cls<T, DH, 8, 1>(a, grid, st); break;
-        case 4: launch_cls<T, DH, 4, 2>(a, grid, st); break;
-        case 2: launch_cls<T, DH, 2, 2>(a, grid, st); break;
-        default: launch_cls<T, DH, 1, 2>(a, grid, st); break;
-      }
-    } else {
-      switch (tl) {
-        case 8: launch_cls<T, DH, 8, 1>(a, grid, st); break;
-        case 4: launch_cls<T, DH, 4, 1>(a, grid, st); break;
-        case 2: launch_cls<T, DH, 2, 1>(a, grid, st); break;
-        default: launch_cls<T, DH, 1, 1>(a, grid, st); break;
-      }
-    }
-  }
-  constexpr size_t tlds = (size_t)2 * TAIL_ROWS * AttnT<T, DH>::ROWB;
-  static const bool tattr = hipFuncSetAttribute((const void*)&la_attn_tail_merge_kernel<T, DH>,
-                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)tlds) == hipSuccess;
-  (void)tattr;
-  hipLaunchKernelGGL((la_attn_tail_merge_kernel<T, DH>), dim3(a.Hkv * tiles), dim3(64), a.n_tail > 0 ? tlds : 0, st,
-                     a);
+  const int grid = 8 * ((a.Hkv + 7) / 8) * a.rgroups;
+  if (tl == 2) launch_tl<T, DH, 2>(a, grid, l2, st);
+  else launch_tl<T, DH, 1>(a, grid, l1, st);
+  return 0;
 }
 
 int la_attention_launch(int dtype, const LaAttnArgs& a0, hipStream_t st) {
@@ -717,17 +701,19 @@ int la_attention_launch(int dtype, const LaAttnArgs& a0, hipStream_t st) {
   a.class_last = tail ? se / CH - 1 : a.max_pos / CH;
   a.tail0 = se / CH;
   a.n_tail = tail ? a.max_pos / CH - se / CH + 1 : 0;
-  // tail positions are read through a 64-entry path table per branch
+  // at most one tail chunk per class; tail positions come from a 64-entry path table per branch
   if (a.n_tail > NTAIL || (tail && a.max_pos - se >= 64)) return -2;
   a.scale_log2 = a.scale * 1.4426950408889634f;
+  int rc;
   if (dtype == LA_DT_BF16) {
-    if (a.dh == 128) launch_dh<bf16_t, 128>(a, st);
-    else if (a.dh == 64) launch_dh<bf16_t, 64>(a, st);
+    if (a.dh == 128) rc = launch_dh<bf16_t, 128>(a, st);
+    else if (a.dh == 64) rc = launch_dh<bf16_t, 64>(a, st);
     else return -2;
   } else {
-    if (a.dh == 16) launch_dh<float, 16>(a, st);
-    else if (a.dh == 64) launch_dh<float, 64>(a, st);
+    if (a.dh == 16) rc = launch_dh<float, 16>(a, st);
+    else if (a.dh == 64) rc = launch_dh<float, 64>(a, st);
     else return -2;
   }
+  if (rc) return rc;
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

@@ -79,6 +79,7 @@ struct LaAttnArgs {
   int class_last;       // last chunk taken by the class workgroups (-1: none)
   int tail0, n_tail;    // first chunk and number of chunks reaching past shared_end
   int rgroups;          // row groups per KV head
+  int trows;            // staged tail rows per tile
   float scale_log2;     // scale * log2(e)
 };
 int la_attention_launch(int dtype, const LaAttnArgs& a, hipStream_t st);
