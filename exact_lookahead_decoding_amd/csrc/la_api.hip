@@ -201,7 +201,7 @@ static void setup_dims(la_ctx* c) {
   c->m_max = std::max(c->q_max, PREFILL_CHUNK);
   c->ws_cap = c->q_max;
   c->t_cap = g.max_prompt + g.max_new + 16;
-  c->parts = la_attention_parts();
+  c->parts = la_attention_parts(c->t_cap + c->maxp_max);   // positions stay below t_cap + maxp
   c->rope_rows = c->t_cap + c->q_max + 1;
   c->wstride = g.W + g.N;
   c->rows_words = 8 * c->q_max + c->nb_max * c->maxp_max + c->nb_max + c->n_logit_max + c->q_max * c->words_max;
@@ -325,7 +325,7 @@ static int forward(la_ctx* c, int M, const int32_t* tok, const int32_t* pos, con
   const size_t wsl = (size_t)c->Hkv * c->ws_cap * c->dh;
   la_embed_launch(c->dtype, c->w.embed, tok, c->x, M, c->d, c->st);
   LaAttnArgs at{};
-  at.q = c->q; at.o = c->o; at.part_o = c->attn_po; at.part_ml = c->attn_pml;
+  at.q = c->q; at.o = c->o; at.part_o = c->attn_po; at.part_ml = c->attn_pml; at.max_splits = c->parts;
   at.pos = pos; at.branch = branch; at.path = path; at.path_len = path_len;
   at.Q = M; at.H = c->H; at.Hkv = c->Hkv; at.dh = c->dh; at.T_cap = c->t_cap; at.ws_cap = c->ws_cap; at.maxp = maxp;
   at.shared_end = shared_end;
@@ -813,8 +813,7 @@ extern "C" int la_build_rows(const la_rows_desc* desc, const int32_t* window, co
 }
 
 extern "C" size_t la_attention_workspace(int32_t Q, int32_t H, int32_t dh, int32_t max_pos) {
-  (void)max_pos;
-  const size_t parts = (size_t)la_attention_parts();
+  const size_t parts = (size_t)la_attention_parts(max_pos);
   return parts * H * Q * ((size_t)dh + 2) * 4 + 512;
 }
 
@@ -832,7 +831,8 @@ extern "C" int la_attention(int32_t dtype, const void* q, const void* k_cache, c
   if (workspace_bytes < need) return fail(nullptr, LA_EOVERFLOW, "workspace %zu < %zu bytes", workspace_bytes, need);
   LaAttnArgs a{};
   a.q = q; a.kc = k_cache; a.vc = v_cache; a.kw = k_ws ? k_ws : k_cache; a.vw = v_ws ? v_ws : v_cache; a.o = out;
-  const size_t parts = (size_t)la_attention_parts();
+  const size_t parts = (size_t)la_attention_parts(max_pos);
+  a.max_splits = (int)parts;
   a.part_o = (float*)workspace;
   a.part_ml = (float*)((char*)workspace + parts * H * info->Q * (size_t)dh * 4);
   a.pos = rows + info->off_pos; a.branch = rows + info->off_branch; a.path = rows + info->off_path;

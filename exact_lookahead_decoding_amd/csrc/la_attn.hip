@@ -52,7 +52,7 @@
 #define CH 32         // keys per chunk
 #define NCLS 4        // chunk classes
 #define NTAIL 4       // most chunks per call that reach past shared_end
-#define TAIL_ROWS 128 // key rows the tail + merge kernel stages in LDS at once
+#define SPB 8         // ring stages (128 keys each) per key split: a split is 1024 positions
 #define NEG_INF (-__builtin_inff())
 
 
@@ -241,8 +241,12 @@ __device__ __forceinline__ void fold_state(float& ma, float& la, f32x4* oa, floa
 }
 
 
-// One workgroup per (KV head, row group of TL tiles of 16 query rows);
-// wave w is class c = w / TL of tile slot w % TL.  Three phases:
+// One workgroup per (KV head, row group of TL tiles of 16 query rows, key
+// split of 1024 positions); wave w is class c = w / TL of tile slot w % TL.
+// Several splits leave one folded state per row each, and a merge kernel
+// folds them in split order (a split's chunks, tail chunks included, are
+// fixed by position, so the tree still depends on positions only).
+// Three phases per workgroup:
 //   1. prefix: ring stage s holds keys [128 s, 128 s + 128) of the head (the
 //      class-c chunk 4 s + c, K and V, 16-byte pieces XOR-swizzled by row) for
 //      every chunk below shared_end (or up to the largest row position when
@@ -278,10 +282,12 @@ __global__ void __launch_bounds__(256 * TL) __attribute__((amdgpu_waves_per_eu(1
   extern __shared__ __attribute__((aligned(1024))) char lds[];
   char* const ring = lds + FIX;                 // ring stages, later the tail rows, then the fold states
 
-  // block -> (XCD, KV head, row group): the row groups of one head share an XCD (and its L2)
+  // block -> (XCD, KV head, row group, key split): the workgroups of one
+  // head share an XCD (and its L2)
   const int xcd = blockIdx.x & 7, bi = blockIdx.x >> 3;
-  const int rg = bi % a.rgroups;
-  const int g_kv = xcd + 8 * (bi / a.rgroups);
+  const int sp = bi % a.nsplit;
+  const int rg = (bi / a.nsplit) % a.rgroups;
+  const int g_kv = xcd + 8 * (bi / (a.nsplit * a.rgroups));
   if (g_kv >= a.Hkv) return;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -318,7 +324,9 @@ __global__ void __launch_bounds__(256 * TL) __attribute__((amdgpu_waves_per_eu(1
   // ring stage s: chunks 4 s .. 4 s + 3; past the last stage every lane loads
   // one 16-byte piece (a dummy that nobody reads), so every wave issues CW
   // DMA instructions per stage on every path
-  const int nblk = (a.class_last + NCLS) / NCLS;   // stages (class_last = -1: none)
+  const int nblk = (a.class_last + NCLS) / NCLS;   // stages of the whole prefix (class_last = -1: none)
+  const int s_begin = sp * SPB;                       // this split's stages
+  const int s_end = min(s_begin + SPB, nblk);
   // wave w brings the DMA blocks w*CW .. w*CW + CW - 1 of a stage (a
   // contiguous run inside its chunk cw of the stage: CW divides the 1 KB
   // blocks of a chunk half or is a multiple of them).  The lane's source
@@ -341,14 +349,14 @@ __global__ void __launch_bounds__(256 * TL) __attribute__((amdgpu_waves_per_eu(1
   }
   auto issue = [&](char* stage, int s) __attribute__((always_inline)) {
     const int x0 = CH * (NCLS * s + cw);
-    if (s < nblk && x0 + CH <= se) {            // the whole chunk lies below shared_end
+    if (s < s_end && x0 + CH <= se) {           // the whole chunk lies below shared_end
 #pragma unroll
       for (int j = 0; j < CW; ++j) {
         const char* base = kv_of(j);
         __builtin_amdgcn_global_load_lds((const void*)(base + (size_t)x0 * ROWB + oj[j]),
                                          (lds_void_t*)(stage + (b0 + j) * 1024), 16, 0, 0);
       }
-    } else if (s < nblk) {                      // rows past shared_end - 1 repeat it (never visible)
+    } else if (s < s_end) {                     // rows past shared_end - 1 repeat it (never visible)
 #pragma unroll
       for (int j = 0; j < CW; ++j) {
         const char* base = kv_of(j);
@@ -367,7 +375,7 @@ __global__ void __launch_bounds__(256 * TL) __attribute__((amdgpu_waves_per_eu(1
   // the row's branch (read now, used by the tail phase after the ring)
   const int br = (a.n_tail > 0 && rvalid) ? a.branch[row] : -1;
 #pragma unroll
-  for (int k = 0; k < DEPTH; ++k) issue(ring + k * BLKB, k);
+  for (int k = 0; k < DEPTH; ++k) issue(ring + k * BLKB, s_begin + k);
   wait_vm<(CW * DEPTH < 63 ? CW * DEPTH : 63)>();   // this wave's Q and positions (issued first) have landed
   ring_barrier();                                    // ... and those of the other waves
   QF qf;
@@ -416,7 +424,7 @@ __global__ void __launch_bounds__(256 * TL) __attribute__((amdgpu_waves_per_eu(1
     wait_vm<CW * (DEPTH - 1)>();                // stage s landed (the next one may be in flight)
     ring_barrier();
     const int k = NCLS * s + cls;               // the class's chunk
-    const bool live = k <= a.class_last;
+    const bool live = s < s_end && k <= a.class_last;
     // the chunk's K and V go to registers first, so the stage is released
     // (and the stage two steps ahead issued) before any arithmetic
     typename LdsT<16>::T kraw[2 * LP];
@@ -463,12 +471,15 @@ __global__ void __launch_bounds__(256 * TL) __attribute__((amdgpu_waves_per_eu(1
       for (int dt = 0; dt < NDT; ++dt) O[dt] = AT::pv(dt, vv, pp, O[dt]);
     }
   };
-  for (int s0 = 0; s0 < nblk; s0 += DEPTH)
+  for (int s0 = s_begin; s0 < s_end; s0 += DEPTH)
     static_for<0, DEPTH>([&](auto SI) { step(SI, s0 + decltype(SI)::value); });
+
   wait_vm<0>();                                   // the dummy stages have landed: the ring is free
   ring_barrier();
 
-  if (a.n_tail > 0) {
+  // tail chunks of this split (a chunk belongs to the split of its position)
+  const int t_lo = max(a.tail0, sp * SPB * NCLS), t_hi = min(a.tail0 + a.n_tail, (sp + 1) * SPB * NCLS);
+  if (t_lo < t_hi) {
     // the tile's branches that reach a tail chunk (at most 16); every class
     // wave of the tile finds the same list
     const bool need0 = rvalid && pos >= CH * a.tail0;
@@ -514,7 +525,8 @@ __global__ void __launch_bounds__(256 * TL) __attribute__((amdgpu_waves_per_eu(1
     const char* vw = (const char*)a.vw + (size_t)g_kv * a.ws_cap * ROWB;
     const int tau = (cls - a.tail0 % NCLS + NCLS) % NCLS;   // the class's tail chunk (at most one)
     const int x0 = CH * (a.tail0 + tau);
-    const bool need = tau < a.n_tail && rvalid && pos >= x0;
+    const bool mine_chunk = tau < a.n_tail && a.tail0 + tau >= t_lo && a.tail0 + tau < t_hi;
+    const bool need = mine_chunk && rvalid && pos >= x0;
     for (int bt = 0; bt < nbatch; ++bt) {
       const int i0 = bt * bb;
       const int nb = max(0, min(bb, nbr - i0));
@@ -619,6 +631,19 @@ __global__ void __launch_bounds__(256 * TL) __attribute__((amdgpu_waves_per_eu(1
         for (int r = 0; r < 4; ++r) Oc[dt][r] = d[2 + 4 * dt + r];
       fold_state<NDT>(Mf, Lf, Of, d[0], d[1], Oc);
     }
+    if (a.nsplit > 1) {
+      // the split's state: (m, l) and O, lane dims NDT*(4g + r) + dt (4*NDT contiguous floats)
+      const size_t base = ((size_t)sp * a.H + hh) * a.Q + row;
+      if (g == 0) *(float2*)(a.part_ml + base * 2) = make_float2(Mf, Lf);
+      float4* po = (float4*)(a.part_o + base * DH + 4 * NDT * g);
+#pragma unroll
+      for (int q = 0; q < NDT; ++q) {
+        const int i0 = 4 * q;
+        po[q] = make_float4(Of[(i0 + 0) % NDT][(i0 + 0) / NDT], Of[(i0 + 1) % NDT][(i0 + 1) / NDT],
+                            Of[(i0 + 2) % NDT][(i0 + 2) / NDT], Of[(i0 + 3) % NDT][(i0 + 3) / NDT]);
+      }
+      return;
+    }
     // lane holds head dimensions NDT*(4g + r) + dt: 4*NDT contiguous values,
     // stored as 16-byte pieces
     constexpr int EPW = 4 / sizeof(T);            // elements per 32-bit word
@@ -640,7 +665,29 @@ __global__ void __launch_bounds__(256 * TL) __attribute__((amdgpu_waves_per_eu(1
   }
 }
 
-int la_attention_parts() { return NCLS; }
+// Fold of the key splits' states in split order (the same sequence of
+// roundings as fold_state), then O / l.  One thread per head dimension.
+template <typename T, int DH>
+__global__ void __launch_bounds__(DH) la_attn_merge_kernel(LaAttnArgs a) {
+  const int idx = blockIdx.x;                   // row * H + head
+  const int row = idx / a.H, hh = idx % a.H;
+  const int d = threadIdx.x;
+  float ma = NEG_INF, la = 0.f, oa = 0.f;
+  for (int s = 0; s < a.nsplit; ++s) {
+    const size_t base = ((size_t)s * a.H + hh) * a.Q + row;
+    const float2 ml = *(const float2*)(a.part_ml + base * 2);
+    if (ml.x == NEG_INF) continue;
+    const float ob = a.part_o[base * DH + d];
+    const float mn = fmaxf(ma, ml.x);
+    const float wa = ex2(ma - mn), wb = ex2(ml.x - mn);
+    la = lin2(la, wa, ml.y, wb);
+    oa = lin2(oa, wa, ob, wb);
+    ma = mn;
+  }
+  st<T>((T*)a.o + ((size_t)row * a.H + hh) * DH + d, oa / la);
+}
+
+int la_attention_parts(int max_pos) { return max_pos < 0 ? 1 : max_pos / (CH * NCLS * SPB) + 1; }
 
 // dynamic LDS of the kernel: the fixed part, then the largest of the ring,
 // the tail rows of TL tiles (trows each, K and V) and the fold states
@@ -685,9 +732,10 @@ static int launch_dh(LaAttnArgs a, hipStream_t st) {
   const size_t l2 = attn_lds<T, DH, 2>(a.trows), l1 = attn_lds<T, DH, 1>(a.trows);
   if ((tl == 1 ? l1 : l2) > LDS_BYTES) return -2;
   a.rgroups = (tiles + tl - 1) / tl;
-  const int grid = 8 * ((a.Hkv + 7) / 8) * a.rgroups;
+  const int grid = 8 * ((a.Hkv + 7) / 8) * a.rgroups * a.nsplit;
   if (tl == 2) launch_tl<T, DH, 2>(a, grid, l2, st);
   else launch_tl<T, DH, 1>(a, grid, l1, st);
+  if (a.nsplit > 1) hipLaunchKernelGGL((la_attn_merge_kernel<T, DH>), dim3(a.Q * a.H), dim3(DH), 0, st, a);
   return 0;
 }
 
@@ -704,6 +752,10 @@ int la_attention_launch(int dtype, const LaAttnArgs& a0, hipStream_t st) {
   // at most one tail chunk per class; tail positions come from a 64-entry path table per branch
   if (a.n_tail > NTAIL || (tail && a.max_pos - se >= 64)) return -2;
   a.scale_log2 = a.scale * 1.4426950408889634f;
+  // key splits: the split of the last chunk any row reaches, plus one
+  const int last_chunk = tail ? a.tail0 + a.n_tail - 1 : a.class_last;
+  a.nsplit = last_chunk / (NCLS * SPB) + 1;
+  if (a.nsplit > 1 && (a.part_o == nullptr || a.part_ml == nullptr || a.nsplit > a.max_splits)) return -2;
   int rc;
   if (dtype == LA_DT_BF16) {
     if (a.dh == 128) rc = launch_dh<bf16_t, 128>(a, st);

@@ -63,8 +63,9 @@ struct LaAttnArgs {
   const void* kw;       // workspace K [Hkv][ws_cap][dh] (one layer), packed row k -> ws row k-1
   const void* vw;
   void* o;              // [Q][H][dh]
-  float* part_o;        // [la_attention_parts()][H][Q][dh] softmax states (class chunks, then tail chunks)
-  float* part_ml;       // [la_attention_parts()][H][Q][2]  (m, l) of those states
+  float* part_o;        // [splits][H][Q][dh] softmax states of the key splits (several splits only)
+  float* part_ml;       // [splits][H][Q][2]  (m, l) of those states
+  int max_splits;       // splits part_o / part_ml hold (la_attention_parts(max_pos))
   const int32_t* pos;
   const int32_t* branch;
   const int32_t* path;
@@ -80,10 +81,11 @@ struct LaAttnArgs {
   int tail0, n_tail;    // first chunk and number of chunks reaching past shared_end
   int rgroups;          // row groups per KV head
   int trows;            // staged tail rows per tile
+  int nsplit;           // key splits (512 positions each)
   float scale_log2;     // scale * log2(e)
 };
 int la_attention_launch(int dtype, const LaAttnArgs& a, hipStream_t st);
-int la_attention_parts();   // softmax-state slots per (head, row) in part_o / part_ml
+int la_attention_parts(int max_pos);   // key splits of a call whose rows reach max_pos
 
 // model pieces
 void la_embed_launch(int dtype, const void* E, const int32_t* tok, void* x, int M, int d, hipStream_t st);

@@ -158,6 +158,13 @@ ATTN = [
      2e-2),
     ([3, 0], [1, 0], [], 2, 0, 4, 4, 16, "f32", 1e-5),                 # empty prefix
     ([0, 0], [1, 0], [], 2, 255, 4, 2, 64, "bf16", 2e-2),               # one ordinary row
+    # key splits (1024 positions each): a 3000-key GQA prefix (3 splits), the
+    # 8192-key long-prefix round (9 splits) and the 34B-shaped GQA round
+    ([6, 7, 7, 7], [1, 0, 0, 0], [tuple(range(i, i + 4)) for i in range(7)], 4, 3000, 16, 4, 128, "bf16", 2e-2),
+    ([15, 15, 15, 15], [1, 1, 1, 1], [tuple(range(i, i + 4)) for i in range(15)], 4, 8192, 32, 32, 128, "bf16",
+     2e-2),
+    ([14] + [15] * 5, [1, 0, 0, 0, 0, 0], [tuple(range(i, i + 6)) for i in range(15)], 6, 2048, 64, 8, 128, "bf16",
+     2e-2),
 ]
 
 
@@ -171,12 +178,14 @@ def test_attention_matches_oracle(case):
     assert err <= tol
 
 
-def test_attention_batch_invariance():
+@pytest.mark.parametrize("p", [1000, 2040])
+def test_attention_batch_invariance(p):
     """A packed row's output equals, bit for bit, the same row computed alone
-    with its branch ancestors committed to the cache (an autoregressive call)."""
+    with its branch ancestors committed to the cache (an autoregressive call).
+    Both prefixes put the round's rows across a 1024-position key split."""
     sizes, starts = [6, 7, 7, 7], [1, 0, 0, 0]
     cands = [tuple(range(i, i + 4)) for i in range(7)]
-    p, H, Hkv, dh = 1000, 8, 2, 128
+    H, Hkv, dh = 8, 2, 128
     got, want, ctx = _attn_case(sizes, starts, cands, 4, p, H, Hkv, dh, "bf16", seed=3)
     comp, b, info, perm, dev, q, kc, vc, kw, vw, out = ctx
     out_np = out.view(torch.int16).cpu().numpy()
