@@ -135,6 +135,128 @@ def attention_op(reps=200, sets=16):
             "peak_GBps": HBM_PEAK_GBS, "frac": gbs / HBM_PEAK_GBS, "reps": reps, "input_sets": sets}
 
 
+TRAFFIC_MD = os.path.join(ROOT, "profiles", "la_gemm_kernel_llama7b_w7n5g7_hbm_traffic.md")
+GEMM_SRC = os.path.join(ROOT, "exact_lookahead_decoding_amd", "csrc", "la_gemm.hip")
+COPY_BYTES = 1 << 30
+
+
+def _sha256(path):
+    import hashlib
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+
+
+def gemm_traffic():
+    """HBM bytes per round GEMM launch from the committed counter summary, or
+    None when the GEMM source changed since the counters were taken."""
+    try:
+        txt = open(TRAFFIC_MD).read()
+    except OSError:
+        return None
+    vals = dict(l.split(":", 1) for l in txt.splitlines() if l.startswith(("traffic_bytes_per_launch:",
+                                                                               "la_gemm.hip sha256:")))
+    if vals.get("la_gemm.hip sha256", "").strip() != _sha256(GEMM_SRC):
+        return None
+    return float(vals["traffic_bytes_per_launch"])
+
+
+def pmc_sample(rounds=16):
+    """The workload rounds whose GEMM dispatches the counter runs read, then a
+    plain copy of COPY_BYTES that calibrates FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    import synthetic
+    import exact_lookahead_decoding_amd.la as la
+    la.load()
+    torch.cuda.set_device(0)
+    wl = WORKLOADS["llama7b_w7n5g7"]
+    dims = synthetic.PRESETS[wl["model"]]
+    model = la.DeviceModel(dims, seed=0)
+    prompt = synthetic.markov_prompt(dims.vocab, wl["prompt"], 0)
+    sess = la.Session(model, prompt, W=wl["W"], N=wl["N"], G=wl["G"], max_new=wl["max_new"])
+    sess.la_profile(True)
+    for _ in range(rounds):
+        sess.la_step()
+    torch.cuda.synchronize()
+    pr = sess.la_profile_read()
+    src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"rounds": rounds, "gemm_launches": pr["gemm_launches"],
+                      "gemm_alg_bytes_per_launch": pr["gemm_bytes"] / max(1, pr["gemm_launches"]),
+                      "copy_bytes": COPY_BYTES}), flush=True)
+
+
+def pmc_summary(fetch_db, write_db, sample_json):
+    """Per-launch HBM traffic of the round GEMMs (la_gemm_kernel with at most 4
+    row tiles: the prefill chunks use 8) from a FETCH_SIZE and a WRITE_SIZE
+    run of --pmc-sample, each scaled by what the counter reads for the copy."""
+    import collections
+    import re
+    import sqlite3
+
+    def per_dispatch(db, counter):
+        con = sqlite3.connect(db)
+        rows = con.execute("select dispatch_id, kernel_name, value from counters_collection where counter_name = ?",
+                           (counter,)).fetchall()
+        agg = collections.defaultdict(float)
+        names = {}
+        for d, k, v in rows:
+            agg[d] += v
+            names[d] = k
+        return agg, names
+
+    out = {}
+    for counter, db in (("FETCH_SIZE", fetch_db), ("WRITE_SIZE", write_db)):
+        agg, names = per_dispatch(db, counter)
+        gemm = [agg[d] for d, k in names.items()
+                if (m := re.search(r"la_gemm_kernel<[^,]+, (\d+),", k)) and int(m.group(1)) <= 4]
+        copy = [agg[d] for d, k in names.items() if "copy" in k.lower()]
+        out[counter] = (gemm, max(copy) if copy else 0.0)
+    sample = json.loads(open(sample_json).read().strip().splitlines()[-1])
+    f_gemm, f_copy = out["FETCH_SIZE"]
+    w_gemm, w_copy = out["WRITE_SIZE"]
+    ff = sample["copy_bytes"] / (f_copy * 1024.0)
+    fw = sample["copy_bytes"] / (w_copy * 1024.0)
+    fetch = sum(f_gemm) / len(f_gemm) * 1024.0 * ff
+    write = sum(w_gemm) / len(w_gemm) * 1024.0 * fw
+    alg = sample["gemm_alg_bytes_per_launch"]
+    return "\n".join([
+        "# HBM traffic of the round GEMM: 7B-shaped lookahead rounds (W=7, N=5, G=7, 512-token prompt)",
+        "",
+        "Commands (run from /tmp with TMPDIR=/tmp on one MI355X; each counter in a run of its own):",
+        "",
+        "```",
+        "python3 bench.py --pmc-sample > gpurun_out/pmc_sample.json",
+        "rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_fetch -o f -- python3 bench.py --pmc-sample",
+        "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_write -o w -- python3 bench.py --pmc-sample",
+        "python3 bench.py --pmc-summary gpurun_out/pmc_fetch/f_results.db gpurun_out/pmc_write/w_results.db "
+        "gpurun_out/pmc_sample.json",
+        "```",
+        "",
+        f"The sample runs {sample['rounds']} lookahead rounds after prefill, then copies a "
+        f"{sample['copy_bytes'] >> 20} MiB buffer three times.  Round GEMM dispatches: la_gemm_kernel with at "
+        f"most 4 row tiles ({len(f_gemm)} dispatches; prefill chunks use 8).",
+        "",
+        "| quantity | value |",
+        "|---|---:|",
+        f"| copy: FETCH_SIZE (KiB) | {f_copy:.0f} |",
+        f"| copy: WRITE_SIZE (KiB) | {w_copy:.0f} |",
+        f"| FETCH_SIZE scale (copy bytes / counter bytes) | {ff:.3f} |",
+        f"| WRITE_SIZE scale | {fw:.3f} |",
+        f"| round GEMM: mean FETCH_SIZE per dispatch (KiB) | {sum(f_gemm) / len(f_gemm):.0f} |",
+        f"| round GEMM: mean WRITE_SIZE per dispatch (KiB) | {sum(w_gemm) / len(w_gemm):.0f} |",
+        f"| HBM read per launch, scaled (MB) | {fetch / 1e6:.2f} |",
+        f"| HBM write per launch, scaled (MB) | {write / 1e6:.2f} |",
+        f"| algorithmic bytes per launch (MB) | {alg / 1e6:.2f} |",
+        f"| traffic / algorithmic | {(fetch + write) / alg:.3f} |",
+        "",
+        f"traffic_bytes_per_launch: {fetch + write:.0f}",
+        f"la_gemm.hip sha256: {_sha256(GEMM_SRC)}",
+        "",
+    ])
+
+
 def cpu_baseline(wl, budget_rounds=2, prefix=32):
     """The oracle as it stands, on host cores: a 64-token prefix, then `budget_rounds` rounds."""
     import synthetic
@@ -167,7 +289,24 @@ def main():
     ap.add_argument("--workload", default="llama7b_w7n5g7", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-attn", action="store_true")
+    ap.add_argument("--pmc-sample", action="store_true", help="run the GEMM counter sample (see profiles/)")
+    ap.add_argument("--attention-op-only", action="store_true", help="time only the isolated attention op")
+    ap.add_argument("--pmc-summary", nargs=3, metavar=("FETCH_DB", "WRITE_DB", "SAMPLE_JSON"),
+                    help="write the GEMM traffic summary under profiles/ from two counter runs")
     args = ap.parse_args()
+    if args.pmc_summary:
+        md = pmc_summary(*args.pmc_summary)
+        open(TRAFFIC_MD, "w").write(md)
+        print(md)
+        return
+    if args.pmc_sample:
+        pmc_sample()
+        return
+    if args.attention_op_only:
+        import torch
+        torch.cuda.set_device(0)
+        print(json.dumps(attention_op()), flush=True)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the lookahead round runs on a single MI355X (got --gpus {args.gpus}); "
               f"lookahead parallelism across GPUs is not part of this build", file=sys.stderr)
@@ -229,7 +368,7 @@ def main():
         "ar_tokens_per_s": ar_tps,
         "speedup_vs_ar": value / ar_tps,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": gemm_traffic(),
                      "kernel": "la_gemm_kernel (+ split reduction), all projections, MLP and LM head of a round",
                      "avg_launch_us": gemm_avg_ms * 1e3, "algorithmic_bytes_per_launch": gemm_bytes,
                      "launches": pr["gemm_launches"]},
