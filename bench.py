@@ -258,7 +258,7 @@ def pmc_summary(fetch_db, write_db, sample_json):
 
 
 def cpu_baseline(wl, budget_rounds=2, prefix=32):
-    """The oracle as it stands, on host cores: a 64-token prefix, then `budget_rounds` rounds."""
+    """The oracle as it stands, on host cores: a `prefix`-token prompt, then `budget_rounds` rounds."""
     import synthetic
     from oracle.decode import lookahead_generate
     from oracle.model import OracleModel

@@ -19,28 +19,29 @@
 //     + V^T P^T accumulated by MFMA over a fixed key -> slot assignment;
 //   * the 4 class states are folded in class order (fold_state), then O / l.
 //
-// Work decomposition (gfx950, wave64; a wave owns one tile of 16 query rows
-// of one q-head):
-//   * class kernel: a workgroup (KV head, class, row group) of up to 8 tiles
-//     streams its class's committed chunks once from HBM: K and V of a chunk
-//     land in LDS through global_load_lds_dwordx4 (16-byte pieces XOR-swizzled
-//     by row, so the QK and the PV fragment reads are bank-conflict free) in a
-//     4-stage ring shared by all tiles of the workgroup; the row positions and
-//     the tile's Q come in the same way, so the only waits are the ring's own;
-//     each row's class state goes to the workspace;
+// Work decomposition (gfx950, wave64; a wave owns one class of one tile of
+// 16 query rows of one q-head):
+//   * one workgroup per (KV head, row group of TL tiles, key split of 1024
+//     positions), 4 class waves per tile; K and V of every committed chunk
+//     land in LDS through global_load_lds_dwordx4 (16-byte pieces
+//     XOR-swizzled by row, so the QK and the PV fragment reads are
+//     bank-conflict free) in a ring of 128-key stages shared by all tiles and
+//     classes of the workgroup; the row positions and the tiles' Q come in
+//     the same way, so the only waits are the ring's own;
 //   * QK: S^T = K Q^T, 16x16x32 bf16 MFMA (16x16x4 fp32): one query row per
 //     lane column, so the softmax statistics stay in-lane;
 //   * PV: O^T += V^T P^T; output tile dt holds head dimensions NDT*m + dt, so
 //     a lane reads NDT contiguous elements of each key row and transposes
 //     them in registers; bf16 P enters as a hi + lo pair (fp32-level P);
-//   * tail + merge kernel: one wave per tile folds the class states in order;
-//     the class owning a chunk that reaches past shared_end (at most a few per
-//     call) gets that chunk applied first, computed right there by gathering
-//     each key's K/V row from the cache or, through the branch path, from the
-//     packed rows' workspace, once per branch in the tile (rows of other
-//     branches get p = 0 in that pass, which leaves their sums unchanged).
-// The block -> work mapping keeps every class workgroup of one KV head on one
-// XCD (blockIdx % 8), so the head's Q and the row groups' shared K/V chunks
+//   * the chunks that reach past shared_end (at most one per class) are
+//     applied last in their class, from rows gathered out of the cache or,
+//     through each branch's path, out of the packed rows' workspace, once per
+//     branch in the tile (rows of other branches get p = 0 in that pass,
+//     which leaves their sums unchanged);
+//   * the class states are folded in class order inside the workgroup; with
+//     several key splits a small kernel folds the splits' states in order.
+// The block -> work mapping keeps every workgroup of one KV head on one XCD
+// (blockIdx % 8), so the head's Q and the K/V chunks shared by its row groups
 // are fetched from HBM once.
 #include <algorithm>
 #include <type_traits>
@@ -55,17 +56,6 @@
 #define SPB 8         // ring stages (128 keys each) per key split: a split is 1024 positions
 #define NEG_INF (-__builtin_inff())
 
-
-
-// Stages of the class workgroup's LDS ring: as many 2*CHB-byte stages as fit
-// next to the Q tiles (at most 8), and no more than the vmcnt field (63) can
-// wait on (CW DMA instructions per stage and wave).
-constexpr int ring_depth(int chb, int tl, int rowb, int cw) {
-  const int fit = (LDS_BYTES - tl * (16 * rowb + 256)) / (2 * chb);
-  const int cnt = 1 + 63 / cw;
-  const int d = fit < cnt ? fit : cnt;
-  return d < 8 ? d : 8;
-}
 
 
 template <int W> struct alignas(4 * W) Words { uint32_t w[W]; };

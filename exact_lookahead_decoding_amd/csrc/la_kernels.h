@@ -81,7 +81,7 @@ struct LaAttnArgs {
   int tail0, n_tail;    // first chunk and number of chunks reaching past shared_end
   int rgroups;          // row groups per KV head
   int trows;            // staged tail rows per tile
-  int nsplit;           // key splits (512 positions each)
+  int nsplit;           // key splits (1024 positions each)
   float scale_log2;     // scale * log2(e)
 };
 int la_attention_launch(int dtype, const LaAttnArgs& a, hipStream_t st);
