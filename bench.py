@@ -104,7 +104,7 @@ def attention_op(reps=200, sets=16):
     mk = lambda *s: torch.randn(*s, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
     bufs = [(mk(Q, H, dh), mk(Hkv, p + 8, dh), mk(Hkv, p + 8, dh), mk(Hkv, Q, dh), mk(Hkv, Q, dh))
             for _ in range(sets)]
-    ws = torch.empty(la.load().la_attention_workspace(Q, H, dh, p + 1 + info.maxp), dtype=torch.uint8,
+    ws = torch.empty(la.load().la_attention_workspace(Q, H, dh, p + 1 + info.maxp, p + 8), dtype=torch.uint8,
                      device="cuda")
     outs = [torch.empty(Q, H, dh, dtype=torch.bfloat16, device="cuda") for _ in range(sets)]
     for i in range(sets):

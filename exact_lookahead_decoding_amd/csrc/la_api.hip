@@ -201,7 +201,7 @@ static void setup_dims(la_ctx* c) {
   c->m_max = std::max(c->q_max, PREFILL_CHUNK);
   c->ws_cap = c->q_max;
   c->t_cap = g.max_prompt + g.max_new + 16;
-  c->parts = la_attention_parts(c->t_cap + c->maxp_max);   // positions stay below t_cap + maxp
+  c->parts = la_attention_parts(c->t_cap + c->maxp_max, c->t_cap);   // positions stay below t_cap + maxp
   c->rope_rows = c->t_cap + c->q_max + 1;
   c->wstride = g.W + g.N;
   c->rows_words = 8 * c->q_max + c->nb_max * c->maxp_max + c->nb_max + c->n_logit_max + c->q_max * c->words_max;
@@ -812,8 +812,8 @@ extern "C" int la_build_rows(const la_rows_desc* desc, const int32_t* window, co
   return LA_OK;
 }
 
-extern "C" size_t la_attention_workspace(int32_t Q, int32_t H, int32_t dh, int32_t max_pos) {
-  const size_t parts = (size_t)la_attention_parts(max_pos);
+extern "C" size_t la_attention_workspace(int32_t Q, int32_t H, int32_t dh, int32_t max_pos, int32_t t_cap) {
+  const size_t parts = (size_t)la_attention_parts(max_pos, t_cap);
   return parts * H * Q * ((size_t)dh + 2) * 4 + 512;
 }
 
@@ -827,11 +827,11 @@ extern "C" int la_attention(int32_t dtype, const void* q, const void* k_cache, c
   if (info->Q > 1 && (!k_ws || !v_ws || ws_cap < info->Q - 1)) return fail(nullptr, LA_EINVAL, "workspace K/V too small");
   // positions never exceed shared_end + maxp (a row's path covers its own position)
   const int max_pos = shared_end - 1 + info->maxp;
-  const size_t need = la_attention_workspace(info->Q, H, dh, max_pos);
+  const size_t need = la_attention_workspace(info->Q, H, dh, max_pos, t_cap);
   if (workspace_bytes < need) return fail(nullptr, LA_EOVERFLOW, "workspace %zu < %zu bytes", workspace_bytes, need);
   LaAttnArgs a{};
   a.q = q; a.kc = k_cache; a.vc = v_cache; a.kw = k_ws ? k_ws : k_cache; a.vw = v_ws ? v_ws : v_cache; a.o = out;
-  const size_t parts = (size_t)la_attention_parts(max_pos);
+  const size_t parts = (size_t)la_attention_parts(max_pos, t_cap);
   a.max_splits = (int)parts;
   a.part_o = (float*)workspace;
   a.part_ml = (float*)((char*)workspace + parts * H * info->Q * (size_t)dh * 4);

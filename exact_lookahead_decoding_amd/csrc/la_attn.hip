@@ -21,8 +21,10 @@
 //
 // Work decomposition (gfx950, wave64; a wave owns one class of one tile of
 // 16 query rows of one q-head):
-//   * one workgroup per (KV head, row group of TL tiles, key split of 1024
-//     positions), 4 class waves per tile; K and V of every committed chunk
+//   * one workgroup per (KV head, row group of up to 4 tiles, key split of
+//     a fixed number of 128-position stages), 4 class waves per tile pair
+//     (a wave computes two tiles from one read of the chunk's K and V); K
+//     and V of every committed chunk
 //     land in LDS through global_load_lds_dwordx4 (16-byte pieces
 //     XOR-swizzled by row, so the QK and the PV fragment reads are
 //     bank-conflict free) in a ring of 128-key stages shared by all tiles and
@@ -32,7 +34,7 @@
 //     lane column, so the softmax statistics stay in-lane;
 //   * PV: O^T += V^T P^T; output tile dt holds head dimensions NDT*m + dt, so
 //     a lane reads NDT contiguous elements of each key row and transposes
-//     them in registers; bf16 P enters as a hi + lo pair (fp32-level P);
+//     them in registers; P enters rounded to bf16 (fp32 accumulation);
 //   * the chunks that reach past shared_end (at most one per class) are
 //     applied last in their class, from rows gathered out of the cache or,
 //     through each branch's path, out of the packed rows' workspace, once per
@@ -53,7 +55,6 @@
 #define CH 32         // keys per chunk
 #define NCLS 4        // chunk classes
 #define NTAIL 4       // most chunks per call that reach past shared_end
-#define SPB 8         // ring stages (128 keys each) per key split: a split is 1024 positions
 #define NEG_INF (-__builtin_inff())
 
 
@@ -88,25 +89,22 @@ template <int DH> struct AttnT<bf16_t, DH> {
       acc = mfma_bf16_32(__builtin_bit_cast(bf16x8, k.p[s]), __builtin_bit_cast(bf16x8, q.p[s]), acc);
     return acc;
   }
-  // P^T operand of one chunk: p of slot e as a hi + lo bf16 pair
-  struct PP { bf16x8 hi, lo; };
+  // P^T operand of one chunk: p of slot e rounded to bf16 (nearest even)
+  typedef bf16x8 PP;
   static __device__ __forceinline__ PP prep(const float* ps) {
     typedef float f2 __attribute__((ext_vector_type(2)));
     typedef __bf16 b2 __attribute__((ext_vector_type(2)));
-    uint32_t bh[4], bl[4];
+    uint32_t bh[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const f2 v = {ps[2 * j], ps[2 * j + 1]};
-      const uint32_t hw = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, b2));   // nearest even
-      const f2 r = {v[0] - __uint_as_float(hw << 16), v[1] - __uint_as_float(hw & 0xffff0000u)};
-      bh[j] = hw;
-      bl[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, b2));
+      bh[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, b2));
     }
-    return PP{__builtin_bit_cast(bf16x8, bh), __builtin_bit_cast(bf16x8, bl)};
+    return __builtin_bit_cast(bf16x8, bh);
   }
-  // o += V^T(dt) P^T over the chunk's 8 slots; vv[e] holds the lane's elements of slot e
-  template <typename V>
-  static __device__ __forceinline__ f32x4 pv(int dt, const V* vv, const PP& pp, f32x4 o) {
+  // V^T(dt) operand of the chunk's 8 slots; vv[e] holds the lane's elements of slot e
+  typedef bf16x8 VA;
+  template <typename V> static __device__ __forceinline__ VA va(int dt, const V* vv) {
     uint32_t w[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -114,8 +112,13 @@ template <int DH> struct AttnT<bf16_t, DH> {
       // element dt of key slot 2j (low half) and of key slot 2j + 1 (high half)
       w[j] = __builtin_amdgcn_perm(hi, lo, (dt & 1) ? 0x07060302u : 0x05040100u);
     }
-    const bf16x8 A = __builtin_bit_cast(bf16x8, w);
-    return mfma_bf16_32(A, pp.lo, mfma_bf16_32(A, pp.hi, o));
+    return __builtin_bit_cast(bf16x8, w);
+  }
+  // o += V^T(dt) P^T
+  static __device__ __forceinline__ f32x4 pva(const VA& A, const PP& pp, f32x4 o) { return mfma_bf16_32(A, pp, o); }
+  template <typename V>
+  static __device__ __forceinline__ f32x4 pv(int dt, const V* vv, const PP& pp, f32x4 o) {
+    return pva(va(dt, vv), pp, o);
   }
 };
 
@@ -145,11 +148,21 @@ template <int DH> struct AttnT<float, DH> {
     for (int e = 0; e < 8; ++e) r.p[e] = ps[e];
     return r;
   }
+  struct VA { float v[8]; };
+  template <typename V> static __device__ __forceinline__ VA va(int dt, const V* vv) {
+    VA r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r.v[e] = __uint_as_float(vv[e].w[dt]);
+    return r;
+  }
+  static __device__ __forceinline__ f32x4 pva(const VA& A, const PP& pp, f32x4 o) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o = mfma_f32_4(A.v[e], pp.p[e], o);
+    return o;
+  }
   template <typename V>
   static __device__ __forceinline__ f32x4 pv(int dt, const V* vv, const PP& pp, f32x4 o) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o = mfma_f32_4(__uint_as_float(vv[e].w[dt]), pp.p[e], o);
-    return o;
+    return pva(va(dt, vv), pp, o);
   }
 };
 
@@ -231,11 +244,14 @@ __device__ __forceinline__ void fold_state(float& ma, float& la, f32x4* oa, floa
 }
 
 
-// One workgroup per (KV head, row group of TL tiles of 16 query rows, key
-// split of 1024 positions); wave w is class c = w / TL of tile slot w % TL.
-// Several splits leave one folded state per row each, and a merge kernel
-// folds them in split order (a split's chunks, tail chunks included, are
-// fixed by position, so the tree still depends on positions only).
+// One workgroup per (KV head, row group, key split); a row group is NT =
+// TP * TPW tiles of 16 query rows; wave w is class c = w / TP of tile pair
+// slot w % TP, which holds TPW tiles: the K and V fragments a wave reads
+// from the ring serve all its tiles.  A key split is a fixed run of spb ring
+// stages (spb is a function of the cache capacity only); several splits
+// leave one folded state per row each, and a merge kernel folds them in
+// split order (a split's chunks, tail chunks included, are fixed by
+// position, so the tree still depends on positions only).
 // Three phases per workgroup:
 //   1. prefix: ring stage s holds keys [128 s, 128 s + 128) of the head (the
 //      class-c chunk 4 s + c, K and V, 16-byte pieces XOR-swizzled by row) for
@@ -250,15 +266,25 @@ __device__ __forceinline__ void fold_state(float& ma, float& la, f32x4* oa, floa
 //      through the branch path); the scores come per branch and P V runs once
 //      per branch (rows of other branches add exact zeros);
 //   3. fold: classes 1..3 hand their states to class 0 through LDS, which
-//      folds 0, 1, 2, 3 in order and stores O / l.
-// Every global load is a DMA into LDS read back with inline asm; the waits
-// are static vmcnt counts (every wave issues the same DMA count per stage).
-template <typename T, int DH, int TL>
-__global__ void __launch_bounds__(256 * TL) __attribute__((amdgpu_waves_per_eu(1, TL))) la_attn_kernel(LaAttnArgs a) {
+//      folds 0, 1, 2, 3 in order and stores O / l (or the split's state).
+// Every global load of the ring is a DMA into LDS read back with inline asm;
+// the waits are static vmcnt counts (every wave issues the same DMA count per
+// stage).
+// Whether key split s holds chunks that reach past shared_end (a chunk
+// belongs to the split of its position).
+__host__ __device__ __forceinline__ bool split_has_tail(const LaAttnArgs& a, int s) {
+  const int per = a.spb * NCLS;
+  return max(a.tail0, s * per) < min(a.tail0 + a.n_tail, (s + 1) * per);
+}
+
+template <typename T, int DH, int TP, int TPW>
+__global__ void __launch_bounds__(64 * NCLS * TP) __attribute__((amdgpu_waves_per_eu(1, TP)))
+la_attn_kernel(LaAttnArgs a) {
   typedef AttnT<T, DH> AT;
   typedef typename AT::QF QF;
   typedef typename AT::VV VV;
-  constexpr int NW = NCLS * TL;
+  constexpr int NW = NCLS * TP;                 // waves
+  constexpr int NT = TP * TPW;                  // tiles per workgroup
   constexpr int ROWB = AT::ROWB, PIECES = AT::PIECES, LP = AT::LP, NDT = AT::NDT, VB = AT::VB;
   constexpr int CHB = CH * ROWB;                // K (or V) of one chunk
   constexpr int BLKB = NCLS * 2 * CHB;          // one ring stage: 4 chunks, K then V each
@@ -267,47 +293,70 @@ __global__ void __launch_bounds__(256 * TL) __attribute__((amdgpu_waves_per_eu(1
   static_assert(NDMA % NW == 0 && CW >= 1, "DMA blocks per wave");
   constexpr int DEPTH = 2;
   constexpr int RPB = 1024 / ROWB;              // key rows per 1 KB DMA block
-  // Q tiles, row positions (one DMA of 64 lanes), branch paths; the ring starts 1 KB aligned
-  constexpr int FIX = (TL * (16 * ROWB + 256 + 16 * 64 * 4) + 1023) & ~1023;
+  // Q tiles and row positions (one DMA of 64 lanes per tile); the ring starts 1 KB aligned
+  constexpr int FIX = (NT * (16 * ROWB + 256) + 1023) & ~1023;
   extern __shared__ __attribute__((aligned(1024))) char lds[];
   char* const ring = lds + FIX;                 // ring stages, later the tail rows, then the fold states
 
-  // block -> (XCD, KV head, row group, key split): the workgroups of one
-  // head share an XCD (and its L2)
+  // block -> (XCD, KV head, key split, row group): the workgroups of one
+  // head share an XCD (and its L2).  A split holding tail chunks gets two
+  // workgroups per row group when a wave has two tiles (each takes one tile
+  // of every tile pair), so the tail work of a tile pair runs in parallel.
   const int xcd = blockIdx.x & 7, bi = blockIdx.x >> 3;
-  const int sp = bi % a.nsplit;
-  const int rg = (bi / a.nsplit) % a.rgroups;
-  const int g_kv = xcd + 8 * (bi / (a.nsplit * a.rgroups));
+  const int g_kv = xcd + 8 * (bi / a.wg_head);
   if (g_kv >= a.Hkv) return;
+  int li = bi % a.wg_head, sp = 0, hf = -1;
+  for (; sp < a.nsplit; ++sp) {
+    const bool half = TPW == 2 && split_has_tail(a, sp);
+    const int n = a.rgroups * (half ? 2 : 1);
+    if (li < n) {
+      if (half) {
+        hf = li % 2;
+        li /= 2;
+      }
+      break;
+    }
+    li -= n;
+  }
+  if (sp == a.nsplit) return;
+  const int rg = li;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int cls = wave / TL, tslot = wave % TL;
+  const int cls = wave / TP, pslot = wave % TP;
   const int g = lane >> 4, c16 = lane & 15;
   const int se = a.shared_end;
   const float sl2 = a.scale_log2;
   const char* kc = (const char*)a.kc + (size_t)g_kv * a.T_cap * ROWB;
   const char* vc = (const char*)a.vc + (size_t)g_kv * a.T_cap * ROWB;
 
-  // the wave's tile: 16 rows of q-head hh (rows past Q load row Q - 1 and stay unused)
+  // the wave's tiles: 16 rows of q-head hh each (rows past Q load row Q - 1
+  // and stay unused; a tile past the head group is skipped)
   const int group = a.H / a.Hkv;
   const int rtiles = (a.Q + 15) >> 4;
-  const int tile = rg * TL + tslot;
-  const bool tv = tile < group * rtiles;
-  const int hh = g_kv * group + (tv ? tile / rtiles : 0);
-  const int row0 = (tv ? tile % rtiles : 0) * 16;
-  const int row = row0 + c16;
-  const bool rvalid = tv && row < a.Q;
-  char* const qa = lds + tslot * 16 * ROWB;
-  char* const pa = lds + TL * 16 * ROWB + tslot * 256;
-  int* const spath = (int*)(lds + TL * (16 * ROWB + 256)) + tslot * 1024;  // [16 branches][64 positions]
-  if (cls == 0) {
-    __builtin_amdgcn_global_load_lds((const void*)(a.pos + min(row0 + (lane & 15), a.Q - 1)), (lds_void_t*)pa, 4, 0,
-                                     0);
+  bool tv[TPW], rvalid[TPW];
+  int hh[TPW], row[TPW];
 #pragma unroll
-    for (int j = 0; j < 16 / RPB; ++j) {
-      const int r = min(row0 + j * RPB + lane / PIECES, a.Q - 1);
-      const char* src = (const char*)a.q + ((size_t)r * a.H + hh) * ROWB + 16 * (lane % PIECES);
-      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(qa + j * 1024), 16, 0, 0);
+  for (int u = 0; u < TPW; ++u) {
+    const int tile = rg * NT + pslot * TPW + (hf >= 0 ? hf : u);
+    tv[u] = (hf < 0 || u == 0) && tile < group * rtiles;
+    hh[u] = g_kv * group + (tv[u] ? tile / rtiles : 0);
+    row[u] = (tv[u] ? tile % rtiles : 0) * 16 + c16;
+    rvalid[u] = tv[u] && row[u] < a.Q;
+  }
+  auto qa = [&](int u) __attribute__((always_inline)) { return lds + (pslot * TPW + u) * 16 * ROWB; };
+  auto pa = [&](int u) __attribute__((always_inline)) { return lds + NT * 16 * ROWB + (pslot * TPW + u) * 256; };
+  if (cls == 0) {
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const int row0 = row[u] - c16;
+      __builtin_amdgcn_global_load_lds((const void*)(a.pos + min(row0 + (lane & 15), a.Q - 1)), (lds_void_t*)pa(u), 4,
+                                       0, 0);
+#pragma unroll
+      for (int j = 0; j < 16 / RPB; ++j) {
+        const int r = min(row0 + j * RPB + lane / PIECES, a.Q - 1);
+        const char* src = (const char*)a.q + ((size_t)r * a.H + hh[u]) * ROWB + 16 * (lane % PIECES);
+        __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(qa(u) + j * 1024), 16, 0, 0);
+      }
     }
   }
 
@@ -315,8 +364,8 @@ __global__ void __launch_bounds__(256 * TL) __attribute__((amdgpu_waves_per_eu(1
   // one 16-byte piece (a dummy that nobody reads), so every wave issues CW
   // DMA instructions per stage on every path
   const int nblk = (a.class_last + NCLS) / NCLS;   // stages of the whole prefix (class_last = -1: none)
-  const int s_begin = sp * SPB;                       // this split's stages
-  const int s_end = min(s_begin + SPB, nblk);
+  const int s_begin = sp * a.spb;                     // this split's stages
+  const int s_end = min(s_begin + a.spb, nblk);
   // wave w brings the DMA blocks w*CW .. w*CW + CW - 1 of a stage (a
   // contiguous run inside its chunk cw of the stage: CW divides the 1 KB
   // blocks of a chunk half or is a multiple of them).  The lane's source
@@ -362,33 +411,36 @@ __global__ void __launch_bounds__(256 * TL) __attribute__((amdgpu_waves_per_eu(1
                                          (lds_void_t*)(stage + (b0 + j) * 1024), 16, 0, 0);
     }
   };
-  // the row's branch (read now, used by the tail phase after the ring)
-  const int br = (a.n_tail > 0 && rvalid) ? a.branch[row] : -1;
+  // the rows' branches (read now, used by the tail phase after the ring)
+  int br[TPW];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) br[u] = (a.n_tail > 0 && rvalid[u]) ? a.branch[row[u]] : -1;
 #pragma unroll
   for (int k = 0; k < DEPTH; ++k) issue(ring + k * BLKB, s_begin + k);
   wait_vm<(CW * DEPTH < 63 ? CW * DEPTH : 63)>();   // this wave's Q and positions (issued first) have landed
   ring_barrier();                                    // ... and those of the other waves
-  QF qf;
-  int pos;
-  {
+  QF qf[TPW];
+  int pos[TPW], pmin[TPW];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
     typename LdsT<16>::T qraw[LP];
-    const uint32_t qaddr = lds_addr(qa + c16 * ROWB + 16 * LP * g);
+    const uint32_t qaddr = lds_addr(qa(u) + c16 * ROWB + 16 * LP * g);
     if constexpr (LP >= 1) qraw[0] = lds_read<16, 0>(qaddr);
     if constexpr (LP >= 2) qraw[1] = lds_read<16, 16>(qaddr);
     if constexpr (LP >= 3) qraw[2] = lds_read<16, 32>(qaddr);
     if constexpr (LP >= 4) qraw[3] = lds_read<16, 48>(qaddr);
-    unsigned int praw[1] = {lds_read<4, 0>(lds_addr(pa + 4 * c16))};
+    unsigned int praw[1] = {lds_read<4, 0>(lds_addr(pa(u) + 4 * c16))};
     lds_wait(qraw);
     lds_wait(praw);
 #pragma unroll
-    for (int s = 0; s < LP; ++s) qf.p[s] = rvalid ? __builtin_bit_cast(u32x4, qraw[s]) : u32x4{0, 0, 0, 0};
-    pos = rvalid ? (int)praw[0] : -1;
-  }
-  // smallest position among the wave's rows: chunks ending at or below it need no mask
-  int pmin = rvalid ? pos : 0x7fffffff;
+    for (int s = 0; s < LP; ++s) qf[u].p[s] = rvalid[u] ? __builtin_bit_cast(u32x4, qraw[s]) : u32x4{0, 0, 0, 0};
+    pos[u] = rvalid[u] ? (int)praw[0] : -1;
+    // smallest position among the tile's rows: chunks ending at or below it need no mask
+    int pm = rvalid[u] ? pos[u] : 0x7fffffff;
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) pmin = min(pmin, __shfl_xor(pmin, o, 64));
-  pmin = __builtin_amdgcn_readfirstlane(pmin);
+    for (int o = 32; o > 0; o >>= 1) pm = min(pm, __shfl_xor(pm, o, 64));
+    pmin[u] = __builtin_amdgcn_readfirstlane(pm);
+  }
 
   // lane parts of the fragment addresses of the class's chunk (stage offsets are immediates)
   uint32_t koff[LP], voff[4];
@@ -402,10 +454,15 @@ __global__ void __launch_bounds__(256 * TL) __attribute__((amdgpu_waves_per_eu(1
     voff[e] = lds_addr(ring + cls * 2 * CHB + CHB + kk * ROWB + 16 * ((off / 16) ^ (kk % PIECES)) + off % 16);
   }
 
-  float M = NEG_INF, L = 0.f;
-  f32x4 O[NDT];
+  float M[TPW], L[TPW];
+  f32x4 O[TPW][NDT];
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) O[dt] = f32x4{0, 0, 0, 0};
+  for (int u = 0; u < TPW; ++u) {
+    M[u] = NEG_INF;
+    L[u] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) O[u][dt] = f32x4{0, 0, 0, 0};
+  }
 
   auto step = [&](auto SI, int s) __attribute__((always_inline)) {
     constexpr int S = decltype(SI)::value;
@@ -437,183 +494,225 @@ __global__ void __launch_bounds__(256 * TL) __attribute__((amdgpu_waves_per_eu(1
     issue(ring + SB, s + DEPTH);
     if (live) {
       const int x0 = CH * k;
-      float sc[8];
+      float sc[TPW][8];
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj) {
         QF kf;
 #pragma unroll
         for (int q = 0; q < LP; ++q) kf.p[q] = __builtin_bit_cast(u32x4, kraw[LP * jj + q]);
-        const f32x4 s4 = AT::qk(kf, qf);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sc[4 * jj + r] = s4[r];
-      }
-      if (x0 + CH - 1 > pmin) {                 // some key of the chunk lies past some row
+        for (int u = 0; u < TPW; ++u) {
+          if (!tv[u]) continue;
+          const f32x4 s4 = AT::qk(kf, qf[u]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sc[e] = x0 + slot_key(g, e) <= pos ? sc[e] : NEG_INF;
+          for (int r = 0; r < 4; ++r) sc[u][4 * jj + r] = s4[r];
+        }
       }
-      const float wa = chunk_softmax(sc, sl2, M, L);
+      typename AT::PP pp[TPW];
+#pragma unroll
+      for (int u = 0; u < TPW; ++u) {
+        if (!tv[u]) continue;
+        if (x0 + CH - 1 > pmin[u]) {            // some key of the chunk lies past some row
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sc[u][e] = x0 + slot_key(g, e) <= pos[u] ? sc[u][e] : NEG_INF;
+        }
+        const float wa = chunk_softmax(sc[u], sl2, M[u], L[u]);
+        pp[u] = AT::prep(sc[u]);
+        scale_o<NDT>(O[u], wa);
+      }
       VV vv[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) vv[e] = __builtin_bit_cast(VV, vraw[e]);
-      const typename AT::PP pp = AT::prep(sc);
-      scale_o<NDT>(O, wa);
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) O[dt] = AT::pv(dt, vv, pp, O[dt]);
+      for (int dt = 0; dt < NDT; ++dt) {
+        const typename AT::VA A = AT::va(dt, vv);
+#pragma unroll
+        for (int u = 0; u < TPW; ++u)
+          if (tv[u]) O[u][dt] = AT::pva(A, pp[u], O[u][dt]);
+      }
     }
   };
   for (int s0 = s_begin; s0 < s_end; s0 += DEPTH)
-    static_for<0, DEPTH>([&](auto SI) { step(SI, s0 + decltype(SI)::value); });
+    static_for<0, DEPTH>([&](auto SI) {
+      if (decltype(SI)::value == 0 || s0 + decltype(SI)::value < s_end) step(SI, s0 + decltype(SI)::value);
+    });
 
   wait_vm<0>();                                   // the dummy stages have landed: the ring is free
   ring_barrier();
 
   // tail chunks of this split (a chunk belongs to the split of its position)
-  const int t_lo = max(a.tail0, sp * SPB * NCLS), t_hi = min(a.tail0 + a.n_tail, (sp + 1) * SPB * NCLS);
-  if (t_lo < t_hi) {
-    // the tile's branches that reach a tail chunk (at most 16); every class
-    // wave of the tile finds the same list
-    const bool need0 = rvalid && pos >= CH * a.tail0;
-    int nbr = 0;
-    int bl = -1;                                  // lane i < nbr: branch i
-    unsigned long long pend = __ballot(need0 && g == 0);
-    while (pend) {
-      const int b = __builtin_amdgcn_readfirstlane(__shfl(br, __ffsll((long long)pend) - 1, 64));
-      pend &= ~__ballot(need0 && g == 0 && br == b);
-      if (lane == nbr) bl = b;
-      ++nbr;
-    }
+  const int t_lo = max(a.tail0, sp * a.spb * NCLS), t_hi = min(a.tail0 + a.n_tail, (sp + 1) * a.spb * NCLS);
+  if (t_lo < t_hi) {   // split_has_tail(a, sp)
     const int X0 = CH * a.tail0;
     const int ncom = se - X0;                       // 0 .. 31
     const int EP = a.max_pos - se + 1;              // 1 .. 64
-    // the tile's branch paths: spath[i][e] = workspace row of position se + e
+    // tail LDS: the tiles' branch paths, then the staged rows of each tile pair slot
+    int* const spath0 = (int*)ring;                 // [NT][16 branches][64 positions]
+    char* const ks = ring + NT * 16 * 64 * 4 + pslot * 2 * a.trows * ROWB;
+    char* const vs = ks + a.trows * ROWB;
+    // the tiles' branches that reach a tail chunk (at most 16 each); every
+    // class wave of a tile finds the same list (lane i < nbr: branch i)
+    int nbr[TPW], bl[TPW];
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const bool need0 = rvalid[u] && pos[u] >= X0;
+      nbr[u] = 0;
+      bl[u] = -1;
+      unsigned long long pend = __ballot(need0 && g == 0);
+      while (pend) {
+        const int b = __builtin_amdgcn_readfirstlane(__shfl(br[u], __ffsll((long long)pend) - 1, 64));
+        pend &= ~__ballot(need0 && g == 0 && br[u] == b);
+        if (lane == nbr[u]) bl[u] = b;
+        ++nbr[u];
+      }
+    }
+    // the tiles' branch paths: spath[i][e] = workspace row of position se + e
     // on branch i (-1 when the position is not on it); class 0 writes them,
     // every load issued before any is used
     if (cls == 0) {
-      const int plen = lane < nbr ? min(a.path_len[bl], a.maxp) : 0;
-      int wv[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int b = __shfl(bl, i, 64), pl = __shfl(plen, i, 64);
-        wv[i] = (i < nbr && lane < pl) ? a.path[(size_t)b * a.maxp + lane] : -1;
+      for (int u = 0; u < TPW; ++u) {
+        int* const spath = spath0 + (pslot * TPW + u) * 1024;
+        const int plen = lane < nbr[u] ? min(a.path_len[bl[u]], a.maxp) : 0;
+        int wv[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int b = __shfl(bl[u], i, 64), pl = __shfl(plen, i, 64);
+          wv[i] = (i < nbr[u] && lane < pl) ? a.path[(size_t)b * a.maxp + lane] : -1;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (i < nbr[u]) spath[i * 64 + lane] = (unsigned)wv[i] < (unsigned)a.n_ws ? wv[i] : -1;
       }
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if (i < nbr) spath[i * 64 + lane] = (unsigned)wv[i] < (unsigned)a.n_ws ? wv[i] : -1;
     }
     // branches staged at once per tile (the committed rows, then EP rows per
     // branch), and the batches every tile of the workgroup goes through
     const int bb = (a.trows - ncom) / EP;           // >= 1 (the launcher sizes trows)
-    int* const nbat = (int*)(lds + TL * 16 * ROWB);   // the row positions' space, free since the prologue
-    if (cls == 0 && lane == 0) nbat[tslot] = (nbr + bb - 1) / bb;
+    int* const nbat = (int*)(lds + NT * 16 * ROWB);   // the row positions' space, free since the prologue
+    if (cls == 0 && lane == 0) {
+#pragma unroll
+      for (int u = 0; u < TPW; ++u) nbat[pslot * TPW + u] = (nbr[u] + bb - 1) / bb;
+    }
     __syncthreads();
     int nbatch = 0;
 #pragma unroll
-    for (int t = 0; t < TL; ++t) nbatch = max(nbatch, nbat[t]);
-    char* const ks = ring + tslot * 2 * a.trows * ROWB;
-    char* const vs = ks + a.trows * ROWB;
+    for (int t = 0; t < NT; ++t) nbatch = max(nbatch, nbat[t]);
     const char* kw = (const char*)a.kw + (size_t)g_kv * a.ws_cap * ROWB;
     const char* vw = (const char*)a.vw + (size_t)g_kv * a.ws_cap * ROWB;
     const int tau = (cls - a.tail0 % NCLS + NCLS) % NCLS;   // the class's tail chunk (at most one)
     const int x0 = CH * (a.tail0 + tau);
     const bool mine_chunk = tau < a.n_tail && a.tail0 + tau >= t_lo && a.tail0 + tau < t_hi;
-    const bool need = mine_chunk && rvalid && pos >= x0;
-    for (int bt = 0; bt < nbatch; ++bt) {
-      const int i0 = bt * bb;
-      const int nb = max(0, min(bb, nbr - i0));
-      // staged row of key x on batch branch bi (x >= X0); a clamped committed
-      // row where a position is not on the branch's path (never visible to it)
-      const int nr = nb > 0 ? ncom + nb * EP : 0;
-      for (int blk = cls; blk * RPB < nr; blk += NCLS) {
-        const int j = blk * RPB + lane / PIECES;
-        const int piece = (lane % PIECES) ^ (j % PIECES);
-        int crow = se - 1, wrow = -1;
-        if (j < ncom) crow = X0 + j;
-        else if (j < nr) wrow = spath[(i0 + (j - ncom) / EP) * 64 + (j - ncom) % EP];
-        const size_t off = (size_t)(wrow >= 0 ? wrow : crow) * ROWB + 16 * piece;
-        __builtin_amdgcn_global_load_lds((const void*)((wrow >= 0 ? kw : kc) + off), (lds_void_t*)(ks + blk * 1024),
-                                         16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void*)((wrow >= 0 ? vw : vc) + off), (lds_void_t*)(vs + blk * 1024),
-                                         16, 0, 0);
-      }
-      wait_vm<0>();
-      __syncthreads();
-      auto srow = [&](int x, int bi) -> int {
-        if (x < se) return x - X0;
-        const int e = x - se;
-        return e < EP ? ncom + bi * EP + e : 0;
-      };
-      // rows of this batch's branches: the chunk's online step (for the
-      // wave's other rows every score stays -inf, which leaves their state
-      // exactly as it is, and P V adds exact zeros)
-      if (nb > 0 && __ballot(need) != 0ull) {
-        float sc[8];
+    auto srow = [&](int x, int bi) -> int {
+      if (x < se) return x - X0;
+      const int e = x - se;
+      return e < EP ? ncom + bi * EP + e : 0;
+    };
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sc[e] = NEG_INF;
-        for (int bi = 0; bi < nb; ++bi) {
-          const int b = __shfl(bl, i0 + bi, 64);
-          const bool mine = need && br == b;
-          if (__ballot(mine) == 0ull) continue;
+    for (int u = 0; u < TPW; ++u) {
+      const int* const spath = spath0 + (pslot * TPW + u) * 1024;
+      const bool need = mine_chunk && rvalid[u] && pos[u] >= x0;
+      for (int bt = 0; bt < nbatch; ++bt) {
+        const int i0 = bt * bb;
+        const int nb = max(0, min(bb, nbr[u] - i0));
+        // staged row of key x on batch branch bi (x >= X0); a clamped committed
+        // row where a position is not on the branch's path (never visible to it)
+        const int nr = nb > 0 ? ncom + nb * EP : 0;
+        for (int blk = cls; blk * RPB < nr; blk += NCLS) {
+          const int j = blk * RPB + lane / PIECES;
+          const int piece = (lane % PIECES) ^ (j % PIECES);
+          int crow = se - 1, wrow = -1;
+          if (j < ncom) crow = X0 + j;
+          else if (j < nr) wrow = spath[(i0 + (j - ncom) / EP) * 64 + (j - ncom) % EP];
+          const size_t off = (size_t)(wrow >= 0 ? wrow : crow) * ROWB + 16 * piece;
+          __builtin_amdgcn_global_load_lds((const void*)((wrow >= 0 ? kw : kc) + off), (lds_void_t*)(ks + blk * 1024),
+                                           16, 0, 0);
+          __builtin_amdgcn_global_load_lds((const void*)((wrow >= 0 ? vw : vc) + off), (lds_void_t*)(vs + blk * 1024),
+                                           16, 0, 0);
+        }
+        wait_vm<0>();
+        __syncthreads();
+        // rows of this batch's branches: the chunk's online step (for the
+        // wave's other rows every score stays -inf, which leaves their state
+        // exactly as it is, and P V adds exact zeros)
+        if (nb > 0 && __ballot(need) != 0ull) {
+          float sc[8];
 #pragma unroll
-          for (int jj = 0; jj < 2; ++jj) {
-            const int r = srow(x0 + 16 * jj + c16, bi);
-            QF kf;
+          for (int e = 0; e < 8; ++e) sc[e] = NEG_INF;
+          for (int bi = 0; bi < nb; ++bi) {
+            const int b = __shfl(bl[u], i0 + bi, 64);
+            const bool mine = need && br[u] == b;
+            if (__ballot(mine) == 0ull) continue;
 #pragma unroll
-            for (int q = 0; q < LP; ++q)
-              kf.p[q] = *(const u32x4*)(ks + r * ROWB + 16 * ((LP * g + q) ^ (r % PIECES)));
-            const f32x4 s4 = AT::qk(kf, qf);
+            for (int jj = 0; jj < 2; ++jj) {
+              const int r = srow(x0 + 16 * jj + c16, bi);
+              QF kf;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const float v = (x0 + 16 * jj + 4 * g + q <= pos) ? s4[q] : NEG_INF;
-              sc[4 * jj + q] = mine ? v : sc[4 * jj + q];
+              for (int q = 0; q < LP; ++q)
+                kf.p[q] = *(const u32x4*)(ks + r * ROWB + 16 * ((LP * g + q) ^ (r % PIECES)));
+              const f32x4 s4 = AT::qk(kf, qf[u]);
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const float v = (x0 + 16 * jj + 4 * g + q <= pos[u]) ? s4[q] : NEG_INF;
+                sc[4 * jj + q] = mine ? v : sc[4 * jj + q];
+              }
             }
           }
-        }
-        const float wa = chunk_softmax(sc, sl2, M, L);
-        scale_o<NDT>(O, wa);
-        for (int bi = 0; bi < nb; ++bi) {
-          const int b = __shfl(bl, i0 + bi, 64);
-          const bool mine = need && br == b;
-          if (__ballot(mine) == 0ull) continue;
-          VV vv[8];
-          float ps[8];
+          const float wa = chunk_softmax(sc, sl2, M[u], L[u]);
+          scale_o<NDT>(O[u], wa);
+          for (int bi = 0; bi < nb; ++bi) {
+            const int b = __shfl(bl[u], i0 + bi, 64);
+            const bool mine = need && br[u] == b;
+            if (__ballot(mine) == 0ull) continue;
+            VV vv[8];
+            float ps[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int r = srow(x0 + slot_key(g, e), bi);
-            const int off = VB * c16;
-            vv[e] = *(const VV*)(vs + r * ROWB + 16 * ((off / 16) ^ (r % PIECES)) + off % 16);
-            ps[e] = mine ? sc[e] : 0.f;
+            for (int e = 0; e < 8; ++e) {
+              const int r = srow(x0 + slot_key(g, e), bi);
+              const int off = VB * c16;
+              vv[e] = *(const VV*)(vs + r * ROWB + 16 * ((off / 16) ^ (r % PIECES)) + off % 16);
+              ps[e] = mine ? sc[e] : 0.f;
+            }
+            const typename AT::PP pp = AT::prep(ps);
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) O[u][dt] = AT::pv(dt, vv, pp, O[u][dt]);
           }
-          const typename AT::PP pp = AT::prep(ps);
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) O[dt] = AT::pv(dt, vv, pp, O[dt]);
         }
+        __syncthreads();                          // the staged rows are no longer read
       }
-      __syncthreads();                            // the staged rows are no longer read
     }
   }
 
   // fold: classes 1..3 hand (m, l, O) over (lane for lane: same row, same
   // head dimensions), class 0 folds 0, 1, 2, 3 in order
-  float* const xf = (float*)ring + (size_t)(tslot * (NCLS - 1)) * 64 * (4 * NDT + 2);
+  constexpr int FS = 64 * (4 * NDT + 2);          // floats of one wave's state
+  auto xf = [&](int u, int c) __attribute__((always_inline)) {
+    return (float*)ring + (size_t)((pslot * TPW + u) * (NCLS - 1) + (c - 1)) * FS + lane * (4 * NDT + 2);
+  };
   if (cls > 0) {
-    float* d = xf + (size_t)(cls - 1) * 64 * (4 * NDT + 2) + lane * (4 * NDT + 2);
-    d[0] = M;
-    d[1] = L;
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
+    for (int u = 0; u < TPW; ++u) {
+      float* d = xf(u, cls);
+      d[0] = M[u];
+      d[1] = L[u];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) d[2 + 4 * dt + r] = O[dt][r];
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) d[2 + 4 * dt + r] = O[u][dt][r];
+    }
   }
   __syncthreads();
-  if (cls == 0 && rvalid) {
+  if (cls != 0) return;
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    if (!rvalid[u]) continue;
     float Mf = NEG_INF, Lf = 0.f;
     f32x4 Of[NDT];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) Of[dt] = f32x4{0, 0, 0, 0};
-    fold_state<NDT>(Mf, Lf, Of, M, L, O);
+    fold_state<NDT>(Mf, Lf, Of, M[u], L[u], O[u]);
 #pragma unroll
     for (int c = 1; c < NCLS; ++c) {
-      const float* d = xf + (size_t)(c - 1) * 64 * (4 * NDT + 2) + lane * (4 * NDT + 2);
+      const float* d = xf(u, c);
       f32x4 Oc[NDT];
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
@@ -623,7 +722,7 @@ __global__ void __launch_bounds__(256 * TL) __attribute__((amdgpu_waves_per_eu(1
     }
     if (a.nsplit > 1) {
       // the split's state: (m, l) and O, lane dims NDT*(4g + r) + dt (4*NDT contiguous floats)
-      const size_t base = ((size_t)sp * a.H + hh) * a.Q + row;
+      const size_t base = ((size_t)sp * a.H + hh[u]) * a.Q + row[u];
       if (g == 0) *(float2*)(a.part_ml + base * 2) = make_float2(Mf, Lf);
       float4* po = (float4*)(a.part_o + base * DH + 4 * NDT * g);
 #pragma unroll
@@ -632,7 +731,7 @@ __global__ void __launch_bounds__(256 * TL) __attribute__((amdgpu_waves_per_eu(1
         po[q] = make_float4(Of[(i0 + 0) % NDT][(i0 + 0) / NDT], Of[(i0 + 1) % NDT][(i0 + 1) / NDT],
                             Of[(i0 + 2) % NDT][(i0 + 2) / NDT], Of[(i0 + 3) % NDT][(i0 + 3) / NDT]);
       }
-      return;
+      continue;
     }
     // lane holds head dimensions NDT*(4g + r) + dt: 4*NDT contiguous values,
     // stored as 16-byte pieces
@@ -649,54 +748,73 @@ __global__ void __launch_bounds__(256 * TL) __attribute__((amdgpu_waves_per_eu(1
       }
       ow[w] = v;
     }
-    u32x4* dst = (u32x4*)((T*)a.o + ((size_t)row * a.H + hh) * DH + 4 * NDT * g);
+    u32x4* dst = (u32x4*)((T*)a.o + ((size_t)row[u] * a.H + hh[u]) * DH + 4 * NDT * g);
 #pragma unroll
     for (int q = 0; q < 4 * NDT / EPW / 4; ++q) dst[q] = u32x4{ow[4 * q], ow[4 * q + 1], ow[4 * q + 2], ow[4 * q + 3]};
   }
 }
 
 // Fold of the key splits' states in split order (the same sequence of
-// roundings as fold_state), then O / l.  One thread per head dimension.
+// roundings as fold_state), then O / l.  One thread per 4 head dimensions of
+// a (row, head).
 template <typename T, int DH>
-__global__ void __launch_bounds__(DH) la_attn_merge_kernel(LaAttnArgs a) {
-  const int idx = blockIdx.x;                   // row * H + head
-  const int row = idx / a.H, hh = idx % a.H;
-  const int d = threadIdx.x;
-  float ma = NEG_INF, la = 0.f, oa = 0.f;
+__global__ void __launch_bounds__(256) la_attn_merge_kernel(LaAttnArgs a) {
+  constexpr int V4 = DH / 4;
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= a.Q * a.H * V4) return;
+  const int d4 = idx % V4, rh = idx / V4;
+  const int row = rh / a.H, hh = rh % a.H;
+  float ma = NEG_INF, la = 0.f;
+  float oa[4] = {0.f, 0.f, 0.f, 0.f};
   for (int s = 0; s < a.nsplit; ++s) {
     const size_t base = ((size_t)s * a.H + hh) * a.Q + row;
     const float2 ml = *(const float2*)(a.part_ml + base * 2);
     if (ml.x == NEG_INF) continue;
-    const float ob = a.part_o[base * DH + d];
+    const float4 ob = *(const float4*)(a.part_o + base * DH + 4 * d4);
     const float mn = fmaxf(ma, ml.x);
     const float wa = ex2(ma - mn), wb = ex2(ml.x - mn);
     la = lin2(la, wa, ml.y, wb);
-    oa = lin2(oa, wa, ob, wb);
+    oa[0] = lin2(oa[0], wa, ob.x, wb);
+    oa[1] = lin2(oa[1], wa, ob.y, wb);
+    oa[2] = lin2(oa[2], wa, ob.z, wb);
+    oa[3] = lin2(oa[3], wa, ob.w, wb);
     ma = mn;
   }
-  st<T>((T*)a.o + ((size_t)row * a.H + hh) * DH + d, oa / la);
+  T* dst = (T*)a.o + ((size_t)row * a.H + hh) * DH + 4 * d4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) st<T>(dst + i, oa[i] / la);
 }
 
-int la_attention_parts(int max_pos) { return max_pos < 0 ? 1 : max_pos / (CH * NCLS * SPB) + 1; }
+// Ring stages (128 positions each) per key split: a function of the cache
+// capacity only (about four splits when the cache is full), so every call on
+// one cache cuts its keys the same way.
+int la_attention_spb(int t_cap) {
+  const int stages = (std::max(t_cap, 1) + CH * NCLS - 1) / (CH * NCLS);
+  return std::max(1, (stages + 3) / 4);
+}
+int la_attention_parts(int max_pos, int t_cap) {
+  return max_pos < 0 ? 1 : max_pos / (CH * NCLS * la_attention_spb(t_cap)) + 1;
+}
 
 // dynamic LDS of the kernel: the fixed part, then the largest of the ring,
-// the tail rows of TL tiles (trows each, K and V) and the fold states
-template <typename T, int DH, int TL>
+// the tail (branch paths of NT tiles, rows of TP tiles: trows each, K and V)
+// and the fold states
+template <typename T, int DH, int TP, int TPW>
 static size_t attn_lds(int trows) {
-  constexpr int ROWB = AttnT<T, DH>::ROWB, NDT = AttnT<T, DH>::NDT;
-  const size_t fix = ((size_t)TL * (16 * ROWB + 256 + 16 * 64 * 4) + 1023) & ~(size_t)1023;
+  constexpr int ROWB = AttnT<T, DH>::ROWB, NDT = AttnT<T, DH>::NDT, NT = TP * TPW;
+  const size_t fix = ((size_t)NT * (16 * ROWB + 256) + 1023) & ~(size_t)1023;
   const size_t ring = (size_t)2 * NCLS * 2 * CH * ROWB;
-  const size_t tail = (size_t)TL * 2 * trows * ROWB;
-  const size_t fold = (size_t)TL * (NCLS - 1) * 64 * (4 * NDT + 2) * 4;
+  const size_t tail = (size_t)NT * 16 * 64 * 4 + (size_t)TP * 2 * trows * ROWB;
+  const size_t fold = (size_t)NT * (NCLS - 1) * 64 * (4 * NDT + 2) * 4;
   return fix + std::max(ring, std::max(tail, fold));
 }
 
-template <typename T, int DH, int TL>
-static void launch_tl(const LaAttnArgs& a, int grid, size_t lds, hipStream_t st) {
-  static const bool attr = hipFuncSetAttribute((const void*)&la_attn_kernel<T, DH, TL>,
+template <typename T, int DH, int TP, int TPW>
+static void launch_cfg(const LaAttnArgs& a, int grid, size_t lds, hipStream_t st) {
+  static const bool attr = hipFuncSetAttribute((const void*)&la_attn_kernel<T, DH, TP, TPW>,
                                                hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES) == hipSuccess;
   (void)attr;
-  hipLaunchKernelGGL((la_attn_kernel<T, DH, TL>), dim3(grid), dim3(256 * TL), lds, st, a);
+  hipLaunchKernelGGL((la_attn_kernel<T, DH, TP, TPW>), dim3(grid), dim3(64 * NCLS * TP), lds, st, a);
 }
 
 template <typename T, int DH>
@@ -704,28 +822,43 @@ static int launch_dh(LaAttnArgs a, hipStream_t st) {
   const int group = a.H / a.Hkv;
   const int tiles = group * ((a.Q + 15) / 16);
   // staged tail rows per tile (K and V): what the LDS left after the fixed
-  // part holds, at least the committed rows of a tail chunk (< 32) and the
-  // EP positions of one branch; at most those of 16 branches
+  // part and the branch paths holds, at least the committed rows of a tail
+  // chunk (< 32) and the EP positions of one branch; at most those of 16
+  // branches
   constexpr int ROWB = AttnT<T, DH>::ROWB, RPB = 1024 / ROWB;
   const int EP = a.n_tail > 0 ? a.max_pos - a.shared_end + 1 : 0;
-  auto rows_for = [&](int tl) {
-    const size_t fix = (((size_t)tl * (16 * ROWB + 256 + 16 * 64 * 4)) + 1023) & ~(size_t)1023;
-    const int fit = (int)((LDS_BYTES - fix) / ((size_t)tl * 2 * ROWB)) / RPB * RPB;
+  auto rows_for = [&](int tp, int nt) {
+    const size_t fix = (((size_t)nt * (16 * ROWB + 256)) + 1023) & ~(size_t)1023;
+    const size_t paths = (size_t)nt * 16 * 64 * 4;
+    const int fit = (int)((LDS_BYTES - fix - paths) / ((size_t)tp * 2 * ROWB)) / RPB * RPB;
     const int want = ((CH - 1 + 16 * EP) + RPB - 1) / RPB * RPB;
     return std::min(fit, want);
   };
   const int need_rows = ((CH - 1 + EP) + RPB - 1) / RPB * RPB;
-  int tl = tiles >= 4 ? 2 : 1;
-  if (a.n_tail > 0 && rows_for(tl) < need_rows) tl = 1;
-  if (a.n_tail > 0 && rows_for(tl) < need_rows) return -2;
-  a.trows = a.n_tail > 0 ? rows_for(tl) : 0;
-  const size_t l2 = attn_lds<T, DH, 2>(a.trows), l1 = attn_lds<T, DH, 1>(a.trows);
-  if ((tl == 1 ? l1 : l2) > LDS_BYTES) return -2;
-  a.rgroups = (tiles + tl - 1) / tl;
-  const int grid = 8 * ((a.Hkv + 7) / 8) * a.rgroups * a.nsplit;
-  if (tl == 2) launch_tl<T, DH, 2>(a, grid, l2, st);
-  else launch_tl<T, DH, 1>(a, grid, l1, st);
-  if (a.nsplit > 1) hipLaunchKernelGGL((la_attn_merge_kernel<T, DH>), dim3(a.Q * a.H), dim3(DH), 0, st, a);
+  // tiles per workgroup: 4 (two tile pairs) while that still gives about 160
+  // workgroups, else 2, or 1 for a single tile
+  const int kv = 8 * ((a.Hkv + 7) / 8);
+  auto wgs = [&](int nt) { return kv * ((tiles + nt - 1) / nt) * a.nsplit; };
+  int nt = tiles == 1 ? 1 : (tiles >= 3 && wgs(4) >= 160) ? 4 : 2;
+  const int tp = nt == 4 ? 2 : 1;
+  if (a.n_tail > 0 && rows_for(tp, nt) < need_rows) return -2;
+  a.trows = a.n_tail > 0 ? rows_for(tp, nt) : 0;
+  a.rgroups = (tiles + nt - 1) / nt;
+  a.wg_head = 0;
+  for (int s = 0; s < a.nsplit; ++s) a.wg_head += a.rgroups * (nt > 1 && split_has_tail(a, s) ? 2 : 1);
+  const int grid = kv * a.wg_head;
+  size_t lds;
+  if (nt == 4) lds = attn_lds<T, DH, 2, 2>(a.trows);
+  else if (nt == 2) lds = attn_lds<T, DH, 1, 2>(a.trows);
+  else lds = attn_lds<T, DH, 1, 1>(a.trows);
+  if (lds > LDS_BYTES) return -2;
+  if (nt == 4) launch_cfg<T, DH, 2, 2>(a, grid, lds, st);
+  else if (nt == 2) launch_cfg<T, DH, 1, 2>(a, grid, lds, st);
+  else launch_cfg<T, DH, 1, 1>(a, grid, lds, st);
+  if (a.nsplit > 1) {
+    const int n = a.Q * a.H * (DH / 4);
+    hipLaunchKernelGGL((la_attn_merge_kernel<T, DH>), dim3((n + 255) / 256), dim3(256), 0, st, a);
+  }
   return 0;
 }
 
@@ -744,7 +877,8 @@ int la_attention_launch(int dtype, const LaAttnArgs& a0, hipStream_t st) {
   a.scale_log2 = a.scale * 1.4426950408889634f;
   // key splits: the split of the last chunk any row reaches, plus one
   const int last_chunk = tail ? a.tail0 + a.n_tail - 1 : a.class_last;
-  a.nsplit = last_chunk / (NCLS * SPB) + 1;
+  a.spb = la_attention_spb(a.T_cap);
+  a.nsplit = last_chunk / (NCLS * a.spb) + 1;
   if (a.nsplit > 1 && (a.part_o == nullptr || a.part_ml == nullptr || a.nsplit > a.max_splits)) return -2;
   int rc;
   if (dtype == LA_DT_BF16) {

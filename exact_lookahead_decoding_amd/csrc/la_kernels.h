@@ -65,7 +65,7 @@ struct LaAttnArgs {
   void* o;              // [Q][H][dh]
   float* part_o;        // [splits][H][Q][dh] softmax states of the key splits (several splits only)
   float* part_ml;       // [splits][H][Q][2]  (m, l) of those states
-  int max_splits;       // splits part_o / part_ml hold (la_attention_parts(max_pos))
+  int max_splits;       // splits part_o / part_ml hold (la_attention_parts(max_pos, T_cap))
   const int32_t* pos;
   const int32_t* branch;
   const int32_t* path;
@@ -80,12 +80,15 @@ struct LaAttnArgs {
   int class_last;       // last chunk taken by the class workgroups (-1: none)
   int tail0, n_tail;    // first chunk and number of chunks reaching past shared_end
   int rgroups;          // row groups per KV head
+  int wg_head;          // workgroups per KV head (all splits)
   int trows;            // staged tail rows per tile
-  int nsplit;           // key splits (1024 positions each)
+  int spb;              // ring stages (128 positions) per key split (la_attention_spb(T_cap))
+  int nsplit;           // key splits
   float scale_log2;     // scale * log2(e)
 };
 int la_attention_launch(int dtype, const LaAttnArgs& a, hipStream_t st);
-int la_attention_parts(int max_pos);   // key splits of a call whose rows reach max_pos
+int la_attention_spb(int t_cap);                 // stages per key split on a cache of t_cap rows
+int la_attention_parts(int max_pos, int t_cap);   // key splits of a call whose rows reach max_pos
 
 // model pieces
 void la_embed_launch(int dtype, const void* E, const int32_t* tok, void* x, int M, int d, hipStream_t st);

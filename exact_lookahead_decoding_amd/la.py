@@ -134,7 +134,7 @@ def load() -> C.CDLL:
         "la_last_error": ([VP], C.c_char_p),
         "la_rows_query": ([P(la_rows_desc), P(la_rows_info)], I32),
         "la_build_rows": ([P(la_rows_desc), VP, VP, VP, VP, P(la_rows_info)], I32),
-        "la_attention_workspace": ([I32, I32, I32, I32], C.c_size_t),
+        "la_attention_workspace": ([I32, I32, I32, I32, I32], C.c_size_t),
         "la_attention": ([I32, VP, VP, VP, I32, VP, VP, I32, I32, I32, I32, VP, P(la_rows_info), I32, VP, VP,
                           C.c_size_t, VP], I32),
         "la_linear_workspace": ([I32, I32, I32, I32, I32], C.c_size_t),
@@ -406,7 +406,7 @@ def la_attention(q, k_cache, v_cache, k_ws, v_ws, rows, info, shared_end, out=No
     Hkv, t_cap, _ = k_cache.shape
     ws_cap = k_ws.shape[1] if k_ws is not None else 0
     lib = load()
-    need = lib.la_attention_workspace(Q, H, dh, shared_end + info.maxp)
+    need = lib.la_attention_workspace(Q, H, dh, shared_end + info.maxp, t_cap)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     if out is None:

@@ -290,12 +290,14 @@ int la_build_rows(const la_rows_desc* desc, const int32_t* window, const int32_t
  * buffer filled by la_build_rows with its info; out: device [Q][H][dh].
  * Row i attends positions 0..pos_i: those below shared_end from the cache,
  * the others through its branch path.  workspace: device scratch of
- * la_attention_workspace(Q, H, dh, max_pos) bytes, max_pos = shared_end - 1
- * + info->maxp (the largest position a row reaches): one softmax state per
- * row, head and 1024-position key split.  Batch invariant: a row's result
- * does not depend on the other rows of the call (its reduction tree is a
- * function of key positions only). */
-size_t la_attention_workspace(int32_t Q, int32_t H, int32_t dh, int32_t max_pos);
+ * la_attention_workspace(Q, H, dh, max_pos, t_cap) bytes, max_pos =
+ * shared_end - 1 + info->maxp (the largest position a row reaches): one
+ * softmax state per row, head and key split.  A key split is a fixed run of
+ * positions whose length depends on t_cap only (about a quarter of it,
+ * rounded up to 128 positions).  Batch invariant: a row's result does not
+ * depend on the other rows of the call (its reduction tree is a function of
+ * key positions and t_cap only). */
+size_t la_attention_workspace(int32_t Q, int32_t H, int32_t dh, int32_t max_pos, int32_t t_cap);
 int la_attention(int32_t dtype, const void* q, const void* k_cache, const void* v_cache, int32_t t_cap,
                  const void* k_ws, const void* v_ws, int32_t ws_cap, int32_t H, int32_t Hkv, int32_t dh,
                  const int32_t* rows, const la_rows_info* info, int32_t shared_end, void* out, void* workspace,

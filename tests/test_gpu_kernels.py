@@ -105,7 +105,7 @@ def test_build_rows_matches_oracle(case):
             assert bit == int(comp.visible[perm[i], perm[k]]), (i, k)
 
 
-def _attn_case(sizes, starts, cands, S, p, H, Hkv, dh, dtype, seed=0):
+def _attn_case(sizes, starts, cands, S, p, H, Hkv, dh, dtype, seed=0, t_cap=None):
     """Inputs in oracle row order -> GPU placement; returns (gpu out in oracle order, oracle out)."""
     comp, b, info = _build(sizes, starts, cands, S, p=p)
     Q = comp.Q
@@ -121,7 +121,7 @@ def _attn_case(sizes, starts, cands, S, p, H, Hkv, dh, dtype, seed=0):
 
     f64 = (lambda a: synthetic.f32_from_bf16_bits(a).astype(np.float64)) if dtype == "bf16" else \
         (lambda a: a.astype(np.float64))
-    t_cap = p + 8
+    t_cap = p + 8 if t_cap is None else t_cap
     kc = np.zeros((Hkv, t_cap, dh), kp.dtype)
     vc = np.zeros((Hkv, t_cap, dh), vp.dtype)
     kc[:, :p] = kp
@@ -158,8 +158,8 @@ ATTN = [
      2e-2),
     ([3, 0], [1, 0], [], 2, 0, 4, 4, 16, "f32", 1e-5),                 # empty prefix
     ([0, 0], [1, 0], [], 2, 255, 4, 2, 64, "bf16", 2e-2),               # one ordinary row
-    # key splits (1024 positions each): a 3000-key GQA prefix (3 splits), the
-    # 8192-key long-prefix round (9 splits) and the 34B-shaped GQA round
+    # several key splits (about a quarter of the cache each): a 3000-key GQA
+    # prefix, the 8192-key long-prefix round and the 34B-shaped GQA round
     ([6, 7, 7, 7], [1, 0, 0, 0], [tuple(range(i, i + 4)) for i in range(7)], 4, 3000, 16, 4, 128, "bf16", 2e-2),
     ([15, 15, 15, 15], [1, 1, 1, 1], [tuple(range(i, i + 4)) for i in range(15)], 4, 8192, 32, 32, 128, "bf16",
      2e-2),
@@ -178,15 +178,16 @@ def test_attention_matches_oracle(case):
     assert err <= tol
 
 
-@pytest.mark.parametrize("p", [1000, 2040])
-def test_attention_batch_invariance(p):
+@pytest.mark.parametrize("p,t_cap", [(1150, 1166), (2300, 3000)])
+def test_attention_batch_invariance(p, t_cap):
     """A packed row's output equals, bit for bit, the same row computed alone
-    with its branch ancestors committed to the cache (an autoregressive call).
-    Both prefixes put the round's rows across a 1024-position key split."""
+    with its branch ancestors committed to a cache of the same capacity (an
+    autoregressive call).  Both cases put the round's rows across a key-split
+    boundary (384 positions at capacity 1166, 768 at 3000)."""
     sizes, starts = [6, 7, 7, 7], [1, 0, 0, 0]
     cands = [tuple(range(i, i + 4)) for i in range(7)]
     H, Hkv, dh = 8, 2, 128
-    got, want, ctx = _attn_case(sizes, starts, cands, 4, p, H, Hkv, dh, "bf16", seed=3)
+    got, want, ctx = _attn_case(sizes, starts, cands, 4, p, H, Hkv, dh, "bf16", seed=3, t_cap=t_cap)
     comp, b, info, perm, dev, q, kc, vc, kw, vw, out = ctx
     out_np = out.view(torch.int16).cpu().numpy()
     kn = np.zeros((comp.Q, Hkv, dh), np.uint16)
@@ -201,7 +202,6 @@ def test_attention_batch_invariance(p):
         i = perm[g_row]
         vis = sorted((j for j in range(comp.Q) if comp.visible[i, j]), key=lambda j: comp.rows[j].logical_position)
         pos = comp.rows[i].logical_position
-        t_cap = pos + 8
         kc1 = np.zeros((Hkv, t_cap, dh), np.uint16)
         vc1 = np.zeros_like(kc1)
         kc1[:, :p] = kc[:, :p]
