@@ -204,7 +204,8 @@ static void setup_dims(la_ctx* c) {
   c->parts = la_attention_parts(c->t_cap + c->maxp_max, c->t_cap);   // positions stay below t_cap + maxp
   c->rope_rows = c->t_cap + c->q_max + 1;
   c->wstride = g.W + g.N;
-  c->rows_words = 8 * c->q_max + c->nb_max * c->maxp_max + c->nb_max + c->n_logit_max + c->q_max * c->words_max;
+  c->rows_words = 8 * c->q_max + c->nb_max * c->maxp_max + c->nb_max + c->n_logit_max + c->q_max * c->words_max +
+                  (c->q_max + 15) / 16 * (64 + 16 * 64);
 }
 
 static size_t gemm_partial_floats(la_ctx* c) {
@@ -318,7 +319,8 @@ static int resid_gemm(la_ctx* c, const void* X, const void* W, int M, int K, int
 // the others to workspace rows m - n_direct.  Keys below shared_end come
 // from the cache.  Logits (fp32) of logit_rows[0..n_logit) land in c->logits.
 static int forward(la_ctx* c, int M, const int32_t* tok, const int32_t* pos, const int32_t* branch,
-                   const int32_t* path, const int32_t* path_len, int nb, int maxp, int n_direct, int cache_row0,
+                   const int32_t* path, const int32_t* path_len, const int32_t* tile_meta, const int32_t* tile_path,
+                   int nb, int maxp, int n_direct, int cache_row0,
                    int shared_end, int max_pos, const int32_t* logit_rows, int n_logit) {
   const int esz = c->esz;
   const size_t kvl = (size_t)c->Hkv * c->t_cap * c->dh;   // elements per layer
@@ -327,6 +329,7 @@ static int forward(la_ctx* c, int M, const int32_t* tok, const int32_t* pos, con
   LaAttnArgs at{};
   at.q = c->q; at.o = c->o; at.part_o = c->attn_po; at.part_ml = c->attn_pml; at.max_splits = c->parts;
   at.pos = pos; at.branch = branch; at.path = path; at.path_len = path_len;
+  at.tile_meta = tile_meta; at.tile_path = tile_path;
   at.Q = M; at.H = c->H; at.Hkv = c->Hkv; at.dh = c->dh; at.T_cap = c->t_cap; at.ws_cap = c->ws_cap; at.maxp = maxp;
   at.shared_end = shared_end;
   at.max_pos = max_pos;
@@ -388,11 +391,14 @@ static void rows_layout(const LaLayout& L, int32_t* base, LaRowsDev* r, la_rows_
   const int o_tok = take(Q), o_pos = take(Q), o_role = take(Q), o_level = take(Q), o_col = take(Q),
             o_cand = take(Q), o_off = take(Q), o_branch = take(Q), o_path = take(L.NB * L.maxp),
             o_plen = take(L.NB), o_logit = take(L.n_logit), o_mask = take(Q * L.mask_words);
+  const int ntiles = (Q + 15) / 16;
+  const int o_tmeta = take(ntiles * 64), o_tpath = take(ntiles * 16 * 64);
   if (r) {
     r->tok = base + o_tok; r->pos = base + o_pos; r->role = base + o_role; r->level = base + o_level;
     r->col = base + o_col; r->cand = base + o_cand; r->off = base + o_off; r->branch = base + o_branch;
     r->path = base + o_path; r->path_len = base + o_plen; r->logit_rows = base + o_logit;
     r->mask = (uint32_t*)(base + o_mask);
+    r->tile_meta = base + o_tmeta; r->tile_path = base + o_tpath;
   }
   if (info) {
     info->Q = Q; info->NB = L.NB; info->maxp = L.maxp; info->n_logit = L.n_logit; info->n_inp = L.n_inp;
@@ -400,6 +406,7 @@ static void rows_layout(const LaLayout& L, int32_t* base, LaRowsDev* r, la_rows_
     info->off_tok = o_tok; info->off_pos = o_pos; info->off_role = o_role; info->off_level = o_level;
     info->off_col = o_col; info->off_cand = o_cand; info->off_off = o_off; info->off_branch = o_branch;
     info->off_path = o_path; info->off_path_len = o_plen; info->off_logit_rows = o_logit; info->off_mask = o_mask;
+    info->off_tile_meta = o_tmeta; info->off_tile_path = o_tpath;
   }
 }
 
@@ -466,7 +473,8 @@ extern "C" int la_init(const la_config* cfg, const la_model_dims* dims, const la
     CK(hipMemcpyAsync(c->pf_path, zero, 4, hipMemcpyHostToDevice, c->st));
     CK(hipMemcpyAsync(c->pf_logit, zero + 1, 4, hipMemcpyHostToDevice, c->st));
     const bool last = c0 + M >= prompt_len;
-    rc = forward(c, M, c->pf_tok, c->pf_pos, c->pf_branch, c->pf_path, c->pf_path, 1, 1, M, c0, c0 + M,
+    rc = forward(c, M, c->pf_tok, c->pf_pos, c->pf_branch, c->pf_path, c->pf_path, nullptr, nullptr, 1, 1, M, c0,
+                 c0 + M,
                  c0 + M - 1, c->pf_logit, last ? 1 : 0);
     if (rc) { g_err = c->err; return bail(rc); }
     CK(hipStreamSynchronize(c->st));        // the host-side chunk arrays are reused
@@ -547,8 +555,9 @@ extern "C" int la_predict(la_ctx* c, la_round_info* info) {
   rows_layout(L, c->rowbuf, &c->rows, nullptr);
   la_build_rows_launch(L, x_t, c->win[c->cur], c->wstride, c->cand, c->rows, c->st);
   const int maxpos = p + L.maxp;             // a row's branch path covers its own position
-  int rc = forward(c, L.Q, c->rows.tok, c->rows.pos, c->rows.branch, c->rows.path, c->rows.path_len, L.NB, L.maxp,
-                   1, p, p + 1, maxpos, c->rows.logit_rows, L.n_logit);
+  int rc = forward(c, L.Q, c->rows.tok, c->rows.pos, c->rows.branch, c->rows.path, c->rows.path_len,
+                   c->rows.tile_meta, c->rows.tile_path, L.NB, L.maxp, 1, p, p + 1, maxpos, c->rows.logit_rows,
+                   L.n_logit);
   if (rc) return rc;
   c->lay = L;
   c->pending = true;
@@ -837,6 +846,7 @@ extern "C" int la_attention(int32_t dtype, const void* q, const void* k_cache, c
   a.part_ml = (float*)((char*)workspace + parts * H * info->Q * (size_t)dh * 4);
   a.pos = rows + info->off_pos; a.branch = rows + info->off_branch; a.path = rows + info->off_path;
   a.path_len = rows + info->off_path_len;
+  a.tile_meta = rows + info->off_tile_meta; a.tile_path = rows + info->off_tile_path;
   a.Q = info->Q; a.H = H; a.Hkv = Hkv; a.dh = dh; a.T_cap = t_cap; a.ws_cap = ws_cap > 0 ? ws_cap : 1;
   a.maxp = info->maxp; a.shared_end = shared_end;
   a.max_pos = max_pos; a.nb = info->NB; a.n_ws = info->Q - 1;

@@ -10,14 +10,17 @@
 // Reduction tree (a function of logical positions only, so a row gets the
 // same bits whether it is alone in an autoregressive step or packed with a
 // whole lookahead round):
-//   * keys are cut into chunks of 32 positions; chunk c belongs to class
-//     c % 4;
-//   * inside a class the chunks are taken in increasing position with the
-//     online softmax: the chunk's exact maximum gives the new running maximum
-//     m', the running sums are scaled by 2^(m - m'), p = 2^(s - m'),
+//   * keys are cut into chunks of 32 positions and the chunks into key
+//     splits of a fixed number of chunks (set by the cache capacity); chunk
+//     c belongs to class c % 4;
+//   * inside a split, a class takes its chunks in decreasing position with
+//     the online softmax: the reference maximum m' moves to the chunk's
+//     exact maximum only when that exceeds it by more than RESCALE, the
+//     running sums are scaled by 2^(m - m'), p = 2^(s - m'),
 //     l' = l * 2^(m - m') + sum p (fixed lane order), and O' = O * 2^(m - m')
 //     + V^T P^T accumulated by MFMA over a fixed key -> slot assignment;
-//   * the 4 class states are folded in class order (fold_state), then O / l.
+//   * a split's 4 class states are folded in class order, the splits' states
+//     in split order, then O / l.
 //
 // Work decomposition (gfx950, wave64; a wave owns one class of one tile of
 // 16 query rows of one q-head):
@@ -228,22 +231,6 @@ template <int NDT> __device__ __forceinline__ void scale_o(f32x4* O, float wa) {
     for (int r = 0; r < 4; ++r) O[dt][r] *= wa;
 }
 
-// Fold the class state (mb, lb, ob) into (ma, la, oa); an empty state has
-// m = -inf (an empty ma gives wa = 2^-inf = 0).
-template <int NDT>
-__device__ __forceinline__ void fold_state(float& ma, float& la, f32x4* oa, float mb, float lb, const f32x4* ob) {
-  if (mb == NEG_INF) return;
-  const float mn = fmaxf(ma, mb);
-  const float wa = ex2(ma - mn), wb = ex2(mb - mn);
-  la = lin2(la, wa, lb, wb);
-#pragma unroll
-  for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) oa[dt][r] = lin2(oa[dt][r], wa, ob[dt][r], wb);
-  ma = mn;
-}
-
-
 // One workgroup per (KV head, row group, key split); a row group is NT =
 // TP * TPW tiles of 16 query rows; wave w is class c = w / TP of tile pair
 // slot w % TP, which holds TPW tiles: the K and V fragments a wave reads
@@ -253,20 +240,23 @@ __device__ __forceinline__ void fold_state(float& ma, float& la, f32x4* oa, floa
 // split order (a split's chunks, tail chunks included, are fixed by
 // position, so the tree still depends on positions only).
 // Three phases per workgroup:
-//   1. prefix: ring stage s holds keys [128 s, 128 s + 128) of the head (the
-//      class-c chunk 4 s + c, K and V, 16-byte pieces XOR-swizzled by row) for
-//      every chunk below shared_end (or up to the largest row position when
-//      nothing reaches past it); each class wave takes its chunk of the stage
-//      with the online step, so a stage is read from HBM once for all the
-//      workgroup's tiles and classes;
-//   2. tail: the chunks reaching past shared_end (at most one per class) are
-//      applied last in their class: the ring's space is reused to stage, per
-//      tile, the committed rows [32 tail0, shared_end) and, for each branch in
-//      the tile, its workspace rows of positions shared_end .. max_pos (read
+//   1. tail (splits that hold one): the chunks reaching past shared_end (at
+//      most one per class, the highest positions of the split, so the first
+//      in their class): the ring's space is used to stage, per tile, the
+//      committed rows [32 tail0, shared_end) and, for each branch in the
+//      tile, its workspace rows of positions shared_end .. max_pos (read
 //      through the branch path); the scores come per branch and P V runs once
 //      per branch (rows of other branches add exact zeros);
-//   3. fold: classes 1..3 hand their states to class 0 through LDS, which
-//      folds 0, 1, 2, 3 in order and stores O / l (or the split's state).
+//   2. prefix: ring stage s holds keys [128 s, 128 s + 128) of the head (the
+//      class-c chunk 4 s + c, K and V, 16-byte pieces XOR-swizzled by row)
+//      for every chunk below shared_end (or up to the largest row position
+//      when nothing reaches past it), stages taken from the split's last to
+//      its first; each class wave takes its chunk of the stage with the
+//      online step, so a stage is read from HBM once for all the workgroup's
+//      tiles and classes;
+//   3. fold: every class wave hands its states over through LDS and folds,
+//      for one accumulator row of each tile, classes 0, 1, 2, 3 in order,
+//      then stores O / l (or the split's state).
 // Every global load of the ring is a DMA into LDS read back with inline asm;
 // the waits are static vmcnt counts (every wave issues the same DMA count per
 // stage).
@@ -345,6 +335,15 @@ la_attn_kernel(LaAttnArgs a) {
   }
   auto qa = [&](int u) __attribute__((always_inline)) { return lds + (pslot * TPW + u) * 16 * ROWB; };
   auto pa = [&](int u) __attribute__((always_inline)) { return lds + NT * 16 * ROWB + (pslot * TPW + u) * 256; };
+  // Chunks of a class are taken in decreasing position, so a split's tail
+  // chunks (the highest positions) come first: a workgroup with tail chunks
+  // applies them before its ring starts (the ring's space holds the tiles'
+  // branch tables and staged rows meanwhile), and the ring then walks its
+  // stages from the last to the first.
+  const int t_lo = max(a.tail0, sp * a.spb * NCLS), t_hi = min(a.tail0 + a.n_tail, (sp + 1) * a.spb * NCLS);
+  const bool has_tail = t_lo < t_hi;              // split_has_tail(a, sp): uniform over the workgroup
+  int* const spath0 = (int*)ring;                 // tail: [NT][16 branches][64 positions] workspace rows
+  int* const meta0 = (int*)(ring + NT * 16 * 64 * 4);   // tail: [NT][64] branch count, branch ids
   if (cls == 0) {
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
@@ -357,12 +356,21 @@ la_attn_kernel(LaAttnArgs a) {
         const char* src = (const char*)a.q + ((size_t)r * a.H + hh[u]) * ROWB + 16 * (lane % PIECES);
         __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(qa(u) + j * 1024), 16, 0, 0);
       }
+      if (has_tail && tv[u]) {                    // the tile's branch tables (row builder)
+        const int rt = row0 >> 4;
+        __builtin_amdgcn_global_load_lds((const void*)(a.tile_meta + (size_t)rt * 64 + lane),
+                                         (lds_void_t*)(meta0 + (pslot * TPW + u) * 64), 4, 0, 0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          __builtin_amdgcn_global_load_lds((const void*)(a.tile_path + (size_t)rt * 1024 + j * 256 + 4 * lane),
+                                           (lds_void_t*)(spath0 + (pslot * TPW + u) * 1024 + j * 256), 16, 0, 0);
+      }
     }
   }
 
-  // ring stage s: chunks 4 s .. 4 s + 3; past the last stage every lane loads
-  // one 16-byte piece (a dummy that nobody reads), so every wave issues CW
-  // DMA instructions per stage on every path
+  // ring stage s: chunks 4 s .. 4 s + 3; outside the split's stages every
+  // lane loads one 16-byte piece (a dummy that nobody reads), so every wave
+  // issues CW DMA instructions per stage on every path
   const int nblk = (a.class_last + NCLS) / NCLS;   // stages of the whole prefix (class_last = -1: none)
   const int s_begin = sp * a.spb;                     // this split's stages
   const int s_end = min(s_begin + a.spb, nblk);
@@ -388,14 +396,15 @@ la_attn_kernel(LaAttnArgs a) {
   }
   auto issue = [&](char* stage, int s) __attribute__((always_inline)) {
     const int x0 = CH * (NCLS * s + cw);
-    if (s < s_end && x0 + CH <= se) {           // the whole chunk lies below shared_end
+    const bool in = s >= s_begin && s < s_end;
+    if (in && x0 + CH <= se) {                  // the whole chunk lies below shared_end
 #pragma unroll
       for (int j = 0; j < CW; ++j) {
         const char* base = kv_of(j);
         __builtin_amdgcn_global_load_lds((const void*)(base + (size_t)x0 * ROWB + oj[j]),
                                          (lds_void_t*)(stage + (b0 + j) * 1024), 16, 0, 0);
       }
-    } else if (s < s_end) {                     // rows past shared_end - 1 repeat it (never visible)
+    } else if (in) {                            // rows past shared_end - 1 repeat it (never visible)
 #pragma unroll
       for (int j = 0; j < CW; ++j) {
         const char* base = kv_of(j);
@@ -404,20 +413,24 @@ la_attn_kernel(LaAttnArgs a) {
         __builtin_amdgcn_global_load_lds((const void*)(base + (size_t)min(x0 + r, se - 1) * ROWB + off),
                                          (lds_void_t*)(stage + (b0 + j) * 1024), 16, 0, 0);
       }
-    } else {                                    // past the last stage: one valid 16-byte piece
+    } else {                                    // outside the split: one valid 16-byte piece
 #pragma unroll
       for (int j = 0; j < CW; ++j)
         __builtin_amdgcn_global_load_lds((const void*)(kc + (size_t)(se - 1) * ROWB),
                                          (lds_void_t*)(stage + (b0 + j) * 1024), 16, 0, 0);
     }
   };
-  // the rows' branches (read now, used by the tail phase after the ring)
+  // the rows' branches (read now, used by the tail phase)
   int br[TPW];
 #pragma unroll
   for (int u = 0; u < TPW; ++u) br[u] = (a.n_tail > 0 && rvalid[u]) ? a.branch[row[u]] : -1;
+  if (!has_tail) {
 #pragma unroll
-  for (int k = 0; k < DEPTH; ++k) issue(ring + k * BLKB, s_begin + k);
-  wait_vm<(CW * DEPTH < 63 ? CW * DEPTH : 63)>();   // this wave's Q and positions (issued first) have landed
+    for (int k = 0; k < DEPTH; ++k) issue(ring + k * BLKB, s_end - 1 - k);
+    wait_vm<(CW * DEPTH < 63 ? CW * DEPTH : 63)>();   // this wave's Q, positions and branches (issued first) have landed
+  } else {
+    wait_vm<0>();
+  }
   ring_barrier();                                    // ... and those of the other waves
   QF qf[TPW];
   int pos[TPW], pmin[TPW];
@@ -442,6 +455,181 @@ la_attn_kernel(LaAttnArgs a) {
     pmin[u] = __builtin_amdgcn_readfirstlane(pm);
   }
 
+  float M[TPW], L[TPW];
+  f32x4 O[TPW][NDT];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    M[u] = NEG_INF;
+    L[u] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) O[u][dt] = f32x4{0, 0, 0, 0};
+  }
+
+  if (has_tail) {
+    const int X0 = CH * a.tail0;
+    const int ncom = se - X0;                       // 0 .. 31
+    const int EP = a.max_pos - se + 1;              // 1 .. 64
+    // staged rows of each tile pair slot, after the branch tables
+    char* const ks = ring + NT * (16 * 64 + 64) * 4 + pslot * 2 * a.trows * ROWB;
+    char* const vs = ks + a.trows * ROWB;
+    // the tiles' distinct branches (lane i < nbr: branch i)
+    int nbr[TPW], bl[TPW];
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const int* mt = meta0 + (pslot * TPW + u) * 64;
+      nbr[u] = tv[u] ? min(mt[0], 16) : 0;
+      bl[u] = (tv[u] && lane < 16) ? mt[1 + lane] : -1;
+    }
+    // branches staged at once per tile (the committed rows, then EP rows per
+    // branch), and the batches every tile of the workgroup goes through
+    const int bb = (a.trows - ncom) / EP;           // >= 1 (the launcher sizes trows)
+    int* const nbat = (int*)(lds + NT * 16 * ROWB);   // the row positions' space, free since they were read
+    if (cls == 0 && lane == 0) {
+#pragma unroll
+      for (int u = 0; u < TPW; ++u) nbat[pslot * TPW + u] = (nbr[u] + bb - 1) / bb;
+    }
+    __syncthreads();
+    int nbatch = 0;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) nbatch = max(nbatch, nbat[t]);
+    const char* kw = (const char*)a.kw + (size_t)g_kv * a.ws_cap * ROWB;
+    const char* vw = (const char*)a.vw + (size_t)g_kv * a.ws_cap * ROWB;
+    const int tau = (cls - a.tail0 % NCLS + NCLS) % NCLS;   // the class's tail chunk (at most one)
+    const bool mine_chunk = tau < a.n_tail && a.tail0 + tau >= t_lo && a.tail0 + tau < t_hi;
+    // With a single tail chunk in the split its branches are spread over the
+    // four class waves (wave c takes the batch branches i with i % 4 == c);
+    // every wave starts from the empty state (the tail comes first), and the
+    // chunk's class wave then collects each row's state from the wave that
+    // handled the row's branch, through the staging space.
+    constexpr int SF = 2 + 4 * NDT;                 // floats of one lane's state
+    const bool spread = t_hi - t_lo == 1 && 2 * a.trows * ROWB >= NCLS * SF * 64 * 4;
+    const int cstar = t_lo % NCLS;
+    const int x0 = CH * (spread ? t_lo : a.tail0 + tau);
+    const bool work = spread || mine_chunk;
+    auto srow = [&](int x, int bi) -> int {
+      if (x < se) return x - X0;
+      const int e = x - se;
+      return e < EP ? ncom + bi * EP + e : 0;
+    };
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      if (hf >= 0 && u > 0) break;                // one tile per pair slot (uniform over the workgroup)
+      const int* const spath = spath0 + (pslot * TPW + u) * 1024;
+      const bool need = work && rvalid[u] && pos[u] >= x0;
+      bool own = false;                           // a branch this wave handled holds the lane's row
+      for (int bt = 0; bt < nbatch; ++bt) {
+        const int i0 = bt * bb;
+        const int nb = max(0, min(bb, nbr[u] - i0));
+        // staged row of key x on batch branch bi (x >= X0); a clamped committed
+        // row where a position is not on the branch's path (never visible to it)
+        const int nr = nb > 0 ? ncom + nb * EP : 0;
+        for (int blk = cls; blk * RPB < nr; blk += NCLS) {
+          const int j = blk * RPB + lane / PIECES;
+          const int piece = (lane % PIECES) ^ (j % PIECES);
+          int crow = se - 1, wrow = -1;
+          if (j < ncom) crow = X0 + j;
+          else if (j < nr) {
+            wrow = spath[(i0 + (j - ncom) / EP) * 64 + (j - ncom) % EP];
+            if ((unsigned)wrow >= (unsigned)a.n_ws) wrow = -1;
+          }
+          const size_t off = (size_t)(wrow >= 0 ? wrow : crow) * ROWB + 16 * piece;
+          __builtin_amdgcn_global_load_lds((const void*)((wrow >= 0 ? kw : kc) + off), (lds_void_t*)(ks + blk * 1024),
+                                           16, 0, 0);
+          __builtin_amdgcn_global_load_lds((const void*)((wrow >= 0 ? vw : vc) + off), (lds_void_t*)(vs + blk * 1024),
+                                           16, 0, 0);
+        }
+        wait_vm<0>();
+        __syncthreads();
+        // rows of this batch's branches: the chunk's online step (for the
+        // wave's other rows every score stays -inf, which leaves their state
+        // exactly as it is, and P V adds exact zeros)
+        if (nb > 0 && __ballot(need) != 0ull) {
+          float sc[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sc[e] = NEG_INF;
+          for (int bi = 0; bi < nb; ++bi) {
+            if (spread && (i0 + bi) % NCLS != cls) continue;
+            const int b = __shfl(bl[u], i0 + bi, 64);
+            const bool mine = need && br[u] == b;
+            own |= mine;
+            if (__ballot(mine) == 0ull) continue;
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+              const int r = srow(x0 + 16 * jj + c16, bi);
+              QF kf;
+#pragma unroll
+              for (int q = 0; q < LP; ++q)
+                kf.p[q] = *(const u32x4*)(ks + r * ROWB + 16 * ((LP * g + q) ^ (r % PIECES)));
+              const f32x4 s4 = AT::qk(kf, qf[u]);
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const float v = (x0 + 16 * jj + 4 * g + q <= pos[u]) ? s4[q] : NEG_INF;
+                sc[4 * jj + q] = mine ? v : sc[4 * jj + q];
+              }
+            }
+          }
+          const float wa = chunk_softmax(sc, sl2, M[u], L[u]);
+          scale_o<NDT>(O[u], wa);
+          for (int bi = 0; bi < nb; ++bi) {
+            if (spread && (i0 + bi) % NCLS != cls) continue;
+            const int b = __shfl(bl[u], i0 + bi, 64);
+            const bool mine = need && br[u] == b;
+            if (__ballot(mine) == 0ull) continue;
+            VV vv[8];
+            float ps[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int r = srow(x0 + slot_key(g, e), bi);
+              const int off = VB * c16;
+              vv[e] = *(const VV*)(vs + r * ROWB + 16 * ((off / 16) ^ (r % PIECES)) + off % 16);
+              ps[e] = mine ? sc[e] : 0.f;
+            }
+            const typename AT::PP pp = AT::prep(ps);
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) O[u][dt] = AT::pv(dt, vv, pp, O[u][dt]);
+          }
+        }
+        __syncthreads();                          // the staged rows are no longer read
+      }
+      if (spread) {
+        float* const sl = (float*)ks;             // [NCLS][SF][64] lane states, in the staging space
+        unsigned long long* const om = (unsigned long long*)(lds + NT * 16 * ROWB + 64) + pslot * NCLS;
+        const unsigned long long ownm = __ballot(own);
+        float* const my = sl + (size_t)cls * SF * 64;
+        my[lane] = M[u];
+        my[64 + lane] = L[u];
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) my[(2 + 4 * dt + r) * 64 + lane] = O[u][dt][r];
+        if (lane == 0) om[cls] = ownm;
+        __syncthreads();
+        if (cls == cstar) {
+#pragma unroll
+          for (int w = 0; w < NCLS; ++w) {
+            if (w == cls || ((om[w] >> lane) & 1ull) == 0ull) continue;
+            const float* src = sl + (size_t)w * SF * 64;
+            M[u] = src[lane];
+            L[u] = src[64 + lane];
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) O[u][dt][r] = src[(2 + 4 * dt + r) * 64 + lane];
+          }
+        } else {                                  // this class has no chunk in the tail
+          M[u] = NEG_INF;
+          L[u] = 0.f;
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) O[u][dt] = f32x4{0, 0, 0, 0};
+        }
+        __syncthreads();                          // the states are no longer read
+      }
+    }
+    // the tail is done with the ring's space: the ring starts
+#pragma unroll
+    for (int k = 0; k < DEPTH; ++k) issue(ring + k * BLKB, s_end - 1 - k);
+  }
+
   // lane parts of the fragment addresses of the class's chunk (stage offsets are immediates)
   uint32_t koff[LP], voff[4];
 #pragma unroll
@@ -454,16 +642,6 @@ la_attn_kernel(LaAttnArgs a) {
     voff[e] = lds_addr(ring + cls * 2 * CHB + CHB + kk * ROWB + 16 * ((off / 16) ^ (kk % PIECES)) + off % 16);
   }
 
-  float M[TPW], L[TPW];
-  f32x4 O[TPW][NDT];
-#pragma unroll
-  for (int u = 0; u < TPW; ++u) {
-    M[u] = NEG_INF;
-    L[u] = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) O[u][dt] = f32x4{0, 0, 0, 0};
-  }
-
   auto step = [&](auto SI, int s) __attribute__((always_inline)) {
     constexpr int S = decltype(SI)::value;
     constexpr int SB = S * BLKB;                // stage base
@@ -471,7 +649,7 @@ la_attn_kernel(LaAttnArgs a) {
     wait_vm<CW * (DEPTH - 1)>();                // stage s landed (the next one may be in flight)
     ring_barrier();
     const int k = NCLS * s + cls;               // the class's chunk
-    const bool live = s < s_end && k <= a.class_last;
+    const bool live = k <= a.class_last;
     // the chunk's K and V go to registers first, so the stage is released
     // (and the stage two steps ahead issued) before any arithmetic
     typename LdsT<16>::T kraw[2 * LP];
@@ -491,7 +669,7 @@ la_attn_kernel(LaAttnArgs a) {
       lds_wait(vraw);
     }
     ring_barrier();                             // every wave has read the stage
-    issue(ring + SB, s + DEPTH);
+    issue(ring + SB, s - DEPTH);
     if (live) {
       const int x0 = CH * k;
       float sc[TPW][8];
@@ -532,230 +710,73 @@ la_attn_kernel(LaAttnArgs a) {
       }
     }
   };
-  for (int s0 = s_begin; s0 < s_end; s0 += DEPTH)
+  for (int s0 = s_end - 1; s0 >= s_begin; s0 -= DEPTH)
     static_for<0, DEPTH>([&](auto SI) {
-      if (decltype(SI)::value == 0 || s0 + decltype(SI)::value < s_end) step(SI, s0 + decltype(SI)::value);
+      if (decltype(SI)::value == 0 || s0 - decltype(SI)::value >= s_begin) step(SI, s0 - decltype(SI)::value);
     });
 
   wait_vm<0>();                                   // the dummy stages have landed: the ring is free
   ring_barrier();
 
-  // tail chunks of this split (a chunk belongs to the split of its position)
-  const int t_lo = max(a.tail0, sp * a.spb * NCLS), t_hi = min(a.tail0 + a.n_tail, (sp + 1) * a.spb * NCLS);
-  if (t_lo < t_hi) {   // split_has_tail(a, sp)
-    const int X0 = CH * a.tail0;
-    const int ncom = se - X0;                       // 0 .. 31
-    const int EP = a.max_pos - se + 1;              // 1 .. 64
-    // tail LDS: the tiles' branch paths, then the staged rows of each tile pair slot
-    int* const spath0 = (int*)ring;                 // [NT][16 branches][64 positions]
-    char* const ks = ring + NT * 16 * 64 * 4 + pslot * 2 * a.trows * ROWB;
-    char* const vs = ks + a.trows * ROWB;
-    // the tiles' branches that reach a tail chunk (at most 16 each); every
-    // class wave of a tile finds the same list (lane i < nbr: branch i)
-    int nbr[TPW], bl[TPW];
-#pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-      const bool need0 = rvalid[u] && pos[u] >= X0;
-      nbr[u] = 0;
-      bl[u] = -1;
-      unsigned long long pend = __ballot(need0 && g == 0);
-      while (pend) {
-        const int b = __builtin_amdgcn_readfirstlane(__shfl(br[u], __ffsll((long long)pend) - 1, 64));
-        pend &= ~__ballot(need0 && g == 0 && br[u] == b);
-        if (lane == nbr[u]) bl[u] = b;
-        ++nbr[u];
-      }
-    }
-    // the tiles' branch paths: spath[i][e] = workspace row of position se + e
-    // on branch i (-1 when the position is not on it); class 0 writes them,
-    // every load issued before any is used
-    if (cls == 0) {
-#pragma unroll
-      for (int u = 0; u < TPW; ++u) {
-        int* const spath = spath0 + (pslot * TPW + u) * 1024;
-        const int plen = lane < nbr[u] ? min(a.path_len[bl[u]], a.maxp) : 0;
-        int wv[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int b = __shfl(bl[u], i, 64), pl = __shfl(plen, i, 64);
-          wv[i] = (i < nbr[u] && lane < pl) ? a.path[(size_t)b * a.maxp + lane] : -1;
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (i < nbr[u]) spath[i * 64 + lane] = (unsigned)wv[i] < (unsigned)a.n_ws ? wv[i] : -1;
-      }
-    }
-    // branches staged at once per tile (the committed rows, then EP rows per
-    // branch), and the batches every tile of the workgroup goes through
-    const int bb = (a.trows - ncom) / EP;           // >= 1 (the launcher sizes trows)
-    int* const nbat = (int*)(lds + NT * 16 * ROWB);   // the row positions' space, free since the prologue
-    if (cls == 0 && lane == 0) {
-#pragma unroll
-      for (int u = 0; u < TPW; ++u) nbat[pslot * TPW + u] = (nbr[u] + bb - 1) / bb;
-    }
-    __syncthreads();
-    int nbatch = 0;
-#pragma unroll
-    for (int t = 0; t < NT; ++t) nbatch = max(nbatch, nbat[t]);
-    const char* kw = (const char*)a.kw + (size_t)g_kv * a.ws_cap * ROWB;
-    const char* vw = (const char*)a.vw + (size_t)g_kv * a.ws_cap * ROWB;
-    const int tau = (cls - a.tail0 % NCLS + NCLS) % NCLS;   // the class's tail chunk (at most one)
-    const int x0 = CH * (a.tail0 + tau);
-    const bool mine_chunk = tau < a.n_tail && a.tail0 + tau >= t_lo && a.tail0 + tau < t_hi;
-    auto srow = [&](int x, int bi) -> int {
-      if (x < se) return x - X0;
-      const int e = x - se;
-      return e < EP ? ncom + bi * EP + e : 0;
-    };
-#pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-      const int* const spath = spath0 + (pslot * TPW + u) * 1024;
-      const bool need = mine_chunk && rvalid[u] && pos[u] >= x0;
-      for (int bt = 0; bt < nbatch; ++bt) {
-        const int i0 = bt * bb;
-        const int nb = max(0, min(bb, nbr[u] - i0));
-        // staged row of key x on batch branch bi (x >= X0); a clamped committed
-        // row where a position is not on the branch's path (never visible to it)
-        const int nr = nb > 0 ? ncom + nb * EP : 0;
-        for (int blk = cls; blk * RPB < nr; blk += NCLS) {
-          const int j = blk * RPB + lane / PIECES;
-          const int piece = (lane % PIECES) ^ (j % PIECES);
-          int crow = se - 1, wrow = -1;
-          if (j < ncom) crow = X0 + j;
-          else if (j < nr) wrow = spath[(i0 + (j - ncom) / EP) * 64 + (j - ncom) % EP];
-          const size_t off = (size_t)(wrow >= 0 ? wrow : crow) * ROWB + 16 * piece;
-          __builtin_amdgcn_global_load_lds((const void*)((wrow >= 0 ? kw : kc) + off), (lds_void_t*)(ks + blk * 1024),
-                                           16, 0, 0);
-          __builtin_amdgcn_global_load_lds((const void*)((wrow >= 0 ? vw : vc) + off), (lds_void_t*)(vs + blk * 1024),
-                                           16, 0, 0);
-        }
-        wait_vm<0>();
-        __syncthreads();
-        // rows of this batch's branches: the chunk's online step (for the
-        // wave's other rows every score stays -inf, which leaves their state
-        // exactly as it is, and P V adds exact zeros)
-        if (nb > 0 && __ballot(need) != 0ull) {
-          float sc[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) sc[e] = NEG_INF;
-          for (int bi = 0; bi < nb; ++bi) {
-            const int b = __shfl(bl[u], i0 + bi, 64);
-            const bool mine = need && br[u] == b;
-            if (__ballot(mine) == 0ull) continue;
-#pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-              const int r = srow(x0 + 16 * jj + c16, bi);
-              QF kf;
-#pragma unroll
-              for (int q = 0; q < LP; ++q)
-                kf.p[q] = *(const u32x4*)(ks + r * ROWB + 16 * ((LP * g + q) ^ (r % PIECES)));
-              const f32x4 s4 = AT::qk(kf, qf[u]);
-#pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                const float v = (x0 + 16 * jj + 4 * g + q <= pos[u]) ? s4[q] : NEG_INF;
-                sc[4 * jj + q] = mine ? v : sc[4 * jj + q];
-              }
-            }
-          }
-          const float wa = chunk_softmax(sc, sl2, M[u], L[u]);
-          scale_o<NDT>(O[u], wa);
-          for (int bi = 0; bi < nb; ++bi) {
-            const int b = __shfl(bl[u], i0 + bi, 64);
-            const bool mine = need && br[u] == b;
-            if (__ballot(mine) == 0ull) continue;
-            VV vv[8];
-            float ps[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int r = srow(x0 + slot_key(g, e), bi);
-              const int off = VB * c16;
-              vv[e] = *(const VV*)(vs + r * ROWB + 16 * ((off / 16) ^ (r % PIECES)) + off % 16);
-              ps[e] = mine ? sc[e] : 0.f;
-            }
-            const typename AT::PP pp = AT::prep(ps);
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) O[u][dt] = AT::pv(dt, vv, pp, O[u][dt]);
-          }
-        }
-        __syncthreads();                          // the staged rows are no longer read
-      }
-    }
-  }
-
-  // fold: classes 1..3 hand (m, l, O) over (lane for lane: same row, same
-  // head dimensions), class 0 folds 0, 1, 2, 3 in order
-  constexpr int FS = 64 * (4 * NDT + 2);          // floats of one wave's state
+  // fold: every class wave hands (m, l, O) over through LDS; class wave c
+  // then folds accumulator row c (head dimensions NDT*(4g + c) + dt, NDT
+  // contiguous values) of every tile of its pair slot, classes 0, 1, 2, 3 in
+  // order, and stores them
+  constexpr int FS = 64 * (2 + 4 * NDT);          // floats of one wave's state: (m, l) per lane, then O by row
   auto xf = [&](int u, int c) __attribute__((always_inline)) {
-    return (float*)ring + (size_t)((pslot * TPW + u) * (NCLS - 1) + (c - 1)) * FS + lane * (4 * NDT + 2);
+    return (float*)ring + (size_t)((pslot * TPW + u) * NCLS + c) * FS;
   };
-  if (cls > 0) {
 #pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-      float* d = xf(u, cls);
-      d[0] = M[u];
-      d[1] = L[u];
+  for (int u = 0; u < TPW; ++u) {
+    if (!tv[u]) continue;
+    float* d = xf(u, cls);
+    *(float2*)(d + 2 * lane) = make_float2(M[u], L[u]);
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
+    for (int r = 0; r < 4; ++r) {
+      float* dr = d + 128 + (r * 64 + lane) * NDT;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) d[2 + 4 * dt + r] = O[u][dt][r];
+      for (int dt = 0; dt < NDT; ++dt) dr[dt] = O[u][dt][r];
     }
   }
   __syncthreads();
-  if (cls != 0) return;
 #pragma unroll
   for (int u = 0; u < TPW; ++u) {
-    if (!rvalid[u]) continue;
+    if (!tv[u] || !rvalid[u]) continue;
     float Mf = NEG_INF, Lf = 0.f;
-    f32x4 Of[NDT];
+    float Of[NDT];
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) Of[dt] = f32x4{0, 0, 0, 0};
-    fold_state<NDT>(Mf, Lf, Of, M[u], L[u], O[u]);
+    for (int dt = 0; dt < NDT; ++dt) Of[dt] = 0.f;
 #pragma unroll
-    for (int c = 1; c < NCLS; ++c) {
+    for (int c = 0; c < NCLS; ++c) {
       const float* d = xf(u, c);
-      f32x4 Oc[NDT];
+      const float2 ml = *(const float2*)(d + 2 * lane);
+      if (ml.x == NEG_INF) continue;
+      const float* dr = d + 128 + (cls * 64 + lane) * NDT;
+      const float mn = fmaxf(Mf, ml.x);
+      const float wa = ex2(Mf - mn), wb = ex2(ml.x - mn);
+      Lf = lin2(Lf, wa, ml.y, wb);
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) Oc[dt][r] = d[2 + 4 * dt + r];
-      fold_state<NDT>(Mf, Lf, Of, d[0], d[1], Oc);
+      for (int dt = 0; dt < NDT; ++dt) Of[dt] = lin2(Of[dt], wa, dr[dt], wb);
+      Mf = mn;
     }
+    const int d0 = NDT * (4 * g + cls);             // first of the NDT contiguous head dimensions
     if (a.nsplit > 1) {
-      // the split's state: (m, l) and O, lane dims NDT*(4g + r) + dt (4*NDT contiguous floats)
+      // the split's state: (m, l) and O in natural dimension order
       const size_t base = ((size_t)sp * a.H + hh[u]) * a.Q + row[u];
-      if (g == 0) *(float2*)(a.part_ml + base * 2) = make_float2(Mf, Lf);
-      float4* po = (float4*)(a.part_o + base * DH + 4 * NDT * g);
+      if (g == 0 && cls == 0) *(float2*)(a.part_ml + base * 2) = make_float2(Mf, Lf);
+      float* po = a.part_o + base * DH + d0;
 #pragma unroll
-      for (int q = 0; q < NDT; ++q) {
-        const int i0 = 4 * q;
-        po[q] = make_float4(Of[(i0 + 0) % NDT][(i0 + 0) / NDT], Of[(i0 + 1) % NDT][(i0 + 1) / NDT],
-                            Of[(i0 + 2) % NDT][(i0 + 2) / NDT], Of[(i0 + 3) % NDT][(i0 + 3) / NDT]);
-      }
+      for (int dt = 0; dt < NDT; ++dt) po[dt] = Of[dt];
       continue;
     }
-    // lane holds head dimensions NDT*(4g + r) + dt: 4*NDT contiguous values,
-    // stored as 16-byte pieces
-    constexpr int EPW = 4 / sizeof(T);            // elements per 32-bit word
-    uint32_t ow[4 * NDT / EPW];
+    T* dst = (T*)a.o + ((size_t)row[u] * a.H + hh[u]) * DH + d0;
 #pragma unroll
-    for (int w = 0; w < 4 * NDT / EPW; ++w) {
-      uint32_t v = 0;
-#pragma unroll
-      for (int q = 0; q < EPW; ++q) {
-        const int i = w * EPW + q, r = i / NDT, dt = i % NDT;
-        const float x = Of[dt][r] / Lf;
-        v |= (sizeof(T) == 2 ? (uint32_t)f2bf(x) : __float_as_uint(x)) << (16 * q);
-      }
-      ow[w] = v;
-    }
-    u32x4* dst = (u32x4*)((T*)a.o + ((size_t)row[u] * a.H + hh[u]) * DH + 4 * NDT * g);
-#pragma unroll
-    for (int q = 0; q < 4 * NDT / EPW / 4; ++q) dst[q] = u32x4{ow[4 * q], ow[4 * q + 1], ow[4 * q + 2], ow[4 * q + 3]};
+    for (int dt = 0; dt < NDT; ++dt) st<T>(dst + dt, Of[dt] / Lf);
   }
 }
 
 // Fold of the key splits' states in split order (the same sequence of
-// roundings as fold_state), then O / l.  One thread per 4 head dimensions of
+// roundings as the class fold), then O / l.  One thread per 4 head dimensions of
 // a (row, head).
 template <typename T, int DH>
 __global__ void __launch_bounds__(256) la_attn_merge_kernel(LaAttnArgs a) {
@@ -804,8 +825,8 @@ static size_t attn_lds(int trows) {
   constexpr int ROWB = AttnT<T, DH>::ROWB, NDT = AttnT<T, DH>::NDT, NT = TP * TPW;
   const size_t fix = ((size_t)NT * (16 * ROWB + 256) + 1023) & ~(size_t)1023;
   const size_t ring = (size_t)2 * NCLS * 2 * CH * ROWB;
-  const size_t tail = (size_t)NT * 16 * 64 * 4 + (size_t)TP * 2 * trows * ROWB;
-  const size_t fold = (size_t)NT * (NCLS - 1) * 64 * (4 * NDT + 2) * 4;
+  const size_t tail = (size_t)NT * (16 * 64 + 64) * 4 + (size_t)TP * 2 * trows * ROWB;
+  const size_t fold = (size_t)NT * NCLS * 64 * (4 * NDT + 2) * 4;
   return fix + std::max(ring, std::max(tail, fold));
 }
 
@@ -829,7 +850,7 @@ static int launch_dh(LaAttnArgs a, hipStream_t st) {
   const int EP = a.n_tail > 0 ? a.max_pos - a.shared_end + 1 : 0;
   auto rows_for = [&](int tp, int nt) {
     const size_t fix = (((size_t)nt * (16 * ROWB + 256)) + 1023) & ~(size_t)1023;
-    const size_t paths = (size_t)nt * 16 * 64 * 4;
+    const size_t paths = (size_t)nt * (16 * 64 + 64) * 4;
     const int fit = (int)((LDS_BYTES - fix - paths) / ((size_t)tp * 2 * ROWB)) / RPB * RPB;
     const int want = ((CH - 1 + 16 * EP) + RPB - 1) / RPB * RPB;
     return std::min(fit, want);

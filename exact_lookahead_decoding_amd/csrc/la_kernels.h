@@ -41,6 +41,8 @@ struct LaRowsDev {
   int32_t* path_len;   // [NB]
   int32_t* logit_rows; // [n_logit]: out, inp (column order), guess ((c, s) order)
   uint32_t* mask;      // [Q][mask_words] visibility bits among current rows
+  int32_t* tile_meta;  // [ceil(Q/16)][64]: distinct branches of each 16-row tile (count, then ids)
+  int32_t* tile_path;  // [ceil(Q/16)][16][64]: their paths (-1: none)
 };
 
 struct LaLayout {        // host-side description of one round's rows
@@ -70,6 +72,8 @@ struct LaAttnArgs {
   const int32_t* branch;
   const int32_t* path;
   const int32_t* path_len;
+  const int32_t* tile_meta;   // per 16-row tile: branch count and ids (row builder)
+  const int32_t* tile_path;   // per 16-row tile: [16][64] workspace rows of positions shared_end + k
   int Q, H, Hkv, dh, T_cap, ws_cap, maxp;
   int shared_end;       // keys [0, shared_end) come from the cache, later ones from the row's path
   int max_pos;          // largest row position (an upper bound is fine)

@@ -161,6 +161,34 @@ __global__ void __launch_bounds__(256) build_rows_kernel(LaLayout L, int x_t, co
     }
     o.mask[(size_t)i * nw + w] = bits;
   }
+  // per 16-row tile: its distinct branches in row order (rows are branch
+  // major, so a tile holds a few consecutive runs) and their paths, which
+  // the attention kernel stages for the keys past the committed prefix
+  const int ntiles = (L.Q + 15) / 16;
+  for (int tt = t; tt < ntiles; tt += blockDim.x) {
+    int32_t* meta = o.tile_meta + (size_t)tt * 64;
+    int nb = 0;
+    for (int i = 16 * tt; i < 16 * tt + 16 && i < L.Q; ++i) {
+      const int b = o.branch[i];
+      bool seen = false;
+      for (int k = 0; k < nb; ++k) seen |= meta[1 + k] == b;
+      if (!seen) meta[1 + nb++] = b;
+    }
+    meta[0] = nb;
+    for (int k = 1 + nb; k < 64; ++k) meta[k] = -1;
+  }
+  __syncthreads();
+  for (int idx = t; idx < ntiles * 1024; idx += blockDim.x) {
+    const int tt = idx / 1024, i = (idx / 64) % 16, e = idx % 64;
+    const int32_t* meta = o.tile_meta + (size_t)tt * 64;
+    int v = -1;
+    if (i < meta[0]) {
+      const int b = meta[1 + i];
+      if (e < o.path_len[b] && e < L.maxp) v = o.path[(size_t)b * L.maxp + e];
+      if (v < 0 || v >= L.Q - 1) v = -1;
+    }
+    o.tile_path[idx] = v;
+  }
 }
 
 void la_build_rows_launch(const LaLayout& L, int x_t, const int32_t* win, int win_stride, const int32_t* cands,

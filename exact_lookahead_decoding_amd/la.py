@@ -91,7 +91,7 @@ class la_rows_info(C.Structure):
     _fields_ = [(n, C.c_int32) for n in (
         "Q", "NB", "maxp", "n_logit", "n_inp", "n_cols", "mask_words", "total_words",
         "off_tok", "off_pos", "off_role", "off_level", "off_col", "off_cand", "off_off", "off_branch",
-        "off_path", "off_path_len", "off_logit_rows", "off_mask")]
+        "off_path", "off_path_len", "off_logit_rows", "off_mask", "off_tile_meta", "off_tile_path")]
 
 
 EXPORTS = ["la_query_sizes", "la_init", "la_destroy", "la_step", "la_generate", "la_predict", "la_verify",

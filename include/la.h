@@ -259,9 +259,16 @@ const char* la_last_error(const la_ctx* ctx);
  * out (device int32) receives, at the offsets reported in info:
  *   tok[Q] pos[Q] role[Q] (0 ordinary, 1 lookahead, 2 verify) level[Q]
  *   col[Q] cand[Q] off[Q] branch[Q] path[NB][maxp] path_len[NB]
- *   logit_rows[n_logit] mask[Q][mask_words] (bit k of row i: i sees k).
+ *   logit_rows[n_logit] mask[Q][mask_words] (bit k of row i: i sees k)
+ *   tile_meta[T][64] tile_path[T][16][64]   (T = ceil(Q / 16) row tiles).
  * path[b][k] is the packed row (minus one) holding logical position
- * p + 1 + k on branch b.  window: device [R][win_stride] tokens; cand:
+ * p + 1 + k on branch b.  For the row tile t (packed rows 16t .. 16t+15),
+ * tile_meta[t][0] is the number n of distinct branches among its rows and
+ * tile_meta[t][1 + i] (i < n) the i-th of them in row order (-1 after);
+ * tile_path[t][i][k] is path[tile_meta[t][1 + i]][k] where k is below that
+ * branch's path length and the value names a packed row other than the
+ * ordinary one, else -1.  The attention kernel reads these per-tile tables
+ * for the keys past the committed prefix.  window: device [R][win_stride] tokens; cand:
  * device [C][S].  la_rows_query fills info without launching anything. */
 typedef struct la_rows_desc {
   int32_t p;                /* logical position of the ordinary row */
@@ -276,7 +283,7 @@ typedef struct la_rows_desc {
 typedef struct la_rows_info {
   int32_t Q, NB, maxp, n_logit, n_inp, n_cols, mask_words, total_words;
   int32_t off_tok, off_pos, off_role, off_level, off_col, off_cand, off_off, off_branch;
-  int32_t off_path, off_path_len, off_logit_rows, off_mask;
+  int32_t off_path, off_path_len, off_logit_rows, off_mask, off_tile_meta, off_tile_path;
 } la_rows_info;
 
 int la_rows_query(const la_rows_desc* desc, la_rows_info* info);

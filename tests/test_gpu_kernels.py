@@ -103,6 +103,37 @@ def test_build_rows_matches_oracle(case):
         for k in range(comp.Q):
             bit = (int(m[i, k // 32]) >> (k % 32)) & 1
             assert bit == int(comp.visible[perm[i], perm[k]]), (i, k)
+    # per-tile branch tables, from the oracle's rows and Vis sets: branch of a
+    # row = its column (ordinary, lookahead) or n_cols + candidate (verify);
+    # a branch's path entry e = the packed row (minus one) at position
+    # p + 1 + e that the branch's deepest row sees
+    n_cols = info.n_cols
+    inv = {o: g for g, o in enumerate(perm)}
+    def branch_of(o):
+        r = comp.rows[o]
+        return n_cols + r.identity[3] if r.identity[0] == orows.VERIFY else r.identity[2]
+    ntiles = (comp.Q + 15) // 16
+    meta = b[info.off_tile_meta: info.off_tile_meta + ntiles * 64].reshape(ntiles, 64)
+    tpath = b[info.off_tile_path: info.off_tile_path + ntiles * 1024].reshape(ntiles, 16, 64)
+    p0 = comp.rows[comp.out].logical_position
+    for t in range(ntiles):
+        brs = []
+        for g in range(16 * t, min(16 * t + 16, comp.Q)):
+            bb = branch_of(perm[g])
+            if bb not in brs:
+                brs.append(bb)
+        assert meta[t, 0] == len(brs) and list(meta[t, 1: 1 + len(brs)]) == brs, t
+        assert (meta[t, 1 + len(brs):] == -1).all()
+        for i in range(16):
+            want_row = np.full(64, -1)
+            if i < len(brs):
+                members = [o for o in range(comp.Q) if branch_of(o) == brs[i]]
+                deep = max(members, key=lambda o: comp.rows[o].logical_position)
+                for k in range(comp.Q):
+                    e = comp.rows[k].logical_position - p0 - 1
+                    if k != comp.out and comp.visible[deep, k] and 0 <= e < 64:
+                        want_row[e] = inv[k] - 1
+            assert list(tpath[t, i]) == list(want_row), (t, i)
 
 
 def _attn_case(sizes, starts, cands, S, p, H, Hkv, dh, dtype, seed=0, t_cap=None):
