@@ -780,18 +780,15 @@ la_attn_kernel(LaAttnArgs a) {
 // a (row, head).
 template <typename T, int DH>
 __global__ void __launch_bounds__(256) la_attn_merge_kernel(LaAttnArgs a) {
-  constexpr int V4 = DH / 4;
+  constexpr int V4 = DH / 4, MS = 8;            // splits whose loads are all issued before the fold
   const int idx = blockIdx.x * 256 + threadIdx.x;
   if (idx >= a.Q * a.H * V4) return;
   const int d4 = idx % V4, rh = idx / V4;
   const int row = rh / a.H, hh = rh % a.H;
   float ma = NEG_INF, la = 0.f;
   float oa[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < a.nsplit; ++s) {
-    const size_t base = ((size_t)s * a.H + hh) * a.Q + row;
-    const float2 ml = *(const float2*)(a.part_ml + base * 2);
-    if (ml.x == NEG_INF) continue;
-    const float4 ob = *(const float4*)(a.part_o + base * DH + 4 * d4);
+  auto fold = [&](float2 ml, float4 ob) __attribute__((always_inline)) {
+    if (ml.x == NEG_INF) return;
     const float mn = fmaxf(ma, ml.x);
     const float wa = ex2(ma - mn), wb = ex2(ml.x - mn);
     la = lin2(la, wa, ml.y, wb);
@@ -800,10 +797,31 @@ __global__ void __launch_bounds__(256) la_attn_merge_kernel(LaAttnArgs a) {
     oa[2] = lin2(oa[2], wa, ob.z, wb);
     oa[3] = lin2(oa[3], wa, ob.w, wb);
     ma = mn;
+  };
+  for (int s0 = 0; s0 < a.nsplit; s0 += MS) {
+    float2 ml[MS];
+    float4 ob[MS];
+#pragma unroll
+    for (int k = 0; k < MS; ++k) {
+      const int s = s0 + k;
+      if (s < a.nsplit) {
+        const size_t base = ((size_t)s * a.H + hh) * a.Q + row;
+        ml[k] = *(const float2*)(a.part_ml + base * 2);
+        ob[k] = *(const float4*)(a.part_o + base * DH + 4 * d4);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < MS; ++k)
+      if (s0 + k < a.nsplit) fold(ml[k], ob[k]);
   }
   T* dst = (T*)a.o + ((size_t)row * a.H + hh) * DH + 4 * d4;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) st<T>(dst + i, oa[i] / la);
+  if constexpr (sizeof(T) == 2) {
+    const uint32_t w0 = (uint32_t)f2bf(oa[0] / la) | ((uint32_t)f2bf(oa[1] / la) << 16);
+    const uint32_t w1 = (uint32_t)f2bf(oa[2] / la) | ((uint32_t)f2bf(oa[3] / la) << 16);
+    *(uint2*)dst = make_uint2(w0, w1);
+  } else {
+    *(float4*)dst = make_float4(oa[0] / la, oa[1] / la, oa[2] / la, oa[3] / la);
+  }
 }
 
 // Ring stages (128 positions each) per key split: a function of the cache
