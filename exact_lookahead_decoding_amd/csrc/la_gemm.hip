@@ -4,9 +4,8 @@
 // every weight matrix ("M7.3 - Lookahead Decoding", 0x05C row and FLOP
 // ledger: token-wise target work over Q rows), so the round's cost is one
 // pass over the weights and the kernel's only job is to keep HBM busy:
-//   * a workgroup (WV = 3 or 4 waves, a function of the weight shape) owns
-//     WV*NTW output tiles of 16 columns (SwiGLU: WV gate/up tile pairs) and
-//     one split of K;
+//   * a workgroup (4 waves) owns 4*NTW output tiles of 16 columns (SwiGLU:
+//     4 gate/up tile pairs) and one split of K;
 //   * W is stored packed (la_gemm_pack_launch): the MFMA B fragments of one
 //     workgroup step lie in one contiguous run of 4*NTW*NKB KB, in the order
 //     the DMA instructions read them, so every instruction reads 1 KB
@@ -16,8 +15,8 @@
 //   * W and X reach LDS through global_load_lds, one 1 KB MFMA fragment per
 //     DMA instruction (lane l's 16 bytes at 16 l, read back with
 //     conflict-free ds_read_b128), in a ring of DW+1 stages: each wave brings
-//     its own W fragments and its share of the X fragments used by all the
-//     workgroup's waves, DW steps ahead of the MFMAs;
+//     its own W fragments and a quarter of the X fragments shared by all
+//     four, DW steps ahead of the MFMAs;
 //   * per step: wait for this wave's step (a static vmcnt: every step is the
 //     same G loads per wave, steps past the end load 16 bytes of a valid
 //     address), a barrier that leaves the later steps in flight, issue step
@@ -61,20 +60,15 @@ template <typename T> __device__ __forceinline__ f32x4 kblock(v4u a, v4u b, f32x
 }
 
 // A ring step is NKB k-blocks (4 for narrow stages, 2 once the X and W
-// fragments of a k-block reach 12 KB); the X fragments of a step are spread
-// over the WV waves (slots rounded up to whole loads per wave, the extra
-// slots take dummy loads); the ring holds DW+1 stages and the per-step wait
-// may not exceed vmcnt's 63.
-constexpr int gemm_nkb(int mt, int ntw, int wv) { return mt + wv * ntw >= 12 ? 2 : 4; }
-constexpr int gemm_xslots(int mt, int ntw, int wv) { return (mt * gemm_nkb(mt, ntw, wv) + wv - 1) / wv * wv; }
-constexpr int gemm_stage(int mt, int ntw, int wv) {
-  return (gemm_xslots(mt, ntw, wv) + wv * ntw * gemm_nkb(mt, ntw, wv)) * 1024;
-}
-constexpr int gemm_loads(int mt, int ntw, int wv) { return ntw * gemm_nkb(mt, ntw, wv) + gemm_xslots(mt, ntw, wv) / wv; }
-constexpr int gemm_depth(int mt, int ntw, int wv) {
+// fragments of a k-block reach 12 KB); the ring holds DW+1 stages and the
+// per-step wait may not exceed vmcnt's 63.
+constexpr int gemm_nkb(int mt, int ntw) { return mt + 4 * ntw >= 12 ? 2 : 4; }
+constexpr int gemm_stage(int mt, int ntw) { return (mt + 4 * ntw) * gemm_nkb(mt, ntw) * 1024; }
+constexpr int gemm_loads(int mt, int ntw) { return (ntw + mt / 4) * gemm_nkb(mt, ntw) + (mt % 4) * gemm_nkb(mt, ntw) / 4; }
+constexpr int gemm_depth(int mt, int ntw) {
   int d = 5;
-  while (d > 1 && (d + 1) * gemm_stage(mt, ntw, wv) > LDS_BYTES) --d;
-  while (d > 1 && (d - 1) * gemm_loads(mt, ntw, wv) > 63) --d;
+  while (d > 1 && (d + 1) * gemm_stage(mt, ntw) > LDS_BYTES) --d;
+  while (d > 1 && (d - 1) * gemm_loads(mt, ntw) > 63) --d;
   return d;
 }
 
@@ -94,18 +88,18 @@ __device__ __forceinline__ void gemm_store(const LaGemmArgs& a, int m, int n, fl
   }
 }
 
-template <typename T, int MT, int NTW, int EPI, int WV>
-__global__ void __launch_bounds__(64 * WV) la_gemm_kernel(LaGemmArgs a) {
+template <typename T, int MT, int NTW, int EPI>
+__global__ void __launch_bounds__(256) la_gemm_kernel(LaGemmArgs a) {
   constexpr int KC = GT<T>::KC, EPL = GT<T>::EPL, KB = KC / 4;
-  constexpr int NKB = gemm_nkb(MT, NTW, WV);     // k-blocks per ring step
-  constexpr int DW = gemm_depth(MT, NTW, WV);
+  constexpr int NKB = gemm_nkb(MT, NTW);         // k-blocks per ring step
+  constexpr int DW = gemm_depth(MT, NTW);
   constexpr int R = DW + 1;                      // ring stages
-  constexpr int STAGE = gemm_stage(MT, NTW, WV);
-  constexpr int NXF = MT * NKB;                  // X fragments of a step
-  constexpr int WOFF = gemm_xslots(MT, NTW, WV) * 1024;   // W fragments after the X slots
-  constexpr int XF = gemm_xslots(MT, NTW, WV) / WV;       // X loads per step and wave
+  constexpr int STAGE = gemm_stage(MT, NTW);
+  constexpr int WOFF = MT * NKB * 1024;          // W fragments after the X fragments
+  constexpr int XF = MT * NKB / 4;               // X fragments per step and wave
   constexpr int G = NTW * NKB + XF;              // DMA instructions per step and wave
-  static_assert(G == gemm_loads(MT, NTW, WV), "load count");
+  static_assert((MT * NKB) % 4 == 0, "X fragments split evenly over the waves");
+  static_assert(G == gemm_loads(MT, NTW), "load count");
   extern __shared__ __attribute__((aligned(1024))) char lds[];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -118,23 +112,22 @@ __global__ void __launch_bounds__(64 * WV) la_gemm_kernel(LaGemmArgs a) {
 
   // tile t of this wave: output columns colw + 16 t (SwiGLU: gate columns
   // colw and their up rows); its fragment for k-block kb sits at packed
-  // fragment ((blockIdx.x * nkb + kb) * WV + wave) * NTW + t
-  const int colw = (blockIdx.x * WV + wave) * 16 * (swiglu ? 1 : NTW);
+  // fragment ((blockIdx.x * nkb + kb) * 4 + wave) * NTW + t
+  const int colw = (blockIdx.x * 4 + wave) * 16 * (swiglu ? 1 : NTW);
   const size_t nkb = (size_t)(a.K / KB);
   const T* W = (const T*)a.W;
   const T* X = (const T*)a.X;
   const T* wp[NTW];
 #pragma unroll
   for (int t = 0; t < NTW; ++t)
-    wp[t] = W + ((((size_t)blockIdx.x * nkb + (size_t)c_begin * 4) * WV + wave) * NTW + t) * 64 * EPL + lane * EPL;
-  // X fragments this wave brings in: f = wave + WV j is (row tile f / NKB,
-  // k-block f % NKB); rows past M load row M - 1 and are never stored;
-  // slots f >= NXF take a dummy load nobody reads
+    wp[t] = W + ((((size_t)blockIdx.x * nkb + (size_t)c_begin * 4) * 4 + wave) * NTW + t) * 64 * EPL + lane * EPL;
+  // X fragments this wave brings in: f = wave + 4 j is (row tile f / NKB,
+  // k-block f % NKB); rows past M load row M - 1 and are never stored
   const T* xp = X + (size_t)c_begin * KC + EPL * g;
   int xoff[XF];
 #pragma unroll
   for (int j = 0; j < XF; ++j) {
-    const int f = min(wave + WV * j, NXF - 1);
+    const int f = wave + 4 * j;
     xoff[j] = min((f / NKB) * 16 + c16, a.M - 1) * a.ldx + (f % NKB) * KB;
   }
 
@@ -155,7 +148,7 @@ __global__ void __launch_bounds__(64 * WV) la_gemm_kernel(LaGemmArgs a) {
     for (int t = 0; t < NTW; ++t) {
 #pragma unroll
       for (int s = 0; s < NKB; ++s) {
-        const T* src = live ? wp[t] + ((size_t)i * NKB + s) * (WV * NTW * 64 * EPL) : W;
+        const T* src = live ? wp[t] + ((size_t)i * NKB + s) * (4 * NTW * 64 * EPL) : W;
         __builtin_amdgcn_global_load_lds((const void*)src,
                                          (lds_void_t*)(stage + WOFF + ((wave * NTW + t) * NKB + s) * 1024), 16, 0,
                                          CPOL_NT);
@@ -163,8 +156,8 @@ __global__ void __launch_bounds__(64 * WV) la_gemm_kernel(LaGemmArgs a) {
     }
 #pragma unroll
     for (int j = 0; j < XF; ++j) {
-      const T* src = (live && wave + WV * j < NXF) ? xp + xoff[j] + k0 : X;
-      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(stage + (wave + WV * j) * 1024), 16, 0, 0);
+      const T* src = live ? xp + xoff[j] + k0 : X;
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(stage + (wave + 4 * j) * 1024), 16, 0, 0);
     }
   };
 
@@ -266,32 +259,21 @@ __global__ void __launch_bounds__(256) la_gemm_reduce_kernel(LaGemmArgs a) {
 // (its gate and up tiles).
 int la_gemm_ntw(int N, int swiglu) { return swiglu ? 2 : (N >= 25600 ? 2 : 1); }
 
-// Waves per workgroup, also a function of the weight shape only: three
-// when four would leave 32 or more CUs without a workgroup and three give
-// every CU at most one (so the weight stream spreads over more CUs), else
-// four.  Shapes with fewer than 128 blocks split K instead.
-int la_gemm_waves(int N, int swiglu) {
-  const int pw = swiglu ? 1 : la_gemm_ntw(N, swiglu);   // output tiles per wave
-  const int tiles = N / 16;
-  const int b4 = (tiles + 4 * pw - 1) / (4 * pw), b3 = (tiles + 3 * pw - 1) / (3 * pw);
-  return (b4 >= 128 && b4 < 224 && b3 <= 256) ? 3 : 4;
-}
-
 static size_t pack_blocks(int N, int swiglu) {
-  const int per = (swiglu ? 1 : la_gemm_ntw(N, swiglu)) * la_gemm_waves(N, swiglu);   // output tiles per workgroup
+  const int per = swiglu ? 4 : 4 * la_gemm_ntw(N, swiglu);   // output tiles per workgroup
   return (size_t)((N / 16 + per - 1) / per);
 }
 
 size_t la_gemm_packed_elems(int N, int K, int swiglu) {
-  return pack_blocks(N, swiglu) * la_gemm_waves(N, swiglu) * la_gemm_ntw(N, swiglu) * 16 * (size_t)K;
+  return pack_blocks(N, swiglu) * 4 * la_gemm_ntw(N, swiglu) * 16 * (size_t)K;
 }
 
-// Packed W: fragment f = ((b * nkb + kb) * WV + w) * NTW + t holds, lane l
+// Packed W: fragment f = ((b * nkb + kb) * 4 + w) * NTW + t holds, lane l
 // after lane, the 16 bytes of W row (tile row0 + l % 16), k = kb * KB +
 // EPL * (l / 16) .. +EPL-1; rows of tiles past N are zero.
 template <typename T>
 __global__ void __launch_bounds__(256) la_gemm_pack_kernel(const T* W, T* P, int N, int K, int up_off, int ntw,
-                                                           int wv, int swiglu, size_t pieces) {
+                                                           int swiglu, size_t pieces) {
   constexpr int KB = GT<T>::KC / 4, EPL = GT<T>::EPL;
   const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= pieces) return;
@@ -299,10 +281,10 @@ __global__ void __launch_bounds__(256) la_gemm_pack_kernel(const T* W, T* P, int
   const size_t f = idx >> 6;
   const size_t nkb = (size_t)(K / KB);
   const int t = (int)(f % ntw);
-  const int w = (int)((f / ntw) % wv);
-  const int kb = (int)((f / (wv * ntw)) % nkb);
-  const size_t b = f / (wv * ntw * nkb);
-  const int col = swiglu ? (int)(b * wv + w) * 16 : (int)(b * wv + w) * 16 * ntw + 16 * t;
+  const int w = (int)((f / ntw) % 4);
+  const int kb = (int)((f / (4 * ntw)) % nkb);
+  const size_t b = f / (4 * ntw * nkb);
+  const int col = swiglu ? (int)(b * 4 + w) * 16 : (int)(b * 4 + w) * 16 * ntw + 16 * t;
   u32x4 v = {0, 0, 0, 0};
   if (col < N) {
     const int row = (swiglu ? col + t * up_off : col) + (lane & 15);
@@ -319,10 +301,10 @@ int la_gemm_pack_launch(int dtype, const void* W, void* P, int N, int K, int swi
   const unsigned grid = (unsigned)((pieces + 255) / 256);
   if (dtype == LA_DT_BF16)
     hipLaunchKernelGGL(la_gemm_pack_kernel<bf16_t>, dim3(grid), dim3(256), 0, st, (const bf16_t*)W, (bf16_t*)P, N, K,
-                       N, ntw, la_gemm_waves(N, swiglu), swiglu, pieces);
+                       N, ntw, swiglu, pieces);
   else
     hipLaunchKernelGGL(la_gemm_pack_kernel<float>, dim3(grid), dim3(256), 0, st, (const float*)W, (float*)P, N, K, N,
-                       ntw, la_gemm_waves(N, swiglu), swiglu, pieces);
+                       ntw, swiglu, pieces);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
@@ -331,7 +313,7 @@ int la_gemm_splits(int N, int K, int dtype, int swiglu) {
   // are too few column tiles to give every CU a workgroup, up to 4 ways
   const int kc = dtype == LA_DT_BF16 ? GT<bf16_t>::KC : GT<float>::KC;
   const int nchunks = K / kc;
-  const int blocks = (int)pack_blocks(N, swiglu);
+  const int blocks = (N / 16 + 3) / 4;
   if (swiglu || blocks >= 128 || nchunks < 2) return 1;
   int s = (256 + blocks - 1) / blocks;
   s = std::min(s, 4);
@@ -339,39 +321,32 @@ int la_gemm_splits(int N, int K, int dtype, int swiglu) {
   return std::max(s, 1);
 }
 
-template <typename T, int MT, int NTW, int EPI, int WV>
+template <typename T, int MT, int NTW, int EPI>
 static void launch_k(const LaGemmArgs& a, dim3 grid, hipStream_t st) {
-  constexpr int lds = (gemm_depth(MT, NTW, WV) + 1) * gemm_stage(MT, NTW, WV);
+  constexpr int lds = (gemm_depth(MT, NTW) + 1) * gemm_stage(MT, NTW);
   static_assert(lds <= LDS_BYTES, "LDS");
-  auto kern = la_gemm_kernel<T, MT, NTW, EPI, WV>;
+  auto kern = la_gemm_kernel<T, MT, NTW, EPI>;
   static bool attr = false;   // idempotent, so a race between threads only repeats it
   if (!attr) {
     hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     attr = true;
   }
-  hipLaunchKernelGGL(kern, grid, dim3(64 * WV), lds, st, a);
-}
-
-template <typename T, int EPI, int MT, int NTW>
-static void launch_ntw(const LaGemmArgs& a, int wv, dim3 grid, hipStream_t st) {
-  const bool part = a.splits > 1;
-  if (wv == 3) {
-    if (part) launch_k<T, MT, NTW, LA_EPI_PARTIAL, 3>(a, grid, st);
-    else launch_k<T, MT, NTW, EPI, 3>(a, grid, st);
-  } else {
-    if (part) launch_k<T, MT, NTW, LA_EPI_PARTIAL, 4>(a, grid, st);
-    else launch_k<T, MT, NTW, EPI, 4>(a, grid, st);
-  }
+  hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, a);
 }
 
 template <typename T, int EPI, int MT>
 static void launch_mt(const LaGemmArgs& a, int ntw, hipStream_t st) {
   const int tiles = a.N / 16;
-  const int wv = la_gemm_waves(a.N, a.swiglu_partial);
-  const int per = (a.swiglu_partial ? 1 : ntw) * wv;
+  const int per = a.swiglu_partial ? 4 : 4 * ntw;
   dim3 grid((tiles + per - 1) / per, a.splits);
-  if (ntw == 2) launch_ntw<T, EPI, MT, 2>(a, wv, grid, st);
-  else launch_ntw<T, EPI, MT, 1>(a, wv, grid, st);
+  const bool part = a.splits > 1;
+  if (ntw == 2) {
+    if (part) launch_k<T, MT, 2, LA_EPI_PARTIAL>(a, grid, st);
+    else launch_k<T, MT, 2, EPI>(a, grid, st);
+  } else {
+    if (part) launch_k<T, MT, 1, LA_EPI_PARTIAL>(a, grid, st);
+    else launch_k<T, MT, 1, EPI>(a, grid, st);
+  }
 }
 
 template <typename T, int EPI>

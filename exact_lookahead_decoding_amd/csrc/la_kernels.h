@@ -22,7 +22,6 @@ struct LaGemmArgs {
 };
 int la_gemm_splits(int N, int K, int dtype, int swiglu);
 int la_gemm_ntw(int N, int swiglu);
-int la_gemm_waves(int N, int swiglu);   // waves per workgroup (3 or 4), part of the packed layout
 size_t la_gemm_packed_elems(int N, int K, int swiglu);   // elements of the packed copy of W
 // W [rows][K] (SwiGLU: gate rows 0..N-1, up rows N..2N-1) -> packed P
 int la_gemm_pack_launch(int dtype, const void* W, void* P, int N, int K, int swiglu, hipStream_t st);

@@ -378,8 +378,6 @@ LINEAR = [
     ("store", 181, 1536, 256),      # ragged M (12 row tiles), small K
     ("swiglu", 17, 512, 256),
     ("store", 40, 1040, 384),       # ragged N: the last workgroup holds one live tile of four
-    ("store", 24, 11200, 256),      # three-wave workgroups, the last one with one live tile of three
-    ("swiglu", 9, 11200, 128),
 ]
 
 
