@@ -287,8 +287,15 @@ static const char* wptr(const void* base, size_t elems_per_layer, int l, int esz
   return (const char*)base + (size_t)l * elems_per_layer * esz;
 }
 
+// The QKV projection writes q, k and v (rotated, placed) from its epilogue
+// when its K is not split; its weights are then packed pair-major.  A
+// function of the shape only, shared by the packer and the forward.
+static bool qkv_fused(int qkvdim, int d, int dt, int dh) {
+  return la_gemm_splits(qkvdim, d, dt, 0) == 1 && dh >= 16 && (dh & (dh - 1)) == 0;
+}
+
 static int gemm(la_ctx* c, int epi, const void* X, const void* W, void* Y, const void* Rr, int M, int N, int K,
-                int up_off, bool defer = false) {
+                int up_off, bool defer = false, const LaQkvOut* qo = nullptr) {
   LaGemmArgs a{};
   a.X = X; a.W = W; a.Y = Y; a.R = Rr; a.P = c->gemm_p;
   a.M = M; a.N = N; a.K = K; a.ldx = K; a.ldy = N;
@@ -296,6 +303,7 @@ static int gemm(la_ctx* c, int epi, const void* X, const void* W, void* Y, const
   a.up_off = up_off;
   a.pcols = epi == LA_EPI_SWIGLU ? 2 * N : N;
   a.defer_reduce = defer ? 1 : 0;
+  if (qo) a.qo = *qo;
   const double wrows = epi == LA_EPI_SWIGLU ? 2.0 * N : (double)N;
   const double ybytes = epi == LA_EPI_F32 ? 4.0 : (double)c->esz;
   const double bytes = (wrows * K + (double)M * K) * c->esz + (double)M * N * ybytes * (epi == LA_EPI_RESID ? 2 : 1);
@@ -353,9 +361,15 @@ static int forward(la_ctx* c, int M, const int32_t* tok, const int32_t* pos, con
     const size_t pstride = (size_t)M * c->d;
     la_addnorm_launch(c->dtype, c->x, c->gemm_p, pend, pstride, 1, attn_norm, c->nrm, nullptr, M, c->d, c->dims.eps,
                       c->st);
-    if ((rc = gemm(c, LA_EPI_STORE, c->nrm, wqkv, c->qkv, nullptr, M, c->qkvdim, c->d, 0))) return rc;
-    la_qkv_post_launch(c->dtype, c->qkv, c->rope, pos, M, c->H, c->Hkv, c->dh, c->q, kc, vc, c->t_cap, cache_row0,
-                       n_direct, kw, vw, c->ws_cap, c->st);
+    if (qkv_fused(c->qkvdim, c->d, c->dtype, c->dh)) {
+      const LaQkvOut qo{c->rope, pos, c->q, kc, vc, kw, vw, c->H, c->Hkv, c->dh, c->t_cap, cache_row0, n_direct,
+                        c->ws_cap};
+      if ((rc = gemm(c, LA_EPI_QKV, c->nrm, wqkv, c->qkv, nullptr, M, c->qkvdim, c->d, 0, false, &qo))) return rc;
+    } else {
+      if ((rc = gemm(c, LA_EPI_STORE, c->nrm, wqkv, c->qkv, nullptr, M, c->qkvdim, c->d, 0))) return rc;
+      la_qkv_post_launch(c->dtype, c->qkv, c->rope, pos, M, c->H, c->Hkv, c->dh, c->q, kc, vc, c->t_cap, cache_row0,
+                         n_direct, kw, vw, c->ws_cap, c->st);
+    }
     at.kc = kc; at.vc = vc; at.kw = kw; at.vw = vw;
     {
       // committed K/V read once (positions below shared_end), each packed row's K/V, Q in, O out
@@ -951,7 +965,7 @@ extern "C" int la_pack_weights(const la_model_dims* dims, const la_model* plain,
   for (int l = 0; l < dims->n_layers; ++l) {
     char* pl = out + pk.layer * l * esz;
     rc = la_gemm_pack_launch(dt, (const char*)plain->wqkv + (size_t)l * qkvdim * d * esz, pl + pk.qkv * esz, qkvdim,
-                             d, 0, st);
+                             d, 0, st, qkv_fused(qkvdim, d, dt, dims->head_dim) ? dims->head_dim : 0);
     rc = rc ? rc : la_gemm_pack_launch(dt, (const char*)plain->wo + (size_t)l * d * hd * esz, pl + pk.o * esz, d, hd,
                                        0, st);
     rc = rc ? rc : la_gemm_pack_launch(dt, (const char*)plain->w_gate_up + (size_t)l * 2 * F * d * esz,

@@ -88,6 +88,44 @@ __device__ __forceinline__ void gemm_store(const LaGemmArgs& a, int m, int n, fl
   }
 }
 
+// Fused QKV epilogue of packed column n (pair-major inside each head) of row
+// m: the value is rounded to the storage type, as a stored projection would
+// be; q and k are rotated at the row's logical position with the rotation
+// partner from lane ^ 8 (same row, same tile), then written where the
+// attention reads them.  Every lane of the wave calls it (the partner
+// exchange is a wave operation); rows past M are not stored.
+// (cos, sin) of packed column n at row m (1, 0 for v columns and dead lanes)
+__device__ __forceinline__ float2 qkv_rope(const LaQkvOut& o, int m, int n, bool live) {
+  const int hb = n >> o.lg_dh, j = n & (o.dh - 1);
+  if (!live || hb >= o.H + o.Hkv) return make_float2(1.f, 0.f);
+  return o.rope[((size_t)o.pos[m] << (o.lg_dh - 1)) + 8 * (j >> 4) + (j & 7)];
+}
+
+template <typename T>
+__device__ __forceinline__ void qkv_store(const LaQkvOut& o, int m, int n, float v, bool live, float2 cs) {
+  const float x = StoreT<T>::round(v);
+  const float xp = __shfl_xor(x, 8, 64);
+  if (!live) return;
+  const int dh = o.dh, half = dh / 2;
+  const int hb = n >> o.lg_dh, j = n & (dh - 1), k = j >> 4, c = j & 15;
+  const int i = 8 * k + (c & 7);                  // rotation index
+  const int d = c < 8 ? i : half + i;             // natural head dimension
+  T* dst;
+  bool rot = true;
+  if (hb < o.H) {
+    dst = (T*)o.q + ((size_t)m * o.H + hb) * dh;
+  } else {
+    const bool isk = hb < o.H + o.Hkv;
+    const int g = isk ? hb - o.H : hb - o.H - o.Hkv;
+    rot = isk;
+    if (m < o.n_direct) dst = (T*)(isk ? o.kc : o.vc) + ((size_t)g * o.T_cap + o.cache_row0 + m) * dh;
+    else dst = (T*)(isk ? o.kw : o.vw) + ((size_t)g * o.ws_cap + (m - o.n_direct)) * dh;
+  }
+  float y = x;
+  if (rot) y = c < 8 ? x * cs.x - xp * cs.y : x * cs.x + xp * cs.y;
+  st<T>(dst + d, y);
+}
+
 template <typename T, int MT, int NTW, int EPI>
 __global__ void __launch_bounds__(256) la_gemm_kernel(LaGemmArgs a) {
   constexpr int KC = GT<T>::KC, EPL = GT<T>::EPL, KB = KC / 4;
@@ -191,6 +229,22 @@ __global__ void __launch_bounds__(256) la_gemm_kernel(LaGemmArgs a) {
     });
   };
 
+  // fused QKV epilogue: the rotation factors of the lane's outputs are
+  // fetched before the ring starts (few rows), so their latency hides
+  // behind the weight stream
+  constexpr bool QPRE = EPI == LA_EPI_QKV && MT <= 4;
+  float2 qcs[QPRE ? MT : 1][4][NTW];
+  if constexpr (QPRE) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int t = 0; t < NTW; ++t) {
+          const int m = mt * 16 + 4 * g + r, col = colw + 16 * t;
+          qcs[mt][r][t] = qkv_rope(a.qo, m, col + c16, m < a.M && col < a.N);
+        }
+  }
   static_for<0, DW>([&](auto J) { issue(J, decltype(J)::value); });
   for (int i0 = 0; i0 < n; i0 += R) {
     static_for<0, R>([&](auto J) {
@@ -207,6 +261,22 @@ __global__ void __launch_bounds__(256) la_gemm_kernel(LaGemmArgs a) {
   wait_vm<0>();   // no DMA may land after the workgroup has left
 
   // D lane l holds rows 4*g + r, column c16 of each 16x16 tile
+  if constexpr (EPI == LA_EPI_QKV) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int t = 0; t < NTW; ++t) {
+          const int m = mt * 16 + 4 * g + r, col = colw + 16 * t;
+          const bool live = m < a.M && col < a.N;
+          float2 cs;
+          if constexpr (QPRE) cs = qcs[mt][r][t];
+          else cs = qkv_rope(a.qo, m, col + c16, live);
+          qkv_store<T>(a.qo, m, col + c16, acc[mt][t][r], live, cs);
+        }
+    return;
+  }
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
@@ -268,12 +338,20 @@ size_t la_gemm_packed_elems(int N, int K, int swiglu) {
   return pack_blocks(N, swiglu) * 4 * la_gemm_ntw(N, swiglu) * 16 * (size_t)K;
 }
 
+// Natural column of packed column n under the pair-major order of the fused
+// QKV epilogue: inside each dh-wide head, tile k holds dims 8k .. 8k+7 in
+// its lanes 0..7 and their rotation partners dh/2 + 8k .. in lanes 8..15.
+__host__ __device__ __forceinline__ int qkv_natural(int n, int dh) {
+  const int j = n % dh, k = j / 16, c = j % 16;
+  return n - j + (c < 8 ? 8 * k + c : dh / 2 + 8 * k + c - 8);
+}
+
 // Packed W: fragment f = ((b * nkb + kb) * 4 + w) * NTW + t holds, lane l
 // after lane, the 16 bytes of W row (tile row0 + l % 16), k = kb * KB +
 // EPL * (l / 16) .. +EPL-1; rows of tiles past N are zero.
 template <typename T>
 __global__ void __launch_bounds__(256) la_gemm_pack_kernel(const T* W, T* P, int N, int K, int up_off, int ntw,
-                                                           int swiglu, size_t pieces) {
+                                                           int swiglu, int rope_dh, size_t pieces) {
   constexpr int KB = GT<T>::KC / 4, EPL = GT<T>::EPL;
   const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= pieces) return;
@@ -287,24 +365,26 @@ __global__ void __launch_bounds__(256) la_gemm_pack_kernel(const T* W, T* P, int
   const int col = swiglu ? (int)(b * 4 + w) * 16 : (int)(b * 4 + w) * 16 * ntw + 16 * t;
   u32x4 v = {0, 0, 0, 0};
   if (col < N) {
-    const int row = (swiglu ? col + t * up_off : col) + (lane & 15);
+    int row = (swiglu ? col + t * up_off : col) + (lane & 15);
+    if (rope_dh > 0) row = qkv_natural(row, rope_dh);
     v = *(const u32x4*)(W + (size_t)row * K + (size_t)kb * KB + EPL * (lane >> 4));
   }
   *(u32x4*)(P + idx * EPL) = v;
 }
 
-int la_gemm_pack_launch(int dtype, const void* W, void* P, int N, int K, int swiglu, hipStream_t st) {
+int la_gemm_pack_launch(int dtype, const void* W, void* P, int N, int K, int swiglu, hipStream_t st, int rope_dh) {
   const int kc = dtype == LA_DT_BF16 ? GT<bf16_t>::KC : GT<float>::KC;
   if (N % 16 != 0 || K % kc != 0 || N <= 0) return -2;
+  if (rope_dh > 0 && (swiglu || rope_dh % 16 != 0 || N % rope_dh != 0)) return -2;
   const int ntw = la_gemm_ntw(N, swiglu);
   const size_t pieces = la_gemm_packed_elems(N, K, swiglu) / (dtype == LA_DT_BF16 ? 8 : 4);
   const unsigned grid = (unsigned)((pieces + 255) / 256);
   if (dtype == LA_DT_BF16)
     hipLaunchKernelGGL(la_gemm_pack_kernel<bf16_t>, dim3(grid), dim3(256), 0, st, (const bf16_t*)W, (bf16_t*)P, N, K,
-                       N, ntw, swiglu, pieces);
+                       N, ntw, swiglu, rope_dh, pieces);
   else
     hipLaunchKernelGGL(la_gemm_pack_kernel<float>, dim3(grid), dim3(256), 0, st, (const float*)W, (float*)P, N, K, N,
-                       ntw, swiglu, pieces);
+                       ntw, swiglu, rope_dh, pieces);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
@@ -386,12 +466,17 @@ int la_gemm_launch(int dtype, int epi, LaGemmArgs a, hipStream_t st) {
   if (a.splits > a.nchunks) return -2;
   if (a.splits > 1 && a.P == nullptr) return -2;
   if (a.defer_reduce && (a.splits < 2 || epi != LA_EPI_RESID)) return -2;
+  if (epi == LA_EPI_QKV) {
+    if (a.splits != 1 || a.qo.dh < 16 || (a.qo.dh & (a.qo.dh - 1)) != 0 || a.N % a.qo.dh != 0) return -2;
+    a.qo.lg_dh = __builtin_ctz((unsigned)a.qo.dh);
+  }
   if (dtype == LA_DT_BF16) {
     switch (epi) {
       case LA_EPI_STORE: return launch_t<bf16_t, LA_EPI_STORE>(a, st);
       case LA_EPI_RESID: return launch_t<bf16_t, LA_EPI_RESID>(a, st);
       case LA_EPI_SWIGLU: return launch_t<bf16_t, LA_EPI_SWIGLU>(a, st);
       case LA_EPI_F32: return launch_t<bf16_t, LA_EPI_F32>(a, st);
+      case LA_EPI_QKV: return launch_t<bf16_t, LA_EPI_QKV>(a, st);
     }
   } else {
     switch (epi) {
@@ -399,6 +484,7 @@ int la_gemm_launch(int dtype, int epi, LaGemmArgs a, hipStream_t st) {
       case LA_EPI_RESID: return launch_t<float, LA_EPI_RESID>(a, st);
       case LA_EPI_SWIGLU: return launch_t<float, LA_EPI_SWIGLU>(a, st);
       case LA_EPI_F32: return launch_t<float, LA_EPI_F32>(a, st);
+      case LA_EPI_QKV: return launch_t<float, LA_EPI_QKV>(a, st);
     }
   }
   return -2;

@@ -4,7 +4,17 @@
 #include <stdint.h>
 
 enum { LA_DT_F32 = 0, LA_DT_BF16 = 1 };
-enum { LA_EPI_STORE = 0, LA_EPI_RESID = 1, LA_EPI_SWIGLU = 2, LA_EPI_F32 = 3, LA_EPI_PARTIAL = 4 };
+enum { LA_EPI_STORE = 0, LA_EPI_RESID = 1, LA_EPI_SWIGLU = 2, LA_EPI_F32 = 3, LA_EPI_PARTIAL = 4, LA_EPI_QKV = 5 };
+// Fused QKV epilogue: the projection's columns are packed pair-major (la_gemm_pack_launch with rope_dh = dh), each
+// value is rounded to the storage type, rotated at its row's logical position (q and k) and written to q [M][H][dh]
+// and to the K/V cache (the first n_direct rows, at cache row cache_row0 + m) or the workspace (row m - n_direct).
+struct LaQkvOut {
+  const float2* rope;   // [positions][dh/2] (cos, sin)
+  const int32_t* pos;   // [M]
+  void *q, *kc, *vc, *kw, *vw;   // one layer's K/V cache [Hkv][T_cap][dh] and workspace [Hkv][ws_cap][dh]
+  int H, Hkv, dh, T_cap, cache_row0, n_direct, ws_cap;
+  int lg_dh;            // log2(dh) (set by the launcher)
+};
 
 struct LaGemmArgs {
   const void* X;      // [M][ldx] storage dtype
@@ -19,12 +29,14 @@ struct LaGemmArgs {
   int pcols;          // partial row length (SWIGLU: 2F, else N)
   int swiglu_partial; // set by the launcher
   int defer_reduce;   // RESID with splits > 1: leave the partials for la_addnorm_launch
+  LaQkvOut qo;        // QKV epilogue only
 };
 int la_gemm_splits(int N, int K, int dtype, int swiglu);
 int la_gemm_ntw(int N, int swiglu);
 size_t la_gemm_packed_elems(int N, int K, int swiglu);   // elements of the packed copy of W
-// W [rows][K] (SwiGLU: gate rows 0..N-1, up rows N..2N-1) -> packed P
-int la_gemm_pack_launch(int dtype, const void* W, void* P, int N, int K, int swiglu, hipStream_t st);
+// W [rows][K] (SwiGLU: gate rows 0..N-1, up rows N..2N-1) -> packed P; rope_dh > 0 packs the columns of each
+// dh-wide head pair-major (tile k of a head holds dims 8k..8k+7 and dh/2+8k..dh/2+8k+7) for LA_EPI_QKV
+int la_gemm_pack_launch(int dtype, const void* W, void* P, int N, int K, int swiglu, hipStream_t st, int rope_dh = 0);
 int la_gemm_launch(int dtype, int epi, LaGemmArgs a, hipStream_t st);
 
 // row metadata produced by the packed-row builder (device int32 arrays)

@@ -88,7 +88,10 @@ typedef struct la_model {
 /* Packed projections.  A round streams every projection matrix once over the
  * packed rows ("M7.3", 0x05C), so the library keeps them in the order its
  * GEMM reads them: the 16-row MFMA operand slices one workgroup consumes per
- * step lie in one contiguous run.  la_packed_weight_bytes: size of that
+ * step lie in one contiguous run.  When the QKV projection's K is not split,
+ * its columns are packed pair-major inside each head (a 16-column tile holds
+ * 8 dimensions and their rotary partners), so its GEMM rotates q and k and
+ * places q, k and v itself.  la_packed_weight_bytes: size of that
  * buffer for dims (0 for bad dims).  la_pack_weights: fill it (device,
  * 256-byte aligned, caller-owned) from plain's wqkv, wo, w_gate_up, w_down
  * and lm_head, on stream; LA_EINVAL for bad dims or null pointers. */
