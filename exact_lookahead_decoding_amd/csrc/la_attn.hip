@@ -424,13 +424,11 @@ la_attn_kernel(LaAttnArgs a) {
   int br[TPW];
 #pragma unroll
   for (int u = 0; u < TPW; ++u) br[u] = (a.n_tail > 0 && rvalid[u]) ? a.branch[row[u]] : -1;
-  if (!has_tail) {
-#pragma unroll
-    for (int k = 0; k < DEPTH; ++k) issue(ring + k * BLKB, s_end - 1 - k);
-    wait_vm<(CW * DEPTH < 63 ? CW * DEPTH : 63)>();   // this wave's Q, positions and branches (issued first) have landed
-  } else {
-    wait_vm<0>();
-  }
+  // Without tail chunks the ring's first stage goes out with Q and is waited
+  // for here; its second stage follows once Q is read, so the first stage
+  // is not held up behind every workgroup's second one.
+  if (!has_tail) issue(ring, s_end - 1);
+  wait_vm<0>();                                      // this wave's Q, positions, branches (and first stage)
   ring_barrier();                                    // ... and those of the other waves
   QF qf[TPW];
   int pos[TPW], pmin[TPW];
@@ -626,9 +624,10 @@ la_attn_kernel(LaAttnArgs a) {
       }
     }
     // the tail is done with the ring's space: the ring starts
-#pragma unroll
-    for (int k = 0; k < DEPTH; ++k) issue(ring + k * BLKB, s_end - 1 - k);
+    issue(ring, s_end - 1);
   }
+  static_assert(DEPTH == 2, "ring start");
+  issue(ring + BLKB, s_end - 2);                   // the first step waits for the first stage only
 
   // lane parts of the fragment addresses of the class's chunk (stage offsets are immediates)
   uint32_t koff[LP], voff[4];
