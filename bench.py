@@ -309,6 +309,7 @@ def main():
         import torch
         torch.cuda.set_device(0)
         print(json.dumps(attention_op()), flush=True)
+        print(json.dumps(attention_op(reps=24, sets=4, p=8192)), flush=True)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the lookahead round runs on a single MI355X (got --gpus {args.gpus}); "

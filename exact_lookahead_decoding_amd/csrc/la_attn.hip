@@ -297,7 +297,7 @@ la_attn_kernel(LaAttnArgs a) {
   if (g_kv >= a.Hkv) return;
   int li = bi % a.wg_head, sp = 0, hf = -1;
   for (; sp < a.nsplit; ++sp) {
-    const bool half = TPW == 2 && split_has_tail(a, sp);
+    const bool half = TPW == 2 && a.tail_half && split_has_tail(a, sp);
     const int n = a.rgroups * (half ? 2 : 1);
     if (li < n) {
       if (half) {
@@ -855,6 +855,18 @@ static void launch_cfg(const LaAttnArgs& a, int grid, size_t lds, hipStream_t st
   hipLaunchKernelGGL((la_attn_kernel<T, DH, TP, TPW>), dim3(grid), dim3(64 * NCLS * TP), lds, st, a);
 }
 
+// compute units of the current device (cached per device)
+static int cu_count() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    cache[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0 ? n : 256;
+  }
+  return cache[dev];
+}
+
 template <typename T, int DH>
 static int launch_dh(LaAttnArgs a, hipStream_t st) {
   const int group = a.H / a.Hkv;
@@ -882,8 +894,17 @@ static int launch_dh(LaAttnArgs a, hipStream_t st) {
   if (a.n_tail > 0 && rows_for(tp, nt) < need_rows) return -2;
   a.trows = a.n_tail > 0 ? rows_for(tp, nt) : 0;
   a.rgroups = (tiles + nt - 1) / nt;
-  a.wg_head = 0;
-  for (int s = 0; s < a.nsplit; ++s) a.wg_head += a.rgroups * (nt > 1 && split_has_tail(a, s) ? 2 : 1);
+  // Two workgroups per row group in the tail's split, unless that adds a
+  // round of workgroups to the grid (one workgroup fits a CU at a time).
+  auto per_head = [&](bool half) {
+    int n = 0;
+    for (int s = 0; s < a.nsplit; ++s) n += a.rgroups * (half && split_has_tail(a, s) ? 2 : 1);
+    return n;
+  };
+  const int ncu = cu_count();
+  const int single = per_head(false), doubled = per_head(nt > 1);
+  a.tail_half = nt > 1 && (kv * doubled + ncu - 1) / ncu <= (kv * single + ncu - 1) / ncu;
+  a.wg_head = a.tail_half ? doubled : single;
   const int grid = kv * a.wg_head;
   size_t lds;
   if (nt == 4) lds = attn_lds<T, DH, 2, 2>(a.trows);

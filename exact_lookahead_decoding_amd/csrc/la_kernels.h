@@ -97,6 +97,7 @@ struct LaAttnArgs {
   int tail0, n_tail;    // first chunk and number of chunks reaching past shared_end
   int rgroups;          // row groups per KV head
   int wg_head;          // workgroups per KV head (all splits)
+  int tail_half;        // a split holding tail chunks gets two workgroups per row group (one tile per pair slot)
   int trows;            // staged tail rows per tile
   int spb;              // ring stages (128 positions) per key split (la_attention_spb(T_cap))
   int nsplit;           // key splits
