@@ -780,10 +780,16 @@ la_attn_kernel(LaAttnArgs a) {
 template <typename T, int DH>
 __global__ void __launch_bounds__(256) la_attn_merge_kernel(LaAttnArgs a) {
   constexpr int V4 = DH / 4, MS = 8;            // splits whose loads are all issued before the fold
-  const int idx = blockIdx.x * 256 + threadIdx.x;
-  if (idx >= a.Q * a.H * V4) return;
-  const int d4 = idx % V4, rh = idx / V4;
-  const int row = rh / a.H, hh = rh % a.H;
+  // block -> (XCD, KV head): the head's split states were written on that
+  // XCD (the attention kernel's mapping), so they are read from its L2
+  const int group = a.H / a.Hkv;
+  const int per = a.Q * group * V4;               // (row, q-head, 4 dims) items of one KV head
+  const int wpk = (per + 255) / 256;
+  const int g_kv = (blockIdx.x & 7) + 8 * ((blockIdx.x >> 3) / wpk);
+  const int item = ((blockIdx.x >> 3) % wpk) * 256 + threadIdx.x;
+  if (g_kv >= a.Hkv || item >= per) return;
+  const int d4 = item % V4, r2 = item / V4;
+  const int row = r2 / group, hh = g_kv * group + r2 % group;
   float ma = NEG_INF, la = 0.f;
   float oa[4] = {0.f, 0.f, 0.f, 0.f};
   auto fold = [&](float2 ml, float4 ob) __attribute__((always_inline)) {
@@ -915,8 +921,8 @@ static int launch_dh(LaAttnArgs a, hipStream_t st) {
   else if (nt == 2) launch_cfg<T, DH, 1, 2>(a, grid, lds, st);
   else launch_cfg<T, DH, 1, 1>(a, grid, lds, st);
   if (a.nsplit > 1) {
-    const int n = a.Q * a.H * (DH / 4);
-    hipLaunchKernelGGL((la_attn_merge_kernel<T, DH>), dim3((n + 255) / 256), dim3(256), 0, st, a);
+    const int wpk = (a.Q * group * (DH / 4) + 255) / 256;
+    hipLaunchKernelGGL((la_attn_merge_kernel<T, DH>), dim3(kv * wpk), dim3(256), 0, st, a);
   }
   return 0;
 }
