@@ -896,7 +896,9 @@ static int launch_dh(LaAttnArgs a, hipStream_t st) {
   const int kv = 8 * ((a.Hkv + 7) / 8);
   auto wgs = [&](int nt) { return kv * ((tiles + nt - 1) / nt) * a.nsplit; };
   int nt = tiles == 1 ? 1 : (tiles >= 3 && wgs(4) >= 160) ? 4 : 2;
-  const int tp = nt == 4 ? 2 : 1;
+  // two tiles: two pair slots of one tile each (8 waves, two per SIMD)
+  const int tp = nt == 1 ? 1 : 2;
+  const int tpw = nt / tp;
   if (a.n_tail > 0 && rows_for(tp, nt) < need_rows) return -2;
   a.trows = a.n_tail > 0 ? rows_for(tp, nt) : 0;
   a.rgroups = (tiles + nt - 1) / nt;
@@ -908,17 +910,17 @@ static int launch_dh(LaAttnArgs a, hipStream_t st) {
     return n;
   };
   const int ncu = cu_count();
-  const int single = per_head(false), doubled = per_head(nt > 1);
-  a.tail_half = nt > 1 && (kv * doubled + ncu - 1) / ncu <= (kv * single + ncu - 1) / ncu;
+  const int single = per_head(false), doubled = per_head(tpw == 2);
+  a.tail_half = tpw == 2 && (kv * doubled + ncu - 1) / ncu <= (kv * single + ncu - 1) / ncu;
   a.wg_head = a.tail_half ? doubled : single;
   const int grid = kv * a.wg_head;
   size_t lds;
   if (nt == 4) lds = attn_lds<T, DH, 2, 2>(a.trows);
-  else if (nt == 2) lds = attn_lds<T, DH, 1, 2>(a.trows);
+  else if (nt == 2) lds = attn_lds<T, DH, 2, 1>(a.trows);
   else lds = attn_lds<T, DH, 1, 1>(a.trows);
   if (lds > LDS_BYTES) return -2;
   if (nt == 4) launch_cfg<T, DH, 2, 2>(a, grid, lds, st);
-  else if (nt == 2) launch_cfg<T, DH, 1, 2>(a, grid, lds, st);
+  else if (nt == 2) launch_cfg<T, DH, 2, 1>(a, grid, lds, st);
   else launch_cfg<T, DH, 1, 1>(a, grid, lds, st);
   if (a.nsplit > 1) {
     const int wpk = (a.Q * group * (DH / 4) + 255) / 256;
