@@ -567,7 +567,8 @@ extern "C" int la_predict(la_ctx* c, la_round_info* info) {
   if (L.Q > c->q_max) return fail(c, LA_EOVERFLOW, "round needs %d rows > q_max %d", L.Q, c->q_max);
   if (p + L.maxp >= c->rope_rows) return fail(c, LA_EOVERFLOW, "position %d beyond the RoPE table", p + L.maxp);
   rows_layout(L, c->rowbuf, &c->rows, nullptr);
-  la_build_rows_launch(L, x_t, c->win[c->cur], c->wstride, c->cand, c->rows, c->st);
+  if (la_build_rows_launch(L, x_t, c->win[c->cur], c->wstride, c->cand, c->rows, c->st))
+    return fail(c, LA_EOVERFLOW, "row builder: %d rows exceed its LDS tables", L.Q);
   const int maxpos = p + L.maxp;             // a row's branch path covers its own position
   int rc = forward(c, L.Q, c->rows.tok, c->rows.pos, c->rows.branch, c->rows.path, c->rows.path_len,
                    c->rows.tile_meta, c->rows.tile_path, L.NB, L.maxp, 1, p, p + 1, maxpos, c->rows.logit_rows,
@@ -829,7 +830,8 @@ extern "C" int la_build_rows(const la_rows_desc* desc, const int32_t* window, co
   if (!out || !window || (L.C > 0 && !cand) || !info) return fail(nullptr, LA_EINVAL, "null argument");
   LaRowsDev r;
   rows_layout(L, out, &r, info);
-  la_build_rows_launch(L, desc->x_t, window, desc->win_stride, cand, r, (hipStream_t)stream);
+  if (la_build_rows_launch(L, desc->x_t, window, desc->win_stride, cand, r, (hipStream_t)stream))
+    return fail(nullptr, LA_EOVERFLOW, "row builder: %d rows exceed its LDS tables", L.Q);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(nullptr, LA_EDEVICE, "build rows: %s", hipGetErrorString(e));
   return LA_OK;

@@ -66,8 +66,9 @@ struct LaLayout {        // host-side description of one round's rows
   int Q, NB, maxp, n_logit, n_inp, n_cols, mask_words;
 };
 int la_layout_finish(LaLayout* L);   // fills Q, NB, ... ; returns 0 or -1 if inconsistent
-void la_build_rows_launch(const LaLayout& L, int x_t, const int32_t* win, int win_stride,
-                          const int32_t* cands, LaRowsDev rows, hipStream_t st);
+// returns -2 when the round's tables exceed the builder's LDS
+int la_build_rows_launch(const LaLayout& L, int x_t, const int32_t* win, int win_stride,
+                         const int32_t* cands, LaRowsDev rows, hipStream_t st);
 
 // attention
 struct LaAttnArgs {

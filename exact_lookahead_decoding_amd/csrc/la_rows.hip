@@ -24,6 +24,7 @@
 // The attention kernel gathers keys through the path; the bit mask is the
 // same relation written out (for auditing against the dense definition).
 #include "la_common.h"
+#include "la_dev.h"
 #include "la_kernels.h"
 
 static int level_at(const LaLayout* L, int r, int j) {
@@ -77,56 +78,63 @@ __device__ static int d_col_start(const LaLayout& L, int j) {
   return s;
 }
 
+// LDS mirrors of what the later phases read back (positions, branches,
+// paths, tile tables), so the mask and tile phases do no global loads
+__host__ __device__ static size_t rows_lds_bytes(const LaLayout& L) {
+  const int ntiles = (L.Q + 15) / 16;
+  return ((size_t)2 * L.Q + L.NB + (size_t)L.NB * L.maxp + (size_t)ntiles * 64) * 4;
+}
+
 __global__ void __launch_bounds__(256) build_rows_kernel(LaLayout L, int x_t, const int32_t* win, int win_stride,
                                                          const int32_t* cands, LaRowsDev o) {
+  extern __shared__ int32_t sm[];
+  const int ntiles = (L.Q + 15) / 16;
+  int32_t* const s_pos = sm;                       // [Q]
+  int32_t* const s_br = s_pos + L.Q;               // [Q]
+  int32_t* const s_plen = s_br + L.Q;              // [NB]
+  int32_t* const s_path = s_plen + L.NB;           // [NB][maxp]
+  int32_t* const s_meta = s_path + (size_t)L.NB * L.maxp;   // [ntiles][64]
   const int t = threadIdx.x;
   const int p = L.p;
   const int cand_start = L.Q - L.C * L.S;
+  auto put_row = [&](int row, int tok, int pos, int role, int level, int col, int cand, int off, int br) {
+    o.tok[row] = tok;
+    o.pos[row] = pos;
+    o.role[row] = role;
+    o.level[row] = level;
+    o.col[row] = col;
+    o.cand[row] = cand;
+    o.off[row] = off;
+    o.branch[row] = br;
+    s_pos[row] = pos;
+    s_br[row] = br;
+  };
+  auto put_path = [&](int b, int e, int v) {
+    o.path[(size_t)b * L.maxp + e] = v;
+    s_path[(size_t)b * L.maxp + e] = v;
+  };
   // columns
   for (int j = t; j < L.n_cols; j += blockDim.x) {
     const int cs = d_col_start(L, j);
     const int depth = d_depth(L, j);
-    // b_j
-    o.tok[cs] = j == 0 ? x_t : win[j - 1];
-    o.pos[cs] = p + j;
-    o.role[cs] = j == 0 ? 0 : 1;
-    o.level[cs] = 0;
-    o.col[cs] = j;
-    o.cand[cs] = -1;
-    o.off[cs] = -1;
-    o.branch[cs] = j;
-    for (int r = 1; r <= depth; ++r) {
-      const int row = cs + r;
-      o.tok[row] = win[r * win_stride + (j - L.starts[r])];
-      o.pos[row] = p + j + r;
-      o.role[row] = 1;
-      o.level[row] = r;
-      o.col[row] = j;
-      o.cand[row] = -1;
-      o.off[row] = -1;
-      o.branch[row] = j;
-    }
-    int32_t* pth = o.path + (size_t)j * L.maxp;
-    for (int k = 0; k < j; ++k) pth[k] = d_col_start(L, k + 1) - 1;
-    for (int r = 1; r <= depth; ++r) pth[j + r - 1] = cs + r - 1;
+    put_row(cs, j == 0 ? x_t : win[j - 1], p + j, j == 0 ? 0 : 1, 0, j, -1, -1, j);   // b_j
+    for (int r = 1; r <= depth; ++r)
+      put_row(cs + r, win[r * win_stride + (j - L.starts[r])], p + j + r, 1, r, j, -1, -1, j);
+    for (int k = 0; k < j; ++k) put_path(j, k, d_col_start(L, k + 1) - 1);
+    for (int r = 1; r <= depth; ++r) put_path(j, j + r - 1, cs + r - 1);
     o.path_len[j] = j + depth;
+    s_plen[j] = j + depth;
   }
   // candidates
   for (int c = t; c < L.C; c += blockDim.x) {
     const int b = L.n_cols + c;
     for (int s = 0; s < L.S; ++s) {
       const int row = cand_start + c * L.S + s;
-      o.tok[row] = cands[c * L.S + s];
-      o.pos[row] = p + 1 + s;
-      o.role[row] = 2;
-      o.level[row] = -1;
-      o.col[row] = -1;
-      o.cand[row] = c;
-      o.off[row] = s;
-      o.branch[row] = b;
-      o.path[(size_t)b * L.maxp + s] = row - 1;
+      put_row(row, cands[c * L.S + s], p + 1 + s, 2, -1, -1, c, s, b);
+      put_path(b, s, row - 1);
     }
     o.path_len[b] = L.S;
+    s_plen[b] = L.S;
   }
   // logit rows: out, inp (deepest level, column order), guess ((c, s) order)
   int deepest = 0;
@@ -143,9 +151,9 @@ __global__ void __launch_bounds__(256) build_rows_kernel(LaLayout L, int x_t, co
   const int nw = L.mask_words;
   for (int idx = t; idx < L.Q * nw; idx += blockDim.x) {
     const int i = idx / nw, w = idx % nw;
-    const int pi = o.pos[i];
-    const int32_t* pth = o.path + (size_t)o.branch[i] * L.maxp;
-    const int plen = o.path_len[o.branch[i]];
+    const int pi = s_pos[i];
+    const int32_t* pth = s_path + (size_t)s_br[i] * L.maxp;
+    const int plen = s_plen[s_br[i]];
     uint32_t bits = 0;
     for (int b = 0; b < 32; ++b) {
       const int k = w * 32 + b;
@@ -153,7 +161,7 @@ __global__ void __launch_bounds__(256) build_rows_kernel(LaLayout L, int x_t, co
       bool vis;
       if (k == 0) vis = true;
       else {
-        const int pk = o.pos[k];
+        const int pk = s_pos[k];
         const int e = pk - p - 1;
         vis = pk <= pi && e >= 0 && e < plen && pth[e] == k - 1;
       }
@@ -164,12 +172,11 @@ __global__ void __launch_bounds__(256) build_rows_kernel(LaLayout L, int x_t, co
   // per 16-row tile: its distinct branches in row order (rows are branch
   // major, so a tile holds a few consecutive runs) and their paths, which
   // the attention kernel stages for the keys past the committed prefix
-  const int ntiles = (L.Q + 15) / 16;
   for (int tt = t; tt < ntiles; tt += blockDim.x) {
-    int32_t* meta = o.tile_meta + (size_t)tt * 64;
+    int32_t* meta = s_meta + (size_t)tt * 64;
     int nb = 0;
     for (int i = 16 * tt; i < 16 * tt + 16 && i < L.Q; ++i) {
-      const int b = o.branch[i];
+      const int b = s_br[i];
       bool seen = false;
       for (int k = 0; k < nb; ++k) seen |= meta[1 + k] == b;
       if (!seen) meta[1 + nb++] = b;
@@ -178,20 +185,27 @@ __global__ void __launch_bounds__(256) build_rows_kernel(LaLayout L, int x_t, co
     for (int k = 1 + nb; k < 64; ++k) meta[k] = -1;
   }
   __syncthreads();
+  for (int idx = t; idx < ntiles * 64; idx += blockDim.x) o.tile_meta[idx] = s_meta[idx];
   for (int idx = t; idx < ntiles * 1024; idx += blockDim.x) {
     const int tt = idx / 1024, i = (idx / 64) % 16, e = idx % 64;
-    const int32_t* meta = o.tile_meta + (size_t)tt * 64;
+    const int32_t* meta = s_meta + (size_t)tt * 64;
     int v = -1;
     if (i < meta[0]) {
       const int b = meta[1 + i];
-      if (e < o.path_len[b] && e < L.maxp) v = o.path[(size_t)b * L.maxp + e];
+      if (e < s_plen[b] && e < L.maxp) v = s_path[(size_t)b * L.maxp + e];
       if (v < 0 || v >= L.Q - 1) v = -1;
     }
     o.tile_path[idx] = v;
   }
 }
 
-void la_build_rows_launch(const LaLayout& L, int x_t, const int32_t* win, int win_stride, const int32_t* cands,
-                          LaRowsDev rows, hipStream_t st) {
-  hipLaunchKernelGGL(build_rows_kernel, dim3(1), dim3(256), 0, st, L, x_t, win, win_stride, cands, rows);
+int la_build_rows_launch(const LaLayout& L, int x_t, const int32_t* win, int win_stride, const int32_t* cands,
+                         LaRowsDev rows, hipStream_t st) {
+  const size_t lds = rows_lds_bytes(L);
+  if (lds > LDS_BYTES) return -2;
+  static const bool attr = hipFuncSetAttribute((const void*)&build_rows_kernel,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES) == hipSuccess;
+  (void)attr;
+  hipLaunchKernelGGL(build_rows_kernel, dim3(1), dim3(256), lds, st, L, x_t, win, win_stride, cands, rows);
+  return 0;
 }
