@@ -75,6 +75,13 @@ struct la_ctx {
   std::vector<Mark> marks;      // recorded this round
   std::vector<hipEvent_t> evpool;
   size_t evnext = 0;
+  // the next round's pool lookup, started by la_commit: its count and
+  // candidates land in pinned host memory (lk_key: the key, -1: none)
+  int32_t* lk_host = nullptr;   // [1 + 64 * LA_MAX_N]
+  int lk_key = -1;
+  ~la_ctx() {
+    if (lk_host) (void)hipHostFree(lk_host);
+  }
 };
 
 static hipEvent_t prof_event(la_ctx* c) {
@@ -450,6 +457,11 @@ extern "C" int la_init(const la_config* cfg, const la_model_dims* dims, const la
   c->kc = (char*)kv;
   c->vc = (char*)kv + kvb;
   carve(c, (char*)arena);
+  if (hipHostMalloc((void**)&c->lk_host, (1 + 64 * LA_MAX_N) * sizeof(int32_t), hipHostMallocDefault) != hipSuccess) {
+    c->lk_host = nullptr;
+    delete c;
+    return fail(nullptr, LA_EDEVICE, "pinned host buffer");
+  }
   memset(&c->stats, 0, sizeof c->stats);
   for (int r = 0; r < LA_MAX_N; ++r) c->sizes[r] = 0;
   c->cur = 0;
@@ -539,6 +551,16 @@ static bool is_warm(const la_ctx* c) {
   return true;
 }
 
+// Pool lookup of key into c->cand / c->ncand, with the count and all G
+// candidate slots copied to the pinned host buffer (read after a sync).
+static int start_lookup(la_ctx* c, int key) {
+  la_pool_lookup_launch(c->pool_cnt, c->pool_ent, key, c->cfg.G, c->S, c->cand, c->ncand, c->st);
+  HIPCHK(c, hipMemcpyAsync(c->lk_host, c->ncand, 4, hipMemcpyDeviceToHost, c->st));
+  HIPCHK(c, hipMemcpyAsync(c->lk_host + 1, c->cand, (size_t)c->cfg.G * c->S * 4, hipMemcpyDeviceToHost, c->st));
+  c->lk_key = key;
+  return LA_OK;
+}
+
 extern "C" int la_predict(la_ctx* c, la_round_info* info) {
   if (!c) return fail(nullptr, LA_EINVAL, "null ctx");
   if (c->pending) return fail(c, LA_ESTATE, "round %d is pending commit", c->round_id + 1);
@@ -550,15 +572,18 @@ extern "C" int la_predict(la_ctx* c, la_round_info* info) {
   int C = 0;
   c->cand_host.clear();
   if (warm && c->cfg.G > 0) {
-    la_pool_lookup_launch(c->pool_cnt, c->pool_ent, x_t, c->cfg.G, c->S, c->cand, c->ncand, c->st);
-    int32_t nc = 0;
-    HIPCHK(c, hipMemcpyAsync(&nc, c->ncand, 4, hipMemcpyDeviceToHost, c->st));
-    HIPCHK(c, hipStreamSynchronize(c->st));
-    C = nc;
-    if (C > 0) {
-      c->cand_host.resize((size_t)C * c->S);
-      HIPCHK(c, hipMemcpyAsync(c->cand_host.data(), c->cand, (size_t)C * c->S * 4, hipMemcpyDeviceToHost, c->st));
+    // usually started by the last commit (same key, pool unchanged since)
+    if (c->lk_key != x_t) {
+      const int rc = start_lookup(c, x_t);
+      if (rc) return rc;
     }
+    c->lk_key = -1;
+    HIPCHK(c, hipStreamSynchronize(c->st));
+    C = c->lk_host[0];
+    if (C < 0 || C > c->cfg.G) return fail(c, LA_EDEVICE, "pool lookup returned %d candidates", C);
+    c->cand_host.assign(c->lk_host + 1, c->lk_host + 1 + (size_t)C * c->S);
+  } else {
+    c->lk_key = -1;
   }
   LaLayout L{};
   L.p = p; L.R = c->R; L.C = C; L.S = c->S;
@@ -692,6 +717,11 @@ extern "C" int la_commit(la_ctx* c, const la_accept* a) {
   c->stats.candidates += L.C;
   c->stats.accepted += a->h;
   if (a->n_emit < LA_MAX_EMIT) c->stats.hist[a->n_emit] += 1;
+  // the next round's lookup goes out now, so the host's way back to the
+  // next la_predict overlaps it
+  c->lk_key = -1;
+  if (!c->cfg.ar_only && c->cfg.G > 0 && is_warm(c) && (int)c->out.size() < c->cfg.max_new)
+    (void)start_lookup(c, c->out.back());   // published already; a failed start is retried by la_predict
   return LA_OK;
 }
 
@@ -748,6 +778,7 @@ extern "C" int la_pool_lookup(la_ctx* c, int32_t key, int32_t* out, int32_t* n) 
 }
 
 extern "C" int la_pool_insert(la_ctx* c, const int32_t* keys, const int32_t* suffixes, int32_t n) {
+  if (c) c->lk_key = -1;   // a lookup started by the last commit no longer sees the pool as it will be
   if (!c || (n > 0 && (!keys || !suffixes))) return fail(c, LA_EINVAL, "null argument");
   if (n < 0 || n > 64) return fail(c, LA_EINVAL, "n=%d outside [0, 64] per call", n);
   if (c->pending) return fail(c, LA_ESTATE, "a predicted round is pending");
