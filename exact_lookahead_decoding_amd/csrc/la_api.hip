@@ -144,6 +144,8 @@ static int validate_cfg(const la_config* cfg, const la_model_dims* d, la_ctx* c)
   if (cfg->verify_mode != LA_VERIFY_GREEDY && cfg->verify_mode != LA_VERIFY_SAMPLE)
     return fail(c, LA_EINVAL, "verify_mode %d", cfg->verify_mode);
   if (cfg->verify_mode == LA_VERIFY_SAMPLE && !(cfg->temperature > 0.0)) return fail(c, LA_EINVAL, "temperature must be > 0");
+  if (cfg->pool_from_prompt != 0 && cfg->pool_from_prompt != 1)
+    return fail(c, LA_EINVAL, "pool_from_prompt %d (0 or 1)", cfg->pool_from_prompt);
   if (d->dtype != LA_DTYPE_F32 && d->dtype != LA_DTYPE_BF16) return fail(c, LA_EINVAL, "dtype %d", d->dtype);
   if (d->n_layers < 1 || d->d_model < 16 || d->n_heads < 1 || d->n_kv_heads < 1 || d->n_heads % d->n_kv_heads)
     return fail(c, LA_EINVAL, "bad model dims");
@@ -476,6 +478,23 @@ extern "C" int la_init(const la_config* cfg, const la_model_dims* dims, const la
   } while (0)
   la_rope_table_launch(c->rope, c->rope_rows, c->dh, c->dims.rope_theta, c->st);
   la_pool_clear_launch(c->pool_cnt, c->V, c->st);
+  // POOL_FROM_PROMPT: the prompt's N-grams in order, through the candidate
+  // scratch in chunks (one wavefront upserts them serially, the LRU rule)
+  if (c->cfg.pool_from_prompt && !c->cfg.ar_only && c->cfg.G > 0) {
+    const int S = c->S, per = (64 * LA_MAX_N) / (1 + S);
+    std::vector<int32_t> buf;
+    for (int i0 = 0; i0 + S < prompt_len; i0 += per) {
+      const int n = std::min(per, prompt_len - S - i0);
+      buf.assign((size_t)n * (1 + S), 0);
+      for (int i = 0; i < n; ++i) {
+        buf[i] = prompt[i0 + i];
+        for (int s = 0; s < S; ++s) buf[n + (size_t)i * S + s] = prompt[i0 + i + 1 + s];
+      }
+      CK(hipMemcpyAsync(c->vcand, buf.data(), buf.size() * 4, hipMemcpyHostToDevice, c->st));
+      la_pool_upsert_launch(c->pool_cnt, c->pool_ent, c->vcand, c->vcand + n, n, c->cfg.G, S, c->st);
+      CK(hipStreamSynchronize(c->st));      // buf is reused
+    }
+  }
   // window: level 0 seeded with the last W + N - 3 prompt tokens (cyclic)
   if (!c->cfg.ar_only) {
     const int n0 = c->cfg.W + c->cfg.N - 3;

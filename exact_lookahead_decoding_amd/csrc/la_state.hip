@@ -56,7 +56,8 @@ __device__ void pool_upsert_one(int32_t* cnt, int32_t* ent, int key, const int* 
     for (int s = 0; s < S; ++s) bucket[(lane - 1) * S + s] = mine[s];
   if (lane < S) bucket[slot * S + lane] = suf[lane];
   if (lane == 0 && !bal && c < G) cnt[key] = c + 1;
-  __threadfence();
+  // the next upsert is this wavefront's own: workgroup scope orders it (no L2 write-back)
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
 }
 
 __global__ void __launch_bounds__(64) pool_upsert_kernel(int32_t* cnt, int32_t* ent, const int32_t* keys,

@@ -88,6 +88,30 @@ def test_tiny_rounds_match_oracle(tiny):
         assert sess.la_pool_lookup(key) == opool.lookup(ref["token_map"], key, G), key
 
 
+@pytest.mark.parametrize("W,N,G", [(5, 3, 5), (4, 4, 2)])
+def test_pool_from_prompt_matches_oracle(tiny, W, N, G):
+    """POOL_FROM_PROMPT: right after la_init the device pool equals the
+    oracle's seeded pool for every key; the generation's rounds (candidates,
+    accepted lengths) and tokens equal the oracle's seeded run, and the
+    tokens still equal autoregressive greedy."""
+    dims, w, dm, om = tiny
+    prompt = synthetic.markov_prompt(dims.vocab, 48, 2)
+    max_new = 40
+    seeded = {}
+    opool.seed_pool_from_prompt(seeded, prompt, N, G)
+    sess = la.Session(dm, prompt, W=W, N=N, G=G, max_new=max_new, pool_from_prompt=True)
+    for key in range(dims.vocab):
+        assert sess.la_pool_lookup(key) == opool.lookup(seeded, key, G), key
+    ref = lookahead_generate(om, prompt, W, N, G, max_new, pool_from_prompt=True)
+    for k, rr in enumerate(ref["rounds"]):
+        info = sess.la_predict()
+        assert info.C == len(rr.candidates), k
+        acc, _ = sess.la_verify()
+        assert (acc.h, acc.winner) == (rr.h, rr.winner), k
+        sess.la_commit(acc)
+    assert sess.la_get_state()["output"] == ref["tokens"] == ar_generate(om, prompt, max_new)
+
+
 @pytest.mark.parametrize("W,N,G", [(5, 3, 5), (4, 4, 3), (7, 5, 7)])
 def test_tiny_generate_equals_ar(tiny, W, N, G):
     dims, w, dm, om = tiny
