@@ -146,6 +146,8 @@ static int validate_cfg(const la_config* cfg, const la_model_dims* d, la_ctx* c)
   if (cfg->verify_mode == LA_VERIFY_SAMPLE && !(cfg->temperature > 0.0)) return fail(c, LA_EINVAL, "temperature must be > 0");
   if (cfg->pool_from_prompt != 0 && cfg->pool_from_prompt != 1)
     return fail(c, LA_EINVAL, "pool_from_prompt %d (0 or 1)", cfg->pool_from_prompt);
+  if (cfg->advance_by_accepted != 0 && cfg->advance_by_accepted != 1)
+    return fail(c, LA_EINVAL, "advance_by_accepted %d (0 or 1)", cfg->advance_by_accepted);
   if (d->dtype != LA_DTYPE_F32 && d->dtype != LA_DTYPE_BF16) return fail(c, LA_EINVAL, "dtype %d", d->dtype);
   if (d->n_layers < 1 || d->d_model < 16 || d->n_heads < 1 || d->n_kv_heads < 1 || d->n_heads % d->n_kv_heads)
     return fail(c, LA_EINVAL, "bad model dims");
@@ -718,8 +720,10 @@ extern "C" int la_commit(la_ctx* c, const la_accept* a) {
       for (int r = 0; r <= deepest; ++r) nsz[r] = c->sizes[r] - 1;
       nsz[deepest + 1] = c->sizes[deepest] - (deepest >= 1 ? 1 : 0);
     }
+    // ALWAYS_FWD_ONE=False: the h accepted tokens move the live position h further
+    const int shift = c->cfg.advance_by_accepted ? a->h : 0;
     la_window_next_launch(c->win[c->cur], c->win[c->cur ^ 1], c->wstride, c->R, c->sizes, nsz, deepest, warm ? 1 : 0,
-                          c->z, L.n_inp, c->st);
+                          c->z, L.n_inp, shift, a->emitted[a->n_emit - 1], c->st);
     HIPCHK(c, hipGetLastError());
     c->cur ^= 1;
     for (int r = 0; r < c->R; ++r) c->sizes[r] = nsz[r];

@@ -146,8 +146,10 @@ void la_pool_collect_launch(int32_t* cnt, int32_t* ent, int x_t, const int32_t* 
                             int W, const int32_t* z, int G, hipStream_t st);
 
 // window and commit
+// warm: shift > 0 slices every advanced level by shift and refills its tail with fill (ALWAYS_FWD_ONE=False)
 void la_window_next_launch(const int32_t* win, int32_t* out, int stride, int R, const int* sizes_old,
-                           const int* sizes_new, int deepest, int warm, const int32_t* z, int nz, hipStream_t st);
+                           const int* sizes_new, int deepest, int warm, const int32_t* z, int nz, int shift, int fill,
+                           hipStream_t st);
 void la_kv_commit_launch(int dtype, void* kc, void* vc, const void* kw, const void* vw, int L, int Hkv, int dh,
                          int T_cap, int ws_cap, int dst_row0, int src_row0, int h, hipStream_t st);
 void la_fill_i32_launch(int32_t* p, int n, int v, hipStream_t st);

@@ -113,16 +113,21 @@ struct WinArgs {
   int so[16], sn[16];
 };
 
+// steady state: entry i of the advanced level r is entry i + shift of the
+// pinned advance (level 0 <- level 1 from its second entry, level r <- r + 1,
+// the deepest <- z), or `fill` past its end (shift 0: the pinned advance)
 __global__ void window_next_kernel(const int32_t* win, int32_t* out, int stride, int R, WinArgs sz, int deepest,
-                                   int warm, const int32_t* z, int nz) {
+                                   int warm, const int32_t* z, int nz, int shift, int fill) {
   for (int idx = threadIdx.x; idx < R * stride; idx += blockDim.x) {
     const int r = idx / stride, i = idx % stride;
     int v = 0;
     if (i < sz.sn[r]) {
       if (warm) {
-        if (r == 0) v = win[1 * stride + i + 1];
-        else if (r < R - 1) v = win[(r + 1) * stride + i];
-        else v = z[i];
+        const int k = i + shift;
+        if (k >= sz.sn[r]) v = fill;
+        else if (r == 0) v = win[1 * stride + k + 1];
+        else if (r < R - 1) v = win[(r + 1) * stride + k];
+        else v = z[k];
       } else {
         if (r <= deepest) v = win[r * stride + i + 1];
         else if (r == deepest + 1) v = deepest >= 1 ? z[i + 1] : z[i];
@@ -133,13 +138,15 @@ __global__ void window_next_kernel(const int32_t* win, int32_t* out, int stride,
 }
 
 void la_window_next_launch(const int32_t* win, int32_t* out, int stride, int R, const int* sizes_old,
-                           const int* sizes_new, int deepest, int warm, const int32_t* z, int nz, hipStream_t st) {
+                           const int* sizes_new, int deepest, int warm, const int32_t* z, int nz, int shift,
+                           int fill, hipStream_t st) {
   WinArgs a;
   for (int r = 0; r < 16; ++r) {
     a.so[r] = r < R ? sizes_old[r] : 0;
     a.sn[r] = r < R ? sizes_new[r] : 0;
   }
-  hipLaunchKernelGGL(window_next_kernel, dim3(1), dim3(256), 0, st, win, out, stride, R, a, deepest, warm, z, nz);
+  hipLaunchKernelGGL(window_next_kernel, dim3(1), dim3(256), 0, st, win, out, stride, R, a, deepest, warm, z, nz,
+                     warm ? shift : 0, fill);
 }
 
 // ---------------------------------------------------------------- K/V commit

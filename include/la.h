@@ -113,7 +113,11 @@ typedef struct la_config {
                                ("M7.3", 0x02B POOL_FROM_PROMPT): for i = 0, 1, ... while
                                i + N - 1 < prompt_len, key prompt[i] and suffix
                                prompt[i+1 .. i+N-1], by the per-key LRU rule (0x03B); 0: off */
-  int32_t reserved[2];
+  int32_t advance_by_accepted; /* 1: ALWAYS_FWD_ONE=False window schedule (0x03C alternative):
+                               after the pinned one-column advance every level drops its first
+                               h entries and its tail is refilled with the newest committed
+                               token; 0: ALWAYS_FWD_ONE=True (pinned) */
+  int32_t reserved[1];
 } la_config;
 
 /* Buffer sizes for a (config, dims) pair.  The caller allocates

@@ -8,7 +8,11 @@
   new, deeper level, the new level dropping its first output where needed
   (N=4, W=5: [6,-,-] -> [5,6,-] -> [4,5,5]); no verification meanwhile;
 * 0x03C -- steady advance with ALWAYS_FWD_ONE: new window is
-  [past[1][1:]] + past[2:] + [z], keeping the ragged sizes [W-1, W, ..., W].
+  [past[1][1:]] + past[2:] + [z], keeping the ragged sizes [W-1, W, ..., W];
+  its alternative (ALWAYS_FWD_ONE=False) slices each level by the accepted
+  count and refills the tail (0x03C, 0x06 "drop positions consumed by
+  committed output, shift the remaining future slots left, refill vacated
+  slots from the configured seed/reset source").
 
 Readings (the pages leave these open):
 * initial level-0 content: "seeds lookahead slots from prompt tokens" is
@@ -16,7 +20,14 @@ Readings (the pages leave these open):
 * "drops its first output where needed" is read as: the new level drops its
   first output exactly when the level it was computed from has index >= 1
   (the only reading that reproduces [5,6,-] -> [4,5,5] and keeps every cell
-  at the position it was predicted for).
+  at the position it was predicted for);
+* ALWAYS_FWD_ONE=False: after the pinned advance, which accounts for the
+  one position every round publishes, each level drops its first h entries
+  (the h accepted tokens moved the live position h further) and appends h
+  copies of the newest committed token (the page lists "copy the last
+  token" among the seed choices); the ragged sizes are kept, and every
+  surviving cell stays at the position it was predicted for.  Warmup fills
+  are unchanged.
 """
 from __future__ import annotations
 
@@ -86,8 +97,21 @@ def advance_pinned_window(window, z, N, W):
     return [list(window[1])[1:], *promoted, list(z)]
 
 
-def next_window(window, z, N, W):
-    """Warmup fill while levels are missing, otherwise the steady advance."""
+def advance_by_accepted(window, z, N, W, h: int, fill: int):
+    """ALWAYS_FWD_ONE=False: the pinned advance, then every level drops its
+    first h entries and its tail is refilled with `fill`."""
+    out = []
+    for lv in advance_pinned_window(window, z, N, W):
+        k = min(int(h), len(lv))
+        out.append(lv[k:] + [int(fill)] * k)
+    return out
+
+
+def next_window(window, z, N, W, h: int = 0, fill=None):
+    """Warmup fill while levels are missing, otherwise the steady advance
+    (by the accepted count h when `fill` is given, ALWAYS_FWD_ONE=False)."""
     if is_warm(window):
+        if fill is not None:
+            return advance_by_accepted(window, z, N, W, h, fill)
         return advance_pinned_window(window, z, N, W)
     return fill_window(window, z)

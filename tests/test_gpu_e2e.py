@@ -112,6 +112,30 @@ def test_pool_from_prompt_matches_oracle(tiny, W, N, G):
     assert sess.la_get_state()["output"] == ref["tokens"] == ar_generate(om, prompt, max_new)
 
 
+@pytest.mark.parametrize("W,N,G,seed", [(5, 3, 5, 0), (4, 4, 3, 1)])
+def test_advance_by_accepted_matches_oracle(tiny, W, N, G, seed):
+    """ALWAYS_FWD_ONE=False window schedule: every round (candidates, accepted
+    length, winner), the final window and pool equal the oracle's run of the
+    same schedule, and the tokens still equal autoregressive greedy."""
+    dims, w, dm, om = tiny
+    prompt = synthetic.markov_prompt(dims.vocab, 32, seed)
+    max_new = 64
+    ref = lookahead_generate(om, prompt, W, N, G, max_new, advance_by_accepted=True)
+    assert sum(1 for rr in ref["rounds"] if rr.h > 0) > 0        # the slice is exercised
+    sess = la.Session(dm, prompt, W=W, N=N, G=G, max_new=max_new, advance_by_accepted=True)
+    for k, rr in enumerate(ref["rounds"]):
+        info = sess.la_predict()
+        assert info.C == len(rr.candidates), k
+        acc, _ = sess.la_verify()
+        assert (acc.h, acc.winner) == (rr.h, rr.winner), k
+        sess.la_commit(acc)
+    st = sess.la_get_state()
+    assert st["output"] == ref["tokens"] == ar_generate(om, prompt, max_new)
+    assert st["levels"] == ref["window"]
+    for key in range(dims.vocab):
+        assert sess.la_pool_lookup(key) == opool.lookup(ref["token_map"], key, G), key
+
+
 @pytest.mark.parametrize("W,N,G", [(5, 3, 5), (4, 4, 3), (7, 5, 7)])
 def test_tiny_generate_equals_ar(tiny, W, N, G):
     dims, w, dm, om = tiny
