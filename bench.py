@@ -22,6 +22,8 @@ Also reported on the same line:
     exceed the 256 MB Infinity Cache;
   * lookahead_attn_8192: the same op over 8192 committed keys (the
     long-prefix workload's per-layer shape, 134 MB of K/V per call);
+  * lookahead_attn_34b_gqa: the op at the 34B-shaped round's per-layer shape
+    (64 query heads on 8 KV heads, N=7: 180 rows, 2048 committed keys);
   * ar_tokens_per_s: plain autoregressive decoding with the same kernels;
   * cpu_baseline: the CPU oracle on a bounded sample of the same workload.
 """
@@ -88,19 +90,23 @@ def run_steps(make_session, sess, steps):
     return tokens, elapsed, sess, done
 
 
-def attention_op(reps=200, sets=16, p=1024):
-    """Isolated lookahead-mask attention (W=15, N=5, G=15: 121 rows, 32 heads x 128, bf16) over a
-    committed prefix of p keys, rotating input sets (more bytes than the 256 MB Infinity Cache)."""
+def attention_op(reps=200, sets=16, p=1024, H=32, Hkv=32, N=5):
+    """Isolated lookahead-mask attention (W=15, G=15, bf16, head dim 128) over a committed prefix
+    of p keys, rotating input sets (more bytes than the 256 MB Infinity Cache).  N=5, 32 heads:
+    the rectangular window of the config, 121 rows; N=7 with 64 query heads on 8 KV heads: the
+    34B-shaped round's pinned layout ([14, 15, 15, 15, 15, 15] + 15 x 6 candidate rows = 180)."""
     import numpy as np
     import torch
     import exact_lookahead_decoding_amd.la as la
-    H = Hkv = 32
-    dh, S = 128, 4
-    levels = [list(range(100, 115))] * 4
-    desc = la.rows_desc(p, levels, S, 15, 7, 16, starts=[1, 1, 1, 1])
-    win = torch.zeros((4, 16), dtype=torch.int32, device="cuda")
+    dh, S, R = 128, N - 1, N - 1
+    if N == 5:
+        levels, starts = [list(range(100, 115))] * 4, [1, 1, 1, 1]
+    else:
+        levels, starts = [list(range(100, 114))] + [list(range(100, 115))] * (R - 1), [1] + [0] * (R - 1)
+    desc = la.rows_desc(p, levels, S, 15, 7, 16, starts=starts)
+    win = torch.zeros((R, 16), dtype=torch.int32, device="cuda")
     win[:, :15] = torch.arange(100, 115, dtype=torch.int32, device="cuda")
-    cand = torch.arange(60, dtype=torch.int32, device="cuda")
+    cand = torch.arange(15 * S, dtype=torch.int32, device="cuda")
     rows, info = la.la_build_rows(desc, win, cand)
     Q = info.Q
     g = torch.Generator(device="cuda").manual_seed(0)
@@ -133,7 +139,8 @@ def attention_op(reps=200, sets=16, p=1024):
     alg = 2 * Hkv * p * dh * 2 + Q * Hkv * dh * 2 * 2 + 2 * Q * H * dh * 2
     gbs = alg / (ms * 1e-3) / 1e9
     kv_gbs = (2 * Hkv * p * dh * 2) / (ms * 1e-3) / 1e9
-    return {"workload": f"lookahead-mask attention, bf16, 32 heads x 128, prefix {p}, {Q} rows (W=15 N=5 G=15)",
+    heads = f"{H} heads" if H == Hkv else f"{H} query heads on {Hkv} KV heads"
+    return {"workload": f"lookahead-mask attention, bf16, {heads} x 128, prefix {p}, {Q} rows (W=15 N={N} G=15)",
             "avg_us": ms * 1e3, "algorithmic_bytes": alg, "achieved_GBps": gbs, "kv_stream_GBps": kv_gbs,
             "peak_GBps": HBM_PEAK_GBS, "frac": gbs / HBM_PEAK_GBS, "reps": reps, "input_sets": sets}
 
@@ -310,6 +317,7 @@ def main():
         torch.cuda.set_device(0)
         print(json.dumps(attention_op()), flush=True)
         print(json.dumps(attention_op(reps=24, sets=4, p=8192)), flush=True)
+        print(json.dumps(attention_op(reps=64, sets=32, p=2048, H=64, Hkv=8, N=7)), flush=True)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the lookahead round runs on a single MI355X (got --gpus {args.gpus}); "
@@ -388,6 +396,11 @@ def main():
         log(f"lookahead attention op, prefix 8192: {a['avg_us']:.2f} us, {a['achieved_GBps']:.0f} GB/s "
             f"({a['frac'] * 100:.1f}%)")
         line["lookahead_attn_8192"] = a
+        # the 34B-shaped round's attention: 64 query heads on 8 KV heads, 180 rows, 2048 keys
+        a = attention_op(reps=64, sets=32, p=2048, H=64, Hkv=8, N=7)
+        log(f"lookahead attention op, 34B GQA shape: {a['avg_us']:.2f} us, {a['achieved_GBps']:.0f} GB/s "
+            f"({a['frac'] * 100:.1f}%)")
+        line["lookahead_attn_34b_gqa"] = a
     if not args.no_cpu_baseline:
         t = time.time()
         line["cpu_baseline"] = cpu_baseline(wl)
