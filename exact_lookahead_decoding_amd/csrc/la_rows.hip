@@ -72,11 +72,7 @@ __device__ static int d_depth(const LaLayout& L, int j) {
     if (d_level_at(L, r, j)) d = r;
   return d;
 }
-__device__ static int d_col_start(const LaLayout& L, int j) {
-  int s = 0;
-  for (int k = 0; k < j; ++k) s += 1 + d_depth(L, k);
-  return s;
-}
+#define LA_MAX_COLS 128   // window columns the builder's tables hold (W + N - 2 <= 64 + 14)
 
 // LDS mirrors of what the later phases read back (positions, branches,
 // paths, tile tables), so the mask and tile phases do no global loads
@@ -97,6 +93,19 @@ __global__ void __launch_bounds__(256) build_rows_kernel(LaLayout L, int x_t, co
   const int t = threadIdx.x;
   const int p = L.p;
   const int cand_start = L.Q - L.C * L.S;
+  // column depths and first rows, once (the layout's level table is read per column here only)
+  __shared__ int s_depth[LA_MAX_COLS], s_cs[LA_MAX_COLS + 1];
+  for (int j = t; j < L.n_cols; j += blockDim.x) s_depth[j] = d_depth(L, j);
+  __syncthreads();
+  if (t == 0) {
+    int acc = 0;
+    for (int j = 0; j < L.n_cols; ++j) {
+      s_cs[j] = acc;
+      acc += 1 + s_depth[j];
+    }
+    s_cs[L.n_cols] = acc;
+  }
+  __syncthreads();
   auto put_row = [&](int row, int tok, int pos, int role, int level, int col, int cand, int off, int br) {
     o.tok[row] = tok;
     o.pos[row] = pos;
@@ -115,12 +124,12 @@ __global__ void __launch_bounds__(256) build_rows_kernel(LaLayout L, int x_t, co
   };
   // columns
   for (int j = t; j < L.n_cols; j += blockDim.x) {
-    const int cs = d_col_start(L, j);
-    const int depth = d_depth(L, j);
+    const int cs = s_cs[j];
+    const int depth = s_depth[j];
     put_row(cs, j == 0 ? x_t : win[j - 1], p + j, j == 0 ? 0 : 1, 0, j, -1, -1, j);   // b_j
     for (int r = 1; r <= depth; ++r)
       put_row(cs + r, win[r * win_stride + (j - L.starts[r])], p + j + r, 1, r, j, -1, -1, j);
-    for (int k = 0; k < j; ++k) put_path(j, k, d_col_start(L, k + 1) - 1);
+    for (int k = 0; k < j; ++k) put_path(j, k, s_cs[k + 1] - 1);
     for (int r = 1; r <= depth; ++r) put_path(j, j + r - 1, cs + r - 1);
     o.path_len[j] = j + depth;
     s_plen[j] = j + depth;
@@ -143,31 +152,29 @@ __global__ void __launch_bounds__(256) build_rows_kernel(LaLayout L, int x_t, co
   if (t == 0) o.logit_rows[0] = 0;
   for (int i = t; i < L.n_inp; i += blockDim.x) {
     const int j = deepest == 0 ? 1 + i : L.starts[deepest] + i;
-    o.logit_rows[1 + i] = d_col_start(L, j) + deepest;
+    o.logit_rows[1 + i] = s_cs[j] + deepest;
   }
   for (int i = t; i < L.C * L.S; i += blockDim.x) o.logit_rows[1 + L.n_inp + i] = cand_start + i;
   __syncthreads();
-  // compact visibility mask, derived from the paths
+  // compact visibility mask, derived from the paths: one bit per lane (row
+  // i, word w, bit b at index (i * nw + w) * 32 + b), the wave's ballot gives
+  // two whole words (the loop steps whole waves, so words never straddle)
   const int nw = L.mask_words;
-  for (int idx = t; idx < L.Q * nw; idx += blockDim.x) {
-    const int i = idx / nw, w = idx % nw;
-    const int pi = s_pos[i];
-    const int32_t* pth = s_path + (size_t)s_br[i] * L.maxp;
-    const int plen = s_plen[s_br[i]];
-    uint32_t bits = 0;
-    for (int b = 0; b < 32; ++b) {
-      const int k = w * 32 + b;
-      if (k >= L.Q) break;
-      bool vis;
+  const int nbits = L.Q * nw * 32;
+  for (int base = t - (t & 63); base < nbits; base += blockDim.x) {
+    const int idx = base + (t & 63);
+    bool vis = false;
+    if (idx < nbits) {
+      const int i = idx / (nw * 32), k = idx % (nw * 32);
       if (k == 0) vis = true;
-      else {
-        const int pk = s_pos[k];
-        const int e = pk - p - 1;
-        vis = pk <= pi && e >= 0 && e < plen && pth[e] == k - 1;
+      else if (k < L.Q) {
+        const int pk = s_pos[k], e = pk - p - 1;
+        const int bi = s_br[i];
+        vis = pk <= s_pos[i] && e >= 0 && e < s_plen[bi] && s_path[(size_t)bi * L.maxp + e] == k - 1;
       }
-      if (vis) bits |= 1u << b;
     }
-    o.mask[(size_t)i * nw + w] = bits;
+    const unsigned long long m = __ballot(vis);
+    if ((t & 31) == 0 && idx < nbits) o.mask[idx / 32] = (uint32_t)(m >> (t & 32));
   }
   // per 16-row tile: its distinct branches in row order (rows are branch
   // major, so a tile holds a few consecutive runs) and their paths, which
@@ -202,10 +209,13 @@ __global__ void __launch_bounds__(256) build_rows_kernel(LaLayout L, int x_t, co
 int la_build_rows_launch(const LaLayout& L, int x_t, const int32_t* win, int win_stride, const int32_t* cands,
                          LaRowsDev rows, hipStream_t st) {
   const size_t lds = rows_lds_bytes(L);
-  if (lds > LDS_BYTES) return -2;
-  static const bool attr = hipFuncSetAttribute((const void*)&build_rows_kernel,
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES) == hipSuccess;
-  (void)attr;
+  constexpr int DYN_MAX = LDS_BYTES - 2048;       // beside the static column tables
+  if (lds > DYN_MAX || L.n_cols > LA_MAX_COLS) return -2;
+  if (lds > 65536) {                              // above the default dynamic limit
+    static const bool attr = hipFuncSetAttribute((const void*)&build_rows_kernel,
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, DYN_MAX) == hipSuccess;
+    if (!attr) return -2;
+  }
   hipLaunchKernelGGL(build_rows_kernel, dim3(1), dim3(256), lds, st, L, x_t, win, win_stride, cands, rows);
   return 0;
 }
