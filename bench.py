@@ -44,6 +44,9 @@ WORKLOADS = {
         "Llama-2-7B-shaped bf16 decoder, 512-token Markov prompt, greedy lookahead W=7 N=5 G=7, 256 new tokens")),
     "llama7b_long_w15n5g15": dict(model="llama7b", W=15, N=5, G=15, prompt=8192, max_new=256, desc=(
         "Llama-2-7B-shaped bf16 decoder, 8192-token Markov prompt, greedy lookahead W=15 N=5 G=15")),
+    "codellama34b_w15n7g15": dict(model="codellama34b", W=15, N=7, G=15, prompt=2048, max_new=256, copyspan=True, desc=(
+        "CodeLlama-34B-shaped bf16 decoder (GQA 64/8 heads), 2048-token Markov prompt with 30% copied spans, "
+        "greedy lookahead W=15 N=7 G=15, 256 new tokens")),
     "tiny_w5n3g5": dict(model="tiny", W=5, N=3, G=5, prompt=32, max_new=64, desc=(
         "tiny fp32 decoder (2 layers, d 64), 32-token Markov prompt, greedy lookahead W=5 N=3 G=5, 64 new tokens")),
 }
@@ -299,6 +302,8 @@ def main():
     ap.add_argument("--workload", default="llama7b_w7n5g7", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-attn", action="store_true")
+    ap.add_argument("--pool-from-prompt", action="store_true",
+                    help="seed the n-gram pool with the prompt's n-grams (lookahead sessions)")
     ap.add_argument("--pmc-sample", action="store_true", help="run the GEMM counter sample (see profiles/)")
     ap.add_argument("--attention-op-only", action="store_true", help="time only the isolated attention op")
     ap.add_argument("--pmc-summary", nargs=3, metavar=("FETCH_DB", "WRITE_DB", "SAMPLE_JSON"),
@@ -333,10 +338,15 @@ def main():
     t = time.time()
     model = la.DeviceModel(dims, seed=0)
     log(f"weights on device: {model.weight_bytes / 1e9:.2f} GB in {time.time() - t:.1f} s")
-    prompt = synthetic.markov_prompt(dims.vocab, wl["prompt"], 0)
+    if wl.get("copyspan"):
+        prompt, copied = synthetic.copyspan_prompt(dims.vocab, wl["prompt"], 0)
+        log(f"prompt: {len(prompt)} tokens, {copied * 100:.1f}% copied spans")
+    else:
+        prompt = synthetic.markov_prompt(dims.vocab, wl["prompt"], 0)
 
     def make(ar=False, profile=False):
-        s = la.Session(model, prompt, W=wl["W"], N=wl["N"], G=wl["G"], max_new=wl["max_new"], ar_only=ar)
+        s = la.Session(model, prompt, W=wl["W"], N=wl["N"], G=wl["G"], max_new=wl["max_new"], ar_only=ar,
+                       pool_from_prompt=args.pool_from_prompt and not ar)
         if profile:
             s.la_profile(True)
         return s
@@ -375,7 +385,8 @@ def main():
         "warmup": args.warmup, "ms_per_step": secs * 1e3 / steps, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16" if dims.dtype == "bf16" else "f32", "data": "synthetic",
         "config": {"workload": wl["desc"], "W": wl["W"], "N": wl["N"], "G": wl["G"], "prompt_tokens": wl["prompt"],
-                   "max_new": wl["max_new"], "verify": "greedy", "batch": 1},
+                   "max_new": wl["max_new"], "verify": "greedy", "batch": 1,
+                   "pool_from_prompt": bool(args.pool_from_prompt)},
         "tokens_per_round": tokens / steps,
         "ar_tokens_per_s": ar_tps,
         "speedup_vs_ar": value / ar_tps,
@@ -401,7 +412,9 @@ def main():
         log(f"lookahead attention op, 34B GQA shape: {a['avg_us']:.2f} us, {a['achieved_GBps']:.0f} GB/s "
             f"({a['frac'] * 100:.1f}%)")
         line["lookahead_attn_34b_gqa"] = a
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and wl["model"] == "codellama34b":
+        log("cpu baseline skipped: the oracle would hold the 34B-shaped weights in host memory")
+    elif not args.no_cpu_baseline:
         t = time.time()
         line["cpu_baseline"] = cpu_baseline(wl)
         log(f"cpu baseline: {line['cpu_baseline']['value']:.4f} tokens/s ({time.time() - t:.0f} s)")
