@@ -240,11 +240,10 @@ def pmc_summary(fetch_db, write_db, sample_json):
         "Commands (run from /tmp with TMPDIR=/tmp on one MI355X; each counter in a run of its own):",
         "",
         "```",
-        "python3 bench.py --pmc-sample > gpurun_out/pmc_sample.json",
-        "rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_fetch -o f -- python3 bench.py --pmc-sample",
-        "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_write -o w -- python3 bench.py --pmc-sample",
-        "python3 bench.py --pmc-summary gpurun_out/pmc_fetch/f_results.db gpurun_out/pmc_write/w_results.db "
-        "gpurun_out/pmc_sample.json",
+        "python3 bench.py --pmc-sample > out/pmc_sample.json",
+        "rocprofv3 --pmc FETCH_SIZE -d out/pmc_fetch -o f -- python3 bench.py --pmc-sample",
+        "rocprofv3 --pmc WRITE_SIZE -d out/pmc_write -o w -- python3 bench.py --pmc-sample",
+        "python3 bench.py --pmc-summary out/pmc_fetch/f_results.db out/pmc_write/w_results.db out/pmc_sample.json",
         "```",
         "",
         f"The sample runs {sample['rounds']} lookahead rounds after prefill, then copies a "

@@ -249,7 +249,7 @@ def test_llama7b_2layer_parity_and_invariance():
     want = om.sequence_logits(seq)
     d = np.abs(lg - want)
     err = d.max()
-    print(f"7B-wide 2-layer: round-1 ordinary-row logits max abs err {err:.3g}, mean {d.mean():.3g}, "
+    print(f"7B-wide 2-layer: first-round ordinary-row logits max abs err {err:.3g}, mean {d.mean():.3g}, "
           f"logit std {want.std():.3g}, argmax gpu {int(np.argmax(lg))} oracle {int(np.argmax(want))}", flush=True)
     assert err <= BF16_2LAYER_LOGIT_TOL
     assert int(np.argmax(lg)) == int(np.argmax(want)) or _top2_gap(want) < 2e-2
