@@ -110,7 +110,7 @@ typedef struct la_config {
   uint64_t seed;            /* sampling: Philox4x32-10 key */
   int32_t max_prompt;       /* capacity planning: longest prompt passed to la_init */
   int32_t pool_from_prompt; /* 1: la_init inserts the prompt's observed N-grams into the pool
-                               ("M7.3", 0x02B POOL_FROM_PROMPT): for i = 0, 1, ... while
+                               ("M7.3", 0x03A POOL_FROM_PROMPT): for i = 0, 1, ... while
                                i + N - 1 < prompt_len, key prompt[i] and suffix
                                prompt[i+1 .. i+N-1], by the per-key LRU rule (0x03B); 0: off */
   int32_t advance_by_accepted; /* 1: ALWAYS_FWD_ONE=False window schedule (0x03C alternative):

@@ -10,7 +10,7 @@
 * 0x03C -- steady advance with ALWAYS_FWD_ONE: new window is
   [past[1][1:]] + past[2:] + [z], keeping the ragged sizes [W-1, W, ..., W];
   its alternative (ALWAYS_FWD_ONE=False) slices each level by the accepted
-  count and refills the tail (0x03C, 0x06 "drop positions consumed by
+  count and refills the tail (0x03C, 0x06C "drop positions consumed by
   committed output, shift the remaining future slots left, refill vacated
   slots from the configured seed/reset source").
 
