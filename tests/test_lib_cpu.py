@@ -45,6 +45,52 @@ def test_invalid_configs_rejected():
         assert e.value.code == la.LA_EINVAL
 
 
+def test_option_flags_validated():
+    """pool_from_prompt and advance_by_accepted are 0 or 1."""
+    d = la.dims_struct(synthetic.PRESETS["tiny"])
+    la.la_query_sizes(la.make_config(5, 3, 5, 10, 10, pool_from_prompt=True, advance_by_accepted=True), d)
+    for field in ("pool_from_prompt", "advance_by_accepted"):
+        cfg = la.make_config(5, 3, 5, 10, 10)
+        setattr(cfg, field, 2)
+        with pytest.raises(la.LaError) as e:
+            la.la_query_sizes(cfg, d)
+        assert e.value.code == la.LA_EINVAL, field
+
+
+def test_attention_rejects_bad_arguments():
+    """Host-side validation of la_attention: every case below is refused before
+    anything is launched (the pointers are never dereferenced)."""
+    import ctypes as C
+    lib = _lib()
+    info = la.la_rows_query(la.rows_desc(100, [list(range(4)), list(range(5))], 2, 2, 1, 8, [1, 0]))
+    fake = C.c_void_p(0x1000)
+    rows = C.cast(fake, C.POINTER(C.c_int32))
+    Q, H, Hkv, dh, t_cap = info.Q, 4, 2, 64, 256
+    need = lib.la_attention_workspace(Q, H, dh, 100 + info.maxp, t_cap)
+
+    def call(dtype=la.LA_DTYPE_BF16, q=fake, H=H, Hkv=Hkv, shared_end=101, ws_bytes=need, t_cap=t_cap):
+        return lib.la_attention(dtype, q, fake, fake, t_cap, fake, fake, Q, H, Hkv, dh, rows, C.byref(info),
+                                shared_end, fake, fake, ws_bytes, None)
+    assert call(q=None) == la.LA_EINVAL                   # null argument
+    assert call(dtype=7) == la.LA_EINVAL                  # unknown dtype
+    assert call(H=5) == la.LA_EINVAL                      # H not a multiple of Hkv
+    assert call(shared_end=0) == la.LA_EINVAL             # nothing committed
+    assert call(shared_end=t_cap + 1) == la.LA_EINVAL     # past the cache
+    assert call(ws_bytes=need - 1) == la.LA_EOVERFLOW     # workspace too small
+
+
+def test_build_rows_rejects_oversized_window():
+    """More window columns than the row builder's tables hold: refused before any launch."""
+    import ctypes as C
+    lib = _lib()
+    desc = la.rows_desc(100, [list(range(200)), None], 2, 0, 1, 256, [1, 0])
+    info = la.la_rows_info()
+    fake = C.c_void_p(0x1000)
+    rc = lib.la_build_rows(C.byref(desc), C.cast(fake, C.POINTER(C.c_int32)), C.cast(fake, C.POINTER(C.c_int32)),
+                           C.cast(fake, C.POINTER(C.c_int32)), None, C.byref(info))
+    assert rc == la.LA_EOVERFLOW
+
+
 def _oracle_layout(levels, starts, C, S):
     cands = [tuple(range(S)) for _ in range(C)]
     return orows.compile_round(1, 10, levels, cands, S, starts=starts)
