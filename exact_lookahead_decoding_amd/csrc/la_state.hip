@@ -75,13 +75,22 @@ void la_pool_upsert_launch(int32_t* cnt, int32_t* ent, const int32_t* keys, cons
   hipLaunchKernelGGL(pool_upsert_kernel, dim3(1), dim3(64), 0, st, cnt, ent, keys, sufs, n, G, S);
 }
 
-// extraction of the W keyed n-grams from the pre-shift window and z, then upsert in column order
+// extraction of the W keyed n-grams from the pre-shift window and z, then
+// upsert in column order.  Workgroup j owns key k_j when no earlier column
+// has the same key, and applies every column with that key in column order:
+// different keys touch different buckets, so the per-key order (all the LRU
+// rule depends on) is the serial one and the keys proceed in parallel.
 __global__ void __launch_bounds__(64) pool_collect_kernel(int32_t* cnt, int32_t* ent, int x_t, const int32_t* win,
                                                           int stride, int R, int W, const int32_t* z, int G) {
   const int S = R;
+  const int j0 = blockIdx.x;
+  auto key_of = [&](int j) { return j == 0 ? x_t : win[j - 1]; };
+  const int key = key_of(j0);
+  for (int j = 0; j < j0; ++j)
+    if (key_of(j) == key) return;               // an earlier column owns this key
   int suf[POOL_MAX_S];
-  for (int j = 0; j < W; ++j) {
-    const int key = j == 0 ? x_t : win[j - 1];
+  for (int j = j0; j < W; ++j) {
+    if (j > j0 && key_of(j) != key) continue;
     for (int r = 1; r < R; ++r) suf[r - 1] = win[r * stride + j];
     suf[R - 1] = z[j];
     pool_upsert_one(cnt, ent, key, suf, G, S);
@@ -90,7 +99,8 @@ __global__ void __launch_bounds__(64) pool_collect_kernel(int32_t* cnt, int32_t*
 
 void la_pool_collect_launch(int32_t* cnt, int32_t* ent, int x_t, const int32_t* win, int win_stride, int R, int W,
                             const int32_t* z, int G, hipStream_t st) {
-  hipLaunchKernelGGL(pool_collect_kernel, dim3(1), dim3(64), 0, st, cnt, ent, x_t, win, win_stride, R, W, z, G);
+  if (W <= 0) return;
+  hipLaunchKernelGGL(pool_collect_kernel, dim3(W), dim3(64), 0, st, cnt, ent, x_t, win, win_stride, R, W, z, G);
 }
 
 __global__ void __launch_bounds__(64) pool_lookup_kernel(const int32_t* cnt, const int32_t* ent, int key, int G,
