@@ -60,13 +60,15 @@ template <typename T> __device__ __forceinline__ f32x4 kblock(v4u a, v4u b, f32x
 }
 
 // A ring step is NKB k-blocks (4 for narrow stages, 2 once the X and W
-// fragments of a k-block reach 12 KB); the ring holds DW+1 stages and the
-// per-step wait may not exceed vmcnt's 63.
+// fragments of a k-block reach 12 KB); the ring holds DW+1 stages, at most
+// 4 (three steps in flight per wave measured fastest on the round's shapes:
+// deeper rings only lengthen the queues), and the per-step wait may not
+// exceed vmcnt's 63.
 constexpr int gemm_nkb(int mt, int ntw) { return mt + 4 * ntw >= 12 ? 2 : 4; }
 constexpr int gemm_stage(int mt, int ntw) { return (mt + 4 * ntw) * gemm_nkb(mt, ntw) * 1024; }
 constexpr int gemm_loads(int mt, int ntw) { return (ntw + mt / 4) * gemm_nkb(mt, ntw) + (mt % 4) * gemm_nkb(mt, ntw) / 4; }
 constexpr int gemm_depth(int mt, int ntw) {
-  int d = 5;
+  int d = 3;
   while (d > 1 && (d + 1) * gemm_stage(mt, ntw) > LDS_BYTES) --d;
   while (d > 1 && (d - 1) * gemm_loads(mt, ntw) > 63) --d;
   return d;
