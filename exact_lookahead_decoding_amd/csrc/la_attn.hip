@@ -830,10 +830,12 @@ __global__ void __launch_bounds__(256) la_attn_merge_kernel(LaAttnArgs a) {
 }
 
 // Ring stages (128 positions each) per key split: a function of the cache
-// capacity only (about four splits when the cache is full), so every call on
-// one cache cuts its keys the same way.
+// capacity only, so every call on one cache cuts its keys the same way: one
+// stage per split up to 8 stages (short caches: more, shorter workgroups),
+// else about four splits when the cache is full.
 int la_attention_spb(int t_cap) {
   const int stages = (std::max(t_cap, 1) + CH * NCLS - 1) / (CH * NCLS);
+  if (stages <= 8) return 1;
   return std::max(1, (stages + 3) / 4);
 }
 int la_attention_parts(int max_pos, int t_cap) {

@@ -311,8 +311,8 @@ int la_build_rows(const la_rows_desc* desc, const int32_t* window, const int32_t
  * la_attention_workspace(Q, H, dh, max_pos, t_cap) bytes, max_pos =
  * shared_end - 1 + info->maxp (the largest position a row reaches): one
  * softmax state per row, head and key split.  A key split is a fixed run of
- * positions whose length depends on t_cap only (about a quarter of it,
- * rounded up to 128 positions).  Batch invariant: a row's result does not
+ * positions whose length depends on t_cap only (128 positions while t_cap
+ * <= 1024, else about a quarter of t_cap rounded up to 128 positions).  Batch invariant: a row's result does not
  * depend on the other rows of the call (its reduction tree is a function of
  * key positions and t_cap only). */
 size_t la_attention_workspace(int32_t Q, int32_t H, int32_t dh, int32_t max_pos, int32_t t_cap);
