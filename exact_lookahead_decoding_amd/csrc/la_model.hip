@@ -63,13 +63,15 @@ void la_embed_launch(int dtype, const void* E, const int32_t* tok, void* x, int 
 // and rounding as that GEMM's own epilogue), written back to x when write_x;
 // y[m] = T(x' * rs * w), rs = 1/sqrt(mean(x'^2) + eps), src = rows ? rows[m] : m.
 // The sum of squares has one fixed order for every row: each thread's
-// elements in index order, then a butterfly within the wave, then the four
-// wave sums in a fixed grouping.  All loads of a thread are issued first.
-template <typename T, int VPT, int NS>
-__global__ void __launch_bounds__(256) addnorm_kernel(T* x, const float* P, size_t pstride, int write_x, const T* w,
+// elements in index order, then a butterfly within the wave, then the wave
+// sums in a fixed pairwise grouping.  All loads of a thread are issued first;
+// NTH threads per row (512 once a row needs two 16-byte vectors per thread
+// at 256, so its loads come from twice as many waves).
+template <typename T, int VPT, int NS, int NTH>
+__global__ void __launch_bounds__(NTH) addnorm_kernel(T* x, const float* P, size_t pstride, int write_x, const T* w,
                                                       T* y, const int32_t* rows, int d, float eps) {
   constexpr int E = 16 / sizeof(T);
-  __shared__ float red[4];
+  __shared__ float red[NTH / 64];
   const int m = blockIdx.x;
   const int src = rows ? rows[m] : m;
   const int nv = d / E;
@@ -79,7 +81,7 @@ __global__ void __launch_bounds__(256) addnorm_kernel(T* x, const float* P, size
   float4 pv[NS > 0 ? NS : 1][VPT][E / 4];
 #pragma unroll
   for (int j = 0; j < VPT; ++j) {
-    const int v = threadIdx.x + 256 * j;
+    const int v = threadIdx.x + NTH * j;
     if (v < nv) {
       xv[j] = xr[v];
       wv[j] = wr[v];
@@ -95,7 +97,7 @@ __global__ void __launch_bounds__(256) addnorm_kernel(T* x, const float* P, size
   float ss = 0.f;
 #pragma unroll
   for (int j = 0; j < VPT; ++j) {
-    const int v = threadIdx.x + 256 * j;
+    const int v = threadIdx.x + NTH * j;
     if (v < nv) {
       const T* e = (const T*)&xv[j];
 #pragma unroll
@@ -124,12 +126,13 @@ __global__ void __launch_bounds__(256) addnorm_kernel(T* x, const float* P, size
   for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
   __syncthreads();
-  const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+  float tot = (red[0] + red[1]) + (red[2] + red[3]);
+  if constexpr (NTH == 512) tot = tot + ((red[4] + red[5]) + (red[6] + red[7]));
   const float rs = 1.0f / sqrtf(tot / (float)d + eps);
   u32x4* yr = (u32x4*)(y + (size_t)m * d);
 #pragma unroll
   for (int j = 0; j < VPT; ++j) {
-    const int v = threadIdx.x + 256 * j;
+    const int v = threadIdx.x + NTH * j;
     if (v < nv) {
       const T* we = (const T*)&wv[j];
       u32x4 ov;
@@ -141,22 +144,22 @@ __global__ void __launch_bounds__(256) addnorm_kernel(T* x, const float* P, size
   }
 }
 
-template <typename T, int VPT, int NS>
+template <typename T, int VPT, int NS, int NTH>
 static void an_t(void* x, const float* P, size_t pstride, int write_x, const void* w, void* y, const int32_t* rows,
                  int M, int d, float eps, hipStream_t st) {
-  hipLaunchKernelGGL((addnorm_kernel<T, VPT, NS>), dim3(M), dim3(256), 0, st, (T*)x, P, pstride, write_x,
+  hipLaunchKernelGGL((addnorm_kernel<T, VPT, NS, NTH>), dim3(M), dim3(NTH), 0, st, (T*)x, P, pstride, write_x,
                      (const T*)w, (T*)y, rows, d, eps);
 }
 
-template <typename T, int VPT>
+template <typename T, int VPT, int NTH>
 static void an_s(int S, void* x, const float* P, size_t pstride, int write_x, const void* w, void* y,
                  const int32_t* rows, int M, int d, float eps, hipStream_t st) {
   switch (S) {
-    case 0: an_t<T, VPT, 0>(x, P, pstride, write_x, w, y, rows, M, d, eps, st); break;
-    case 1: an_t<T, VPT, 1>(x, P, pstride, write_x, w, y, rows, M, d, eps, st); break;
-    case 2: an_t<T, VPT, 2>(x, P, pstride, write_x, w, y, rows, M, d, eps, st); break;
-    case 3: an_t<T, VPT, 3>(x, P, pstride, write_x, w, y, rows, M, d, eps, st); break;
-    default: an_t<T, VPT, 4>(x, P, pstride, write_x, w, y, rows, M, d, eps, st); break;
+    case 0: an_t<T, VPT, 0, NTH>(x, P, pstride, write_x, w, y, rows, M, d, eps, st); break;
+    case 1: an_t<T, VPT, 1, NTH>(x, P, pstride, write_x, w, y, rows, M, d, eps, st); break;
+    case 2: an_t<T, VPT, 2, NTH>(x, P, pstride, write_x, w, y, rows, M, d, eps, st); break;
+    case 3: an_t<T, VPT, 3, NTH>(x, P, pstride, write_x, w, y, rows, M, d, eps, st); break;
+    default: an_t<T, VPT, 4, NTH>(x, P, pstride, write_x, w, y, rows, M, d, eps, st); break;
   }
 }
 
@@ -166,14 +169,14 @@ void la_addnorm_launch(int dtype, void* x, const float* P, int S, size_t pstride
   if (!P) S = 0;
   const int esz = dtype == LA_DT_BF16 ? 2 : 4;
   switch (vpt_for(d, esz) * 2 + (dtype == LA_DT_BF16)) {
-    case 2: an_s<float, 1>(S, x, P, pstride, write_x, w, y, rows, M, d, eps, st); break;
-    case 3: an_s<bf16_t, 1>(S, x, P, pstride, write_x, w, y, rows, M, d, eps, st); break;
-    case 4: an_s<float, 2>(S, x, P, pstride, write_x, w, y, rows, M, d, eps, st); break;
-    case 5: an_s<bf16_t, 2>(S, x, P, pstride, write_x, w, y, rows, M, d, eps, st); break;
-    case 8: an_s<float, 4>(S, x, P, pstride, write_x, w, y, rows, M, d, eps, st); break;
-    case 9: an_s<bf16_t, 4>(S, x, P, pstride, write_x, w, y, rows, M, d, eps, st); break;
-    case 16: an_s<float, 8>(S, x, P, pstride, write_x, w, y, rows, M, d, eps, st); break;
-    default: an_s<bf16_t, 8>(S, x, P, pstride, write_x, w, y, rows, M, d, eps, st); break;
+    case 2: an_s<float, 1, 256>(S, x, P, pstride, write_x, w, y, rows, M, d, eps, st); break;
+    case 3: an_s<bf16_t, 1, 256>(S, x, P, pstride, write_x, w, y, rows, M, d, eps, st); break;
+    case 4: an_s<float, 1, 512>(S, x, P, pstride, write_x, w, y, rows, M, d, eps, st); break;
+    case 5: an_s<bf16_t, 1, 512>(S, x, P, pstride, write_x, w, y, rows, M, d, eps, st); break;
+    case 8: an_s<float, 2, 512>(S, x, P, pstride, write_x, w, y, rows, M, d, eps, st); break;
+    case 9: an_s<bf16_t, 2, 512>(S, x, P, pstride, write_x, w, y, rows, M, d, eps, st); break;
+    case 16: an_s<float, 4, 512>(S, x, P, pstride, write_x, w, y, rows, M, d, eps, st); break;
+    default: an_s<bf16_t, 4, 512>(S, x, P, pstride, write_x, w, y, rows, M, d, eps, st); break;
   }
 }
 
