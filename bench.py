@@ -325,7 +325,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the lookahead round runs on a single MI355X (got --gpus {args.gpus}); "
-              f"lookahead parallelism across GPUs is not part of this build", file=sys.stderr)
+              f"lookahead parallelism across GPUs is not implemented: the library runs on one device", file=sys.stderr)
         sys.exit(2)
     import torch
     import synthetic
