@@ -209,12 +209,13 @@ def test_attention_matches_oracle(case):
     assert err <= tol
 
 
-@pytest.mark.parametrize("p,t_cap", [(1150, 1166), (2300, 3000)])
+@pytest.mark.parametrize("p,t_cap", [(765, 1000), (1150, 1166), (2300, 3000)])
 def test_attention_batch_invariance(p, t_cap):
     """A packed row's output equals, bit for bit, the same row computed alone
     with its branch ancestors committed to a cache of the same capacity (an
-    autoregressive call).  Both cases put the round's rows across a key-split
-    boundary (384 positions at capacity 1166, 768 at 3000)."""
+    autoregressive call).  Every case puts the round's rows across a key-split
+    boundary (768 at capacity 1000, whose splits are 128 positions; 384 at
+    capacity 1166; 768 at 3000)."""
     sizes, starts = [6, 7, 7, 7], [1, 0, 0, 0]
     cands = [tuple(range(i, i + 4)) for i in range(7)]
     H, Hkv, dh = 8, 2, 128
