@@ -24,6 +24,10 @@ Also reported on the same line:
     long-prefix workload's per-layer shape, 134 MB of K/V per call);
   * lookahead_attn_34b_gqa: the op at the 34B-shaped round's per-layer shape
     (64 query heads on 8 KV heads, N=7: 180 rows, 2048 committed keys);
+  * step_roofline: the round against the HBM bound (streamed weight bytes
+    plus the committed K/V read at the mean committed length, over 8 TB/s);
+  * init_prefill_ms: context set-up and prompt prefill (wall clock, untimed
+    in value);
   * ar_tokens_per_s: plain autoregressive decoding with the same kernels;
   * cpu_baseline: the CPU oracle on a bounded sample of the same workload.
 """
@@ -54,6 +58,20 @@ WORKLOADS = {
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def step_roofline(model, dims, wl, tokens, steps, secs):
+    """The round against the HBM bound: every streamed weight byte (all layers
+    and the LM head; the embedding is gathered, not streamed) plus the committed
+    K/V the attention reads, at the mean committed length of the timed rounds
+    (prompt + half the tokens they emitted), over 8 TB/s."""
+    streamed = model.weight_bytes - model.embed.numel() * model.embed.element_size()
+    esize = 2 if dims.dtype == "bf16" else 4
+    kv = 2 * dims.n_layers * dims.n_kv_heads * dims.head_dim * esize * (wl["prompt"] + tokens / 2)
+    at_peak_ms = (streamed + kv) / (HBM_PEAK_GBS * 1e9) * 1e3
+    ms = secs * 1e3 / steps
+    return {"bytes_per_round": streamed + kv, "weight_bytes": streamed, "kv_bytes": kv,
+            "ms_at_peak": at_peak_ms, "ms_per_round": ms, "frac": at_peak_ms / ms}
 
 
 def run_steps(make_session, sess, steps):
@@ -366,7 +384,14 @@ def main():
     # dominant kernel: GEMM weight stream, events around each launch
     # a second pass with HIP events around every GEMM / attention launch (one
     # context's totals; with --steps K the first context's rounds are the ones read)
-    prof = make(profile=True)
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    prof = make(profile=True)           # context set-up and prompt prefill, outside every timed region
+    torch.cuda.synchronize()
+    init_prefill_ms = (time.perf_counter() - t) * 1e3
+    sr = step_roofline(model, dims, wl, tokens, steps, secs)
+    log(f"round vs HBM bound: {sr['bytes_per_round'] / 1e9:.2f} GB per round, {sr['ms_at_peak']:.2f} ms at 8 TB/s, "
+        f"{sr['frac'] * 100:.1f}% of it; set-up + prefill {init_prefill_ms:.0f} ms")
     for _ in range(args.warmup):
         prof.la_step()
     prof.la_profile(True)
@@ -394,6 +419,8 @@ def main():
                      "kernel": "la_gemm_kernel (+ split reduction), all projections, MLP and LM head of a round",
                      "avg_launch_us": gemm_avg_ms * 1e3, "algorithmic_bytes_per_launch": gemm_bytes,
                      "launches": pr["gemm_launches"]},
+        "step_roofline": sr,
+        "init_prefill_ms": init_prefill_ms,
         "attention_in_step": {"achieved_GBps": attn_in_step, "avg_launch_us":
                               pr["attn_ms"] / max(1, pr["attn_launches"]) * 1e3, "launches": pr["attn_launches"]},
     }
