@@ -24,8 +24,10 @@ Parity status per module:
   numerics, rows, window, pool, commit, verify, philox, jacobi, acceptance,
   attention -- pinned by page values, closed forms or brute force in
   tests/test_oracle_*.py.
-  model -- parity unpinned by the pages (they print no activations); pinned
-  internally by textbook identities (softmax attention against an explicit
-  loop, RoPE rotation invariants, RMSNorm scale invariance) and by the
-  separate-forwards == dense-mask == autoregressive equalities.
+  model -- the pages print no activations; pinned by a second, independent
+  fp64 forward written in torch (tests/test_oracle_forward_torch.py: bit-equal
+  K/V and logits within one fp32 rounding on tiny, small bf16 GQA and
+  7B-width rounds), by textbook identities (softmax attention against an
+  explicit loop, RoPE rotation invariants, RMSNorm scale invariance) and by
+  the separate-forwards == dense-mask == autoregressive equalities.
 """

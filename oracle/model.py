@@ -23,8 +23,10 @@ Storage points (each stored value is rounded to the model dtype, "f32" or
       x    = s(h + a Wd^T)
     logits = f32(s(x * rs(x) * w_final) Wlm^T)
 
-Parity unpinned by the pages (no activations are printed); the tests pin it
-by textbook identities and by separate-forwards == dense-mask == AR.
+The pages print no activations; the tests pin this forward against a second,
+independent fp64 forward in torch (same storage points, its own matmuls,
+rotation and attention), by textbook identities and by separate-forwards ==
+dense-mask == AR.
 """
 from __future__ import annotations
 

@@ -18,9 +18,10 @@
 * slices: out = the ordinary row, inp = the deepest trajectory level's rows,
   guess = all verification rows.
 
-Logical positions (the pages give them only in words: "next committed
-position", "the future position represented by its window column",
-"prefix length + suffix offset"): with p the ordinary row's position,
+Logical positions (the pages describe them only in words: the ordinary row
+takes the next committed position, a lookahead row the future position its
+window column stands for, a verification row the prefix length plus its
+offset): with p the ordinary row's position,
     pos(b_j) = p + j,   pos(u_(r,j)) = p + j + r,   pos(v_(c,s)) = p + 1 + s.
 This is the only choice under which the n-gram extraction of 0x03B and the
 window shift of 0x03C keep every cell at the position it was predicted for.

@@ -19,6 +19,11 @@ max(0, p - q) normalised; one-hot q = delta_c reduces it to the rule above.
 Readings:
 * a candidate matching all S tokens emits S + 1 tokens (the extra one read
   from its last row); accepted length h lies in [0, S];
+* capped convention (0x05A contrasts the paper's full match plus one target
+  token with the implementation's max_hit count): with cap_full_match, at
+  most S - 1 candidate tokens are accepted; the round then stops at offset
+  S - 1 and emits the target token of that offset's survivor row, so it emits
+  at most S tokens.  Every emitted token is still the target's;
 * the winner is the lowest-index survivor (the oldest pool entry), so the
   K/V copied is that candidate's;
 * sampling: greedy proposals; temperature only; draw counters
@@ -36,17 +41,18 @@ from .philox import DRAW_RESIDUAL, uniform
 from .sampling import blocked_sum, masses, residual_draw
 
 
-def greedy_verify(out_logits, guess_logits, candidates, check_invariant=True):
+def greedy_verify(out_logits, guess_logits, candidates, check_invariant=True, cap_full_match=False):
     """Survivor view.  guess_logits[c][s] is the row whose input is candidates[c][s].
 
     Returns (emitted, winner, h): emitted = h + 1 tokens, winner = index of the
-    candidate whose rows are committed (-1 when h == 0).
+    candidate whose rows are committed (-1 when h == 0).  With cap_full_match
+    at most S - 1 offsets are matched.
     """
     S = len(candidates[0]) if candidates else 0
     target = argmax_lowest(out_logits)
     emitted = [target]
     survivors = list(range(len(candidates)))
-    for offset in range(S):
+    for offset in range(max(0, S - 1) if cap_full_match else S):
         alive = [c for c in survivors if candidates[c][offset] == target]
         if not alive:
             break
@@ -75,16 +81,20 @@ def greedy_hits(out_logits, guess_logits, candidates):
     return hits
 
 
-def sample_verify(out_logits, guess_logits, candidates, T: float, seed: int, round_id: int):
-    """One-hot sampling verification of one round.  Returns (emitted, winner, h)."""
+def sample_verify(out_logits, guess_logits, candidates, T: float, seed: int, round_id: int,
+                  cap_full_match=False):
+    """One-hot sampling verification of one round.  Returns (emitted, winner, h).
+    With cap_full_match the offsets tested stop at S - 1 (the draw at offset
+    S - 1 is then a plain target sample of that survivor row)."""
     S = len(candidates[0]) if candidates else 0
+    last = max(0, S - 1) if cap_full_match else S      # offsets whose candidate tokens are tested
     survivors = list(range(len(candidates)))
     emitted = []
-    for a in range(S + 1):
+    for a in range(last + 1):
         row = out_logits if a == 0 else guess_logits[survivors[0]][a - 1]
         e = masses(row, T)
         offered = []
-        if a < S:
+        if a < last:
             for c in survivors:
                 t = int(candidates[c][a])
                 if t not in offered:
@@ -171,10 +181,11 @@ def naive_top1_distribution(p: dict, q: dict) -> dict:
     return out
 
 
-def lookahead_joint(cond, prefix: tuple, candidates: list, horizon: int) -> dict:
+def lookahead_joint(cond, prefix: tuple, candidates: list, horizon: int, cap_full_match=False) -> dict:
     """Exact joint of the first `horizon` tokens: one lookahead round with the
     given candidate suffixes (one-hot sampling verification), then plain
-    autoregressive sampling.  cond(prefix) -> {token: Fraction}."""
+    autoregressive sampling.  cond(prefix) -> {token: Fraction}.  With
+    cap_full_match no candidate token is offered at offset S - 1."""
     joint = {}
 
     def ar_tail(seq, prob):
@@ -189,8 +200,9 @@ def lookahead_joint(cond, prefix: tuple, candidates: list, horizon: int) -> dict
     def step(seq, survivors, a, prob):
         # seq: tokens emitted so far in this round; survivors: candidate indices
         S = len(candidates[0]) if candidates else 0
+        last = max(0, S - 1) if cap_full_match else S
         p = cond(tuple(prefix) + tuple(seq))
-        offered = [candidates[c][a] for c in survivors] if a < S else []
+        offered = [candidates[c][a] for c in survivors] if a < last else []
         dist_reach = Fraction(1)
         mass = Fraction(1)
         resid = dict(p)

@@ -1,54 +1,61 @@
-"""Jacobi trajectory window: depth admission, warmup fill, pinned advance.
+"""Jacobi trajectory window: depth admission, warmup fill, steady advance.
 
 "M7.3 - Lookahead Decoding":
-* 0x01A -- the illustrated pinned schedule needs an integer N >= 3
-  (S = R = N - 1), otherwise ValueError, before any state is built;
-* 0x03A -- warmup: level 0 starts with W + N - 3 cells; at each fill the
-  existing levels shift left by one and the deepest level's outputs become a
-  new, deeper level, the new level dropping its first output where needed
-  (N=4, W=5: [6,-,-] -> [5,6,-] -> [4,5,5]); no verification meanwhile;
-* 0x03C -- steady advance with ALWAYS_FWD_ONE: new window is
-  [past[1][1:]] + past[2:] + [z], keeping the ragged sizes [W-1, W, ..., W];
-  its alternative (ALWAYS_FWD_ONE=False) slices each level by the accepted
-  count and refills the tail (0x03C, 0x06C "drop positions consumed by
-  committed output, shift the remaining future slots left, refill vacated
-  slots from the configured seed/reset source").
+* 0x01A -- the pinned multilevel schedule is defined for integer N >= 3
+  (S = R = N - 1); anything else is refused before any state is built;
+* 0x03A -- warmup: level 0 starts with W + N - 3 cells; each fill shifts the
+  existing levels left by one and turns the deepest level's outputs into a
+  new, deeper level, which loses its first output where needed (the page's
+  N=4, W=5 trace: sizes [6,-,-] -> [5,6,-] -> [4,5,5]); no verification
+  meanwhile;
+* 0x03C -- steady advance under ALWAYS_FWD_ONE: one column per round
+  whatever was accepted, keeping the ragged sizes [W-1, W, ..., W]; the
+  page also names, in words only, a variant that slices the levels by the
+  accepted count and refills the emptied slots.
+
+Coordinates used below (reading 18 of the build's notes): with the live token
+at logical position p, level r holds the cell of column j at position
+p + j + r; level 0 holds columns 1..W-1 (column 0 is the live token itself),
+deeper levels columns 0..W-1.  Each rule is written as "which old cell (or
+new output) lands at each new cell"; every cell keeps the position it was
+predicted for.
 
 Readings (the pages leave these open):
-* initial level-0 content: "seeds lookahead slots from prompt tokens" is
-  read as the last W + N - 3 prompt tokens, cycling if the prompt is short;
-* "drops its first output where needed" is read as: the new level drops its
-  first output exactly when the level it was computed from has index >= 1
-  (the only reading that reproduces [5,6,-] -> [4,5,5] and keeps every cell
-  at the position it was predicted for);
-* ALWAYS_FWD_ONE=False: after the pinned advance, which accounts for the
-  one position every round publishes, each level drops its first h entries
-  (the h accepted tokens moved the live position h further) and appends h
-  copies of the newest committed token (the page lists "copy the last
-  token" among the seed choices); the ragged sizes are kept, and every
-  surviving cell stays at the position it was predicted for.  Warmup fills
-  are unchanged.
+* initial level-0 content: the page only says the lookahead slots are seeded
+  from the prompt; read as the last W + N - 3 prompt tokens, cycling when
+  the prompt is shorter;
+* the new warmup level loses its first output exactly when the level it was
+  computed from has index >= 1 (the only reading that reproduces the page's
+  [5,6,-] -> [4,5,5] and keeps positions);
+* ALWAYS_FWD_ONE=False: after the one-column advance (the one position every
+  round publishes), each level drops its first h cells (the h accepted
+  tokens moved the live position h further) and is refilled at its tail with
+  h copies of the newest committed token (the page lists copying the last
+  token among the seed choices); sizes are kept.  Warmup fills are unchanged.
 """
 from __future__ import annotations
 
 
-def pinned_suffix_length(N) -> int:
-    """S = R = N - 1, admitted only for integer N >= 3 (0x01A).
+def admitted_depth(N) -> int:
+    """S = R = N - 1 for an admitted depth (0x01A).
 
-    N = 2 would leave a single trajectory level, but both the first warmup
-    fill and the steady advance read a second level, so it is refused before
-    any state exists.
+    Depth 2 would leave one trajectory level, while the first warmup fill and
+    the steady advance both read a second one; such a schedule (and any
+    non-integer N) is refused before state exists.
     """
-    admitted = isinstance(N, int) and not isinstance(N, bool) and N >= 3
-    if not admitted:
-        raise ValueError(f"depth N={N!r} not admitted: the pinned schedule needs an integer N >= 3")
+    if isinstance(N, bool) or not isinstance(N, int) or N < 3:
+        raise ValueError(f"N={N!r}: the multilevel schedule takes an integer depth of at least 3")
     return N - 1
 
 
+def _check_width(W):
+    if isinstance(W, bool) or not isinstance(W, int) or W < 1:
+        raise ValueError(f"W={W!r}: the window needs at least one column")
+
+
 def init_window(prompt, W: int, N: int):
-    R = pinned_suffix_length(N)
-    if not isinstance(W, int) or W < 1:
-        raise ValueError("window width must be a positive integer")
+    R = admitted_depth(N)
+    _check_width(W)
     n0 = W + N - 3
     P = len(prompt)
     level0 = [int(prompt[(P - n0 + i) % P]) for i in range(n0)]
@@ -76,32 +83,38 @@ def fill_window(window, z):
     return new + [None] * (len(window) - len(new))
 
 
-def advance_pinned_window(window, z, N, W):
-    """Steady ALWAYS_FWD_ONE advance (one column per round, whatever was accepted).
+def advance_one_column(window, z, N, W):
+    """Steady advance by one column (ALWAYS_FWD_ONE).
 
-    Time axis: the oldest level is dropped and every other level moves up one;
-    sequence axis: the level that becomes level 0 loses its first column,
-    because the live token now stands in for it; the new outputs z become the
-    deepest level.  Shapes are checked first: R levels, ragged [W-1, W, ..., W],
-    and W outputs.
+    The live position moves from p to p + 1, so new cell (r, j) at position
+    p + 1 + j + r is old cell (r + 1, j), and the deepest new level is the
+    outputs z (old deepest cell (R - 1, j) predicted position p + j + R).
+    Old level 0 and old cell (1, 0) -- the new live token's position -- drop
+    out.  The warm ragged layout and W outputs are required.
     """
-    R = pinned_suffix_length(N)
-    if not isinstance(W, int) or W < 1:
-        raise ValueError("window width must be a positive integer")
-    expected = [W - 1] + [W] * (R - 1)
-    if len(window) != R or level_sizes(window) != expected:
-        raise ValueError(f"window sizes {level_sizes(window)} are not the warm layout {expected}")
+    R = admitted_depth(N)
+    _check_width(W)
+    want = [W - 1] + [W] * (R - 1)
+    if len(window) != R or level_sizes(window) != want:
+        raise ValueError(f"level sizes {level_sizes(window)} differ from the warm layout {want}")
     if len(z) != W:
-        raise ValueError(f"{len(z)} new outputs, expected W={W}")
-    promoted = [list(window[r]) for r in range(2, R)]
-    return [list(window[1])[1:], *promoted, list(z)]
+        raise ValueError(f"{len(z)} outputs for a {W}-column window")
+
+    def old(r, j):                 # old level r at column j (level 0 starts at column 1)
+        return window[r][j - 1] if r == 0 else window[r][j]
+
+    new = []
+    for r in range(R):
+        cols = range(1, W) if r == 0 else range(W)
+        new.append([int(z[j]) if r == R - 1 else old(r + 1, j) for j in cols])
+    return new
 
 
 def advance_by_accepted(window, z, N, W, h: int, fill: int):
-    """ALWAYS_FWD_ONE=False: the pinned advance, then every level drops its
-    first h entries and its tail is refilled with `fill`."""
+    """ALWAYS_FWD_ONE=False: the one-column advance, then every level drops
+    its first h cells and is refilled at its tail with `fill`."""
     out = []
-    for lv in advance_pinned_window(window, z, N, W):
+    for lv in advance_one_column(window, z, N, W):
         k = min(int(h), len(lv))
         out.append(lv[k:] + [int(fill)] * k)
     return out
@@ -113,5 +126,5 @@ def next_window(window, z, N, W, h: int = 0, fill=None):
     if is_warm(window):
         if fill is not None:
             return advance_by_accepted(window, z, N, W, h, fill)
-        return advance_pinned_window(window, z, N, W)
+        return advance_one_column(window, z, N, W)
     return fill_window(window, z)

@@ -133,6 +133,6 @@ def test_pool_is_exactly_the_trajectory_ngrams(tiny):
         # its output; that output closes one n-gram per window column
         for col, path, zj in zip(r.inp_columns, r.deep_paths, r.z):
             gram = path[-(N - 1):] + [zj]
-            pool.upsert_suffix_lru(replay, gram[0], tuple(gram[1:]), G)
+            pool.lru_upsert(replay, gram[0], tuple(gram[1:]), G)
     assert replay == la["token_map"]
     assert all(len(v) <= G for v in replay.values())

@@ -65,6 +65,22 @@ def test_lookahead_sampling_joint_equals_ar_joint(case):
     assert verify.lookahead_joint(cond, (0,), cands, horizon) == verify.ar_joint(cond, (0,), horizon)
 
 
+@pytest.mark.parametrize("case", range(6))
+def test_capped_sampling_joint_equals_ar_joint(case):
+    """The capped full-match convention (no candidate token tested at offset
+    S - 1; that position is a plain target draw) is exact as well."""
+    rng = np.random.default_rng(300 + case)
+    V = 3 + case % 2
+    S = 2 + case % 2
+    C = 1 + case % 3
+    cond = _random_cond(V, 50 + case)
+    base = [tuple(int(t) for t in rng.integers(0, V, S)) for _ in range(C)]
+    cands = base + [base[0]]
+    horizon = S + 2
+    capped = verify.lookahead_joint(cond, (0,), cands, horizon, cap_full_match=True)
+    assert capped == verify.ar_joint(cond, (0,), horizon)
+
+
 def test_naive_greedy_check_is_not_exact():
     """Keeping a candidate only when it equals the greedy top-1 collapses the distribution."""
     V = 3
@@ -130,6 +146,23 @@ def test_sample_verify_offsets_and_bonus():
     em, win, h = verify.sample_verify(out, guess, cands, 1.0, seed=3, round_id=9)
     # offset 0 accepts 2 (all survive); offset 1 row = candidate 0's -> 0 accepted
     assert em == [2, 0, 1, 1] and h == 3 and win == 0
+
+
+def test_sample_verify_capped_stops_before_last_offset():
+    """Under cap_full_match the same certain acceptances stop after S - 1
+    offsets: the S-th token is a plain draw from the survivor's row at offset
+    S - 2 (a one-hot row, so it is that row's token), h = S - 1."""
+    V, S = 5, 3
+    big = np.float32(80.0)
+
+    def onehot(t):
+        r = np.full(V, -big, np.float32)
+        r[t] = big
+        return r
+    cands = [(2, 0, 1), (2, 4, 4), (2, 4, 3)]
+    guess = [[onehot(c[s + 1]) if s + 1 < S else onehot(1) for s in range(S)] for c in cands]
+    em, win, h = verify.sample_verify(onehot(2), guess, cands, 1.0, seed=3, round_id=9, cap_full_match=True)
+    assert em == [2, 0, 1] and h == 2 and win == 0
 
 
 def test_uniform_is_53_bit():
