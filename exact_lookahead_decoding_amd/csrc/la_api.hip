@@ -41,6 +41,8 @@ struct la_ctx {
   int R, S;
   int t_cap, q_max, m_max, ws_cap, n_logit_max, nb_max, maxp_max, words_max, parts, wstride, rows_words;
   int rope_rows;      // positions reach kv_len + maxp, beyond the K/V capacity
+  int hmax;           // most accepted candidate tokens per round: S, or S - 1 under cap_full_match
+  bool rows_fit;      // every round layout fits the row builder's tables
   // device
   char* kc;
   char* vc;
@@ -148,6 +150,8 @@ static int validate_cfg(const la_config* cfg, const la_model_dims* d, la_ctx* c)
     return fail(c, LA_EINVAL, "pool_from_prompt %d (0 or 1)", cfg->pool_from_prompt);
   if (cfg->advance_by_accepted != 0 && cfg->advance_by_accepted != 1)
     return fail(c, LA_EINVAL, "advance_by_accepted %d (0 or 1)", cfg->advance_by_accepted);
+  if (cfg->cap_full_match != 0 && cfg->cap_full_match != 1)
+    return fail(c, LA_EINVAL, "cap_full_match %d (0 or 1)", cfg->cap_full_match);
   if (d->dtype != LA_DTYPE_F32 && d->dtype != LA_DTYPE_BF16) return fail(c, LA_EINVAL, "dtype %d", d->dtype);
   if (d->n_layers < 1 || d->d_model < 16 || d->n_heads < 1 || d->n_kv_heads < 1 || d->n_heads % d->n_kv_heads)
     return fail(c, LA_EINVAL, "bad model dims");
@@ -159,6 +163,11 @@ static int validate_cfg(const la_config* cfg, const la_model_dims* d, la_ctx* c)
   const int kc = d->dtype == LA_DTYPE_BF16 ? 128 : 64;
   if (d->d_model % kc || (d->n_heads * dh) % kc || d->d_ff % kc || d->vocab % 16 || d->d_ff % 16)
     return fail(c, LA_EINVAL, "d_model, n_heads*head_dim and d_ff must be multiples of %d, vocab of 16", kc);
+  // the embedding gather and the residual fold + RMSNorm hold a row in at most
+  // 2048 16-byte vectors (256 threads x 8)
+  const int esz = d->dtype == LA_DTYPE_BF16 ? 2 : 4;
+  if ((long)d->d_model * esz / 16 > 2048)
+    return fail(c, LA_EINVAL, "d_model %d exceeds the %d the row kernels hold", d->d_model, 2048 * 16 / esz);
   return LA_OK;
 }
 
@@ -184,10 +193,12 @@ static void setup_dims(la_ctx* c) {
   c->F = d.d_ff; c->V = d.vocab;
   c->qkvdim = (c->H + 2 * c->Hkv) * c->dh;
   c->R = g.N - 1; c->S = g.N - 1;
+  c->hmax = c->S - (g.cap_full_match ? 1 : 0);
   // most rows over the warmup schedule and the steady state with G candidates
   int sz[LA_MAX_N] = {0};
   sz[0] = g.W + g.N - 3;
   int qmax = 0, lmax = 0, ncmax = 0, pmax = c->S;
+  c->rows_fit = true;
   for (int stage = 0; stage < c->R; ++stage) {
     LaLayout L{};
     L.p = 0; L.R = c->R; L.C = g.G; L.S = c->S;
@@ -195,6 +206,7 @@ static void setup_dims(la_ctx* c) {
     if (la_layout_finish(&L) == 0) {
       qmax = std::max(qmax, L.Q); lmax = std::max(lmax, L.n_logit);
       ncmax = std::max(ncmax, L.NB); pmax = std::max(pmax, L.maxp);
+      c->rows_fit = c->rows_fit && la_build_rows_fits(L);
     }
     int dpt = 0;
     for (int r = 0; r < c->R; ++r) if (sz[r] > 0) dpt = r;
@@ -217,6 +229,23 @@ static void setup_dims(la_ctx* c) {
   c->wstride = g.W + g.N;
   c->rows_words = 8 * c->q_max + c->nb_max * c->maxp_max + c->nb_max + c->n_logit_max + c->q_max * c->words_max +
                   (c->q_max + 15) / 16 * (64 + 16 * 64);
+}
+
+// Admission of the round shapes a config produces, before any state exists
+// ("M7.3", 0x01A: unsupported schedules are refused before a round is
+// compiled): every kernel of the round must take the largest round.
+#define LA_MAX_ROWS 256      // packed rows one GEMM launch holds (16 row tiles)
+#define LA_MAX_BRANCH 64     // positions a branch may reach past the committed prefix (attention path table)
+static int admit(la_ctx* c) {
+  const la_config& g = c->cfg;
+  if (c->q_max > LA_MAX_ROWS)
+    return fail(c, LA_EINVAL, "W=%d N=%d G=%d needs %d packed rows in a round; at most %d are admitted", g.W, g.N, g.G,
+                c->q_max, LA_MAX_ROWS);
+  if (c->maxp_max > LA_MAX_BRANCH)
+    return fail(c, LA_EINVAL, "W=%d N=%d: a branch reaches %d positions past the committed prefix; at most %d are admitted",
+                g.W, g.N, c->maxp_max, LA_MAX_BRANCH);
+  if (!c->rows_fit) return fail(c, LA_EINVAL, "W=%d N=%d G=%d: the row builder's tables do not fit", g.W, g.N, g.G);
+  return LA_OK;
 }
 
 static size_t gemm_partial_floats(la_ctx* c) {
@@ -283,6 +312,7 @@ extern "C" int la_query_sizes(const la_config* cfg, const la_model_dims* dims, l
   c.cfg = *cfg;
   c.dims = *dims;
   setup_dims(&c);
+  if ((rc = admit(&c))) return rc;
   out->kv_bytes = 2ull * c.L * c.Hkv * (size_t)c.t_cap * c.dh * c.esz;
   out->arena_bytes = carve(&c, nullptr);
   out->t_cap = c.t_cap;
@@ -457,6 +487,11 @@ extern "C" int la_init(const la_config* cfg, const la_model_dims* dims, const la
   c->pk = packed_offsets(*dims);
   c->st = (hipStream_t)stream;
   setup_dims(c);
+  if ((rc = admit(c))) {
+    g_err = c->err;
+    delete c;
+    return rc;
+  }
   const size_t kvb = (size_t)c->L * c->Hkv * c->t_cap * c->dh * c->esz;
   c->kc = (char*)kv;
   c->vc = (char*)kv + kvb;
@@ -660,10 +695,10 @@ extern "C" int la_verify(la_ctx* c, const float* logits, int32_t n_inp, const in
   const int rid = c->round_id + 1;          // the draws of the round being decided
   la_argmax_launch(logits, n_logit, c->V, c->amax, c->st);
   if (c->cfg.verify_mode == LA_VERIFY_SAMPLE)
-    la_sample_accept_launch(logits, c->V, n_inp, c->amax, cand_dev, C, c->S, c->cfg.temperature, c->cfg.seed, rid,
-                            c->escr, c->acc, zdev, c->st);
+    la_sample_accept_launch(logits, c->V, n_inp, c->amax, cand_dev, C, c->S, c->hmax, c->cfg.temperature,
+                            c->cfg.seed, rid, c->escr, c->acc, zdev, c->st);
   else
-    la_greedy_accept_launch(c->amax, n_inp, cand_dev, C, c->S, c->acc, zdev, c->st);
+    la_greedy_accept_launch(c->amax, n_inp, cand_dev, C, c->S, c->hmax, c->acc, zdev, c->st);
   LaAcceptDev a;
   HIPCHK(c, hipGetLastError());
   HIPCHK(c, hipMemcpyAsync(&a, c->acc, sizeof a, hipMemcpyDeviceToHost, c->st));
@@ -691,7 +726,7 @@ extern "C" int la_commit(la_ctx* c, const la_accept* a) {
   const LaLayout& L = c->lay;
   const int S = c->S;
   // --- validation: nothing below this block may fail before publication ---
-  if (a->h < 0 || a->h > S) return fail(c, LA_EPLAN, "h=%d outside [0, S=%d]", a->h, S);
+  if (a->h < 0 || a->h > c->hmax) return fail(c, LA_EPLAN, "h=%d outside [0, %d]", a->h, c->hmax);
   if (a->n_emit != a->h + 1) return fail(c, LA_EPLAN, "n_emit=%d != h+1", a->n_emit);
   if (a->h > 0 && (a->winner < 0 || a->winner >= L.C)) return fail(c, LA_EPLAN, "winner %d not a candidate", a->winner);
   if (a->h == 0 && a->winner != -1) return fail(c, LA_EPLAN, "winner %d with h=0", a->winner);

@@ -66,6 +66,8 @@ struct LaLayout {        // host-side description of one round's rows
   int Q, NB, maxp, n_logit, n_inp, n_cols, mask_words;
 };
 int la_layout_finish(LaLayout* L);   // fills Q, NB, ... ; returns 0 or -1 if inconsistent
+// whether the builder's LDS tables hold the round (la_build_rows_launch returns -2 otherwise)
+int la_build_rows_fits(const LaLayout& L);
 // returns -2 when the round's tables exceed the builder's LDS
 int la_build_rows_launch(const LaLayout& L, int x_t, const int32_t* win, int win_stride,
                          const int32_t* cands, LaRowsDev rows, hipStream_t st);
@@ -128,10 +130,11 @@ struct LaAcceptDev {     // device image of one verification result
   int32_t h, winner, n_emit, pad;
   int32_t emitted[32];
 };
-void la_greedy_accept_launch(const int32_t* amax, int n_inp, const int32_t* cand, int C, int S,
+// hmax: most candidate tokens accepted (S, or S - 1 when a full match is capped)
+void la_greedy_accept_launch(const int32_t* amax, int n_inp, const int32_t* cand, int C, int S, int hmax,
                              LaAcceptDev* acc, int32_t* z, hipStream_t st);
 void la_sample_accept_launch(const float* logits, int V, int n_inp, const int32_t* amax, const int32_t* cand,
-                             int C, int S, double T, uint64_t seed, int round_id, double* scratch,
+                             int C, int S, int hmax, double T, uint64_t seed, int round_id, double* scratch,
                              LaAcceptDev* acc, int32_t* z, hipStream_t st);
 void la_sample_row_launch(const float* logits, int V, double T, uint64_t seed, int round_id, const int32_t* amax,
                           double* scratch, int32_t* out, hipStream_t st);

@@ -206,6 +206,10 @@ __global__ void __launch_bounds__(256) build_rows_kernel(LaLayout L, int x_t, co
   }
 }
 
+int la_build_rows_fits(const LaLayout& L) {
+  return rows_lds_bytes(L) <= (size_t)(LDS_BYTES - 2048) && L.n_cols <= LA_MAX_COLS;
+}
+
 int la_build_rows_launch(const LaLayout& L, int x_t, const int32_t* win, int win_stride, const int32_t* cands,
                          LaRowsDev rows, hipStream_t st) {
   const size_t lds = rows_lds_bytes(L);

@@ -5,7 +5,9 @@
 // g_(1..a) = z^(c)_(1..a), z^(c) = (argmax out, argmax guess^(c)_1, ...);
 // the accepted length h is the maximum hit, and every candidate reaching it
 // exposes the same conditionals, so the lowest-index one is committed.  A
-// full match emits S + 1 tokens.  Ties in argmax go to the lowest token id.
+// full match emits S + 1 tokens; under the capped convention (the page's
+// implementation-side max_hit count) hits stop at S - 1 and a round emits at
+// most S tokens.  Ties in argmax go to the lowest token id.
 //
 // 0x05B: at each offset the distinct tokens offered by the surviving
 // candidates are tested in candidate order as point masses -- token c is
@@ -78,7 +80,7 @@ void la_argmax_launch(const float* logits, int rows, int V, int32_t* out, hipStr
 }
 
 // ---------------------------------------------------------------- greedy
-__global__ void greedy_accept_kernel(const int32_t* amax, int n_inp, const int32_t* cand, int C, int S,
+__global__ void greedy_accept_kernel(const int32_t* amax, int n_inp, const int32_t* cand, int C, int S, int hmax,
                                      LaAcceptDev* acc, int32_t* z) {
   __shared__ int hits[64];
   const int t = threadIdx.x;
@@ -86,7 +88,7 @@ __global__ void greedy_accept_kernel(const int32_t* amax, int n_inp, const int32
   for (int c = t; c < 64; c += blockDim.x) {
     int a = 0;
     if (c < C) {
-      while (a < S) {
+      while (a < hmax) {
         const int za = a == 0 ? amax[0] : amax[gbase + c * S + a - 1];
         if (cand[c * S + a] != za) break;
         ++a;
@@ -108,9 +110,9 @@ __global__ void greedy_accept_kernel(const int32_t* amax, int n_inp, const int32
   }
 }
 
-void la_greedy_accept_launch(const int32_t* amax, int n_inp, const int32_t* cand, int C, int S, LaAcceptDev* acc,
-                             int32_t* z, hipStream_t st) {
-  hipLaunchKernelGGL(greedy_accept_kernel, dim3(1), dim3(64), 0, st, amax, n_inp, cand, C, S, acc, z);
+void la_greedy_accept_launch(const int32_t* amax, int n_inp, const int32_t* cand, int C, int S, int hmax,
+                             LaAcceptDev* acc, int32_t* z, hipStream_t st) {
+  hipLaunchKernelGGL(greedy_accept_kernel, dim3(1), dim3(64), 0, st, amax, n_inp, cand, C, S, hmax, acc, z);
 }
 
 // ---------------------------------------------------------------- sampling
@@ -209,8 +211,8 @@ __device__ void exclude(double* e, double* bs, int V, const int* rej, int nrej) 
 
 __global__ void __launch_bounds__(256) sample_accept_kernel(const float* logits, int V, int n_inp,
                                                             const int32_t* amax, const int32_t* cand, int C, int S,
-                                                            double T, uint64_t seed, int round_id, double* e,
-                                                            LaAcceptDev* acc, int32_t* z) {
+                                                            int hmax, double T, uint64_t seed, int round_id,
+                                                            double* e, LaAcceptDev* acc, int32_t* z) {
   __shared__ double bs[MAXBLK];
   __shared__ float red[256];
   __shared__ int surv[64];
@@ -226,7 +228,7 @@ __global__ void __launch_bounds__(256) sample_accept_kernel(const float* logits,
   }
   __syncthreads();
   int n_emit = 0;
-  for (int a = 0; a <= S; ++a) {
+  for (int a = 0; a <= hmax; ++a) {
     const int row = a == 0 ? 0 : gbase + surv[0] * S + a - 1;
     row_masses(logits + (size_t)row * V, V, T, e, bs, red);
     if (threadIdx.x == 0) {
@@ -236,7 +238,7 @@ __global__ void __launch_bounds__(256) sample_accept_kernel(const float* logits,
       double remaining = Z;
       int nrej = 0;
       accepted = -1;
-      if (a < S) {
+      if (a < hmax) {
         int k = 0;
         for (int si = 0; si < nsurv && accepted < 0; ++si) {
           const int tok = cand[surv[si] * S + a];
@@ -279,10 +281,10 @@ __global__ void __launch_bounds__(256) sample_accept_kernel(const float* logits,
 }
 
 void la_sample_accept_launch(const float* logits, int V, int n_inp, const int32_t* amax, const int32_t* cand,
-                               int C, int S, double T, uint64_t seed, int round_id, double* scratch,
+                               int C, int S, int hmax, double T, uint64_t seed, int round_id, double* scratch,
                                LaAcceptDev* acc, int32_t* z, hipStream_t st) {
-  hipLaunchKernelGGL(sample_accept_kernel, dim3(1), dim3(256), 0, st, logits, V, n_inp, amax, cand, C, S, T, seed,
-                     round_id, scratch, acc, z);
+  hipLaunchKernelGGL(sample_accept_kernel, dim3(1), dim3(256), 0, st, logits, V, n_inp, amax, cand, C, S, hmax, T,
+                     seed, round_id, scratch, acc, z);
 }
 
 // plain target sample of row 0 (first token after prefill; autoregressive sampling)

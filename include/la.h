@@ -117,7 +117,13 @@ typedef struct la_config {
                                after the pinned one-column advance every level drops its first
                                h entries and its tail is refilled with the newest committed
                                token; 0: ALWAYS_FWD_ONE=True (pinned) */
-  int32_t reserved[1];
+  int32_t cap_full_match;   /* 1: the capped full-match convention ("M7.3", 0x05A names the
+                               implementation's max_hit count beside the paper's full match plus
+                               one extra target token): at most S - 1 candidate tokens are
+                               accepted per round, so a round emits at most S tokens and copies
+                               at most S - 1 K/V rows; 0: a full match of S tokens also emits the
+                               target token read from its last row (S + 1 tokens).  The output
+                               is exact either way; only accepted lengths differ */
 } la_config;
 
 /* Buffer sizes for a (config, dims) pair.  The caller allocates
@@ -178,37 +184,62 @@ typedef struct la_ctx la_ctx;
 
 /* ------------------------------------------------------------- lifecycle */
 
-/* Sizes of the caller-provided buffers.  LA_EINVAL for an inadmissible
- * config (N < 3, W < 1, G < 0, N > LA_MAX_N, bad dims). */
+/* Sizes of the caller-provided buffers for a (config, dims) pair ("M7.3",
+ * 0x01A: the round's coordinate system and admission are fixed before any
+ * state; 0x05C: rows per round, (W + G)(N - 1) when warm).  cfg, dims: host,
+ * read only; out: host, written on success.  LA_EINVAL, with nothing
+ * written, for an inadmissible config: N < 3 or N > LA_MAX_N, W < 1 or
+ * W > 64, G < 0 or G > 64, bad dims, or a largest round the kernels do not
+ * take (more than 256 packed rows, a branch reaching more than 64 positions
+ * past the committed prefix, d_model beyond 2048 16-byte vectors a row). */
 int la_query_sizes(const la_config* cfg, const la_model_dims* dims, la_sizes* out);
 
-/* Validate, clear the pool, seed the window from the prompt (level 0 holds
- * the last W + N - 3 prompt tokens, cyclically), prefill the prompt (plain
- * causal forward; its K/V land in kv rows 0..P-1) and select the first
- * output token.  kv/arena: device buffers of at least la_query_sizes bytes.
- * prompt: host [prompt_len], 1 <= prompt_len <= cfg->max_prompt. */
+/* Create a request ("M7.3", 0x03A lifecycle step 1: window and pool set-up;
+ * 0x06 loop set-up): validate and admit as la_query_sizes, clear the pool
+ * (or seed it with the prompt's N-grams under pool_from_prompt), seed the
+ * window from the prompt (level 0 holds the last W + N - 3 prompt tokens,
+ * cyclically), prefill the prompt (one plain causal forward; its K/V land in
+ * kv rows 0..P-1) and select the first output token from its last row.
+ * weights: device pointers (la_model); kv/arena: device buffers of at least
+ * la_query_sizes bytes, 256-byte aligned, borrowed until la_destroy; prompt:
+ * host [prompt_len], 1 <= prompt_len <= cfg->max_prompt, tokens in
+ * [0, vocab); *out receives the context (NULL on error).  LA_EINVAL for bad
+ * arguments, LA_EDEVICE for a HIP failure (no context is created). */
 int la_init(const la_config* cfg, const la_model_dims* dims, const la_model* weights, void* kv, void* arena,
             const int32_t* prompt, int32_t prompt_len, void* stream, la_ctx** out);
+/* Release a context (its host state and events); the borrowed device
+ * buffers stay the caller's.  NULL is ignored. */
 void la_destroy(la_ctx* ctx);
 
-/* One full round: la_predict, la_verify on the round's logits, la_commit.
- * Writes the round's emitted tokens (after truncation at max_new) to
- * out_tokens (host, cap entries); n_out receives their number (0 once
- * max_new tokens exist).  LA_EOVERFLOW if cap is too small. */
+/* One full round ("M7.3", 0x06 loop: predict, verify, publish): la_predict,
+ * la_verify on the round's own logits, la_commit.  Writes the round's
+ * emitted tokens (after truncation at max_new) to out_tokens (host, cap
+ * entries); n_out receives their number (0 once max_new tokens exist).
+ * LA_EOVERFLOW if cap < N; any error of the three steps is returned with
+ * the round unpublished. */
 int la_step(la_ctx* ctx, int32_t* out_tokens, int32_t cap, int32_t* n_out);
 
-/* Run rounds until max_new tokens exist; out_tokens (host) receives the
- * whole output (first token included); n_out its length. */
+/* Run rounds ("M7.3", 0x06) until max_new tokens exist; out_tokens (host,
+ * cap >= max_new entries, else LA_EOVERFLOW) receives the whole output,
+ * first token included; n_out its length. */
 int la_generate(la_ctx* ctx, int32_t* out_tokens, int32_t cap, int32_t* n_out);
 
 /* ------------------------------------------------------- round, in steps */
 
-/* Predict: look up <= G suffixes for the current token (after warmup),
- * compile the packed rows, run the target forward.  Mutates nothing that
- * la_commit publishes.  LA_ESTATE if a predicted round is pending commit. */
+/* Predict ("M7.3", 0x03A lifecycle steps 2-4; 0x04A row records and
+ * visibility; 0x04C one causal forward over the uncached rows): look up
+ * <= G suffixes for the current token (after warmup), compile the packed
+ * rows, run the target forward and the LM head on the out / inp / guess
+ * rows.  info (host, may be NULL) receives the round's description; its
+ * logits pointer stays valid until the next la_predict.  Mutates nothing
+ * that la_commit publishes.  LA_ESTATE if a predicted round is pending
+ * commit or max_new tokens exist; LA_EOVERFLOW if the K/V capacity is
+ * exhausted. */
 int la_predict(la_ctx* ctx, la_round_info* info);
 
-/* Verify (pure: no request state changes).  logits: device
+/* Verify ("M7.3", 0x05A greedy survivor matching, 0x05B exact one-hot
+ * sampling; 0x06A the publication plan's output part), pure: no request
+ * state changes.  logits: device
  * [1 + n_inp + C*S][vocab] fp32 laid out like la_round_info.logits, or NULL
  * for the pending round's own logits.  cand: host [C][S] suffixes in pool
  * order (NULL with logits == NULL: the pending round's candidates).
@@ -218,8 +249,11 @@ int la_predict(la_ctx* ctx, la_round_info* info);
 int la_verify(la_ctx* ctx, const float* logits, int32_t n_inp, const int32_t* cand, int32_t C, la_accept* out,
               int32_t* z);
 
-/* Publish one accepted path of the pending round, fail-closed: the plan is
- * validated first (round_id of the pending round, 0 <= h <= S, winner in
+/* Publish one accepted path of the pending round ("M7.3", 0x06B output and
+ * K/V frontiers, 0x06C compaction, 0x03B / 0x03C pool then window, 0x07
+ * fail-closed publication).  The plan is
+ * validated first (round_id of the pending round, 0 <= h <= hmax (S, or
+ * S - 1 under cap_full_match), winner in
  * [0, C) iff h > 0, n_emit = h + 1, emitted[0..h-1] equal the winner's
  * suffix, tokens in range, K/V capacity); only then are the winner's h K/V
  * rows copied behind the ordinary row, the W new n-grams upserted into the
@@ -230,21 +264,31 @@ int la_commit(la_ctx* ctx, const la_accept* acc);
 
 /* -------------------------------------------------------- pool and state */
 
-/* Suffixes stored for key, least recently used first (at most G).
- * out: host [G][S]; n receives the count. */
+/* Suffixes stored for key ("M7.3", 0x03 lookup of the live token's list,
+ * 0x03B order), least recently used first (at most G).  out: host [G][S];
+ * n (host) receives the count.  LA_EINVAL for a key outside [0, vocab). */
 int la_pool_lookup(la_ctx* ctx, int32_t key, int32_t* out, int32_t* n);
 
-/* Upsert n (key, suffix) pairs in order with the per-key LRU rule.
- * keys: host [n]; suffixes: host [n][S]. */
+/* Upsert n (key, suffix) pairs in order with the per-key LRU rule ("M7.3",
+ * 0x03B).  keys: host [n], suffixes: host [n][S], tokens in [0, vocab);
+ * 0 <= n <= 64 per call.  LA_EINVAL for bad tokens or sizes, LA_ESTATE
+ * while a predicted round is pending (the pool may only change between
+ * rounds, 0x03C). */
 int la_pool_insert(la_ctx* ctx, const int32_t* keys, const int32_t* suffixes, int32_t n);
 
-/* Host snapshot of the request state; window (host, may be NULL) receives
- * [R][win_stride] tokens, output (host, may be NULL) up to out_cap tokens. */
+/* Host snapshot of the request state ("M7.3", 0x01A manifest: round id,
+ * window, K/V length, output): st (host) receives the counters and level
+ * sizes; window (host, may be NULL) receives [R][win_stride] tokens, output
+ * (host, may be NULL) up to out_cap tokens. */
 int la_get_state(la_ctx* ctx, la_state_t* st, int32_t* window, int32_t* output, int32_t out_cap);
 
+/* Acceptance counters ("M7.3", 0x05: the step-compression statistics a
+ * round produces): rounds, tokens, candidates, accepted and the histogram of
+ * emitted counts.  out: host.  LA_EINVAL for NULL arguments. */
 int la_stats(const la_ctx* ctx, la_stats_t* out);
 
-/* Opt-in kernel timing: while enabled, every GEMM launch (projections, MLP,
+/* Opt-in kernel timing (measurement of "M7.3", 0x05C's cost terms: weight
+ * stream and attention per round): while enabled, every GEMM launch (projections, MLP,
  * LM head, with their split reductions) and every attention launch (with
  * its span merge) of the context's rounds is bracketed by HIP events on the
  * context's stream; elapsed times are accumulated at each verification sync,
@@ -256,8 +300,10 @@ typedef struct la_profile_t {
   double attn_ms, attn_bytes, attn_flops;
   int64_t gemm_launches, attn_launches;
 } la_profile_t;
-int la_profile(la_ctx* ctx, int32_t enable);
+int la_profile(la_ctx* ctx, int32_t enable);     /* LA_ESTATE while a round is pending */
 int la_profile_read(const la_ctx* ctx, la_profile_t* out);
+/* Message of the last error on ctx (or of this thread's last context-free
+ * call when ctx is NULL); owned by the library, valid until the next call. */
 const char* la_last_error(const la_ctx* ctx);
 
 /* ------------------------------------------------ context-free operators */
@@ -280,7 +326,13 @@ const char* la_last_error(const la_ctx* ctx);
  * branch's path length and the value names a packed row other than the
  * ordinary one, else -1.  The attention kernel reads these per-tile tables
  * for the keys past the committed prefix.  window: device [R][win_stride] tokens; cand:
- * device [C][S].  la_rows_query fills info without launching anything. */
+ * device [C][S].  la_rows_query fills info (host) without launching
+ * anything; la_build_rows launches one kernel on stream and returns (out is
+ * complete once the stream reaches it).  Errors: LA_EINVAL for a bad
+ * descriptor (R or S outside 1..16, C outside 0..64, a level longer than
+ * win_stride, levels not nested column by column, more than 1024 rows) or a
+ * NULL pointer; LA_EOVERFLOW when the round's tables exceed the builder's
+ * LDS. */
 typedef struct la_rows_desc {
   int32_t p;                /* logical position of the ordinary row */
   int32_t R;                /* levels */
@@ -314,7 +366,13 @@ int la_build_rows(const la_rows_desc* desc, const int32_t* window, const int32_t
  * positions whose length depends on t_cap only (128 positions while t_cap
  * <= 1024, else about a quarter of t_cap rounded up to 128 positions).  Batch invariant: a row's result does not
  * depend on the other rows of the call (its reduction tree is a function of
- * key positions and t_cap only). */
+ * key positions and t_cap only).  The call only launches (on stream).
+ * Errors: LA_EINVAL for a NULL pointer, an unknown dtype, H not a multiple
+ * of Hkv, shared_end outside [1, t_cap], ws_cap < Q - 1, or a shape the
+ * kernel does not take (dh other than 64/128 in bf16 or 16/64 in fp32, a
+ * row reaching more than 64 positions past shared_end); LA_EOVERFLOW for a
+ * workspace smaller than la_attention_workspace; LA_EDEVICE for a failed
+ * launch. */
 size_t la_attention_workspace(int32_t Q, int32_t H, int32_t dh, int32_t max_pos, int32_t t_cap);
 int la_attention(int32_t dtype, const void* q, const void* k_cache, const void* v_cache, int32_t t_cap,
                  const void* k_ws, const void* v_ws, int32_t ws_cap, int32_t H, int32_t Hkv, int32_t dh,
@@ -339,7 +397,10 @@ int la_attention(int32_t dtype, const void* q, const void* k_cache, const void* 
  * la_pack_linear: W -> Wp (la_packed_linear_bytes bytes, device, 256-byte
  * aligned), the layout la_pack_weights uses; la_linear_packed: the same
  * product from a packed Wp, workspace as for la_linear (its first
- * la_packed_linear_bytes, rounded up to 256, are not used). */
+ * la_packed_linear_bytes, rounded up to 256, are not used).  The calls only
+ * launch (on stream).  Errors: LA_EINVAL for a NULL pointer, an unknown
+ * dtype or epilogue, or a shape outside the bounds above; LA_EOVERFLOW for
+ * a short workspace; LA_EDEVICE for a failed launch. */
 enum { LA_LINEAR_STORE = 0, LA_LINEAR_RESIDUAL = 1, LA_LINEAR_SWIGLU = 2, LA_LINEAR_F32 = 3 };
 size_t la_linear_workspace(int32_t dtype, int32_t epilogue, int32_t M, int32_t N, int32_t K);
 int la_linear(int32_t dtype, int32_t epilogue, const void* X, const void* W, void* Y, const void* R, int32_t M,

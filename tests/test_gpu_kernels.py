@@ -361,7 +361,7 @@ def test_pool_upserts_match_oracle(verify_session):
         sufs = rng.integers(0, 3, (n, S))
         sess.la_pool_insert(keys, sufs)
         for k, s in zip(keys, sufs):
-            opool.upsert_suffix_lru(tm, int(k), tuple(int(t) for t in s), G)
+            opool.lru_upsert(tm, int(k), tuple(int(t) for t in s), G)
             keys_used.add(int(k))
     for k in sorted(keys_used) + [100, 31999]:
         assert sess.la_pool_lookup(k) == opool.lookup(tm, k, G), k

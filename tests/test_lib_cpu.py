@@ -46,10 +46,11 @@ def test_invalid_configs_rejected():
 
 
 def test_option_flags_validated():
-    """pool_from_prompt and advance_by_accepted are 0 or 1."""
+    """pool_from_prompt, advance_by_accepted and cap_full_match are 0 or 1."""
     d = la.dims_struct(synthetic.PRESETS["tiny"])
-    la.la_query_sizes(la.make_config(5, 3, 5, 10, 10, pool_from_prompt=True, advance_by_accepted=True), d)
-    for field in ("pool_from_prompt", "advance_by_accepted"):
+    la.la_query_sizes(la.make_config(5, 3, 5, 10, 10, pool_from_prompt=True, advance_by_accepted=True,
+                                     cap_full_match=True), d)
+    for field in ("pool_from_prompt", "advance_by_accepted", "cap_full_match"):
         cfg = la.make_config(5, 3, 5, 10, 10)
         setattr(cfg, field, 2)
         with pytest.raises(la.LaError) as e:
@@ -111,3 +112,49 @@ def test_rows_query_matches_oracle(sizes, starts, C, S):
     assert info.Q == comp.Q
     assert info.n_inp == len(comp.inp)
     assert info.n_logit == 1 + len(comp.inp) + len(comp.guess)
+
+
+@pytest.mark.parametrize("W,N,G,why", [
+    (40, 8, 5, "rows"),        # (W + G) * (N - 1) = 315 packed rows: above one GEMM launch's 256
+    (60, 10, 5, "rows"),       # 585 rows
+    (62, 3, 64, "rows"),       # 252 lookahead + 126 verification rows
+    (64, 4, 0, "reach"),       # 192 rows, but the first warmup fill's last column reaches 65 positions
+    (63, 4, 0, None),          # 189 rows, 64 positions: admitted
+    (15, 7, 15, None),         # the 34B-shaped workload: 180 rows
+])
+def test_round_shapes_admitted_before_state(W, N, G, why):
+    """A config whose largest round exceeds what the round's kernels take is
+    refused by la_query_sizes (and la_init) with LA_EINVAL, before any state
+    exists ("M7.3", 0x01A admission), instead of failing at its first warm
+    round: more than 256 packed rows (one GEMM launch), or a branch reaching
+    more than 64 positions past the committed prefix (the attention's path
+    table)."""
+    d = la.dims_struct(synthetic.PRESETS["llama7b"])
+    cfg = la.make_config(W, N, G, 64, 100)
+    rows = (W + G) * (N - 1)
+    reach = W + N - 3           # the farthest row (last column of level 0 at the first warmup round) past the ordinary row
+    if rows <= 256 and reach <= 64:
+        s = la.la_query_sizes(cfg, d)
+        assert s.q_max == rows
+        return
+    with pytest.raises(la.LaError) as e:
+        la.la_query_sizes(cfg, d)
+    assert e.value.code == la.LA_EINVAL
+    msg = str(e.value)
+    assert ("packed rows" in msg) if rows > 256 else ("positions past" in msg), msg
+
+
+def test_d_model_bound_admitted():
+    """The embedding gather and the residual-fold RMSNorm hold a row in 2048
+    16-byte vectors: bf16 d_model up to 16384, fp32 up to 8192."""
+    import dataclasses
+    base = synthetic.PRESETS["llama7b"]
+    cfg = la.make_config(7, 5, 7, 64, 100)
+    la.la_query_sizes(cfg, la.dims_struct(dataclasses.replace(base, d_model=16384)))
+    with pytest.raises(la.LaError) as e:
+        la.la_query_sizes(cfg, la.dims_struct(dataclasses.replace(base, d_model=16384 + 128)))
+    assert e.value.code == la.LA_EINVAL
+    f32 = dataclasses.replace(base, dtype="f32", d_model=8192 + 64)
+    with pytest.raises(la.LaError) as e:
+        la.la_query_sizes(cfg, la.dims_struct(f32))
+    assert e.value.code == la.LA_EINVAL
