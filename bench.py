@@ -5,31 +5,26 @@
 
 A step is one full round (pool lookup, row manifest, target forward over the
 packed rows, LM head on the required rows, verification, K/V commit, pool
-upsert, window advance) through the C ABI's la_step.  Default workload: a
-Llama-2-7B-shaped random-init bf16 decoder (32 layers, d 4096, 32 heads,
-MLP 11008, vocab 32000), 512-token prompt from the seeded order-2 Markov
-chain, greedy lookahead with W=7, N=5, G=7, 256 new tokens.  Weights and
-prompt are resident in HBM before timing; prefill is outside the timed
-region.  value = emitted tokens / wall time of the K timed rounds.
+upsert, window advance) through the C ABI's la_step.  Default workload, the
+largest configuration that fits one GPU: a CodeLlama-34B-shaped random-init
+bf16 decoder (48 layers, d 8192, 64 query heads on 8 KV heads, MLP 22016,
+vocab 32000), 2048-token prompt from the seeded order-2 Markov chain with
+~30% copied spans, greedy lookahead with W=15, N=7, G=15, 256 new tokens,
+batch 1.  Weights and prompt are resident in HBM before timing; prefill is
+outside the timed region.  value = emitted tokens / wall time of the K timed
+rounds (K = --steps; 0 times one complete generation).
 
-Also reported on the same line:
+Also on the same line:
   * roofline: the dominant kernel of the step (the batch-invariant GEMM that
-    streams the weights), algorithmic bytes per launch over its average
+    streams the weights): algorithmic bytes per launch over its average
     launch time from HIP events on the library's stream;
-  * lookahead_attn: the isolated lookahead-mask attention op (bf16, 32 heads
-    x 128, committed prefix 1024, 121 query rows: W=15, N=5, G=15 with the
-    rectangular window), timed with HIP events over rotating input sets that
-    exceed the 256 MB Infinity Cache;
-  * lookahead_attn_8192: the same op over 8192 committed keys (the
-    long-prefix workload's per-layer shape, 134 MB of K/V per call);
-  * lookahead_attn_34b_gqa: the op at the 34B-shaped round's per-layer shape
-    (64 query heads on 8 KV heads, N=7: 180 rows, 2048 committed keys);
-  * step_roofline: the round against the HBM bound (streamed weight bytes
-    plus the committed K/V read at the mean committed length, over 8 TB/s);
-  * init_prefill_ms: context set-up and prompt prefill (wall clock, untimed
-    in value);
-  * ar_tokens_per_s: plain autoregressive decoding with the same kernels;
-  * cpu_baseline: the CPU oracle on a bounded sample of the same workload.
+  * cpu_baseline: the CPU oracle on a bounded slice of the same workload;
+  * lookahead_attn (+ _8192, _34b_gqa): the isolated lookahead-mask attention
+    op, bf16, timed with HIP events over rotating input sets larger than the
+    256 MB Infinity Cache;
+  * extra_workloads: the 7B-shaped workloads (512-token prompt, W=7 N=5 G=7;
+    8192-token prompt, W=15 N=5 G=15 greedy and temperature-0.7 sampled over
+    five prompt/sampler seeds), each with the same round measurements.
 """
 import argparse
 import json
@@ -42,15 +37,17 @@ sys.path.insert(0, ROOT)
 
 METRIC = "accepted tokens/sec per sequence + lookahead-attn HBM GB/s (% of peak), 1 GPU"
 HBM_PEAK_GBS = 8000.0
+HEADLINE = "codellama34b_w15n7g15"
 
 WORKLOADS = {
+    "codellama34b_w15n7g15": dict(model="codellama34b", W=15, N=7, G=15, prompt=2048, max_new=256, copyspan=True,
+                                  desc=("CodeLlama-34B-shaped bf16 decoder (48 layers, GQA 64/8 heads), 2048-token "
+                                        "Markov prompt with ~30% copied spans, greedy lookahead W=15 N=7 G=15, "
+                                        "256 new tokens, batch 1")),
     "llama7b_w7n5g7": dict(model="llama7b", W=7, N=5, G=7, prompt=512, max_new=256, desc=(
         "Llama-2-7B-shaped bf16 decoder, 512-token Markov prompt, greedy lookahead W=7 N=5 G=7, 256 new tokens")),
     "llama7b_long_w15n5g15": dict(model="llama7b", W=15, N=5, G=15, prompt=8192, max_new=256, desc=(
-        "Llama-2-7B-shaped bf16 decoder, 8192-token Markov prompt, greedy lookahead W=15 N=5 G=15")),
-    "codellama34b_w15n7g15": dict(model="codellama34b", W=15, N=7, G=15, prompt=2048, max_new=256, copyspan=True, desc=(
-        "CodeLlama-34B-shaped bf16 decoder (GQA 64/8 heads), 2048-token Markov prompt with 30% copied spans, "
-        "greedy lookahead W=15 N=7 G=15, 256 new tokens")),
+        "Llama-2-7B-shaped bf16 decoder, 8192-token Markov prompt, lookahead W=15 N=5 G=15, 256 new tokens")),
     "tiny_w5n3g5": dict(model="tiny", W=5, N=3, G=5, prompt=32, max_new=64, desc=(
         "tiny fp32 decoder (2 layers, d 64), 32-token Markov prompt, greedy lookahead W=5 N=3 G=5, 64 new tokens")),
 }
@@ -58,6 +55,14 @@ WORKLOADS = {
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def make_prompt(wl, dims, seed=0):
+    import synthetic
+    if wl.get("copyspan"):
+        prompt, copied = synthetic.copyspan_prompt(dims.vocab, wl["prompt"], seed)
+        return prompt, copied
+    return synthetic.markov_prompt(dims.vocab, wl["prompt"], seed), 0.0
 
 
 def step_roofline(model, dims, wl, tokens, steps, secs):
@@ -96,19 +101,91 @@ def run_steps(make_session, sess, steps):
     while done < steps:
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        n_here = 0
         while done < steps:
             out = sess.la_step()
             if not out:
                 break
             tokens += len(out)
             done += 1
-            n_here += 1
         torch.cuda.synchronize()
         elapsed += time.perf_counter() - t0
         if done < steps:
             sess = make_session()
     return tokens, elapsed, sess, done
+
+
+def kernel_rates(pr):
+    """Per-launch averages of the GEMM and attention launches from la_profile's HIP events."""
+    g_ms, a_ms = pr["gemm_ms"], pr["attn_ms"]
+    return {
+        "gemm_launches": pr["gemm_launches"],
+        "gemm_avg_launch_us": g_ms / max(1, pr["gemm_launches"]) * 1e3,
+        "gemm_bytes_per_launch": pr["gemm_bytes"] / max(1, pr["gemm_launches"]),
+        "gemm_GBps": pr["gemm_bytes"] / (g_ms * 1e-3) / 1e9 if g_ms > 0 else 0.0,
+        "gemm_ms_total": g_ms,
+        "attn_launches": pr["attn_launches"],
+        "attn_avg_launch_us": a_ms / max(1, pr["attn_launches"]) * 1e3,
+        "attn_GBps": pr["attn_bytes"] / (a_ms * 1e-3) / 1e9 if a_ms > 0 else 0.0,
+        "attn_ms_total": a_ms,
+    }
+
+
+def measure(model, dims, wl, steps, warmup, verify="greedy", temperature=0.7, seed=0, with_ar=True,
+            with_profile=True, pool_from_prompt=False):
+    """Lookahead rounds of one workload (prompt and sampler seed `seed`): tokens/s,
+    rounds, the same generation autoregressively with the same kernels, and a
+    separate HIP-event pass over the GEMM and attention launches."""
+    import torch
+    import exact_lookahead_decoding_amd.la as la
+    prompt, copied = make_prompt(wl, dims, seed)
+    vm = la.LA_VERIFY_SAMPLE if verify == "sample" else la.LA_VERIFY_GREEDY
+
+    def make(ar=False, profile=False):
+        s = la.Session(model, prompt, W=wl["W"], N=wl["N"], G=wl["G"], max_new=wl["max_new"], ar_only=ar,
+                       verify_mode=vm, temperature=temperature, seed=seed,
+                       pool_from_prompt=pool_from_prompt and not ar)
+        if profile:
+            s.la_profile(True)
+        return s
+
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    sess = make()
+    torch.cuda.synchronize()
+    init_prefill_ms = (time.perf_counter() - t) * 1e3
+    for _ in range(warmup):
+        sess.la_step()
+    tokens, secs, sess, done = run_steps(make, sess, steps)
+    st = sess.la_stats()
+    res = {"value": tokens / secs, "tokens": tokens, "rounds": done, "ms_per_round": secs * 1e3 / done,
+           "tokens_per_round": tokens / done, "init_prefill_ms": init_prefill_ms,
+           "step_roofline": step_roofline(model, dims, wl, tokens, done, secs),
+           "accepted_hist": st["hist"][: wl["N"] + 2], "copied_fraction": copied}
+    log(f"  lookahead: {tokens} tokens in {done} rounds, {res['ms_per_round']:.3f} ms/round, "
+        f"{res['value']:.1f} tokens/s, {res['tokens_per_round']:.3f} tokens/round")
+    if with_ar:
+        ar = make(ar=True)
+        for _ in range(warmup):
+            ar.la_step()
+        ar_tokens, ar_secs, _, ar_done = run_steps(lambda: make(ar=True), ar, steps)
+        res["ar_tokens_per_s"] = ar_tokens / ar_secs
+        res["ar_ms_per_step"] = ar_secs * 1e3 / ar_done
+        res["speedup_vs_ar"] = res["value"] / res["ar_tokens_per_s"]
+        log(f"  autoregressive: {ar_tokens} tokens in {ar_done} steps, {res['ar_tokens_per_s']:.1f} tokens/s")
+    if with_profile:
+        prof = make(profile=True)
+        for _ in range(warmup):
+            prof.la_step()
+        prof.la_profile(True)
+        _, psecs, pend, pdone = run_steps(lambda: make(profile=True), prof, steps)
+        rates = kernel_rates((pend if steps == 0 else prof).la_profile_read())
+        rates["share_of_round_gemm"] = rates["gemm_ms_total"] / (psecs * 1e3)
+        rates["share_of_round_attn"] = rates["attn_ms_total"] / (psecs * 1e3)
+        res["kernels"] = rates
+        log(f"  gemm: {rates['gemm_launches']} launches, avg {rates['gemm_avg_launch_us']:.1f} us, "
+            f"{rates['gemm_GBps']:.0f} GB/s, {rates['share_of_round_gemm'] * 100:.0f}% of the rounds; attention: "
+            f"avg {rates['attn_avg_launch_us']:.1f} us, {rates['attn_GBps']:.0f} GB/s")
+    return res
 
 
 def attention_op(reps=200, sets=16, p=1024, H=32, Hkv=32, N=5):
@@ -131,7 +208,7 @@ def attention_op(reps=200, sets=16, p=1024, H=32, Hkv=32, N=5):
     rows, info = la.la_build_rows(desc, win, cand)
     Q = info.Q
     g = torch.Generator(device="cuda").manual_seed(0)
-    mk = lambda *s: torch.randn(*s, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    mk = lambda *s: torch.randn(*s, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)  # noqa
     bufs = [(mk(Q, H, dh), mk(Hkv, p + 8, dh), mk(Hkv, p + 8, dh), mk(Hkv, Q, dh), mk(Hkv, Q, dh))
             for _ in range(sets)]
     ws = torch.empty(la.load().la_attention_workspace(Q, H, dh, p + 1 + info.maxp, p + 8), dtype=torch.uint8,
@@ -158,15 +235,20 @@ def attention_op(reps=200, sets=16, p=1024, H=32, Hkv=32, N=5):
     ms = float(np.mean([a.elapsed_time(b) for a, b in ev])) / sets
     reps = n_rep * sets
     alg = 2 * Hkv * p * dh * 2 + Q * Hkv * dh * 2 * 2 + 2 * Q * H * dh * 2
+    flops = 4.0 * Q * H * dh * (p + 1 + info.maxp)
     gbs = alg / (ms * 1e-3) / 1e9
     kv_gbs = (2 * Hkv * p * dh * 2) / (ms * 1e-3) / 1e9
     heads = f"{H} heads" if H == Hkv else f"{H} query heads on {Hkv} KV heads"
     return {"workload": f"lookahead-mask attention, bf16, {heads} x 128, prefix {p}, {Q} rows (W=15 N={N} G=15)",
             "avg_us": ms * 1e3, "algorithmic_bytes": alg, "achieved_GBps": gbs, "kv_stream_GBps": kv_gbs,
-            "peak_GBps": HBM_PEAK_GBS, "frac": gbs / HBM_PEAK_GBS, "reps": reps, "input_sets": sets}
+            "peak_GBps": HBM_PEAK_GBS, "frac": gbs / HBM_PEAK_GBS, "mfma_TFLOPs": flops / (ms * 1e-3) / 1e12,
+            "reps": reps, "input_sets": sets}
 
 
-TRAFFIC_MD = os.path.join(ROOT, "profiles", "la_gemm_kernel_llama7b_w7n5g7_hbm_traffic.md")
+ATTN_OPS = [dict(), dict(reps=24, sets=4, p=8192), dict(reps=64, sets=32, p=2048, H=64, Hkv=8, N=7)]
+ATTN_KEYS = ["lookahead_attn", "lookahead_attn_8192", "lookahead_attn_34b_gqa"]
+
+TRAFFIC_MD = os.path.join(ROOT, "profiles", "la_gemm_kernel_{wl}_hbm_traffic.md")
 GEMM_SRC = os.path.join(ROOT, "exact_lookahead_decoding_amd", "csrc", "la_gemm.hip")
 COPY_BYTES = 1 << 30
 
@@ -176,11 +258,11 @@ def _sha256(path):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()
 
 
-def gemm_traffic():
-    """HBM bytes per round GEMM launch from the committed counter summary, or
-    None when the GEMM source changed since the counters were taken."""
+def gemm_traffic(wl_name):
+    """HBM bytes per round GEMM launch from the committed counter summary of the
+    workload, or None when the GEMM source changed since the counters were taken."""
     try:
-        txt = open(TRAFFIC_MD).read()
+        txt = open(TRAFFIC_MD.format(wl=wl_name)).read()
     except OSError:
         return None
     vals = dict(l.split(":", 1) for l in txt.splitlines() if l.startswith(("traffic_bytes_per_launch:",
@@ -190,83 +272,159 @@ def gemm_traffic():
     return float(vals["traffic_bytes_per_launch"])
 
 
-def pmc_sample(rounds=16):
-    """The workload rounds whose GEMM dispatches the counter runs read, then a
-    plain copy of COPY_BYTES that calibrates FETCH_SIZE / WRITE_SIZE."""
+def profile_rounds(wl_name, rounds, warmup=5):
+    """The workload's lookahead rounds alone (after prefill and warmup rounds),
+    with HIP events around every GEMM and attention launch, then a plain copy
+    of COPY_BYTES that calibrates the FETCH_SIZE / WRITE_SIZE counters.  The
+    rounds' launches are the last GEMM / attention dispatches of the process
+    before the copy; the JSON line says how many there were."""
     import torch
     import synthetic
     import exact_lookahead_decoding_amd.la as la
     la.load()
     torch.cuda.set_device(0)
-    wl = WORKLOADS["llama7b_w7n5g7"]
+    wl = WORKLOADS[wl_name]
     dims = synthetic.PRESETS[wl["model"]]
     model = la.DeviceModel(dims, seed=0)
-    prompt = synthetic.markov_prompt(dims.vocab, wl["prompt"], 0)
+    prompt, _ = make_prompt(wl, dims, 0)
     sess = la.Session(model, prompt, W=wl["W"], N=wl["N"], G=wl["G"], max_new=wl["max_new"])
+    for _ in range(warmup):
+        sess.la_step()
+    torch.cuda.synchronize()
     sess.la_profile(True)
+    t = time.perf_counter()
     for _ in range(rounds):
         sess.la_step()
     torch.cuda.synchronize()
+    secs = time.perf_counter() - t
     pr = sess.la_profile_read()
     src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0)
     dst = torch.empty_like(src)
     for _ in range(3):
         dst.copy_(src)
     torch.cuda.synchronize()
-    print(json.dumps({"rounds": rounds, "gemm_launches": pr["gemm_launches"],
-                      "gemm_alg_bytes_per_launch": pr["gemm_bytes"] / max(1, pr["gemm_launches"]),
-                      "copy_bytes": COPY_BYTES}), flush=True)
+    print(json.dumps({"workload": wl_name, "rounds": rounds, "ms_per_round": secs * 1e3 / rounds,
+                      "copy_bytes": COPY_BYTES, **kernel_rates(pr)}), flush=True)
 
 
-def pmc_summary(fetch_db, write_db, sample_json):
-    """Per-launch HBM traffic of the round GEMMs (la_gemm_kernel with at most 4
-    row tiles: the prefill chunks use 8) from a FETCH_SIZE and a WRITE_SIZE
-    run of --pmc-sample, each scaled by what the counter reads for the copy."""
-    import collections
-    import re
+def _dispatches(db_or_csv):
+    """(kernel name, duration ns, counter values) per dispatch, in dispatch order,
+    from a rocprofv3 results database or kernel-trace CSV."""
+    if db_or_csv.endswith(".csv"):
+        import csv
+        rows = []
+        with open(db_or_csv) as f:
+            for r in csv.DictReader(f):
+                rows.append((int(r.get("Dispatch_Id", len(rows))), r["Kernel_Name"],
+                             int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+        rows.sort()
+        return [(k, d, {}) for _, k, d in rows]
     import sqlite3
+    con = sqlite3.connect(db_or_csv)
+    out = {}
+    for d, k, c, v in con.execute("select dispatch_id, kernel_name, counter_name, value from counters_collection"):
+        e = out.setdefault(d, [k, 0, {}])
+        e[2][c] = e[2].get(c, 0.0) + v
+    return [tuple(out[d]) for d in sorted(out)]
 
-    def per_dispatch(db, counter):
-        con = sqlite3.connect(db)
-        rows = con.execute("select dispatch_id, kernel_name, value from counters_collection where counter_name = ?",
-                           (counter,)).fetchall()
-        agg = collections.defaultdict(float)
-        names = {}
-        for d, k, v in rows:
-            agg[d] += v
-            names[d] = k
-        return agg, names
 
+def _round_gemms(disp, n):
+    """The last n GEMM dispatches before the calibration copy."""
+    gemm = [i for i, (k, _, _) in enumerate(disp) if k.startswith("la_gemm_kernel") or
+            k.startswith("void la_gemm_kernel") or "la_gemm_reduce_kernel" in k]
+    return [disp[i] for i in gemm[-n:]]
+
+
+def trace_summary(trace_csv, run_json, out_md, cmd):
+    """Average duration of the rounds' GEMM and attention launches from a
+    rocprofv3 kernel trace, next to the HIP-event averages of the same run."""
+    import collections
+    run = json.loads(open(run_json).read().strip().splitlines()[-1])
+    disp = _dispatches(trace_csv)
+    # a GEMM launch with split K is the GEMM kernel plus its reduction kernel (or, for the
+    # residual projections, nothing: the next RMSNorm folds the partials)
+    names = [k for k, _, _ in disp]
+    g_idx = [i for i, k in enumerate(names) if "la_gemm_kernel" in k or "la_gemm_reduce_kernel" in k]
+    a_idx = [i for i, k in enumerate(names) if "la_attn_kernel" in k or "la_attn_merge_kernel" in k]
+    last_copy = max([i for i, k in enumerate(names) if "copy" in k.lower()] or [len(names)])
+    g_idx = [i for i in g_idx if i < last_copy]
+    a_idx = [i for i in a_idx if i < last_copy]
+    # HIP-event brackets cover a GEMM kernel and its reduction together
+    g_main = [i for i in g_idx if "la_gemm_kernel" in names[i]][-run["gemm_launches"]:]
+    first = g_main[0]
+    g_sel = [i for i in g_idx if i >= first]
+    a_main = [i for i in a_idx if "la_attn_kernel" in names[i]][-run["attn_launches"]:]
+    a_sel = [i for i in a_idx if i >= a_main[0]] if a_main else []
+    g_us = sum(disp[i][1] for i in g_sel) / 1e3 / len(g_main)
+    a_us = sum(disp[i][1] for i in a_sel) / 1e3 / max(1, len(a_main))
+    per = collections.defaultdict(lambda: [0, 0.0])
+    for i in g_sel + a_sel:
+        per[names[i]][0] += 1
+        per[names[i]][1] += disp[i][1] / 1e3
+    lines = [f"# Kernel trace of the rounds: {run['workload']} ({WORKLOADS[run['workload']]['desc']})", "",
+             "Command (run from /tmp with TMPDIR=/tmp on one MI355X):", "", "```", cmd, "```", "",
+             f"{run['rounds']} lookahead rounds after prefill and 5 warmup rounds, "
+             f"{run['ms_per_round']:.3f} ms per round in the traced run.", "",
+             "| kernel | calls | total us | avg us |", "|---|---:|---:|---:|"]
+    for k, (c, t) in sorted(per.items(), key=lambda x: -x[1][1]):
+        lines.append(f"| `{k[:90]}` | {c} | {t:.0f} | {t / c:.2f} |")
+    lines += ["", "| quantity | rocprofv3 trace | HIP events (same run) |", "|---|---:|---:|",
+              f"| GEMM launches | {len(g_main)} | {run['gemm_launches']} |",
+              f"| GEMM average launch (us) | {g_us:.2f} | {run['gemm_avg_launch_us']:.2f} |",
+              f"| GEMM algorithmic bytes per launch (MB) | | {run['gemm_bytes_per_launch'] / 1e6:.2f} |",
+              f"| GEMM GB/s | {run['gemm_bytes_per_launch'] / (g_us * 1e-6) / 1e9:.0f} | {run['gemm_GBps']:.0f} |",
+              f"| attention launches | {len(a_main)} | {run['attn_launches']} |",
+              f"| attention average launch, with split merge (us) | {a_us:.2f} | {run['attn_avg_launch_us']:.2f} |",
+              "", "A GEMM launch is the GEMM kernel plus, where K is split and the output is not a residual,",
+              "its reduction kernel; an attention launch is the attention kernel plus its split merge.", ""]
+    md = "\n".join(lines)
+    open(out_md, "w").write(md)
+    print(md)
+
+
+def pmc_summary(fetch_db, write_db, run_json, wl_name):
+    """Per-launch HBM traffic of the rounds' GEMMs from a FETCH_SIZE and a
+    WRITE_SIZE run of --profile-rounds, each scaled by what the counter reads
+    for the calibration copy."""
+    run = json.loads(open(run_json).read().strip().splitlines()[-1])
     out = {}
     for counter, db in (("FETCH_SIZE", fetch_db), ("WRITE_SIZE", write_db)):
-        agg, names = per_dispatch(db, counter)
-        gemm = [agg[d] for d, k in names.items()
-                if (m := re.search(r"la_gemm_kernel<[^,]+, (\d+),", k)) and int(m.group(1)) <= 4]
-        copy = [agg[d] for d, k in names.items() if "copy" in k.lower()]
-        out[counter] = (gemm, max(copy) if copy else 0.0)
-    sample = json.loads(open(sample_json).read().strip().splitlines()[-1])
-    f_gemm, f_copy = out["FETCH_SIZE"]
-    w_gemm, w_copy = out["WRITE_SIZE"]
-    ff = sample["copy_bytes"] / (f_copy * 1024.0)
-    fw = sample["copy_bytes"] / (w_copy * 1024.0)
-    fetch = sum(f_gemm) / len(f_gemm) * 1024.0 * ff
-    write = sum(w_gemm) / len(w_gemm) * 1024.0 * fw
-    alg = sample["gemm_alg_bytes_per_launch"]
+        disp = _dispatches(db)
+        names = [k for k, _, _ in disp]
+        copies = [i for i, k in enumerate(names) if "copy" in k.lower()]
+        end = copies[0] if copies else len(names)
+        g = [i for i in range(end) if "la_gemm_kernel" in names[i] or "la_gemm_reduce_kernel" in names[i]]
+        main = [i for i in g if "la_gemm_kernel" in names[i]][-run["gemm_launches"]:]
+        sel = [i for i in g if i >= main[0]]
+        tot = sum(disp[i][2].get(counter, 0.0) for i in sel)
+        copy = max(disp[i][2].get(counter, 0.0) for i in copies) if copies else 0.0
+        out[counter] = (tot / len(main), copy, len(main))
+    f_gemm, f_copy, n = out["FETCH_SIZE"]
+    w_gemm, w_copy, _ = out["WRITE_SIZE"]
+    ff = run["copy_bytes"] / (f_copy * 1024.0)
+    fw = run["copy_bytes"] / (w_copy * 1024.0)
+    fetch = f_gemm * 1024.0 * ff
+    write = w_gemm * 1024.0 * fw
+    alg = run["gemm_bytes_per_launch"]
+    wl = WORKLOADS[wl_name]
     return "\n".join([
-        "# HBM traffic of the round GEMM: 7B-shaped lookahead rounds (W=7, N=5, G=7, 512-token prompt)",
+        f"# HBM traffic of the round GEMM: {wl_name} ({wl['desc']})",
         "",
         "Commands (run from /tmp with TMPDIR=/tmp on one MI355X; each counter in a run of its own):",
         "",
         "```",
-        "python3 bench.py --pmc-sample > out/pmc_sample.json",
-        "rocprofv3 --pmc FETCH_SIZE -d out/pmc_fetch -o f -- python3 bench.py --pmc-sample",
-        "rocprofv3 --pmc WRITE_SIZE -d out/pmc_write -o w -- python3 bench.py --pmc-sample",
-        "python3 bench.py --pmc-summary out/pmc_fetch/f_results.db out/pmc_write/w_results.db out/pmc_sample.json",
+        f"python3 bench.py --profile-rounds {run['rounds']} --workload {wl_name} > out/run.json",
+        f"rocprofv3 --pmc FETCH_SIZE -d out/pmc_fetch -o f -- python3 bench.py --profile-rounds {run['rounds']} "
+        f"--workload {wl_name}",
+        f"rocprofv3 --pmc WRITE_SIZE -d out/pmc_write -o w -- python3 bench.py --profile-rounds {run['rounds']} "
+        f"--workload {wl_name}",
+        f"python3 bench.py --pmc-summary out/pmc_fetch/f_results.db out/pmc_write/w_results.db out/run.json "
+        f"--workload {wl_name}",
         "```",
         "",
-        f"The sample runs {sample['rounds']} lookahead rounds after prefill, then copies a "
-        f"{sample['copy_bytes'] >> 20} MiB buffer three times.  Round GEMM dispatches: la_gemm_kernel with at "
-        f"most 4 row tiles ({len(f_gemm)} dispatches; prefill chunks use 8).",
+        f"The run makes {run['rounds']} lookahead rounds after prefill and warmup, then copies a "
+        f"{run['copy_bytes'] >> 20} MiB buffer three times.  Round GEMM launches: the last {n} `la_gemm_kernel` "
+        "dispatches before the copy (with the split-K reductions that follow them).",
         "",
         "| quantity | value |",
         "|---|---:|",
@@ -274,8 +432,8 @@ def pmc_summary(fetch_db, write_db, sample_json):
         f"| copy: WRITE_SIZE (KiB) | {w_copy:.0f} |",
         f"| FETCH_SIZE scale (copy bytes / counter bytes) | {ff:.3f} |",
         f"| WRITE_SIZE scale | {fw:.3f} |",
-        f"| round GEMM: mean FETCH_SIZE per dispatch (KiB) | {sum(f_gemm) / len(f_gemm):.0f} |",
-        f"| round GEMM: mean WRITE_SIZE per dispatch (KiB) | {sum(w_gemm) / len(w_gemm):.0f} |",
+        f"| round GEMM launch: mean FETCH_SIZE (KiB) | {f_gemm:.0f} |",
+        f"| round GEMM launch: mean WRITE_SIZE (KiB) | {w_gemm:.0f} |",
         f"| HBM read per launch, scaled (MB) | {fetch / 1e6:.2f} |",
         f"| HBM write per launch, scaled (MB) | {write / 1e6:.2f} |",
         f"| algorithmic bytes per launch (MB) | {alg / 1e6:.2f} |",
@@ -287,27 +445,49 @@ def pmc_summary(fetch_db, write_db, sample_json):
     ])
 
 
-def cpu_baseline(wl, budget_rounds=2, prefix=32):
-    """The oracle as it stands, on host cores: a `prefix`-token prompt, then `budget_rounds` rounds."""
+def cpu_baseline(wl_name, rounds=1, prefix=32):
+    """The oracle as it stands, on host cores, over a bounded slice of the workload:
+    the same W/N/G and model widths, the first `prefix` tokens of the prompt
+    (prefill untimed), the first steady rounds timed.  For the 34B shape a
+    2-layer slice of the model (its first two layers, same seeded weights) runs
+    and the round time is scaled by 48/2 (the LM head and round bookkeeping,
+    counted 24 times, make the scaled time an overestimate)."""
+    import dataclasses
+    import numpy as np
     import synthetic
     from oracle.decode import lookahead_generate
     from oracle.model import OracleModel
+    wl = WORKLOADS[wl_name]
+    dims = synthetic.PRESETS[wl["model"]]
+    layers = dims.n_layers
+    if wl["model"] == "codellama34b":
+        dims = dataclasses.replace(dims, n_layers=2)
+    t = time.time()
+    w = synthetic.model_weights(dims, 0)
+    gen_s = time.time() - t
+    prompt, _ = make_prompt(wl, dims, 0)
+    prompt = prompt[:prefix]
+    om = OracleModel(dims, w)
+    times = []
+    warm = wl["N"] - 2                      # warmup rounds before the window is complete
+    res = lookahead_generate(om, prompt, wl["W"], wl["N"], wl["G"], 1 + warm + rounds, round_times=times)
+    steady = times[warm:warm + rounds]
+    toks = sum(len(r.emitted) for r in res["rounds"][warm:warm + rounds])
+    scale = layers / dims.n_layers
+    secs = sum(steady) * scale
     try:
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         cores = len(os.sched_getaffinity(0))
-    dims = synthetic.PRESETS[wl["model"]]
-    w = synthetic.model_weights(dims, 0)
-    prompt = synthetic.markov_prompt(dims.vocab, wl["prompt"], 0)[:prefix]
-    om = OracleModel(dims, w)
-    times = []
-    res = lookahead_generate(om, prompt, wl["W"], wl["N"], wl["G"], 1 + budget_rounds, round_times=times)
-    toks = len(res["tokens"]) - 1
-    secs = sum(times)
+    q = [r.Q for r in res["rounds"][warm:warm + rounds]]
+    slice_txt = (f"{dims.n_layers} of the {layers} layers (layers 0-1, same seeded weights), round time scaled by "
+                 f"{scale:g}" if scale != 1 else "all layers")
     return {"value": toks / secs, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"numpy fp64 oracle, same model and W/N/G, prompt truncated to its first {prefix} tokens, "
-                      f"prefill untimed, then {budget_rounds} rounds ({toks} tokens) in {secs:.1f} s"}
+            "sample": (f"numpy fp64 oracle, same model widths and W/N/G, {slice_txt}; prompt cut to its first "
+                       f"{prefix} tokens, prefill and {warm} warmup rounds untimed, then {rounds} steady rounds "
+                       f"({q} packed rows, {toks} tokens) in {sum(steady):.1f} s unscaled; weights generated in "
+                       f"{gen_s:.0f} s outside the timing")}
 
 
 def main():
@@ -315,31 +495,38 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=0,
                     help="rounds to time; 0 (default) times one complete generation of the workload")
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="llama7b_w7n5g7", choices=sorted(WORKLOADS))
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=HEADLINE, choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-attn", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip the 7B-shaped extra workloads")
     ap.add_argument("--pool-from-prompt", action="store_true",
                     help="seed the n-gram pool with the prompt's n-grams (lookahead sessions)")
-    ap.add_argument("--pmc-sample", action="store_true", help="run the GEMM counter sample (see profiles/)")
     ap.add_argument("--attention-op-only", action="store_true", help="time only the isolated attention op")
-    ap.add_argument("--pmc-summary", nargs=3, metavar=("FETCH_DB", "WRITE_DB", "SAMPLE_JSON"),
+    ap.add_argument("--profile-rounds", type=int, default=0,
+                    help="run only N rounds of --workload with kernel events (for rocprofv3 runs)")
+    ap.add_argument("--trace-summary", nargs=3, metavar=("TRACE_CSV", "RUN_JSON", "OUT_MD"))
+    ap.add_argument("--pmc-summary", nargs=3, metavar=("FETCH_DB", "WRITE_DB", "RUN_JSON"),
                     help="write the GEMM traffic summary under profiles/ from two counter runs")
     args = ap.parse_args()
+    if args.trace_summary:
+        trace_summary(*args.trace_summary, cmd=" ".join(
+            ["rocprofv3 --kernel-trace --stats --output-format csv -d out/trace -o t -- python3 bench.py",
+             f"--profile-rounds N --workload {args.workload}"]))
+        return
     if args.pmc_summary:
-        md = pmc_summary(*args.pmc_summary)
-        open(TRAFFIC_MD, "w").write(md)
+        md = pmc_summary(*args.pmc_summary, args.workload)
+        open(TRAFFIC_MD.format(wl=args.workload), "w").write(md)
         print(md)
         return
-    if args.pmc_sample:
-        pmc_sample()
+    if args.profile_rounds:
+        profile_rounds(args.workload, args.profile_rounds)
         return
     if args.attention_op_only:
         import torch
         torch.cuda.set_device(0)
-        print(json.dumps(attention_op()), flush=True)
-        print(json.dumps(attention_op(reps=24, sets=4, p=8192)), flush=True)
-        print(json.dumps(attention_op(reps=64, sets=32, p=2048, H=64, Hkv=8, N=7)), flush=True)
+        for kw in ATTN_OPS:
+            print(json.dumps(attention_op(**kw)), flush=True)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the lookahead round runs on a single MI355X (got --gpus {args.gpus}); "
@@ -354,96 +541,72 @@ def main():
     dims = synthetic.PRESETS[wl["model"]]
     t = time.time()
     model = la.DeviceModel(dims, seed=0)
-    log(f"weights on device: {model.weight_bytes / 1e9:.2f} GB in {time.time() - t:.1f} s")
-    if wl.get("copyspan"):
-        prompt, copied = synthetic.copyspan_prompt(dims.vocab, wl["prompt"], 0)
-        log(f"prompt: {len(prompt)} tokens, {copied * 100:.1f}% copied spans")
-    else:
-        prompt = synthetic.markov_prompt(dims.vocab, wl["prompt"], 0)
-
-    def make(ar=False, profile=False):
-        s = la.Session(model, prompt, W=wl["W"], N=wl["N"], G=wl["G"], max_new=wl["max_new"], ar_only=ar,
-                       pool_from_prompt=args.pool_from_prompt and not ar)
-        if profile:
-            s.la_profile(True)
-        return s
-
-    sess = make()
-    for _ in range(args.warmup):
-        sess.la_step()
-    tokens, secs, sess, steps = run_steps(make, sess, args.steps)
-    value = tokens / secs
-    log(f"lookahead: {tokens} tokens in {steps} rounds, {secs * 1e3 / steps:.3f} ms/round, {value:.1f} tokens/s")
-    # autoregressive decoding with the same kernels
-    ar = make(ar=True)
-    for _ in range(args.warmup):
-        ar.la_step()
-    ar_tokens, ar_secs, _, ar_steps = run_steps(lambda: make(ar=True), ar, args.steps)
-    ar_tps = ar_tokens / ar_secs
-    log(f"autoregressive: {ar_tokens} tokens in {ar_steps} rounds, {ar_tps:.1f} tokens/s")
-    # dominant kernel: GEMM weight stream, events around each launch
-    # a second pass with HIP events around every GEMM / attention launch (one
-    # context's totals; with --steps K the first context's rounds are the ones read)
-    torch.cuda.synchronize()
-    t = time.perf_counter()
-    prof = make(profile=True)           # context set-up and prompt prefill, outside every timed region
-    torch.cuda.synchronize()
-    init_prefill_ms = (time.perf_counter() - t) * 1e3
-    sr = step_roofline(model, dims, wl, tokens, steps, secs)
-    log(f"round vs HBM bound: {sr['bytes_per_round'] / 1e9:.2f} GB per round, {sr['ms_at_peak']:.2f} ms at 8 TB/s, "
-        f"{sr['frac'] * 100:.1f}% of it; set-up + prefill {init_prefill_ms:.0f} ms")
-    for _ in range(args.warmup):
-        prof.la_step()
-    prof.la_profile(True)
-    _, prof_secs, prof_end, _ = run_steps(lambda: make(profile=True), prof, args.steps)
-    pr = (prof_end if args.steps == 0 else prof).la_profile_read()
-    gemm_avg_ms = pr["gemm_ms"] / max(1, pr["gemm_launches"])
-    gemm_bytes = pr["gemm_bytes"] / max(1, pr["gemm_launches"])
-    achieved = pr["gemm_bytes"] / (pr["gemm_ms"] * 1e-3) / 1e9 if pr["gemm_ms"] > 0 else 0.0
-    attn_in_step = pr["attn_bytes"] / (pr["attn_ms"] * 1e-3) / 1e9 if pr["attn_ms"] > 0 else 0.0
-    log(f"gemm: {pr['gemm_launches']} launches, avg {gemm_avg_ms * 1e3:.1f} us, {achieved:.0f} GB/s; "
-        f"attention in step: {pr['attn_launches']} launches, avg {pr['attn_ms'] / max(1, pr['attn_launches']) * 1e3:.1f} us, "
-        f"{attn_in_step:.0f} GB/s; share of step: gemm {pr['gemm_ms'] / (secs * 1e3) * 100:.0f}%")
+    log(f"{args.workload}: weights on device, {model.weight_bytes / 1e9:.2f} GB in {time.time() - t:.1f} s")
+    head = measure(model, dims, wl, args.steps, args.warmup, pool_from_prompt=args.pool_from_prompt)
+    k = head["kernels"]
+    traffic = gemm_traffic(args.workload)
     line = {
-        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": steps,
-        "warmup": args.warmup, "ms_per_step": secs * 1e3 / steps, "higher_is_better": True, "scaling": "weak",
+        "metric": METRIC, "value": head["value"], "unit": "tokens/s", "n_gpus": 1, "steps": head["rounds"],
+        "warmup": args.warmup, "ms_per_step": head["ms_per_round"], "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16" if dims.dtype == "bf16" else "f32", "data": "synthetic",
         "config": {"workload": wl["desc"], "W": wl["W"], "N": wl["N"], "G": wl["G"], "prompt_tokens": wl["prompt"],
                    "max_new": wl["max_new"], "verify": "greedy", "batch": 1,
                    "pool_from_prompt": bool(args.pool_from_prompt)},
-        "tokens_per_round": tokens / steps,
-        "ar_tokens_per_s": ar_tps,
-        "speedup_vs_ar": value / ar_tps,
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": gemm_traffic(),
-                     "kernel": "la_gemm_kernel (+ split reduction), all projections, MLP and LM head of a round",
-                     "avg_launch_us": gemm_avg_ms * 1e3, "algorithmic_bytes_per_launch": gemm_bytes,
-                     "launches": pr["gemm_launches"]},
-        "step_roofline": sr,
-        "init_prefill_ms": init_prefill_ms,
-        "attention_in_step": {"achieved_GBps": attn_in_step, "avg_launch_us":
-                              pr["attn_ms"] / max(1, pr["attn_launches"]) * 1e3, "launches": pr["attn_launches"]},
+        "roofline": {"bound": "hbm", "achieved": k["gemm_GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": k["gemm_GBps"] / HBM_PEAK_GBS,
+                     "traffic": traffic,
+                     "kernel": "la_gemm_kernel (+ split reduction): every projection, MLP and LM-head launch of "
+                               "the timed rounds",
+                     "avg_launch_us": k["gemm_avg_launch_us"], "algorithmic_bytes_per_launch":
+                         k["gemm_bytes_per_launch"], "launches": k["gemm_launches"],
+                     "share_of_round": k["share_of_round_gemm"]},
     }
+    for key in ("tokens_per_round", "ar_tokens_per_s", "ar_ms_per_step", "speedup_vs_ar", "step_roofline",
+                "init_prefill_ms", "accepted_hist", "copied_fraction"):
+        line[key] = head[key]
+    line["attention_in_step"] = {"achieved_GBps": k["attn_GBps"], "avg_launch_us": k["attn_avg_launch_us"],
+                                 "launches": k["attn_launches"], "share_of_round": k["share_of_round_attn"]}
+    log(f"headline: {head['value']:.2f} tokens/s, GEMM {k['gemm_GBps']:.0f} GB/s "
+        f"({k['gemm_GBps'] / HBM_PEAK_GBS * 100:.1f}% of HBM peak)")
     if not args.no_attn:
-        a = attention_op()
-        log(f"lookahead attention op: {a['avg_us']:.2f} us, {a['achieved_GBps']:.0f} GB/s ({a['frac'] * 100:.1f}%)")
-        line["lookahead_attn"] = a
-        # the same op over the long-prefix workload's 8192 committed keys (134 MB of K/V per call)
-        a = attention_op(reps=24, sets=4, p=8192)
-        log(f"lookahead attention op, prefix 8192: {a['avg_us']:.2f} us, {a['achieved_GBps']:.0f} GB/s "
-            f"({a['frac'] * 100:.1f}%)")
-        line["lookahead_attn_8192"] = a
-        # the 34B-shaped round's attention: 64 query heads on 8 KV heads, 180 rows, 2048 keys
-        a = attention_op(reps=64, sets=32, p=2048, H=64, Hkv=8, N=7)
-        log(f"lookahead attention op, 34B GQA shape: {a['avg_us']:.2f} us, {a['achieved_GBps']:.0f} GB/s "
-            f"({a['frac'] * 100:.1f}%)")
-        line["lookahead_attn_34b_gqa"] = a
-    if not args.no_cpu_baseline and wl["model"] == "codellama34b":
-        log("cpu baseline skipped: the oracle would hold the 34B-shaped weights in host memory")
-    elif not args.no_cpu_baseline:
+        for key, kw in zip(ATTN_KEYS, ATTN_OPS):
+            a = attention_op(**kw)
+            log(f"{key}: {a['avg_us']:.2f} us, {a['achieved_GBps']:.0f} GB/s ({a['frac'] * 100:.1f}%)")
+            line[key] = a
+    if not args.no_cpu_baseline:
         t = time.time()
-        line["cpu_baseline"] = cpu_baseline(wl)
-        log(f"cpu baseline: {line['cpu_baseline']['value']:.4f} tokens/s ({time.time() - t:.0f} s)")
+        line["cpu_baseline"] = cpu_baseline(args.workload)
+        log(f"cpu baseline: {line['cpu_baseline']['value']:.5f} tokens/s ({time.time() - t:.0f} s)")
+    if not args.no_extras and args.workload == HEADLINE:
+        del model
+        torch.cuda.empty_cache()
+        extras = {}
+        d7 = synthetic.PRESETS["llama7b"]
+        t = time.time()
+        m7 = la.DeviceModel(d7, seed=0)
+        log(f"7B-shaped weights on device in {time.time() - t:.1f} s")
+        log("llama7b_w7n5g7 (greedy):")
+        extras["llama7b_w7n5g7"] = dict(desc=WORKLOADS["llama7b_w7n5g7"]["desc"],
+                                        **measure(m7, d7, WORKLOADS["llama7b_w7n5g7"], args.steps, args.warmup))
+        long = WORKLOADS["llama7b_long_w15n5g15"]
+        for mode in ("greedy", "sample"):
+            runs = []
+            for seed in range(5):
+                log(f"llama7b_long_w15n5g15 ({mode}, seed {seed}):")
+                runs.append(measure(m7, d7, long, args.steps, args.warmup, verify=mode, temperature=0.7, seed=seed,
+                                    with_ar=seed == 0, with_profile=seed == 0))
+            agg = {"desc": long["desc"] + (", temperature-0.7 one-hot sampling" if mode == "sample" else
+                                           ", greedy"),
+                   "seeds": list(range(5)), "value": sum(r["tokens"] for r in runs) / sum(
+                       r["rounds"] * r["ms_per_round"] * 1e-3 for r in runs),
+                   "value_per_seed": [r["value"] for r in runs],
+                   "tokens_per_round": sum(r["tokens"] for r in runs) / sum(r["rounds"] for r in runs),
+                   "ms_per_round": sum(r["rounds"] * r["ms_per_round"] for r in runs) / sum(r["rounds"]
+                                                                                             for r in runs)}
+            for key in ("ar_tokens_per_s", "speedup_vs_ar", "step_roofline", "kernels", "init_prefill_ms"):
+                agg[key] = runs[0][key]
+            extras[f"llama7b_long_w15n5g15_{mode}"] = agg
+        line["extra_workloads"] = extras
     print(json.dumps(line), flush=True)
 
 
