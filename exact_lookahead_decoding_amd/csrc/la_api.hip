@@ -19,10 +19,12 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
 #define PREFILL_CHUNK 128
+#define LA_MAX_DEVICES 64
 
 static thread_local std::string g_err;
 
@@ -931,10 +933,11 @@ extern "C" size_t la_attention_workspace(int32_t Q, int32_t H, int32_t dh, int32
   return parts * H * Q * ((size_t)dh + 2) * 4 + 512;
 }
 
-extern "C" int la_attention(int32_t dtype, const void* q, const void* k_cache, const void* v_cache, int32_t t_cap,
-                            const void* k_ws, const void* v_ws, int32_t ws_cap, int32_t H, int32_t Hkv, int32_t dh,
-                            const int32_t* rows, const la_rows_info* info, int32_t shared_end, void* out,
-                            void* workspace, size_t workspace_bytes, void* stream) {
+// Argument checks and launch shared by la_attention and la_attention_noalloc.
+static int attention_call(int32_t dtype, const void* q, const void* k_cache, const void* v_cache, int32_t t_cap,
+                          const void* k_ws, const void* v_ws, int32_t ws_cap, int32_t H, int32_t Hkv, int32_t dh,
+                          const int32_t* rows, const la_rows_info* info, int32_t shared_end, void* out,
+                          void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !k_cache || !v_cache || !rows || !info || !out || !workspace) return fail(nullptr, LA_EINVAL, "null argument");
   if (dtype != LA_DTYPE_F32 && dtype != LA_DTYPE_BF16) return fail(nullptr, LA_EINVAL, "dtype");
   if (H < 1 || Hkv < 1 || H % Hkv || shared_end < 1 || shared_end > t_cap) return fail(nullptr, LA_EINVAL, "bad shape");
@@ -959,6 +962,61 @@ extern "C" int la_attention(int32_t dtype, const void* q, const void* k_cache, c
   const int rc = la_attention_launch(dtype == LA_DTYPE_BF16 ? LA_DT_BF16 : LA_DT_F32, a, (hipStream_t)stream);
   if (rc) return fail(nullptr, rc == -2 ? LA_EINVAL : LA_EDEVICE, "attention launch failed");
   return LA_OK;
+}
+
+extern "C" int la_attention(int32_t dtype, const void* q, const void* k_cache, const void* v_cache, int32_t t_cap,
+                            const void* k_ws, const void* v_ws, int32_t ws_cap, int32_t H, int32_t Hkv, int32_t dh,
+                            const int32_t* rows, const la_rows_info* info, int32_t shared_end, void* out,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  return attention_call(dtype, q, k_cache, v_cache, t_cap, k_ws, v_ws, ws_cap, H, Hkv, dh, rows, info, shared_end,
+                        out, workspace, workspace_bytes, stream);
+}
+
+// ------------------------------------------------------------------ allocation-free attention
+//
+// la_attention_noalloc keeps the key splits' softmax states in this
+// file-scope device array instead of a caller workspace.  Host code never
+// passes the array's name to a kernel (on the host it is only a stand-in
+// symbol): its device address is taken once per device with
+// hipGetSymbolAddress, with that device current, and kept in g_scratch.
+static __device__ __align__(256) char scratch[LA_NOALLOC_SCRATCH_BYTES];
+
+static std::mutex g_scratch_mu;
+static void* g_scratch[LA_MAX_DEVICES];
+
+// Device address of `scratch` on the current device (taken on the first call per device).
+static int scratch_ptr(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(nullptr, LA_EDEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= LA_MAX_DEVICES) return fail(nullptr, LA_EDEVICE, "device %d beyond %d", dev, LA_MAX_DEVICES);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(nullptr, LA_EDEVICE, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return LA_OK;
+}
+
+extern "C" int la_attention_noalloc(int32_t dtype, const void* q, const void* k_cache, const void* v_cache,
+                                    int32_t t_cap, const void* k_ws, const void* v_ws, int32_t ws_cap, int32_t H,
+                                    int32_t Hkv, int32_t dh, const int32_t* rows, const la_rows_info* info,
+                                    int32_t shared_end, void* out, void* stream) {
+  if (!info) return fail(nullptr, LA_EINVAL, "null argument");
+  if (H < 1 || dh < 1 || shared_end < 1 || shared_end > t_cap) return fail(nullptr, LA_EINVAL, "bad shape");
+  const size_t need = la_attention_workspace(info->Q, H, dh, shared_end - 1 + info->maxp, t_cap);
+  if (need > LA_NOALLOC_SCRATCH_BYTES)
+    return fail(nullptr, LA_EOVERFLOW, "this call needs %zu bytes of split state, beyond the %u the allocation-free "
+                "entry point holds; use la_attention with a workspace", need, (unsigned)LA_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  const int rc = scratch_ptr(&ws);
+  if (rc) return rc;
+  return attention_call(dtype, q, k_cache, v_cache, t_cap, k_ws, v_ws, ws_cap, H, Hkv, dh, rows, info, shared_end,
+                        out, ws, LA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 static int linear_epi(int32_t epilogue) {

@@ -19,6 +19,7 @@ from . import build as _build
 LA_OK, LA_EINVAL, LA_ESTATE, LA_EPLAN, LA_EOVERFLOW, LA_EDEVICE = 0, -1, -2, -3, -4, -5
 LA_MAX_N = 16
 LA_MAX_EMIT = 32
+LA_NOALLOC_SCRATCH_BYTES = 32 << 20
 LA_DTYPE_F32, LA_DTYPE_BF16 = 0, 1
 LA_VERIFY_GREEDY, LA_VERIFY_SAMPLE = 0, 1
 
@@ -99,7 +100,7 @@ EXPORTS = ["la_query_sizes", "la_init", "la_destroy", "la_step", "la_generate", 
            "la_commit", "la_pool_lookup", "la_pool_insert", "la_get_state", "la_stats", "la_last_error",
            "la_rows_query", "la_build_rows", "la_attention_workspace", "la_attention", "la_linear_workspace",
            "la_linear", "la_packed_linear_bytes", "la_pack_linear", "la_linear_packed", "la_packed_weight_bytes",
-           "la_pack_weights", "la_profile", "la_profile_read"]
+           "la_pack_weights", "la_profile", "la_profile_read", "la_attention_noalloc"]
 LA_LINEAR_STORE, LA_LINEAR_RESIDUAL, LA_LINEAR_SWIGLU, LA_LINEAR_F32 = 0, 1, 2, 3
 
 _lib = None
@@ -138,6 +139,8 @@ def load() -> C.CDLL:
         "la_attention_workspace": ([I32, I32, I32, I32, I32], C.c_size_t),
         "la_attention": ([I32, VP, VP, VP, I32, VP, VP, I32, I32, I32, I32, VP, P(la_rows_info), I32, VP, VP,
                           C.c_size_t, VP], I32),
+        "la_attention_noalloc": ([I32, VP, VP, VP, I32, VP, VP, I32, I32, I32, I32, VP, P(la_rows_info), I32, VP,
+                                  VP], I32),
         "la_linear_workspace": ([I32, I32, I32, I32, I32], C.c_size_t),
         "la_linear": ([I32, I32, VP, VP, VP, VP, I32, I32, I32, VP, C.c_size_t, VP], I32),
         "la_packed_linear_bytes": ([I32, I32, I32, I32], C.c_size_t),
@@ -418,6 +421,20 @@ def la_attention(q, k_cache, v_cache, k_ws, v_ws, rows, info, shared_end, out=No
     _check(lib.la_attention(dtype, _ptr(q), _ptr(k_cache), _ptr(v_cache), t_cap, _ptr(k_ws), _ptr(v_ws), ws_cap,
                             H, Hkv, dh, _ptr(rows), C.byref(info), shared_end, _ptr(out), _ptr(workspace),
                             workspace.numel(), _stream(stream)))
+    return out
+
+
+def la_attention_noalloc(q, k_cache, v_cache, k_ws, v_ws, rows, info, shared_end, out=None, stream=None):
+    """la_attention with the library's own split-state array (see include/la.h)."""
+    dtype = LA_DTYPE_BF16 if q.dtype == torch.bfloat16 else LA_DTYPE_F32
+    Q, H, dh = q.shape
+    Hkv, t_cap, _ = k_cache.shape
+    ws_cap = k_ws.shape[1] if k_ws is not None else 0
+    if out is None:
+        out = torch.empty_like(q)
+    _check(load().la_attention_noalloc(dtype, _ptr(q), _ptr(k_cache), _ptr(v_cache), t_cap, _ptr(k_ws), _ptr(v_ws),
+                                       ws_cap, H, Hkv, dh, _ptr(rows), C.byref(info), shared_end, _ptr(out),
+                                       _stream(stream)))
     return out
 
 

@@ -379,6 +379,23 @@ int la_attention(int32_t dtype, const void* q, const void* k_cache, const void* 
                  const int32_t* rows, const la_rows_info* info, int32_t shared_end, void* out, void* workspace,
                  size_t workspace_bytes, void* stream);
 
+/* Allocation-free la_attention, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same kernels and results as la_attention (same
+ * arguments minus the workspace), with the key splits' softmax states kept
+ * in a library-owned device array of LA_NOALLOC_SCRATCH_BYTES per device
+ * (allocated by the HIP runtime when the library's code is loaded, held
+ * until the process ends).  The call allocates nothing; its first call on
+ * a device looks up that device's array address.  Every call on one device
+ * shares the array, so calls that overlap on one device (concurrent
+ * streams, or host threads) race: order them on one stream.  LA_EOVERFLOW,
+ * before anything is launched, when la_attention_workspace for the shape
+ * exceeds LA_NOALLOC_SCRATCH_BYTES; otherwise the errors of la_attention. */
+#define LA_NOALLOC_SCRATCH_BYTES (32u << 20)
+int la_attention_noalloc(int32_t dtype, const void* q, const void* k_cache, const void* v_cache, int32_t t_cap,
+                         const void* k_ws, const void* v_ws, int32_t ws_cap, int32_t H, int32_t Hkv, int32_t dh,
+                         const int32_t* rows, const la_rows_info* info, int32_t shared_end, void* out, void* stream);
+
 /* Token-wise linear layer of the target forward ("M7.3", 0x05C: the
  * projections and MLP run over every packed row), Y = epilogue(X W^T):
  *   LA_LINEAR_STORE    Y[M][N] = round(X W^T)
