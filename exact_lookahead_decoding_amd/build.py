@@ -21,6 +21,10 @@ LIB = os.path.join(OUT_DIR, "liblookahead.so")
 SOURCES = ["la_gemm.hip", "la_model.hip", "la_rows.hip", "la_attn.hip", "la_verify.hip", "la_state.hip",
            "la_api.hip"]
 ARCH = "gfx950"
+# per-file code generation options: the attention kernel post-processes its
+# MFMA results with vector ALU code (softmax, rescaling), so its accumulators
+# are kept in the architectural VGPRs (no AGPR <-> VGPR copies per chunk)
+EXTRA = {"la_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:
@@ -43,7 +47,7 @@ def build(verbose: bool = False) -> str:
 
     def compile_one(src):
         obj = os.path.join(OUT_DIR, src.replace(".hip", ".o"))
-        cmd = [cc] + flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc] + flags() + EXTRA.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

@@ -247,6 +247,9 @@ static int admit(la_ctx* c) {
     return fail(c, LA_EINVAL, "W=%d N=%d: a branch reaches %d positions past the committed prefix; at most %d are admitted",
                 g.W, g.N, c->maxp_max, LA_MAX_BRANCH);
   if (!c->rows_fit) return fail(c, LA_EINVAL, "W=%d N=%d G=%d: the row builder's tables do not fit", g.W, g.N, g.G);
+  if (!la_attention_fits(c->dh, c->esz, c->q_max, c->nb_max, c->maxp_max))
+    return fail(c, LA_EINVAL, "W=%d N=%d G=%d needs %d packed rows in a round; the attention's tail stage does not "
+                "hold them at head dim %d", g.W, g.N, g.G, c->q_max, c->dh);
   return LA_OK;
 }
 

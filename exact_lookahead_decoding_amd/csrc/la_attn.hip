@@ -7,47 +7,52 @@
 // sees exactly logical positions 0 .. pos_i, position t taken from the
 // cache when t < shared_end and through the row's branch path otherwise.
 //
-// Reduction tree (a function of logical positions only, so a row gets the
-// same bits whether it is alone in an autoregressive step or packed with a
-// whole lookahead round):
+// Reduction tree (a function of key positions, the cache capacity and the
+// model's head counts only, so a row gets the same bits whether it is alone
+// in an autoregressive step or packed with a whole lookahead round):
 //   * keys are cut into chunks of 32 positions and the chunks into key
-//     splits of a fixed number of chunks (set by the cache capacity); chunk
-//     c belongs to class c % 4;
-//   * inside a split, a class takes its chunks in decreasing position with
-//     the online softmax: the reference maximum m' moves to the chunk's
-//     exact maximum only when that exceeds it by more than RESCALE, the
-//     running sums are scaled by 2^(m - m'), p = 2^(s - m'),
-//     l' = l * 2^(m - m') + sum p (fixed lane order), and O' = O * 2^(m - m')
-//     + V^T P^T accumulated by MFMA over a fixed key -> slot assignment;
-//   * a split's 4 class states are folded in class order, the splits' states
-//     in split order, then O / l.
+//     splits of `spl` chunks (la_attention_spl);
+//   * inside a split the chunks are taken in decreasing position with the
+//     online softmax: the reference maximum m' moves to the chunk's exact
+//     maximum only when that exceeds it by more than RESCALE, the running
+//     sums are scaled by 2^(m - m'), p = 2^(s - m'), l' = l * 2^(m - m') +
+//     sum p (fixed lane order), and O' = O * 2^(m - m') + V^T P^T
+//     accumulated by MFMA over a fixed key -> slot assignment;
+//   * the splits' states are folded in split order by a small merge
+//     kernel, then O / l.
+// A chunk's scores are the same numbers whichever rows share the MFMA, and
+// a row's probabilities and products sit in the same MFMA slots whether the
+// chunk's keys came from the cache or from the row's branch (other
+// branches add exact zeros).
 //
-// Work decomposition (gfx950, wave64; a wave owns one class of one tile of
-// 16 query rows of one q-head):
-//   * one workgroup per (KV head, row group of up to 4 tiles, key split of
-//     a fixed number of 128-position stages), 4 class waves per tile pair
-//     (a wave computes two tiles from one read of the chunk's K and V); K
-//     and V of every committed chunk
-//     land in LDS through global_load_lds_dwordx4 (16-byte pieces
-//     XOR-swizzled by row, so the QK and the PV fragment reads are
-//     bank-conflict free) in a ring of 128-key stages shared by all tiles and
-//     classes of the workgroup; the row positions and the tiles' Q come in
-//     the same way, so the only waits are the ring's own;
-//   * QK: S^T = K Q^T, 16x16x32 bf16 MFMA (16x16x4 fp32): one query row per
-//     lane column, so the softmax statistics stay in-lane;
-//   * PV: O^T += V^T P^T; output tile dt holds head dimensions NDT*m + dt, so
-//     a lane reads NDT contiguous elements of each key row and transposes
-//     them in registers; P enters rounded to bf16 (fp32 accumulation);
-//   * the chunks that reach past shared_end (at most one per class) are
-//     applied last in their class, from rows gathered out of the cache or,
-//     through each branch's path, out of the packed rows' workspace, once per
-//     branch in the tile (rows of other branches get p = 0 in that pass,
-//     which leaves their sums unchanged);
-//   * the class states are folded in class order inside the workgroup; with
-//     several key splits a small kernel folds the splits' states in order.
-// The block -> work mapping keeps every workgroup of one KV head on one XCD
-// (blockIdx % 8), so the head's Q and the K/V chunks shared by its row groups
-// are fetched from HBM once.
+// Work decomposition (gfx950, wave64):
+//   * one workgroup per (KV head, key split, row group); a row group is
+//     eight waves x one tile of 16 query rows (two waves per SIMD, so one
+//     wave's vector ALU work overlaps the other's MFMAs and LDS waits).
+//     Tiles are row-tile major over the query heads of a KV head
+//     (grouped-query attention), every wave holds its tile's Q in registers
+//     and walks every chunk of the split, so each K/V byte of the split
+//     reaches the workgroup once;
+//   * K and V of committed chunks arrive through a ring of D chunk slots in
+//     LDS by global_load_lds DMA (16-byte pieces XOR-swizzled by row), one
+//     barrier per chunk.  The DMA is issued as inline asm and the LDS reads
+//     are ordinary loads, so the compiler places only LDS waits on them and
+//     the ring orders the DMA with explicit vmcnt waits.  One set of
+//     fragment registers: K of chunk i + 1 is read once the QK^T MFMAs of
+//     chunk i have their operands, V once its P V MFMAs have theirs;
+//   * QK: S^T = K Q^T with 16x16x32 bf16 MFMA (one query row per lane
+//     column, softmax statistics stay in-lane); PV: O^T += V^T P^T, the V^T
+//     operand read straight from the row-major chunk with ds_read_b64_tr_b16
+//     (the 64 halves a 16-lane group names are dealt out so that lane i
+//     receives items i, i+16, i+32, i+48);
+//   * chunks reaching past shared_end (at most three) are the highest
+//     positions of their split, so they come first: the committed rows of
+//     the first of them and every packed row's K/V are staged in LDS once,
+//     and each wave walks the distinct branches of its tiles (the row
+//     builder's tables), indexing the staged rows through the branch path;
+//   * the block -> work map keeps every workgroup of one KV head on one XCD
+//     (blockIdx % 8), so the head's K/V shared by its row groups and its
+//     split states are fetched from that XCD's L2.
 #include <algorithm>
 #include <type_traits>
 
@@ -55,18 +60,13 @@
 #include "la_dev.h"
 #include "la_kernels.h"
 
-#define CH 32         // keys per chunk
-#define NCLS 4        // chunk classes
-#define NTAIL 4       // most chunks per call that reach past shared_end
+#define CH 32          // keys per chunk
 #define NEG_INF (-__builtin_inff())
-
-
-
-template <int W> struct alignas(4 * W) Words { uint32_t w[W]; };
+#define RESCALE 8.0f   // log2 units: the reference maximum moves only past this
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// a*wa + b*wb as fma(a, wa, b*wb): the one rounding sequence of the class fold
+// a*wa + b*wb as fma(a, wa, b*wb): the one rounding sequence of the split fold
 __device__ __forceinline__ float lin2(float a, float wa, float b, float wb) {
 #pragma clang fp contract(off)
   return __builtin_fmaf(a, wa, b * wb);
@@ -75,25 +75,130 @@ __device__ __forceinline__ float lin2(float a, float wa, float b, float wb) {
 // MFMA k-slot e (0..7) of lane group g <-> key offset inside the chunk.
 __device__ __forceinline__ int slot_key(int g, int e) { return 16 * (e >> 2) + 4 * g + (e & 3); }
 
+template <int W> struct alignas(4 * W) Words { uint32_t w[W]; };
+
+// LDS address of 16-byte piece q of chunk row r (pieces XOR-swizzled by row)
+template <int ROWB> __device__ __forceinline__ uint32_t piece_addr(uint32_t base, int r, int q) {
+  constexpr int PIECES = ROWB / 16;
+  return base + (uint32_t)(r * ROWB + 16 * (q ^ (r % PIECES)));
+}
+
+// LDS reads are ordinary loads (the compiler places their lgkmcnt waits);
+// the DMA into LDS is inline asm, so the compiler sees no pending LDS write
+// and never waits for DMA before an LDS read -- the ring orders the DMA with
+// its own vmcnt waits and barriers.  The DMA has no register results.
+template <typename V> __device__ __forceinline__ V lds_get(uint32_t addr) {
+  return *(const __attribute__((address_space(3))) V*)addr;
+}
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ LdsT<8>::T lds_get_tr16(uint32_t addr) {
+  const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)addr);
+  return __builtin_bit_cast(LdsT<8>::T, v);
+}
+// lane l's 16 (4) bytes of src land at LDS offset lds_off + 16 l (4 l); m0 is restored
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_off) {
+  uint32_t keep;
+  lds_off = __builtin_amdgcn_readfirstlane(lds_off);   // wave-uniform by construction; an SGPR for m0
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(keep) : "v"(src), "s"(lds_off) : "memory");
+}
+__device__ __forceinline__ void dma4(const void* src, uint32_t lds_off) {
+  uint32_t keep;
+  lds_off = __builtin_amdgcn_readfirstlane(lds_off);
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(keep) : "v"(src), "s"(lds_off) : "memory");
+}
+// uniform base + per-lane offset as one VALU add the compiler keeps as is
+// (left alone, it hoists every base-independent offset into its own register)
+__device__ __forceinline__ uint32_t add_sv(uint32_t sbase, uint32_t voff) {
+  uint32_t a;
+  sbase = __builtin_amdgcn_readfirstlane(sbase);
+  asm("v_add_u32 %0, %1, %2" : "=v"(a) : "s"(sbase), "v"(voff));
+  return a;
+}
+// s_waitcnt vmcnt(N) for the asm DMA (an asm statement the compiler keeps as written)
+template <int N> __device__ __forceinline__ void dma_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 template <typename T, int DH> struct AttnT;
 
+// bf16: 16x16x32 MFMA; lane (g, c) = (lane / 16, lane % 16).
+typedef LdsT<16>::T V4u;
+
 template <int DH> struct AttnT<bf16_t, DH> {
-  static constexpr int ROWB = DH * 2;         // bytes per key row
-  static constexpr int PIECES = ROWB / 16;    // 16-byte pieces per row
-  static constexpr int LP = PIECES / 4;       // pieces a lane group supplies for QK (one per MFMA step)
-  static constexpr int NDT = DH / 16;         // output tiles
-  static constexpr int VB = NDT * 2;          // bytes of one key row a lane supplies for PV
-  typedef Words<VB / 4> VV;
-  struct QF { u32x4 p[LP]; };
-  static __device__ __forceinline__ f32x4 qk(const QF& k, const QF& q) {
+  static constexpr int ROWB = DH * 2, KS = DH / 32, NDT = DH / 16;
+  struct QF { V4u p[KS]; };                           // Q[row c][32 s + 8 g ..]
+  struct KF { V4u p[2][KS]; };                        // K[key 16 kg + .][32 s + 8 g ..]
+  struct VF { LdsT<8>::T p[NDT][2]; };                // V^T operand halves (transposed reads)
+  static constexpr int NVR = 2;                      // V rows a lane reads per chunk
+  // Q fragments of lane (g, c) from its row
+  static __device__ __forceinline__ void load_q(QF& q, const char* row, int g) {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) q.p[s] = *(const V4u*)(row + 16 * (4 * s + g));
+  }
+  // chunk key offset of V row j of lane (g, c)
+  static __device__ __forceinline__ int vkey(int g, int c, int j) { return 16 * j + 4 * g + (c >> 2); }
+  // K fragments of lane (g, c): key rows rk[kg] of the chunk at base
+  static __device__ __forceinline__ void load_k(KF& k, uint32_t base, const int (&rk)[2], int g) {
+#pragma unroll
+    for (int kg = 0; kg < 2; ++kg)
+#pragma unroll
+      for (int s = 0; s < KS; ++s) k.p[kg][s] = lds_get<V4u>(piece_addr<ROWB>(base, rk[kg], 4 * s + g));
+  }
+  // V^T operand of tile dt: lane (g, c) names row rv[h] (slot keys 4g + c/4 and 16 + 4g + c/4) and dims
+  // 16 dt + 4 (c % 4) .. +3; after the transposed read it holds dim 16 dt + c of slot keys slot_key(g, e)
+  static __device__ __forceinline__ void load_v(VF& v, uint32_t base, const int (&rv)[2], int c) {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t a = piece_addr<ROWB>(base, rv[h], 2 * dt + ((c & 3) >> 1)) + 8 * (c & 1);
+        v.p[dt][h] = lds_get_tr16(a);
+      }
+  }
+  static __device__ __forceinline__ void load_vr(VF& v, uint32_t base, const int (&rv)[NVR], int c) {
+    load_v(v, base, rv, c);
+  }
+  // A chunk slot's fragments at fixed per-lane offsets (the second 16-row
+  // half of a chunk adds 16 rows, an immediate offset of the LDS read)
+  struct Lofs { uint32_t k[KS], v[NDT]; };
+  static __device__ __forceinline__ Lofs lane_ofs(int g, int c) {
+    constexpr int P = ROWB / 16;
+    Lofs o;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) o.k[s] = c * ROWB + 16 * ((4 * s + g) ^ (c % P));
+    const int r = 4 * g + (c >> 2);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) o.v[dt] = r * ROWB + 16 * ((2 * dt + ((c & 3) >> 1)) ^ (r % P)) + 8 * (c & 1);
+    return o;
+  }
+  static __device__ __forceinline__ void load_k_at(KF& k, uint32_t base, const Lofs& o, int, int) {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const uint32_t a = add_sv(base, o.k[s]);
+#pragma unroll
+      for (int kg = 0; kg < 2; ++kg) k.p[kg][s] = lds_get<V4u>(a + kg * 16 * ROWB);
+    }
+  }
+  static __device__ __forceinline__ void load_v_at(VF& v, uint32_t base, const Lofs& o, int, int) {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const uint32_t a = add_sv(base, o.v[dt]);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) v.p[dt][h] = lds_get_tr16(a + h * 16 * ROWB);
+    }
+  }
+  static __device__ __forceinline__ f32x4 qk(const KF& k, int kg, const QF& q) {
     f32x4 acc = {0, 0, 0, 0};
 #pragma unroll
-    for (int s = 0; s < LP; ++s)
-      acc = mfma_bf16_32(__builtin_bit_cast(bf16x8, k.p[s]), __builtin_bit_cast(bf16x8, q.p[s]), acc);
+    for (int s = 0; s < KS; ++s)
+      acc = mfma_bf16_32(__builtin_bit_cast(bf16x8, k.p[kg][s]), __builtin_bit_cast(bf16x8, q.p[s]), acc);
     return acc;
   }
-  // P^T operand of one chunk: p of slot e rounded to bf16 (nearest even)
   typedef bf16x8 PP;
+  // P^T operand: p of slot e rounded to bf16 (nearest even)
   static __device__ __forceinline__ PP prep(const float* ps) {
     typedef float f2 __attribute__((ext_vector_type(2)));
     typedef __bf16 b2 __attribute__((ext_vector_type(2)));
@@ -105,43 +210,67 @@ template <int DH> struct AttnT<bf16_t, DH> {
     }
     return __builtin_bit_cast(bf16x8, bh);
   }
-  // V^T(dt) operand of the chunk's 8 slots; vv[e] holds the lane's elements of slot e
-  typedef bf16x8 VA;
-  template <typename V> static __device__ __forceinline__ VA va(int dt, const V* vv) {
-    uint32_t w[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t lo = vv[2 * j].w[dt >> 1], hi = vv[2 * j + 1].w[dt >> 1];
-      // element dt of key slot 2j (low half) and of key slot 2j + 1 (high half)
-      w[j] = __builtin_amdgcn_perm(hi, lo, (dt & 1) ? 0x07060302u : 0x05040100u);
-    }
-    return __builtin_bit_cast(bf16x8, w);
+  static __device__ __forceinline__ f32x4 pv(const VF& v, int dt, const PP& pp, f32x4 o) {
+    const uint32_t w[4] = {v.p[dt][0].x, v.p[dt][0].y, v.p[dt][1].x, v.p[dt][1].y};
+    return mfma_bf16_32(__builtin_bit_cast(bf16x8, w), pp, o);
   }
-  // o += V^T(dt) P^T
-  static __device__ __forceinline__ f32x4 pva(const VA& A, const PP& pp, f32x4 o) { return mfma_bf16_32(A, pp, o); }
-  template <typename V>
-  static __device__ __forceinline__ f32x4 pv(int dt, const V* vv, const PP& pp, f32x4 o) {
-    return pva(va(dt, vv), pp, o);
-  }
+  // head dimension of accumulator row i (0..15) of output tile dt
+  static __device__ __forceinline__ int dim(int dt, int i) { return 16 * dt + i; }
 };
 
+// fp32: 16x16x4 MFMA; lane (g, c) holds 16-byte pieces LP*g .. of its rows.
 template <int DH> struct AttnT<float, DH> {
-  static constexpr int ROWB = DH * 4;
-  static constexpr int PIECES = ROWB / 16;
-  static constexpr int LP = PIECES / 4;       // pieces = 4*LP floats = DH/4 MFMA steps
-  static constexpr int NDT = DH / 16;
-  static constexpr int VB = NDT * 4;
+  static constexpr int ROWB = DH * 4, PIECES = ROWB / 16, LP = PIECES / 4, NDT = DH / 16, VB = NDT * 4;
+  struct QF { V4u p[LP]; };
+  struct KF { V4u p[2][LP]; };
   typedef Words<NDT> VV;
-  struct QF { u32x4 p[LP]; };
-  static __device__ __forceinline__ f32x4 qk(const QF& k, const QF& q) {
+  struct VF { VV v[8]; };
+  static constexpr int NVR = 8;
+  static __device__ __forceinline__ void load_q(QF& q, const char* row, int g) {
+#pragma unroll
+    for (int s = 0; s < LP; ++s) q.p[s] = *(const V4u*)(row + 16 * (LP * g + s));
+  }
+  static __device__ __forceinline__ int vkey(int g, int c, int j) { return slot_key(g, j); }
+  static __device__ __forceinline__ void load_k(KF& k, uint32_t base, const int (&rk)[2], int g) {
+#pragma unroll
+    for (int kg = 0; kg < 2; ++kg)
+#pragma unroll
+      for (int s = 0; s < LP; ++s) k.p[kg][s] = lds_get<V4u>(piece_addr<ROWB>(base, rk[kg], LP * g + s));
+  }
+  // slot e of lane (g, c): key row rvs[e]; the lane reads the NDT dims NDT*c .. of it
+  static __device__ __forceinline__ void load_v8(VF& v, uint32_t base, const int (&rvs)[8], int c) {
+    const int off = VB * c;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t a = piece_addr<ROWB>(base, rvs[e], off / 16) + off % 16;
+      if constexpr (NDT == 1) {
+        v.v[e].w[0] = lds_get<uint32_t>(a);
+      } else {
+        v.v[e] = __builtin_bit_cast(VV, lds_get<V4u>(a));
+      }
+    }
+  }
+  static __device__ __forceinline__ void load_vr(VF& v, uint32_t base, const int (&rv)[NVR], int c) {
+    load_v8(v, base, rv, c);
+  }
+  struct Lofs {};
+  static __device__ __forceinline__ Lofs lane_ofs(int, int) { return Lofs{}; }
+  static __device__ __forceinline__ void load_k_at(KF& k, uint32_t base, const Lofs&, int g, int c) {
+    const int rk[2] = {c, 16 + c};
+    load_k(k, base, rk, g);
+  }
+  static __device__ __forceinline__ void load_v_at(VF& v, uint32_t base, const Lofs&, int g, int c) {
+    int rv[NVR];
+#pragma unroll
+    for (int j = 0; j < NVR; ++j) rv[j] = vkey(g, c, j);
+    load_v8(v, base, rv, c);
+  }
+  static __device__ __forceinline__ f32x4 qk(const KF& k, int kg, const QF& q) {
     f32x4 acc = {0, 0, 0, 0};
 #pragma unroll
-    for (int s = 0; s < LP; ++s) {
-      acc = mfma_f32_4(__uint_as_float(k.p[s].x), __uint_as_float(q.p[s].x), acc);
-      acc = mfma_f32_4(__uint_as_float(k.p[s].y), __uint_as_float(q.p[s].y), acc);
-      acc = mfma_f32_4(__uint_as_float(k.p[s].z), __uint_as_float(q.p[s].z), acc);
-      acc = mfma_f32_4(__uint_as_float(k.p[s].w), __uint_as_float(q.p[s].w), acc);
-    }
+    for (int s = 0; s < LP; ++s)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc = mfma_f32_4(__uint_as_float(k.p[kg][s][j]), __uint_as_float(q.p[s][j]), acc);
     return acc;
   }
   struct PP { float p[8]; };
@@ -151,22 +280,12 @@ template <int DH> struct AttnT<float, DH> {
     for (int e = 0; e < 8; ++e) r.p[e] = ps[e];
     return r;
   }
-  struct VA { float v[8]; };
-  template <typename V> static __device__ __forceinline__ VA va(int dt, const V* vv) {
-    VA r;
+  static __device__ __forceinline__ f32x4 pv(const VF& v, int dt, const PP& pp, f32x4 o) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) r.v[e] = __uint_as_float(vv[e].w[dt]);
-    return r;
-  }
-  static __device__ __forceinline__ f32x4 pva(const VA& A, const PP& pp, f32x4 o) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o = mfma_f32_4(A.v[e], pp.p[e], o);
+    for (int e = 0; e < 8; ++e) o = mfma_f32_4(__uint_as_float(v.v[e].w[dt]), pp.p[e], o);
     return o;
   }
-  template <typename V>
-  static __device__ __forceinline__ f32x4 pv(int dt, const V* vv, const PP& pp, f32x4 o) {
-    return pva(va(dt, vv), pp, o);
-  }
+  static __device__ __forceinline__ int dim(int dt, int i) { return NDT * i + dt; }
 };
 
 // Reductions over the 4 lanes of a row (lanes l, l^16, l^32, l^48) with the
@@ -185,15 +304,11 @@ __device__ __forceinline__ float row4_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// Rescale threshold of the running reference (log2 units): the reference m
-// moves to a chunk's maximum only when that maximum exceeds it by more than
-// this, so p = 2^(s - m) stays below 2^RESCALE and O is rarely rescaled.
-#define RESCALE 8.0f
-
 // Softmax half of one online chunk step for the lane's row.  s[e]: raw QK
 // score of slot e (-inf: not visible).  Updates the reference m and l, leaves
 // p in s and returns the factor the running O must be scaled by before P V is
 // added.  A row that has seen no key yet keeps its state (factor 1, p = 0).
+// Straight-line code: a chunk's tiles interleave freely.
 __device__ __forceinline__ float chunk_softmax(float (&s)[8], float sl2, float& m, float& l) {
   float mx = s[0];
 #pragma unroll
@@ -202,21 +317,13 @@ __device__ __forceinline__ float chunk_softmax(float (&s)[8], float sl2, float& 
   const float mn = (m == NEG_INF || mc > m + RESCALE) ? mc : m;
   const bool live = mn != NEG_INF;
   const float wa = (live && mn != m) ? ex2(m - mn) : 1.f;
+  // -mn, or -inf for a row with nothing visible (its scores are all -inf, so p = 2^-inf = 0)
+  const float nm = live ? -mn : NEG_INF;
   float ls = 0.f;
-  if (__ballot(!live) == 0ull) {                  // every row has a visible key (the usual case)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float p = ex2(__builtin_fmaf(s[e], sl2, -mn));
-      s[e] = p;
-      ls += p;
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float p = live ? ex2(__builtin_fmaf(s[e], sl2, -mn)) : 0.f;
-      s[e] = p;
-      ls += p;
-    }
+  for (int e = 0; e < 8; ++e) {
+    s[e] = ex2(__builtin_fmaf(s[e], sl2, nm));
+    ls += s[e];
   }
   l = __builtin_fmaf(l, wa, row4_sum(ls));
   m = live ? mn : m;
@@ -224,235 +331,142 @@ __device__ __forceinline__ float chunk_softmax(float (&s)[8], float sl2, float& 
 }
 
 template <int NDT> __device__ __forceinline__ void scale_o(f32x4* O, float wa) {
-  if (__ballot(wa != 1.f) == 0ull) return;       // running maximum unchanged everywhere: O * 1 = O
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
     for (int r = 0; r < 4; ++r) O[dt][r] *= wa;
 }
 
-// One workgroup per (KV head, row group, key split); a row group is NT =
-// TP * TPW tiles of 16 query rows; wave w is class c = w / TP of tile pair
-// slot w % TP, which holds TPW tiles: the K and V fragments a wave reads
-// from the ring serve all its tiles.  A key split is a fixed run of spb ring
-// stages (spb is a function of the cache capacity only); several splits
-// leave one folded state per row each, and a merge kernel folds them in
-// split order (a split's chunks, tail chunks included, are fixed by
-// position, so the tree still depends on positions only).
-// Three phases per workgroup:
-//   1. tail (splits that hold one): the chunks reaching past shared_end (at
-//      most one per class, the highest positions of the split, so the first
-//      in their class): the ring's space is used to stage, per tile, the
-//      committed rows [32 tail0, shared_end) and, for each branch in the
-//      tile, its workspace rows of positions shared_end .. max_pos (read
-//      through the branch path); the scores come per branch and P V runs once
-//      per branch (rows of other branches add exact zeros);
-//   2. prefix: ring stage s holds keys [128 s, 128 s + 128) of the head (the
-//      class-c chunk 4 s + c, K and V, 16-byte pieces XOR-swizzled by row)
-//      for every chunk below shared_end (or up to the largest row position
-//      when nothing reaches past it), stages taken from the split's last to
-//      its first; each class wave takes its chunk of the stage with the
-//      online step, so a stage is read from HBM once for all the workgroup's
-//      tiles and classes;
-//   3. fold: every class wave hands its states over through LDS and folds,
-//      for one accumulator row of each tile, classes 0, 1, 2, 3 in order,
-//      then stores O / l (or the split's state).
-// Every global load of the ring is a DMA into LDS read back with inline asm;
-// the waits are static vmcnt counts (every wave issues the same DMA count per
-// stage).
-// Whether key split s holds chunks that reach past shared_end (a chunk
-// belongs to the split of its position).
-__host__ __device__ __forceinline__ bool split_has_tail(const LaAttnArgs& a, int s) {
-  const int per = a.spb * NCLS;
-  return max(a.tail0, s * per) < min(a.tail0 + a.n_tail, (s + 1) * per);
+// Tail stage addressing.  Stage row of position x on a branch: committed
+// positions (below shared_end) sit at x - tbase; later ones at ncom + the
+// branch's workspace row for x, read from the staged path table (word w of
+// path_read).  Positions the branch does not reach are never visible to its
+// rows; they read staged row 0.
+template <int NR> __device__ __forceinline__ void path_read(uint32_t (&w)[NR], uint32_t pst, int b,
+                                                            const int (&x)[NR], int se, int maxp) {
+#pragma unroll
+  for (int j = 0; j < NR; ++j) w[j] = lds_get<uint32_t>(pst + 4 * (uint32_t)(b * maxp + min(max(x[j] - se, 0), maxp - 1)));
+}
+template <int NR> __device__ __forceinline__ void path_rows(int (&r)[NR], const uint32_t (&w)[NR], const int (&x)[NR],
+                                                            int se, int tbase, int ncom, int nws) {
+#pragma unroll
+  for (int j = 0; j < NR; ++j) r[j] = x[j] < se ? x[j] - tbase : (w[j] < (unsigned)nws ? ncom + (int)w[j] : 0);
 }
 
-template <typename T, int DH, int TP, int TPW>
-__global__ void __launch_bounds__(64 * NCLS * TP) __attribute__((amdgpu_waves_per_eu(1, TP)))
-la_attn_kernel(LaAttnArgs a) {
-  typedef AttnT<T, DH> AT;
-  typedef typename AT::QF QF;
-  typedef typename AT::VV VV;
-  constexpr int NW = NCLS * TP;                 // waves
-  constexpr int NT = TP * TPW;                  // tiles per workgroup
-  constexpr int ROWB = AT::ROWB, PIECES = AT::PIECES, LP = AT::LP, NDT = AT::NDT, VB = AT::VB;
-  constexpr int CHB = CH * ROWB;                // K (or V) of one chunk
-  constexpr int BLKB = NCLS * 2 * CHB;          // one ring stage: 4 chunks, K then V each
-  constexpr int NDMA = BLKB / 1024;
-  constexpr int CW = NDMA / NW;                 // DMA instructions per stage and wave
-  static_assert(NDMA % NW == 0 && CW >= 1, "DMA blocks per wave");
-  constexpr int DEPTH = 2;
-  constexpr int RPB = 1024 / ROWB;              // key rows per 1 KB DMA block
-  // Q tiles and row positions (one DMA of 64 lanes per tile); the ring starts 1 KB aligned
-  constexpr int FIX = (NT * (16 * ROWB + 256) + 1023) & ~1023;
-  extern __shared__ __attribute__((aligned(1024))) char lds[];
-  char* const ring = lds + FIX;                 // ring stages, later the tail rows, then the fold states
+// Wait until at most k of the wave's chunk loads (pw loads each) are in flight, 0 <= k < KMAX.
+template <int PW, int KMAX, int K = 0> __device__ __forceinline__ void ring_wait(int k) {
+  if constexpr (K + 1 >= KMAX) {
+    dma_wait<K * PW>();
+  } else {
+    if (k <= K) dma_wait<K * PW>();
+    else ring_wait<PW, KMAX, K + 1>(k);
+  }
+}
 
-  // block -> (XCD, KV head, key split, row group): the workgroups of one
-  // head share an XCD (and its L2).  A split holding tail chunks gets two
-  // workgroups per row group when a wave has two tiles (each takes one tile
-  // of every tile pair), so the tail work of a tile pair runs in parallel.
+// One workgroup per (KV head, key split, row group of NW x TPW tiles); a
+// ring of D chunk slots.
+template <typename T, int DH, int NW, int TPW, int D>
+__global__ void __launch_bounds__(64 * NW) la_attn_kernel(LaAttnArgs a) {
+  typedef AttnT<T, DH> AT;
+  constexpr int ROWB = AT::ROWB, NDT = AT::NDT, NVR = AT::NVR;
+  constexpr int CHB = CH * ROWB;                 // K (or V) of one chunk
+  constexpr int SLOT = 2 * CHB;                  // one ring slot: K then V
+  constexpr int NI = SLOT / 1024;                // 1 KB DMA instructions per chunk
+  constexpr int PW = NI >= NW ? NI / NW : 1;     // per wave (waves past NI repeat wave w % NI's load)
+  static_assert(NI % NW == 0 || NW % NI == 0, "DMA split");
+  static_assert(D >= 2 && (D - 1) * PW < 64, "ring depth within the vmcnt range");
+  constexpr int RPB = 1024 / ROWB;               // rows per DMA instruction
+  constexpr int PIECES = ROWB / 16;
+  extern __shared__ __attribute__((aligned(1024))) char lds[];
+
+  // block -> (XCD, KV head, split, row group); the highest splits (tail chunks) first
   const int xcd = blockIdx.x & 7, bi = blockIdx.x >> 3;
   const int g_kv = xcd + 8 * (bi / a.wg_head);
   if (g_kv >= a.Hkv) return;
-  int li = bi % a.wg_head, sp = 0, hf = -1;
-  for (; sp < a.nsplit; ++sp) {
-    const bool half = TPW == 2 && a.tail_half && split_has_tail(a, sp);
-    const int n = a.rgroups * (half ? 2 : 1);
-    if (li < n) {
-      if (half) {
-        hf = li % 2;
-        li /= 2;
-      }
-      break;
-    }
-    li -= n;
-  }
-  if (sp == a.nsplit) return;
-  const int rg = li;
+  const int li = bi % a.wg_head;
+  const int sp = a.nsplit - 1 - li / a.rgroups;
+  const int rg = li % a.rgroups;
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int cls = wave / TP, pslot = wave % TP;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, c16 = lane & 15;
   const int se = a.shared_end;
   const float sl2 = a.scale_log2;
   const char* kc = (const char*)a.kc + (size_t)g_kv * a.T_cap * ROWB;
   const char* vc = (const char*)a.vc + (size_t)g_kv * a.T_cap * ROWB;
 
-  // the wave's tiles: 16 rows of q-head hh each (rows past Q load row Q - 1
-  // and stay unused; a tile past the head group is skipped)
+  // this split's chunks: ring chunks [r_lo, r_hi), tail chunks [t_lo, t_hi), all taken in decreasing order
+  const int s_lo = sp * a.spl, s_hi = s_lo + a.spl;
+  const int r_lo = s_lo, r_hi = min(s_hi, a.ring_end);
+  const int t_lo = max(s_lo, a.tail0), t_hi = min(s_hi, a.tail0 + a.n_tail);
+  const bool has_tail = t_lo < t_hi;              // uniform over the workgroup
+  const int nring = max(0, r_hi - r_lo);
+
+  // the wave's tiles, row-tile major: tile t = rows 16 (t / group) .., query
+  // head g_kv * group + t % group (a wave's tiles share their rows when the
+  // group is at least TPW, and so their branches).  Rows past Q (and tiles
+  // past the last) compute on row Q - 1's data and store nothing.  Nothing
+  // is computed from the loads until they are needed: the compiler does not
+  // count the asm DMA, so its wait for them also waits for the DMA issued
+  // before that point.
   const int group = a.H / a.Hkv;
   const int rtiles = (a.Q + 15) >> 4;
   bool tv[TPW], rvalid[TPW];
-  int hh[TPW], row[TPW];
+  int hh[TPW], row[TPW], pos[TPW];
+  typename AT::QF qf[TPW];
 #pragma unroll
   for (int u = 0; u < TPW; ++u) {
-    const int tile = rg * NT + pslot * TPW + (hf >= 0 ? hf : u);
-    tv[u] = (hf < 0 || u == 0) && tile < group * rtiles;
-    hh[u] = g_kv * group + (tv[u] ? tile / rtiles : 0);
-    row[u] = (tv[u] ? tile % rtiles : 0) * 16 + c16;
+    const int tile = (rg * NW + wave) * TPW + u;
+    tv[u] = tile < group * rtiles;
+    hh[u] = g_kv * group + (tv[u] ? tile % group : 0);
+    row[u] = (tv[u] ? tile / group : 0) * 16 + c16;
     rvalid[u] = tv[u] && row[u] < a.Q;
-  }
-  auto qa = [&](int u) __attribute__((always_inline)) { return lds + (pslot * TPW + u) * 16 * ROWB; };
-  auto pa = [&](int u) __attribute__((always_inline)) { return lds + NT * 16 * ROWB + (pslot * TPW + u) * 256; };
-  // Chunks of a class are taken in decreasing position, so a split's tail
-  // chunks (the highest positions) come first: a workgroup with tail chunks
-  // applies them before its ring starts (the ring's space holds the tiles'
-  // branch tables and staged rows meanwhile), and the ring then walks its
-  // stages from the last to the first.
-  const int t_lo = max(a.tail0, sp * a.spb * NCLS), t_hi = min(a.tail0 + a.n_tail, (sp + 1) * a.spb * NCLS);
-  const bool has_tail = t_lo < t_hi;              // split_has_tail(a, sp): uniform over the workgroup
-  int* const spath0 = (int*)ring;                 // tail: [NT][16 branches][64 positions] workspace rows
-  int* const meta0 = (int*)(ring + NT * 16 * 64 * 4);   // tail: [NT][64] branch count, branch ids
-  if (cls == 0) {
-#pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-      const int row0 = row[u] - c16;
-      __builtin_amdgcn_global_load_lds((const void*)(a.pos + min(row0 + (lane & 15), a.Q - 1)), (lds_void_t*)pa(u), 4,
-                                       0, 0);
-#pragma unroll
-      for (int j = 0; j < 16 / RPB; ++j) {
-        const int r = min(row0 + j * RPB + lane / PIECES, a.Q - 1);
-        const char* src = (const char*)a.q + ((size_t)r * a.H + hh[u]) * ROWB + 16 * (lane % PIECES);
-        __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(qa(u) + j * 1024), 16, 0, 0);
-      }
-      if (has_tail && tv[u]) {                    // the tile's branch tables (row builder)
-        const int rt = row0 >> 4;
-        __builtin_amdgcn_global_load_lds((const void*)(a.tile_meta + (size_t)rt * 64 + lane),
-                                         (lds_void_t*)(meta0 + (pslot * TPW + u) * 64), 4, 0, 0);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          __builtin_amdgcn_global_load_lds((const void*)(a.tile_path + (size_t)rt * 1024 + j * 256 + 4 * lane),
-                                           (lds_void_t*)(spath0 + (pslot * TPW + u) * 1024 + j * 256), 16, 0, 0);
-      }
-    }
+    const int rr = min(row[u], a.Q - 1);
+    AT::load_q(qf[u], (const char*)a.q + ((size_t)rr * a.H + hh[u]) * ROWB, g);
+    pos[u] = a.pos[rr];
   }
 
-  // ring stage s: chunks 4 s .. 4 s + 3; outside the split's stages every
-  // lane loads one 16-byte piece (a dummy that nobody reads), so every wave
-  // issues CW DMA instructions per stage on every path
-  const int nblk = (a.class_last + NCLS) / NCLS;   // stages of the whole prefix (class_last = -1: none)
-  const int s_begin = sp * a.spb;                     // this split's stages
-  const int s_end = min(s_begin + a.spb, nblk);
-  // wave w brings the DMA blocks w*CW .. w*CW + CW - 1 of a stage (a
-  // contiguous run inside its chunk cw of the stage: CW divides the 1 KB
-  // blocks of a chunk half or is a multiple of them).  The lane's source
-  // offset inside a chunk is the same for every stage; only stages that
-  // reach past shared_end clamp rows.
-  constexpr int HB = CHB / 1024;                // 1 KB blocks in a chunk's K (or V)
-  static_assert(HB % CW == 0 || CW % HB == 0, "DMA runs");
-  const int b0 = wave * CW;
-  const int cw = b0 / (2 * HB);
-  // K or V of block j: one half for the whole run when CW <= HB, else the
-  // run is a whole chunk (K blocks, then V blocks)
-  constexpr bool WHOLE = CW > HB;
-  const char* const half0 = ((b0 / HB) & 1) ? vc : kc;
-  auto kv_of = [&](int j) __attribute__((always_inline)) -> const char* { return WHOLE ? ((j / HB) ? vc : kc) : half0; };
-  int oj[CW];
+  // LDS: [tail stage (K rows, V rows, path table)] [ring of D slots]
+  const int st_bytes = has_tail ? a.st_bytes : 0;
+  char* const ring = lds + st_bytes;
+
+  // ring chunk i (0 = the split's last ring chunk, i < nring) into slot
+  // i % D.  A chunk wholly below shared_end is one affine run of rows; in
+  // the last chunk of a call without tail, rows past shared_end - 1 repeat
+  // it (never visible).
+  uint32_t lsrc[PW];                              // the lane's byte offset inside a chunk, per load
 #pragma unroll
-  for (int j = 0; j < CW; ++j) {
-    const int r = ((b0 + j) % HB) * RPB + lane / PIECES;
-    oj[j] = r * ROWB + 16 * ((lane % PIECES) ^ (r % PIECES));
+  for (int j = 0; j < PW; ++j) {
+    const int ins = (wave * PW + j) % NI;
+    const int r = (ins % (NI / 2)) * RPB + lane / PIECES;
+    lsrc[j] = r * ROWB + 16 * ((lane % PIECES) ^ (r % PIECES));
   }
-  auto issue = [&](char* stage, int s) __attribute__((always_inline)) {
-    const int x0 = CH * (NCLS * s + cw);
-    const bool in = s >= s_begin && s < s_end;
-    if (in && x0 + CH <= se) {                  // the whole chunk lies below shared_end
+  auto issue = [&](int i) __attribute__((always_inline)) {
+    const int cidx = r_hi - 1 - i;
+    const uint32_t slot = lds_addr(ring) + (uint32_t)(i % D) * SLOT;
+    if (CH * cidx + CH <= se) {
 #pragma unroll
-      for (int j = 0; j < CW; ++j) {
-        const char* base = kv_of(j);
-        __builtin_amdgcn_global_load_lds((const void*)(base + (size_t)x0 * ROWB + oj[j]),
-                                         (lds_void_t*)(stage + (b0 + j) * 1024), 16, 0, 0);
+      for (int j = 0; j < PW; ++j) {
+        const int ins = (wave * PW + j) % NI;     // 0 .. NI-1: K blocks, then V blocks
+        const int half = ins / (NI / 2), blk = ins % (NI / 2);
+        dma16((half ? vc : kc) + (size_t)cidx * CHB + lsrc[j], slot + half * CHB + blk * 1024);
       }
-    } else if (in) {                            // rows past shared_end - 1 repeat it (never visible)
+    } else {
 #pragma unroll
-      for (int j = 0; j < CW; ++j) {
-        const char* base = kv_of(j);
-        const int r = ((b0 + j) % HB) * RPB + lane / PIECES;
-        const int off = oj[j] - r * ROWB;
-        __builtin_amdgcn_global_load_lds((const void*)(base + (size_t)min(x0 + r, se - 1) * ROWB + off),
-                                         (lds_void_t*)(stage + (b0 + j) * 1024), 16, 0, 0);
+      for (int j = 0; j < PW; ++j) {
+        const int ins = (wave * PW + j) % NI;
+        const int half = ins / (NI / 2), blk = ins % (NI / 2);
+        const int r = blk * RPB + lane / PIECES;
+        const int src_row = min(CH * cidx + r, se - 1);
+        dma16((half ? vc : kc) + (size_t)src_row * ROWB + 16 * ((lane % PIECES) ^ (r % PIECES)),
+              slot + half * CHB + blk * 1024);
       }
-    } else {                                    // outside the split: one valid 16-byte piece
-#pragma unroll
-      for (int j = 0; j < CW; ++j)
-        __builtin_amdgcn_global_load_lds((const void*)(kc + (size_t)(se - 1) * ROWB),
-                                         (lds_void_t*)(stage + (b0 + j) * 1024), 16, 0, 0);
     }
   };
-  // the rows' branches (read now, used by the tail phase)
-  int br[TPW];
-#pragma unroll
-  for (int u = 0; u < TPW; ++u) br[u] = (a.n_tail > 0 && rvalid[u]) ? a.branch[row[u]] : -1;
-  // Without tail chunks the ring's first stage goes out with Q and is waited
-  // for here; its second stage follows once Q is read, so the first stage
-  // is not held up behind every workgroup's second one.
-  if (!has_tail) issue(ring, s_end - 1);
-  wait_vm<0>();                                      // this wave's Q, positions, branches (and first stage)
-  ring_barrier();                                    // ... and those of the other waves
-  QF qf[TPW];
-  int pos[TPW], pmin[TPW];
-#pragma unroll
-  for (int u = 0; u < TPW; ++u) {
-    typename LdsT<16>::T qraw[LP];
-    const uint32_t qaddr = lds_addr(qa(u) + c16 * ROWB + 16 * LP * g);
-    if constexpr (LP >= 1) qraw[0] = lds_read<16, 0>(qaddr);
-    if constexpr (LP >= 2) qraw[1] = lds_read<16, 16>(qaddr);
-    if constexpr (LP >= 3) qraw[2] = lds_read<16, 32>(qaddr);
-    if constexpr (LP >= 4) qraw[3] = lds_read<16, 48>(qaddr);
-    unsigned int praw[1] = {lds_read<4, 0>(lds_addr(pa(u) + 4 * c16))};
-    lds_wait(qraw);
-    lds_wait(praw);
-#pragma unroll
-    for (int s = 0; s < LP; ++s) qf[u].p[s] = rvalid[u] ? __builtin_bit_cast(u32x4, qraw[s]) : u32x4{0, 0, 0, 0};
-    pos[u] = rvalid[u] ? (int)praw[0] : -1;
-    // smallest position among the tile's rows: chunks ending at or below it need no mask
-    int pm = rvalid[u] ? pos[u] : 0x7fffffff;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) pm = min(pm, __shfl_xor(pm, o, 64));
-    pmin[u] = __builtin_amdgcn_readfirstlane(pm);
-  }
 
+  // tail WGs: each tile's distinct branches (lane i < 16: the i-th) and each row's branch, loaded with Q
+  int nbr[TPW], bid[TPW], br[TPW];
+  const int ncom = se - CH * a.tail0;
   float M[TPW], L[TPW];
   f32x4 O[TPW][NDT];
 #pragma unroll
@@ -463,320 +477,311 @@ la_attn_kernel(LaAttnArgs a) {
     for (int dt = 0; dt < NDT; ++dt) O[u][dt] = f32x4{0, 0, 0, 0};
   }
 
-  if (has_tail) {
-    const int X0 = CH * a.tail0;
-    const int ncom = se - X0;                       // 0 .. 31
-    const int EP = a.max_pos - se + 1;              // 1 .. 64
-    // staged rows of each tile pair slot, after the branch tables
-    char* const ks = ring + NT * (16 * 64 + 64) * 4 + pslot * 2 * a.trows * ROWB;
-    char* const vs = ks + a.trows * ROWB;
-    // the tiles' distinct branches (lane i < nbr: branch i)
-    int nbr[TPW], bl[TPW];
-#pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-      const int* mt = meta0 + (pslot * TPW + u) * 64;
-      nbr[u] = tv[u] ? min(mt[0], 16) : 0;
-      bl[u] = (tv[u] && lane < 16) ? mt[1 + lane] : -1;
-    }
-    // branches staged at once per tile (the committed rows, then EP rows per
-    // branch), and the batches every tile of the workgroup goes through
-    const int bb = (a.trows - ncom) / EP;           // >= 1 (the launcher sizes trows)
-    int* const nbat = (int*)(lds + NT * 16 * ROWB);   // the row positions' space, free since they were read
-    if (cls == 0 && lane == 0) {
-#pragma unroll
-      for (int u = 0; u < TPW; ++u) nbat[pslot * TPW + u] = (nbr[u] + bb - 1) / bb;
-    }
-    __syncthreads();
-    int nbatch = 0;
-#pragma unroll
-    for (int t = 0; t < NT; ++t) nbatch = max(nbatch, nbat[t]);
-    const char* kw = (const char*)a.kw + (size_t)g_kv * a.ws_cap * ROWB;
-    const char* vw = (const char*)a.vw + (size_t)g_kv * a.ws_cap * ROWB;
-    const int tau = (cls - a.tail0 % NCLS + NCLS) % NCLS;   // the class's tail chunk (at most one)
-    const bool mine_chunk = tau < a.n_tail && a.tail0 + tau >= t_lo && a.tail0 + tau < t_hi;
-    // With a single tail chunk in the split its branches are spread over the
-    // four class waves (wave c takes the batch branches i with i % 4 == c);
-    // every wave starts from the empty state (the tail comes first), and the
-    // chunk's class wave then collects each row's state from the wave that
-    // handled the row's branch, through the staging space.
-    constexpr int SF = 2 + 4 * NDT;                 // floats of one lane's state
-    const bool spread = t_hi - t_lo == 1 && 2 * a.trows * ROWB >= NCLS * SF * 64 * 4;
-    const int cstar = t_lo % NCLS;
-    const int x0 = CH * (spread ? t_lo : a.tail0 + tau);
-    const bool work = spread || mine_chunk;
-    auto srow = [&](int x, int bi) -> int {
-      if (x < se) return x - X0;
-      const int e = x - se;
-      return e < EP ? ncom + bi * EP + e : 0;
-    };
-#pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-      if (hf >= 0 && u > 0) break;                // one tile per pair slot (uniform over the workgroup)
-      const int* const spath = spath0 + (pslot * TPW + u) * 1024;
-      const bool need = work && rvalid[u] && pos[u] >= x0;
-      bool own = false;                           // a branch this wave handled holds the lane's row
-      for (int bt = 0; bt < nbatch; ++bt) {
-        const int i0 = bt * bb;
-        const int nb = max(0, min(bb, nbr[u] - i0));
-        // staged row of key x on batch branch bi (x >= X0); a clamped committed
-        // row where a position is not on the branch's path (never visible to it)
-        const int nr = nb > 0 ? ncom + nb * EP : 0;
-        for (int blk = cls; blk * RPB < nr; blk += NCLS) {
-          const int j = blk * RPB + lane / PIECES;
-          const int piece = (lane % PIECES) ^ (j % PIECES);
-          int crow = se - 1, wrow = -1;
-          if (j < ncom) crow = X0 + j;
-          else if (j < nr) {
-            wrow = spath[(i0 + (j - ncom) / EP) * 64 + (j - ncom) % EP];
-            if ((unsigned)wrow >= (unsigned)a.n_ws) wrow = -1;
-          }
-          const size_t off = (size_t)(wrow >= 0 ? wrow : crow) * ROWB + 16 * piece;
-          __builtin_amdgcn_global_load_lds((const void*)((wrow >= 0 ? kw : kc) + off), (lds_void_t*)(ks + blk * 1024),
-                                           16, 0, 0);
-          __builtin_amdgcn_global_load_lds((const void*)((wrow >= 0 ? vw : vc) + off), (lds_void_t*)(vs + blk * 1024),
-                                           16, 0, 0);
-        }
-        wait_vm<0>();
-        __syncthreads();
-        // rows of this batch's branches: the chunk's online step (for the
-        // wave's other rows every score stays -inf, which leaves their state
-        // exactly as it is, and P V adds exact zeros)
-        if (nb > 0 && __ballot(need) != 0ull) {
-          float sc[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) sc[e] = NEG_INF;
-          for (int bi = 0; bi < nb; ++bi) {
-            if (spread && (i0 + bi) % NCLS != cls) continue;
-            const int b = __shfl(bl[u], i0 + bi, 64);
-            const bool mine = need && br[u] == b;
-            own |= mine;
-            if (__ballot(mine) == 0ull) continue;
-#pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-              const int r = srow(x0 + 16 * jj + c16, bi);
-              QF kf;
-#pragma unroll
-              for (int q = 0; q < LP; ++q)
-                kf.p[q] = *(const u32x4*)(ks + r * ROWB + 16 * ((LP * g + q) ^ (r % PIECES)));
-              const f32x4 s4 = AT::qk(kf, qf[u]);
-#pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                const float v = (x0 + 16 * jj + 4 * g + q <= pos[u]) ? s4[q] : NEG_INF;
-                sc[4 * jj + q] = mine ? v : sc[4 * jj + q];
-              }
-            }
-          }
-          const float wa = chunk_softmax(sc, sl2, M[u], L[u]);
-          scale_o<NDT>(O[u], wa);
-          for (int bi = 0; bi < nb; ++bi) {
-            if (spread && (i0 + bi) % NCLS != cls) continue;
-            const int b = __shfl(bl[u], i0 + bi, 64);
-            const bool mine = need && br[u] == b;
-            if (__ballot(mine) == 0ull) continue;
-            VV vv[8];
-            float ps[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int r = srow(x0 + slot_key(g, e), bi);
-              const int off = VB * c16;
-              vv[e] = *(const VV*)(vs + r * ROWB + 16 * ((off / 16) ^ (r % PIECES)) + off % 16);
-              ps[e] = mine ? sc[e] : 0.f;
-            }
-            const typename AT::PP pp = AT::prep(ps);
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) O[u][dt] = AT::pv(dt, vv, pp, O[u][dt]);
-          }
-        }
-        __syncthreads();                          // the staged rows are no longer read
-      }
-      if (spread) {
-        float* const sl = (float*)ks;             // [NCLS][SF][64] lane states, in the staging space
-        unsigned long long* const om = (unsigned long long*)(lds + NT * 16 * ROWB + 64) + pslot * NCLS;
-        const unsigned long long ownm = __ballot(own);
-        float* const my = sl + (size_t)cls * SF * 64;
-        my[lane] = M[u];
-        my[64 + lane] = L[u];
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) my[(2 + 4 * dt + r) * 64 + lane] = O[u][dt][r];
-        if (lane == 0) om[cls] = ownm;
-        __syncthreads();
-        if (cls == cstar) {
-#pragma unroll
-          for (int w = 0; w < NCLS; ++w) {
-            if (w == cls || ((om[w] >> lane) & 1ull) == 0ull) continue;
-            const float* src = sl + (size_t)w * SF * 64;
-            M[u] = src[lane];
-            L[u] = src[64 + lane];
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-              for (int r = 0; r < 4; ++r) O[u][dt][r] = src[(2 + 4 * dt + r) * 64 + lane];
-          }
-        } else {                                  // this class has no chunk in the tail
-          M[u] = NEG_INF;
-          L[u] = 0.f;
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) O[u][dt] = f32x4{0, 0, 0, 0};
-        }
-        __syncthreads();                          // the states are no longer read
-      }
-    }
-    // the tail is done with the ring's space: the ring starts
-    issue(ring, s_end - 1);
-  }
-  static_assert(DEPTH == 2, "ring start");
-  issue(ring + BLKB, s_end - 2);                   // the first step waits for the first stage only
-
-  // lane parts of the fragment addresses of the class's chunk (stage offsets are immediates)
-  uint32_t koff[LP], voff[4];
-#pragma unroll
-  for (int s = 0; s < LP; ++s)
-    koff[s] = lds_addr(ring + cls * 2 * CHB + c16 * ROWB + 16 * ((LP * g + s) ^ (c16 % PIECES)));
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int kk = 4 * g + e;                   // slot_key(g, e); slot e + 4 is 16 rows further
-    const int off = VB * c16;
-    voff[e] = lds_addr(ring + cls * 2 * CHB + CHB + kk * ROWB + 16 * ((off / 16) ^ (kk % PIECES)) + off % 16);
-  }
-
-  auto step = [&](auto SI, int s) __attribute__((always_inline)) {
-    constexpr int S = decltype(SI)::value;
-    constexpr int SB = S * BLKB;                // stage base
-    constexpr int SBH = SB & ~65535, SBL = SB & 65535;   // ds offsets reach 64 KB
-    wait_vm<CW * (DEPTH - 1)>();                // stage s landed (the next one may be in flight)
+  // committed chunks through the ring, in decreasing position, one set of
+  // K / V fragment registers: K of chunk i + 1 is read from LDS once the
+  // QK^T MFMAs of chunk i have their operands, V of chunk i + 1 once its P V
+  // MFMAs have theirs, so the reads overlap the softmax and the products.
+  // One barrier per chunk: chunk i + 1 has landed, and every wave has read
+  // chunk i, whose slot is then refilled.
+  const typename AT::Lofs lofs = AT::lane_ofs(g, c16);
+  auto slot_base = [&](int i) __attribute__((always_inline)) {
+    return (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr(ring) + (uint32_t)(i % D) * SLOT);
+  };
+  auto ring_part = [&]() __attribute__((always_inline)) {
+    if (nring <= 0) return;
+    typename AT::KF kf;
+    typename AT::VF vf;
+    ring_wait<PW, D - 1>(min(D - 2, nring - 1));   // chunk 0 landed (chunks 1 .. D - 2 may be in flight)
     ring_barrier();
-    const int k = NCLS * s + cls;               // the class's chunk
-    const bool live = k <= a.class_last;
-    // the chunk's K and V go to registers first, so the stage is released
-    // (and the stage two steps ahead issued) before any arithmetic
-    typename LdsT<16>::T kraw[2 * LP];
-    typename LdsT<VB>::T vraw[8];
-    if (live) {
+    // first use of Q and the positions where nothing used them yet: the
+    // compiler's wait for them (which also waits for the chunks issued so
+    // far) falls here, once, and not inside the loop
 #pragma unroll
-      for (int q = 0; q < LP; ++q) {
-        kraw[q] = lds_read<16, SBL>(koff[q] + SBH);
-        kraw[LP + q] = lds_read<16, SBL + 16 * ROWB>(koff[q] + SBH);
-      }
+    for (int u = 0; u < TPW; ++u) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        vraw[e] = lds_read<VB, SBL>(voff[e] + SBH);
-        vraw[e + 4] = lds_read<VB, SBL + 16 * ROWB>(voff[e] + SBH);
-      }
-      lds_wait(kraw);
-      lds_wait(vraw);
+      for (int s = 0; s < (int)(sizeof(qf[u].p) / sizeof(qf[u].p[0])); ++s) asm volatile("" : "+v"(qf[u].p[s]));
+      asm volatile("" : "+v"(pos[u]));
     }
-    ring_barrier();                             // every wave has read the stage
-    issue(ring + SB, s - DEPTH);
-    if (live) {
-      const int x0 = CH * k;
+    int pmin = 0x7fffffff;                          // smallest row position of the wave
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) pmin = min(pmin, pos[u]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) pmin = min(pmin, __shfl_xor(pmin, o, 64));
+    pmin = __builtin_amdgcn_readfirstlane(pmin);
+    if (D - 1 < nring) issue(D - 1);
+    AT::load_k_at(kf, slot_base(0), lofs, g, c16);
+    AT::load_v_at(vf, slot_base(0) + CHB, lofs, g, c16);
+    for (int i = 0; i < nring; ++i) {
+      const int x0 = CH * (r_hi - 1 - i);
       float sc[TPW][8];
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        QF kf;
+      for (int u = 0; u < TPW; ++u)
 #pragma unroll
-        for (int q = 0; q < LP; ++q) kf.p[q] = __builtin_bit_cast(u32x4, kraw[LP * jj + q]);
+        for (int kg = 0; kg < 2; ++kg) {
+          const f32x4 s4 = AT::qk(kf, kg, qf[u]);
 #pragma unroll
-        for (int u = 0; u < TPW; ++u) {
-          if (!tv[u]) continue;
-          const f32x4 s4 = AT::qk(kf, qf[u]);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) sc[u][4 * jj + r] = s4[r];
+          for (int r = 0; r < 4; ++r) sc[u][4 * kg + r] = s4[r];
         }
+      const bool more = i + 1 < nring;
+      if (more) {
+        ring_wait<PW, D - 1>(min(D - 2, nring - 2 - i));   // chunk i + 1 landed
+        ring_barrier();                           // every wave has read chunk i: its slot is free
+        if (i + D < nring) issue(i + D);
+        AT::load_k_at(kf, slot_base(i + 1), lofs, g, c16);
       }
-      typename AT::PP pp[TPW];
-#pragma unroll
-      for (int u = 0; u < TPW; ++u) {
-        if (!tv[u]) continue;
-        if (x0 + CH - 1 > pmin[u]) {            // some key of the chunk lies past some row
-#pragma unroll
-          for (int e = 0; e < 8; ++e) sc[u][e] = x0 + slot_key(g, e) <= pos[u] ? sc[u][e] : NEG_INF;
-        }
-        const float wa = chunk_softmax(sc[u], sl2, M[u], L[u]);
-        pp[u] = AT::prep(sc[u]);
-        scale_o<NDT>(O[u], wa);
-      }
-      VV vv[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) vv[e] = __builtin_bit_cast(VV, vraw[e]);
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const typename AT::VA A = AT::va(dt, vv);
+      if (x0 + CH - 1 > pmin) {                   // some key of the chunk lies past some row
 #pragma unroll
         for (int u = 0; u < TPW; ++u)
-          if (tv[u]) O[u][dt] = AT::pva(A, pp[u], O[u][dt]);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sc[u][e] = x0 + slot_key(g, e) <= pos[u] ? sc[u][e] : NEG_INF;
+      }
+      typename AT::PP pp[TPW];
+      float wa[TPW];
+      bool rescale = false;
+#pragma unroll
+      for (int u = 0; u < TPW; ++u) {
+        wa[u] = chunk_softmax(sc[u], sl2, M[u], L[u]);
+        pp[u] = AT::prep(sc[u]);
+        rescale |= wa[u] != 1.f;
+      }
+      if (__ballot(rescale) != 0ull) {            // a running maximum moved: O * wa (else O * 1 = O)
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) scale_o<NDT>(O[u], wa[u]);
+      }
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) O[u][dt] = AT::pv(vf, dt, pp[u], O[u][dt]);
+      if (more) AT::load_v_at(vf, slot_base(i + 1) + CHB, lofs, g, c16);
+    }
+  };
+  // chunks past shared_end, from the tail stage (the highest positions of the split: they come first)
+  auto tail_part = [&]() __attribute__((always_inline)) {
+    ring_barrier();                               // every wave's part of the stage is visible
+    int pmax[TPW];                                // largest row position of each tile
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      int px = pos[u];
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) px = max(px, __shfl_xor(px, o, 64));
+      pmax[u] = __builtin_amdgcn_readfirstlane(px);
+    }
+    // the distinct branches of the wave's tiles: lane k < nu holds the k-th
+    int ub = -1, nu = 0;
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const int n = __builtin_amdgcn_readfirstlane(nbr[u]);
+      for (int i = 0; i < n; ++i) {
+        const int b = __builtin_amdgcn_readlane(bid[u], i);
+        if (__ballot(ub == b) == 0ull) {
+          ub = lane == nu ? b : ub;
+          ++nu;
+        }
+      }
+    }
+    const uint32_t kst = lds_addr(lds), vst = kst + a.st_half, pst = kst + 2 * a.st_half;
+    const int maxp = a.maxp, nws = a.n_ws, tbase = CH * a.tail0;
+    for (int cidx = t_hi - 1; cidx >= t_lo; --cidx) {
+      const int x0 = CH * cidx;
+      bool tl[TPW];                               // tiles with a row reaching the chunk (uniform)
+#pragma unroll
+      for (int u = 0; u < TPW; ++u) tl[u] = tv[u] && pmax[u] >= x0;
+      const int xk[2] = {x0 + c16, x0 + 16 + c16};
+      int xv[NVR];
+#pragma unroll
+      for (int j = 0; j < NVR; ++j) xv[j] = x0 + AT::vkey(g, c16, j);
+
+      // QK^T, branch by branch: branch k's K fragments are read while the
+      // MFMAs of branch k - 1 run; a row keeps the scores of its own branch
+      float sc[TPW][8];
+#pragma unroll
+      for (int u = 0; u < TPW; ++u)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sc[u][e] = NEG_INF;
+      auto qk_branch = [&](const typename AT::KF& kf, int b) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+          const bool mine = br[u] == b;
+          if (!tl[u] || __ballot(mine) == 0ull) continue;
+#pragma unroll
+          for (int kg = 0; kg < 2; ++kg) {
+            const f32x4 s4 = AT::qk(kf, kg, qf[u]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float v = (x0 + 16 * kg + 4 * g + r <= pos[u]) ? s4[r] : NEG_INF;
+              sc[u][4 * kg + r] = mine ? v : sc[u][4 * kg + r];
+            }
+          }
+        }
+      };
+      if (nu > 0) {
+        typename AT::KF ka, kb;
+        uint32_t w[2];
+        int rk[2];
+        path_read(w, pst, __builtin_amdgcn_readlane(ub, 0), xk, se, maxp);
+        path_rows(rk, w, xk, se, tbase, ncom, nws);
+        AT::load_k(ka, kst, rk, g);
+        if (nu > 1) path_read(w, pst, __builtin_amdgcn_readlane(ub, 1), xk, se, maxp);
+        for (int k = 0; k < nu; k += 2) {
+          // ka: branch k; w: path words of branch k + 1
+          if (k + 1 < nu) {
+            path_rows(rk, w, xk, se, tbase, ncom, nws);
+            AT::load_k(kb, kst, rk, g);
+            if (k + 2 < nu) path_read(w, pst, __builtin_amdgcn_readlane(ub, k + 2), xk, se, maxp);
+          }
+          qk_branch(ka, __builtin_amdgcn_readlane(ub, k));
+          if (k + 1 >= nu) break;
+          if (k + 2 < nu) {
+            path_rows(rk, w, xk, se, tbase, ncom, nws);
+            AT::load_k(ka, kst, rk, g);
+            if (k + 3 < nu) path_read(w, pst, __builtin_amdgcn_readlane(ub, k + 3), xk, se, maxp);
+          }
+          qk_branch(kb, __builtin_amdgcn_readlane(ub, k + 1));
+        }
+      }
+      float wa[TPW];
+      bool rescale = false;
+#pragma unroll
+      for (int u = 0; u < TPW; ++u) {
+        wa[u] = chunk_softmax(sc[u], sl2, M[u], L[u]);
+        rescale |= tl[u] && wa[u] != 1.f;
+      }
+      if (__ballot(rescale) != 0ull) {
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) scale_o<NDT>(O[u], wa[u]);
+      }
+      // P V, branch by branch: a row's probabilities enter only its own
+      // branch's product (the other branches add exact zeros)
+      auto pv_branch = [&](const typename AT::VF& vf, int b) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+          const bool mine = br[u] == b;
+          if (!tl[u] || __ballot(mine) == 0ull) continue;
+          float ps[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ps[e] = mine ? sc[u][e] : 0.f;
+          const typename AT::PP pp = AT::prep(ps);
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) O[u][dt] = AT::pv(vf, dt, pp, O[u][dt]);
+        }
+      };
+      if (nu > 0) {
+        typename AT::VF va, vb;
+        uint32_t w[NVR];
+        int rv[NVR];
+        path_read(w, pst, __builtin_amdgcn_readlane(ub, 0), xv, se, maxp);
+        path_rows(rv, w, xv, se, tbase, ncom, nws);
+        AT::load_vr(va, vst, rv, c16);
+        if (nu > 1) path_read(w, pst, __builtin_amdgcn_readlane(ub, 1), xv, se, maxp);
+        for (int k = 0; k < nu; k += 2) {
+          if (k + 1 < nu) {
+            path_rows(rv, w, xv, se, tbase, ncom, nws);
+            AT::load_vr(vb, vst, rv, c16);
+            if (k + 2 < nu) path_read(w, pst, __builtin_amdgcn_readlane(ub, k + 2), xv, se, maxp);
+          }
+          pv_branch(va, __builtin_amdgcn_readlane(ub, k));
+          if (k + 1 >= nu) break;
+          if (k + 2 < nu) {
+            path_rows(rv, w, xv, se, tbase, ncom, nws);
+            AT::load_vr(va, vst, rv, c16);
+            if (k + 3 < nu) path_read(w, pst, __builtin_amdgcn_readlane(ub, k + 3), xv, se, maxp);
+          }
+          pv_branch(vb, __builtin_amdgcn_readlane(ub, k + 1));
+        }
       }
     }
   };
-  for (int s0 = s_end - 1; s0 >= s_begin; s0 -= DEPTH)
-    static_for<0, DEPTH>([&](auto SI) {
-      if (decltype(SI)::value == 0 || s0 - decltype(SI)::value >= s_begin) step(SI, s0 - decltype(SI)::value);
-    });
 
-  wait_vm<0>();                                   // the dummy stages have landed: the ring is free
-  ring_barrier();
-
-  // fold: every class wave hands (m, l, O) over through LDS; class wave c
-  // then folds accumulator row c (head dimensions NDT*(4g + c) + dt, NDT
-  // contiguous values) of every tile of its pair slot, classes 0, 1, 2, 3 in
-  // order, and stores them
-  constexpr int FS = 64 * (2 + 4 * NDT);          // floats of one wave's state: (m, l) per lane, then O by row
-  auto xf = [&](int u, int c) __attribute__((always_inline)) {
-    return (float*)ring + (size_t)((pslot * TPW + u) * NCLS + c) * FS;
-  };
+  // The two kinds of workgroup run separate copies of the code, so that the
+  // compiler's waits for Q and the positions fall where each needs them.
+  if (has_tail) {
 #pragma unroll
-  for (int u = 0; u < TPW; ++u) {
-    if (!tv[u]) continue;
-    float* d = xf(u, cls);
-    *(float2*)(d + 2 * lane) = make_float2(M[u], L[u]);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float* dr = d + 128 + (r * 64 + lane) * NDT;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) dr[dt] = O[u][dt][r];
+    for (int u = 0; u < TPW; ++u) {
+      const int* meta = a.tile_meta + (size_t)(row[u] >> 4) * 64;
+      nbr[u] = meta[0];
+      bid[u] = meta[1 + (lane & 15)];
+      br[u] = a.branch[min(row[u], a.Q - 1)];
     }
+    // the stage: committed rows [32 tail0, shared_end), then every packed
+    // row's K/V (workspace rows), K rows then V rows, then the row builder's
+    // branch path table [nb][maxp]; it lands before the ring is issued
+    const char* kw = (const char*)a.kw + (size_t)g_kv * a.ws_cap * ROWB;
+    const char* vw = (const char*)a.vw + (size_t)g_kv * a.ws_cap * ROWB;
+    const int st_rows = a.st_rows;
+    const int nblk = (st_rows + RPB - 1) / RPB;
+    for (int ins = wave; ins < 2 * nblk; ins += NW) {
+      const int half = ins / nblk, blk = ins % nblk;
+      const int r = blk * RPB + lane / PIECES;
+      const char* src;
+      if (r < ncom) src = (half ? vc : kc) + (size_t)(CH * a.tail0 + r) * ROWB;
+      else if (r < st_rows) src = (half ? vw : kw) + (size_t)(r - ncom) * ROWB;
+      else src = (half ? vc : kc) + (size_t)(se - 1) * ROWB;
+      dma16(src + 16 * ((lane % PIECES) ^ (r % PIECES)), lds_addr(lds + half * a.st_half + blk * 1024));
+    }
+    const int npath = a.nb * a.maxp;
+    for (int ins = wave; ins * 64 < npath; ins += NW)
+      dma4(a.path + min(ins * 64 + lane, npath - 1), lds_addr(lds + 2 * a.st_half + ins * 256));
+    dma_wait<0>();                                // stage and this wave's loads landed
+    // the compiler does not count the DMA: tie the loaded values here, so
+    // that its own wait for them falls here and not after the ring's issue
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+#pragma unroll
+      for (int s = 0; s < (int)(sizeof(qf[u].p) / sizeof(qf[u].p[0])); ++s) asm volatile("" : "+v"(qf[u].p[s]));
+      asm volatile("" : "+v"(pos[u]), "+v"(nbr[u]), "+v"(bid[u]), "+v"(br[u]));
+      nbr[u] = tv[u] ? min(nbr[u], 16) : 0;
+      bid[u] = lane < 16 ? bid[u] : -1;
+    }
+    // the ring's first D - 1 chunks
+#pragma unroll
+    for (int i = 0; i < D - 1; ++i)
+      if (i < nring) issue(i);
+    tail_part();
+    ring_part();
+  } else {
+#pragma unroll
+    for (int i = 0; i < D - 1; ++i)
+      if (i < nring) issue(i);
+    ring_part();
   }
-  __syncthreads();
+  dma_wait<0>();                                   // no DMA may land after the workgroup has left
+
+  // results: lane (g, c) holds rows c, accumulator rows 4 g + r of every output tile
 #pragma unroll
   for (int u = 0; u < TPW; ++u) {
-    if (!tv[u] || !rvalid[u]) continue;
-    float Mf = NEG_INF, Lf = 0.f;
-    float Of[NDT];
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) Of[dt] = 0.f;
-#pragma unroll
-    for (int c = 0; c < NCLS; ++c) {
-      const float* d = xf(u, c);
-      const float2 ml = *(const float2*)(d + 2 * lane);
-      if (ml.x == NEG_INF) continue;
-      const float* dr = d + 128 + (cls * 64 + lane) * NDT;
-      const float mn = fmaxf(Mf, ml.x);
-      const float wa = ex2(Mf - mn), wb = ex2(ml.x - mn);
-      Lf = lin2(Lf, wa, ml.y, wb);
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) Of[dt] = lin2(Of[dt], wa, dr[dt], wb);
-      Mf = mn;
-    }
-    const int d0 = NDT * (4 * g + cls);             // first of the NDT contiguous head dimensions
+    if (!rvalid[u]) continue;
     if (a.nsplit > 1) {
-      // the split's state: (m, l) and O in natural dimension order
       const size_t base = ((size_t)sp * a.H + hh[u]) * a.Q + row[u];
-      if (g == 0 && cls == 0) *(float2*)(a.part_ml + base * 2) = make_float2(Mf, Lf);
-      float* po = a.part_o + base * DH + d0;
+      if (g == 0) *(float2*)(a.part_ml + base * 2) = make_float2(M[u], L[u]);
+      float* po = a.part_o + base * DH;
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) po[dt] = Of[dt];
+      for (int dt = 0; dt < NDT; ++dt) {
+        if constexpr (std::is_same<T, bf16_t>::value) {
+          *(float4*)(po + AT::dim(dt, 4 * g)) = make_float4(O[u][dt][0], O[u][dt][1], O[u][dt][2], O[u][dt][3]);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) po[AT::dim(dt, 4 * g + r)] = O[u][dt][r];
+        }
+      }
       continue;
     }
-    T* dst = (T*)a.o + ((size_t)row[u] * a.H + hh[u]) * DH + d0;
+    T* dst = (T*)a.o + ((size_t)row[u] * a.H + hh[u]) * DH;
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) st<T>(dst + dt, Of[dt] / Lf);
+    for (int dt = 0; dt < NDT; ++dt) {
+      if constexpr (std::is_same<T, bf16_t>::value) {
+        const uint32_t w0 = (uint32_t)f2bf(O[u][dt][0] / L[u]) | ((uint32_t)f2bf(O[u][dt][1] / L[u]) << 16);
+        const uint32_t w1 = (uint32_t)f2bf(O[u][dt][2] / L[u]) | ((uint32_t)f2bf(O[u][dt][3] / L[u]) << 16);
+        *(uint2*)(dst + AT::dim(dt, 4 * g)) = make_uint2(w0, w1);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dst[AT::dim(dt, 4 * g + r)] = O[u][dt][r] / L[u];
+      }
+    }
   }
 }
 
-// Fold of the key splits' states in split order (the same sequence of
-// roundings as the class fold), then O / l.  One thread per 4 head dimensions of
-// a (row, head).
+// Fold of the key splits' states in split order (m, l, O), then O / l.  One
+// thread per 4 head dimensions of a (row, head).
 template <typename T, int DH>
 __global__ void __launch_bounds__(256) la_attn_merge_kernel(LaAttnArgs a) {
   constexpr int V4 = DH / 4, MS = 8;            // splits whose loads are all issued before the fold
@@ -829,101 +834,99 @@ __global__ void __launch_bounds__(256) la_attn_merge_kernel(LaAttnArgs a) {
   }
 }
 
-// Ring stages (128 positions each) per key split: a function of the cache
-// capacity only, so every call on one cache cuts its keys the same way: one
-// stage per split up to 8 stages (short caches: more, shorter workgroups),
-// else about four splits when the cache is full.
-int la_attention_spb(int t_cap) {
-  const int stages = (std::max(t_cap, 1) + CH * NCLS - 1) / (CH * NCLS);
-  if (stages <= 8) return 1;
-  return std::max(1, (stages + 3) / 4);
+// Chunks per key split: a function of the cache capacity and the model's head
+// counts only (never of the rows of a call), so every call on one cache cuts
+// its keys the same way.  About `target` splits when the cache is full --
+// eight for plain multi-head attention, fewer when many query heads share a KV
+// head (their rows already give enough workgroups) -- and at least 4 chunks.
+static int spl_for(int t_cap, int H, int Hkv) {
+  const int nch = (std::max(t_cap, 1) + CH - 1) / CH;
+  const int target = std::max(1, std::min(8, 256 / std::max(1, H)));
+  return std::max(4, (nch + target - 1) / target);
 }
+int la_attention_spl(int t_cap, int H, int Hkv) { return spl_for(t_cap, H, Hkv); }
+// upper bound over head counts (the smallest split length is the one of 8 splits)
 int la_attention_parts(int max_pos, int t_cap) {
-  return max_pos < 0 ? 1 : max_pos / (CH * NCLS * la_attention_spb(t_cap)) + 1;
+  const int nch = (std::max(t_cap, 1) + CH - 1) / CH;
+  const int spl = std::max(4, (nch + 7) / 8);
+  return max_pos < 0 ? 1 : max_pos / (CH * spl) + 1;
 }
 
-// dynamic LDS of the kernel: the fixed part, then the largest of the ring,
-// the tail (branch paths of NT tiles, rows of TP tiles: trows each, K and V)
-// and the fold states
-template <typename T, int DH, int TP, int TPW>
-static size_t attn_lds(int trows) {
-  constexpr int ROWB = AttnT<T, DH>::ROWB, NDT = AttnT<T, DH>::NDT, NT = TP * TPW;
-  const size_t fix = ((size_t)NT * (16 * ROWB + 256) + 1023) & ~(size_t)1023;
-  const size_t ring = (size_t)2 * NCLS * 2 * CH * ROWB;
-  const size_t tail = (size_t)NT * (16 * 64 + 64) * 4 + (size_t)TP * 2 * trows * ROWB;
-  const size_t fold = (size_t)NT * NCLS * 64 * (4 * NDT + 2) * 4;
-  return fix + std::max(ring, std::max(tail, fold));
+// The tail stage holds the committed part of the first tail chunk (< 32
+// rows) and every packed row but the ordinary one, K and V, and the branch
+// path table, beside a ring of at least two chunk slots.
+int la_attention_fits(int dh, int esz, int q_max, int nb_max, int maxp_max) {
+  const size_t rowb = (size_t)dh * esz, ring2 = 2 * 2 * CH * rowb;
+  const size_t rows = (size_t)(CH - 1) + std::max(q_max - 1, 0);
+  const size_t half = (rows * rowb + 1023) / 1024 * 1024;
+  const size_t paths = ((size_t)nb_max * maxp_max * 4 + 1023) / 1024 * 1024;
+  return 2 * half + paths + ring2 <= LDS_BYTES;
 }
 
-template <typename T, int DH, int TP, int TPW>
+template <typename T, int DH, int NW, int TPW, int D>
 static void launch_cfg(const LaAttnArgs& a, int grid, size_t lds, hipStream_t st) {
-  static const bool attr = hipFuncSetAttribute((const void*)&la_attn_kernel<T, DH, TP, TPW>,
+  static const bool attr = hipFuncSetAttribute((const void*)&la_attn_kernel<T, DH, NW, TPW, D>,
                                                hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES) == hipSuccess;
   (void)attr;
-  hipLaunchKernelGGL((la_attn_kernel<T, DH, TP, TPW>), dim3(grid), dim3(64 * NCLS * TP), lds, st, a);
+  hipLaunchKernelGGL((la_attn_kernel<T, DH, NW, TPW, D>), dim3(grid), dim3(64 * NW), lds, st, a);
 }
 
-// compute units of the current device (cached per device)
-static int cu_count() {
-  static int cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] == 0) {
-    int n = 0;
-    cache[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0 ? n : 256;
-  }
-  return cache[dev];
+// ring depth: 6 chunk slots where the LDS holds them beside the tail stage
+// (bf16), else 4, else 2; a single wave issues a whole chunk's 16 loads, so it
+// keeps at most 4 slots (the vmcnt counter holds 63 loads)
+template <typename T, int DH, int NW, int TPW>
+static void launch_depth(const LaAttnArgs& a, int depth, int grid, size_t lds, hipStream_t st) {
+  constexpr bool deep = std::is_same<T, bf16_t>::value && NW > 1;
+  if (deep && depth == 6) launch_cfg<T, DH, NW, TPW, deep ? 6 : 4>(a, grid, lds, st);
+  else if (depth == 4) launch_cfg<T, DH, NW, TPW, 4>(a, grid, lds, st);
+  else launch_cfg<T, DH, NW, TPW, 2>(a, grid, lds, st);
 }
 
 template <typename T, int DH>
 static int launch_dh(LaAttnArgs a, hipStream_t st) {
+  constexpr int ROWB = AttnT<T, DH>::ROWB;
+  constexpr size_t SLOT = 2 * CH * ROWB;
   const int group = a.H / a.Hkv;
-  const int tiles = group * ((a.Q + 15) / 16);
-  // staged tail rows per tile (K and V): what the LDS left after the fixed
-  // part and the branch paths holds, at least the committed rows of a tail
-  // chunk (< 32) and the EP positions of one branch; at most those of 16
-  // branches
-  constexpr int ROWB = AttnT<T, DH>::ROWB, RPB = 1024 / ROWB;
-  const int EP = a.n_tail > 0 ? a.max_pos - a.shared_end + 1 : 0;
-  auto rows_for = [&](int tp, int nt) {
-    const size_t fix = (((size_t)nt * (16 * ROWB + 256)) + 1023) & ~(size_t)1023;
-    const size_t paths = (size_t)nt * (16 * 64 + 64) * 4;
-    const int fit = (int)((LDS_BYTES - fix - paths) / ((size_t)tp * 2 * ROWB)) / RPB * RPB;
-    const int want = ((CH - 1 + 16 * EP) + RPB - 1) / RPB * RPB;
-    return std::min(fit, want);
-  };
-  const int need_rows = ((CH - 1 + EP) + RPB - 1) / RPB * RPB;
-  // tiles per workgroup: 4 (two tile pairs) while that still gives about 160
-  // workgroups, else 2, or 1 for a single tile
+  const int tiles = group * ((a.Q + 15) / 16);    // 16-row tiles of one KV head
   const int kv = 8 * ((a.Hkv + 7) / 8);
-  auto wgs = [&](int nt) { return kv * ((tiles + nt - 1) / nt) * a.nsplit; };
-  int nt = tiles == 1 ? 1 : (tiles >= 3 && wgs(4) >= 160) ? 4 : 2;
-  // two tiles: two pair slots of one tile each (8 waves, two per SIMD)
-  const int tp = nt == 1 ? 1 : 2;
-  const int tpw = nt / tp;
-  if (a.n_tail > 0 && rows_for(tp, nt) < need_rows) return -2;
-  a.trows = a.n_tail > 0 ? rows_for(tp, nt) : 0;
+  // tiles per workgroup: the most (up to 8) that still leave about 200
+  // workgroups, one wave per tile (eight waves: two per SIMD, so one wave's
+  // vector ALU work overlaps the other's MFMAs and LDS waits)
+  struct Cfg { int nw, tpw; };
+  const Cfg cfgs[] = {{8, 1}, {4, 1}, {2, 1}, {1, 1}};
+  Cfg cfg = {1, 1};
+  for (const Cfg& c : cfgs) {
+    const int nt = c.nw * c.tpw;
+    if (nt > tiles && !(c.nw == 1)) continue;
+    const int wgs = kv * a.nsplit * ((tiles + nt - 1) / nt);
+    cfg = c;
+    if (wgs >= 200) break;
+  }
+  const int nt = cfg.nw * cfg.tpw;
   a.rgroups = (tiles + nt - 1) / nt;
-  // Two workgroups per row group in the tail's split, unless that adds a
-  // round of workgroups to the grid (one workgroup fits a CU at a time).
-  auto per_head = [&](bool half) {
-    int n = 0;
-    for (int s = 0; s < a.nsplit; ++s) n += a.rgroups * (half && split_has_tail(a, s) ? 2 : 1);
-    return n;
-  };
-  const int ncu = cu_count();
-  const int single = per_head(false), doubled = per_head(tpw == 2);
-  a.tail_half = tpw == 2 && (kv * doubled + ncu - 1) / ncu <= (kv * single + ncu - 1) / ncu;
-  a.wg_head = a.tail_half ? doubled : single;
+  a.wg_head = a.rgroups * a.nsplit;
+  // LDS: the tail stage (committed rows of the first tail chunk + every packed
+  // row, K and V, 1 KB aligned, then the path table) before the ring
+  size_t st_bytes = 0;
+  if (a.n_tail > 0) {
+    const int rows = (a.shared_end - CH * a.tail0) + a.n_ws;
+    const int rpb = 1024 / ROWB;
+    a.st_rows = rows;
+    a.st_half = ((rows + rpb - 1) / rpb) * 1024;
+    st_bytes = 2 * (size_t)a.st_half + ((size_t)a.nb * a.maxp * 4 + 1023) / 1024 * 1024;
+    a.st_bytes = (int)st_bytes;
+  }
+  const int dmax = std::is_same<T, bf16_t>::value && cfg.nw > 1 ? 6 : 4;
+  int depth = dmax;
+  while (depth > 2 && st_bytes + depth * SLOT > LDS_BYTES) depth -= 2;
+  if (st_bytes + depth * SLOT > LDS_BYTES) return -2;
+  a.ring_depth = depth;
+  const size_t lds = st_bytes + depth * SLOT;
   const int grid = kv * a.wg_head;
-  size_t lds;
-  if (nt == 4) lds = attn_lds<T, DH, 2, 2>(a.trows);
-  else if (nt == 2) lds = attn_lds<T, DH, 2, 1>(a.trows);
-  else lds = attn_lds<T, DH, 1, 1>(a.trows);
-  if (lds > LDS_BYTES) return -2;
-  if (nt == 4) launch_cfg<T, DH, 2, 2>(a, grid, lds, st);
-  else if (nt == 2) launch_cfg<T, DH, 2, 1>(a, grid, lds, st);
-  else launch_cfg<T, DH, 1, 1>(a, grid, lds, st);
+  if (cfg.nw == 8) launch_depth<T, DH, 8, 1>(a, depth, grid, lds, st);
+  else if (cfg.nw == 4) launch_depth<T, DH, 4, 1>(a, depth, grid, lds, st);
+  else if (cfg.nw == 2) launch_depth<T, DH, 2, 1>(a, depth, grid, lds, st);
+  else launch_depth<T, DH, 1, 1>(a, depth, grid, lds, st);
   if (a.nsplit > 1) {
     const int wpk = (a.Q * group * (DH / 4) + 255) / 256;
     hipLaunchKernelGGL((la_attn_merge_kernel<T, DH>), dim3(kv * wpk), dim3(256), 0, st, a);
@@ -938,16 +941,17 @@ int la_attention_launch(int dtype, const LaAttnArgs& a0, hipStream_t st) {
   if (a.n_ws < 0 || a.n_ws > a.ws_cap || a.maxp < 1) return -2;
   const int se = a.shared_end;
   const bool tail = a.max_pos >= se;
-  a.class_last = tail ? se / CH - 1 : a.max_pos / CH;
+  // ring chunks: every chunk below the first one that reaches past shared_end
+  // (or up to the largest row position when nothing does); tail chunks after it
   a.tail0 = se / CH;
-  a.n_tail = tail ? a.max_pos / CH - se / CH + 1 : 0;
-  // at most one tail chunk per class; tail positions come from a 64-entry path table per branch
-  if (a.n_tail > NTAIL || (tail && a.max_pos - se >= 64)) return -2;
+  a.ring_end = tail ? a.tail0 : a.max_pos / CH + 1;
+  a.n_tail = tail ? a.max_pos / CH - a.tail0 + 1 : 0;
+  // a branch reaches at most 64 positions past shared_end (the row builder's path table)
+  if (tail && a.max_pos - se >= 64) return -2;
   a.scale_log2 = a.scale * 1.4426950408889634f;
-  // key splits: the split of the last chunk any row reaches, plus one
-  const int last_chunk = tail ? a.tail0 + a.n_tail - 1 : a.class_last;
-  a.spb = la_attention_spb(a.T_cap);
-  a.nsplit = last_chunk / (NCLS * a.spb) + 1;
+  a.spl = spl_for(a.T_cap, a.H, a.Hkv);
+  const int last_chunk = a.max_pos / CH;
+  a.nsplit = last_chunk / a.spl + 1;
   if (a.nsplit > 1 && (a.part_o == nullptr || a.part_ml == nullptr || a.nsplit > a.max_splits)) return -2;
   int rc;
   if (dtype == LA_DT_BF16) {

@@ -96,19 +96,22 @@ struct LaAttnArgs {
   int n_ws;             // workspace rows written by this call (packed rows other than the ordinary row)
   float scale;          // softmax scale (1/sqrt(dh))
   // set by the launcher
-  int class_last;       // last chunk taken by the class workgroups (-1: none)
   int tail0, n_tail;    // first chunk and number of chunks reaching past shared_end
+  int ring_end;         // chunks below it are read from the cache through the ring
+  int spl;              // chunks per key split (la_attention_spl)
+  int nsplit;           // key splits
   int rgroups;          // row groups per KV head
   int wg_head;          // workgroups per KV head (all splits)
-  int tail_half;        // a split holding tail chunks gets two workgroups per row group (one tile per pair slot)
-  int trows;            // staged tail rows per tile
-  int spb;              // ring stages (128 positions) per key split (la_attention_spb(T_cap))
-  int nsplit;           // key splits
+  int ring_depth;       // ring slots of one chunk each
+  int st_rows, st_half, st_bytes;  // tail stage: rows (committed part of the first tail chunk + packed rows),
+                                   // bytes of its K (and of its V) part, bytes with the path table
   float scale_log2;     // scale * log2(e)
 };
 int la_attention_launch(int dtype, const LaAttnArgs& a, hipStream_t st);
-int la_attention_spb(int t_cap);                 // stages per key split on a cache of t_cap rows
-int la_attention_parts(int max_pos, int t_cap);   // key splits of a call whose rows reach max_pos
+int la_attention_spl(int t_cap, int H, int Hkv); // chunks of 32 positions per key split
+int la_attention_parts(int max_pos, int t_cap);   // upper bound on the key splits of a call reaching max_pos
+// whether a round of q_max rows (nb_max branches reaching maxp_max positions) fits the tail stage's LDS
+int la_attention_fits(int dh, int esz, int q_max, int nb_max, int maxp_max);
 
 // model pieces
 void la_embed_launch(int dtype, const void* E, const int32_t* tok, void* x, int M, int d, hipStream_t st);

@@ -363,10 +363,11 @@ int la_build_rows(const la_rows_desc* desc, const int32_t* window, const int32_t
  * la_attention_workspace(Q, H, dh, max_pos, t_cap) bytes, max_pos =
  * shared_end - 1 + info->maxp (the largest position a row reaches): one
  * softmax state per row, head and key split.  A key split is a fixed run of
- * positions whose length depends on t_cap only (128 positions while t_cap
- * <= 1024, else about a quarter of t_cap rounded up to 128 positions).  Batch invariant: a row's result does not
- * depend on the other rows of the call (its reduction tree is a function of
- * key positions and t_cap only).  The call only launches (on stream).
+ * chunks of 32 positions whose length depends on t_cap and the head counts
+ * only: max(4, ceil(chunks(t_cap) / min(8, 256 / H))) chunks.  Batch
+ * invariant: a row's result does not depend on the other rows of the call
+ * (its reduction tree is a function of key positions, t_cap and the head
+ * counts only).  The call only launches (on stream).
  * Errors: LA_EINVAL for a NULL pointer, an unknown dtype, H not a multiple
  * of Hkv, shared_end outside [1, t_cap], ws_cap < Q - 1, or a shape the
  * kernel does not take (dh other than 64/128 in bf16 or 16/64 in fp32, a

@@ -209,13 +209,14 @@ def test_attention_matches_oracle(case):
     assert err <= tol
 
 
-@pytest.mark.parametrize("p,t_cap", [(765, 1000), (1150, 1166), (2300, 3000)])
+@pytest.mark.parametrize("p,t_cap", [(765, 1000), (1115, 1166), (2300, 3000)])
 def test_attention_batch_invariance(p, t_cap):
     """A packed row's output equals, bit for bit, the same row computed alone
     with its branch ancestors committed to a cache of the same capacity (an
     autoregressive call).  Every case puts the round's rows across a key-split
-    boundary (768 at capacity 1000, whose splits are 128 positions; 384 at
-    capacity 1166; 768 at 3000)."""
+    boundary (8 query heads: splits of max(4, ceil(ceil(t_cap / 32) / 8))
+    chunks of 32 positions -- 768 at capacity 1000, 1120 at 1166, 2304 at
+    3000)."""
     sizes, starts = [6, 7, 7, 7], [1, 0, 0, 0]
     cands = [tuple(range(i, i + 4)) for i in range(7)]
     H, Hkv, dh = 8, 2, 128

@@ -117,23 +117,29 @@ def test_rows_query_matches_oracle(sizes, starts, C, S):
 @pytest.mark.parametrize("W,N,G,why", [
     (40, 8, 5, "rows"),        # (W + G) * (N - 1) = 315 packed rows: above one GEMM launch's 256
     (60, 10, 5, "rows"),       # 585 rows
-    (62, 3, 64, "rows"),       # 252 lookahead + 126 verification rows
+    (62, 3, 64, "stage"),      # 252 rows: under 256, but beyond the tail stage
     (64, 4, 0, "reach"),       # 192 rows, but the first warmup fill's last column reaches 65 positions
     (63, 4, 0, None),          # 189 rows, 64 positions: admitted
     (15, 7, 15, None),         # the 34B-shaped workload: 180 rows
+    (36, 6, 5, None),          # 205 rows: the attention's tail stage still holds them at head dim 128
+    (30, 8, 0, None),          # 210 rows
+    (38, 6, 5, "stage"),       # 215 rows: it does not
+    (20, 7, 20, "stage"),      # 240 rows
 ])
 def test_round_shapes_admitted_before_state(W, N, G, why):
     """A config whose largest round exceeds what the round's kernels take is
     refused by la_query_sizes (and la_init) with LA_EINVAL, before any state
     exists ("M7.3", 0x01A admission), instead of failing at its first warm
-    round: more than 256 packed rows (one GEMM launch), or a branch reaching
+    round: more than 256 packed rows (one GEMM launch), a branch reaching
     more than 64 positions past the committed prefix (the attention's path
-    table)."""
+    table), or more rows than the attention's tail stage holds in LDS (the
+    committed part of the first tail chunk, every packed row's K and V and
+    the branch path table beside two ring slots: about 210 rows at head dim
+    128 in bf16)."""
     d = la.dims_struct(synthetic.PRESETS["llama7b"])
     cfg = la.make_config(W, N, G, 64, 100)
     rows = (W + G) * (N - 1)
-    reach = W + N - 3           # the farthest row (last column of level 0 at the first warmup round) past the ordinary row
-    if rows <= 256 and reach <= 64:
+    if why is None:
         s = la.la_query_sizes(cfg, d)
         assert s.q_max == rows
         return
@@ -141,7 +147,8 @@ def test_round_shapes_admitted_before_state(W, N, G, why):
         la.la_query_sizes(cfg, d)
     assert e.value.code == la.LA_EINVAL
     msg = str(e.value)
-    assert ("packed rows" in msg) if rows > 256 else ("positions past" in msg), msg
+    want = {"rows": "at most 256", "reach": "positions past", "stage": "tail stage"}[why]
+    assert want in msg, msg
 
 
 def test_d_model_bound_admitted():
