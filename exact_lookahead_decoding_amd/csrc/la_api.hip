@@ -177,12 +177,13 @@ static PackedOffsets packed_offsets(const la_model_dims& d) {
   const int qkvdim = (d.n_heads + 2 * d.n_kv_heads) * d.head_dim;
   PackedOffsets p{};
   p.qkv = 0;
-  p.o = la_gemm_packed_elems(qkvdim, d.d_model, 0);
-  p.gu = p.o + la_gemm_packed_elems(d.d_model, d.n_heads * d.head_dim, 0);
-  p.dn = p.gu + la_gemm_packed_elems(d.d_ff, d.d_model, 1);
-  p.layer = p.dn + la_gemm_packed_elems(d.d_model, d.d_ff, 0);
+  const int dt = d.dtype == LA_DTYPE_BF16 ? LA_DT_BF16 : LA_DT_F32;
+  p.o = la_gemm_packed_elems(dt, qkvdim, d.d_model, 0);
+  p.gu = p.o + la_gemm_packed_elems(dt, d.d_model, d.n_heads * d.head_dim, 0);
+  p.dn = p.gu + la_gemm_packed_elems(dt, d.d_ff, d.d_model, 1);
+  p.layer = p.dn + la_gemm_packed_elems(dt, d.d_model, d.d_ff, 0);
   p.lm = p.layer * d.n_layers;
-  p.total = p.lm + la_gemm_packed_elems(d.vocab, d.d_model, 0);
+  p.total = p.lm + la_gemm_packed_elems(dt, d.vocab, d.d_model, 0);
   return p;
 }
 
@@ -333,11 +334,12 @@ static const char* wptr(const void* base, size_t elems_per_layer, int l, int esz
   return (const char*)base + (size_t)l * elems_per_layer * esz;
 }
 
-// The QKV projection writes q, k and v (rotated, placed) from its epilogue
-// when its K is not split; its weights are then packed pair-major.  A
-// function of the shape only, shared by the packer and the forward.
+// The fp32 QKV projection writes q, k and v (rotated, placed) from its
+// epilogue when its K is not split; its weights are then packed pair-major.
+// A function of the shape only, shared by the packer and the forward.  bf16
+// stores the projection and rotates / places it with la_qkv_post_launch.
 static bool qkv_fused(int qkvdim, int d, int dt, int dh) {
-  return la_gemm_splits(qkvdim, d, dt, 0) == 1 && dh >= 16 && (dh & (dh - 1)) == 0;
+  return dt == LA_DT_F32 && la_gemm_splits(qkvdim, d, dt, 0) == 1 && dh >= 16 && (dh & (dh - 1)) == 0;
 }
 
 static int gemm(la_ctx* c, int epi, const void* X, const void* W, void* Y, const void* Rr, int M, int N, int K,
@@ -405,12 +407,18 @@ static int forward(la_ctx* c, int M, const int32_t* tok, const int32_t* pos, con
     char* vw = (char*)c->vw + l * wsl * esz;
     int rc;
     const size_t pstride = (size_t)M * c->d;
-    la_addnorm_launch(c->dtype, c->x, c->gemm_p, pend, pstride, 1, attn_norm, c->nrm, nullptr, M, c->d, c->dims.eps,
-                      c->st);
+    if (la_addnorm_launch(c->dtype, c->x, c->gemm_p, pend, pstride, 1, attn_norm, c->nrm, nullptr, M, c->d,
+                          c->dims.eps, c->st))
+      return fail(c, LA_EINVAL, "residual fold of %d split partials exceeds %d", pend, LA_ADDNORM_MAX_SPLITS);
     if (qkv_fused(c->qkvdim, c->d, c->dtype, c->dh)) {
       const LaQkvOut qo{c->rope, pos, c->q, kc, vc, kw, vw, c->H, c->Hkv, c->dh, c->t_cap, cache_row0, n_direct,
                         c->ws_cap};
       if ((rc = gemm(c, LA_EPI_QKV, c->nrm, wqkv, c->qkv, nullptr, M, c->qkvdim, c->d, 0, false, &qo))) return rc;
+    } else if (const int qs = la_gemm_splits(c->qkvdim, c->d, c->dtype, 0); qs > 1) {
+      // split K: the partials go straight to the rotate-and-place pass (one fixed-order sum per value)
+      if ((rc = gemm(c, LA_EPI_STORE, c->nrm, wqkv, c->qkv, nullptr, M, c->qkvdim, c->d, 0, true))) return rc;
+      la_qkv_reduce_post_launch(c->dtype, c->gemm_p, qs, M, c->rope, pos, c->H, c->Hkv, c->dh, c->q, kc, vc,
+                                c->t_cap, cache_row0, n_direct, kw, vw, c->ws_cap, c->st);
     } else {
       if ((rc = gemm(c, LA_EPI_STORE, c->nrm, wqkv, c->qkv, nullptr, M, c->qkvdim, c->d, 0))) return rc;
       la_qkv_post_launch(c->dtype, c->qkv, c->rope, pos, M, c->H, c->Hkv, c->dh, c->q, kc, vc, c->t_cap, cache_row0,
@@ -428,14 +436,16 @@ static int forward(la_ctx* c, int M, const int32_t* tok, const int32_t* pos, con
     prof_mark(c, false, 1, 0, 0);
     if (rc) return fail(c, LA_EDEVICE, "attention launch failed (%d)", rc);
     if ((rc = resid_gemm(c, c->o, wo, M, c->H * c->dh, &pend))) return rc;
-    la_addnorm_launch(c->dtype, c->x, c->gemm_p, pend, pstride, 1, mlp_norm, c->nrm, nullptr, M, c->d, c->dims.eps,
-                      c->st);
+    if (la_addnorm_launch(c->dtype, c->x, c->gemm_p, pend, pstride, 1, mlp_norm, c->nrm, nullptr, M, c->d,
+                          c->dims.eps, c->st))
+      return fail(c, LA_EINVAL, "residual fold of %d split partials exceeds %d", pend, LA_ADDNORM_MAX_SPLITS);
     if ((rc = gemm(c, LA_EPI_SWIGLU, c->nrm, wgu, c->act, nullptr, M, c->F, c->d, c->F))) return rc;
     if ((rc = resid_gemm(c, c->act, wdn, M, c->F, &pend))) return rc;
   }
   if (n_logit > 0) {
-    la_addnorm_launch(c->dtype, c->x, c->gemm_p, pend, (size_t)M * c->d, 0, c->w.final_norm, c->fin, logit_rows,
-                      n_logit, c->d, c->dims.eps, c->st);
+    if (la_addnorm_launch(c->dtype, c->x, c->gemm_p, pend, (size_t)M * c->d, 0, c->w.final_norm, c->fin, logit_rows,
+                      n_logit, c->d, c->dims.eps, c->st))
+      return fail(c, LA_EINVAL, "residual fold of %d split partials exceeds %d", pend, LA_ADDNORM_MAX_SPLITS);
     int rc = gemm(c, LA_EPI_F32, c->fin, (const char*)c->w.packed + c->pk.lm * esz, c->logits, nullptr, n_logit, c->V,
                   c->d, 0);
     if (rc) return rc;
@@ -1030,7 +1040,8 @@ static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 extern "C" size_t la_packed_linear_bytes(int32_t dtype, int32_t epilogue, int32_t N, int32_t K) {
   if (N <= 0 || K <= 0) return 0;
-  return la_gemm_packed_elems(N, K, epilogue == LA_LINEAR_SWIGLU) * (dtype == LA_DTYPE_BF16 ? 2 : 4);
+  return la_gemm_packed_elems(dtype == LA_DTYPE_BF16 ? LA_DT_BF16 : LA_DT_F32, N, K, epilogue == LA_LINEAR_SWIGLU) *
+         (dtype == LA_DTYPE_BF16 ? 2 : 4);
 }
 
 extern "C" size_t la_linear_workspace(int32_t dtype, int32_t epilogue, int32_t M, int32_t N, int32_t K) {

@@ -308,20 +308,296 @@ __global__ void __launch_bounds__(256) la_gemm_kernel(LaGemmArgs a) {
   }
 }
 
-// Fixed-order reduction of split partials, then the epilogue.
+// Fixed-order reduction of split partials (split 0 first), then the
+// epilogue; a thread takes four adjacent columns (N is a multiple of 16).
 template <typename T, int EPI>
 __global__ void __launch_bounds__(256) la_gemm_reduce_kernel(LaGemmArgs a) {
   const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
-  const size_t total = (size_t)a.M * a.N;
-  if (idx >= total) return;
-  const int m = (int)(idx / a.N), n = (int)(idx % a.N);
-  float s0 = 0.f, s1 = 0.f;
+  const int n4 = a.N / 4;
+  if (idx >= (size_t)a.M * n4) return;
+  const int m = (int)(idx / n4), n = 4 * (int)(idx % n4);
+  float4 s0 = make_float4(0.f, 0.f, 0.f, 0.f), s1 = s0;
   for (int s = 0; s < a.splits; ++s) {
     const float* P = a.P + ((size_t)s * a.M + m) * a.pcols;
-    s0 += P[n];
-    if (EPI == LA_EPI_SWIGLU) s1 += P[a.up_off + n];
+    const float4 v = *(const float4*)(P + n);
+    s0.x += v.x; s0.y += v.y; s0.z += v.z; s0.w += v.w;
+    if (EPI == LA_EPI_SWIGLU) {
+      const float4 u = *(const float4*)(P + a.up_off + n);
+      s1.x += u.x; s1.y += u.y; s1.z += u.z; s1.w += u.w;
+    }
   }
-  gemm_store<T, EPI>(a, m, n, s0, s1);
+  gemm_store<T, EPI>(a, m, n, s0.x, s1.x);
+  gemm_store<T, EPI>(a, m, n + 1, s0.y, s1.y);
+  gemm_store<T, EPI>(a, m, n + 2, s0.z, s1.z);
+  gemm_store<T, EPI>(a, m, n + 3, s0.w, s1.w);
+}
+
+// ---------------------------------------------------------------------------
+// bf16: 32x32x16 MFMA kernel.
+//
+// A wave owns CW = 2 column tiles of 32 (SwiGLU: the gate and the up tile of
+// the same 32 output columns) over every row tile of 32, so a workgroup of
+// four waves covers 256 columns (SwiGLU: 128 outputs).  Per k16 block a wave
+// reads RT X fragments (shared by the four waves) and its 2 W fragments from
+// LDS for 2 RT MFMAs of 32 cycles: 64 bytes of LDS reads per clock and CU at
+// full MFMA rate, where 16x16x32 tiles would need four times as much.
+//   * W packed (la_gemm_pack_launch): fragment (column tile ct, k16 block
+//     kb) is 1 KB, lane l's 16 bytes = W[32 ct + l % 32][16 kb + 8 (l / 32)
+//     .. +7], ordered [ct][kb] (SwiGLU: [pair][kb][gate, up]); the B operand
+//     layout of the MFMA;
+//   * X and W reach LDS by global_load_lds DMA (issued as inline asm, so
+//     the compiler places only LDS waits on the reads; the ring waits for
+//     its own stages with exact vmcnt counts), a ring of NS stages of SK k16
+//     blocks; X rows are stored row-major per 32-row tile with their 16-byte
+//     pieces XOR-swizzled by row, so the A-operand reads (one row per lane)
+//     are conflict-free and the DMA reads each row's run contiguously;
+//   * the K partition: units of 64 (four k16 blocks), a split count that is a
+//     function of (N, K) only; inside a split the k16 blocks are taken in
+//     order, so an output element gets the same bits whatever M and row tile.
+// D of a 32x32 tile: lane l, value v holds row 8 (v / 4) + 4 (l / 32) + v % 4,
+// column l % 32.
+
+__device__ __forceinline__ f32x16 mfma_bf16_32x32(v4u a, v4u b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                 0, 0);
+}
+
+template <typename V> __device__ __forceinline__ V g2_lds(uint32_t addr) {
+  return *(const __attribute__((address_space(3))) V*)addr;
+}
+// uniform base + per-lane offset as one VALU add the compiler keeps as written
+__device__ __forceinline__ uint32_t g2_add(uint32_t sbase, uint32_t voff) {
+  uint32_t r;
+  sbase = __builtin_amdgcn_readfirstlane(sbase);
+  asm("v_add_u32 %0, %1, %2" : "=v"(r) : "s"(sbase), "v"(voff));
+  return r;
+}
+// lane l's 16 bytes of src land at LDS offset lds_off + 16 l; m0 is restored
+__device__ __forceinline__ void g2_dma(const void* src, uint32_t lds_off) {
+  uint32_t keep;
+  lds_off = __builtin_amdgcn_readfirstlane(lds_off);
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(keep) : "v"(src), "s"(lds_off) : "memory");
+}
+// the same, non-temporal: the weight stream is read once and so does not
+// displace the activation rows every workgroup re-reads from L2
+__device__ __forceinline__ void g2_dma_nt(const void* src, uint32_t lds_off) {
+  uint32_t keep;
+  lds_off = __builtin_amdgcn_readfirstlane(lds_off);
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt\n\ts_mov_b32 m0, %0"
+               : "=&s"(keep) : "v"(src), "s"(lds_off) : "memory");
+}
+template <int N> __device__ __forceinline__ void g2_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// at most k (< KMAX) of the wave's stages (PW loads each) still in flight
+template <int PW, int KMAX, int K = 0> __device__ __forceinline__ void g2_ring_wait(int k) {
+  if constexpr (K + 1 >= KMAX) {
+    g2_wait<K * PW>();
+  } else {
+    if (k <= K) g2_wait<K * PW>();
+    else g2_ring_wait<PW, KMAX, K + 1>(k);
+  }
+}
+
+constexpr int G2_CW = 2;
+constexpr int g2_sk(int rt) { return rt <= 4 ? 4 : 2; }                      // k16 blocks per stage
+constexpr int g2_stage(int rt) { return (rt + 4 * G2_CW) * g2_sk(rt) * 1024; }
+constexpr int g2_slots(int rt) { return LDS_BYTES / g2_stage(rt) < 6 ? LDS_BYTES / g2_stage(rt) : 6; }
+
+template <int RT, int EPI>
+__global__ void __launch_bounds__(256) la_gemm2_kernel(LaGemmArgs a) {
+  constexpr int CW = G2_CW, SK = g2_sk(RT), NS = g2_slots(RT);
+  constexpr int XB = RT * SK * 1024;              // X bytes of a stage (row tile rt at rt * SK KB)
+  constexpr int STAGE = g2_stage(RT);
+  constexpr int XI = RT * SK / 4;                 // X DMA instructions per wave and stage
+  constexpr int G = CW * SK + XI;                 // DMA instructions per wave and stage
+  constexpr int ROWB = SK * 32;                   // bytes of an X row in a stage
+  constexpr int PP = ROWB / 16;                   // its 16-byte pieces
+  constexpr int RPW = 256 / ROWB;                 // rows per 256-byte bank window
+  constexpr int RPI = 1024 / ROWB;                // rows per 1 KB DMA instruction
+  static_assert((RT * SK) % 4 == 0 && NS >= 3 && (NS - 1) * G < 64, "ring shape");
+  extern __shared__ __attribute__((aligned(1024))) char lds[];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool sw = (EPI == LA_EPI_SWIGLU) || (a.swiglu_partial != 0);
+  const int split = blockIdx.y;
+  const int nu = a.K / 64;                        // K units of four k16 blocks
+  const int u0 = (int)((long)split * nu / a.splits), u1 = (int)((long)(split + 1) * nu / a.splits);
+  const int n = (u1 - u0) * (4 / SK);             // ring stages of the split
+  const int kb0 = u0 * 4;                         // first k16 block of the split
+  const int nkb = a.K / 16;
+  const int tw = blockIdx.x * 4 + wave;           // the wave's tile pair
+  const char* W = (const char*)a.W;
+  const bf16_t* X = (const bf16_t*)a.X;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
+
+  // the wave's W fragment (t, k16 block kb) in the packed order; tiles past
+  // the last (a ragged N) read the last tile and store nothing
+  const int ntile = (a.N + 31) / 32;
+  auto wfrag = [&](int t, int kb) -> const char* {
+    const size_t f = sw ? ((size_t)min(tw, ntile - 1) * nkb + kb) * 2 + t
+                        : (size_t)min(2 * tw + t, ntile - 1) * nkb + kb;
+    return W + f * 1024 + 16 * lane;
+  };
+  // the lane's X source row and piece per X instruction of a stage (row tile rt = q / SK, part ii = q % SK)
+  const bf16_t* xsrc[XI];
+  uint32_t xdst[XI];
+#pragma unroll
+  for (int x = 0; x < XI; ++x) {
+    const int q = wave * XI + x, rt = q / SK, ii = q % SK;
+    const int r = ii * RPI + lane / PP;           // row inside the 32-row tile
+    const int p = lane % PP, lq = p ^ ((r / RPW) % PP);
+    const int m = min(rt * 32 + r, a.M - 1);      // rows past M repeat row M - 1 (never stored)
+    xsrc[x] = X + (size_t)m * a.ldx + 8 * lq;
+    xdst[x] = (uint32_t)(rt * SK + ii) * 1024;
+  }
+  auto issue = [&](int i) __attribute__((always_inline)) {
+    const uint32_t slot = lds0 + (uint32_t)(i % NS) * STAGE;
+    const int kb = kb0 + i * SK;
+#pragma unroll
+    for (int t = 0; t < CW; ++t)
+#pragma unroll
+      for (int j = 0; j < SK; ++j) g2_dma_nt(wfrag(t, kb + j), slot + XB + ((wave * CW + t) * SK + j) * 1024);
+#pragma unroll
+    for (int x = 0; x < XI; ++x) g2_dma(xsrc[x] + (size_t)kb * 16, slot + xdst[x]);
+  };
+
+  // LDS offsets of the lane's fragments: A (X row l % 32, piece 2 j + l / 32 swizzled), B (16 l)
+  uint32_t xo[SK];
+  {
+    const int r = lane % 32, sel = lane / 32, gsw = (r / RPW) % PP;
+#pragma unroll
+    for (int j = 0; j < SK; ++j) xo[j] = r * ROWB + 16 * ((2 * j + sel) ^ gsw);
+  }
+  const uint32_t wo = 16 * lane;
+
+  f32x16 acc[RT][CW];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int t = 0; t < CW; ++t)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[rt][t][v] = 0.f;
+
+#pragma unroll
+  for (int i = 0; i < NS - 1; ++i)
+    if (i < n) issue(i);
+  for (int i = 0; i < n; ++i) {
+    g2_ring_wait<G, NS - 1>(min(NS - 2, n - 1 - i));   // stage i landed (later ones may be in flight)
+    ring_barrier();                                  // ... for every wave; stage i - 1's slot is free
+    if (i + NS - 1 < n) issue(i + NS - 1);
+    const uint32_t slot = lds0 + (uint32_t)(i % NS) * STAGE;
+    const uint32_t wb = slot + XB + (uint32_t)wave * CW * SK * 1024;
+#pragma unroll
+    for (int j = 0; j < SK; ++j) {
+      const uint32_t xa = g2_add(slot, xo[j]), wa = g2_add(wb, wo);
+      v4u A[RT], B[CW];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) A[rt] = g2_lds<v4u>(xa + rt * SK * 1024);
+#pragma unroll
+      for (int t = 0; t < CW; ++t) B[t] = g2_lds<v4u>(wa + (t * SK + j) * 1024);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int t = 0; t < CW; ++t) acc[rt][t] = mfma_bf16_32x32(A[rt], B[t], acc[rt][t]);
+    }
+  }
+  g2_wait<0>();   // no DMA may land after the workgroup has left
+
+  const int c32 = lane % 32, rq = 4 * (lane / 32);
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int m = rt * 32 + 8 * (v / 4) + rq + (v % 4);
+      if (m >= a.M) continue;
+      if (sw) {
+        const int col = tw * 32 + c32;
+        if (col >= a.N) continue;
+        if (EPI == LA_EPI_PARTIAL) {
+          float* P = a.P + ((size_t)split * a.M + m) * a.pcols;
+          P[col] = acc[rt][0][v];
+          P[a.up_off + col] = acc[rt][1][v];
+        } else {
+          gemm_store<bf16_t, EPI>(a, m, col, acc[rt][0][v], acc[rt][1][v]);
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < CW; ++t) {
+          const int col = (2 * tw + t) * 32 + c32;
+          if (col >= a.N) continue;
+          if (EPI == LA_EPI_PARTIAL) a.P[((size_t)split * a.M + m) * a.pcols + col] = acc[rt][t][v];
+          else gemm_store<bf16_t, EPI>(a, m, col, acc[rt][t][v], 0.f);
+        }
+      }
+    }
+}
+
+// Packed bf16 W for la_gemm2_kernel: thread idx writes lane idx % 64 of fragment idx / 64.
+__global__ void __launch_bounds__(256) la_gemm2_pack_kernel(const bf16_t* W, bf16_t* P, int N, int K, int up_off,
+                                                            int swiglu, size_t pieces) {
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= pieces) return;
+  const int lane = (int)(idx & 63);
+  const size_t f = idx >> 6;
+  const size_t nkb = (size_t)(K / 16);
+  int t = 0;
+  size_t rest = f;
+  if (swiglu) {
+    t = (int)(f & 1);
+    rest = f >> 1;
+  }
+  const int ct = (int)(rest / nkb), kb = (int)(rest % nkb);
+  const int col = ct * 32 + lane % 32;
+  u32x4 v = {0, 0, 0, 0};
+  if (col < N) {
+    const int row = (swiglu && t ? up_off : 0) + col;
+    v = *(const u32x4*)(W + (size_t)row * K + (size_t)kb * 16 + 8 * (lane / 32));
+  }
+  *(u32x4*)(P + idx * 8) = v;
+}
+
+template <int RT, int EPI>
+static void launch_g2(const LaGemmArgs& a, dim3 grid, hipStream_t st) {
+  constexpr int lds = g2_slots(RT) * g2_stage(RT);
+  static_assert(lds <= LDS_BYTES, "LDS");
+  auto kern = la_gemm2_kernel<RT, EPI>;
+  static bool attr = false;   // idempotent, so a race between threads only repeats it
+  if (!attr) {
+    hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    attr = true;
+  }
+  hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, a);
+}
+
+template <int EPI>
+static void launch_g2_rt(const LaGemmArgs& a, dim3 grid, hipStream_t st) {
+  const int rt = (a.M + 31) / 32;
+  if (rt <= 1) launch_g2<1, EPI>(a, grid, st);
+  else if (rt <= 2) launch_g2<2, EPI>(a, grid, st);
+  else if (rt <= 3) launch_g2<3, EPI>(a, grid, st);
+  else if (rt <= 4) launch_g2<4, EPI>(a, grid, st);
+  else if (rt <= 6) launch_g2<6, EPI>(a, grid, st);
+  else launch_g2<8, EPI>(a, grid, st);
+}
+
+template <int EPI>
+static int launch_g2_t(LaGemmArgs a, hipStream_t st) {
+  const bool swiglu = EPI == LA_EPI_SWIGLU;
+  a.swiglu_partial = swiglu ? 1 : 0;
+  const int per = swiglu ? 4 * 32 : 4 * 32 * G2_CW;   // output columns per workgroup
+  dim3 grid((a.N + per - 1) / per, a.splits);
+  if (a.splits > 1) launch_g2_rt<LA_EPI_PARTIAL>(a, grid, st);
+  else launch_g2_rt<EPI>(a, grid, st);
+  if (a.splits > 1 && !a.defer_reduce) {
+    const size_t total = (size_t)a.M * (a.N / 4);
+    hipLaunchKernelGGL((la_gemm_reduce_kernel<bf16_t, EPI>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
+                       a);
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 // ---------------------------------------------------------------------------
@@ -336,7 +612,8 @@ static size_t pack_blocks(int N, int swiglu) {
   return (size_t)((N / 16 + per - 1) / per);
 }
 
-size_t la_gemm_packed_elems(int N, int K, int swiglu) {
+size_t la_gemm_packed_elems(int dtype, int N, int K, int swiglu) {
+  if (dtype == LA_DT_BF16) return (size_t)((N + 31) / 32) * (swiglu ? 2 : 1) * 32 * (size_t)K;
   return pack_blocks(N, swiglu) * 4 * la_gemm_ntw(N, swiglu) * 16 * (size_t)K;
 }
 
@@ -379,21 +656,30 @@ int la_gemm_pack_launch(int dtype, const void* W, void* P, int N, int K, int swi
   if (N % 16 != 0 || K % kc != 0 || N <= 0) return -2;
   if (rope_dh > 0 && (swiglu || rope_dh % 16 != 0 || N % rope_dh != 0)) return -2;
   const int ntw = la_gemm_ntw(N, swiglu);
-  const size_t pieces = la_gemm_packed_elems(N, K, swiglu) / (dtype == LA_DT_BF16 ? 8 : 4);
+  const size_t pieces = la_gemm_packed_elems(dtype, N, K, swiglu) / (dtype == LA_DT_BF16 ? 8 : 4);
   const unsigned grid = (unsigned)((pieces + 255) / 256);
-  if (dtype == LA_DT_BF16)
-    hipLaunchKernelGGL(la_gemm_pack_kernel<bf16_t>, dim3(grid), dim3(256), 0, st, (const bf16_t*)W, (bf16_t*)P, N, K,
-                       N, ntw, swiglu, rope_dh, pieces);
-  else
+  if (dtype == LA_DT_BF16) {
+    if (rope_dh > 0) return -2;                  // the pair-major QKV layout is fp32-only
+    hipLaunchKernelGGL(la_gemm2_pack_kernel, dim3(grid), dim3(256), 0, st, (const bf16_t*)W, (bf16_t*)P, N, K, N,
+                       swiglu, pieces);
+  } else
     hipLaunchKernelGGL(la_gemm_pack_kernel<float>, dim3(grid), dim3(256), 0, st, (const float*)W, (float*)P, N, K, N,
                        ntw, swiglu, rope_dh, pieces);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 int la_gemm_splits(int N, int K, int dtype, int swiglu) {
-  // a function of the weight shape only (never of M): split K only when there
-  // are too few column tiles to give every CU a workgroup, up to 4 ways
-  const int kc = dtype == LA_DT_BF16 ? GT<bf16_t>::KC : GT<float>::KC;
+  // a function of the weight shape only (never of M)
+  if (dtype == LA_DT_BF16) {
+    // bf16: as many K splits (units of 64, at most 8) as keep the workgroups
+    // within one per CU of the 256
+    const int groups = (N + (swiglu ? 128 : 256) - 1) / (swiglu ? 128 : 256);
+    const int units = K / 64;
+    return std::max(1, std::min(std::min(8, units), 256 / std::max(groups, 1)));
+  }
+  // fp32: split K only when there are too few column tiles to give every CU
+  // a workgroup, up to 4 ways
+  const int kc = GT<float>::KC;
   const int nchunks = K / kc;
   const int blocks = (N / 16 + 3) / 4;
   if (swiglu || blocks >= 128 || nchunks < 2) return 1;
@@ -453,7 +739,7 @@ static int launch_t(LaGemmArgs a, hipStream_t st) {
     else launch_mt<T, EPI, 16>(a, ntw, st);
   }
   if (a.splits > 1 && !a.defer_reduce) {
-    const size_t total = (size_t)a.M * a.N;
+    const size_t total = (size_t)a.M * (a.N / 4);
     hipLaunchKernelGGL((la_gemm_reduce_kernel<T, EPI>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, a);
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;
@@ -463,22 +749,23 @@ int la_gemm_launch(int dtype, int epi, LaGemmArgs a, hipStream_t st) {
   const int kc = dtype == LA_DT_BF16 ? GT<bf16_t>::KC : GT<float>::KC;
   if (a.M < 1 || a.M > 256 || a.K % kc != 0 || a.N % 16 != 0 || a.ldx % (16 / (dtype == LA_DT_BF16 ? 2 : 4)))
     return -2;
-  a.nchunks = a.K / kc;
+  // K units a split is made of (bf16: 64, fp32: one chunk)
+  a.nchunks = dtype == LA_DT_BF16 ? a.K / 64 : a.K / kc;
   if (a.splits < 1) a.splits = 1;
   if (a.splits > a.nchunks) return -2;
   if (a.splits > 1 && a.P == nullptr) return -2;
-  if (a.defer_reduce && (a.splits < 2 || epi != LA_EPI_RESID)) return -2;
+  if (a.defer_reduce && (a.splits < 2 || (epi != LA_EPI_RESID && epi != LA_EPI_STORE))) return -2;
   if (epi == LA_EPI_QKV) {
     if (a.splits != 1 || a.qo.dh < 16 || (a.qo.dh & (a.qo.dh - 1)) != 0 || a.N % a.qo.dh != 0) return -2;
     a.qo.lg_dh = __builtin_ctz((unsigned)a.qo.dh);
   }
   if (dtype == LA_DT_BF16) {
     switch (epi) {
-      case LA_EPI_STORE: return launch_t<bf16_t, LA_EPI_STORE>(a, st);
-      case LA_EPI_RESID: return launch_t<bf16_t, LA_EPI_RESID>(a, st);
-      case LA_EPI_SWIGLU: return launch_t<bf16_t, LA_EPI_SWIGLU>(a, st);
-      case LA_EPI_F32: return launch_t<bf16_t, LA_EPI_F32>(a, st);
-      case LA_EPI_QKV: return launch_t<bf16_t, LA_EPI_QKV>(a, st);
+      case LA_EPI_STORE: return launch_g2_t<LA_EPI_STORE>(a, st);
+      case LA_EPI_RESID: return launch_g2_t<LA_EPI_RESID>(a, st);
+      case LA_EPI_SWIGLU: return launch_g2_t<LA_EPI_SWIGLU>(a, st);
+      case LA_EPI_F32: return launch_g2_t<LA_EPI_F32>(a, st);
+      case LA_EPI_QKV: return -2;                // bf16 QKV: stored, then rotated and placed by la_qkv_post_launch
     }
   } else {
     switch (epi) {

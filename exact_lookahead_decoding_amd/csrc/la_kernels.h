@@ -33,9 +33,10 @@ struct LaGemmArgs {
 };
 int la_gemm_splits(int N, int K, int dtype, int swiglu);
 int la_gemm_ntw(int N, int swiglu);
-size_t la_gemm_packed_elems(int N, int K, int swiglu);   // elements of the packed copy of W
-// W [rows][K] (SwiGLU: gate rows 0..N-1, up rows N..2N-1) -> packed P; rope_dh > 0 packs the columns of each
-// dh-wide head pair-major (tile k of a head holds dims 8k..8k+7 and dh/2+8k..dh/2+8k+7) for LA_EPI_QKV
+size_t la_gemm_packed_elems(int dtype, int N, int K, int swiglu);   // elements of the packed copy of W
+// W [rows][K] (SwiGLU: gate rows 0..N-1, up rows N..2N-1) -> packed P; rope_dh > 0 (fp32 only) packs the
+// columns of each dh-wide head pair-major (tile k of a head holds dims 8k..8k+7 and dh/2+8k..dh/2+8k+7) for
+// LA_EPI_QKV
 int la_gemm_pack_launch(int dtype, const void* W, void* P, int N, int K, int swiglu, hipStream_t st, int rope_dh = 0);
 int la_gemm_launch(int dtype, int epi, LaGemmArgs a, hipStream_t st);
 
@@ -120,9 +121,14 @@ void la_rmsnorm_launch(int dtype, const void* x, const void* w, void* y, const i
 // Residual fold + RMSNorm: x' = T(((P_0 + P_1) + ...) + x) for the split
 // partials P_s = P + s * pstride ([M][d] fp32 each; none when S == 0), written
 // back to x when write_x; y[m] = RMSNorm(x'[src]) with src = rows ? rows[m] : m.
-void la_addnorm_launch(int dtype, void* x, const float* P, int S, size_t pstride, int write_x, const void* w, void* y,
-                       const int32_t* rows, int M, int d, float eps, hipStream_t st);
+#define LA_ADDNORM_MAX_SPLITS 8   // partials the fold takes (the GEMM's K split never exceeds it); -2 beyond
+int la_addnorm_launch(int dtype, void* x, const float* P, int S, size_t pstride, int write_x, const void* w, void* y,
+                      const int32_t* rows, int M, int d, float eps, hipStream_t st);
 void la_rope_table_launch(float2* tab, int T, int dh, float theta, hipStream_t st);
+// la_qkv_post_launch from the S K-split partials [S][M][(H + 2 Hkv) dh] of the projection (fixed-order sum, rounded)
+void la_qkv_reduce_post_launch(int dtype, const float* P, int S, int M, const float2* rope, const int32_t* pos, int H,
+                               int Hkv, int dh, void* q, void* kc, void* vc, int T_cap, int cache_row0, int n_direct,
+                               void* kw, void* vw, int ws_cap, hipStream_t st);
 void la_qkv_post_launch(int dtype, const void* qkv, const float2* rope, const int32_t* pos, int M, int H, int Hkv,
                         int dh, void* q, void* kc, void* vc, int T_cap, int cache_row0, int n_direct, void* kw,
                         void* vw, int ws_cap, hipStream_t st);

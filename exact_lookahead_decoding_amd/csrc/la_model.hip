@@ -159,14 +159,19 @@ static void an_s(int S, void* x, const float* P, size_t pstride, int write_x, co
     case 1: an_t<T, VPT, 1, NTH>(x, P, pstride, write_x, w, y, rows, M, d, eps, st); break;
     case 2: an_t<T, VPT, 2, NTH>(x, P, pstride, write_x, w, y, rows, M, d, eps, st); break;
     case 3: an_t<T, VPT, 3, NTH>(x, P, pstride, write_x, w, y, rows, M, d, eps, st); break;
-    default: an_t<T, VPT, 4, NTH>(x, P, pstride, write_x, w, y, rows, M, d, eps, st); break;
+    case 4: an_t<T, VPT, 4, NTH>(x, P, pstride, write_x, w, y, rows, M, d, eps, st); break;
+    case 5: an_t<T, VPT, 5, NTH>(x, P, pstride, write_x, w, y, rows, M, d, eps, st); break;
+    case 6: an_t<T, VPT, 6, NTH>(x, P, pstride, write_x, w, y, rows, M, d, eps, st); break;
+    case 7: an_t<T, VPT, 7, NTH>(x, P, pstride, write_x, w, y, rows, M, d, eps, st); break;
+    default: an_t<T, VPT, 8, NTH>(x, P, pstride, write_x, w, y, rows, M, d, eps, st); break;
   }
 }
 
-void la_addnorm_launch(int dtype, void* x, const float* P, int S, size_t pstride, int write_x, const void* w, void* y,
-                       const int32_t* rows, int M, int d, float eps, hipStream_t st) {
-  if (M <= 0) return;
+int la_addnorm_launch(int dtype, void* x, const float* P, int S, size_t pstride, int write_x, const void* w, void* y,
+                      const int32_t* rows, int M, int d, float eps, hipStream_t st) {
+  if (M <= 0) return 0;
   if (!P) S = 0;
+  if (S < 0 || S > LA_ADDNORM_MAX_SPLITS) return -2;
   const int esz = dtype == LA_DT_BF16 ? 2 : 4;
   switch (vpt_for(d, esz) * 2 + (dtype == LA_DT_BF16)) {
     case 2: an_s<float, 1, 256>(S, x, P, pstride, write_x, w, y, rows, M, d, eps, st); break;
@@ -178,11 +183,12 @@ void la_addnorm_launch(int dtype, void* x, const float* P, int S, size_t pstride
     case 16: an_s<float, 4, 512>(S, x, P, pstride, write_x, w, y, rows, M, d, eps, st); break;
     default: an_s<bf16_t, 4, 512>(S, x, P, pstride, write_x, w, y, rows, M, d, eps, st); break;
   }
+  return 0;
 }
 
 void la_rmsnorm_launch(int dtype, const void* x, const void* w, void* y, const int32_t* rows, int M, int d,
                        float eps, hipStream_t st) {
-  la_addnorm_launch(dtype, (void*)x, nullptr, 0, 0, 0, w, y, rows, M, d, eps, st);
+  (void)la_addnorm_launch(dtype, (void*)x, nullptr, 0, 0, 0, w, y, rows, M, d, eps, st);
 }
 
 // cos/sin of t * theta^(-2i/dh), evaluated in fp64 and stored as fp32
@@ -234,6 +240,63 @@ __global__ void __launch_bounds__(64) qkv_post_kernel(const T* qkv, const float2
       st<T>(dst + i + half, x2);
     }
   }
+}
+
+// The same from the K-split partials of the projection: each value is the
+// fixed-order sum of its splits rounded to the storage type (what the
+// split reduction stores), then rotated and placed as above.
+template <typename T>
+__global__ void __launch_bounds__(64) qkv_reduce_post_kernel(const float* P, int S, int pcols, int M, const float2* rope,
+                                                             const int32_t* pos, int H, int Hkv, int dh, T* q, T* kc,
+                                                             T* vc, int T_cap, int cache_row0, int n_direct, T* kw,
+                                                             T* vw, int ws_cap) {
+  const int m = blockIdx.x;
+  const int hh = blockIdx.y;
+  const int half = dh / 2;
+  const int p = pos[m];
+  T* dst;
+  if (hh < H) {
+    dst = q + ((size_t)m * H + hh) * dh;
+  } else {
+    const int g = hh < H + Hkv ? hh - H : hh - H - Hkv;
+    const bool isk = hh < H + Hkv;
+    if (m < n_direct) dst = (isk ? kc : vc) + ((size_t)g * T_cap + cache_row0 + m) * dh;
+    else dst = (isk ? kw : vw) + ((size_t)g * ws_cap + (m - n_direct)) * dh;
+  }
+  const bool rot = hh < H + Hkv;
+  const float* src = P + (size_t)m * pcols + (size_t)hh * dh;
+  const size_t sstride = (size_t)M * pcols;
+  for (int i = threadIdx.x; i < half; i += 64) {
+    float a1 = 0.f, a2 = 0.f;
+    for (int s = 0; s < S; ++s) {
+      a1 += src[s * sstride + i];
+      a2 += src[s * sstride + i + half];
+    }
+    const float x1 = StoreT<T>::round(a1), x2 = StoreT<T>::round(a2);
+    if (rot) {
+      const float2 cs = rope[(size_t)p * half + i];
+      st<T>(dst + i, x1 * cs.x - x2 * cs.y);
+      st<T>(dst + i + half, x2 * cs.x + x1 * cs.y);
+    } else {
+      st<T>(dst + i, x1);
+      st<T>(dst + i + half, x2);
+    }
+  }
+}
+
+void la_qkv_reduce_post_launch(int dtype, const float* P, int S, int M, const float2* rope, const int32_t* pos, int H,
+                               int Hkv, int dh, void* q, void* kc, void* vc, int T_cap, int cache_row0, int n_direct,
+                               void* kw, void* vw, int ws_cap, hipStream_t st) {
+  if (M <= 0) return;
+  dim3 grid(M, H + 2 * Hkv);
+  const int pcols = (H + 2 * Hkv) * dh;
+  if (dtype == LA_DT_BF16)
+    hipLaunchKernelGGL(qkv_reduce_post_kernel<bf16_t>, grid, dim3(64), 0, st, P, S, pcols, M, rope, pos, H, Hkv, dh,
+                       (bf16_t*)q, (bf16_t*)kc, (bf16_t*)vc, T_cap, cache_row0, n_direct, (bf16_t*)kw, (bf16_t*)vw,
+                       ws_cap);
+  else
+    hipLaunchKernelGGL(qkv_reduce_post_kernel<float>, grid, dim3(64), 0, st, P, S, pcols, M, rope, pos, H, Hkv, dh,
+                       (float*)q, (float*)kc, (float*)vc, T_cap, cache_row0, n_direct, (float*)kw, (float*)vw, ws_cap);
 }
 
 void la_qkv_post_launch(int dtype, const void* qkv, const float2* rope, const int32_t* pos, int M, int H, int Hkv,
