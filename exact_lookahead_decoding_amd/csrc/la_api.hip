@@ -25,6 +25,7 @@
 
 #define PREFILL_CHUNK 128
 #define LA_MAX_DEVICES 64
+#define LK_WORDS (1 + 64 * LA_MAX_N)
 
 static thread_local std::string g_err;
 
@@ -66,6 +67,8 @@ struct la_ctx {
   int sizes[LA_MAX_N];
   bool warm = false;
   bool pending = false, verified = false;
+  bool paused = false;          // this round runs without the lookahead branch (batch throttle)
+  const float* lg = nullptr;    // the pending round's logits (own buffer, or a batch's rows)
   LaLayout lay;
   LaRowsDev rows;
   std::vector<int32_t> cand_host;
@@ -80,8 +83,10 @@ struct la_ctx {
   std::vector<hipEvent_t> evpool;
   size_t evnext = 0;
   // the next round's pool lookup, started by la_commit: its count and
-  // candidates land in pinned host memory (lk_key: the key, -1: none)
-  int32_t* lk_host = nullptr;   // [1 + 64 * LA_MAX_N]
+  // candidates land in pinned host memory (lk_key: the key, -1: none);
+  // the verification result follows them in the same allocation
+  int32_t* lk_host = nullptr;   // [LK_WORDS] then one LaAcceptDev
+  LaAcceptDev* acc_host = nullptr;
   int lk_key = -1;
   ~la_ctx() {
     if (lk_host) (void)hipHostFree(lk_host);
@@ -139,21 +144,7 @@ static int fail(la_ctx* c, int code, const char* fmt, ...) {
 
 // ------------------------------------------------------------------ sizing
 
-static int validate_cfg(const la_config* cfg, const la_model_dims* d, la_ctx* c) {
-  if (!cfg || !d) return fail(c, LA_EINVAL, "null config or dims");
-  if (cfg->N < 3 || cfg->N > LA_MAX_N) return fail(c, LA_EINVAL, "N=%d not admitted (pinned schedule needs 3 <= N <= %d)", cfg->N, LA_MAX_N);
-  if (cfg->W < 1 || cfg->W > 64) return fail(c, LA_EINVAL, "W=%d out of range [1, 64]", cfg->W);
-  if (cfg->G < 0 || cfg->G > 64) return fail(c, LA_EINVAL, "G=%d out of range [0, 64]", cfg->G);
-  if (cfg->max_new < 1 || cfg->max_prompt < 1) return fail(c, LA_EINVAL, "max_new and max_prompt must be >= 1");
-  if (cfg->verify_mode != LA_VERIFY_GREEDY && cfg->verify_mode != LA_VERIFY_SAMPLE)
-    return fail(c, LA_EINVAL, "verify_mode %d", cfg->verify_mode);
-  if (cfg->verify_mode == LA_VERIFY_SAMPLE && !(cfg->temperature > 0.0)) return fail(c, LA_EINVAL, "temperature must be > 0");
-  if (cfg->pool_from_prompt != 0 && cfg->pool_from_prompt != 1)
-    return fail(c, LA_EINVAL, "pool_from_prompt %d (0 or 1)", cfg->pool_from_prompt);
-  if (cfg->advance_by_accepted != 0 && cfg->advance_by_accepted != 1)
-    return fail(c, LA_EINVAL, "advance_by_accepted %d (0 or 1)", cfg->advance_by_accepted);
-  if (cfg->cap_full_match != 0 && cfg->cap_full_match != 1)
-    return fail(c, LA_EINVAL, "cap_full_match %d (0 or 1)", cfg->cap_full_match);
+static int validate_dims(const la_model_dims* d, la_ctx* c) {
   if (d->dtype != LA_DTYPE_F32 && d->dtype != LA_DTYPE_BF16) return fail(c, LA_EINVAL, "dtype %d", d->dtype);
   if (d->n_layers < 1 || d->d_model < 16 || d->n_heads < 1 || d->n_kv_heads < 1 || d->n_heads % d->n_kv_heads)
     return fail(c, LA_EINVAL, "bad model dims");
@@ -171,6 +162,24 @@ static int validate_cfg(const la_config* cfg, const la_model_dims* d, la_ctx* c)
   if ((long)d->d_model * esz / 16 > 2048)
     return fail(c, LA_EINVAL, "d_model %d exceeds the %d the row kernels hold", d->d_model, 2048 * 16 / esz);
   return LA_OK;
+}
+
+static int validate_cfg(const la_config* cfg, const la_model_dims* d, la_ctx* c) {
+  if (!cfg || !d) return fail(c, LA_EINVAL, "null config or dims");
+  if (cfg->N < 3 || cfg->N > LA_MAX_N) return fail(c, LA_EINVAL, "N=%d not admitted (pinned schedule needs 3 <= N <= %d)", cfg->N, LA_MAX_N);
+  if (cfg->W < 1 || cfg->W > 64) return fail(c, LA_EINVAL, "W=%d out of range [1, 64]", cfg->W);
+  if (cfg->G < 0 || cfg->G > 64) return fail(c, LA_EINVAL, "G=%d out of range [0, 64]", cfg->G);
+  if (cfg->max_new < 1 || cfg->max_prompt < 1) return fail(c, LA_EINVAL, "max_new and max_prompt must be >= 1");
+  if (cfg->verify_mode != LA_VERIFY_GREEDY && cfg->verify_mode != LA_VERIFY_SAMPLE)
+    return fail(c, LA_EINVAL, "verify_mode %d", cfg->verify_mode);
+  if (cfg->verify_mode == LA_VERIFY_SAMPLE && !(cfg->temperature > 0.0)) return fail(c, LA_EINVAL, "temperature must be > 0");
+  if (cfg->pool_from_prompt != 0 && cfg->pool_from_prompt != 1)
+    return fail(c, LA_EINVAL, "pool_from_prompt %d (0 or 1)", cfg->pool_from_prompt);
+  if (cfg->advance_by_accepted != 0 && cfg->advance_by_accepted != 1)
+    return fail(c, LA_EINVAL, "advance_by_accepted %d (0 or 1)", cfg->advance_by_accepted);
+  if (cfg->cap_full_match != 0 && cfg->cap_full_match != 1)
+    return fail(c, LA_EINVAL, "cap_full_match %d (0 or 1)", cfg->cap_full_match);
+  return validate_dims(d, c);
 }
 
 static PackedOffsets packed_offsets(const la_model_dims& d) {
@@ -254,16 +263,19 @@ static int admit(la_ctx* c) {
   return LA_OK;
 }
 
-static size_t gemm_partial_floats(la_ctx* c) {
-  struct { int N, K, sw, M; } mats[] = {
-      {c->qkvdim, c->d, 0, c->m_max}, {c->d, c->H * c->dh, 0, c->m_max}, {c->F, c->d, 1, c->m_max},
-      {c->d, c->F, 0, c->m_max},      {c->V, c->d, 0, c->n_logit_max}};
+// fp32 floats of the K-split partials for M projection rows and Ml LM-head rows
+static size_t partial_floats(int dt, int d, int qkvdim, int qd, int F, int V, int M, int Ml) {
+  struct { int N, K, sw, M; } mats[] = {{qkvdim, d, 0, M}, {d, qd, 0, M}, {F, d, 1, M}, {d, F, 0, M}, {V, d, 0, Ml}};
   size_t mx = 0;
   for (auto& m : mats) {
-    const int s = la_gemm_splits(m.N, m.K, c->dtype, m.sw);
+    const int s = la_gemm_splits(m.N, m.K, dt, m.sw);
     if (s > 1) mx = std::max(mx, (size_t)s * m.M * (m.sw ? 2 * m.N : m.N));
   }
   return mx;
+}
+
+static size_t gemm_partial_floats(la_ctx* c) {
+  return partial_floats(c->dtype, c->d, c->qkvdim, c->H * c->dh, c->F, c->V, c->m_max, c->n_logit_max);
 }
 
 static size_t carve(la_ctx* c, char* base) {
@@ -342,10 +354,32 @@ static bool qkv_fused(int qkvdim, int d, int dt, int dh) {
   return dt == LA_DT_F32 && la_gemm_splits(qkvdim, d, dt, 0) == 1 && dh >= 16 && (dh & (dh - 1)) == 0;
 }
 
-static int gemm(la_ctx* c, int epi, const void* X, const void* W, void* Y, const void* Rr, int M, int N, int K,
-                int up_off, bool defer = false, const LaQkvOut* qo = nullptr) {
+// Activation buffers of one forward: a context's own (one request) or a
+// batch's (several requests whose rows are stacked).
+struct FwdBufs {
+  void *x, *nrm, *qkv, *q, *o, *act, *fin;
+  float *gemm_p, *logits;
+};
+
+static FwdBufs own_bufs(la_ctx* c) {
+  return FwdBufs{c->x, c->nrm, c->qkv, c->q, c->o, c->act, c->fin, c->gemm_p, c->logits};
+}
+
+// One request's rows inside a forward: rows r0 .. r0 + M - 1 of the stacked
+// activations, its logit rows at l0 .. l0 + n_logit - 1 of the logits.
+// K/V of its rows < n_direct go to cache rows cache_row0 + m, the others to
+// workspace rows m - n_direct; keys below shared_end come from the cache.
+struct Seg {
+  la_ctx* s;
+  int r0, M, l0;
+  const int32_t *tok, *pos, *branch, *path, *path_len, *tile_meta, *tile_path, *logit_rows;
+  int nb, maxp, n_direct, cache_row0, shared_end, max_pos, n_logit;
+};
+
+static int gemm(la_ctx* c, float* P, int epi, const void* X, const void* W, void* Y, const void* Rr, int M, int N,
+                int K, int up_off, bool defer = false, const LaQkvOut* qo = nullptr) {
   LaGemmArgs a{};
-  a.X = X; a.W = W; a.Y = Y; a.R = Rr; a.P = c->gemm_p;
+  a.X = X; a.W = W; a.Y = Y; a.R = Rr; a.P = P;
   a.M = M; a.N = N; a.K = K; a.ldx = K; a.ldy = N;
   a.splits = la_gemm_splits(N, K, c->dtype, epi == LA_EPI_SWIGLU);
   a.up_off = up_off;
@@ -363,36 +397,36 @@ static int gemm(la_ctx* c, int epi, const void* X, const void* W, void* Y, const
 }
 
 // A residual projection x += Y W^T.  With a split K its partials stay in
-// gemm_p and the next RMSNorm folds them into x (same sum, same rounding);
-// returns the number of pending partials (0 when x was updated in place).
-static int resid_gemm(la_ctx* c, const void* X, const void* W, int M, int K, int* pending) {
+// the partial buffer and the next RMSNorm folds them into x (same sum, same
+// rounding); returns the number of pending partials (0 when x was updated in
+// place).
+static int resid_gemm(la_ctx* c, const FwdBufs& B, const void* X, const void* W, int M, int K, int* pending) {
   const int s = la_gemm_splits(c->d, K, c->dtype, 0);
   *pending = s > 1 ? s : 0;
-  return gemm(c, LA_EPI_RESID, X, W, c->x, c->x, M, c->d, K, 0, s > 1);
+  return gemm(c, B.gemm_p, LA_EPI_RESID, X, W, B.x, B.x, M, c->d, K, 0, s > 1);
 }
 
-// Forward M rows.  K/V of rows < n_direct go to cache rows cache_row0 + m,
-// the others to workspace rows m - n_direct.  Keys below shared_end come
-// from the cache.  Logits (fp32) of logit_rows[0..n_logit) land in c->logits.
-static int forward(la_ctx* c, int M, const int32_t* tok, const int32_t* pos, const int32_t* branch,
-                   const int32_t* path, const int32_t* path_len, const int32_t* tile_meta, const int32_t* tile_path,
-                   int nb, int maxp, int n_direct, int cache_row0,
-                   int shared_end, int max_pos, const int32_t* logit_rows, int n_logit) {
+// The target forward over the stacked rows of ns requests ("M7.3", 0x04C:
+// one causal forward over the packed rows; "Speculative Decoding", Chapter 7:
+// concurrent requests share one read of the weights per step).  Every
+// projection, RMSNorm and the LM head runs once over all rows; the rotary
+// placement of q, k and v and the attention run per request against its own
+// cache.  Each row's arithmetic is the same whatever rows share the launch
+// (the GEMM's K split depends on the shape only), so a request's logits are
+// bitwise those of its own forward.  c supplies the dims, the weights and
+// the stream (all requests share them); fp32 logits of request i land in
+// B.logits rows sg[i].l0 ...
+static int forward_segs(la_ctx* c, const FwdBufs& B, const Seg* sg, int ns) {
   const int esz = c->esz;
-  const size_t kvl = (size_t)c->Hkv * c->t_cap * c->dh;   // elements per layer
-  const size_t wsl = (size_t)c->Hkv * c->ws_cap * c->dh;
-  la_embed_launch(c->dtype, c->w.embed, tok, c->x, M, c->d, c->st);
-  LaAttnArgs at{};
-  at.q = c->q; at.o = c->o; at.part_o = c->attn_po; at.part_ml = c->attn_pml; at.max_splits = c->parts;
-  at.pos = pos; at.branch = branch; at.path = path; at.path_len = path_len;
-  at.tile_meta = tile_meta; at.tile_path = tile_path;
-  at.Q = M; at.H = c->H; at.Hkv = c->Hkv; at.dh = c->dh; at.T_cap = c->t_cap; at.ws_cap = c->ws_cap; at.maxp = maxp;
-  at.shared_end = shared_end;
-  at.max_pos = max_pos;
-  at.nb = nb;
-  at.n_ws = M - n_direct;
-  at.scale = 1.0f / sqrtf((float)c->dh);
+  int M = 0, n_logit = 0;
+  for (int i = 0; i < ns; ++i) { M += sg[i].M; n_logit += sg[i].n_logit; }
+  const int qd = c->H * c->dh;
+  for (int i = 0; i < ns; ++i)
+    la_embed_launch(c->dtype, c->w.embed, sg[i].tok, (char*)B.x + (size_t)sg[i].r0 * c->d * esz, sg[i].M, c->d, c->st);
+  const bool fused = qkv_fused(c->qkvdim, c->d, c->dtype, c->dh);
+  const int qs = la_gemm_splits(c->qkvdim, c->d, c->dtype, 0);
   int pend = 0;   // split partials of the last residual projection not yet folded into x
+  const size_t pstride = (size_t)M * c->d;
   for (int l = 0; l < c->L; ++l) {
     const char* attn_norm = wptr(c->w.attn_norm, c->d, l, esz);
     const char* mlp_norm = wptr(c->w.mlp_norm, c->d, l, esz);
@@ -401,57 +435,100 @@ static int forward(la_ctx* c, int M, const int32_t* tok, const int32_t* pos, con
     const char* wo = wl + c->pk.o * esz;
     const char* wgu = wl + c->pk.gu * esz;
     const char* wdn = wl + c->pk.dn * esz;
-    char* kc = c->kc + l * kvl * esz;
-    char* vc = c->vc + l * kvl * esz;
-    char* kw = (char*)c->kw + l * wsl * esz;
-    char* vw = (char*)c->vw + l * wsl * esz;
     int rc;
-    const size_t pstride = (size_t)M * c->d;
-    if (la_addnorm_launch(c->dtype, c->x, c->gemm_p, pend, pstride, 1, attn_norm, c->nrm, nullptr, M, c->d,
+    if (la_addnorm_launch(c->dtype, B.x, B.gemm_p, pend, pstride, 1, attn_norm, B.nrm, nullptr, M, c->d,
                           c->dims.eps, c->st))
       return fail(c, LA_EINVAL, "residual fold of %d split partials exceeds %d", pend, LA_ADDNORM_MAX_SPLITS);
-    if (qkv_fused(c->qkvdim, c->d, c->dtype, c->dh)) {
-      const LaQkvOut qo{c->rope, pos, c->q, kc, vc, kw, vw, c->H, c->Hkv, c->dh, c->t_cap, cache_row0, n_direct,
-                        c->ws_cap};
-      if ((rc = gemm(c, LA_EPI_QKV, c->nrm, wqkv, c->qkv, nullptr, M, c->qkvdim, c->d, 0, false, &qo))) return rc;
-    } else if (const int qs = la_gemm_splits(c->qkvdim, c->d, c->dtype, 0); qs > 1) {
+    if (!fused) {
       // split K: the partials go straight to the rotate-and-place pass (one fixed-order sum per value)
-      if ((rc = gemm(c, LA_EPI_STORE, c->nrm, wqkv, c->qkv, nullptr, M, c->qkvdim, c->d, 0, true))) return rc;
-      la_qkv_reduce_post_launch(c->dtype, c->gemm_p, qs, M, c->rope, pos, c->H, c->Hkv, c->dh, c->q, kc, vc,
-                                c->t_cap, cache_row0, n_direct, kw, vw, c->ws_cap, c->st);
-    } else {
-      if ((rc = gemm(c, LA_EPI_STORE, c->nrm, wqkv, c->qkv, nullptr, M, c->qkvdim, c->d, 0))) return rc;
-      la_qkv_post_launch(c->dtype, c->qkv, c->rope, pos, M, c->H, c->Hkv, c->dh, c->q, kc, vc, c->t_cap, cache_row0,
-                         n_direct, kw, vw, c->ws_cap, c->st);
+      if ((rc = gemm(c, B.gemm_p, LA_EPI_STORE, B.nrm, wqkv, B.qkv, nullptr, M, c->qkvdim, c->d, 0, qs > 1)))
+        return rc;
     }
-    at.kc = kc; at.vc = vc; at.kw = kw; at.vw = vw;
-    {
-      // committed K/V read once (positions below shared_end), each packed row's K/V, Q in, O out
-      const double kvrow = 2.0 * c->Hkv * c->dh * c->esz;
-      const double bytes = shared_end * kvrow + (double)(M - n_direct) * kvrow + 2.0 * M * c->H * c->dh * c->esz;
-      const double flops = 4.0 * M * c->H * c->dh * (double)(max_pos + 1);
-      prof_mark(c, true, 1, bytes, flops);
+    for (int i = 0; i < ns; ++i) {
+      const Seg& g = sg[i];
+      la_ctx* s = g.s;
+      const size_t skvl = (size_t)s->Hkv * s->t_cap * s->dh;
+      const size_t swsl = (size_t)s->Hkv * s->ws_cap * s->dh;
+      char* kc = s->kc + l * skvl * esz;
+      char* vc = s->vc + l * skvl * esz;
+      char* kw = (char*)s->kw + l * swsl * esz;
+      char* vw = (char*)s->vw + l * swsl * esz;
+      char* q = (char*)B.q + (size_t)g.r0 * qd * esz;
+      if (fused) {
+        // the fused epilogue places into one request's cache: one launch per request
+        const LaQkvOut qo{s->rope, g.pos, q, kc, vc, kw, vw, c->H, c->Hkv, c->dh, s->t_cap, g.cache_row0, g.n_direct,
+                          s->ws_cap};
+        if ((rc = gemm(c, B.gemm_p, LA_EPI_QKV, (char*)B.nrm + (size_t)g.r0 * c->d * esz, wqkv, B.qkv, nullptr, g.M,
+                       c->qkvdim, c->d, 0, false, &qo)))
+          return rc;
+      } else if (qs > 1) {
+        la_qkv_reduce_post_launch(c->dtype, B.gemm_p + (size_t)g.r0 * c->qkvdim, qs, M, g.M, s->rope, g.pos, c->H,
+                                  c->Hkv, c->dh, q, kc, vc, s->t_cap, g.cache_row0, g.n_direct, kw, vw, s->ws_cap,
+                                  c->st);
+      } else {
+        la_qkv_post_launch(c->dtype, (char*)B.qkv + (size_t)g.r0 * c->qkvdim * esz, s->rope, g.pos, g.M, c->H,
+                           c->Hkv, c->dh, q, kc, vc, s->t_cap, g.cache_row0, g.n_direct, kw, vw, s->ws_cap, c->st);
+      }
+      LaAttnArgs at{};
+      at.q = q; at.o = (char*)B.o + (size_t)g.r0 * qd * esz;
+      at.part_o = s->attn_po; at.part_ml = s->attn_pml; at.max_splits = s->parts;
+      at.pos = g.pos; at.branch = g.branch; at.path = g.path; at.path_len = g.path_len;
+      at.tile_meta = g.tile_meta; at.tile_path = g.tile_path;
+      at.Q = g.M; at.H = c->H; at.Hkv = c->Hkv; at.dh = c->dh; at.T_cap = s->t_cap; at.ws_cap = s->ws_cap;
+      at.maxp = g.maxp;
+      at.shared_end = g.shared_end;
+      at.max_pos = g.max_pos;
+      at.nb = g.nb;
+      at.n_ws = g.M - g.n_direct;
+      at.scale = 1.0f / sqrtf((float)c->dh);
+      at.kc = kc; at.vc = vc; at.kw = kw; at.vw = vw;
+      {
+        // committed K/V read once (positions below shared_end), each packed row's K/V, Q in, O out
+        const double kvrow = 2.0 * c->Hkv * c->dh * esz;
+        const double bytes = g.shared_end * kvrow + (double)(g.M - g.n_direct) * kvrow + 2.0 * g.M * qd * esz;
+        const double flops = 4.0 * g.M * qd * (double)(g.max_pos + 1);
+        prof_mark(c, true, 1, bytes, flops);
+      }
+      rc = la_attention_launch(c->dtype, at, c->st);
+      prof_mark(c, false, 1, 0, 0);
+      if (rc) return fail(c, LA_EDEVICE, "attention launch failed (%d)", rc);
     }
-    rc = la_attention_launch(c->dtype, at, c->st);
-    prof_mark(c, false, 1, 0, 0);
-    if (rc) return fail(c, LA_EDEVICE, "attention launch failed (%d)", rc);
-    if ((rc = resid_gemm(c, c->o, wo, M, c->H * c->dh, &pend))) return rc;
-    if (la_addnorm_launch(c->dtype, c->x, c->gemm_p, pend, pstride, 1, mlp_norm, c->nrm, nullptr, M, c->d,
+    if ((rc = resid_gemm(c, B, B.o, wo, M, qd, &pend))) return rc;
+    if (la_addnorm_launch(c->dtype, B.x, B.gemm_p, pend, pstride, 1, mlp_norm, B.nrm, nullptr, M, c->d,
                           c->dims.eps, c->st))
       return fail(c, LA_EINVAL, "residual fold of %d split partials exceeds %d", pend, LA_ADDNORM_MAX_SPLITS);
-    if ((rc = gemm(c, LA_EPI_SWIGLU, c->nrm, wgu, c->act, nullptr, M, c->F, c->d, c->F))) return rc;
-    if ((rc = resid_gemm(c, c->act, wdn, M, c->F, &pend))) return rc;
+    if ((rc = gemm(c, B.gemm_p, LA_EPI_SWIGLU, B.nrm, wgu, B.act, nullptr, M, c->F, c->d, c->F))) return rc;
+    if ((rc = resid_gemm(c, B, B.act, wdn, M, c->F, &pend))) return rc;
   }
   if (n_logit > 0) {
-    if (la_addnorm_launch(c->dtype, c->x, c->gemm_p, pend, (size_t)M * c->d, 0, c->w.final_norm, c->fin, logit_rows,
-                      n_logit, c->d, c->dims.eps, c->st))
-      return fail(c, LA_EINVAL, "residual fold of %d split partials exceeds %d", pend, LA_ADDNORM_MAX_SPLITS);
-    int rc = gemm(c, LA_EPI_F32, c->fin, (const char*)c->w.packed + c->pk.lm * esz, c->logits, nullptr, n_logit, c->V,
-                  c->d, 0);
+    for (int i = 0; i < ns; ++i) {
+      const Seg& g = sg[i];
+      if (g.n_logit <= 0) continue;
+      if (la_addnorm_launch(c->dtype, (char*)B.x + (size_t)g.r0 * c->d * esz, B.gemm_p + (size_t)g.r0 * c->d, pend,
+                            pstride, 0, c->w.final_norm, (char*)B.fin + (size_t)g.l0 * c->d * esz, g.logit_rows,
+                            g.n_logit, c->d, c->dims.eps, c->st))
+        return fail(c, LA_EINVAL, "residual fold of %d split partials exceeds %d", pend, LA_ADDNORM_MAX_SPLITS);
+    }
+    int rc = gemm(c, B.gemm_p, LA_EPI_F32, B.fin, (const char*)c->w.packed + c->pk.lm * esz, B.logits, nullptr,
+                  n_logit, c->V, c->d, 0);
     if (rc) return rc;
   }
   HIPCHK(c, hipGetLastError());
   return LA_OK;
+}
+
+// Forward M rows of one request into its own buffers.
+static int forward(la_ctx* c, int M, const int32_t* tok, const int32_t* pos, const int32_t* branch,
+                   const int32_t* path, const int32_t* path_len, const int32_t* tile_meta, const int32_t* tile_path,
+                   int nb, int maxp, int n_direct, int cache_row0,
+                   int shared_end, int max_pos, const int32_t* logit_rows, int n_logit) {
+  Seg g{};
+  g.s = c; g.r0 = 0; g.M = M; g.l0 = 0;
+  g.tok = tok; g.pos = pos; g.branch = branch; g.path = path; g.path_len = path_len;
+  g.tile_meta = tile_meta; g.tile_path = tile_path; g.logit_rows = logit_rows;
+  g.nb = nb; g.maxp = maxp; g.n_direct = n_direct; g.cache_row0 = cache_row0; g.shared_end = shared_end;
+  g.max_pos = max_pos; g.n_logit = n_logit;
+  return forward_segs(c, own_bufs(c), &g, 1);
 }
 
 static void rows_layout(const LaLayout& L, int32_t* base, LaRowsDev* r, la_rows_info* info) {
@@ -511,11 +588,13 @@ extern "C" int la_init(const la_config* cfg, const la_model_dims* dims, const la
   c->kc = (char*)kv;
   c->vc = (char*)kv + kvb;
   carve(c, (char*)arena);
-  if (hipHostMalloc((void**)&c->lk_host, (1 + 64 * LA_MAX_N) * sizeof(int32_t), hipHostMallocDefault) != hipSuccess) {
+  if (hipHostMalloc((void**)&c->lk_host, LK_WORDS * sizeof(int32_t) + sizeof(LaAcceptDev), hipHostMallocDefault) !=
+      hipSuccess) {
     c->lk_host = nullptr;
     delete c;
     return fail(nullptr, LA_EDEVICE, "pinned host buffer");
   }
+  c->acc_host = (LaAcceptDev*)(c->lk_host + LK_WORDS);
   memset(&c->stats, 0, sizeof c->stats);
   for (int r = 0; r < LA_MAX_N; ++r) c->sizes[r] = 0;
   c->cur = 0;
@@ -632,56 +711,149 @@ static int start_lookup(la_ctx* c, int key) {
   return LA_OK;
 }
 
-extern "C" int la_predict(la_ctx* c, la_round_info* info) {
-  if (!c) return fail(nullptr, LA_EINVAL, "null ctx");
+// A round in parts, shared by la_predict / la_verify and la_batch_step.
+
+// Checks before a round is compiled.
+static int round_check(la_ctx* c) {
   if (c->pending) return fail(c, LA_ESTATE, "round %d is pending commit", c->round_id + 1);
   if ((int)c->out.size() >= c->cfg.max_new) return fail(c, LA_ESTATE, "max_new tokens already generated");
-  const int x_t = c->out.back();
-  const int p = c->kv_len;
-  if (p + 1 + c->S > c->t_cap) return fail(c, LA_EOVERFLOW, "K/V capacity %d exhausted", c->t_cap);
-  const bool warm = !c->cfg.ar_only && is_warm(c);
-  int C = 0;
-  c->cand_host.clear();
-  if (warm && c->cfg.G > 0) {
-    // usually started by the last commit (same key, pool unchanged since)
-    if (c->lk_key != x_t) {
-      const int rc = start_lookup(c, x_t);
-      if (rc) return rc;
-    }
+  if (c->kv_len + 1 + c->S > c->t_cap) return fail(c, LA_EOVERFLOW, "K/V capacity %d exhausted", c->t_cap);
+  return LA_OK;
+}
+
+// Whether the round reads the pool; if so its lookup for the current token
+// is under way after this (usually started by the last commit: same key,
+// pool unchanged since).  Its count is read after a stream synchronisation.
+static int round_lookup(la_ctx* c, bool* uses_pool) {
+  *uses_pool = !c->cfg.ar_only && is_warm(c) && c->cfg.G > 0;
+  if (!*uses_pool) {
     c->lk_key = -1;
-    HIPCHK(c, hipStreamSynchronize(c->st));
-    C = c->lk_host[0];
-    if (C < 0 || C > c->cfg.G) return fail(c, LA_EDEVICE, "pool lookup returned %d candidates", C);
-    c->cand_host.assign(c->lk_host + 1, c->lk_host + 1 + (size_t)C * c->S);
-  } else {
-    c->lk_key = -1;
+    return LA_OK;
   }
-  LaLayout L{};
-  L.p = p; L.R = c->R; L.C = C; L.S = c->S;
-  for (int r = 0; r < c->R; ++r) { L.sizes[r] = c->cfg.ar_only ? 0 : c->sizes[r]; L.starts[r] = r == 0 ? 1 : 0; }
-  if (la_layout_finish(&L)) return fail(c, LA_EINVAL, "inconsistent window layout");
+  if (c->lk_key != c->out.back()) return start_lookup(c, c->out.back());
+  return LA_OK;
+}
+
+// Candidates the lookup found (its copy has landed).
+static int round_found(la_ctx* c, bool uses_pool, int* C) {
+  *C = 0;
+  if (!uses_pool) return LA_OK;
+  const int n = c->lk_host[0];
+  if (n < 0 || n > c->cfg.G) return fail(c, LA_EDEVICE, "pool lookup returned %d candidates", n);
+  *C = n;
+  return LA_OK;
+}
+
+// The round's layout with C candidates: the lookahead branch (the window's
+// levels), or none when paused or autoregressive.
+static int round_layout(const la_ctx* c, int C, bool paused, LaLayout* L) {
+  *L = LaLayout{};
+  L->p = c->kv_len; L->R = c->R; L->C = C; L->S = c->S;
+  for (int r = 0; r < c->R; ++r) {
+    L->sizes[r] = c->cfg.ar_only || paused ? 0 : c->sizes[r];
+    L->starts[r] = r == 0 ? 1 : 0;
+  }
+  return la_layout_finish(L);
+}
+
+// Compile the round's rows on the stream: the first C of the candidates found
+// (pool order: the oldest first, "M7.3" 0x03B), the lookahead branch unless
+// paused.
+static int round_rows(la_ctx* c, int C, bool paused) {
+  const int p = c->kv_len;
+  c->lk_key = -1;
+  c->cand_host.assign(c->lk_host + 1, c->lk_host + 1 + (size_t)C * c->S);
+  LaLayout L;
+  if (round_layout(c, C, paused, &L)) return fail(c, LA_EINVAL, "inconsistent window layout");
   if (L.Q > c->q_max) return fail(c, LA_EOVERFLOW, "round needs %d rows > q_max %d", L.Q, c->q_max);
   if (p + L.maxp >= c->rope_rows) return fail(c, LA_EOVERFLOW, "position %d beyond the RoPE table", p + L.maxp);
   rows_layout(L, c->rowbuf, &c->rows, nullptr);
-  if (la_build_rows_launch(L, x_t, c->win[c->cur], c->wstride, c->cand, c->rows, c->st))
+  if (la_build_rows_launch(L, c->out.back(), c->win[c->cur], c->wstride, c->cand, c->rows, c->st))
     return fail(c, LA_EOVERFLOW, "row builder: %d rows exceed its LDS tables", L.Q);
-  const int maxpos = p + L.maxp;             // a row's branch path covers its own position
-  int rc = forward(c, L.Q, c->rows.tok, c->rows.pos, c->rows.branch, c->rows.path, c->rows.path_len,
-                   c->rows.tile_meta, c->rows.tile_path, L.NB, L.maxp, 1, p, p + 1, maxpos, c->rows.logit_rows,
-                   L.n_logit);
-  if (rc) return rc;
   c->lay = L;
+  c->paused = paused;
+  return LA_OK;
+}
+
+// The round's rows as one segment of a forward: the ordinary row's K/V go to
+// the cache at p, the rest to the workspace; the prefix below p + 1 is shared.
+static Seg round_seg(la_ctx* c, int r0, int l0) {
+  const LaLayout& L = c->lay;
+  const int p = c->kv_len;
+  Seg g{};
+  g.s = c; g.r0 = r0; g.M = L.Q; g.l0 = l0;
+  g.tok = c->rows.tok; g.pos = c->rows.pos; g.branch = c->rows.branch; g.path = c->rows.path;
+  g.path_len = c->rows.path_len; g.tile_meta = c->rows.tile_meta; g.tile_path = c->rows.tile_path;
+  g.logit_rows = c->rows.logit_rows;
+  g.nb = L.NB; g.maxp = L.maxp; g.n_direct = 1; g.cache_row0 = p; g.shared_end = p + 1;
+  g.max_pos = p + L.maxp;                   // a row's branch path covers its own position
+  g.n_logit = L.n_logit;
+  return g;
+}
+
+static void round_predicted(la_ctx* c, const float* logits) {
+  c->lg = logits;
   c->pending = true;
   c->verified = false;
-  c->warm = warm;
+  c->warm = !c->cfg.ar_only && is_warm(c);
+}
+
+extern "C" int la_predict(la_ctx* c, la_round_info* info) {
+  if (!c) return fail(nullptr, LA_EINVAL, "null ctx");
+  int rc = round_check(c);
+  if (rc) return rc;
+  bool uses_pool;
+  if ((rc = round_lookup(c, &uses_pool))) return rc;
+  if (uses_pool) HIPCHK(c, hipStreamSynchronize(c->st));
+  int C;
+  if ((rc = round_found(c, uses_pool, &C))) return rc;
+  if ((rc = round_rows(c, C, false))) return rc;
+  const Seg g = round_seg(c, 0, 0);
+  if ((rc = forward_segs(c, own_bufs(c), &g, 1))) return rc;
+  round_predicted(c, c->logits);
   if (info) {
+    const LaLayout& L = c->lay;
     info->round_id = c->round_id + 1;
-    info->p = p; info->Q = L.Q; info->C = C; info->n_inp = L.n_inp; info->n_logit = L.n_logit;
-    info->warm = warm ? 1 : 0;
+    info->p = c->kv_len; info->Q = L.Q; info->C = L.C; info->n_inp = L.n_inp; info->n_logit = L.n_logit;
+    info->warm = c->warm ? 1 : 0;
     info->reserved = 0;
-    info->logits = c->logits;
+    info->logits = c->lg;
   }
   return LA_OK;
+}
+
+// Launch the verification of 1 + n_inp + C * S logit rows and start the copy
+// of its result to the pinned host slot (read after a synchronisation).
+static int verify_issue(la_ctx* c, const float* logits, int n_inp, const int32_t* cand_dev, int C, int32_t* zdev,
+                        int32_t* z_host) {
+  const int n_logit = 1 + n_inp + C * c->S;
+  const int rid = c->round_id + 1;          // the draws of the round being decided
+  la_argmax_launch(logits, n_logit, c->V, c->amax, c->st);
+  if (c->cfg.verify_mode == LA_VERIFY_SAMPLE)
+    la_sample_accept_launch(logits, c->V, n_inp, c->amax, cand_dev, C, c->S, c->hmax, c->cfg.temperature,
+                            c->cfg.seed, rid, c->escr, c->acc, zdev, c->st);
+  else
+    la_greedy_accept_launch(c->amax, n_inp, cand_dev, C, c->S, c->hmax, c->acc, zdev, c->st);
+  HIPCHK(c, hipGetLastError());
+  HIPCHK(c, hipMemcpyAsync(c->acc_host, c->acc, sizeof(LaAcceptDev), hipMemcpyDeviceToHost, c->st));
+  if (z_host && n_inp > 0) HIPCHK(c, hipMemcpyAsync(z_host, zdev, (size_t)n_inp * 4, hipMemcpyDeviceToHost, c->st));
+  return LA_OK;
+}
+
+// The verification result, after the stream synchronisation.
+static void verify_read(la_ctx* c, la_accept* out, bool own) {
+  prof_collect(c);
+  const LaAcceptDev& a = *c->acc_host;
+  memset(out, 0, sizeof *out);
+  out->round_id = c->round_id + 1;
+  out->h = a.h;
+  out->winner = a.winner;
+  out->n_emit = a.n_emit;
+  for (int i = 0; i < a.n_emit && i < LA_MAX_EMIT; ++i) out->emitted[i] = a.emitted[i];
+  if (own) {
+    c->vacc = *out;
+    c->verified = true;
+  }
 }
 
 extern "C" int la_verify(la_ctx* c, const float* logits, int32_t n_inp, const int32_t* cand, int32_t C, la_accept* out,
@@ -692,7 +864,7 @@ extern "C" int la_verify(la_ctx* c, const float* logits, int32_t n_inp, const in
   int32_t* zdev;
   if (own) {
     if (!c->pending) return fail(c, LA_ESTATE, "no predicted round to verify");
-    logits = c->logits;
+    logits = c->lg;
     n_inp = c->lay.n_inp;
     C = c->lay.C;
     cand_dev = c->cand;
@@ -706,30 +878,10 @@ extern "C" int la_verify(la_ctx* c, const float* logits, int32_t n_inp, const in
     cand_dev = c->vcand;
     zdev = c->z2;
   }
-  const int n_logit = 1 + n_inp + C * c->S;
-  const int rid = c->round_id + 1;          // the draws of the round being decided
-  la_argmax_launch(logits, n_logit, c->V, c->amax, c->st);
-  if (c->cfg.verify_mode == LA_VERIFY_SAMPLE)
-    la_sample_accept_launch(logits, c->V, n_inp, c->amax, cand_dev, C, c->S, c->hmax, c->cfg.temperature,
-                            c->cfg.seed, rid, c->escr, c->acc, zdev, c->st);
-  else
-    la_greedy_accept_launch(c->amax, n_inp, cand_dev, C, c->S, c->hmax, c->acc, zdev, c->st);
-  LaAcceptDev a;
-  HIPCHK(c, hipGetLastError());
-  HIPCHK(c, hipMemcpyAsync(&a, c->acc, sizeof a, hipMemcpyDeviceToHost, c->st));
-  if (z_host && n_inp > 0) HIPCHK(c, hipMemcpyAsync(z_host, zdev, (size_t)n_inp * 4, hipMemcpyDeviceToHost, c->st));
+  int rc = verify_issue(c, logits, n_inp, cand_dev, C, zdev, z_host);
+  if (rc) return rc;
   HIPCHK(c, hipStreamSynchronize(c->st));
-  prof_collect(c);
-  memset(out, 0, sizeof *out);
-  out->round_id = rid;
-  out->h = a.h;
-  out->winner = a.winner;
-  out->n_emit = a.n_emit;
-  for (int i = 0; i < a.n_emit && i < LA_MAX_EMIT; ++i) out->emitted[i] = a.emitted[i];
-  if (own) {
-    c->vacc = *out;
-    c->verified = true;
-  }
+  verify_read(c, out, own);
   return LA_OK;
 }
 
@@ -757,7 +909,7 @@ extern "C" int la_commit(la_ctx* c, const la_accept* a) {
   if (a->h > 0)
     la_kv_commit_launch(c->dtype, c->kc, c->vc, c->kw, c->vw, c->L, c->Hkv, c->dh, c->t_cap, c->ws_cap,
                         c->kv_len + 1, cand_start - 1 + a->winner * S, a->h, c->st);
-  if (!c->cfg.ar_only) {
+  if (!c->cfg.ar_only && !c->paused) {
     if (c->warm && c->cfg.G > 0)
       la_pool_collect_launch(c->pool_cnt, c->pool_ent, c->out.back(), c->win[c->cur], c->wstride, c->R, c->cfg.W,
                              c->z, c->cfg.G, c->st);
@@ -789,6 +941,8 @@ extern "C" int la_commit(la_ctx* c, const la_accept* a) {
   c->stats.tokens += added;
   c->stats.candidates += L.C;
   c->stats.accepted += a->h;
+  c->stats.paused += c->paused ? 1 : 0;
+  c->paused = false;
   if (a->n_emit < LA_MAX_EMIT) c->stats.hist[a->n_emit] += 1;
   // the next round's lookup goes out now, so the host's way back to the
   // next la_predict overlaps it
@@ -829,6 +983,217 @@ extern "C" int la_generate(la_ctx* c, int32_t* out_tokens, int32_t cap, int32_t*
   }
   for (size_t i = 0; i < c->out.size(); ++i) out_tokens[i] = c->out[i];
   *n_out = (int32_t)c->out.size();
+  return LA_OK;
+}
+
+// ------------------------------------------------------------------ batch
+
+// Several requests, one round each, in one stacked forward ("Speculative
+// Decoding", Chapter 7 "Speculation Meets the Batch": concurrent requests
+// share one read of the weights per step, and their speculation shares the
+// compute left beside it; "M7.3", 0x03B: each request keeps its own pool,
+// window and K/V).
+struct la_batch {
+  la_model_dims dims;
+  la_model w;
+  hipStream_t st;
+  int max_rows;
+  FwdBufs b;
+  std::vector<int32_t> base, found, cap, paused;
+};
+
+static size_t carve_batch(const la_model_dims& d, int R, char* base, FwdBufs* B) {
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> void* {
+    void* p = base ? (void*)(base + off) : nullptr;
+    off += (bytes + 255) & ~(size_t)255;
+    return p;
+  };
+  const size_t e = d.dtype == LA_DTYPE_BF16 ? 2 : 4;
+  const int dt = d.dtype == LA_DTYPE_BF16 ? LA_DT_BF16 : LA_DT_F32;
+  const int qd = d.n_heads * d.head_dim, qkvdim = (d.n_heads + 2 * d.n_kv_heads) * d.head_dim;
+  FwdBufs b{};
+  b.x = take((size_t)R * d.d_model * e);
+  b.nrm = take((size_t)R * d.d_model * e);
+  b.qkv = take((size_t)R * qkvdim * e);
+  b.q = take((size_t)R * qd * e);
+  b.o = take((size_t)R * qd * e);
+  b.act = take((size_t)R * d.d_ff * e);
+  b.fin = take((size_t)R * d.d_model * e);
+  b.gemm_p = (float*)take(std::max<size_t>(partial_floats(dt, d.d_model, qkvdim, qd, d.d_ff, d.vocab, R, R), 1) * 4);
+  b.logits = (float*)take((size_t)R * d.vocab * 4);
+  if (B) *B = b;
+  return off;
+}
+
+extern "C" uint64_t la_batch_bytes(const la_model_dims* dims, int32_t max_rows) {
+  if (!dims || validate_dims(dims, nullptr) || max_rows < 1 || max_rows > LA_MAX_ROWS) return 0;
+  return carve_batch(*dims, max_rows, nullptr, nullptr);
+}
+
+extern "C" int la_batch_init(const la_model_dims* dims, const la_model* weights, int32_t max_rows, void* workspace,
+                             uint64_t bytes, void* stream, la_batch** out) {
+  if (!out) return fail(nullptr, LA_EINVAL, "null batch output");
+  *out = nullptr;
+  if (!dims || !weights) return fail(nullptr, LA_EINVAL, "null dims or weights");
+  int rc = validate_dims(dims, nullptr);
+  if (rc) return rc;
+  if (max_rows < 1 || max_rows > LA_MAX_ROWS)
+    return fail(nullptr, LA_EINVAL, "max_rows %d outside [1, %d]", max_rows, LA_MAX_ROWS);
+  if (!weights->packed || !weights->embed || !weights->final_norm || !weights->attn_norm || !weights->mlp_norm)
+    return fail(nullptr, LA_EINVAL, "weights: packed projections (la_pack_weights), embed and norms are required");
+  const size_t need = carve_batch(*dims, max_rows, nullptr, nullptr);
+  if (!workspace || bytes < need)
+    return fail(nullptr, LA_EOVERFLOW, "workspace of %llu bytes, %zu needed", (unsigned long long)bytes, need);
+  la_batch* b = new la_batch();
+  b->dims = *dims;
+  b->w = *weights;
+  b->st = (hipStream_t)stream;
+  b->max_rows = max_rows;
+  carve_batch(*dims, max_rows, (char*)workspace, &b->b);
+  *out = b;
+  return LA_OK;
+}
+
+extern "C" void la_batch_destroy(la_batch* b) { delete b; }
+
+// The occupancy throttle ("Speculative Decoding", Chapter 7: speculation
+// spends only the part of the step's row budget that the batch's own rows
+// leave free, per request, and is switched off when nothing is left).  Every
+// active request (base > 0) first gets its own round's rows without
+// candidates (base: its ordinary row plus its lookahead branch).  If that
+// exceeds the budget, requests from the last one backwards run without their
+// lookahead branch (one row each) until it fits.  The rest of the budget is
+// dealt in S-row candidate blocks, one per request in turn (request order),
+// among the requests that kept their branch, up to the candidates each found.
+static int batch_plan(int n, int budget, int S, const int32_t* base, const int32_t* found, int32_t* cap,
+                      int32_t* paused) {
+  long rows = 0;
+  int act = 0;
+  for (int i = 0; i < n; ++i) {
+    cap[i] = 0;
+    paused[i] = 0;
+    if (base[i] > 0) { ++act; rows += base[i]; }
+  }
+  if (act > budget) return fail(nullptr, LA_EOVERFLOW, "%d active requests exceed the row budget %d", act, budget);
+  for (int i = n - 1; i >= 0 && rows > budget; --i)
+    if (base[i] > 1) { rows -= base[i] - 1; paused[i] = 1; }
+  for (bool more = true; more && rows + S <= budget;) {
+    more = false;
+    for (int i = 0; i < n && rows + S <= budget; ++i)
+      if (base[i] > 0 && !paused[i] && cap[i] < found[i]) { ++cap[i]; rows += S; more = true; }
+  }
+  return LA_OK;
+}
+
+extern "C" int la_batch_plan(int32_t n, int32_t row_budget, int32_t S, const int32_t* base_rows, const int32_t* found,
+                             int32_t* cap, int32_t* paused) {
+  if (n < 0 || n > LA_MAX_ROWS || row_budget < 1 || S < 1 || S > LA_MAX_N - 1)
+    return fail(nullptr, LA_EINVAL, "n=%d, row_budget=%d, S=%d out of range", n, row_budget, S);
+  if (n > 0 && (!base_rows || !found || !cap || !paused)) return fail(nullptr, LA_EINVAL, "null array");
+  for (int i = 0; i < n; ++i)
+    if (base_rows[i] < 0 || found[i] < 0) return fail(nullptr, LA_EINVAL, "negative base_rows or found at %d", i);
+  return batch_plan(n, row_budget, S, base_rows, found, cap, paused);
+}
+
+extern "C" int la_batch_step(la_batch* b, la_ctx* const* ctx, int32_t n, int32_t row_budget, int32_t* out_tokens,
+                             int32_t* n_out, la_batch_round* rinfo) {
+  if (!b || !ctx || !out_tokens || !n_out) return fail(nullptr, LA_EINVAL, "null argument");
+  if (n < 1 || n > LA_MAX_ROWS) return fail(nullptr, LA_EINVAL, "n=%d outside [1, %d]", n, LA_MAX_ROWS);
+  const int budget = row_budget <= 0 ? b->max_rows : row_budget;
+  if (budget > b->max_rows) return fail(nullptr, LA_EINVAL, "row budget %d > max_rows %d", budget, b->max_rows);
+  for (int i = 0; i < n; ++i) {
+    la_ctx* c = ctx[i];
+    if (!c) return fail(nullptr, LA_EINVAL, "null context %d", i);
+    for (int j = 0; j < i; ++j)
+      if (ctx[j] == c) return fail(nullptr, LA_EINVAL, "context %d appears twice", i);
+    if (memcmp(&c->dims, &b->dims, sizeof b->dims) || c->w.packed != b->w.packed || c->w.embed != b->w.embed ||
+        c->w.final_norm != b->w.final_norm || c->w.attn_norm != b->w.attn_norm || c->w.mlp_norm != b->w.mlp_norm)
+      return fail(nullptr, LA_EINVAL, "context %d runs another model than the batch", i);
+    if (c->st != b->st) return fail(nullptr, LA_EINVAL, "context %d runs on another stream than the batch", i);
+    if (c->cfg.N != ctx[0]->cfg.N)
+      return fail(nullptr, LA_EINVAL, "context %d has N=%d, context 0 N=%d: a batch shares N", i, c->cfg.N,
+                  ctx[0]->cfg.N);
+    n_out[i] = 0;
+    if (rinfo) rinfo[i] = la_batch_round{};
+  }
+  b->base.assign(n, 0); b->found.assign(n, 0); b->cap.assign(n, 0); b->paused.assign(n, 0);
+  std::vector<int> act;
+  for (int i = 0; i < n; ++i) {
+    la_ctx* c = ctx[i];
+    if ((int)c->out.size() >= c->cfg.max_new) continue;
+    int rc = round_check(c);
+    if (rc) return rc;
+    LaLayout L;
+    if (round_layout(c, 0, false, &L)) return fail(c, LA_EINVAL, "inconsistent window layout");
+    b->base[i] = L.Q;
+    act.push_back(i);
+  }
+  if (act.empty()) return LA_OK;
+  // the lookups (usually under way since the last commit), one synchronisation
+  std::vector<char> uses(n, 0);
+  bool any = false;
+  for (int i : act) {
+    bool u;
+    int rc = round_lookup(ctx[i], &u);
+    if (rc) return rc;
+    uses[i] = u;
+    any = any || u;
+  }
+  if (any) HIPCHK(nullptr, hipStreamSynchronize(b->st));
+  for (int i : act) {
+    int C, rc = round_found(ctx[i], uses[i], &C);
+    if (rc) return rc;
+    b->found[i] = C;
+  }
+  int rc = batch_plan(n, budget, ctx[act[0]]->S, b->base.data(), b->found.data(), b->cap.data(), b->paused.data());
+  if (rc) return rc;
+  // rows and segments
+  std::vector<Seg> seg;
+  int r0 = 0, l0 = 0;
+  for (int i : act) {
+    la_ctx* c = ctx[i];
+    if ((rc = round_rows(c, b->cap[i], b->paused[i] != 0))) return rc;
+    seg.push_back(round_seg(c, r0, l0));
+    r0 += c->lay.Q;
+    l0 += c->lay.n_logit;
+  }
+  if (r0 > b->max_rows) return fail(nullptr, LA_EOVERFLOW, "%d stacked rows > max_rows %d", r0, b->max_rows);
+  la_ctx* lead = ctx[act[0]];
+  if ((rc = forward_segs(lead, b->b, seg.data(), (int)seg.size()))) return rc;
+  for (size_t k = 0; k < act.size(); ++k) round_predicted(ctx[act[k]], b->b.logits + (size_t)seg[k].l0 * b->dims.vocab);
+  auto unwind = [&]() {
+    for (int i : act) { ctx[i]->pending = false; ctx[i]->verified = false; }
+  };
+  for (int i : act) {
+    la_ctx* c = ctx[i];
+    if ((rc = verify_issue(c, c->lg, c->lay.n_inp, c->cand, c->lay.C, c->z, nullptr))) { unwind(); return rc; }
+  }
+  if (hipError_t e = hipStreamSynchronize(b->st); e != hipSuccess) {
+    unwind();
+    return fail(nullptr, LA_EDEVICE, "hipStreamSynchronize: %s", hipGetErrorString(e));
+  }
+  // publication, request by request (a failure leaves the requests before it published)
+  for (int i : act) {
+    la_ctx* c = ctx[i];
+    la_accept a;
+    verify_read(c, &a, true);
+    if (rinfo) {
+      rinfo[i].Q = c->lay.Q;
+      rinfo[i].found = b->found[i];
+      rinfo[i].verified = c->lay.C;
+      rinfo[i].paused = b->paused[i];
+      rinfo[i].h = a.h;
+    }
+    const size_t before = c->out.size();
+    if ((rc = la_commit(c, &a))) {
+      for (int j : act) if (ctx[j]->pending) { ctx[j]->pending = false; ctx[j]->verified = false; }
+      return rc;
+    }
+    const size_t k = c->out.size() - before;
+    for (size_t t = 0; t < k; ++t) out_tokens[(size_t)i * LA_MAX_EMIT + t] = c->out[before + t];
+    n_out[i] = (int32_t)k;
+  }
   return LA_OK;
 }
 

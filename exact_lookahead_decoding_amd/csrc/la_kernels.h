@@ -125,10 +125,11 @@ void la_rmsnorm_launch(int dtype, const void* x, const void* w, void* y, const i
 int la_addnorm_launch(int dtype, void* x, const float* P, int S, size_t pstride, int write_x, const void* w, void* y,
                       const int32_t* rows, int M, int d, float eps, hipStream_t st);
 void la_rope_table_launch(float2* tab, int T, int dh, float theta, hipStream_t st);
-// la_qkv_post_launch from the S K-split partials [S][M][(H + 2 Hkv) dh] of the projection (fixed-order sum, rounded)
-void la_qkv_reduce_post_launch(int dtype, const float* P, int S, int M, const float2* rope, const int32_t* pos, int H,
-                               int Hkv, int dh, void* q, void* kc, void* vc, int T_cap, int cache_row0, int n_direct,
-                               void* kw, void* vw, int ws_cap, hipStream_t st);
+// la_qkv_post_launch from the S K-split partials [S][Prows][(H + 2 Hkv) dh] of the projection (fixed-order
+// sum, rounded) for its rows 0..M-1 (P may point at a later row of a larger partial buffer)
+void la_qkv_reduce_post_launch(int dtype, const float* P, int S, int Prows, int M, const float2* rope,
+                               const int32_t* pos, int H, int Hkv, int dh, void* q, void* kc, void* vc, int T_cap,
+                               int cache_row0, int n_direct, void* kw, void* vw, int ws_cap, hipStream_t st);
 void la_qkv_post_launch(int dtype, const void* qkv, const float2* rope, const int32_t* pos, int M, int H, int Hkv,
                         int dh, void* q, void* kc, void* vc, int T_cap, int cache_row0, int n_direct, void* kw,
                         void* vw, int ws_cap, hipStream_t st);

@@ -246,7 +246,8 @@ __global__ void __launch_bounds__(64) qkv_post_kernel(const T* qkv, const float2
 // fixed-order sum of its splits rounded to the storage type (what the
 // split reduction stores), then rotated and placed as above.
 template <typename T>
-__global__ void __launch_bounds__(64) qkv_reduce_post_kernel(const float* P, int S, int pcols, int M, const float2* rope,
+__global__ void __launch_bounds__(64) qkv_reduce_post_kernel(const float* P, int S, int pcols, int Prows,
+                                                             const float2* rope,
                                                              const int32_t* pos, int H, int Hkv, int dh, T* q, T* kc,
                                                              T* vc, int T_cap, int cache_row0, int n_direct, T* kw,
                                                              T* vw, int ws_cap) {
@@ -265,7 +266,7 @@ __global__ void __launch_bounds__(64) qkv_reduce_post_kernel(const float* P, int
   }
   const bool rot = hh < H + Hkv;
   const float* src = P + (size_t)m * pcols + (size_t)hh * dh;
-  const size_t sstride = (size_t)M * pcols;
+  const size_t sstride = (size_t)Prows * pcols;
   for (int i = threadIdx.x; i < half; i += 64) {
     float a1 = 0.f, a2 = 0.f;
     for (int s = 0; s < S; ++s) {
@@ -284,18 +285,18 @@ __global__ void __launch_bounds__(64) qkv_reduce_post_kernel(const float* P, int
   }
 }
 
-void la_qkv_reduce_post_launch(int dtype, const float* P, int S, int M, const float2* rope, const int32_t* pos, int H,
-                               int Hkv, int dh, void* q, void* kc, void* vc, int T_cap, int cache_row0, int n_direct,
-                               void* kw, void* vw, int ws_cap, hipStream_t st) {
+void la_qkv_reduce_post_launch(int dtype, const float* P, int S, int Prows, int M, const float2* rope,
+                               const int32_t* pos, int H, int Hkv, int dh, void* q, void* kc, void* vc, int T_cap,
+                               int cache_row0, int n_direct, void* kw, void* vw, int ws_cap, hipStream_t st) {
   if (M <= 0) return;
   dim3 grid(M, H + 2 * Hkv);
   const int pcols = (H + 2 * Hkv) * dh;
   if (dtype == LA_DT_BF16)
-    hipLaunchKernelGGL(qkv_reduce_post_kernel<bf16_t>, grid, dim3(64), 0, st, P, S, pcols, M, rope, pos, H, Hkv, dh,
+    hipLaunchKernelGGL(qkv_reduce_post_kernel<bf16_t>, grid, dim3(64), 0, st, P, S, pcols, Prows, rope, pos, H, Hkv, dh,
                        (bf16_t*)q, (bf16_t*)kc, (bf16_t*)vc, T_cap, cache_row0, n_direct, (bf16_t*)kw, (bf16_t*)vw,
                        ws_cap);
   else
-    hipLaunchKernelGGL(qkv_reduce_post_kernel<float>, grid, dim3(64), 0, st, P, S, pcols, M, rope, pos, H, Hkv, dh,
+    hipLaunchKernelGGL(qkv_reduce_post_kernel<float>, grid, dim3(64), 0, st, P, S, pcols, Prows, rope, pos, H, Hkv, dh,
                        (float*)q, (float*)kc, (float*)vc, T_cap, cache_row0, n_direct, (float*)kw, (float*)vw, ws_cap);
 }
 

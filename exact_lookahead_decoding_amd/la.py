@@ -69,7 +69,12 @@ class la_round_info(C.Structure):
 
 class la_stats_t(C.Structure):
     _fields_ = [("rounds", C.c_int64), ("tokens", C.c_int64), ("candidates", C.c_int64), ("accepted", C.c_int64),
-                ("hist", C.c_int32 * LA_MAX_EMIT)]
+                ("hist", C.c_int32 * LA_MAX_EMIT), ("paused", C.c_int64)]
+
+
+class la_batch_round(C.Structure):
+    _fields_ = [("Q", C.c_int32), ("found", C.c_int32), ("verified", C.c_int32), ("paused", C.c_int32),
+                ("h", C.c_int32), ("reserved", C.c_int32 * 3)]
 
 
 class la_state_t(C.Structure):
@@ -100,7 +105,8 @@ EXPORTS = ["la_query_sizes", "la_init", "la_destroy", "la_step", "la_generate", 
            "la_commit", "la_pool_lookup", "la_pool_insert", "la_get_state", "la_stats", "la_last_error",
            "la_rows_query", "la_build_rows", "la_attention_workspace", "la_attention", "la_linear_workspace",
            "la_linear", "la_packed_linear_bytes", "la_pack_linear", "la_linear_packed", "la_packed_weight_bytes",
-           "la_pack_weights", "la_profile", "la_profile_read", "la_attention_noalloc"]
+           "la_pack_weights", "la_profile", "la_profile_read", "la_attention_noalloc", "la_batch_bytes",
+           "la_batch_init", "la_batch_destroy", "la_batch_plan", "la_batch_step"]
 LA_LINEAR_STORE, LA_LINEAR_RESIDUAL, LA_LINEAR_SWIGLU, LA_LINEAR_F32 = 0, 1, 2, 3
 
 _lib = None
@@ -150,6 +156,11 @@ def load() -> C.CDLL:
         "la_pack_weights": ([P(la_model_dims), P(la_model), VP, VP], I32),
         "la_profile": ([VP, I32], I32),
         "la_profile_read": ([VP, P(la_profile_t)], I32),
+        "la_batch_bytes": ([P(la_model_dims), I32], C.c_uint64),
+        "la_batch_init": ([P(la_model_dims), P(la_model), I32, VP, C.c_uint64, VP, P(VP)], I32),
+        "la_batch_destroy": ([VP], None),
+        "la_batch_plan": ([I32, I32, I32, P(I32), P(I32), P(I32), P(I32)], I32),
+        "la_batch_step": ([VP, P(VP), I32, I32, P(I32), P(I32), P(la_batch_round)], I32),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -376,7 +387,57 @@ class Session:
         s = la_stats_t()
         _check(load().la_stats(self.ctx, C.byref(s)), self.ctx)
         return {"rounds": s.rounds, "tokens": s.tokens, "candidates": s.candidates, "accepted": s.accepted,
-                "hist": list(s.hist)}
+                "hist": list(s.hist), "paused": s.paused}
+
+
+# ----------------------------------------------------------------- batch
+
+
+def la_batch_plan(row_budget, S, base_rows, found):
+    """The occupancy throttle on host arrays; returns (cap, paused) lists."""
+    n = len(base_rows)
+    b, bp = _i32(base_rows)
+    f, fp = _i32(found)
+    cap = np.zeros(max(n, 1), np.int32)
+    paused = np.zeros(max(n, 1), np.int32)
+    _check(load().la_batch_plan(n, int(row_budget), int(S), bp, fp, cap.ctypes.data_as(C.POINTER(C.c_int32)),
+                                paused.ctypes.data_as(C.POINTER(C.c_int32))))
+    return [int(x) for x in cap[:n]], [int(x) for x in paused[:n]]
+
+
+class Batch:
+    """Stacked activations for up to max_rows rows of sessions sharing one model (la_batch_*)."""
+
+    def __init__(self, model: DeviceModel, max_rows=256, stream=None):
+        lib = load()
+        self.model = model
+        self.dims = dims_struct(model.dims)
+        nbytes = int(lib.la_batch_bytes(C.byref(self.dims), int(max_rows)))
+        if nbytes == 0:
+            raise LaError(LA_EINVAL, f"max_rows {max_rows} or dims not admitted")
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=model.embed.device)
+        self._mstruct = model.struct()
+        self.max_rows = int(max_rows)
+        self.stream = stream
+        self.b = C.c_void_p()
+        _check(lib.la_batch_init(C.byref(self.dims), C.byref(self._mstruct), int(max_rows), _ptr(self.workspace),
+                                 nbytes, _stream(stream), C.byref(self.b)))
+
+    def __del__(self):
+        if getattr(self, "b", None) and _lib is not None:
+            _lib.la_batch_destroy(self.b)
+            self.b = None
+
+    def la_batch_step(self, sessions, row_budget=0):
+        """One round of every session; returns (tokens per session, la_batch_round per session)."""
+        n = len(sessions)
+        ctxs = (C.c_void_p * n)(*[s.ctx for s in sessions])
+        buf = np.zeros((n, LA_MAX_EMIT), np.int32)
+        nout = np.zeros(n, np.int32)
+        info = (la_batch_round * n)()
+        _check(load().la_batch_step(self.b, ctxs, n, int(row_budget), buf.ctypes.data_as(C.POINTER(C.c_int32)),
+                                    nout.ctypes.data_as(C.POINTER(C.c_int32)), info))
+        return [list(map(int, buf[i, : nout[i]])) for i in range(n)], list(info)
 
 
 # ----------------------------------------------------------------- operators

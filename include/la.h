@@ -168,6 +168,7 @@ typedef struct la_stats_t {
   int64_t candidates;       /* sum of C over rounds */
   int64_t accepted;         /* sum of h over rounds */
   int32_t hist[LA_MAX_EMIT];/* rounds by emitted count (index = n_emit) */
+  int64_t paused;           /* rounds a batch ran without the lookahead branch (la_batch_step) */
 } la_stats_t;
 
 typedef struct la_state_t {
@@ -261,6 +262,77 @@ int la_verify(la_ctx* ctx, const float* logits, int32_t n_inp, const int32_t* ca
  * advanced and the tokens appended.  LA_ESTATE / LA_EPLAN / LA_EOVERFLOW
  * leave every piece of state unchanged. */
 int la_commit(la_ctx* ctx, const la_accept* acc);
+
+/* ------------------------------------------------------------- batching */
+
+/* Several requests decoded together ("Speculative Decoding" lesson, Chapter 7
+ * "Speculation Meets the Batch": concurrent requests share one read of the
+ * weights per step, and speculation may spend only the compute the batch's
+ * own rows leave free, throttled per request; "M7.3", 0x03B: each request
+ * keeps its own pool, window and K/V).  A batch owns the stacked activations
+ * of up to max_rows (<= 256) rows; the requests are ordinary contexts
+ * (la_init) created with the batch's dims and weights, on its stream.
+ *
+ * la_batch_bytes: device workspace bytes for max_rows rows (0 for bad dims
+ * or max_rows outside [1, 256]).
+ * la_batch_init: workspace (device, >= la_batch_bytes, 256-byte aligned) is
+ * borrowed until la_batch_destroy; weights as for la_init.  LA_EINVAL for
+ * bad dims / max_rows / weights, LA_EOVERFLOW for a short workspace. */
+typedef struct la_batch la_batch;
+uint64_t la_batch_bytes(const la_model_dims* dims, int32_t max_rows);
+int la_batch_init(const la_model_dims* dims, const la_model* weights, int32_t max_rows, void* workspace,
+                  uint64_t bytes, void* stream, la_batch** out);
+void la_batch_destroy(la_batch* batch);
+
+/* The occupancy throttle (Chapter 7 above: the step's row budget is shared;
+ * what the requests' own rows leave is spent on speculation, request by
+ * request, down to none).  Host only, pure.  For n requests, base_rows[i] is
+ * the rows of request i's round without candidates (its ordinary row plus
+ * its lookahead branch; 0: the request is not in this step) and found[i] the
+ * candidates its pool lookup returned.  Every request with base_rows > 0
+ * keeps its base rows; if their sum exceeds row_budget, requests from the
+ * last one backwards drop their lookahead branch (paused[i] = 1: one row)
+ * until the sum fits.  The remaining budget is dealt in S-row candidate
+ * blocks, one per request in turn in request order (request order is the
+ * priority order), to requests that are not paused, up to found[i]:
+ * cap[i] receives the candidates request i verifies.  Output arrays: host
+ * [n].  LA_EOVERFLOW when more requests are active than row_budget rows;
+ * LA_EINVAL for sizes out of range (n <= 256, 1 <= S < LA_MAX_N) or
+ * negative inputs. */
+int la_batch_plan(int32_t n, int32_t row_budget, int32_t S, const int32_t* base_rows, const int32_t* found,
+                  int32_t* cap, int32_t* paused);
+
+/* What one request's round did inside la_batch_step. */
+typedef struct la_batch_round {
+  int32_t Q;                /* packed rows (0: the request was finished) */
+  int32_t found;            /* candidates its pool lookup returned */
+  int32_t verified;         /* candidates verified (the throttle's cap) */
+  int32_t paused;           /* 1: the round ran without the lookahead branch */
+  int32_t h;                /* candidate tokens accepted */
+  int32_t reserved[3];
+} la_batch_round;
+
+/* One round for each of n requests ("M7.3", 0x06 loop: predict, verify,
+ * publish, per request) in one stacked forward.  ctx: host [n] distinct
+ * contexts with no round pending, all of the batch's dims, weights and
+ * stream and of one N (W, G and the other options may differ); requests
+ * that already hold max_new tokens are skipped.
+ * row_budget: the step's row budget (<= max_rows; <= 0: max_rows); the
+ * requests' rows are planned with la_batch_plan's rule.  A paused round
+ * verifies no candidates and leaves the window and the pool as they are;
+ * outputs stay exact either way (only the accepted lengths change).  The
+ * per-request arithmetic is that of the request's own la_step (the rows of a
+ * request give bitwise the same logits whatever rows share the step), so
+ * with a budget that throttles nothing every request's rounds are those of
+ * la_step.  out_tokens: host [n][LA_MAX_EMIT], request i's emitted tokens
+ * (after truncation at max_new) at row i; n_out: host [n] their counts;
+ * rinfo: host [n] or NULL.  Errors before the forward (LA_EINVAL for
+ * mismatched or repeated contexts, different N or a budget above max_rows, LA_ESTATE,
+ * LA_EOVERFLOW from any request or the plan) leave every request as it
+ * was; a failure while publishing leaves the requests before it published
+ * (their n_out set) and the rest unchanged. */
+int la_batch_step(la_batch* batch, la_ctx* const* ctx, int32_t n, int32_t row_budget, int32_t* out_tokens,
+                  int32_t* n_out, la_batch_round* rinfo);
 
 /* -------------------------------------------------------- pool and state */
 

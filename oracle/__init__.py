@@ -10,7 +10,8 @@ and notation:
 * "Break the Sequential Dependency of LLM Inference Using Lookahead Decoding"
   (paper summary: lossless claim, G = W practice, expected-accepted model);
 * "Speculative Decoding" lesson, Chapters 1-2 (general p/q rejection
-  sampling, the three-token vocabulary, the acceptance-rate arithmetic).
+  sampling, the three-token vocabulary, the acceptance-rate arithmetic) and
+  Chapter 7 (speculation under batch occupancy).
 
 Floating point is fp64 except where the method fixes a storage precision
 (the model's storage dtype at every stored activation, float32 logits).
@@ -30,4 +31,8 @@ Parity status per module:
   7B-width rounds), by textbook identities (softmax attention against an
   explicit loop, RoPE rotation invariants, RMSNorm scale invariance) and by
   the separate-forwards == dense-mask == autoregressive equalities.
+  batch -- the occupancy throttle ("Speculative Decoding" lesson, Chapter 7);
+  plan_rows pinned by closed forms for uniform requests, the chapter's worked
+  numbers and its defining properties (tests/test_oracle_batch.py); its
+  rounds are decode.LookaheadRequest's.
 """
