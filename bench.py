@@ -24,7 +24,10 @@ Also on the same line:
     256 MB Infinity Cache;
   * extra_workloads: the 7B-shaped workloads (512-token prompt, W=7 N=5 G=7;
     8192-token prompt, W=15 N=5 G=15 greedy and temperature-0.7 sampled over
-    five prompt/sampler seeds), each with the same round measurements.
+    five prompt/sampler seeds), each with the same round measurements; and
+    4, 8 and 16 of the 512-token requests decoded together by la_batch_step
+    under a 256-row budget (aggregate tokens/s against the same requests
+    batched autoregressively).
 """
 import argparse
 import json
@@ -63,6 +66,57 @@ def make_prompt(wl, dims, seed=0):
         prompt, copied = synthetic.copyspan_prompt(dims.vocab, wl["prompt"], seed)
         return prompt, copied
     return synthetic.markov_prompt(dims.vocab, wl["prompt"], seed), 0.0
+
+
+def measure_batch(model, dims, wl, n_req, budget, warmup, steps=0):
+    """n_req requests of one workload (prompt seeds 0..n_req-1) decoded together
+    by la_batch_step under a row budget: aggregate emitted tokens / wall time of
+    the timed steps (steps == 0: every step after the warmup until all requests
+    finish), the rows planned per step, and the same requests decoded
+    autoregressively in one batch (one row each) with the same kernels."""
+    import torch
+    import exact_lookahead_decoding_amd.la as la
+
+    def make(ar):
+        ss = [la.Session(model, make_prompt(wl, dims, seed)[0], W=wl["W"], N=wl["N"], G=wl["G"],
+                         max_new=wl["max_new"], ar_only=ar) for seed in range(n_req)]
+        return ss, la.Batch(model, max_rows=256)
+
+    res = {}
+    for ar in (False, True):
+        sessions, batch = make(ar)
+        for _ in range(warmup):
+            batch.la_batch_step(sessions, row_budget=budget)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        tokens = done = rows = paused = found = verified = 0
+        while steps == 0 or done < steps:
+            toks, info = batch.la_batch_step(sessions, row_budget=budget)
+            if all(i.Q == 0 for i in info):
+                break
+            tokens += sum(len(t) for t in toks)
+            rows += sum(i.Q for i in info)
+            paused += sum(i.paused for i in info)
+            found += sum(i.found for i in info)
+            verified += sum(i.verified for i in info)
+            done += 1
+        torch.cuda.synchronize()
+        secs = time.perf_counter() - t0
+        r = {"value": tokens / secs, "tokens": tokens, "steps": done, "ms_per_step": secs * 1e3 / done,
+             "tokens_per_step": tokens / done, "rows_per_step": rows / done}
+        if not ar:
+            r.update(paused_rounds=paused, candidates_found=found, candidates_verified=verified)
+            res.update(r)
+        else:
+            res["ar_batch_tokens_per_s"] = r["value"]
+            res["ar_batch_ms_per_step"] = r["ms_per_step"]
+            res["speedup_vs_ar_batch"] = res["value"] / r["value"]
+        log(f"  batch {n_req} ({'autoregressive' if ar else 'lookahead'}, budget {budget}): {tokens} tokens in "
+            f"{done} steps, {r['ms_per_step']:.3f} ms/step, {r['value']:.1f} tokens/s, "
+            f"{r['rows_per_step']:.1f} rows/step")
+        del sessions, batch
+        torch.cuda.empty_cache()
+    return res
 
 
 def step_roofline(model, dims, wl, tokens, steps, secs):
@@ -606,6 +660,15 @@ def main():
             for key in ("ar_tokens_per_s", "speedup_vs_ar", "step_roofline", "kernels", "init_prefill_ms"):
                 agg[key] = runs[0][key]
             extras[f"llama7b_long_w15n5g15_{mode}"] = agg
+        w7 = WORKLOADS["llama7b_w7n5g7"]
+        batches = {}
+        for n_req in (4, 8, 16):
+            log(f"llama7b_w7n5g7, {n_req} requests batched:")
+            batches[str(n_req)] = measure_batch(m7, d7, w7, n_req, 256, args.warmup, args.steps)
+        extras["batch_llama7b_w7n5g7"] = {
+            "desc": w7["desc"] + "; n requests (prompt seeds 0..n-1) per la_batch_step under a 256-row budget, "
+                                 "aggregate tokens/s, against the same requests batched autoregressively",
+            "requests": batches}
         line["extra_workloads"] = extras
     print(json.dumps(line), flush=True)
 
