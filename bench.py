@@ -302,9 +302,19 @@ def attention_op(reps=200, sets=16, p=1024, H=32, Hkv=32, N=5):
 ATTN_OPS = [dict(), dict(reps=24, sets=4, p=8192), dict(reps=64, sets=32, p=2048, H=64, Hkv=8, N=7)]
 ATTN_KEYS = ["lookahead_attn", "lookahead_attn_8192", "lookahead_attn_34b_gqa"]
 
-TRAFFIC_MD = os.path.join(ROOT, "profiles", "la_gemm_kernel_{wl}_hbm_traffic.md")
+TRAFFIC_MD = os.path.join(ROOT, "profiles", "{kernel}_{wl}_hbm_traffic.md")
 GEMM_SRC = os.path.join(ROOT, "exact_lookahead_decoding_amd", "csrc", "la_gemm.hip")
 COPY_BYTES = 1 << 30
+
+
+def gemm_kernel(wl_name):
+    """The GEMM kernel a workload's rounds run: la_gemm2_kernel (bf16, 32x32x16 MFMA) or la_gemm_kernel (fp32)."""
+    import synthetic
+    return "la_gemm2_kernel" if synthetic.PRESETS[WORKLOADS[wl_name]["model"]].dtype == "bf16" else "la_gemm_kernel"
+
+
+def _is_gemm(k):
+    return "la_gemm_kernel" in k or "la_gemm2_kernel" in k
 
 
 def _sha256(path):
@@ -316,7 +326,7 @@ def gemm_traffic(wl_name):
     """HBM bytes per round GEMM launch from the committed counter summary of the
     workload, or None when the GEMM source changed since the counters were taken."""
     try:
-        txt = open(TRAFFIC_MD.format(wl=wl_name)).read()
+        txt = open(TRAFFIC_MD.format(kernel=gemm_kernel(wl_name), wl=wl_name)).read()
     except OSError:
         return None
     vals = dict(l.split(":", 1) for l in txt.splitlines() if l.startswith(("traffic_bytes_per_launch:",
@@ -384,8 +394,7 @@ def _dispatches(db_or_csv):
 
 def _round_gemms(disp, n):
     """The last n GEMM dispatches before the calibration copy."""
-    gemm = [i for i, (k, _, _) in enumerate(disp) if k.startswith("la_gemm_kernel") or
-            k.startswith("void la_gemm_kernel") or "la_gemm_reduce_kernel" in k]
+    gemm = [i for i, (k, _, _) in enumerate(disp) if _is_gemm(k) or "la_gemm_reduce_kernel" in k]
     return [disp[i] for i in gemm[-n:]]
 
 
@@ -398,13 +407,13 @@ def trace_summary(trace_csv, run_json, out_md, cmd):
     # a GEMM launch with split K is the GEMM kernel plus its reduction kernel (or, for the
     # residual projections, nothing: the next RMSNorm folds the partials)
     names = [k for k, _, _ in disp]
-    g_idx = [i for i, k in enumerate(names) if "la_gemm_kernel" in k or "la_gemm_reduce_kernel" in k]
+    g_idx = [i for i, k in enumerate(names) if _is_gemm(k) or "la_gemm_reduce_kernel" in k]
     a_idx = [i for i, k in enumerate(names) if "la_attn_kernel" in k or "la_attn_merge_kernel" in k]
     last_copy = max([i for i, k in enumerate(names) if "copy" in k.lower()] or [len(names)])
     g_idx = [i for i in g_idx if i < last_copy]
     a_idx = [i for i in a_idx if i < last_copy]
     # HIP-event brackets cover a GEMM kernel and its reduction together
-    g_main = [i for i in g_idx if "la_gemm_kernel" in names[i]][-run["gemm_launches"]:]
+    g_main = [i for i in g_idx if _is_gemm(names[i])][-run["gemm_launches"]:]
     first = g_main[0]
     g_sel = [i for i in g_idx if i >= first]
     a_main = [i for i in a_idx if "la_attn_kernel" in names[i]][-run["attn_launches"]:]
@@ -422,6 +431,17 @@ def trace_summary(trace_csv, run_json, out_md, cmd):
              "| kernel | calls | total us | avg us |", "|---|---:|---:|---:|"]
     for k, (c, t) in sorted(per.items(), key=lambda x: -x[1][1]):
         lines.append(f"| `{k[:90]}` | {c} | {t:.0f} | {t / c:.2f} |")
+    # every kernel of the timed rounds: the dispatches from the first round GEMM up to the copy
+    span = collections.defaultdict(lambda: [0, 0.0])
+    for i in range(first, last_copy):
+        span[names[i]][0] += 1
+        span[names[i]][1] += disp[i][1] / 1e3
+    busy = sum(t for _, t in span.values())
+    lines += ["", f"All kernels of the {run['rounds']} rounds (per round; GPU busy {busy / run['rounds'] / 1e3:.3f} ms "
+              f"of {run['ms_per_round']:.3f} ms):", "",
+              "| kernel | calls per round | us per round | share of busy |", "|---|---:|---:|---:|"]
+    for k, (c, t) in sorted(span.items(), key=lambda x: -x[1][1]):
+        lines.append(f"| `{k[:90]}` | {c / run['rounds']:.1f} | {t / run['rounds']:.1f} | {t / busy * 100:.1f}% |")
     lines += ["", "| quantity | rocprofv3 trace | HIP events (same run) |", "|---|---:|---:|",
               f"| GEMM launches | {len(g_main)} | {run['gemm_launches']} |",
               f"| GEMM average launch (us) | {g_us:.2f} | {run['gemm_avg_launch_us']:.2f} |",
@@ -445,10 +465,11 @@ def pmc_summary(fetch_db, write_db, run_json, wl_name):
     for counter, db in (("FETCH_SIZE", fetch_db), ("WRITE_SIZE", write_db)):
         disp = _dispatches(db)
         names = [k for k, _, _ in disp]
-        copies = [i for i, k in enumerate(names) if "copy" in k.lower()]
+        # the calibration copies are the process's last three copy dispatches
+        copies = [i for i, k in enumerate(names) if "copy" in k.lower()][-3:]
         end = copies[0] if copies else len(names)
-        g = [i for i in range(end) if "la_gemm_kernel" in names[i] or "la_gemm_reduce_kernel" in names[i]]
-        main = [i for i in g if "la_gemm_kernel" in names[i]][-run["gemm_launches"]:]
+        g = [i for i in range(end) if _is_gemm(names[i]) or "la_gemm_reduce_kernel" in names[i]]
+        main = [i for i in g if _is_gemm(names[i])][-run["gemm_launches"]:]
         sel = [i for i in g if i >= main[0]]
         tot = sum(disp[i][2].get(counter, 0.0) for i in sel)
         copy = max(disp[i][2].get(counter, 0.0) for i in copies) if copies else 0.0
@@ -477,7 +498,7 @@ def pmc_summary(fetch_db, write_db, run_json, wl_name):
         "```",
         "",
         f"The run makes {run['rounds']} lookahead rounds after prefill and warmup, then copies a "
-        f"{run['copy_bytes'] >> 20} MiB buffer three times.  Round GEMM launches: the last {n} `la_gemm_kernel` "
+        f"{run['copy_bytes'] >> 20} MiB buffer three times.  Round GEMM launches: the last {n} `{gemm_kernel(wl_name)}` "
         "dispatches before the copy (with the split-K reductions that follow them).",
         "",
         "| quantity | value |",
@@ -570,7 +591,7 @@ def main():
         return
     if args.pmc_summary:
         md = pmc_summary(*args.pmc_summary, args.workload)
-        open(TRAFFIC_MD.format(wl=args.workload), "w").write(md)
+        open(TRAFFIC_MD.format(kernel=gemm_kernel(args.workload), wl=args.workload), "w").write(md)
         print(md)
         return
     if args.profile_rounds:
@@ -609,8 +630,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": k["gemm_GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": k["gemm_GBps"] / HBM_PEAK_GBS,
                      "traffic": traffic,
-                     "kernel": "la_gemm_kernel (+ split reduction): every projection, MLP and LM-head launch of "
-                               "the timed rounds",
+                     "kernel": gemm_kernel(args.workload) + " (+ split reduction): every projection, MLP and "
+                               "LM-head launch of the timed rounds",
                      "avg_launch_us": k["gemm_avg_launch_us"], "algorithmic_bytes_per_launch":
                          k["gemm_bytes_per_launch"], "launches": k["gemm_launches"],
                      "share_of_round": k["share_of_round_gemm"]},
