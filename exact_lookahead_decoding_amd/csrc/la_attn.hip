@@ -63,6 +63,7 @@
 #define CH 32          // keys per chunk
 #define NEG_INF (-__builtin_inff())
 #define RESCALE 8.0f   // log2 units: the reference maximum moves only past this
+#define M_NONE (-1e30f) // reference maximum of a row that has seen no key (finite: 2^(s - M_NONE) never overflows to NaN)
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -129,6 +130,7 @@ typedef LdsT<16>::T V4u;
 
 template <int DH> struct AttnT<bf16_t, DH> {
   static constexpr int ROWB = DH * 2, KS = DH / 32, NDT = DH / 16;
+  static constexpr int QKN = KS;                      // QK^T MFMAs per 16 keys
   struct QF { V4u p[KS]; };                           // Q[row c][32 s + 8 g ..]
   struct KF { V4u p[2][KS]; };                        // K[key 16 kg + .][32 s + 8 g ..]
   struct VF { LdsT<8>::T p[NDT][2]; };                // V^T operand halves (transposed reads)
@@ -221,6 +223,7 @@ template <int DH> struct AttnT<bf16_t, DH> {
 // fp32: 16x16x4 MFMA; lane (g, c) holds 16-byte pieces LP*g .. of its rows.
 template <int DH> struct AttnT<float, DH> {
   static constexpr int ROWB = DH * 4, PIECES = ROWB / 16, LP = PIECES / 4, NDT = DH / 16, VB = NDT * 4;
+  static constexpr int QKN = 4 * LP;                  // QK^T MFMAs per 16 keys
   struct QF { V4u p[LP]; };
   struct KF { V4u p[2][LP]; };
   typedef Words<NDT> VV;
@@ -305,29 +308,42 @@ __device__ __forceinline__ float row4_sum(float x) {
 }
 
 // Softmax half of one online chunk step for the lane's row.  s[e]: raw QK
-// score of slot e (-inf: not visible).  Updates the reference m and l, leaves
-// p in s and returns the factor the running O must be scaled by before P V is
-// added.  A row that has seen no key yet keeps its state (factor 1, p = 0).
-// Straight-line code: a chunk's tiles interleave freely.
+// score of slot e (-inf: not visible).  The reference m (the same in the
+// row's four lanes) moves to the chunk's row maximum only when that exceeds
+// it by more than RESCALE; p = 2^(s sl2 - m'); the lane keeps its own
+// running sum l' = l 2^(m - m') + sum of its p (fixed order), the row's sum
+// being the four lanes' sum at the end.  Leaves p in s and returns the factor
+// 2^(m - m') the running O must be scaled by before P V is added (exactly 1
+// when m stays; a row that has seen no key keeps m = M_NONE and p = 0).
+__device__ __forceinline__ float row_max8(const float (&s)[8]) {
+  return fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+}
+// The reference moves when fma(max, sl2, -m) > RESCALE, a test monotone in
+// the maximum, so a row moves exactly when one of its lanes' own
+// maxima passes it: the ring's usual-case test and this one agree row by row.
+__device__ __forceinline__ bool ref_moves(float mx, float sl2, float m) {
+  return __builtin_fmaf(mx, sl2, -m) > RESCALE;
+}
 __device__ __forceinline__ float chunk_softmax(float (&s)[8], float sl2, float& m, float& l) {
-  float mx = s[0];
+  const float mr = row4_max(row_max8(s));
+  const float mn = ref_moves(mr, sl2, m) ? mr * sl2 : m;
+  const float wa = ex2(m - mn);
 #pragma unroll
-  for (int e = 1; e < 8; ++e) mx = fmaxf(mx, s[e]);
-  const float mc = row4_max(mx) * sl2;
-  const float mn = (m == NEG_INF || mc > m + RESCALE) ? mc : m;
-  const bool live = mn != NEG_INF;
-  const float wa = (live && mn != m) ? ex2(m - mn) : 1.f;
-  // -mn, or -inf for a row with nothing visible (its scores are all -inf, so p = 2^-inf = 0)
-  const float nm = live ? -mn : NEG_INF;
-  float ls = 0.f;
+  for (int e = 0; e < 8; ++e) s[e] = ex2(__builtin_fmaf(s[e], sl2, -mn));
+  float ls = s[0];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    s[e] = ex2(__builtin_fmaf(s[e], sl2, nm));
-    ls += s[e];
-  }
-  l = __builtin_fmaf(l, wa, row4_sum(ls));
-  m = live ? mn : m;
+  for (int e = 1; e < 8; ++e) ls += s[e];
+  l = __builtin_fmaf(l, wa, ls);
+  m = mn;
   return wa;
+}
+
+// keep a P^T operand where it is computed (an empty asm the compiler must
+// see its value at)
+__device__ __forceinline__ void tie_pp(bf16x8& p) { asm volatile("" : "+v"(p)); }
+template <typename PPT> __device__ __forceinline__ void tie_pp(PPT& p) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) asm volatile("" : "+v"(p.p[e]));
 }
 
 template <int NDT> __device__ __forceinline__ void scale_o(f32x4* O, float wa) {
@@ -471,18 +487,18 @@ __global__ void __launch_bounds__(64 * NW) la_attn_kernel(LaAttnArgs a) {
   f32x4 O[TPW][NDT];
 #pragma unroll
   for (int u = 0; u < TPW; ++u) {
-    M[u] = NEG_INF;
+    M[u] = M_NONE;
     L[u] = 0.f;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) O[u][dt] = f32x4{0, 0, 0, 0};
   }
 
-  // committed chunks through the ring, in decreasing position, one set of
-  // K / V fragment registers: K of chunk i + 1 is read from LDS once the
-  // QK^T MFMAs of chunk i have their operands, V of chunk i + 1 once its P V
-  // MFMAs have theirs, so the reads overlap the softmax and the products.
-  // One barrier per chunk: chunk i + 1 has landed, and every wave has read
-  // chunk i, whose slot is then refilled.
+  // committed chunks through the ring, in decreasing position, software
+  // pipelined: step i issues the QK^T MFMAs of chunk i + 1 (its K fragments
+  // were read in step i - 1) ahead of chunk i's softmax, so the products run
+  // while the vector ALU works; then chunk i's P V.  One set of K and one of V
+  // fragment registers.  One barrier per chunk: chunk i + 2 has landed and
+  // every wave has read chunk i + 1 (K and V), whose slot is then refilled.
   const typename AT::Lofs lofs = AT::lane_ofs(g, c16);
   auto slot_base = [&](int i) __attribute__((always_inline)) {
     return (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr(ring) + (uint32_t)(i % D) * SLOT);
@@ -508,52 +524,117 @@ __global__ void __launch_bounds__(64 * NW) la_attn_kernel(LaAttnArgs a) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) pmin = min(pmin, __shfl_xor(pmin, o, 64));
     pmin = __builtin_amdgcn_readfirstlane(pmin);
+    // chunks 0 .. jm - 1 hold a key past some row of the wave: only they are masked
+    const int jm = min(nring, max(0, r_hi - (pmin + 1) / CH));
     if (D - 1 < nring) issue(D - 1);
     AT::load_k_at(kf, slot_base(0), lofs, g, c16);
     AT::load_v_at(vf, slot_base(0) + CHB, lofs, g, c16);
-    for (int i = 0; i < nring; ++i) {
-      const int x0 = CH * (r_hi - 1 - i);
-      float sc[TPW][8];
+    float sc[TPW][8];
+    auto qk_all = [&](float (&s)[TPW][8]) __attribute__((always_inline)) {
 #pragma unroll
       for (int u = 0; u < TPW; ++u)
 #pragma unroll
         for (int kg = 0; kg < 2; ++kg) {
           const f32x4 s4 = AT::qk(kf, kg, qf[u]);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) sc[u][4 * kg + r] = s4[r];
+          for (int r = 0; r < 4; ++r) s[u][4 * kg + r] = s4[r];
         }
-      const bool more = i + 1 < nring;
-      if (more) {
-        ring_wait<PW, D - 1>(min(D - 2, nring - 2 - i));   // chunk i + 1 landed
-        ring_barrier();                           // every wave has read chunk i: its slot is free
-        if (i + D < nring) issue(i + D);
-        AT::load_k_at(kf, slot_base(i + 1), lofs, g, c16);
-      }
-      if (x0 + CH - 1 > pmin) {                   // some key of the chunk lies past some row
+    };
+    qk_all(sc);
+    if (nring > 1) {
+      ring_wait<PW, D - 1>(min(D - 2, nring - 2));  // chunk 1 landed
+      ring_barrier();                               // every wave has read chunk 0: its slot is free
+      if (D < nring) issue(D);
+      AT::load_k_at(kf, slot_base(1), lofs, g, c16);
+    }
+    auto step = [&](int i, auto masked, auto last) __attribute__((always_inline)) {
+      float sn[TPW][8];
+      if constexpr (!decltype(last)::value) qk_all(sn);   // chunk i + 1, in flight during the softmax
+      if constexpr (decltype(masked)::value) {
+        const int x0 = CH * (r_hi - 1 - i);
 #pragma unroll
         for (int u = 0; u < TPW; ++u)
 #pragma unroll
           for (int e = 0; e < 8; ++e) sc[u][e] = x0 + slot_key(g, e) <= pos[u] ? sc[u][e] : NEG_INF;
       }
+      // the usual case first: no row's maximum moves (p against the current
+      // reference, the sums grow by the chunk's); if some row's would, the
+      // chunk goes through chunk_softmax instead (same arithmetic where the
+      // reference stays, so a row's bits do not depend on the other rows)
       typename AT::PP pp[TPW];
-      float wa[TPW];
-      bool rescale = false;
+      float ps[TPW][8], lsum[TPW];
+      bool moves = false;
 #pragma unroll
       for (int u = 0; u < TPW; ++u) {
-        wa[u] = chunk_softmax(sc[u], sl2, M[u], L[u]);
-        pp[u] = AT::prep(sc[u]);
-        rescale |= wa[u] != 1.f;
+        // the exponents s sl2 - m; their maximum is fma(max s, sl2, -m) (a
+        // monotone map), so the test is ref_moves' on this lane's scores
+        float t[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) t[e] = __builtin_fmaf(sc[u][e], sl2, -M[u]);
+        moves |= row_max8(t) > RESCALE;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ps[u][e] = ex2(t[e]);
+        float ls = ps[u][0];                        // = 0 + p0 (p >= +0)
+#pragma unroll
+        for (int e = 1; e < 8; ++e) ls += ps[u][e];
+        lsum[u] = L[u] + ls;
+        pp[u] = AT::prep(ps[u]);
       }
-      if (__ballot(rescale) != 0ull) {            // a running maximum moved: O * wa (else O * 1 = O)
+      if constexpr (!decltype(last)::value) {
+        // one QK^T MFMA, then a share of the softmax's vector instructions
 #pragma unroll
-        for (int u = 0; u < TPW; ++u) scale_o<NDT>(O[u], wa[u]);
+        for (int k = 0; k < 2 * TPW * AT::QKN; ++k) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        }
       }
+      // computed here, before the branch, in both cases (the compiler would
+      // otherwise sink them past it, away from the QK^T MFMAs)
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
+      for (int u = 0; u < TPW; ++u) {
+        tie_pp(pp[u]);
+        asm volatile("" : "+v"(lsum[u]));
+      }
+      auto pv_all = [&]() __attribute__((always_inline)) {
 #pragma unroll
-        for (int u = 0; u < TPW; ++u) O[u][dt] = AT::pv(vf, dt, pp[u], O[u][dt]);
-      if (more) AT::load_v_at(vf, slot_base(i + 1) + CHB, lofs, g, c16);
-    }
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int u = 0; u < TPW; ++u) O[u][dt] = AT::pv(vf, dt, pp[u], O[u][dt]);
+      };
+      if (__ballot(moves) != 0ull) {                // some reference maximum moves: the full step, O * wa
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+          const float wa = chunk_softmax(sc[u], sl2, M[u], L[u]);
+          pp[u] = AT::prep(sc[u]);
+          scale_o<NDT>(O[u], wa);
+        }
+        pv_all();
+      } else {
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) L[u] = lsum[u];
+        pv_all();
+      }
+      if constexpr (!decltype(last)::value) {
+        AT::load_v_at(vf, slot_base(i + 1) + CHB, lofs, g, c16);
+        if (i + 2 < nring) {
+          ring_wait<PW, D - 1>(min(D - 2, nring - 3 - i));   // chunk i + 2 landed
+          ring_barrier();                           // every wave has read chunk i + 1: its slot is free
+          if (i + 1 + D < nring) issue(i + 1 + D);
+          AT::load_k_at(kf, slot_base(i + 2), lofs, g, c16);
+        }
+#pragma unroll
+        for (int u = 0; u < TPW; ++u)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sc[u][e] = sn[u][e];
+      }
+    };
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+    int i = 0;
+    for (; i < min(jm, nring - 1); ++i) step(i, T_{}, F_{});
+    for (; i < nring - 1; ++i) step(i, F_{}, F_{});
+    if (jm >= nring) step(nring - 1, T_{}, T_{});
+    else step(nring - 1, F_{}, T_{});
   };
   // chunks past shared_end, from the tail stage (the highest positions of the split: they come first)
   auto tail_part = [&]() __attribute__((always_inline)) {
@@ -747,6 +828,11 @@ __global__ void __launch_bounds__(64 * NW) la_attn_kernel(LaAttnArgs a) {
   dma_wait<0>();                                   // no DMA may land after the workgroup has left
 
   // results: lane (g, c) holds rows c, accumulator rows 4 g + r of every output tile
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    L[u] = row4_sum(L[u]);
+    if (M[u] == M_NONE) M[u] = NEG_INF;
+  }
 #pragma unroll
   for (int u = 0; u < TPW; ++u) {
     if (!rvalid[u]) continue;

@@ -104,7 +104,9 @@ def test_7b_8192_sampled_rounds_replay_through_oracle(m7, seed):
     s = la.Session(m, prompt, W=W, N=N, G=G, max_new=256, verify_mode=la.LA_VERIFY_SAMPLE, temperature=T, seed=seed,
                    pool_from_prompt=True)
     checked = with_cands = 0
-    for r in range(10):
+    for r in range(48):
+        if checked >= 10 and with_cands > 0:      # ten rounds, at least one of them verifying candidates
+            break
         st = s.la_get_state(with_window=False)
         x_t = st["output"][-1]
         cands = s.la_pool_lookup(x_t) if st["warm"] else []
