@@ -520,6 +520,89 @@ def pmc_summary(fetch_db, write_db, run_json, wl_name):
     ])
 
 
+def attn_summary(trace_csv, fetch_db, write_db, run_jsonl, out_md):
+    """Kernel time and HBM traffic of the isolated attention op per shape, from a
+    kernel trace and a FETCH_SIZE and a WRITE_SIZE run of
+    `--attention-op-only --calibrate` (each launch: la_attn_kernel and, with
+    several key splits, la_attn_merge_kernel); shapes are told apart by the
+    attention kernel's grid, in the order the op runs them."""
+    runs = [json.loads(l) for l in open(run_jsonl) if l.startswith("{")]
+
+    def per_shape(disp, value):
+        # consecutive attention dispatches of one grid size form a shape; a merge follows its kernel
+        shapes, cur, grid = [], None, None
+        for i, (k, dur, ctr, gsz) in enumerate(disp):
+            if "la_attn_kernel" in k:
+                if gsz != grid:
+                    cur = {"grid": gsz, "attn": [], "merge": []}
+                    shapes.append(cur)
+                    grid = gsz
+                cur["attn"].append(value(dur, ctr))
+            elif "la_attn_merge_kernel" in k and cur is not None:
+                cur["merge"].append(value(dur, ctr))
+        return shapes
+
+    import csv
+    tr = []
+    with open(trace_csv) as f:
+        for r in csv.DictReader(f):
+            tr.append((int(r["Dispatch_Id"]), r["Kernel_Name"], int(r["End_Timestamp"]) - int(r["Start_Timestamp"]),
+                       {}, int(r["Grid_Size_X"]) if "Grid_Size_X" in r else int(r.get("Grid_Size", 0))))
+    tr.sort()
+    t_shapes = per_shape([x[1:] for x in tr], lambda d, c: d / 1e3)
+
+    def pmc(db, counter):
+        import sqlite3
+        con = sqlite3.connect(db)
+        rows = {}
+        for d, k, c, v, gsz in con.execute("select dispatch_id, kernel_name, counter_name, value, grid_size "
+                                           "from counters_collection"):
+            e = rows.setdefault(d, [k, 0, {}, gsz])
+            e[2][c] = e[2].get(c, 0.0) + v
+        disp = [tuple(rows[d]) for d in sorted(rows)]
+        copies = [i for i, x in enumerate(disp) if "copy" in x[0].lower()][-3:]
+        cal = COPY_BYTES / (max(disp[i][2].get(counter, 0.0) for i in copies) * 1024.0)
+        return per_shape(disp, lambda d, c: c.get(counter, 0.0) * 1024.0 * cal), cal
+
+    f_shapes, f_cal = pmc(fetch_db, "FETCH_SIZE")
+    w_shapes, w_cal = pmc(write_db, "WRITE_SIZE")
+    mean = lambda v: sum(v) / len(v) if v else 0.0  # noqa: E731
+    lines = ["# Lookahead-mask attention op: kernel time and HBM traffic per shape", "",
+             "Commands (run from /tmp with TMPDIR=/tmp on one MI355X; each counter in a run of its own):", "", "```",
+             "python3 bench.py --attention-op-only --calibrate > out/run.jsonl",
+             "rocprofv3 --kernel-trace --stats --output-format csv -d out/trace -o a -- "
+             "python3 bench.py --attention-op-only --calibrate",
+             "rocprofv3 --pmc FETCH_SIZE -d out/pmc_fetch -o f -- python3 bench.py --attention-op-only --calibrate",
+             "rocprofv3 --pmc WRITE_SIZE -d out/pmc_write -o w -- python3 bench.py --attention-op-only --calibrate",
+             "python3 bench.py --attn-summary out/trace/a_kernel_trace.csv out/pmc_fetch/f_results.db "
+             "out/pmc_write/w_results.db out/run.jsonl profiles/<this file>", "```", "",
+             "Each shape runs eager warm-up launches, then HIP-graph replays of one launch per rotating input set "
+             "(more bytes than the 256 MB Infinity Cache); the trace and counter averages below take every launch "
+             "of the shape.  Counters are scaled by what they read for a plain 1 GiB copy "
+             f"(FETCH_SIZE x{f_cal:.3f}, WRITE_SIZE x{w_cal:.3f}).", "",
+             "| shape | launches | attention kernel avg us | merge avg us | kernel + merge us | HIP events us "
+             "(op timing, graph) | algorithmic MB | HBM read MB | HBM write MB | traffic / algorithmic | "
+             "achieved GB/s (events) | % of 8 TB/s |",
+             "|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|"]
+    for i, run in enumerate(runs):
+        ts = t_shapes[i] if i < len(t_shapes) else {"attn": [], "merge": []}
+        fs = f_shapes[i] if i < len(f_shapes) else {"attn": [], "merge": []}
+        ws = w_shapes[i] if i < len(w_shapes) else {"attn": [], "merge": []}
+        ka, km = mean(ts["attn"]), mean(ts["merge"])
+        rd = mean(fs["attn"]) + mean(fs["merge"])
+        wr = mean(ws["attn"]) + mean(ws["merge"])
+        alg = run["algorithmic_bytes"]
+        lines.append(f"| {run['workload']} | {len(ts['attn'])} | {ka:.2f} | {km:.2f} | {ka + km:.2f} | "
+                     f"{run['avg_us']:.2f} | {alg / 1e6:.2f} | {rd / 1e6:.2f} | {wr / 1e6:.2f} | "
+                     f"{(rd + wr) / alg:.2f} | {run['achieved_GBps']:.0f} | {run['frac'] * 100:.1f} |")
+    lines += ["", "Algorithmic bytes: the committed K/V read once, each packed row's K/V, Q in and O out (bf16).  "
+              "Traffic above it is the split states' round trip (fp32 partial O, m and l of every key split, "
+              "written by the attention kernel and read by the merge) and re-reads.", ""]
+    md = "\n".join(lines)
+    open(out_md, "w").write(md)
+    print(md)
+
+
 def cpu_baseline(wl_name, rounds=1, prefix=32):
     """The oracle as it stands, on host cores, over a bounded slice of the workload:
     the same W/N/G and model widths, the first `prefix` tokens of the prompt
@@ -578,6 +661,10 @@ def main():
     ap.add_argument("--pool-from-prompt", action="store_true",
                     help="seed the n-gram pool with the prompt's n-grams (lookahead sessions)")
     ap.add_argument("--attention-op-only", action="store_true", help="time only the isolated attention op")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="with --attention-op-only: end with three copies of COPY_BYTES (counter calibration)")
+    ap.add_argument("--attn-summary", nargs=5, metavar=("TRACE_CSV", "FETCH_DB", "WRITE_DB", "RUN_JSONL", "OUT_MD"),
+                    help="write the attention op's kernel-time and HBM-traffic summary under profiles/")
     ap.add_argument("--profile-rounds", type=int, default=0,
                     help="run only N rounds of --workload with kernel events (for rocprofv3 runs)")
     ap.add_argument("--trace-summary", nargs=3, metavar=("TRACE_CSV", "RUN_JSON", "OUT_MD"))
@@ -597,11 +684,20 @@ def main():
     if args.profile_rounds:
         profile_rounds(args.workload, args.profile_rounds)
         return
+    if args.attn_summary:
+        attn_summary(*args.attn_summary)
+        return
     if args.attention_op_only:
         import torch
         torch.cuda.set_device(0)
         for kw in ATTN_OPS:
             print(json.dumps(attention_op(**kw)), flush=True)
+        if args.calibrate:
+            src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+            dst = torch.empty_like(src)
+            for _ in range(3):
+                dst.copy_(src)
+            torch.cuda.synchronize()
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the lookahead round runs on a single MI355X (got --gpus {args.gpus}); "
