@@ -14,10 +14,12 @@
 //     splits of `spl` chunks (la_attention_spl);
 //   * inside a split the chunks are taken in decreasing position with the
 //     online softmax: the reference maximum m' moves to the chunk's exact
-//     maximum only when that exceeds it by more than RESCALE, the running
-//     sums are scaled by 2^(m - m'), p = 2^(s - m'), l' = l * 2^(m - m') +
-//     sum p (fixed lane order), and O' = O * 2^(m - m') + V^T P^T
-//     accumulated by MFMA over a fixed key -> slot assignment;
+//     maximum only when fma(max, scale, -m) exceeds RESCALE (a row that has
+//     seen nothing keeps the finite M_NONE), p = 2^(s - m'), each of a row's
+//     four lanes keeps its own running sum l' = l * 2^(m - m') + its p in a
+//     fixed order (the row's sum is the four lanes' sum at the end), and
+//     O' = O * 2^(m - m') + V^T P^T accumulated by MFMA over a fixed key ->
+//     slot assignment;
 //   * the splits' states are folded in split order by a small merge
 //     kernel, then O / l.
 // A chunk's scores are the same numbers whichever rows share the MFMA, and
@@ -37,9 +39,9 @@
 //     LDS by global_load_lds DMA (16-byte pieces XOR-swizzled by row), one
 //     barrier per chunk.  The DMA is issued as inline asm and the LDS reads
 //     are ordinary loads, so the compiler places only LDS waits on them and
-//     the ring orders the DMA with explicit vmcnt waits.  One set of
-//     fragment registers: K of chunk i + 1 is read once the QK^T MFMAs of
-//     chunk i have their operands, V once its P V MFMAs have theirs;
+//     the ring orders the DMA with explicit vmcnt waits.  Software
+//     pipelined: the QK^T MFMAs of chunk i + 1 are issued beside chunk i's
+//     softmax (one set of K and one of V fragment registers);
 //   * QK: S^T = K Q^T with 16x16x32 bf16 MFMA (one query row per lane
 //     column, softmax statistics stay in-lane); PV: O^T += V^T P^T, the V^T
 //     operand read straight from the row-major chunk with ds_read_b64_tr_b16
