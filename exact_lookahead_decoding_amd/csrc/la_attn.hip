@@ -201,6 +201,16 @@ template <int DH> struct AttnT<bf16_t, DH> {
       acc = mfma_bf16_32(__builtin_bit_cast(bf16x8, k.p[kg][s]), __builtin_bit_cast(bf16x8, q.p[s]), acc);
     return acc;
   }
+  // both 16-key halves, their accumulation chains interleaved (each in the order of qk)
+  static __device__ __forceinline__ void qk2(const KF& k, const QF& q, f32x4& a0, f32x4& a1) {
+    a0 = f32x4{0, 0, 0, 0};
+    a1 = f32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      a0 = mfma_bf16_32(__builtin_bit_cast(bf16x8, k.p[0][s]), __builtin_bit_cast(bf16x8, q.p[s]), a0);
+      a1 = mfma_bf16_32(__builtin_bit_cast(bf16x8, k.p[1][s]), __builtin_bit_cast(bf16x8, q.p[s]), a1);
+    }
+  }
   typedef bf16x8 PP;
   // P^T operand: p of slot e rounded to bf16 (nearest even)
   static __device__ __forceinline__ PP prep(const float* ps) {
@@ -277,6 +287,17 @@ template <int DH> struct AttnT<float, DH> {
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc = mfma_f32_4(__uint_as_float(k.p[kg][s][j]), __uint_as_float(q.p[s][j]), acc);
     return acc;
+  }
+  static __device__ __forceinline__ void qk2(const KF& k, const QF& q, f32x4& a0, f32x4& a1) {
+    a0 = f32x4{0, 0, 0, 0};
+    a1 = f32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int s = 0; s < LP; ++s)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        a0 = mfma_f32_4(__uint_as_float(k.p[0][s][j]), __uint_as_float(q.p[s][j]), a0);
+        a1 = mfma_f32_4(__uint_as_float(k.p[1][s][j]), __uint_as_float(q.p[s][j]), a1);
+      }
   }
   struct PP { float p[8]; };
   static __device__ __forceinline__ PP prep(const float* ps) {
@@ -395,6 +416,9 @@ __global__ void __launch_bounds__(64 * NW) la_attn_kernel(LaAttnArgs a) {
   static_assert(D >= 2 && (D - 1) * PW < 64, "ring depth within the vmcnt range");
   constexpr int RPB = 1024 / ROWB;               // rows per DMA instruction
   constexpr int PIECES = ROWB / 16;
+  // with four or more slots the ring refills a chunk's slot one step late,
+  // so the per-chunk barrier need not wait for the LDS reads just issued
+  constexpr bool LAG = D >= 4;
   extern __shared__ __attribute__((aligned(1024))) char lds[];
 
   // block -> (XCD, KV head, split, row group); the highest splits (tail chunks) first
@@ -534,19 +558,21 @@ __global__ void __launch_bounds__(64 * NW) la_attn_kernel(LaAttnArgs a) {
     float sc[TPW][8];
     auto qk_all = [&](float (&s)[TPW][8]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int u = 0; u < TPW; ++u)
+      for (int u = 0; u < TPW; ++u) {
+        f32x4 s0, s1;
+        AT::qk2(kf, qf[u], s0, s1);
 #pragma unroll
-        for (int kg = 0; kg < 2; ++kg) {
-          const f32x4 s4 = AT::qk(kf, kg, qf[u]);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) s[u][4 * kg + r] = s4[r];
+        for (int r = 0; r < 4; ++r) {
+          s[u][r] = s0[r];
+          s[u][4 + r] = s1[r];
         }
+      }
     };
     qk_all(sc);
     if (nring > 1) {
       ring_wait<PW, D - 1>(min(D - 2, nring - 2));  // chunk 1 landed
       ring_barrier();                               // every wave has read chunk 0: its slot is free
-      if (D < nring) issue(D);
+      if (!LAG && D < nring) issue(D);
       AT::load_k_at(kf, slot_base(1), lofs, g, c16);
     }
     auto step = [&](int i, auto masked, auto last) __attribute__((always_inline)) {
@@ -619,9 +645,16 @@ __global__ void __launch_bounds__(64 * NW) la_attn_kernel(LaAttnArgs a) {
       if constexpr (!decltype(last)::value) {
         AT::load_v_at(vf, slot_base(i + 1) + CHB, lofs, g, c16);
         if (i + 2 < nring) {
-          ring_wait<PW, D - 1>(min(D - 2, nring - 3 - i));   // chunk i + 2 landed
-          ring_barrier();                           // every wave has read chunk i + 1: its slot is free
-          if (i + 1 + D < nring) issue(i + 1 + D);
+          if constexpr (LAG) {
+            // chunks up to i - 1 + D issued; chunk i's reads were used before the barrier
+            ring_wait<PW, D - 1>(min(D - 3, nring - 3 - i));   // chunk i + 2 landed
+            slot_barrier();                         // every wave has used chunk i: its slot is free
+            if (i + D < nring) issue(i + D);
+          } else {
+            ring_wait<PW, D - 1>(min(D - 2, nring - 3 - i));   // chunk i + 2 landed
+            ring_barrier();                         // every wave has read chunk i + 1: its slot is free
+            if (i + 1 + D < nring) issue(i + 1 + D);
+          }
           AT::load_k_at(kf, slot_base(i + 2), lofs, g, c16);
         }
 #pragma unroll

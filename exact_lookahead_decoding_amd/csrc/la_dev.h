@@ -28,6 +28,12 @@ template <int N> __device__ __forceinline__ void wait_vm() {
 __device__ __forceinline__ void ring_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
+// The same without the LDS wait, where the slot about to be refilled was read
+// (and its values used) before the barrier: LDS reads issued just before it
+// from another slot stay in flight across it.
+__device__ __forceinline__ void slot_barrier() {
+  asm volatile("s_barrier" ::: "memory");
+}
 
 // LDS reads of the ring are inline asm: the compiler then sees no LDS load
 // that could alias an in-flight stage DMA (it would wait for all of them),
