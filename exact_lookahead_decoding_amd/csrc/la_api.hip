@@ -376,6 +376,49 @@ struct Seg {
   int nb, maxp, n_direct, cache_row0, shared_end, max_pos, n_logit;
 };
 
+// Device tables of a forward whose per-request passes (rotary placement and
+// attention) run as one launch per layer for all requests: entry i is
+// request i, with layer 0's cache pointers and the distance between layers.
+struct SegTables {
+  const LaAttnSeg* attn;
+  const LaPostSeg* post;
+  LaAttnMulti shape;
+};
+
+// One request's attention arguments for layer l (the launcher completes the rest).
+static LaAttnArgs seg_attn_args(la_ctx* c, const FwdBufs& B, const Seg& g, int l) {
+  la_ctx* s = g.s;
+  const int esz = c->esz, qd = c->H * c->dh;
+  const size_t skvl = (size_t)s->Hkv * s->t_cap * s->dh;
+  const size_t swsl = (size_t)s->Hkv * s->ws_cap * s->dh;
+  LaAttnArgs at{};
+  at.q = (char*)B.q + (size_t)g.r0 * qd * esz;
+  at.o = (char*)B.o + (size_t)g.r0 * qd * esz;
+  at.part_o = s->attn_po; at.part_ml = s->attn_pml; at.max_splits = s->parts;
+  at.pos = g.pos; at.branch = g.branch; at.path = g.path; at.path_len = g.path_len;
+  at.tile_meta = g.tile_meta; at.tile_path = g.tile_path;
+  at.Q = g.M; at.H = c->H; at.Hkv = c->Hkv; at.dh = c->dh; at.T_cap = s->t_cap; at.ws_cap = s->ws_cap;
+  at.maxp = g.maxp;
+  at.shared_end = g.shared_end;
+  at.max_pos = g.max_pos;
+  at.nb = g.nb;
+  at.n_ws = g.M - g.n_direct;
+  at.scale = 1.0f / sqrtf((float)c->dh);
+  at.kc = s->kc + l * skvl * esz;
+  at.vc = s->vc + l * skvl * esz;
+  at.kw = (char*)s->kw + l * swsl * esz;
+  at.vw = (char*)s->vw + l * swsl * esz;
+  return at;
+}
+
+// committed K/V read once (positions below shared_end), each packed row's K/V, Q in, O out
+static void seg_attn_cost(la_ctx* c, const Seg& g, double* bytes, double* flops) {
+  const int qd = c->H * c->dh;
+  const double kvrow = 2.0 * c->Hkv * c->dh * c->esz;
+  *bytes += g.shared_end * kvrow + (double)(g.M - g.n_direct) * kvrow + 2.0 * g.M * qd * c->esz;
+  *flops += 4.0 * g.M * qd * (double)(g.max_pos + 1);
+}
+
 static int gemm(la_ctx* c, float* P, int epi, const void* X, const void* W, void* Y, const void* Rr, int M, int N,
                 int K, int up_off, bool defer = false, const LaQkvOut* qo = nullptr) {
   LaGemmArgs a{};
@@ -415,8 +458,9 @@ static int resid_gemm(la_ctx* c, const FwdBufs& B, const void* X, const void* W,
 // (the GEMM's K split depends on the shape only), so a request's logits are
 // bitwise those of its own forward.  c supplies the dims, the weights and
 // the stream (all requests share them); fp32 logits of request i land in
-// B.logits rows sg[i].l0 ...
-static int forward_segs(la_ctx* c, const FwdBufs& B, const Seg* sg, int ns) {
+// B.logits rows sg[i].l0 ...  With tables (entries in the order of sg), the
+// per-request passes run as one launch per layer.
+static int forward_segs(la_ctx* c, const FwdBufs& B, const Seg* sg, int ns, const SegTables* tab = nullptr) {
   const int esz = c->esz;
   int M = 0, n_logit = 0;
   for (int i = 0; i < ns; ++i) { M += sg[i].M; n_logit += sg[i].n_logit; }
@@ -444,54 +488,55 @@ static int forward_segs(la_ctx* c, const FwdBufs& B, const Seg* sg, int ns) {
       if ((rc = gemm(c, B.gemm_p, LA_EPI_STORE, B.nrm, wqkv, B.qkv, nullptr, M, c->qkvdim, c->d, 0, qs > 1)))
         return rc;
     }
-    for (int i = 0; i < ns; ++i) {
-      const Seg& g = sg[i];
-      la_ctx* s = g.s;
-      const size_t skvl = (size_t)s->Hkv * s->t_cap * s->dh;
-      const size_t swsl = (size_t)s->Hkv * s->ws_cap * s->dh;
-      char* kc = s->kc + l * skvl * esz;
-      char* vc = s->vc + l * skvl * esz;
-      char* kw = (char*)s->kw + l * swsl * esz;
-      char* vw = (char*)s->vw + l * swsl * esz;
-      char* q = (char*)B.q + (size_t)g.r0 * qd * esz;
-      if (fused) {
-        // the fused epilogue places into one request's cache: one launch per request
-        const LaQkvOut qo{s->rope, g.pos, q, kc, vc, kw, vw, c->H, c->Hkv, c->dh, s->t_cap, g.cache_row0, g.n_direct,
-                          s->ws_cap};
-        if ((rc = gemm(c, B.gemm_p, LA_EPI_QKV, (char*)B.nrm + (size_t)g.r0 * c->d * esz, wqkv, B.qkv, nullptr, g.M,
-                       c->qkvdim, c->d, 0, false, &qo)))
-          return rc;
-      } else if (qs > 1) {
-        la_qkv_reduce_post_launch(c->dtype, B.gemm_p + (size_t)g.r0 * c->qkvdim, qs, M, g.M, s->rope, g.pos, c->H,
-                                  c->Hkv, c->dh, q, kc, vc, s->t_cap, g.cache_row0, g.n_direct, kw, vw, s->ws_cap,
-                                  c->st);
-      } else {
-        la_qkv_post_launch(c->dtype, (char*)B.qkv + (size_t)g.r0 * c->qkvdim * esz, s->rope, g.pos, g.M, c->H,
-                           c->Hkv, c->dh, q, kc, vc, s->t_cap, g.cache_row0, g.n_direct, kw, vw, s->ws_cap, c->st);
+    // rotary placement of q, k and v: each request's k and v go to its own cache
+    if (tab && !fused) {
+      la_qkv_post_multi_launch(c->dtype, B.gemm_p, qs > 1 ? qs : 0, B.qkv, M, tab->post, ns, l, c->H, c->Hkv, c->dh,
+                               B.q, c->st);
+    } else {
+      for (int i = 0; i < ns; ++i) {
+        const Seg& g = sg[i];
+        la_ctx* s = g.s;
+        const size_t skvl = (size_t)s->Hkv * s->t_cap * s->dh;
+        const size_t swsl = (size_t)s->Hkv * s->ws_cap * s->dh;
+        char* kc = s->kc + l * skvl * esz;
+        char* vc = s->vc + l * skvl * esz;
+        char* kw = (char*)s->kw + l * swsl * esz;
+        char* vw = (char*)s->vw + l * swsl * esz;
+        char* q = (char*)B.q + (size_t)g.r0 * qd * esz;
+        if (fused) {
+          // the fused epilogue places into one request's cache: one launch per request
+          const LaQkvOut qo{s->rope, g.pos, q, kc, vc, kw, vw, c->H, c->Hkv, c->dh, s->t_cap, g.cache_row0,
+                            g.n_direct, s->ws_cap};
+          if ((rc = gemm(c, B.gemm_p, LA_EPI_QKV, (char*)B.nrm + (size_t)g.r0 * c->d * esz, wqkv, B.qkv, nullptr,
+                         g.M, c->qkvdim, c->d, 0, false, &qo)))
+            return rc;
+        } else if (qs > 1) {
+          la_qkv_reduce_post_launch(c->dtype, B.gemm_p + (size_t)g.r0 * c->qkvdim, qs, M, g.M, s->rope, g.pos, c->H,
+                                    c->Hkv, c->dh, q, kc, vc, s->t_cap, g.cache_row0, g.n_direct, kw, vw, s->ws_cap,
+                                    c->st);
+        } else {
+          la_qkv_post_launch(c->dtype, (char*)B.qkv + (size_t)g.r0 * c->qkvdim * esz, s->rope, g.pos, g.M, c->H,
+                             c->Hkv, c->dh, q, kc, vc, s->t_cap, g.cache_row0, g.n_direct, kw, vw, s->ws_cap, c->st);
+        }
       }
-      LaAttnArgs at{};
-      at.q = q; at.o = (char*)B.o + (size_t)g.r0 * qd * esz;
-      at.part_o = s->attn_po; at.part_ml = s->attn_pml; at.max_splits = s->parts;
-      at.pos = g.pos; at.branch = g.branch; at.path = g.path; at.path_len = g.path_len;
-      at.tile_meta = g.tile_meta; at.tile_path = g.tile_path;
-      at.Q = g.M; at.H = c->H; at.Hkv = c->Hkv; at.dh = c->dh; at.T_cap = s->t_cap; at.ws_cap = s->ws_cap;
-      at.maxp = g.maxp;
-      at.shared_end = g.shared_end;
-      at.max_pos = g.max_pos;
-      at.nb = g.nb;
-      at.n_ws = g.M - g.n_direct;
-      at.scale = 1.0f / sqrtf((float)c->dh);
-      at.kc = kc; at.vc = vc; at.kw = kw; at.vw = vw;
-      {
-        // committed K/V read once (positions below shared_end), each packed row's K/V, Q in, O out
-        const double kvrow = 2.0 * c->Hkv * c->dh * esz;
-        const double bytes = g.shared_end * kvrow + (double)(g.M - g.n_direct) * kvrow + 2.0 * g.M * qd * esz;
-        const double flops = 4.0 * g.M * qd * (double)(g.max_pos + 1);
-        prof_mark(c, true, 1, bytes, flops);
-      }
-      rc = la_attention_launch(c->dtype, at, c->st);
+    }
+    // attention, each request against its own cache
+    if (tab) {
+      double bytes = 0, flops = 0;
+      for (int i = 0; i < ns; ++i) seg_attn_cost(c, sg[i], &bytes, &flops);
+      prof_mark(c, true, 1, bytes, flops);
+      rc = la_attention_multi_launch(c->dtype, tab->shape, tab->attn, ns, l, c->st);
       prof_mark(c, false, 1, 0, 0);
       if (rc) return fail(c, LA_EDEVICE, "attention launch failed (%d)", rc);
+    } else {
+      for (int i = 0; i < ns; ++i) {
+        double bytes = 0, flops = 0;
+        seg_attn_cost(c, sg[i], &bytes, &flops);
+        prof_mark(c, true, 1, bytes, flops);
+        rc = la_attention_launch(c->dtype, seg_attn_args(c, B, sg[i], l), c->st);
+        prof_mark(c, false, 1, 0, 0);
+        if (rc) return fail(c, LA_EDEVICE, "attention launch failed (%d)", rc);
+      }
     }
     if ((rc = resid_gemm(c, B, B.o, wo, M, qd, &pend))) return rc;
     if (la_addnorm_launch(c->dtype, B.x, B.gemm_p, pend, pstride, 1, mlp_norm, B.nrm, nullptr, M, c->d,
@@ -993,16 +1038,29 @@ extern "C" int la_generate(la_ctx* c, int32_t* out_tokens, int32_t cap, int32_t*
 // share one read of the weights per step, and their speculation shares the
 // compute left beside it; "M7.3", 0x03B: each request keeps its own pool,
 // window and K/V).
+// The per-request tables of a step (one entry per request, at most one per
+// row): attention entries, then rotary-placement entries.
+static size_t tab_bytes(int R) {
+  return (size_t)R * sizeof(LaAttnSeg) + (size_t)R * sizeof(LaPostSeg);
+}
+
 struct la_batch {
   la_model_dims dims;
   la_model w;
   hipStream_t st;
   int max_rows;
   FwdBufs b;
+  char* tab_dev = nullptr;     // the tables in the workspace
+  char* tab_host = nullptr;    // pinned staging of the tables
+  hipEvent_t tab_ev = nullptr; // recorded after the last upload: the staging is free once it completed
   std::vector<int32_t> base, found, cap, paused;
+  ~la_batch() {
+    if (tab_ev) (void)hipEventDestroy(tab_ev);
+    if (tab_host) (void)hipHostFree(tab_host);
+  }
 };
 
-static size_t carve_batch(const la_model_dims& d, int R, char* base, FwdBufs* B) {
+static size_t carve_batch(const la_model_dims& d, int R, char* base, FwdBufs* B, char** tab = nullptr) {
   size_t off = 0;
   auto take = [&](size_t bytes) -> void* {
     void* p = base ? (void*)(base + off) : nullptr;
@@ -1022,7 +1080,9 @@ static size_t carve_batch(const la_model_dims& d, int R, char* base, FwdBufs* B)
   b.fin = take((size_t)R * d.d_model * e);
   b.gemm_p = (float*)take(std::max<size_t>(partial_floats(dt, d.d_model, qkvdim, qd, d.d_ff, d.vocab, R, R), 1) * 4);
   b.logits = (float*)take((size_t)R * d.vocab * 4);
+  char* t = (char*)take(tab_bytes(R));
   if (B) *B = b;
+  if (tab) *tab = t;
   return off;
 }
 
@@ -1050,7 +1110,12 @@ extern "C" int la_batch_init(const la_model_dims* dims, const la_model* weights,
   b->w = *weights;
   b->st = (hipStream_t)stream;
   b->max_rows = max_rows;
-  carve_batch(*dims, max_rows, (char*)workspace, &b->b);
+  carve_batch(*dims, max_rows, (char*)workspace, &b->b, &b->tab_dev);
+  if (hipHostMalloc((void**)&b->tab_host, tab_bytes(max_rows), hipHostMallocDefault) != hipSuccess ||
+      hipEventCreateWithFlags(&b->tab_ev, hipEventDisableTiming) != hipSuccess) {
+    delete b;
+    return fail(nullptr, LA_EDEVICE, "batch tables: pinned staging or event");
+  }
   *out = b;
   return LA_OK;
 }
@@ -1160,7 +1225,32 @@ extern "C" int la_batch_step(la_batch* b, la_ctx* const* ctx, int32_t n, int32_t
   }
   if (r0 > b->max_rows) return fail(nullptr, LA_EOVERFLOW, "%d stacked rows > max_rows %d", r0, b->max_rows);
   la_ctx* lead = ctx[act[0]];
-  if ((rc = forward_segs(lead, b->b, seg.data(), (int)seg.size()))) return rc;
+  // the per-request tables: built in the pinned staging (free once the last upload completed), one copy each
+  const int ns = (int)seg.size();
+  HIPCHK(nullptr, hipEventSynchronize(b->tab_ev));
+  LaAttnSeg* ah = (LaAttnSeg*)b->tab_host;
+  LaPostSeg* ph = (LaPostSeg*)(b->tab_host + (size_t)b->max_rows * sizeof(LaAttnSeg));
+  for (int k = 0; k < ns; ++k) {
+    const Seg& g = seg[k];
+    la_ctx* s = g.s;
+    const long long kvl = (long long)s->Hkv * s->t_cap * s->dh * s->esz;
+    const long long wsl = (long long)s->Hkv * s->ws_cap * s->dh * s->esz;
+    ah[k] = LaAttnSeg{};
+    ah[k].a = seg_attn_args(lead, b->b, g, 0);
+    ah[k].kv_layer = kvl;
+    ah[k].ws_layer = wsl;
+    ph[k] = LaPostSeg{g.pos, s->rope, s->kc, s->vc, s->kw, s->vw, kvl, wsl, g.r0, s->t_cap, g.cache_row0,
+                      g.n_direct, s->ws_cap, 0};
+  }
+  SegTables tab{};
+  if (la_attention_multi_plan(lead->dtype, ah, ns, &tab.shape))
+    return fail(lead, LA_EINVAL, "attention of the stacked requests cannot be planned");
+  tab.attn = (const LaAttnSeg*)b->tab_dev;
+  tab.post = (const LaPostSeg*)(b->tab_dev + (size_t)b->max_rows * sizeof(LaAttnSeg));
+  HIPCHK(nullptr, hipMemcpyAsync((void*)tab.attn, ah, ns * sizeof(LaAttnSeg), hipMemcpyHostToDevice, b->st));
+  HIPCHK(nullptr, hipMemcpyAsync((void*)tab.post, ph, ns * sizeof(LaPostSeg), hipMemcpyHostToDevice, b->st));
+  HIPCHK(nullptr, hipEventRecord(b->tab_ev, b->st));
+  if ((rc = forward_segs(lead, b->b, seg.data(), ns, &tab))) return rc;
   for (size_t k = 0; k < act.size(); ++k) round_predicted(ctx[act[k]], b->b.logits + (size_t)seg[k].l0 * b->dims.vocab);
   auto unwind = [&]() {
     for (int i : act) { ctx[i]->pending = false; ctx[i]->verified = false; }

@@ -405,7 +405,7 @@ template <int PW, int KMAX, int K = 0> __device__ __forceinline__ void ring_wait
 // One workgroup per (KV head, key split, row group of NW x TPW tiles); a
 // ring of D chunk slots.
 template <typename T, int DH, int NW, int TPW, int D>
-__global__ void __launch_bounds__(64 * NW) la_attn_kernel(LaAttnArgs a) {
+__device__ __forceinline__ void attn_body(const LaAttnArgs& a, const unsigned blk) {
   typedef AttnT<T, DH> AT;
   constexpr int ROWB = AT::ROWB, NDT = AT::NDT, NVR = AT::NVR;
   constexpr int CHB = CH * ROWB;                 // K (or V) of one chunk
@@ -422,7 +422,7 @@ __global__ void __launch_bounds__(64 * NW) la_attn_kernel(LaAttnArgs a) {
   extern __shared__ __attribute__((aligned(1024))) char lds[];
 
   // block -> (XCD, KV head, split, row group); the highest splits (tail chunks) first
-  const int xcd = blockIdx.x & 7, bi = blockIdx.x >> 3;
+  const int xcd = blk & 7, bi = blk >> 3;
   const int g_kv = xcd + 8 * (bi / a.wg_head);
   if (g_kv >= a.Hkv) return;
   const int li = bi % a.wg_head;
@@ -901,18 +901,45 @@ __global__ void __launch_bounds__(64 * NW) la_attn_kernel(LaAttnArgs a) {
   }
 }
 
+template <typename T, int DH, int NW, int TPW, int D>
+__global__ void __launch_bounds__(64 * NW) la_attn_kernel(LaAttnArgs a) {
+  attn_body<T, DH, NW, TPW, D>(a, blockIdx.x);
+}
+
+// Several requests in one launch: block b belongs to the last entry whose
+// first workgroup is at or below b (every request's block count is a
+// multiple of 8, so b % 8 is also the block's XCD inside the request).
+template <typename T, int DH, int NW, int TPW, int D>
+__global__ void __launch_bounds__(64 * NW) la_attn_multi_kernel(const LaAttnSeg* __restrict__ segs, int n,
+                                                               int layer) {
+  const int b = blockIdx.x;
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (segs[mid].blk0 <= b) lo = mid;
+    else hi = mid - 1;
+  }
+  LaAttnArgs a = segs[lo].a;
+  const long long kvo = layer * segs[lo].kv_layer, wso = layer * segs[lo].ws_layer;
+  a.kc = (const char*)a.kc + kvo;
+  a.vc = (const char*)a.vc + kvo;
+  a.kw = (const char*)a.kw + wso;
+  a.vw = (const char*)a.vw + wso;
+  attn_body<T, DH, NW, TPW, D>(a, (unsigned)(b - segs[lo].blk0));
+}
+
 // Fold of the key splits' states in split order (m, l, O), then O / l.  One
 // thread per 4 head dimensions of a (row, head).
 template <typename T, int DH>
-__global__ void __launch_bounds__(256) la_attn_merge_kernel(LaAttnArgs a) {
+__device__ __forceinline__ void merge_body(const LaAttnArgs& a, const unsigned blk) {
   constexpr int V4 = DH / 4, MS = 8;            // splits whose loads are all issued before the fold
   // block -> (XCD, KV head): the head's split states were written on that
   // XCD (the attention kernel's mapping), so they are read from its L2
   const int group = a.H / a.Hkv;
   const int per = a.Q * group * V4;               // (row, q-head, 4 dims) items of one KV head
   const int wpk = (per + 255) / 256;
-  const int g_kv = (blockIdx.x & 7) + 8 * ((blockIdx.x >> 3) / wpk);
-  const int item = ((blockIdx.x >> 3) % wpk) * 256 + threadIdx.x;
+  const int g_kv = (blk & 7) + 8 * ((blk >> 3) / wpk);
+  const int item = ((blk >> 3) % wpk) * 256 + threadIdx.x;
   if (g_kv >= a.Hkv || item >= per) return;
   const int d4 = item % V4, r2 = item / V4;
   const int row = r2 / group, hh = g_kv * group + r2 % group;
@@ -955,6 +982,25 @@ __global__ void __launch_bounds__(256) la_attn_merge_kernel(LaAttnArgs a) {
   }
 }
 
+template <typename T, int DH>
+__global__ void __launch_bounds__(256) la_attn_merge_kernel(LaAttnArgs a) {
+  merge_body<T, DH>(a, blockIdx.x);
+}
+
+// several requests: block b belongs to the last entry whose first merge
+// workgroup is at or below b (requests of a single split have none)
+template <typename T, int DH>
+__global__ void __launch_bounds__(256) la_attn_merge_multi_kernel(const LaAttnSeg* __restrict__ segs, int n) {
+  const int b = blockIdx.x;
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (segs[mid].mblk0 <= b) lo = mid;
+    else hi = mid - 1;
+  }
+  merge_body<T, DH>(segs[lo].a, (unsigned)(b - segs[lo].mblk0));
+}
+
 // Chunks per key split: a function of the cache capacity and the model's head
 // counts only (never of the rows of a call), so every call on one cache cuts
 // its keys the same way.  About `target` splits when the cache is full --
@@ -984,81 +1030,56 @@ int la_attention_fits(int dh, int esz, int q_max, int nb_max, int maxp_max) {
   return 2 * half + paths + ring2 <= LDS_BYTES;
 }
 
+// What one launch runs: one request's arguments (by value), or a table of
+// requests in device memory for a given layer.
+struct AttnLaunch {
+  const LaAttnArgs* a;
+  const LaAttnSeg* segs;
+  int n, layer;
+};
+
 template <typename T, int DH, int NW, int TPW, int D>
-static void launch_cfg(const LaAttnArgs& a, int grid, size_t lds, hipStream_t st) {
-  static const bool attr = hipFuncSetAttribute((const void*)&la_attn_kernel<T, DH, NW, TPW, D>,
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES) == hipSuccess;
-  (void)attr;
-  hipLaunchKernelGGL((la_attn_kernel<T, DH, NW, TPW, D>), dim3(grid), dim3(64 * NW), lds, st, a);
+static void launch_cfg(const AttnLaunch& L, int grid, size_t lds, hipStream_t st) {
+  if (L.segs) {
+    static const bool attr = hipFuncSetAttribute((const void*)&la_attn_multi_kernel<T, DH, NW, TPW, D>,
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES) == hipSuccess;
+    (void)attr;
+    hipLaunchKernelGGL((la_attn_multi_kernel<T, DH, NW, TPW, D>), dim3(grid), dim3(64 * NW), lds, st, L.segs, L.n,
+                       L.layer);
+  } else {
+    static const bool attr = hipFuncSetAttribute((const void*)&la_attn_kernel<T, DH, NW, TPW, D>,
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES) == hipSuccess;
+    (void)attr;
+    hipLaunchKernelGGL((la_attn_kernel<T, DH, NW, TPW, D>), dim3(grid), dim3(64 * NW), lds, st, *L.a);
+  }
 }
 
 // ring depth: 6 chunk slots where the LDS holds them beside the tail stage
 // (bf16), else 4, else 2; a single wave issues a whole chunk's 16 loads, so it
 // keeps at most 4 slots (the vmcnt counter holds 63 loads)
 template <typename T, int DH, int NW, int TPW>
-static void launch_depth(const LaAttnArgs& a, int depth, int grid, size_t lds, hipStream_t st) {
+static void launch_depth(const AttnLaunch& L, int depth, int grid, size_t lds, hipStream_t st) {
   constexpr bool deep = std::is_same<T, bf16_t>::value && NW > 1;
-  if (deep && depth == 6) launch_cfg<T, DH, NW, TPW, deep ? 6 : 4>(a, grid, lds, st);
-  else if (depth == 4) launch_cfg<T, DH, NW, TPW, 4>(a, grid, lds, st);
-  else launch_cfg<T, DH, NW, TPW, 2>(a, grid, lds, st);
+  if (deep && depth == 6) launch_cfg<T, DH, NW, TPW, deep ? 6 : 4>(L, grid, lds, st);
+  else if (depth == 4) launch_cfg<T, DH, NW, TPW, 4>(L, grid, lds, st);
+  else launch_cfg<T, DH, NW, TPW, 2>(L, grid, lds, st);
 }
 
 template <typename T, int DH>
-static int launch_dh(LaAttnArgs a, hipStream_t st) {
-  constexpr int ROWB = AttnT<T, DH>::ROWB;
-  constexpr size_t SLOT = 2 * CH * ROWB;
-  const int group = a.H / a.Hkv;
-  const int tiles = group * ((a.Q + 15) / 16);    // 16-row tiles of one KV head
-  const int kv = 8 * ((a.Hkv + 7) / 8);
-  // tiles per workgroup: the most (up to 8) that still leave about 200
-  // workgroups, one wave per tile (eight waves: two per SIMD, so one wave's
-  // vector ALU work overlaps the other's MFMAs and LDS waits)
-  struct Cfg { int nw, tpw; };
-  const Cfg cfgs[] = {{8, 1}, {4, 1}, {2, 1}, {1, 1}};
-  Cfg cfg = {1, 1};
-  for (const Cfg& c : cfgs) {
-    const int nt = c.nw * c.tpw;
-    if (nt > tiles && !(c.nw == 1)) continue;
-    const int wgs = kv * a.nsplit * ((tiles + nt - 1) / nt);
-    cfg = c;
-    if (wgs >= 200) break;
-  }
-  const int nt = cfg.nw * cfg.tpw;
-  a.rgroups = (tiles + nt - 1) / nt;
-  a.wg_head = a.rgroups * a.nsplit;
-  // LDS: the tail stage (committed rows of the first tail chunk + every packed
-  // row, K and V, 1 KB aligned, then the path table) before the ring
-  size_t st_bytes = 0;
-  if (a.n_tail > 0) {
-    const int rows = (a.shared_end - CH * a.tail0) + a.n_ws;
-    const int rpb = 1024 / ROWB;
-    a.st_rows = rows;
-    a.st_half = ((rows + rpb - 1) / rpb) * 1024;
-    st_bytes = 2 * (size_t)a.st_half + ((size_t)a.nb * a.maxp * 4 + 1023) / 1024 * 1024;
-    a.st_bytes = (int)st_bytes;
-  }
-  const int dmax = std::is_same<T, bf16_t>::value && cfg.nw > 1 ? 6 : 4;
-  int depth = dmax;
-  while (depth > 2 && st_bytes + depth * SLOT > LDS_BYTES) depth -= 2;
-  if (st_bytes + depth * SLOT > LDS_BYTES) return -2;
-  a.ring_depth = depth;
-  const size_t lds = st_bytes + depth * SLOT;
-  const int grid = kv * a.wg_head;
-  if (cfg.nw == 8) launch_depth<T, DH, 8, 1>(a, depth, grid, lds, st);
-  else if (cfg.nw == 4) launch_depth<T, DH, 4, 1>(a, depth, grid, lds, st);
-  else if (cfg.nw == 2) launch_depth<T, DH, 2, 1>(a, depth, grid, lds, st);
-  else launch_depth<T, DH, 1, 1>(a, depth, grid, lds, st);
-  if (a.nsplit > 1) {
-    const int wpk = (a.Q * group * (DH / 4) + 255) / 256;
-    hipLaunchKernelGGL((la_attn_merge_kernel<T, DH>), dim3(kv * wpk), dim3(256), 0, st, a);
-  }
-  return 0;
+static void launch_shape(const AttnLaunch& L, int nw, int depth, int grid, size_t lds, hipStream_t st) {
+  if (nw == 8) launch_depth<T, DH, 8, 1>(L, depth, grid, lds, st);
+  else if (nw == 4) launch_depth<T, DH, 4, 1>(L, depth, grid, lds, st);
+  else if (nw == 2) launch_depth<T, DH, 2, 1>(L, depth, grid, lds, st);
+  else launch_depth<T, DH, 1, 1>(L, depth, grid, lds, st);
 }
 
-int la_attention_launch(int dtype, const LaAttnArgs& a0, hipStream_t st) {
-  LaAttnArgs a = a0;
-  if (a.Q <= 0) return 0;
-  if (a.H % a.Hkv != 0 || a.shared_end < 1 || a.shared_end > a.T_cap) return -2;
+static int kv_slots(int Hkv) { return 8 * ((Hkv + 7) / 8); }       // KV heads rounded up to the 8 XCDs
+static int attn_tiles(const LaAttnArgs& a) { return (a.H / a.Hkv) * ((a.Q + 15) / 16); }  // 16-row tiles of a KV head
+static int merge_wpk(const LaAttnArgs& a, int dh) { return (a.Q * (a.H / a.Hkv) * (dh / 4) + 255) / 256; }
+
+// Validation, and the key ranges and splits of one call.
+static int attn_prep(LaAttnArgs& a) {
+  if (a.H <= 0 || a.Hkv <= 0 || a.H % a.Hkv != 0 || a.shared_end < 1 || a.shared_end > a.T_cap) return -2;
   if (a.n_ws < 0 || a.n_ws > a.ws_cap || a.maxp < 1) return -2;
   const int se = a.shared_end;
   const bool tail = a.max_pos >= se;
@@ -1074,16 +1095,139 @@ int la_attention_launch(int dtype, const LaAttnArgs& a0, hipStream_t st) {
   const int last_chunk = a.max_pos / CH;
   a.nsplit = last_chunk / a.spl + 1;
   if (a.nsplit > 1 && (a.part_o == nullptr || a.part_ml == nullptr || a.nsplit > a.max_splits)) return -2;
-  int rc;
-  if (dtype == LA_DT_BF16) {
-    if (a.dh == 128) rc = launch_dh<bf16_t, 128>(a, st);
-    else if (a.dh == 64) rc = launch_dh<bf16_t, 64>(a, st);
-    else return -2;
-  } else {
-    if (a.dh == 16) rc = launch_dh<float, 16>(a, st);
-    else if (a.dh == 64) rc = launch_dh<float, 64>(a, st);
-    else return -2;
+  return 0;
+}
+
+// Tiles per workgroup, for calls of tiles[i] tiles per KV head cut in
+// nsplit[i] key splits: the most (up to 8) that still leave about 200
+// workgroups in all, one wave per tile (eight waves: two per SIMD, so one
+// wave's vector ALU work overlaps the other's MFMAs and LDS waits).
+static int pick_nw(const LaAttnArgs* a, int stride_bytes, int n) {
+  auto at = [&](int i) -> const LaAttnArgs& { return *(const LaAttnArgs*)((const char*)a + (size_t)i * stride_bytes); };
+  int tmax = 0;
+  for (int i = 0; i < n; ++i) tmax = std::max(tmax, attn_tiles(at(i)));
+  int nw = 1;
+  for (const int c : {8, 4, 2, 1}) {
+    if (c > tmax && c != 1) continue;
+    long wgs = 0;
+    for (int i = 0; i < n; ++i)
+      wgs += (long)kv_slots(at(i).Hkv) * at(i).nsplit * ((attn_tiles(at(i)) + c - 1) / c);
+    nw = c;
+    if (wgs >= 200) break;
   }
-  if (rc) return rc;
+  return nw;
+}
+
+// The tail stage (committed rows of the first tail chunk + every packed row,
+// K and V, 1 KB aligned, then the path table) before the ring; its bytes
+static size_t attn_stage(LaAttnArgs& a, int rowb) {
+  size_t st_bytes = 0;
+  if (a.n_tail > 0) {
+    const int rows = (a.shared_end - CH * a.tail0) + a.n_ws;
+    const int rpb = 1024 / rowb;
+    a.st_rows = rows;
+    a.st_half = ((rows + rpb - 1) / rpb) * 1024;
+    st_bytes = 2 * (size_t)a.st_half + ((size_t)a.nb * a.maxp * 4 + 1023) / 1024 * 1024;
+    a.st_bytes = (int)st_bytes;
+  }
+  return st_bytes;
+}
+
+// the deepest ring (6, 4 or 2 slots) beside a tail stage of st_bytes; 0 if none fits
+static int ring_depth_for(bool bf16, int nw, int rowb, size_t st_bytes) {
+  const size_t slot = 2 * (size_t)CH * rowb;
+  int depth = bf16 && nw > 1 ? 6 : 4;
+  while (depth > 2 && st_bytes + depth * slot > LDS_BYTES) depth -= 2;
+  return st_bytes + depth * slot > LDS_BYTES ? 0 : depth;
+}
+
+static bool dh_supported(int dtype, int dh) {
+  return dtype == LA_DT_BF16 ? (dh == 128 || dh == 64) : (dh == 16 || dh == 64);
+}
+
+template <typename T, int DH>
+static void launch_merge(const AttnLaunch& L, int grid, hipStream_t st) {
+  if (L.segs) hipLaunchKernelGGL((la_attn_merge_multi_kernel<T, DH>), dim3(grid), dim3(256), 0, st, L.segs, L.n);
+  else hipLaunchKernelGGL((la_attn_merge_kernel<T, DH>), dim3(grid), dim3(256), 0, st, *L.a);
+}
+
+static void launch_any(int dtype, int dh, const AttnLaunch& L, int nw, int depth, int grid, size_t lds, int mgrid,
+                       hipStream_t st) {
+  if (dtype == LA_DT_BF16) {
+    if (dh == 128) { launch_shape<bf16_t, 128>(L, nw, depth, grid, lds, st); if (mgrid) launch_merge<bf16_t, 128>(L, mgrid, st); }
+    else { launch_shape<bf16_t, 64>(L, nw, depth, grid, lds, st); if (mgrid) launch_merge<bf16_t, 64>(L, mgrid, st); }
+  } else {
+    if (dh == 16) { launch_shape<float, 16>(L, nw, depth, grid, lds, st); if (mgrid) launch_merge<float, 16>(L, mgrid, st); }
+    else { launch_shape<float, 64>(L, nw, depth, grid, lds, st); if (mgrid) launch_merge<float, 64>(L, mgrid, st); }
+  }
+}
+
+int la_attention_launch(int dtype, const LaAttnArgs& a0, hipStream_t st) {
+  LaAttnArgs a = a0;
+  if (a.Q <= 0) return 0;
+  if (!dh_supported(dtype, a.dh)) return -2;
+  if (int rc = attn_prep(a)) return rc;
+  const bool bf16 = dtype == LA_DT_BF16;
+  const int rowb = a.dh * (bf16 ? 2 : 4);
+  const int nw = pick_nw(&a, sizeof a, 1);
+  a.rgroups = (attn_tiles(a) + nw - 1) / nw;
+  a.wg_head = a.rgroups * a.nsplit;
+  const size_t st_bytes = attn_stage(a, rowb);
+  const int depth = ring_depth_for(bf16, nw, rowb, st_bytes);
+  if (!depth) return -2;
+  a.ring_depth = depth;
+  const size_t lds = st_bytes + depth * 2 * (size_t)CH * rowb;
+  const int kv = kv_slots(a.Hkv);
+  const AttnLaunch L{&a, nullptr, 1, 0};
+  launch_any(dtype, a.dh, L, nw, depth, kv * a.wg_head, lds, a.nsplit > 1 ? kv * merge_wpk(a, a.dh) : 0, st);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int la_attention_multi_plan(int dtype, LaAttnSeg* segs, int n, LaAttnMulti* m) {
+  if (n <= 0 || !segs || !m) return -2;
+  const int dh = segs[0].a.dh;
+  if (!dh_supported(dtype, dh)) return -2;
+  const bool bf16 = dtype == LA_DT_BF16;
+  const int rowb = dh * (bf16 ? 2 : 4);
+  for (int i = 0; i < n; ++i) {
+    LaAttnArgs& a = segs[i].a;
+    if (a.Q <= 0 || a.dh != dh) return -2;
+    if (int rc = attn_prep(a)) return rc;
+  }
+  const int nw = pick_nw(&segs[0].a, sizeof(LaAttnSeg), n);
+  size_t st_max = 0;
+  for (int i = 0; i < n; ++i) {
+    LaAttnArgs& a = segs[i].a;
+    a.rgroups = (attn_tiles(a) + nw - 1) / nw;
+    a.wg_head = a.rgroups * a.nsplit;
+    st_max = std::max(st_max, attn_stage(a, rowb));
+  }
+  const int depth = ring_depth_for(bf16, nw, rowb, st_max);
+  if (!depth) return -2;
+  int grid = 0, mgrid = 0;
+  for (int i = 0; i < n; ++i) {
+    LaAttnArgs& a = segs[i].a;
+    const int kv = kv_slots(a.Hkv);
+    a.ring_depth = depth;
+    segs[i].blk0 = grid;
+    segs[i].mblk0 = mgrid;
+    grid += kv * a.wg_head;
+    if (a.nsplit > 1) mgrid += kv * merge_wpk(a, dh);
+  }
+  m->nw = nw;
+  m->depth = depth;
+  m->dh = dh;
+  m->grid = grid;
+  m->mgrid = mgrid;
+  m->lds = st_max + depth * 2 * (size_t)CH * rowb;
+  return 0;
+}
+
+int la_attention_multi_launch(int dtype, const LaAttnMulti& m, const LaAttnSeg* segs, int n, int layer,
+                              hipStream_t st) {
+  if (m.grid <= 0) return 0;
+  if (!dh_supported(dtype, m.dh) || !segs || n <= 0) return -2;
+  const AttnLaunch L{nullptr, segs, n, layer};
+  launch_any(dtype, m.dh, L, m.nw, m.depth, m.grid, m.lds, m.mgrid, st);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

@@ -114,6 +114,27 @@ int la_attention_parts(int max_pos, int t_cap);   // upper bound on the key spli
 // whether a round of q_max rows (nb_max branches reaching maxp_max positions) fits the tail stage's LDS
 int la_attention_fits(int dh, int esz, int q_max, int nb_max, int maxp_max);
 
+// Several requests' attention in one launch (each against its own cache).
+// One entry per request: its arguments with layer 0's cache and workspace
+// pointers, and the bytes from one layer's K (or V) to the next one's.
+struct LaAttnSeg {
+  LaAttnArgs a;
+  long long kv_layer, ws_layer;
+  int blk0, mblk0;      // the request's first attention / merge workgroup (set by the plan)
+  int pad[2];
+};
+struct LaAttnMulti {    // the launch shape every request of the launch shares
+  int nw, depth, dh, grid, mgrid;
+  size_t lds;
+};
+// Completes each entry's arguments for one common workgroup shape and ring
+// depth (the shape never changes a row's arithmetic); -2 if a request cannot
+// run.  Layer-independent: the same plan serves every layer.
+int la_attention_multi_plan(int dtype, LaAttnSeg* segs, int n, LaAttnMulti* m);
+// segs: the planned entries in device memory
+int la_attention_multi_launch(int dtype, const LaAttnMulti& m, const LaAttnSeg* segs, int n, int layer,
+                              hipStream_t st);
+
 // model pieces
 void la_embed_launch(int dtype, const void* E, const int32_t* tok, void* x, int M, int d, hipStream_t st);
 void la_rmsnorm_launch(int dtype, const void* x, const void* w, void* y, const int32_t* rows, int M, int d,
@@ -133,6 +154,20 @@ void la_qkv_reduce_post_launch(int dtype, const float* P, int S, int Prows, int 
 void la_qkv_post_launch(int dtype, const void* qkv, const float2* rope, const int32_t* pos, int M, int H, int Hkv,
                         int dh, void* q, void* kc, void* vc, int T_cap, int cache_row0, int n_direct, void* kw,
                         void* vw, int ws_cap, hipStream_t st);
+// Both over the stacked rows of several requests in one launch: entry i
+// owns rows r0 .. (next entry's r0) - 1 (entries in row order), q goes to the
+// stacked q [M][H][dh], k and v to the request's own cache and workspace of
+// the layer (layer 0's pointers + layer * the layer distance in bytes).
+struct LaPostSeg {
+  const int32_t* pos;   // the request's row positions
+  const float2* rope;
+  void *kc, *vc, *kw, *vw;
+  long long kv_layer, ws_layer;
+  int r0, T_cap, cache_row0, n_direct, ws_cap, pad;
+};
+// S > 0: from the partials P [S][M][(H + 2 Hkv) dh]; S == 0: from the stored qkv [M][(H + 2 Hkv) dh]
+void la_qkv_post_multi_launch(int dtype, const float* P, int S, const void* qkv, int M, const LaPostSeg* segs, int n,
+                              int layer, int H, int Hkv, int dh, void* q, hipStream_t st);
 
 // verification
 void la_argmax_launch(const float* logits, int rows, int V, int32_t* out, hipStream_t st);

@@ -210,27 +210,42 @@ void la_rope_table_launch(float2* tab, int T, int dh, float theta, hipStream_t s
 // qkv [M][(H + 2 Hkv) dh] -> q [M][H][dh] with RoPE; k (RoPE) and v to the
 // cache for the first n_direct rows (cache row cache_row0 + m), to the
 // workspace (row m - n_direct) for the others.  One block per (row, head).
+// With RED the row's values are the fixed-order sums of the projection's S
+// K-split partials (sstride floats apart) rounded to the storage type (what
+// the split reduction stores); without, the stored values.
+
+// where head hh (q heads, then k, then v) of the request's row m goes; qrow is the row's q
 template <typename T>
-__global__ void __launch_bounds__(64) qkv_post_kernel(const T* qkv, const float2* rope, const int32_t* pos, int H,
-                                                      int Hkv, int dh, T* q, T* kc, T* vc, int T_cap, int cache_row0,
-                                                      int n_direct, T* kw, T* vw, int ws_cap) {
-  const int m = blockIdx.x;
-  const int hh = blockIdx.y;                     // 0..H-1 q, H..H+Hkv-1 k, then v
+__device__ inline T* post_dst(int m, int hh, int H, int Hkv, int dh, T* qrow, T* kc, T* vc, int T_cap,
+                              int cache_row0, int n_direct, T* kw, T* vw, int ws_cap) {
+  if (hh < H) return qrow + (size_t)hh * dh;
+  const int g = hh < H + Hkv ? hh - H : hh - H - Hkv;
+  const bool isk = hh < H + Hkv;
+  if (m < n_direct) return (isk ? kc : vc) + ((size_t)g * T_cap + cache_row0 + m) * dh;
+  return (isk ? kw : vw) + ((size_t)g * ws_cap + (m - n_direct)) * dh;
+}
+
+// one (row, head): src is the head's first value (RED: in the first partial)
+template <typename T, bool RED>
+__device__ inline void post_head(const void* src0, int S, size_t sstride, const float2* rope, int p, bool rot, int dh,
+                                 T* dst) {
   const int half = dh / 2;
-  const T* src = qkv + (size_t)m * (H + 2 * Hkv) * dh + (size_t)hh * dh;
-  const int p = pos[m];
-  T* dst;
-  if (hh < H) {
-    dst = q + ((size_t)m * H + hh) * dh;
-  } else {
-    const int g = hh < H + Hkv ? hh - H : hh - H - Hkv;
-    const bool isk = hh < H + Hkv;
-    if (m < n_direct) dst = (isk ? kc : vc) + ((size_t)g * T_cap + cache_row0 + m) * dh;
-    else dst = (isk ? kw : vw) + ((size_t)g * ws_cap + (m - n_direct)) * dh;
-  }
-  const bool rot = hh < H + Hkv;
   for (int i = threadIdx.x; i < half; i += 64) {
-    const float x1 = ld<T>(src + i), x2 = ld<T>(src + i + half);
+    float x1, x2;
+    if constexpr (RED) {
+      const float* src = (const float*)src0;
+      float a1 = 0.f, a2 = 0.f;
+      for (int s = 0; s < S; ++s) {
+        a1 += src[s * sstride + i];
+        a2 += src[s * sstride + i + half];
+      }
+      x1 = StoreT<T>::round(a1);
+      x2 = StoreT<T>::round(a2);
+    } else {
+      const T* src = (const T*)src0;
+      x1 = ld<T>(src + i);
+      x2 = ld<T>(src + i + half);
+    }
     if (rot) {
       const float2 cs = rope[(size_t)p * half + i];
       st<T>(dst + i, x1 * cs.x - x2 * cs.y);
@@ -242,47 +257,47 @@ __global__ void __launch_bounds__(64) qkv_post_kernel(const T* qkv, const float2
   }
 }
 
-// The same from the K-split partials of the projection: each value is the
-// fixed-order sum of its splits rounded to the storage type (what the
-// split reduction stores), then rotated and placed as above.
-template <typename T>
-__global__ void __launch_bounds__(64) qkv_reduce_post_kernel(const float* P, int S, int pcols, int Prows,
-                                                             const float2* rope,
-                                                             const int32_t* pos, int H, int Hkv, int dh, T* q, T* kc,
-                                                             T* vc, int T_cap, int cache_row0, int n_direct, T* kw,
-                                                             T* vw, int ws_cap) {
+template <typename T, bool RED>
+__global__ void __launch_bounds__(64) qkv_post_kernel(const void* src, int S, int Prows, const float2* rope,
+                                                      const int32_t* pos, int H, int Hkv, int dh, T* q, T* kc, T* vc,
+                                                      int T_cap, int cache_row0, int n_direct, T* kw, T* vw,
+                                                      int ws_cap) {
   const int m = blockIdx.x;
   const int hh = blockIdx.y;
-  const int half = dh / 2;
-  const int p = pos[m];
-  T* dst;
-  if (hh < H) {
-    dst = q + ((size_t)m * H + hh) * dh;
-  } else {
-    const int g = hh < H + Hkv ? hh - H : hh - H - Hkv;
-    const bool isk = hh < H + Hkv;
-    if (m < n_direct) dst = (isk ? kc : vc) + ((size_t)g * T_cap + cache_row0 + m) * dh;
-    else dst = (isk ? kw : vw) + ((size_t)g * ws_cap + (m - n_direct)) * dh;
+  const int pcols = (H + 2 * Hkv) * dh;
+  const size_t off = (size_t)m * pcols + (size_t)hh * dh;
+  const void* s0 = RED ? (const void*)((const float*)src + off) : (const void*)((const T*)src + off);
+  T* dst = post_dst<T>(m, hh, H, Hkv, dh, q + (size_t)m * H * dh, kc, vc, T_cap, cache_row0, n_direct, kw, vw,
+                       ws_cap);
+  post_head<T, RED>(s0, S, (size_t)Prows * pcols, rope, pos[m], hh < H + Hkv, dh, dst);
+}
+
+// the same over the stacked rows of several requests: block x is stacked row
+// m, owned by the last entry whose r0 <= m
+template <typename T, bool RED>
+__global__ void __launch_bounds__(64) qkv_post_multi_kernel(const void* src, int S, int M,
+                                                            const LaPostSeg* __restrict__ segs, int n, int layer,
+                                                            int H, int Hkv, int dh, T* q) {
+  const int m = blockIdx.x;
+  const int hh = blockIdx.y;
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (segs[mid].r0 <= m) lo = mid;
+    else hi = mid - 1;
   }
-  const bool rot = hh < H + Hkv;
-  const float* src = P + (size_t)m * pcols + (size_t)hh * dh;
-  const size_t sstride = (size_t)Prows * pcols;
-  for (int i = threadIdx.x; i < half; i += 64) {
-    float a1 = 0.f, a2 = 0.f;
-    for (int s = 0; s < S; ++s) {
-      a1 += src[s * sstride + i];
-      a2 += src[s * sstride + i + half];
-    }
-    const float x1 = StoreT<T>::round(a1), x2 = StoreT<T>::round(a2);
-    if (rot) {
-      const float2 cs = rope[(size_t)p * half + i];
-      st<T>(dst + i, x1 * cs.x - x2 * cs.y);
-      st<T>(dst + i + half, x2 * cs.x + x1 * cs.y);
-    } else {
-      st<T>(dst + i, x1);
-      st<T>(dst + i + half, x2);
-    }
-  }
+  const LaPostSeg& g = segs[lo];
+  const int mr = m - g.r0;
+  const int pcols = (H + 2 * Hkv) * dh;
+  const size_t off = (size_t)m * pcols + (size_t)hh * dh;
+  const void* s0 = RED ? (const void*)((const float*)src + off) : (const void*)((const T*)src + off);
+  T* kc = (T*)((char*)g.kc + layer * g.kv_layer);
+  T* vc = (T*)((char*)g.vc + layer * g.kv_layer);
+  T* kw = (T*)((char*)g.kw + layer * g.ws_layer);
+  T* vw = (T*)((char*)g.vw + layer * g.ws_layer);
+  T* dst = post_dst<T>(mr, hh, H, Hkv, dh, q + (size_t)m * H * dh, kc, vc, g.T_cap, g.cache_row0, g.n_direct, kw, vw,
+                       g.ws_cap);
+  post_head<T, RED>(s0, S, (size_t)M * pcols, g.rope, g.pos[mr], hh < H + Hkv, dh, dst);
 }
 
 void la_qkv_reduce_post_launch(int dtype, const float* P, int S, int Prows, int M, const float2* rope,
@@ -290,14 +305,14 @@ void la_qkv_reduce_post_launch(int dtype, const float* P, int S, int Prows, int 
                                int cache_row0, int n_direct, void* kw, void* vw, int ws_cap, hipStream_t st) {
   if (M <= 0) return;
   dim3 grid(M, H + 2 * Hkv);
-  const int pcols = (H + 2 * Hkv) * dh;
   if (dtype == LA_DT_BF16)
-    hipLaunchKernelGGL(qkv_reduce_post_kernel<bf16_t>, grid, dim3(64), 0, st, P, S, pcols, Prows, rope, pos, H, Hkv, dh,
-                       (bf16_t*)q, (bf16_t*)kc, (bf16_t*)vc, T_cap, cache_row0, n_direct, (bf16_t*)kw, (bf16_t*)vw,
-                       ws_cap);
+    hipLaunchKernelGGL((qkv_post_kernel<bf16_t, true>), grid, dim3(64), 0, st, (const void*)P, S, Prows, rope, pos, H,
+                       Hkv, dh, (bf16_t*)q, (bf16_t*)kc, (bf16_t*)vc, T_cap, cache_row0, n_direct, (bf16_t*)kw,
+                       (bf16_t*)vw, ws_cap);
   else
-    hipLaunchKernelGGL(qkv_reduce_post_kernel<float>, grid, dim3(64), 0, st, P, S, pcols, Prows, rope, pos, H, Hkv, dh,
-                       (float*)q, (float*)kc, (float*)vc, T_cap, cache_row0, n_direct, (float*)kw, (float*)vw, ws_cap);
+    hipLaunchKernelGGL((qkv_post_kernel<float, true>), grid, dim3(64), 0, st, (const void*)P, S, Prows, rope, pos, H,
+                       Hkv, dh, (float*)q, (float*)kc, (float*)vc, T_cap, cache_row0, n_direct, (float*)kw,
+                       (float*)vw, ws_cap);
 }
 
 void la_qkv_post_launch(int dtype, const void* qkv, const float2* rope, const int32_t* pos, int M, int H, int Hkv,
@@ -306,13 +321,35 @@ void la_qkv_post_launch(int dtype, const void* qkv, const float2* rope, const in
   if (M <= 0) return;
   dim3 grid(M, H + 2 * Hkv);
   if (dtype == LA_DT_BF16)
-    hipLaunchKernelGGL(qkv_post_kernel<bf16_t>, grid, dim3(64), 0, st, (const bf16_t*)qkv, rope, pos, H, Hkv, dh,
+    hipLaunchKernelGGL((qkv_post_kernel<bf16_t, false>), grid, dim3(64), 0, st, qkv, 0, 0, rope, pos, H, Hkv, dh,
                        (bf16_t*)q, (bf16_t*)kc, (bf16_t*)vc, T_cap, cache_row0, n_direct, (bf16_t*)kw, (bf16_t*)vw,
                        ws_cap);
   else
-    hipLaunchKernelGGL(qkv_post_kernel<float>, grid, dim3(64), 0, st, (const float*)qkv, rope, pos, H, Hkv, dh,
+    hipLaunchKernelGGL((qkv_post_kernel<float, false>), grid, dim3(64), 0, st, qkv, 0, 0, rope, pos, H, Hkv, dh,
                        (float*)q, (float*)kc, (float*)vc, T_cap, cache_row0, n_direct, (float*)kw, (float*)vw,
                        ws_cap);
+}
+
+void la_qkv_post_multi_launch(int dtype, const float* P, int S, const void* qkv, int M, const LaPostSeg* segs, int n,
+                              int layer, int H, int Hkv, int dh, void* q, hipStream_t st) {
+  if (M <= 0 || n <= 0) return;
+  dim3 grid(M, H + 2 * Hkv);
+  const void* src = S > 0 ? (const void*)P : qkv;
+  if (dtype == LA_DT_BF16) {
+    if (S > 0)
+      hipLaunchKernelGGL((qkv_post_multi_kernel<bf16_t, true>), grid, dim3(64), 0, st, src, S, M, segs, n, layer, H,
+                         Hkv, dh, (bf16_t*)q);
+    else
+      hipLaunchKernelGGL((qkv_post_multi_kernel<bf16_t, false>), grid, dim3(64), 0, st, src, 0, M, segs, n, layer, H,
+                         Hkv, dh, (bf16_t*)q);
+  } else {
+    if (S > 0)
+      hipLaunchKernelGGL((qkv_post_multi_kernel<float, true>), grid, dim3(64), 0, st, src, S, M, segs, n, layer, H,
+                         Hkv, dh, (float*)q);
+    else
+      hipLaunchKernelGGL((qkv_post_multi_kernel<float, false>), grid, dim3(64), 0, st, src, 0, M, segs, n, layer, H,
+                         Hkv, dh, (float*)q);
+  }
 }
 
 __global__ void fill_i32_kernel(int32_t* p, int n, int v) {

@@ -276,8 +276,12 @@ int la_commit(la_ctx* ctx, const la_accept* acc);
  * la_batch_bytes: device workspace bytes for max_rows rows (0 for bad dims
  * or max_rows outside [1, 256]).
  * la_batch_init: workspace (device, >= la_batch_bytes, 256-byte aligned) is
- * borrowed until la_batch_destroy; weights as for la_init.  LA_EINVAL for
- * bad dims / max_rows / weights, LA_EOVERFLOW for a short workspace. */
+ * borrowed until la_batch_destroy; weights as for la_init.  The batch also
+ * allocates a small pinned host buffer (the per-request argument tables of a
+ * step, under 100 KB at max_rows = 256) and an event, freed by
+ * la_batch_destroy.  LA_EINVAL for bad dims / max_rows / weights,
+ * LA_EOVERFLOW for a short workspace, LA_EDEVICE if the pinned buffer or the
+ * event cannot be created. */
 typedef struct la_batch la_batch;
 uint64_t la_batch_bytes(const la_model_dims* dims, int32_t max_rows);
 int la_batch_init(const la_model_dims* dims, const la_model* weights, int32_t max_rows, void* workspace,

@@ -11,7 +11,11 @@ the rows their own rounds leave in the step's budget, throttled per request.
   final outputs, windows and pools equal the oracle's, and the greedy
   outputs equal autoregressive greedy;
 * with a budget that throttles nothing, each request's rounds are those of
-  its own la_step, bit for bit (tiny fp32 and small bf16 GQA);
+  its own la_step, bit for bit (tiny fp32 and small bf16 GQA); again with
+  prompts long enough that every request's keys are cut in several splits,
+  on small bf16 and on a two-layer model of 7B's shape (32 heads of 128),
+  which runs the per-request passes as one launch per layer with requests
+  of different key splits and capacities side by side;
 * a throttled bf16 batch still emits the GPU autoregressive tokens;
 * bad batches are refused before anything runs.
 """
@@ -65,7 +69,8 @@ def _specs(vocab):
 
 
 def _session(dm, spec):
-    kw = dict(W=spec["W"], N=spec["N"], G=spec["G"], max_new=spec["max_new"], ar_only=spec.get("ar_only", False))
+    kw = dict(W=spec["W"], N=spec["N"], G=spec["G"], max_new=spec["max_new"], ar_only=spec.get("ar_only", False),
+              max_prompt=spec.get("max_prompt"))
     if spec.get("mode") == "sample":
         kw.update(verify_mode=la.LA_VERIFY_SAMPLE, temperature=spec["T"], seed=spec["seed"])
     return la.Session(dm, spec["prompt"], **kw)
@@ -145,6 +150,39 @@ def test_unthrottled_batch_equals_single_sessions(tiny, small_bf16, name):
         if not specs[i].get("ar_only"):
             for key in range(dims.vocab):
                 assert s_one.la_pool_lookup(key) == sessions[i].la_pool_lookup(key), (i, key)
+
+
+def _long_specs(vocab):
+    mk = synthetic.markov_prompt
+    return [
+        dict(prompt=mk(vocab, 300, 10), W=5, N=4, G=5, max_new=24),
+        dict(prompt=mk(vocab, 140, 11), W=4, N=4, G=3, max_new=20, max_prompt=900),
+        dict(prompt=synthetic.copyspan_prompt(vocab, 520, 12)[0], W=6, N=4, G=6, max_new=28),
+        dict(prompt=mk(vocab, 40, 13), W=5, N=4, G=5, max_new=16, ar_only=True),
+        dict(prompt=mk(vocab, 200, 14), W=5, N=4, G=5, max_new=20, mode="sample", T=0.8, seed=3),
+    ]
+
+
+@pytest.fixture(scope="module")
+def l7_2l():
+    dims = synthetic.PRESETS["llama7b_2l"]
+    return dims, la.DeviceModel(dims, seed=0)
+
+
+@pytest.mark.parametrize("name", ["small_bf16", "llama7b_2l"])
+def test_long_unthrottled_batch_equals_single_sessions(small_bf16, l7_2l, name):
+    dims, dm = (small_bf16[0], small_bf16[2]) if name == "small_bf16" else l7_2l
+    specs = _long_specs(dims.vocab)
+    singles = [_single_rounds(dm, s) for s in specs]
+    sessions = [_session(dm, s) for s in specs]
+    batch = la.Batch(dm, max_rows=256)
+    got = _run_batch(batch, sessions, 0)
+    for i, (s_one, rounds) in enumerate(singles):
+        print(f"request {i}: {len(rounds)} rounds", flush=True)
+        mine = [toks[i] for toks, info in got if info[i].Q > 0]
+        assert mine == rounds, i
+        assert s_one.la_get_state() == sessions[i].la_get_state(), i
+        assert s_one.la_stats() == sessions[i].la_stats(), i
 
 
 def test_bf16_throttled_batch_equals_ar(small_bf16):
