@@ -165,6 +165,18 @@ template <int DH> struct AttnT<bf16_t, DH> {
   static __device__ __forceinline__ void load_vr(VF& v, uint32_t base, const int (&rv)[NVR], int c) {
     load_v(v, base, rv, c);
   }
+  // the lower 16 keys only: K of key group 0, V of keys 0-15 (the upper half's V reads as zeros)
+  static __device__ __forceinline__ void load_k_lo(KF& k, uint32_t base, const int (&rk)[2], int g) {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) k.p[0][s] = lds_get<V4u>(piece_addr<ROWB>(base, rk[0], 4 * s + g));
+  }
+  static __device__ __forceinline__ void load_vr_lo(VF& v, uint32_t base, const int (&rv)[NVR], int c) {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      v.p[dt][0] = lds_get_tr16(piece_addr<ROWB>(base, rv[0], 2 * dt + ((c & 3) >> 1)) + 8 * (c & 1));
+      v.p[dt][1] = LdsT<8>::T{0, 0};
+    }
+  }
   // A chunk slot's fragments at fixed per-lane offsets (the second 16-row
   // half of a chunk adds 16 rows, an immediate offset of the LDS read)
   struct Lofs { uint32_t k[KS], v[NDT]; };
@@ -268,6 +280,26 @@ template <int DH> struct AttnT<float, DH> {
   static __device__ __forceinline__ void load_vr(VF& v, uint32_t base, const int (&rv)[NVR], int c) {
     load_v8(v, base, rv, c);
   }
+  static __device__ __forceinline__ void load_k_lo(KF& k, uint32_t base, const int (&rk)[2], int g) {
+#pragma unroll
+    for (int s = 0; s < LP; ++s) k.p[0][s] = lds_get<V4u>(piece_addr<ROWB>(base, rk[0], LP * g + s));
+  }
+  static __device__ __forceinline__ void load_vr_lo(VF& v, uint32_t base, const int (&rv)[NVR], int c) {
+    const int off = VB * c;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if (e >= 4) {
+        v.v[e] = VV{};
+        continue;
+      }
+      const uint32_t a = piece_addr<ROWB>(base, rv[e], off / 16) + off % 16;
+      if constexpr (NDT == 1) {
+        v.v[e].w[0] = lds_get<uint32_t>(a);
+      } else {
+        v.v[e] = __builtin_bit_cast(VV, lds_get<V4u>(a));
+      }
+    }
+  }
   struct Lofs {};
   static __device__ __forceinline__ Lofs lane_ofs(int, int) { return Lofs{}; }
   static __device__ __forceinline__ void load_k_at(KF& k, uint32_t base, const Lofs&, int g, int c) {
@@ -313,6 +345,21 @@ template <int DH> struct AttnT<float, DH> {
   }
   static __device__ __forceinline__ int dim(int dt, int i) { return NDT * i + dt; }
 };
+
+// Maximum / minimum over the 16 lanes of each DPP row (row rotations by 8,
+// 4, 2 and 1): the rows of a tile sit in lanes c = 0..15 of every 16-lane group.
+__device__ __forceinline__ int row16_max(int x) {
+  x = max(x, __builtin_amdgcn_update_dpp(x, x, 0x128, 0xf, 0xf, false));
+  x = max(x, __builtin_amdgcn_update_dpp(x, x, 0x124, 0xf, 0xf, false));
+  x = max(x, __builtin_amdgcn_update_dpp(x, x, 0x122, 0xf, 0xf, false));
+  return max(x, __builtin_amdgcn_update_dpp(x, x, 0x121, 0xf, 0xf, false));
+}
+__device__ __forceinline__ int row16_min(int x) {
+  x = min(x, __builtin_amdgcn_update_dpp(x, x, 0x128, 0xf, 0xf, false));
+  x = min(x, __builtin_amdgcn_update_dpp(x, x, 0x124, 0xf, 0xf, false));
+  x = min(x, __builtin_amdgcn_update_dpp(x, x, 0x122, 0xf, 0xf, false));
+  return min(x, __builtin_amdgcn_update_dpp(x, x, 0x121, 0xf, 0xf, false));
+}
 
 // Reductions over the 4 lanes of a row (lanes l, l^16, l^32, l^48) with the
 // cross-row swaps: both results of a swap hold the pair (low lane, high lane),
@@ -547,9 +594,7 @@ __device__ __forceinline__ void attn_body(const LaAttnArgs& a, const unsigned bl
     int pmin = 0x7fffffff;                          // smallest row position of the wave
 #pragma unroll
     for (int u = 0; u < TPW; ++u) pmin = min(pmin, pos[u]);
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) pmin = min(pmin, __shfl_xor(pmin, o, 64));
-    pmin = __builtin_amdgcn_readfirstlane(pmin);
+    pmin = __builtin_amdgcn_readfirstlane(row16_min(pmin));
     // chunks 0 .. jm - 1 hold a key past some row of the wave: only they are masked
     const int jm = min(nring, max(0, r_hi - (pmin + 1) / CH));
     if (D - 1 < nring) issue(D - 1);
@@ -676,22 +721,23 @@ __device__ __forceinline__ void attn_body(const LaAttnArgs& a, const unsigned bl
     ring_barrier();                               // every wave's part of the stage is visible
     int pmax[TPW];                                // largest row position of each tile
 #pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-      int px = pos[u];
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) px = max(px, __shfl_xor(px, o, 64));
-      pmax[u] = __builtin_amdgcn_readfirstlane(px);
-    }
+    for (int u = 0; u < TPW; ++u) pmax[u] = __builtin_amdgcn_readfirstlane(row16_max(pos[u]));
     // the distinct branches of the wave's tiles: lane k < nu holds the k-th
     int ub = -1, nu = 0;
+    if constexpr (TPW == 1) {
+      // one tile: the row builder's list of its branches is distinct already
+      nu = __builtin_amdgcn_readfirstlane(nbr[0]);
+      ub = lane < nu ? bid[0] : -1;
+    } else {
 #pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-      const int n = __builtin_amdgcn_readfirstlane(nbr[u]);
-      for (int i = 0; i < n; ++i) {
-        const int b = __builtin_amdgcn_readlane(bid[u], i);
-        if (__ballot(ub == b) == 0ull) {
-          ub = lane == nu ? b : ub;
-          ++nu;
+      for (int u = 0; u < TPW; ++u) {
+        const int n = __builtin_amdgcn_readfirstlane(nbr[u]);
+        for (int i = 0; i < n; ++i) {
+          const int b = __builtin_amdgcn_readlane(bid[u], i);
+          if (__ballot(ub == b) == 0ull) {
+            ub = lane == nu ? b : ub;
+            ++nu;
+          }
         }
       }
     }
@@ -700,8 +746,20 @@ __device__ __forceinline__ void attn_body(const LaAttnArgs& a, const unsigned bl
     for (int cidx = t_hi - 1; cidx >= t_lo; --cidx) {
       const int x0 = CH * cidx;
       bool tl[TPW];                               // tiles with a row reaching the chunk (uniform)
+      int pm = -1;
 #pragma unroll
-      for (int u = 0; u < TPW; ++u) tl[u] = tv[u] && pmax[u] >= x0;
+      for (int u = 0; u < TPW; ++u) {
+        tl[u] = tv[u] && pmax[u] >= x0;
+        pm = tl[u] ? max(pm, pmax[u]) : pm;
+      }
+      // whether some row reaches the chunk's upper 16 keys (uniform); if not,
+      // that half's K, V and QK^T are skipped: its scores stay -inf and its
+      // V reads as zeros, so p = 0 there as before
+      const bool hi = pm >= x0 + 16;
+      auto ldk = [&](typename AT::KF& kf, const int (&rk)[2]) __attribute__((always_inline)) {
+        if (hi) AT::load_k(kf, kst, rk, g);
+        else AT::load_k_lo(kf, kst, rk, g);
+      };
       const int xk[2] = {x0 + c16, x0 + 16 + c16};
       int xv[NVR];
 #pragma unroll
@@ -721,6 +779,7 @@ __device__ __forceinline__ void attn_body(const LaAttnArgs& a, const unsigned bl
           if (!tl[u] || __ballot(mine) == 0ull) continue;
 #pragma unroll
           for (int kg = 0; kg < 2; ++kg) {
+            if (kg == 1 && !hi) break;
             const f32x4 s4 = AT::qk(kf, kg, qf[u]);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -736,20 +795,20 @@ __device__ __forceinline__ void attn_body(const LaAttnArgs& a, const unsigned bl
         int rk[2];
         path_read(w, pst, __builtin_amdgcn_readlane(ub, 0), xk, se, maxp);
         path_rows(rk, w, xk, se, tbase, ncom, nws);
-        AT::load_k(ka, kst, rk, g);
+        ldk(ka, rk);
         if (nu > 1) path_read(w, pst, __builtin_amdgcn_readlane(ub, 1), xk, se, maxp);
         for (int k = 0; k < nu; k += 2) {
           // ka: branch k; w: path words of branch k + 1
           if (k + 1 < nu) {
             path_rows(rk, w, xk, se, tbase, ncom, nws);
-            AT::load_k(kb, kst, rk, g);
+            ldk(kb, rk);
             if (k + 2 < nu) path_read(w, pst, __builtin_amdgcn_readlane(ub, k + 2), xk, se, maxp);
           }
           qk_branch(ka, __builtin_amdgcn_readlane(ub, k));
           if (k + 1 >= nu) break;
           if (k + 2 < nu) {
             path_rows(rk, w, xk, se, tbase, ncom, nws);
-            AT::load_k(ka, kst, rk, g);
+            ldk(ka, rk);
             if (k + 3 < nu) path_read(w, pst, __builtin_amdgcn_readlane(ub, k + 3), xk, se, maxp);
           }
           qk_branch(kb, __builtin_amdgcn_readlane(ub, k + 1));
@@ -781,25 +840,29 @@ __device__ __forceinline__ void attn_body(const LaAttnArgs& a, const unsigned bl
           for (int dt = 0; dt < NDT; ++dt) O[u][dt] = AT::pv(vf, dt, pp, O[u][dt]);
         }
       };
+      auto ldv = [&](typename AT::VF& vf, const int (&rv)[NVR]) __attribute__((always_inline)) {
+        if (hi) AT::load_vr(vf, vst, rv, c16);
+        else AT::load_vr_lo(vf, vst, rv, c16);
+      };
       if (nu > 0) {
         typename AT::VF va, vb;
         uint32_t w[NVR];
         int rv[NVR];
         path_read(w, pst, __builtin_amdgcn_readlane(ub, 0), xv, se, maxp);
         path_rows(rv, w, xv, se, tbase, ncom, nws);
-        AT::load_vr(va, vst, rv, c16);
+        ldv(va, rv);
         if (nu > 1) path_read(w, pst, __builtin_amdgcn_readlane(ub, 1), xv, se, maxp);
         for (int k = 0; k < nu; k += 2) {
           if (k + 1 < nu) {
             path_rows(rv, w, xv, se, tbase, ncom, nws);
-            AT::load_vr(vb, vst, rv, c16);
+            ldv(vb, rv);
             if (k + 2 < nu) path_read(w, pst, __builtin_amdgcn_readlane(ub, k + 2), xv, se, maxp);
           }
           pv_branch(va, __builtin_amdgcn_readlane(ub, k));
           if (k + 1 >= nu) break;
           if (k + 2 < nu) {
             path_rows(rv, w, xv, se, tbase, ncom, nws);
-            AT::load_vr(va, vst, rv, c16);
+            ldv(va, rv);
             if (k + 3 < nu) path_read(w, pst, __builtin_amdgcn_readlane(ub, k + 3), xv, se, maxp);
           }
           pv_branch(vb, __builtin_amdgcn_readlane(ub, k + 1));
