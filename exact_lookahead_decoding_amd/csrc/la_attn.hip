@@ -468,6 +468,10 @@ __device__ __forceinline__ void attn_body(const LaAttnArgs& a, const unsigned bl
   constexpr bool LAG = D >= 4;
   extern __shared__ __attribute__((aligned(1024))) char lds[];
 
+  ARGS_READY("s"(a.Hkv), "s"(a.wg_head), "s"(a.rgroups), "s"(a.nsplit), "s"(a.spl), "s"(a.ring_end), "s"(a.tail0),
+             "s"(a.n_tail), "s"(a.shared_end), "s"(a.scale_log2), "s"(a.T_cap), "s"(a.kc), "s"(a.vc), "s"(a.H),
+             "s"(a.Q), "s"(a.q), "s"(a.pos), "s"(a.st_bytes), "s"(a.tile_meta), "s"(a.branch), "s"(a.kw), "s"(a.vw),
+             "s"(a.ws_cap), "s"(a.st_rows), "s"(a.st_half), "s"(a.path), "s"(a.nb), "s"(a.maxp), "s"(a.n_ws));
   // block -> (XCD, KV head, split, row group); the highest splits (tail chunks) first
   const int xcd = blk & 7, bi = blk >> 3;
   const int g_kv = xcd + 8 * (bi / a.wg_head);
@@ -996,6 +1000,7 @@ __global__ void __launch_bounds__(64 * NW) la_attn_multi_kernel(const LaAttnSeg*
 template <typename T, int DH>
 __device__ __forceinline__ void merge_body(const LaAttnArgs& a, const unsigned blk) {
   constexpr int V4 = DH / 4, MS = 8;            // splits whose loads are all issued before the fold
+  ARGS_READY("s"(a.H), "s"(a.Hkv), "s"(a.Q), "s"(a.nsplit), "s"(a.part_ml), "s"(a.part_o), "s"(a.o));
   // block -> (XCD, KV head): the head's split states were written on that
   // XCD (the attention kernel's mapping), so they are read from its L2
   const int group = a.H / a.Hkv;

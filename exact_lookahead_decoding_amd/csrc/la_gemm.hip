@@ -420,6 +420,7 @@ __global__ void __launch_bounds__(256) la_gemm2_kernel(LaGemmArgs a) {
   static_assert((RT * SK) % 4 == 0 && NS >= 3 && (NS - 1) * G < 64, "ring shape");
   extern __shared__ __attribute__((aligned(1024))) char lds[];
 
+  ARGS_READY("s"(a.X), "s"(a.W), "s"(a.M), "s"(a.N), "s"(a.K), "s"(a.ldx), "s"(a.splits), "s"(a.swiglu_partial));
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const bool sw = (EPI == LA_EPI_SWIGLU) || (a.swiglu_partial != 0);
