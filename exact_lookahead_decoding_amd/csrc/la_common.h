@@ -19,6 +19,12 @@ typedef uint16_t bf16_t;
 
 #define LA_WAVE 64
 
+// Kernel arguments a prologue needs, loaded as one batch: an empty asm that
+// takes them as scalar operands makes the compiler issue their loads back to
+// back behind one wait (left alone, it places the loads behind the first
+// branches, one memory round trip each).
+#define ARGS_READY(...) asm volatile("" ::__VA_ARGS__)
+
 __device__ __forceinline__ float bf2f(bf16_t v) {
   return __uint_as_float(((uint32_t)v) << 16);
 }

@@ -28,11 +28,6 @@ template <int N> __device__ __forceinline__ void wait_vm() {
 __device__ __forceinline__ void ring_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
-// Kernel arguments a prologue needs, loaded as one batch: an empty asm that
-// takes them as scalar operands makes the compiler issue their loads back to
-// back behind one wait (left alone, it places the loads behind the first
-// branches, one memory round trip each).
-#define ARGS_READY(...) asm volatile("" ::__VA_ARGS__)
 // The same without the LDS wait, where the slot about to be refilled was read
 // (and its values used) before the barrier: LDS reads issued just before it
 // from another slot stay in flight across it.

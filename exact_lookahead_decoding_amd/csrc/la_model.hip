@@ -72,6 +72,7 @@ __global__ void __launch_bounds__(NTH) addnorm_kernel(T* x, const float* P, size
                                                       T* y, const int32_t* rows, int d, float eps) {
   constexpr int E = 16 / sizeof(T);
   __shared__ float red[NTH / 64];
+  ARGS_READY("s"(x), "s"(P), "s"(pstride), "s"(write_x), "s"(w), "s"(y), "s"(rows), "s"(d), "s"(eps));
   const int m = blockIdx.x;
   const int src = rows ? rows[m] : m;
   const int nv = d / E;
@@ -262,6 +263,8 @@ __global__ void __launch_bounds__(64) qkv_post_kernel(const void* src, int S, in
                                                       const int32_t* pos, int H, int Hkv, int dh, T* q, T* kc, T* vc,
                                                       int T_cap, int cache_row0, int n_direct, T* kw, T* vw,
                                                       int ws_cap) {
+  ARGS_READY("s"(src), "s"(S), "s"(Prows), "s"(rope), "s"(pos), "s"(H), "s"(Hkv), "s"(dh), "s"(q), "s"(kc), "s"(vc),
+             "s"(T_cap), "s"(cache_row0), "s"(n_direct), "s"(kw), "s"(vw), "s"(ws_cap));
   const int m = blockIdx.x;
   const int hh = blockIdx.y;
   const int pcols = (H + 2 * Hkv) * dh;
@@ -278,6 +281,7 @@ template <typename T, bool RED>
 __global__ void __launch_bounds__(64) qkv_post_multi_kernel(const void* src, int S, int M,
                                                             const LaPostSeg* __restrict__ segs, int n, int layer,
                                                             int H, int Hkv, int dh, T* q) {
+  ARGS_READY("s"(src), "s"(S), "s"(M), "s"(segs), "s"(n), "s"(layer), "s"(H), "s"(Hkv), "s"(dh), "s"(q));
   const int m = blockIdx.x;
   const int hh = blockIdx.y;
   int lo = 0, hi = n - 1;
