@@ -27,7 +27,8 @@ Also on the same line:
     five prompt/sampler seeds), each with the same round measurements; and
     4, 8 and 16 of the 512-token requests decoded together by la_batch_step
     under a 256-row budget (aggregate tokens/s against the same requests
-    batched autoregressively).
+    batched autoregressively); and the tiny fp32 decoder of config 1, whose
+    n-grams recur, over five prompt seeds against autoregressive decoding.
 """
 import argparse
 import json
@@ -131,6 +132,36 @@ def step_roofline(model, dims, wl, tokens, steps, secs):
     ms = secs * 1e3 / steps
     return {"bytes_per_round": streamed + kv, "weight_bytes": streamed, "kv_bytes": kv,
             "ms_at_peak": at_peak_ms, "ms_per_round": ms, "frac": at_peak_ms / ms}
+
+
+def measure_tiny(warmup):
+    """Config 1 (the tiny fp32 decoder, whose Markov-prompt n-grams recur in
+    its own greedy continuations): one complete generation per prompt seed
+    0..4, lookahead and autoregressive with the same kernels, aggregated."""
+    import exact_lookahead_decoding_amd.la as la
+    import synthetic
+    dt = synthetic.PRESETS["tiny"]
+    mt = la.DeviceModel(dt, seed=0)
+    tw = WORKLOADS["tiny_w5n3g5"]
+    runs = []
+    for seed in range(5):
+        log(f"tiny_w5n3g5 (prompt seed {seed}):")
+        runs.append(measure(mt, dt, tw, 0, warmup, seed=seed, with_profile=False))
+    secs = sum(r["rounds"] * r["ms_per_round"] * 1e-3 for r in runs)
+    tokens = sum(r["tokens"] for r in runs)
+    ar_secs = sum(r["tokens"] / r["ar_tokens_per_s"] for r in runs)   # the same tokens, autoregressively
+    hist = [sum(r["accepted_hist"][i] for r in runs) for i in range(len(runs[0]["accepted_hist"]))]
+    res = {"desc": tw["desc"] + "; one complete generation per prompt seed (a warmup session runs first), "
+                                "against the same generations decoded autoregressively",
+           "seeds": list(range(5)), "value": tokens / secs, "tokens": tokens,
+           "rounds": sum(r["rounds"] for r in runs), "tokens_per_round": tokens / sum(r["rounds"] for r in runs),
+           "ms_per_round": secs * 1e3 / sum(r["rounds"] for r in runs),
+           "ar_tokens_per_s": tokens / ar_secs, "speedup_vs_ar": ar_secs / secs, "accepted_hist": hist,
+           "value_per_seed": [r["value"] for r in runs],
+           "tokens_per_round_per_seed": [r["tokens_per_round"] for r in runs]}
+    log(f"  tiny: {res['value']:.1f} tokens/s, {res['tokens_per_round']:.3f} tokens/round, "
+        f"{res['speedup_vs_ar']:.2f}x autoregressive")
+    return res
 
 
 def run_steps(make_session, sess, steps):
@@ -786,6 +817,7 @@ def main():
             "desc": w7["desc"] + "; n requests (prompt seeds 0..n-1) per la_batch_step under a 256-row budget, "
                                  "aggregate tokens/s, against the same requests batched autoregressively",
             "requests": batches}
+        extras["tiny_w5n3g5"] = measure_tiny(args.warmup)
         line["extra_workloads"] = extras
     print(json.dumps(line), flush=True)
 
