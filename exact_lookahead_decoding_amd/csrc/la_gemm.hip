@@ -337,14 +337,18 @@ __global__ void __launch_bounds__(256) la_gemm_reduce_kernel(LaGemmArgs a) {
 //
 // A wave owns CW = 2 column tiles of 32 (SwiGLU: the gate and the up tile of
 // the same 32 output columns) over every row tile of 32, so a workgroup of
-// four waves covers 256 columns (SwiGLU: 128 outputs).  Per k16 block a wave
-// reads RT X fragments (shared by the four waves) and its 2 W fragments from
-// LDS for 2 RT MFMAs of 32 cycles: 64 bytes of LDS reads per clock and CU at
-// full MFMA rate, where 16x16x32 tiles would need four times as much.
-//   * W packed (la_gemm_pack_launch): fragment (column tile ct, k16 block
-//     kb) is 1 KB, lane l's 16 bytes = W[32 ct + l % 32][16 kb + 8 (l / 32)
-//     .. +7], ordered [ct][kb] (SwiGLU: [pair][kb][gate, up]); the B operand
-//     layout of the MFMA;
+// NWV waves (4, 3 or 2, a function of the weight shape: the fewer that fill
+// clearly more CUs in one round of workgroups) covers 64 NWV columns (SwiGLU:
+// 32 NWV outputs).  Per k16 block a wave reads RT X fragments (shared by the
+// workgroup's waves) and its 2 W fragments from LDS for 2 RT MFMAs of 32
+// cycles: 64 bytes of LDS reads per clock and CU at full MFMA rate, where
+// 16x16x32 tiles would need four times as much.
+//   * W packed (la_gemm_pack_launch): fragment (tile pair p, k16 block kb,
+//     tile t) is 1 KB, lane l's 16 bytes = W[32 c + l % 32][16 kb + 8 (l / 32)
+//     .. +7] of column tile c = 2 p + t (SwiGLU: the gate (t = 0) or up (t =
+//     1) rows of output tile p), ordered [p][kb][t], the B operand layout of
+//     the MFMA: a wave's two tiles are one contiguous stream (two streams a
+//     tile apart read measurably slower); tiles past N are zero;
 //   * X and W reach LDS by global_load_lds DMA (issued as inline asm, so
 //     the compiler places only LDS waits on the reads; the ring waits for
 //     its own stages with exact vmcnt counts), a ring of NS stages of SK k16
@@ -403,21 +407,28 @@ template <int PW, int KMAX, int K = 0> __device__ __forceinline__ void g2_ring_w
 
 constexpr int G2_CW = 2;
 constexpr int g2_sk(int rt) { return rt <= 4 ? 4 : 2; }                      // k16 blocks per stage
-constexpr int g2_stage(int rt) { return (rt + 4 * G2_CW) * g2_sk(rt) * 1024; }
-constexpr int g2_slots(int rt) { return LDS_BYTES / g2_stage(rt) < 6 ? LDS_BYTES / g2_stage(rt) : 6; }
+constexpr int g2_xi(int rt, int nwv) { return (rt * g2_sk(rt) + nwv - 1) / nwv; }   // X DMA per wave and stage
+constexpr int g2_stage(int rt, int nwv) { return (rt + nwv * G2_CW) * g2_sk(rt) * 1024; }
+// ring slots: as many stages as the LDS holds, at most 6, and few enough that
+// the DMA of the stages in flight stays within the vmcnt counter (63)
+constexpr int g2_slots(int rt, int nwv) {
+  const int by_lds = LDS_BYTES / g2_stage(rt, nwv) < 6 ? LDS_BYTES / g2_stage(rt, nwv) : 6;
+  const int by_cnt = 63 / (G2_CW * g2_sk(rt) + g2_xi(rt, nwv)) + 1;
+  return by_lds < by_cnt ? by_lds : by_cnt;
+}
 
-template <int RT, int EPI>
-__global__ void __launch_bounds__(256) la_gemm2_kernel(LaGemmArgs a) {
-  constexpr int CW = G2_CW, SK = g2_sk(RT), NS = g2_slots(RT);
+template <int RT, int EPI, int NWV>
+__global__ void __launch_bounds__(64 * NWV) la_gemm2_kernel(LaGemmArgs a) {
+  constexpr int CW = G2_CW, SK = g2_sk(RT), NS = g2_slots(RT, NWV);
   constexpr int XB = RT * SK * 1024;              // X bytes of a stage (row tile rt at rt * SK KB)
-  constexpr int STAGE = g2_stage(RT);
-  constexpr int XI = RT * SK / 4;                 // X DMA instructions per wave and stage
+  constexpr int STAGE = g2_stage(RT, NWV);
+  constexpr int XI = g2_xi(RT, NWV);              // X DMA instructions per wave and stage (the last may repeat)
   constexpr int G = CW * SK + XI;                 // DMA instructions per wave and stage
   constexpr int ROWB = SK * 32;                   // bytes of an X row in a stage
   constexpr int PP = ROWB / 16;                   // its 16-byte pieces
   constexpr int RPW = 256 / ROWB;                 // rows per 256-byte bank window
   constexpr int RPI = 1024 / ROWB;                // rows per 1 KB DMA instruction
-  static_assert((RT * SK) % 4 == 0 && NS >= 3 && (NS - 1) * G < 64, "ring shape");
+  static_assert(NS >= 3 && (NS - 1) * G < 64, "ring shape");
   extern __shared__ __attribute__((aligned(1024))) char lds[];
 
   ARGS_READY("s"(a.X), "s"(a.W), "s"(a.M), "s"(a.N), "s"(a.K), "s"(a.ldx), "s"(a.splits), "s"(a.swiglu_partial));
@@ -430,17 +441,16 @@ __global__ void __launch_bounds__(256) la_gemm2_kernel(LaGemmArgs a) {
   const int n = (u1 - u0) * (4 / SK);             // ring stages of the split
   const int kb0 = u0 * 4;                         // first k16 block of the split
   const int nkb = a.K / 16;
-  const int tw = blockIdx.x * 4 + wave;           // the wave's tile pair
+  const int tw = blockIdx.x * NWV + wave;         // the wave's tile pair
   const char* W = (const char*)a.W;
   const bf16_t* X = (const bf16_t*)a.X;
   const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
 
-  // the wave's W fragment (t, k16 block kb) in the packed order; tiles past
-  // the last (a ragged N) read the last tile and store nothing
-  const int ntile = (a.N + 31) / 32;
+  // the wave's W fragment (t, k16 block kb) in the packed order; pairs past
+  // the last (a ragged N) read the last pair and store nothing
+  const int ntile = (a.N + 31) / 32, npair = sw ? ntile : (ntile + 1) / 2;
   auto wfrag = [&](int t, int kb) -> const char* {
-    const size_t f = sw ? ((size_t)min(tw, ntile - 1) * nkb + kb) * 2 + t
-                        : (size_t)min(2 * tw + t, ntile - 1) * nkb + kb;
+    const size_t f = ((size_t)min(tw, npair - 1) * nkb + kb) * 2 + t;
     return W + f * 1024 + 16 * lane;
   };
   // the lane's X source row and piece per X instruction of a stage (row tile rt = q / SK, part ii = q % SK)
@@ -448,7 +458,9 @@ __global__ void __launch_bounds__(256) la_gemm2_kernel(LaGemmArgs a) {
   uint32_t xdst[XI];
 #pragma unroll
   for (int x = 0; x < XI; ++x) {
-    const int q = wave * XI + x, rt = q / SK, ii = q % SK;
+    // the stage's RT SK X blocks dealt to the waves; a wave's slot past the
+    // last repeats the last block (the same bytes to the same LDS place)
+    const int q = min(wave * XI + x, RT * SK - 1), rt = q / SK, ii = q % SK;
     const int r = ii * RPI + lane / PP;           // row inside the 32-row tile
     const int p = lane % PP, lq = p ^ ((r / RPW) % PP);
     const int m = min(rt * 32 + r, a.M - 1);      // rows past M repeat row M - 1 (never stored)
@@ -545,14 +557,11 @@ __global__ void __launch_bounds__(256) la_gemm2_pack_kernel(const bf16_t* W, bf1
   const int lane = (int)(idx & 63);
   const size_t f = idx >> 6;
   const size_t nkb = (size_t)(K / 16);
-  int t = 0;
-  size_t rest = f;
-  if (swiglu) {
-    t = (int)(f & 1);
-    rest = f >> 1;
-  }
-  const int ct = (int)(rest / nkb), kb = (int)(rest % nkb);
-  const int col = ct * 32 + lane % 32;
+  // f = (p * nkb + kb) * 2 + t: tile pair p (SwiGLU: output tile p, gate t = 0 / up t = 1)
+  const int t = (int)(f & 1);
+  const size_t rest = f >> 1;
+  const int p = (int)(rest / nkb), kb = (int)(rest % nkb);
+  const int col = (swiglu ? p : 2 * p + t) * 32 + lane % 32;
   u32x4 v = {0, 0, 0, 0};
   if (col < N) {
     const int row = (swiglu && t ? up_off : 0) + col;
@@ -561,38 +570,63 @@ __global__ void __launch_bounds__(256) la_gemm2_pack_kernel(const bf16_t* W, bf1
   *(u32x4*)(P + idx * 8) = v;
 }
 
-template <int RT, int EPI>
+template <int RT, int EPI, int NWV>
 static void launch_g2(const LaGemmArgs& a, dim3 grid, hipStream_t st) {
-  constexpr int lds = g2_slots(RT) * g2_stage(RT);
+  constexpr int lds = g2_slots(RT, NWV) * g2_stage(RT, NWV);
   static_assert(lds <= LDS_BYTES, "LDS");
-  auto kern = la_gemm2_kernel<RT, EPI>;
+  auto kern = la_gemm2_kernel<RT, EPI, NWV>;
   static bool attr = false;   // idempotent, so a race between threads only repeats it
   if (!attr) {
     hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     attr = true;
   }
-  hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, a);
+  hipLaunchKernelGGL(kern, grid, dim3(64 * NWV), lds, st, a);
 }
 
-template <int EPI>
+template <int EPI, int NWV>
 static void launch_g2_rt(const LaGemmArgs& a, dim3 grid, hipStream_t st) {
   const int rt = (a.M + 31) / 32;
-  if (rt <= 1) launch_g2<1, EPI>(a, grid, st);
-  else if (rt <= 2) launch_g2<2, EPI>(a, grid, st);
-  else if (rt <= 3) launch_g2<3, EPI>(a, grid, st);
-  else if (rt <= 4) launch_g2<4, EPI>(a, grid, st);
-  else if (rt <= 6) launch_g2<6, EPI>(a, grid, st);
-  else launch_g2<8, EPI>(a, grid, st);
+  if (rt <= 1) launch_g2<1, EPI, NWV>(a, grid, st);
+  else if (rt <= 2) launch_g2<2, EPI, NWV>(a, grid, st);
+  else if (rt <= 3) launch_g2<3, EPI, NWV>(a, grid, st);
+  else if (rt <= 4) launch_g2<4, EPI, NWV>(a, grid, st);
+  else if (rt <= 6) launch_g2<6, EPI, NWV>(a, grid, st);
+  else launch_g2<8, EPI, NWV>(a, grid, st);
+}
+
+// Waves per workgroup for N output columns in `splits` K splits: four, or
+// fewer where that fills clearly more of the 256 CUs in one round of
+// workgroups (each CU streams its share of the weights, and a CU's own load
+// rate is bounded).  A function of the weight shape only; a column's
+// arithmetic is its wave's whatever the workgroup size.
+static int g2_waves(int N, int swiglu, int splits) {
+  int best = 4;
+  long best_wgs = 0;
+  for (const int w : {4, 3, 2}) {
+    const int per = swiglu ? w * 32 : w * 32 * G2_CW;
+    const long wgs = (long)((N + per - 1) / per) * splits;
+    if (wgs > 256) continue;
+    if (wgs > best_wgs + 16) { best = w; best_wgs = wgs; }
+  }
+  return best;
+}
+
+template <int EPI, int NWV>
+static void launch_g2_s(const LaGemmArgs& a, hipStream_t st) {
+  const int per = EPI == LA_EPI_SWIGLU ? NWV * 32 : NWV * 32 * G2_CW;   // output columns per workgroup
+  dim3 grid((a.N + per - 1) / per, a.splits);
+  if (a.splits > 1) launch_g2_rt<LA_EPI_PARTIAL, NWV>(a, grid, st);
+  else launch_g2_rt<EPI, NWV>(a, grid, st);
 }
 
 template <int EPI>
 static int launch_g2_t(LaGemmArgs a, hipStream_t st) {
   const bool swiglu = EPI == LA_EPI_SWIGLU;
   a.swiglu_partial = swiglu ? 1 : 0;
-  const int per = swiglu ? 4 * 32 : 4 * 32 * G2_CW;   // output columns per workgroup
-  dim3 grid((a.N + per - 1) / per, a.splits);
-  if (a.splits > 1) launch_g2_rt<LA_EPI_PARTIAL>(a, grid, st);
-  else launch_g2_rt<EPI>(a, grid, st);
+  const int nwv = g2_waves(a.N, swiglu, a.splits);
+  if (nwv == 2) launch_g2_s<EPI, 2>(a, st);
+  else if (nwv == 3) launch_g2_s<EPI, 3>(a, st);
+  else launch_g2_s<EPI, 4>(a, st);
   if (a.splits > 1 && !a.defer_reduce) {
     const size_t total = (size_t)a.M * (a.N / 4);
     hipLaunchKernelGGL((la_gemm_reduce_kernel<bf16_t, EPI>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
@@ -614,7 +648,8 @@ static size_t pack_blocks(int N, int swiglu) {
 }
 
 size_t la_gemm_packed_elems(int dtype, int N, int K, int swiglu) {
-  if (dtype == LA_DT_BF16) return (size_t)((N + 31) / 32) * (swiglu ? 2 : 1) * 32 * (size_t)K;
+  // bf16: tile pairs (SwiGLU: an output tile's gate and up tiles) of 32 x K
+  if (dtype == LA_DT_BF16) return (size_t)(swiglu ? (N + 31) / 32 : ((N + 31) / 32 + 1) / 2) * 2 * 32 * (size_t)K;
   return pack_blocks(N, swiglu) * 4 * la_gemm_ntw(N, swiglu) * 16 * (size_t)K;
 }
 
