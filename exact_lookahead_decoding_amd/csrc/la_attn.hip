@@ -1167,9 +1167,13 @@ static int attn_prep(LaAttnArgs& a) {
 }
 
 // Tiles per workgroup, for calls of tiles[i] tiles per KV head cut in
-// nsplit[i] key splits: the most (up to 8) that still leave about 200
-// workgroups in all, one wave per tile (eight waves: two per SIMD, so one
-// wave's vector ALU work overlaps the other's MFMAs and LDS waits).
+// nsplit[i] key splits: the most (up to 8) that still leave 128 workgroups
+// (half the CUs) in all, one wave per tile (eight waves: two per SIMD, so one
+// wave's vector ALU work overlaps the other's MFMAs and LDS waits, and one
+// workgroup streams each K/V chunk for all its tiles).  Fewer waves per
+// workgroup to fill more CUs lose more than they gain: a workgroup with a
+// tail stage often leaves room for only one per CU, so four-wave workgroups
+// then run one wave per SIMD.
 static int pick_nw(const LaAttnArgs* a, int stride_bytes, int n) {
   auto at = [&](int i) -> const LaAttnArgs& { return *(const LaAttnArgs*)((const char*)a + (size_t)i * stride_bytes); };
   int tmax = 0;
@@ -1181,7 +1185,7 @@ static int pick_nw(const LaAttnArgs* a, int stride_bytes, int n) {
     for (int i = 0; i < n; ++i)
       wgs += (long)kv_slots(at(i).Hkv) * at(i).nsplit * ((attn_tiles(at(i)) + c - 1) / c);
     nw = c;
-    if (wgs >= 200) break;
+    if (wgs >= 128) break;
   }
   return nw;
 }
