@@ -1055,6 +1055,8 @@ struct la_batch {
   hipEvent_t tab_ev = nullptr; // recorded after the last upload: the staging is free once it completed
   std::vector<int32_t> base, found, cap, paused;
   ~la_batch() {
+    // a step that failed after queuing its table upload may leave the copy in flight
+    if (tab_ev) (void)hipEventSynchronize(tab_ev);
     if (tab_ev) (void)hipEventDestroy(tab_ev);
     if (tab_host) (void)hipHostFree(tab_host);
   }
