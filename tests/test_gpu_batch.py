@@ -13,9 +13,10 @@ the rows their own rounds leave in the step's budget, throttled per request.
 * with a budget that throttles nothing, each request's rounds are those of
   its own la_step, bit for bit (tiny fp32 and small bf16 GQA); again with
   prompts long enough that every request's keys are cut in several splits,
-  on small bf16 and on a two-layer model of 7B's shape (32 heads of 128),
-  which runs the per-request passes as one launch per layer with requests
-  of different key splits and capacities side by side;
+  on small bf16, on a two-layer model of 7B's shape (32 heads of 128) and
+  on a two-layer model of CodeLlama-34B's shape (64 query heads on 8 KV
+  heads), which run the per-request passes as one launch per layer with
+  requests of different key splits and capacities side by side;
 * a throttled bf16 batch still emits the GPU autoregressive tokens;
 * bad batches are refused before anything runs.
 """
@@ -169,9 +170,20 @@ def l7_2l():
     return dims, la.DeviceModel(dims, seed=0)
 
 
-@pytest.mark.parametrize("name", ["small_bf16", "llama7b_2l"])
-def test_long_unthrottled_batch_equals_single_sessions(small_bf16, l7_2l, name):
-    dims, dm = (small_bf16[0], small_bf16[2]) if name == "small_bf16" else l7_2l
+@pytest.fixture(scope="module")
+def cl34_2l():
+    # CodeLlama-34B widths at two layers (GQA: 64 query heads on 8 KV heads)
+    dims = synthetic.ModelDims(2, 8192, 64, 8, 128, 22016, 32000, "bf16")
+    return dims, la.DeviceModel(dims, seed=0)
+
+
+@pytest.mark.parametrize("name", ["small_bf16", "llama7b_2l", "codellama34b_2l"])
+def test_long_unthrottled_batch_equals_single_sessions(request, name):
+    if name == "small_bf16":
+        sb = request.getfixturevalue("small_bf16")
+        dims, dm = sb[0], sb[2]
+    else:
+        dims, dm = request.getfixturevalue("l7_2l" if name == "llama7b_2l" else "cl34_2l")
     specs = _long_specs(dims.vocab)
     singles = [_single_rounds(dm, s) for s in specs]
     sessions = [_session(dm, s) for s in specs]
