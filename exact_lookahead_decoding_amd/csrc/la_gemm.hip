@@ -312,18 +312,29 @@ __global__ void __launch_bounds__(256) la_gemm_kernel(LaGemmArgs a) {
 // epilogue; a thread takes four adjacent columns (N is a multiple of 16).
 template <typename T, int EPI>
 __global__ void __launch_bounds__(256) la_gemm_reduce_kernel(LaGemmArgs a) {
+  constexpr int MS = 8;                           // splits whose loads are all issued before the sums
+  ARGS_READY("s"(a.P), "s"(a.Y), "s"(a.M), "s"(a.N), "s"(a.splits), "s"(a.pcols), "s"(a.up_off), "s"(a.ldy));
   const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
   const int n4 = a.N / 4;
   if (idx >= (size_t)a.M * n4) return;
   const int m = (int)(idx / n4), n = 4 * (int)(idx % n4);
   float4 s0 = make_float4(0.f, 0.f, 0.f, 0.f), s1 = s0;
-  for (int s = 0; s < a.splits; ++s) {
-    const float* P = a.P + ((size_t)s * a.M + m) * a.pcols;
-    const float4 v = *(const float4*)(P + n);
-    s0.x += v.x; s0.y += v.y; s0.z += v.z; s0.w += v.w;
-    if (EPI == LA_EPI_SWIGLU) {
-      const float4 u = *(const float4*)(P + a.up_off + n);
-      s1.x += u.x; s1.y += u.y; s1.z += u.z; s1.w += u.w;
+  for (int s00 = 0; s00 < a.splits; s00 += MS) {
+    float4 v[MS], u[MS];
+#pragma unroll
+    for (int k = 0; k < MS; ++k) {
+      if (s00 + k < a.splits) {
+        const float* P = a.P + ((size_t)(s00 + k) * a.M + m) * a.pcols;
+        v[k] = *(const float4*)(P + n);
+        if (EPI == LA_EPI_SWIGLU) u[k] = *(const float4*)(P + a.up_off + n);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < MS; ++k) {
+      if (s00 + k < a.splits) {
+        s0.x += v[k].x; s0.y += v[k].y; s0.z += v[k].z; s0.w += v[k].w;
+        if (EPI == LA_EPI_SWIGLU) { s1.x += u[k].x; s1.y += u[k].y; s1.z += u[k].z; s1.w += u[k].w; }
+      }
     }
   }
   gemm_store<T, EPI>(a, m, n, s0.x, s1.x);
