@@ -80,10 +80,26 @@ __device__ __forceinline__ int slot_key(int g, int e) { return 16 * (e >> 2) + 4
 
 template <int W> struct alignas(4 * W) Words { uint32_t w[W]; };
 
-// LDS address of 16-byte piece q of chunk row r (pieces XOR-swizzled by row)
+// The 16-byte pieces of an LDS chunk row r are XOR-swizzled: position p
+// holds piece p ^ piece_swz(r).  With 16 pieces (256-byte rows, which span
+// the 64 banks once) the swizzle is a bijection of r mod 16 chosen for both
+// fragment reads: a K read (16 B a lane, 16 rows at one piece) sees 16
+// distinct positions, and a transposed V read (8 B a lane, a lane's row pair
+// of pieces 2i, 2i + 1) gives the rows a lane group reads together distinct
+// piece pairs -- rows 0-7 (and 8-15) as well as rows 0-3 with 8-11 (and 4-7
+// with 12-15): a row's partner on its piece pair is row r ^ 12.
+template <int PIECES> __device__ __forceinline__ int piece_swz(int r) {
+  if constexpr (PIECES == 16) {
+    const int x = r & 15, h = x >> 2;
+    return ((x & 3) << 1) | (((h ^ (h >> 1)) & 1) << 3) | (x >> 3);
+  } else {
+    return r % PIECES;
+  }
+}
+// LDS address of 16-byte piece q of chunk row r
 template <int ROWB> __device__ __forceinline__ uint32_t piece_addr(uint32_t base, int r, int q) {
   constexpr int PIECES = ROWB / 16;
-  return base + (uint32_t)(r * ROWB + 16 * (q ^ (r % PIECES)));
+  return base + (uint32_t)(r * ROWB + 16 * (q ^ piece_swz<PIECES>(r)));
 }
 
 // LDS reads are ordinary loads (the compiler places their lgkmcnt waits);
@@ -184,10 +200,11 @@ template <int DH> struct AttnT<bf16_t, DH> {
     constexpr int P = ROWB / 16;
     Lofs o;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) o.k[s] = c * ROWB + 16 * ((4 * s + g) ^ (c % P));
+    for (int s = 0; s < KS; ++s) o.k[s] = c * ROWB + 16 * ((4 * s + g) ^ piece_swz<P>(c));
     const int r = 4 * g + (c >> 2);
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) o.v[dt] = r * ROWB + 16 * ((2 * dt + ((c & 3) >> 1)) ^ (r % P)) + 8 * (c & 1);
+    for (int dt = 0; dt < NDT; ++dt)
+      o.v[dt] = r * ROWB + 16 * ((2 * dt + ((c & 3) >> 1)) ^ piece_swz<P>(r)) + 8 * (c & 1);
     return o;
   }
   static __device__ __forceinline__ void load_k_at(KF& k, uint32_t base, const Lofs& o, int, int) {
@@ -532,7 +549,7 @@ __device__ __forceinline__ void attn_body(const LaAttnArgs& a, const unsigned bl
   for (int j = 0; j < PW; ++j) {
     const int ins = (wave * PW + j) % NI;
     const int r = (ins % (NI / 2)) * RPB + lane / PIECES;
-    lsrc[j] = r * ROWB + 16 * ((lane % PIECES) ^ (r % PIECES));
+    lsrc[j] = r * ROWB + 16 * ((lane % PIECES) ^ piece_swz<PIECES>(r));
   }
   auto issue = [&](int i) __attribute__((always_inline)) {
     const int cidx = r_hi - 1 - i;
@@ -551,7 +568,7 @@ __device__ __forceinline__ void attn_body(const LaAttnArgs& a, const unsigned bl
         const int half = ins / (NI / 2), blk = ins % (NI / 2);
         const int r = blk * RPB + lane / PIECES;
         const int src_row = min(CH * cidx + r, se - 1);
-        dma16((half ? vc : kc) + (size_t)src_row * ROWB + 16 * ((lane % PIECES) ^ (r % PIECES)),
+        dma16((half ? vc : kc) + (size_t)src_row * ROWB + 16 * ((lane % PIECES) ^ piece_swz<PIECES>(r)),
               slot + half * CHB + blk * 1024);
       }
     }
@@ -899,7 +916,7 @@ __device__ __forceinline__ void attn_body(const LaAttnArgs& a, const unsigned bl
       if (r < ncom) src = (half ? vc : kc) + (size_t)(CH * a.tail0 + r) * ROWB;
       else if (r < st_rows) src = (half ? vw : kw) + (size_t)(r - ncom) * ROWB;
       else src = (half ? vc : kc) + (size_t)(se - 1) * ROWB;
-      dma16(src + 16 * ((lane % PIECES) ^ (r % PIECES)), lds_addr(lds + half * a.st_half + blk * 1024));
+      dma16(src + 16 * ((lane % PIECES) ^ piece_swz<PIECES>(r)), lds_addr(lds + half * a.st_half + blk * 1024));
     }
     const int npath = a.nb * a.maxp;
     for (int ins = wave; ins * 64 < npath; ins += NW)

@@ -209,17 +209,19 @@ def test_attention_matches_oracle(case):
     assert err <= tol
 
 
-@pytest.mark.parametrize("p,t_cap", [(765, 1000), (1115, 1166), (2300, 3000)])
-def test_attention_batch_invariance(p, t_cap):
+@pytest.mark.parametrize("p,t_cap,H,Hkv", [(765, 1000, 8, 2), (1115, 1166, 8, 2), (2300, 3000, 8, 2),
+                                            (950, 1000, 32, 4)])
+def test_attention_batch_invariance(p, t_cap, H, Hkv):
     """A packed row's output equals, bit for bit, the same row computed alone
     with its branch ancestors committed to a cache of the same capacity (an
-    autoregressive call).  Every case puts the round's rows across a key-split
-    boundary (8 query heads: splits of max(4, ceil(ceil(t_cap / 32) / 8))
-    chunks of 32 positions -- 768 at capacity 1000, 1120 at 1166, 2304 at
-    3000)."""
+    autoregressive call).  The first cases put the round's rows across a
+    key-split boundary (8 query heads: splits of max(4, ceil(ceil(t_cap / 32)
+    / 8)) chunks of 32 positions -- 768 at capacity 1000, 1120 at 1166, 2304
+    at 3000).  In the last, 32 query heads on 4 KV heads: the round's 56 rows
+    run eight-wave workgroups, each single row's call four-wave ones."""
     sizes, starts = [6, 7, 7, 7], [1, 0, 0, 0]
     cands = [tuple(range(i, i + 4)) for i in range(7)]
-    H, Hkv, dh = 8, 2, 128
+    dh = 128
     got, want, ctx = _attn_case(sizes, starts, cands, 4, p, H, Hkv, dh, "bf16", seed=3, t_cap=t_cap)
     comp, b, info, perm, dev, q, kc, vc, kw, vw, out = ctx
     out_np = out.view(torch.int16).cpu().numpy()
