@@ -318,7 +318,7 @@ static size_t carve(la_ctx* c, char* base) {
   c->z = (int32_t*)take((size_t)c->wstride * 4);
   c->z2 = (int32_t*)take((size_t)std::max(c->wstride, 64) * 4);
   c->tok1 = (int32_t*)take(64);
-  c->escr = (double*)take((size_t)c->V * 8);
+  c->escr = (double*)take(((size_t)c->V + 256) * 8);   // a row's masses, then its block sums
   return off;
 }
 

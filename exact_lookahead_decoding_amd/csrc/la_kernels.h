@@ -178,6 +178,7 @@ struct LaAcceptDev {     // device image of one verification result
 // hmax: most candidate tokens accepted (S, or S - 1 when a full match is capped)
 void la_greedy_accept_launch(const int32_t* amax, int n_inp, const int32_t* cand, int C, int S, int hmax,
                              LaAcceptDev* acc, int32_t* z, hipStream_t st);
+// scratch: V + 256 doubles (the masses of a row, then its block sums)
 void la_sample_accept_launch(const float* logits, int V, int n_inp, const int32_t* amax, const int32_t* cand,
                              int C, int S, int hmax, double T, uint64_t seed, int round_id, double* scratch,
                              LaAcceptDev* acc, int32_t* z, hipStream_t st);
