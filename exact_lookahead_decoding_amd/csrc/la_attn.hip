@@ -1089,11 +1089,13 @@ __global__ void __launch_bounds__(256) la_attn_merge_multi_kernel(const LaAttnSe
 // Chunks per key split: a function of the cache capacity and the model's head
 // counts only (never of the rows of a call), so every call on one cache cuts
 // its keys the same way.  About `target` splits when the cache is full --
-// eight for plain multi-head attention, fewer when many query heads share a KV
-// head (their rows already give enough workgroups) -- and at least 4 chunks.
+// eight up to 40 query heads, fewer for more (their row tiles already give
+// many workgroups: 64 heads take five, which keeps a 90-row round of 64
+// query heads on 8 KV heads within one workgroup per CU with the shortest
+// splits) -- and at least 4 chunks.
 static int spl_for(int t_cap, int H, int Hkv) {
   const int nch = (std::max(t_cap, 1) + CH - 1) / CH;
-  const int target = std::max(1, std::min(8, 256 / std::max(1, H)));
+  const int target = std::max(1, std::min(8, 320 / std::max(1, H)));
   return std::max(4, (nch + target - 1) / target);
 }
 int la_attention_spl(int t_cap, int H, int Hkv) { return spl_for(t_cap, H, Hkv); }

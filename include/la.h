@@ -440,7 +440,7 @@ int la_build_rows(const la_rows_desc* desc, const int32_t* window, const int32_t
  * shared_end - 1 + info->maxp (the largest position a row reaches): one
  * softmax state per row, head and key split.  A key split is a fixed run of
  * chunks of 32 positions whose length depends on t_cap and the head counts
- * only: max(4, ceil(chunks(t_cap) / min(8, 256 / H))) chunks.  Batch
+ * only: max(4, ceil(chunks(t_cap) / min(8, 320 / H))) chunks.  Batch
  * invariant: a row's result does not depend on the other rows of the call
  * (its reduction tree is a function of key positions, t_cap and the head
  * counts only).  The call only launches (on stream).
