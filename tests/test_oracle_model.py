@@ -136,3 +136,30 @@ def test_pool_is_exactly_the_trajectory_ngrams(tiny):
             pool.lru_upsert(replay, gram[0], tuple(gram[1:]), G)
     assert replay == la["token_map"]
     assert all(len(v) <= G for v in replay.values())
+
+
+def test_generated_prefix_insertion_keeps_ar_and_pool(tiny):
+    """With the generated-prefix insertion the output is still autoregressive
+    greedy, and the pool is the replay of the trajectory n-grams of each round
+    followed by the n-grams that round's new tokens complete (the first token's
+    at the start), with the same lookups feeding later rounds."""
+    W, N, G = 5, 4, 3
+    prompt = synthetic.markov_prompt(256, 32, 0)
+    la = lookahead_generate(tiny, prompt, W, N, G, 64, pool_from_output=True)
+    assert la["tokens"] == ar_generate(tiny, prompt, 64)
+    replay = {}
+    seq = list(prompt) + la["tokens"][:1]
+    pool.insert_output_ngrams(replay, seq, len(prompt), len(seq), N, G)
+    for r in la["rounds"]:
+        if None not in r.level_sizes:
+            for col, path, zj in zip(r.inp_columns, r.deep_paths, r.z):
+                gram = path[-(N - 1):] + [zj]
+                pool.lru_upsert(replay, gram[0], tuple(gram[1:]), G)
+        n0 = len(seq)
+        seq += r.emitted[: 64 - (len(seq) - len(prompt))]
+        pool.insert_output_ngrams(replay, seq, n0, len(seq), N, G)
+    assert seq == list(prompt) + la["tokens"]
+    assert replay == la["token_map"]
+    # the insertion changes what later rounds look up: not the plain run's rounds
+    plain = lookahead_generate(tiny, prompt, W, N, G, 64)
+    assert [r.candidates for r in plain["rounds"]] != [r.candidates for r in la["rounds"]]
