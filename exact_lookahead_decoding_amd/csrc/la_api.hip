@@ -26,6 +26,7 @@
 #define PREFILL_CHUNK 128
 #define LA_MAX_DEVICES 64
 #define LK_WORDS (1 + 64 * LA_MAX_N)
+#define OG_WORDS (LA_MAX_N * LA_MAX_N)   // one round's output n-grams: at most N of N words
 
 static thread_local std::string g_err;
 
@@ -85,8 +86,10 @@ struct la_ctx {
   // the next round's pool lookup, started by la_commit: its count and
   // candidates land in pinned host memory (lk_key: the key, -1: none);
   // the verification result follows them in the same allocation
-  int32_t* lk_host = nullptr;   // [LK_WORDS] then one LaAcceptDev
+  int32_t* lk_host = nullptr;   // [LK_WORDS] then one LaAcceptDev, then [OG_WORDS]
   LaAcceptDev* acc_host = nullptr;
+  int32_t* og_host = nullptr;   // staging of the output n-grams a round inserts
+  std::vector<int32_t> ptail;   // the prompt's last N - 1 tokens (n-grams reaching into the prompt)
   int lk_key = -1;
   ~la_ctx() {
     if (lk_host) (void)hipHostFree(lk_host);
@@ -179,6 +182,8 @@ static int validate_cfg(const la_config* cfg, const la_model_dims* d, la_ctx* c)
     return fail(c, LA_EINVAL, "advance_by_accepted %d (0 or 1)", cfg->advance_by_accepted);
   if (cfg->cap_full_match != 0 && cfg->cap_full_match != 1)
     return fail(c, LA_EINVAL, "cap_full_match %d (0 or 1)", cfg->cap_full_match);
+  if (cfg->pool_from_output != 0 && cfg->pool_from_output != 1)
+    return fail(c, LA_EINVAL, "pool_from_output %d (0 or 1)", cfg->pool_from_output);
   return validate_dims(d, c);
 }
 
@@ -604,6 +609,35 @@ static void rows_layout(const LaLayout& L, int32_t* base, LaRowsDev* r, la_rows_
 
 // ------------------------------------------------------------------ lifecycle
 
+// Generated-prefix insertion (pool_from_output; "M7.3", 0x06A pool plan):
+// the n-grams that output tokens k0.. (all of c->out from k0 on) complete in
+// the text prompt + output, in text order -- key the token N - 1 before,
+// suffix the N - 1 tokens up to the new one -- by one wavefront's LRU upsert
+// on the stream.  Staged in pinned memory: its previous contents were
+// consumed before the caller's last stream synchronisation.
+static int insert_output_ngrams(la_ctx* c, int k0) {
+  if (!c->cfg.pool_from_output || c->cfg.ar_only || c->cfg.G <= 0) return LA_OK;
+  const int S = c->S, np = (int)c->ptail.size(), k1 = (int)c->out.size();
+  auto tok = [&](int g) { return g < np ? c->ptail[g] : c->out[g - np]; };   // g: index in ptail ++ out
+  int32_t key[LA_MAX_N], suf[LA_MAX_N * LA_MAX_N];
+  int n = 0;
+  for (int k = k0; k < k1; ++k) {
+    const int g = np + k;
+    if (g < S) continue;                          // fewer than N tokens of text so far
+    key[n] = tok(g - S);
+    for (int s = 0; s < S; ++s) suf[n * S + s] = tok(g - S + 1 + s);
+    ++n;
+  }
+  if (n == 0) return LA_OK;
+  if (n > LA_MAX_N) return fail(c, LA_EINVAL, "%d output n-grams in one round", n);
+  memcpy(c->og_host, key, (size_t)n * 4);
+  memcpy(c->og_host + n, suf, (size_t)n * S * 4);
+  HIPCHK(c, hipMemcpyAsync(c->vcand, c->og_host, (size_t)n * (1 + S) * 4, hipMemcpyHostToDevice, c->st));
+  la_pool_upsert_launch(c->pool_cnt, c->pool_ent, c->vcand, c->vcand + n, n, c->cfg.G, S, c->st);
+  HIPCHK(c, hipGetLastError());
+  return LA_OK;
+}
+
 extern "C" int la_init(const la_config* cfg, const la_model_dims* dims, const la_model* weights, void* kv,
                        void* arena, const int32_t* prompt, int32_t prompt_len, void* stream, la_ctx** out) {
   if (!out) return fail(nullptr, LA_EINVAL, "null ctx output");
@@ -633,13 +667,16 @@ extern "C" int la_init(const la_config* cfg, const la_model_dims* dims, const la
   c->kc = (char*)kv;
   c->vc = (char*)kv + kvb;
   carve(c, (char*)arena);
-  if (hipHostMalloc((void**)&c->lk_host, LK_WORDS * sizeof(int32_t) + sizeof(LaAcceptDev), hipHostMallocDefault) !=
-      hipSuccess) {
+  if (hipHostMalloc((void**)&c->lk_host,
+                    LK_WORDS * sizeof(int32_t) + sizeof(LaAcceptDev) + OG_WORDS * sizeof(int32_t),
+                    hipHostMallocDefault) != hipSuccess) {
     c->lk_host = nullptr;
     delete c;
     return fail(nullptr, LA_EDEVICE, "pinned host buffer");
   }
   c->acc_host = (LaAcceptDev*)(c->lk_host + LK_WORDS);
+  c->og_host = (int32_t*)(c->acc_host + 1);
+  c->ptail.assign(prompt + std::max(0, prompt_len - c->S), prompt + prompt_len);
   memset(&c->stats, 0, sizeof c->stats);
   for (int r = 0; r < LA_MAX_N; ++r) c->sizes[r] = 0;
   c->cur = 0;
@@ -712,6 +749,7 @@ extern "C" int la_init(const la_config* cfg, const la_model_dims* dims, const la
   c->out.push_back(first);
   c->kv_len = prompt_len;
   c->stats.tokens = 1;
+  if ((rc = insert_output_ngrams(c, 0))) { g_err = c->err; return bail(rc); }   // the n-gram the first token completes
   *out = c;
   return LA_OK;
 }
@@ -978,7 +1016,11 @@ extern "C" int la_commit(la_ctx* c, const la_accept* a) {
   HIPCHK(c, hipGetLastError());
   c->kv_len += 1 + a->h;
   int added = 0;
+  const int k0 = (int)c->out.size();
   for (int k = 0; k < a->n_emit && (int)c->out.size() < c->cfg.max_new; ++k, ++added) c->out.push_back(a->emitted[k]);
+  // after the trajectory's n-grams, before the next round's lookup (a paused round leaves the pool
+  // alone); past publication nothing returns an error -- a failed launch shows at the next call
+  if (!c->paused) (void)insert_output_ngrams(c, k0);
   c->round_id = rid;
   c->pending = false;
   c->verified = false;

@@ -48,7 +48,7 @@ class la_config(C.Structure):
     _fields_ = [("W", C.c_int32), ("N", C.c_int32), ("G", C.c_int32), ("max_new", C.c_int32),
                 ("verify_mode", C.c_int32), ("ar_only", C.c_int32), ("temperature", C.c_double),
                 ("seed", C.c_uint64), ("max_prompt", C.c_int32), ("pool_from_prompt", C.c_int32),
-                ("advance_by_accepted", C.c_int32), ("cap_full_match", C.c_int32)]
+                ("advance_by_accepted", C.c_int32), ("cap_full_match", C.c_int32), ("pool_from_output", C.c_int32)]
 
 
 class la_sizes(C.Structure):
@@ -280,9 +280,10 @@ def la_query_sizes(cfg: la_config, dims: la_model_dims) -> la_sizes:
 
 
 def make_config(W, N, G, max_new, max_prompt, verify_mode=LA_VERIFY_GREEDY, temperature=1.0, seed=0, ar_only=False,
-                pool_from_prompt=False, advance_by_accepted=False, cap_full_match=False):
+                pool_from_prompt=False, advance_by_accepted=False, cap_full_match=False, pool_from_output=False):
     return la_config(W, N, G, max_new, verify_mode, int(bool(ar_only)), float(temperature), int(seed), max_prompt,
-                     int(bool(pool_from_prompt)), int(bool(advance_by_accepted)), int(bool(cap_full_match)))
+                     int(bool(pool_from_prompt)), int(bool(advance_by_accepted)), int(bool(cap_full_match)),
+                     int(bool(pool_from_output)))
 
 
 class Session:
@@ -290,11 +291,11 @@ class Session:
 
     def __init__(self, model: DeviceModel, prompt, W, N, G, max_new, verify_mode=LA_VERIFY_GREEDY, temperature=1.0,
                  seed=0, ar_only=False, max_prompt=None, stream=None, pool_from_prompt=False,
-                 advance_by_accepted=False, cap_full_match=False):
+                 advance_by_accepted=False, cap_full_match=False, pool_from_output=False):
         lib = load()
         self.model = model
         self.cfg = make_config(W, N, G, max_new, max_prompt or len(prompt), verify_mode, temperature, seed, ar_only,
-                               pool_from_prompt, advance_by_accepted, cap_full_match)
+                               pool_from_prompt, advance_by_accepted, cap_full_match, pool_from_output)
         self.dims = dims_struct(model.dims)
         self.sizes = la_query_sizes(self.cfg, self.dims)
         dev = model.embed.device

@@ -124,6 +124,14 @@ typedef struct la_config {
                                at most S - 1 K/V rows; 0: a full match of S tokens also emits the
                                target token read from its last row (S + 1 tokens).  The output
                                is exact either way; only accepted lengths differ */
+  int32_t pool_from_output; /* 1: generated-prefix insertion ("M7.3", 0x06A names it, optional, in
+                               the pool plan): the n-gram each generated token completes in the
+                               text prompt + output (key the token N - 1 before it, suffix the
+                               N - 1 tokens up to it) enters the pool by the per-key LRU rule, in
+                               text order, after the round's trajectory n-grams -- the first
+                               token's at la_init; a paused batch round inserts none.  With
+                               pool_from_prompt the pool so sees every n-gram of the text;
+                               0: off */
 } la_config;
 
 /* Buffer sizes for a (config, dims) pair.  The caller allocates

@@ -63,7 +63,7 @@ def _specs(vocab):
     return [
         dict(prompt=mk(vocab, 32, 0), W=5, N=4, G=5, max_new=48),
         dict(prompt=mk(vocab, 40, 1), W=4, N=4, G=3, max_new=40),
-        dict(prompt=synthetic.copyspan_prompt(vocab, 80, 2)[0], W=6, N=4, G=6, max_new=56),
+        dict(prompt=synthetic.copyspan_prompt(vocab, 80, 2)[0], W=6, N=4, G=6, max_new=56, pool_from_output=True),
         dict(prompt=mk(vocab, 28, 3), W=5, N=4, G=5, max_new=30, ar_only=True),
         dict(prompt=mk(vocab, 36, 4), W=5, N=4, G=5, max_new=40, mode="sample", T=0.7, seed=5),
     ]
@@ -71,7 +71,7 @@ def _specs(vocab):
 
 def _session(dm, spec):
     kw = dict(W=spec["W"], N=spec["N"], G=spec["G"], max_new=spec["max_new"], ar_only=spec.get("ar_only", False),
-              max_prompt=spec.get("max_prompt"))
+              max_prompt=spec.get("max_prompt"), pool_from_output=spec.get("pool_from_output", False))
     if spec.get("mode") == "sample":
         kw.update(verify_mode=la.LA_VERIFY_SAMPLE, temperature=spec["T"], seed=spec["seed"])
     return la.Session(dm, spec["prompt"], **kw)

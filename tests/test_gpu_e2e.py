@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 
 import synthetic
-from oracle.decode import ar_generate, lookahead_generate
+from oracle.decode import LookaheadRequest, ar_generate, lookahead_generate
 from oracle.model import OracleModel
 from oracle import pool as opool
 
@@ -110,6 +110,36 @@ def test_pool_from_prompt_matches_oracle(tiny, W, N, G):
         assert (acc.h, acc.winner) == (rr.h, rr.winner), k
         sess.la_commit(acc)
     assert sess.la_get_state()["output"] == ref["tokens"] == ar_generate(om, prompt, max_new)
+
+
+@pytest.mark.parametrize("W,N,G,from_prompt", [(5, 3, 5, False), (4, 4, 2, True), (6, 5, 4, True)])
+def test_pool_from_output_matches_oracle(tiny, W, N, G, from_prompt):
+    """Generated-prefix insertion: after la_init the device pool equals the
+    oracle's (the first token's n-gram, over the seeded prompt ones when
+    POOL_FROM_PROMPT is on); every round's candidates and accepted length
+    match the oracle's run with the insertion, the final pool equals its pool
+    for every key, and the tokens still equal autoregressive greedy."""
+    dims, w, dm, om = tiny
+    prompt = synthetic.markov_prompt(dims.vocab, 40, 3)
+    max_new = 48
+    print(f"pool_from_output W={W} N={N} G={G} from_prompt={from_prompt}", flush=True)
+    req = LookaheadRequest(om, prompt, W, N, G, max_new, pool_from_prompt=from_prompt, pool_from_output=True)
+    sess = la.Session(dm, prompt, W=W, N=N, G=G, max_new=max_new, pool_from_prompt=from_prompt,
+                      pool_from_output=True)
+    for key in range(dims.vocab):
+        assert sess.la_pool_lookup(key) == opool.lookup(req.token_map, key, G), key
+    k = 0
+    while not req.done():
+        rr = req.round()
+        info = sess.la_predict()
+        assert info.C == len(rr.candidates), k
+        acc, _ = sess.la_verify()
+        assert (acc.h, acc.winner) == (rr.h, rr.winner), k
+        sess.la_commit(acc)
+        k += 1
+    assert sess.la_get_state()["output"] == req.out == ar_generate(om, prompt, max_new)
+    for key in range(dims.vocab):
+        assert sess.la_pool_lookup(key) == opool.lookup(req.token_map, key, G), key
 
 
 @pytest.mark.parametrize("W,N,G,seed", [(5, 3, 5, 0), (4, 4, 3, 1)])

@@ -46,11 +46,11 @@ def test_invalid_configs_rejected():
 
 
 def test_option_flags_validated():
-    """pool_from_prompt, advance_by_accepted and cap_full_match are 0 or 1."""
+    """pool_from_prompt, advance_by_accepted, cap_full_match and pool_from_output are 0 or 1."""
     d = la.dims_struct(synthetic.PRESETS["tiny"])
     la.la_query_sizes(la.make_config(5, 3, 5, 10, 10, pool_from_prompt=True, advance_by_accepted=True,
-                                     cap_full_match=True), d)
-    for field in ("pool_from_prompt", "advance_by_accepted", "cap_full_match"):
+                                     cap_full_match=True, pool_from_output=True), d)
+    for field in ("pool_from_prompt", "advance_by_accepted", "cap_full_match", "pool_from_output"):
         cfg = la.make_config(5, 3, 5, 10, 10)
         setattr(cfg, field, 2)
         with pytest.raises(la.LaError) as e:
