@@ -619,6 +619,7 @@ static int insert_output_ngrams(la_ctx* c, int k0) {
   if (!c->cfg.pool_from_output || c->cfg.ar_only || c->cfg.G <= 0) return LA_OK;
   const int S = c->S, np = (int)c->ptail.size(), k1 = (int)c->out.size();
   auto tok = [&](int g) { return g < np ? c->ptail[g] : c->out[g - np]; };   // g: index in ptail ++ out
+  if (k1 - k0 > LA_MAX_N) return fail(c, LA_EINVAL, "%d output tokens in one round", k1 - k0);
   int32_t key[LA_MAX_N], suf[LA_MAX_N * LA_MAX_N];
   int n = 0;
   for (int k = k0; k < k1; ++k) {
@@ -629,7 +630,6 @@ static int insert_output_ngrams(la_ctx* c, int k0) {
     ++n;
   }
   if (n == 0) return LA_OK;
-  if (n > LA_MAX_N) return fail(c, LA_EINVAL, "%d output n-grams in one round", n);
   memcpy(c->og_host, key, (size_t)n * 4);
   memcpy(c->og_host + n, suf, (size_t)n * S * 4);
   HIPCHK(c, hipMemcpyAsync(c->vcand, c->og_host, (size_t)n * (1 + S) * 4, hipMemcpyHostToDevice, c->st));
