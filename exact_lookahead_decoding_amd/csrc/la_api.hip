@@ -23,7 +23,7 @@
 #include <string>
 #include <vector>
 
-#define PREFILL_CHUNK 128
+#define PREFILL_CHUNK 256
 #define LA_MAX_DEVICES 64
 #define LK_WORDS (1 + 64 * LA_MAX_N)
 #define OG_WORDS (LA_MAX_N * LA_MAX_N)   // one round's output n-grams: at most N of N words
