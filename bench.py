@@ -367,7 +367,7 @@ def gemm_traffic(wl_name):
     return float(vals["traffic_bytes_per_launch"])
 
 
-def profile_rounds(wl_name, rounds, warmup=5):
+def profile_rounds(wl_name, rounds, warmup=5, verify="greedy"):
     """The workload's lookahead rounds alone (after prefill and warmup rounds),
     with HIP events around every GEMM and attention launch, then a plain copy
     of COPY_BYTES that calibrates the FETCH_SIZE / WRITE_SIZE counters.  The
@@ -382,7 +382,9 @@ def profile_rounds(wl_name, rounds, warmup=5):
     dims = synthetic.PRESETS[wl["model"]]
     model = la.DeviceModel(dims, seed=0)
     prompt, _ = make_prompt(wl, dims, 0)
-    sess = la.Session(model, prompt, W=wl["W"], N=wl["N"], G=wl["G"], max_new=wl["max_new"])
+    vm = la.LA_VERIFY_SAMPLE if verify == "sample" else la.LA_VERIFY_GREEDY
+    sess = la.Session(model, prompt, W=wl["W"], N=wl["N"], G=wl["G"], max_new=wl["max_new"], verify_mode=vm,
+                      temperature=0.7, seed=0)
     for _ in range(warmup):
         sess.la_step()
     torch.cuda.synchronize()
@@ -398,7 +400,7 @@ def profile_rounds(wl_name, rounds, warmup=5):
     for _ in range(3):
         dst.copy_(src)
     torch.cuda.synchronize()
-    print(json.dumps({"workload": wl_name, "rounds": rounds, "ms_per_round": secs * 1e3 / rounds,
+    print(json.dumps({"workload": wl_name, "verify": verify, "rounds": rounds, "ms_per_round": secs * 1e3 / rounds,
                       "copy_bytes": COPY_BYTES, **kernel_rates(pr)}), flush=True)
 
 
@@ -455,7 +457,8 @@ def trace_summary(trace_csv, run_json, out_md, cmd):
     for i in g_sel + a_sel:
         per[names[i]][0] += 1
         per[names[i]][1] += disp[i][1] / 1e3
-    lines = [f"# Kernel trace of the rounds: {run['workload']} ({WORKLOADS[run['workload']]['desc']})", "",
+    sampled = ", sampled verification (temperature 0.7)" if run.get("verify") == "sample" else ""
+    lines = [f"# Kernel trace of the rounds: {run['workload']} ({WORKLOADS[run['workload']]['desc']}{sampled})", "",
              "Command (run from /tmp with TMPDIR=/tmp on one MI355X):", "", "```", cmd, "```", "",
              f"{run['rounds']} lookahead rounds after prefill and 5 warmup rounds, "
              f"{run['ms_per_round']:.3f} ms per round in the traced run.", "",
@@ -698,6 +701,9 @@ def main():
                     help="write the attention op's kernel-time and HBM-traffic summary under profiles/")
     ap.add_argument("--profile-rounds", type=int, default=0,
                     help="run only N rounds of --workload with kernel events (for rocprofv3 runs)")
+    ap.add_argument("--verify", choices=("greedy", "sample"), default="greedy",
+                    help="with --profile-rounds (and --trace-summary): the verification of the rounds "
+                         "(sample: temperature 0.7, sampler seed 0)")
     ap.add_argument("--trace-summary", nargs=3, metavar=("TRACE_CSV", "RUN_JSON", "OUT_MD"))
     ap.add_argument("--pmc-summary", nargs=3, metavar=("FETCH_DB", "WRITE_DB", "RUN_JSON"),
                     help="write the GEMM traffic summary under profiles/ from two counter runs")
@@ -705,7 +711,8 @@ def main():
     if args.trace_summary:
         trace_summary(*args.trace_summary, cmd=" ".join(
             ["rocprofv3 --kernel-trace --stats --output-format csv -d out/trace -o t -- python3 bench.py",
-             f"--profile-rounds N --workload {args.workload}"]))
+             f"--profile-rounds N --workload {args.workload}"]
+            + ([f"--verify {args.verify}"] if args.verify != "greedy" else [])))
         return
     if args.pmc_summary:
         md = pmc_summary(*args.pmc_summary, args.workload)
@@ -713,7 +720,7 @@ def main():
         print(md)
         return
     if args.profile_rounds:
-        profile_rounds(args.workload, args.profile_rounds)
+        profile_rounds(args.workload, args.profile_rounds, verify=args.verify)
         return
     if args.attn_summary:
         attn_summary(*args.attn_summary)
