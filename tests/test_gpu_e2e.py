@@ -112,20 +112,25 @@ def test_pool_from_prompt_matches_oracle(tiny, W, N, G):
     assert sess.la_get_state()["output"] == ref["tokens"] == ar_generate(om, prompt, max_new)
 
 
-@pytest.mark.parametrize("W,N,G,from_prompt", [(5, 3, 5, False), (4, 4, 2, True), (6, 5, 4, True)])
-def test_pool_from_output_matches_oracle(tiny, W, N, G, from_prompt):
+@pytest.mark.parametrize("W,N,G,from_prompt,mode", [(5, 3, 5, False, "greedy"), (4, 4, 2, True, "greedy"),
+                                                     (6, 5, 4, True, "greedy"), (5, 4, 5, False, "sample")])
+def test_pool_from_output_matches_oracle(tiny, W, N, G, from_prompt, mode):
     """Generated-prefix insertion: after la_init the device pool equals the
     oracle's (the first token's n-gram, over the seeded prompt ones when
     POOL_FROM_PROMPT is on); every round's candidates and accepted length
     match the oracle's run with the insertion, the final pool equals its pool
-    for every key, and the tokens still equal autoregressive greedy."""
+    for every key, and the tokens equal the oracle's (autoregressive greedy
+    when greedy; under sampling the inserted n-grams are the sampled text's)."""
     dims, w, dm, om = tiny
     prompt = synthetic.markov_prompt(dims.vocab, 40, 3)
     max_new = 48
-    print(f"pool_from_output W={W} N={N} G={G} from_prompt={from_prompt}", flush=True)
-    req = LookaheadRequest(om, prompt, W, N, G, max_new, pool_from_prompt=from_prompt, pool_from_output=True)
+    print(f"pool_from_output W={W} N={N} G={G} from_prompt={from_prompt} {mode}", flush=True)
+    samp = dict(mode="sample", T=0.7, seed=4) if mode == "sample" else {}
+    req = LookaheadRequest(om, prompt, W, N, G, max_new, pool_from_prompt=from_prompt, pool_from_output=True,
+                           **samp)
+    extra = dict(verify_mode=la.LA_VERIFY_SAMPLE, temperature=0.7, seed=4) if mode == "sample" else {}
     sess = la.Session(dm, prompt, W=W, N=N, G=G, max_new=max_new, pool_from_prompt=from_prompt,
-                      pool_from_output=True)
+                      pool_from_output=True, **extra)
     for key in range(dims.vocab):
         assert sess.la_pool_lookup(key) == opool.lookup(req.token_map, key, G), key
     k = 0
@@ -137,7 +142,9 @@ def test_pool_from_output_matches_oracle(tiny, W, N, G, from_prompt):
         assert (acc.h, acc.winner) == (rr.h, rr.winner), k
         sess.la_commit(acc)
         k += 1
-    assert sess.la_get_state()["output"] == req.out == ar_generate(om, prompt, max_new)
+    assert sess.la_get_state()["output"] == req.out
+    if mode == "greedy":
+        assert req.out == ar_generate(om, prompt, max_new)
     for key in range(dims.vocab):
         assert sess.la_pool_lookup(key) == opool.lookup(req.token_map, key, G), key
 
